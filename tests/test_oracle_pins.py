@@ -1,0 +1,406 @@
+"""Pins for the fp64 oracle against what the pages and the mathematics fix.
+
+Each test names the property it checks and the passage (page title plus
+section) or the mathematical fact behind it.  A plausible mistake in the
+oracle -- a dropped norm term, a wrong sign, a missing 1/sqrt(m), a
+transposed operand, an unorthogonalised block, a wrong mask -- fails at least
+one of them.  None of these tests re-types the oracle's formula: each compares
+it with an independent fact (closed form, invariant, brute force, library
+routine, distribution law).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle
+
+pytestmark = []
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# The random stream (pages name none; the draw must be uniform / Gaussian).
+# ---------------------------------------------------------------------------
+def test_uniforms_are_uniform_and_in_half_open_interval():
+    u = oracle.uniforms(123, 0, 200_000)
+    assert u.min() > 0.0 and u.max() <= 1.0
+    assert scipy.stats.kstest(u, "uniform").pvalue > 1e-3
+    # consecutive draws uncorrelated
+    assert abs(np.corrcoef(u[:-1], u[1:])[0, 1]) < 5 / math.sqrt(u.size)
+
+
+def test_uniform_stream_is_counter_based():
+    # any window of the stream equals the same slice of a longer draw
+    a = oracle.uniforms(9, 0, 1000)
+    b = oracle.uniforms(9, 517, 100)
+    np.testing.assert_array_equal(a[517:617], b)
+    # different seeds give different streams
+    assert not np.array_equal(oracle.uniforms(10, 0, 100), a[:100])
+
+
+def test_normals_are_standard_normal():
+    z = oracle.normals(77, 0, 200_000)
+    assert scipy.stats.kstest(z, "norm").pvalue > 1e-3
+    assert abs(z.mean()) < 5 / math.sqrt(z.size)
+    assert abs(z.var() - 1.0) < 5 * math.sqrt(2.0 / z.size)
+    # the cosine and sine halves of each Box-Muller pair are uncorrelated
+    assert abs(np.corrcoef(z[0::2], z[1::2])[0, 1]) < 5 / math.sqrt(z.size / 2)
+
+
+def test_normals_window_consistency_odd_start():
+    full = oracle.normals(5, 0, 101)
+    np.testing.assert_array_equal(oracle.normals(5, 37, 20), full[37:57])
+    np.testing.assert_array_equal(oracle.normals(5, 38, 1), full[38:39])
+
+
+# ---------------------------------------------------------------------------
+# P1-P3: the projection W (summary page, "Key contributions" and
+# "Limitations": positive orthogonal random features, orthogonal for at most
+# d rows; block reading with chi(d) norms).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,d", [(16, 16), (256, 64), (512, 128), (40, 16)])
+def test_P1_block_orthogonality(m, d):
+    W = oracle.draw_w(1000 + m + d, m, d)
+    assert W.shape == (m, d)
+    for b0 in range(0, m, d):
+        Wb = W[b0:b0 + d]
+        G = Wb @ Wb.T
+        diag = np.diag(G)
+        off = G - np.diag(diag)
+        assert np.max(np.abs(off)) <= 1e-12 * diag.mean()
+    # fp32-stored W keeps orthogonality to fp32 rounding
+    W32 = W.astype(np.float32).astype(np.float64)
+    for b0 in range(0, m, d):
+        Wb = W32[b0:b0 + d]
+        G = Wb @ Wb.T
+        off = G - np.diag(np.diag(G))
+        assert np.max(np.abs(off)) <= 1e-6 * np.diag(G).mean()
+
+
+def test_P1_blocks_are_not_orthogonal_to_each_other():
+    # independent blocks: cross-block products are O(|w|^2 / sqrt(d)), not zero
+    W = oracle.draw_w(3, 128, 64)
+    cross = W[:64] @ W[64:].T
+    assert np.max(np.abs(cross)) > 1.0
+
+
+@pytest.mark.parametrize("d", [16, 64])
+def test_P2_row_norms_follow_chi_d(d):
+    W = oracle.draw_w(2024 + d, 256 * d if d == 16 else 64 * d, d)
+    s = np.linalg.norm(W, axis=1)
+    n = s.size
+    assert abs(np.mean(s ** 2) - d) < 5 * math.sqrt(2 * d / n)
+    assert scipy.stats.kstest(s, scipy.stats.chi(d).cdf).pvalue > 1e-3
+    # norms are independent of the direction: the norm is uncorrelated with
+    # the first coordinate of the unit direction
+    u = W / s[:, None]
+    assert abs(np.corrcoef(s, u[:, 0])[0, 1]) < 5 / math.sqrt(n)
+
+
+def test_P3_rows_are_marginally_standard_normal():
+    d = 16
+    W = oracle.draw_w(99, 16 * 4000, d)
+    n = W.shape[0]
+    mean = W.mean(axis=0)
+    assert np.max(np.abs(mean)) < 5 / math.sqrt(n)
+    C = np.cov(W.T)
+    assert np.max(np.abs(np.diag(C) - 1)) < 5 * math.sqrt(2.0 / n)
+    off = C - np.diag(np.diag(C))
+    assert np.max(np.abs(off)) < 5 / math.sqrt(n)
+    # each coordinate is N(0,1)
+    assert scipy.stats.kstest(W[:, 3], "norm").pvalue > 1e-3
+
+
+def test_draw_w_partial_last_block():
+    # m not a multiple of d: the last block takes its first (m mod d) rows
+    Wfull = oracle.draw_w(11, 32, 16)
+    W = oracle.draw_w(11, 24, 16)
+    np.testing.assert_array_equal(W[:16], Wfull[:16])
+    Wb = W[16:]
+    G = Wb @ Wb.T
+    assert np.max(np.abs(G - np.diag(np.diag(G)))) <= 1e-12 * np.diag(G).mean()
+
+
+# ---------------------------------------------------------------------------
+# P4, P5: closed forms of the feature map that hold for every W.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,d", [(16, 16), (256, 64), (37, 8)])
+def test_P4_phi_x_dot_phi_minus_x(m, d):
+    rng = _rng(m * d)
+    W = rng.standard_normal((m, d)) * 1.3
+    X = rng.standard_normal((50, d)) * 0.6
+    lhs = np.sum(oracle.phi(X, W) * oracle.phi(-X, W), axis=1)
+    rhs = np.exp(-np.sum(X * X, axis=1))
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-13, atol=0)
+
+
+def test_P4_phi_scales_with_one_over_sqrt_m():
+    # duplicating every row of W doubles m and leaves phi^T phi unchanged
+    rng = _rng(5)
+    W = rng.standard_normal((16, 8))
+    X = rng.standard_normal((4, 8)) * 0.5
+    Y = rng.standard_normal((4, 8)) * 0.5
+    a = oracle.phi(X, W) @ oracle.phi(Y, W).T
+    W2 = np.concatenate([W, W])
+    b = oracle.phi(X, W2) @ oracle.phi(Y, W2).T
+    np.testing.assert_allclose(a, b, rtol=1e-14)
+
+
+@pytest.mark.parametrize("m", [1, 16, 256])
+def test_P5_phi_of_zero(m):
+    W = _rng(m).standard_normal((m, 8))
+    np.testing.assert_allclose(oracle.phi(np.zeros((1, 8)), W), 1 / math.sqrt(m), rtol=1e-15)
+
+
+def test_phi_is_positive_and_matches_single_feature_closed_form():
+    # one feature, one coordinate: phi = exp(w x - x^2/2)
+    W = np.array([[1.5]])
+    x = np.array([[0.4]])
+    np.testing.assert_allclose(oracle.phi(x, W), [[math.exp(1.5 * 0.4 - 0.08)]], rtol=1e-15)
+    X = _rng(1).standard_normal((100, 16)) * 3
+    assert np.all(oracle.phi(X, _rng(2).standard_normal((64, 16))) > 0)
+
+
+# ---------------------------------------------------------------------------
+# P6, P7: unbiasedness and lower variance ("Rethinking Attention with
+# Performers", abstract; summary page "Key contributions").
+# ---------------------------------------------------------------------------
+def _pair(norm2, seed, d=16):
+    rng = _rng(seed)
+    x = rng.standard_normal(d)
+    y = rng.standard_normal(d)
+    s = x + y
+    f = math.sqrt(norm2) / np.linalg.norm(s)
+    return x * f, y * f
+
+
+def _block_estimates(W, x, y, d):
+    # each d-row block is one independent estimator with m = d features
+    nb = W.shape[0] // d
+    px = oracle.phi(x[None, :], W)[0].reshape(nb, d) * math.sqrt(W.shape[0] / d)
+    py = oracle.phi(y[None, :], W)[0].reshape(nb, d) * math.sqrt(W.shape[0] / d)
+    return np.sum(px * py, axis=1)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("norm2", [0.25, 1.0])
+def test_P6_unbiased_softmax_kernel(norm2):
+    d, N = 16, 20_000
+    x, y = _pair(norm2, 31 + int(norm2 * 4))
+    W = oracle.draw_w(4242 + int(norm2 * 100), d * N, d)
+    est = _block_estimates(W, x, y, d)
+    target = math.exp(x @ y)
+    # closed-form iid variance from the Gaussian moment generating function
+    var = (math.exp(np.sum((x + y) ** 2)) - 1) * math.exp(2 * x @ y) / d
+    z = (est.mean() - target) / math.sqrt(var / N)
+    assert abs(z) < 4, z
+
+
+@pytest.mark.slow
+def test_P6_biased_if_norm_term_dropped():
+    # sanity of the test's power: without the -|x|^2/2 term the mean is off by
+    # exp((|x|^2+|y|^2)/2), far outside 4 sigma
+    d, N = 16, 5000
+    x, y = _pair(1.0, 7)
+    W = oracle.draw_w(555, d * N, d)
+    est = _block_estimates(W, x, y, d) * math.exp(0.5 * (x @ x + y @ y))
+    var = (math.exp(np.sum((x + y) ** 2)) - 1) * math.exp(2 * x @ y) / d
+    z = (est.mean() - math.exp(x @ y)) / math.sqrt(var / N)
+    assert abs(z) > 10
+
+
+@pytest.mark.slow
+def test_P7_orthogonal_features_have_lower_variance():
+    d, N = 16, 20_000
+    x, y = _pair(2.0, 17)
+    est_orf = _block_estimates(oracle.draw_w(8080, d * N, d), x, y, d)
+    est_iid = _block_estimates(oracle.draw_w_iid(8081, d * N, d), x, y, d)
+    ratio = est_orf.var() / est_iid.var()
+    assert ratio < 0.9, ratio
+
+
+# ---------------------------------------------------------------------------
+# P8-P11: the FA-part equation (FAVOR+ method page).
+# ---------------------------------------------------------------------------
+def _inputs(B, H, L, d, m, seed, scale=None):
+    rng = _rng(seed)
+    scale = d ** -0.25 if scale is None else scale
+    Q = rng.standard_normal((B, H, L, d)) * scale
+    K = rng.standard_normal((B, H, L, d)) * scale
+    V = rng.standard_normal((B, H, L, d))
+    W = oracle.draw_w(seed + 1, m, d)
+    return Q, K, V, W
+
+
+def test_P8_ones_in_ones_out():
+    Q, K, V, W = _inputs(2, 2, 64, 16, 32, 1)
+    ones = np.ones_like(V)
+    np.testing.assert_allclose(oracle.bidir(Q, K, ones, W), 1.0, atol=1e-14)
+    np.testing.assert_allclose(oracle.causal(Q, K, ones, W), 1.0, atol=1e-14)
+
+
+def test_P9_rebracketing_equals_quadratic_form():
+    Q, K, V, W = _inputs(2, 3, 96, 16, 48, 2)
+    np.testing.assert_allclose(oracle.bidir(Q, K, V, W), oracle.brute(Q, K, V, W, False),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_P10_single_feature_closed_form():
+    # m = 1: q' cancels, every output row is the k'-weighted mean of V
+    rng = _rng(10)
+    L, d = 40, 8
+    Q = rng.standard_normal((L, d)) * 0.5
+    K = rng.standard_normal((L, d)) * 0.5
+    V = rng.standard_normal((L, d))
+    w = rng.standard_normal(d)
+    kp = np.exp(K @ w - 0.5 * np.sum(K * K, axis=1))
+    expect = (kp @ V) / kp.sum()
+    out = oracle.bidir(Q, K, V, w[None, :])
+    np.testing.assert_allclose(out, np.broadcast_to(expect, out.shape), rtol=1e-12)
+    # causal with m = 1: row i is the weighted mean over the first i+1 tokens
+    outc = oracle.causal(Q, K, V, w[None, :])
+    for i in (0, 5, L - 1):
+        e = (kp[:i + 1] @ V[:i + 1]) / kp[:i + 1].sum()
+        np.testing.assert_allclose(outc[i], e, rtol=1e-12)
+
+
+def test_P11_permutation_symmetry():
+    Q, K, V, W = _inputs(1, 2, 50, 16, 32, 11)
+    out = oracle.bidir(Q, K, V, W)
+    p = _rng(3).permutation(50)
+    # joint permutation of keys and values leaves the output unchanged
+    np.testing.assert_allclose(oracle.bidir(Q, K[..., p, :], V[..., p, :], W), out, rtol=1e-12)
+    # permuting queries permutes the output rows
+    np.testing.assert_allclose(oracle.bidir(Q[..., p, :], K, V, W), out[..., p, :], rtol=1e-12)
+
+
+def test_bidir_is_a_convex_combination_of_values():
+    Q, K, V, W = _inputs(1, 1, 80, 16, 16, 12)
+    out = oracle.bidir(Q, K, V, W)
+    assert np.all(out <= V.max(axis=-2, keepdims=True) + 1e-12)
+    assert np.all(out >= V.min(axis=-2, keepdims=True) - 1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P12-P14: the masked (causal) form (thesis record abstract: masked
+# self-attention; diagonal included).
+# ---------------------------------------------------------------------------
+def test_P12_causal_equals_masked_brute_force_L128():
+    Q, K, V, W = _inputs(8, 8, 128, 64, 256, 12)
+    np.testing.assert_allclose(oracle.causal(Q, K, V, W), oracle.brute(Q, K, V, W, True),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_P13_causal_first_and_last_rows():
+    Q, K, V, W = _inputs(2, 2, 70, 16, 32, 13)
+    outc = oracle.causal(Q, K, V, W)
+    np.testing.assert_allclose(outc[..., 0, :], V[..., 0, :], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(outc[..., -1, :], oracle.bidir(Q, K, V, W)[..., -1, :],
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_P14_causal_prefix_property():
+    Q, K, V, W = _inputs(1, 2, 60, 16, 32, 14)
+    out = oracle.causal(Q, K, V, W)
+    i = 23
+    rng = _rng(99)
+    Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+    Q2[..., i + 1:, :] += rng.standard_normal(Q2[..., i + 1:, :].shape)
+    K2[..., i + 1:, :] += rng.standard_normal(K2[..., i + 1:, :].shape)
+    V2[..., i + 1:, :] += rng.standard_normal(V2[..., i + 1:, :].shape)
+    out2 = oracle.causal(Q2, K2, V2, W)
+    np.testing.assert_array_equal(out2[..., :i + 1, :], out[..., :i + 1, :])
+    assert np.max(np.abs(out2[..., i + 1:, :] - out[..., i + 1:, :])) > 1e-3
+
+
+def test_causal_mask_includes_diagonal():
+    # two tokens: row 1 mixes v0 and v1 with weights q1'k0', q1'k1'
+    Q, K, V, W = _inputs(1, 1, 2, 16, 16, 15)
+    qp = oracle.phi(Q[0, 0], W)
+    kp = oracle.phi(K[0, 0], W)
+    a0, a1 = qp[1] @ kp[0], qp[1] @ kp[1]
+    expect = (a0 * V[0, 0, 0] + a1 * V[0, 0, 1]) / (a0 + a1)
+    np.testing.assert_allclose(oracle.causal(Q, K, V, W)[0, 0, 1], expect, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# P15: convergence toward exact softmax attention as m grows (abstract:
+# the features estimate softmax attention).  The exact side is pinned to a
+# library routine first.
+# ---------------------------------------------------------------------------
+def test_softmax_oracle_matches_library_softmax():
+    rng = _rng(20)
+    Q = rng.standard_normal((2, 30, 8))
+    K = rng.standard_normal((2, 30, 8))
+    V = rng.standard_normal((2, 30, 8))
+    A = scipy.special.softmax(Q @ np.swapaxes(K, -1, -2), axis=-1)
+    np.testing.assert_allclose(oracle.softmax_attention(Q, K, V), A @ V, rtol=1e-12)
+    mask = np.tril(np.ones((30, 30)))
+    S = np.where(mask > 0, Q @ np.swapaxes(K, -1, -2), -np.inf)
+    Ac = scipy.special.softmax(S, axis=-1)
+    np.testing.assert_allclose(oracle.softmax_attention(Q, K, V, True), Ac @ V, rtol=1e-12)
+
+
+def _mean_frob(scale, ms, seeds=range(8)):
+    errs = []
+    for m in ms:
+        e = []
+        for s in seeds:
+            rng = _rng(700 + s)
+            Q = rng.standard_normal((256, 16)) * 16 ** -0.25 * scale
+            K = rng.standard_normal((256, 16)) * 16 ** -0.25 * scale
+            V = rng.standard_normal((256, 16))
+            W = oracle.draw_w(9000 + 31 * s + m, m, 16)
+            ref = oracle.softmax_attention(Q, K, V)
+            e.append(np.linalg.norm(oracle.bidir(Q, K, V, W) - ref) / np.linalg.norm(ref))
+        errs.append(np.mean(e))
+    return np.array(errs)
+
+
+@pytest.mark.slow
+def test_P15_convergence_to_softmax():
+    ms = np.array([16, 64, 256, 1024, 4096])
+    err = _mean_frob(0.5, ms)
+    slope = np.polyfit(np.log(ms), np.log(err), 1)[0]
+    assert -0.6 <= slope <= -0.3, (slope, err)
+    assert err[-1] < 0.06, err
+    assert np.all(np.diff(err) < 0), err
+
+
+@pytest.mark.slow
+def test_P15_convergence_at_full_input_scale():
+    err = _mean_frob(1.0, [16, 65536], seeds=range(4))
+    assert err[1] < 0.5 * err[0], err
+
+
+# ---------------------------------------------------------------------------
+# P16: shift invariance, the premise of any exponent stabiliser.
+# ---------------------------------------------------------------------------
+def test_P16_shift_invariance():
+    Q, K, V, W = _inputs(1, 2, 40, 16, 32, 16)
+    Qp, Kp = oracle.phi(Q, W), oracle.phi(K, W)
+    ref_b = oracle.attend_bidir(Qp, Kp, V)
+    ref_c = oracle.attend_causal(Qp, Kp, V)
+    rows = np.exp(_rng(1).uniform(-20, 20, size=Qp.shape[:-1]))[..., None]
+    for scale_k in (math.exp(-30.0), math.exp(25.0)):
+        np.testing.assert_allclose(oracle.attend_bidir(Qp * rows, Kp * scale_k, V), ref_b,
+                                   rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(oracle.attend_causal(Qp * rows, Kp * scale_k, V), ref_c,
+                                   rtol=1e-12, atol=1e-14)
+    # a per-feature shift on K alone is NOT output-invariant
+    feat = np.exp(_rng(2).uniform(-3, 3, size=Kp.shape[-1]))
+    assert np.max(np.abs(oracle.attend_bidir(Qp, Kp * feat, V) - ref_b)) > 1e-3
+    # ... unless the queries carry the inverse shift
+    np.testing.assert_allclose(oracle.attend_bidir(Qp / feat, Kp * feat, V), ref_b, rtol=1e-12)
+
+
+def test_row_rel_err_metric():
+    ref = np.array([[1.0, -2.0], [0.5, 0.25]])
+    got = ref + np.array([[0.02, 0.0], [0.0, 0.01]])
+    assert math.isclose(oracle.row_rel_err(got, ref), 0.02, rel_tol=1e-12)
