@@ -1,0 +1,143 @@
+/*
+ * favor.h -- C ABI of libfavor.so, the FAVOR+ attention forward pass for one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (page: "FAVOR+", Code with Papers method page, section
+ * "FAVOR+", the kernel definition and the FA-part equation; page: "Rethinking
+ * Attention with Performers", abstract):
+ *
+ *   phi(x)_r = exp(w_r . x - |x|^2 / 2) / sqrt(m),   r = 0 .. m-1,
+ *   rows of Q' and K' are phi(q_i) and phi(k_j),
+ *   bidirectional:  O = D^-1 (Q' ((K')^T V)),  D = diag(Q' ((K')^T 1_L)),
+ *   causal (masked self-attention; thesis record "Random Features for
+ *   Efficient Attention Approximation", abstract): row i uses only keys and
+ *   values j <= i (the diagonal included).
+ *
+ * The diagonal D is printed on the method page with (K')1_L; it is read as
+ * (K')^T 1_L, the only product that type-checks.  The kernel is exp(x^T y)
+ * with no internal 1/sqrt(d): callers who want softmax attention's usual
+ * scale pre-multiply Q and K by d^-1/4.  The library applies no scaling.
+ *
+ * Exponent shifts ("stabilisers") are applied inside the kernels: a
+ * per-feature reference on the key side, compensated on the query side, and a
+ * per-query-row reference.  Such shifts cancel exactly in D^-1, so the result
+ * is the formula above up to floating-point rounding.
+ *
+ * Conventions shared by every entry point below
+ * ---------------------------------------------
+ * Layout      Q, K, V and O are contiguous [B, H, L, d] (d at stride 1),
+ *             16-byte aligned, in device memory.  O has the input dtype.
+ *             W is fp32 [m, d] row-major, 16-byte aligned, in device memory.
+ * dtype       FAVOR_F32 (fp32 inputs, fp32 arithmetic) or FAVOR_BF16 (bf16
+ *             inputs and output, fp32 accumulation).
+ * Shapes      B, H, L >= 1; d in {16, 32, 64, 128}; m a multiple of 16 with
+ *             16 <= m <= 1024; B*H*L*d < 2^31.
+ * Ownership   The caller owns every buffer, the workspace included.  The
+ *             library allocates no device memory and keeps no pointer after
+ *             a call returns.
+ * Execution   Work is enqueued on the HIP stream `stream` (a hipStream_t;
+ *             NULL is the default stream) and the call returns without
+ *             waiting.  Inputs must stay valid until the stream reaches it.
+ * Errors      Every argument is validated on the host before anything is
+ *             enqueued; on error nothing is enqueued and a negative
+ *             favor_status is returned.  A failed HIP launch returns
+ *             FAVOR_ERR_HIP and records the HIP error code for
+ *             favor_last_hip_error() (per thread).  NaN and Inf inputs are not
+ *             checked; they propagate under IEEE rules.
+ * Threads     Re-entrant; no global mutable state except the per-thread last
+ *             HIP error.  Calls that share a workspace must be ordered on one
+ *             stream.
+ */
+#ifndef FAVOR_H
+#define FAVOR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum favor_dtype {
+  FAVOR_F32 = 0,
+  FAVOR_BF16 = 1
+};
+
+enum favor_status {
+  FAVOR_OK = 0,
+  FAVOR_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  FAVOR_ERR_SHAPE = -2,       /* B, H or L < 1, or the tensor is too large      */
+  FAVOR_ERR_UNSUPPORTED = -3, /* d, m or dtype outside the supported set        */
+  FAVOR_ERR_ALIGN = -4,       /* a tensor base is not 16-byte aligned, or the
+                                 workspace base is not 256-byte aligned         */
+  FAVOR_ERR_WORKSPACE = -5,   /* workspace_bytes below favor_workspace_bytes()  */
+  FAVOR_ERR_HIP = -6          /* a HIP runtime call failed                      */
+};
+
+/*
+ * Workspace size, in bytes, that favor_fwd_bidir (causal = 0) or
+ * favor_fwd_causal (causal = 1) needs for this shape; written to *bytes.
+ * The workspace holds the key-side state [(K')^T V | (K')^T 1_L] (m x (d+1)
+ * fp32 per head, per sequence split or segment) and its per-feature exponent
+ * references.  Returns FAVOR_OK or a validation error (bytes untouched).
+ * Pure host function: no HIP call.
+ */
+int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
+                          int32_t dtype, int32_t causal, size_t* bytes);
+
+/*
+ * Bidirectional FAVOR+ forward (FA-part equation of the method page):
+ * O = D^-1 (Q' ((K')^T V)).  Q, K, V: [B,H,L,d] inputs; W: [m,d] fp32
+ * projection; O: [B,H,L,d] output (may not alias Q, K, V); workspace of at
+ * least favor_workspace_bytes(..., causal=0) bytes, 256-byte aligned.
+ */
+int favor_fwd_bidir(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                    const void* Q, const void* K, const void* V, const float* W,
+                    void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Causal (masked) FAVOR+ forward in prefix-sum form:
+ * O_i = q'_i S_i / q'_i z_i with S_i = sum_{j<=i} k'_j v_j^T and
+ * z_i = sum_{j<=i} k'_j.  Arguments as favor_fwd_bidir; workspace of at least
+ * favor_workspace_bytes(..., causal=1) bytes.
+ */
+int favor_fwd_causal(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                     const void* Q, const void* K, const void* V, const float* W,
+                     void* O, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The feature map alone, for testing the projection and exponent arithmetic:
+ * Xp[b,h,l,r] = exp(w_r . x_{b,h,l} - |x_{b,h,l}|^2 / 2) / sqrt(m), fp32
+ * [B,H,L,m] in device memory, with no exponent shift (the caller keeps the
+ * exponents in fp32 range).  X: [B,H,L,d] in `dtype`.  Shapes and alignment
+ * as above.
+ */
+int favor_feature_map(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                      const void* X, const float* W, float* Xp, void* stream);
+
+/*
+ * Draw the projection W [m, d] (fp32, row-major, host memory) from `seed`:
+ * positive orthogonal random features (summary page "Key contributions";
+ * limitation "m <= d" read as orthogonality within blocks of at most d
+ * rows).  Block b (rows b*d ..) is the Gram-Schmidt orthonormalisation
+ * (computed twice, fp64) of the columns of a d x d standard-normal matrix;
+ * each row is then scaled by the norm of an independent d-dimensional
+ * standard-normal vector (a chi(d) draw).  Normals come from a counter-based
+ * SplitMix64 stream (Steele, Lea & Flood, OOPSLA 2014) through the Box-Muller
+ * transform.  1 <= d <= 1024 and 1 <= m; W_host must hold m*d floats.
+ * Pure host function: no HIP call.  Returns FAVOR_OK, FAVOR_ERR_NULL or
+ * FAVOR_ERR_SHAPE.
+ */
+int favor_draw_projection(uint64_t seed, int32_t m, int32_t d, float* W_host);
+
+/* Static English text for a favor_status value (never NULL). */
+const char* favor_status_string(int status);
+
+/* The hipError_t of this thread's last failed HIP call (0 if none). */
+int favor_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAVOR_H */

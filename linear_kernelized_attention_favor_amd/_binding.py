@@ -1,0 +1,146 @@
+"""ctypes binding of libfavor.so (include/favor.h), argument marshalling only.
+
+Every step of the forward pass runs in the HIP library; this module turns
+torch tensors into pointers, sizes and the current HIP stream, allocates the
+workspace through torch's caching allocator when the caller passes none, and
+maps status codes to exceptions.  There is no CPU fallback: if the library is
+missing or cannot be loaded, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
+           "feature_map", "draw_projection", "status_string", "F32", "BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfavor.so")
+
+F32, BF16 = 0, 1
+_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class FavorError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.favor_status_string(status).decode()
+        if status == -6:
+            msg += f" (hipError {lib.favor_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [status {status}]")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run "
+                          "python -m linear_kernelized_attention_favor_amd.build_lib")
+    L = ctypes.CDLL(LIB_PATH)
+    i32, sz, vp, fp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
+    L.favor_workspace_bytes.argtypes = [i32] * 7 + [ctypes.POINTER(sz)]
+    L.favor_workspace_bytes.restype = ctypes.c_int
+    for name in ("favor_fwd_bidir", "favor_fwd_causal"):
+        f = getattr(L, name)
+        f.argtypes = [i32] * 6 + [vp, vp, vp, fp, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+    L.favor_feature_map.argtypes = [i32] * 6 + [vp, fp, vp, vp]
+    L.favor_feature_map.restype = ctypes.c_int
+    L.favor_draw_projection.argtypes = [ctypes.c_uint64, i32, i32, ctypes.c_void_p]
+    L.favor_draw_projection.restype = ctypes.c_int
+    L.favor_status_string.argtypes = [ctypes.c_int]
+    L.favor_status_string.restype = ctypes.c_char_p
+    L.favor_last_hip_error.argtypes = []
+    L.favor_last_hip_error.restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.favor_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise FavorError(status, where)
+
+
+def workspace_bytes(B, H, L, d, m, dtype=BF16, causal=False) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.favor_workspace_bytes(B, H, L, d, m, dtype, int(bool(causal)), ctypes.byref(out)),
+           "favor_workspace_bytes")
+    return out.value
+
+
+def _shape_of(q, k, v, W):
+    if q.dim() != 4:
+        raise ValueError("Q, K, V must be [B, H, L, d]")
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("Q, K, V must share shape, dtype and device")
+    for t in (q, k, v, W):
+        if not t.is_cuda:
+            raise ValueError("tensors must be in GPU memory")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if W.dtype != torch.float32 or W.dim() != 2 or W.shape[1] != q.shape[3]:
+        raise ValueError("W must be fp32 [m, d]")
+    if q.dtype not in _DTYPES:
+        raise ValueError("inputs must be float32 or bfloat16")
+    B, H, L, d = q.shape
+    return B, H, L, d, W.shape[0], _DTYPES[q.dtype]
+
+
+def _stream(q, stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(q.device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _forward(name, causal, q, k, v, W, out, workspace, stream):
+    B, H, L, d, m, dt = _shape_of(q, k, v, W)
+    need = workspace_bytes(B, H, L, d, m, dt, causal)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like Q")
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = getattr(lib, name)(B, H, L, d, m, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            W.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(q, stream))
+    _check(st, name)
+    return out
+
+
+def fwd_bidir(q, k, v, W, out=None, workspace=None, stream=None):
+    """Bidirectional FAVOR+ forward, favor_fwd_bidir (enqueued on the current stream)."""
+    return _forward("favor_fwd_bidir", False, q, k, v, W, out, workspace, stream)
+
+
+def fwd_causal(q, k, v, W, out=None, workspace=None, stream=None):
+    """Causal FAVOR+ forward in prefix-sum form, favor_fwd_causal."""
+    return _forward("favor_fwd_causal", True, q, k, v, W, out, workspace, stream)
+
+
+def feature_map(x, W, out=None, stream=None):
+    """phi(x) = exp(W x - |x|^2/2)/sqrt(m) as fp32 [B, H, L, m], favor_feature_map."""
+    B, H, L, d, m, dt = _shape_of(x, x, x, W)
+    if out is None:
+        out = torch.empty((B, H, L, m), dtype=torch.float32, device=x.device)
+    st = lib.favor_feature_map(B, H, L, d, m, dt, x.data_ptr(), W.data_ptr(), out.data_ptr(),
+                               _stream(x, stream))
+    _check(st, "favor_feature_map")
+    return out
+
+
+def draw_projection(seed: int, m: int, d: int) -> np.ndarray:
+    """Host draw of the orthogonal projection W [m, d] (fp32), favor_draw_projection."""
+    W = np.empty((m, d), dtype=np.float32)
+    _check(lib.favor_draw_projection(ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), m, d,
+                                     W.ctypes.data_as(ctypes.c_void_p)), "favor_draw_projection")
+    return W

@@ -1,0 +1,138 @@
+// C-ABI layer of libfavor.so: argument validation (pure host code, before any
+// HIP call), workspace planning, path selection and error mapping.
+#include <cstdint>
+#include <cstring>
+
+#include <hip/hip_runtime.h>
+
+#include "favor.h"
+#include "favor_internal.h"
+
+namespace favor {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool is_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape checks shared by every entry point.
+int check_shape(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype) {
+  if (B < 1 || H < 1 || L < 1) return FAVOR_ERR_SHAPE;
+  if (!(d == 16 || d == 32 || d == 64 || d == 128)) return FAVOR_ERR_UNSUPPORTED;
+  if (m < 16 || m > 1024 || (m % 16) != 0) return FAVOR_ERR_UNSUPPORTED;
+  if (dtype != FAVOR_F32 && dtype != FAVOR_BF16) return FAVOR_ERR_UNSUPPORTED;
+  const int64_t n = static_cast<int64_t>(B) * H * L * d;
+  if (n >= (static_cast<int64_t>(1) << 31)) return FAVOR_ERR_SHAPE;
+  const int64_t nf = static_cast<int64_t>(B) * H * L * m;  // feature-map output size
+  if (nf >= (static_cast<int64_t>(1) << 40)) return FAVOR_ERR_SHAPE;
+  return FAVOR_OK;
+}
+
+int fail_hip(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return FAVOR_ERR_HIP;
+}
+
+int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
+            const void* Q, const void* K, const void* V, const float* W, void* O, void* ws,
+            size_t ws_bytes, void* stream) {
+  int st = check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  if (!Q || !K || !V || !W || !O || !ws) return FAVOR_ERR_NULL;
+  if (!is_aligned(Q, 16) || !is_aligned(K, 16) || !is_aligned(V, 16) || !is_aligned(W, 16) ||
+      !is_aligned(O, 16) || !is_aligned(ws, 256))
+    return FAVOR_ERR_ALIGN;
+  Plan p;
+  make_plan(B, H, L, d, m, dtype, causal, &p);
+  if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
+  hipError_t e = generic_forward(p, Q, K, V, W, O, ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e);
+  return FAVOR_OK;
+}
+
+}  // namespace
+
+void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+               int32_t causal, Plan* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
+  p->BH = B * H;
+  p->path = kPathGeneric;
+  // Sequence splits (bidirectional) and segments (causal); a multiple of the
+  // 8-token tile of the generic kernels.
+  p->seg = causal ? 256 : 512;
+  p->nseg = (L + p->seg - 1) / p->seg;
+  const size_t ncol = static_cast<size_t>(d) + 1;
+  const size_t BH = static_cast<size_t>(p->BH);
+  size_t off = 0;
+  p->off_T = off;    off = align256(off + BH * p->nseg * m * ncol * sizeof(float));
+  p->off_cseg = off; off = align256(off + BH * p->nseg * m * sizeof(float));
+  p->off_cP = off;   off = align256(off + (causal ? BH * p->nseg * m * sizeof(float) : 0));
+  p->off_KV = off;   off = align256(off + (causal ? 0 : BH * m * ncol * sizeof(float)));
+  p->off_cfin = off; off = align256(off + (causal ? 0 : BH * m * sizeof(float)));
+  p->bytes = off;
+}
+
+}  // namespace favor
+
+extern "C" {
+
+int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                          int32_t causal, size_t* bytes) {
+  const int st = favor::check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  if (!bytes) return FAVOR_ERR_NULL;
+  favor::Plan p;
+  favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p);
+  *bytes = p.bytes;
+  return FAVOR_OK;
+}
+
+int favor_fwd_bidir(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                    const void* Q, const void* K, const void* V, const float* W, void* O,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return favor::forward(B, H, L, d, m, dtype, 0, Q, K, V, W, O, workspace, workspace_bytes,
+                        stream);
+}
+
+int favor_fwd_causal(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                     const void* Q, const void* K, const void* V, const float* W, void* O,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return favor::forward(B, H, L, d, m, dtype, 1, Q, K, V, W, O, workspace, workspace_bytes,
+                        stream);
+}
+
+int favor_feature_map(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                      const void* X, const float* W, float* Xp, void* stream) {
+  const int st = favor::check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  if (!X || !W || !Xp) return FAVOR_ERR_NULL;
+  if (!favor::is_aligned(X, 16) || !favor::is_aligned(W, 16) || !favor::is_aligned(Xp, 16))
+    return FAVOR_ERR_ALIGN;
+  const hipError_t e = favor::generic_feature_map(B * H, L, d, m, dtype, X, W, Xp,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return favor::fail_hip(e);
+  return FAVOR_OK;
+}
+
+const char* favor_status_string(int status) {
+  switch (status) {
+    case FAVOR_OK: return "ok";
+    case FAVOR_ERR_NULL: return "a required pointer is NULL";
+    case FAVOR_ERR_SHAPE: return "invalid shape (B, H or L below 1, or tensor too large)";
+    case FAVOR_ERR_UNSUPPORTED:
+      return "unsupported configuration (d must be 16, 32, 64 or 128; m a multiple of 16 in "
+             "[16, 1024]; dtype FAVOR_F32 or FAVOR_BF16)";
+    case FAVOR_ERR_ALIGN:
+      return "misaligned pointer (tensors need 16-byte, the workspace 256-byte alignment)";
+    case FAVOR_ERR_WORKSPACE: return "workspace smaller than favor_workspace_bytes()";
+    case FAVOR_ERR_HIP: return "a HIP runtime call failed (see favor_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int favor_last_hip_error(void) { return favor::g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Internal declarations shared by the C-ABI layer and the kernel files of
+// libfavor.so.  Not installed; the public interface is include/favor.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime.h>
+
+namespace favor {
+
+// ---------------------------------------------------------------------------
+// Execution plan: which kernel path runs a shape, and the workspace layout.
+// All offsets are in bytes from the workspace base and 256-byte aligned.
+// ---------------------------------------------------------------------------
+enum Path : int32_t {
+  kPathGeneric = 0,  // fp32 FMA kernels, any supported shape and dtype
+  kPathMfma = 1,     // bf16 MFMA kernels (d in {64, 128}, m % 64 == 0)
+};
+
+struct Plan {
+  int32_t B, H, L, d, m, dtype, causal;
+  int32_t BH;
+  int32_t path;
+  int32_t seg;    // tokens per sequence split (bidirectional) or segment (causal)
+  int32_t nseg;   // number of splits / segments per head
+  // Generic-path workspace (all fp32):
+  //   T    [BH][nseg][m][d+1]  per-segment key state, then (causal) its
+  //                            exclusive prefix over earlier segments
+  //   cseg [BH][nseg][m]       per-feature key exponent reference of T
+  //   cP   [BH][nseg][m]       reference of the exclusive prefix (causal)
+  //   KV   [BH][m][d+1]        final key state (bidirectional)
+  //   cfin [BH][m]             its per-feature reference
+  size_t off_T, off_cseg, off_cP, off_KV, off_cfin;
+  size_t bytes;
+};
+
+// Fills *p for a validated shape (the C-ABI layer validates first).
+void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+               int32_t causal, Plan* p);
+
+// Generic path: enqueue the whole forward pass on `stream`.
+hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const void* V,
+                           const float* W, void* O, void* ws, hipStream_t stream);
+
+// Feature map test entry (generic fp32 arithmetic).
+hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                               const void* X, const float* W, float* Xp, hipStream_t stream);
+
+}  // namespace favor

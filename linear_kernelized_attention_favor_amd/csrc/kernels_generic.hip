@@ -1,0 +1,451 @@
+// Generic FAVOR+ kernels: plain fp32 FMA arithmetic for every supported shape
+// and both input dtypes.  They are the path for fp32 inputs and for shapes the
+// MFMA path does not cover, and they are organised the same way:
+//
+//   1. g_state    per (head, segment, 32-feature block): the key state of the
+//                 segment, T = sum_j exp(e_jr - c_r) [v_j | 1], where
+//                 e_jr = w_r . k_j - |k_j|^2 / 2 and c_r = max_j e_jr over the
+//                 segment (a per-feature exponent reference);
+//   2. g_combine  per (head, state entry): bidirectional -- the total over
+//                 segments, rescaled to the largest reference, in segment
+//                 order; causal -- the exclusive prefix over earlier segments;
+//   3. g_apply    per (head, 8-query tile): query features with the key
+//                 references added, a per-row reference (row max), the carry
+//                 term q~ . [KV | z], the masked in-segment term (causal), and
+//                 the division by the last column.
+//
+// Correctness of the shifts: with key references c_r and row references M_i,
+//   sum_r e^{s_ir + c_r - M_i} sum_j e^{e_jr - c_r} [v_j | 1]
+//     = e^{-M_i} sum_r e^{s_ir} sum_j e^{e_jr} [v_j | 1],
+// and e^{-M_i}, e^{-|q_i|^2/2} and 1/sqrt(m) cancel in the final division, so
+// the result is the FA-part equation of the "FAVOR+" method page (bidirectional)
+// or its masked prefix-sum form.  Reductions run in a fixed order, so results
+// are bitwise reproducible.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "favor.h"
+#include "favor_internal.h"
+
+namespace favor {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kFB = 32;   // features per g_state block
+constexpr int kTT = 8;    // tokens per tile
+constexpr int kMaxD = 128;
+constexpr int kMaxM = 1024;
+
+__device__ inline float load_x(const float* p, size_t i) { return p[i]; }
+__device__ inline float load_x(const uint16_t* p, size_t i) {
+  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ inline uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ inline void store_x(float* p, size_t i, float v) { p[i] = v; }
+__device__ inline void store_x(uint16_t* p, size_t i, float v) { p[i] = to_bf16(v); }
+
+// Loads kTT rows [j0, j0+kTT) of a [L, d] matrix into LDS (zero past L).
+template <typename T>
+__device__ inline void load_rows(const T* __restrict__ X, size_t base, int j0, int jend, int d,
+                                 float (*dst)[kMaxD + 1]) {
+  for (int i = threadIdx.x; i < kTT * d; i += kThreads) {
+    const int j = i / d, a = i - j * d;
+    dst[j][a] = (j0 + j < jend) ? load_x(X, base + static_cast<size_t>(j0 + j) * d + a) : 0.f;
+  }
+}
+
+// Half squared norms of the kTT rows in `rows` (first kTT threads).
+__device__ inline void half_norms(const float (*rows)[kMaxD + 1], int d, float* nrm) {
+  if (threadIdx.x < kTT) {
+    float acc = 0.f;
+    for (int a = 0; a < d; ++a) acc = fmaf(rows[threadIdx.x][a], rows[threadIdx.x][a], acc);
+    nrm[threadIdx.x] = 0.5f * acc;
+  }
+}
+
+// w . x over d coordinates, w from global memory (row of W), x from LDS.
+__device__ inline float dot_w(const float* __restrict__ w, const float* x, int d) {
+  float acc = 0.f;
+  for (int a = 0; a < d; a += 4) {
+    const float4 wv = *reinterpret_cast<const float4*>(w + a);
+    acc = fmaf(wv.x, x[a], acc);
+    acc = fmaf(wv.y, x[a + 1], acc);
+    acc = fmaf(wv.z, x[a + 2], acc);
+    acc = fmaf(wv.w, x[a + 3], acc);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------
+// 1. Per-segment key state.  grid (nseg, ceil(m / kFB), BH).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
+                                                    const T* __restrict__ V,
+                                                    const float* __restrict__ W,
+                                                    float* __restrict__ Tout,
+                                                    float* __restrict__ cseg, int L, int d, int m,
+                                                    int seg, int nseg) {
+  const int s = blockIdx.x, fb = blockIdx.y, bh = blockIdx.z;
+  const int t = threadIdx.x;
+  const int r = t % kFB, jj = t / kFB;  // this thread's feature and tile row
+  const int ncol = d + 1;
+  const int nfb = min(kFB, m - fb * kFB);  // features in this block (m % 16 == 0)
+  const bool rv = r < nfb;
+  __shared__ float Kt[kTT][kMaxD + 1];
+  __shared__ float Vt[kTT][kMaxD + 1];
+  __shared__ float nrm[kTT];
+  __shared__ float E[kTT][kFB];
+  __shared__ float cref[kFB];
+
+  const size_t base = static_cast<size_t>(bh) * L * d;
+  const int j0 = s * seg, j1 = min(L, j0 + seg);
+  const float* wrow = W + static_cast<size_t>(fb * kFB + (rv ? r : 0)) * d;
+
+  // Pass 1: per-feature maximum exponent over the segment.
+  float mx = -INFINITY;
+  for (int jt = j0; jt < j1; jt += kTT) {
+    __syncthreads();
+    load_rows(K, base, jt, j1, d, Kt);
+    __syncthreads();
+    half_norms(Kt, d, nrm);
+    __syncthreads();
+    if (rv && jt + jj < j1) mx = fmaxf(mx, dot_w(wrow, Kt[jj], d) - nrm[jj]);
+  }
+  E[jj][r] = mx;
+  __syncthreads();
+  if (jj == 0) {
+    float c = E[0][r];
+    for (int k = 1; k < kTT; ++k) c = fmaxf(c, E[k][r]);
+    cref[r] = c;
+  }
+  __syncthreads();
+
+  // Pass 2: T[r][c] = sum_j exp(e_jr - c_r) * [v_j | 1][c].
+  constexpr int kAcc = (kFB * (kMaxD + 1) + kThreads - 1) / kThreads;
+  float acc[kAcc];
+#pragma unroll
+  for (int u = 0; u < kAcc; ++u) acc[u] = 0.f;
+  const int nent = nfb * ncol;
+  for (int jt = j0; jt < j1; jt += kTT) {
+    __syncthreads();
+    load_rows(K, base, jt, j1, d, Kt);
+    for (int i = t; i < kTT * ncol; i += kThreads) {
+      const int j = i / ncol, c = i - j * ncol;
+      float v = 0.f;
+      if (jt + j < j1) v = (c < d) ? load_x(V, base + static_cast<size_t>(jt + j) * d + c) : 1.f;
+      Vt[j][c] = v;
+    }
+    __syncthreads();
+    half_norms(Kt, d, nrm);
+    __syncthreads();
+    E[jj][r] = (rv && jt + jj < j1) ? expf(dot_w(wrow, Kt[jj], d) - nrm[jj] - cref[r]) : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kAcc; ++u) {
+      const int e = t + u * kThreads;
+      if (e < nent) {
+        const int rr = e / ncol, c = e - rr * ncol;
+        float a = acc[u];
+        for (int j = 0; j < kTT; ++j) a = fmaf(E[j][rr], Vt[j][c], a);
+        acc[u] = a;
+      }
+    }
+  }
+  const size_t sb = static_cast<size_t>(bh) * nseg + s;
+#pragma unroll
+  for (int u = 0; u < kAcc; ++u) {
+    const int e = t + u * kThreads;
+    if (e < nent) {
+      const int rr = e / ncol, c = e - rr * ncol;
+      Tout[(sb * m + fb * kFB + rr) * ncol + c] = acc[u];
+    }
+  }
+  if (jj == 0 && rv) cseg[sb * m + fb * kFB + r] = cref[r];
+}
+
+// ---------------------------------------------------------------------------
+// 2. Combine segment states in segment order.  grid (ceil(m*(d+1)/256), BH).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void g_combine(float* __restrict__ Tst,
+                                                      const float* __restrict__ cseg,
+                                                      float* __restrict__ cP,
+                                                      float* __restrict__ KV,
+                                                      float* __restrict__ cfin, int nseg, int m,
+                                                      int d, int causal) {
+  const int bh = blockIdx.y;
+  const int ncol = d + 1;
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= m * ncol) return;
+  const int r = e / ncol, c = e - r * ncol;
+  const size_t cb = static_cast<size_t>(bh) * nseg * m + r;            // + s*m
+  const size_t tb = static_cast<size_t>(bh) * nseg * m * ncol + e;     // + s*m*ncol
+  if (!causal) {
+    float cm = -INFINITY;
+    for (int s = 0; s < nseg; ++s) cm = fmaxf(cm, cseg[cb + static_cast<size_t>(s) * m]);
+    float acc = 0.f;
+    for (int s = 0; s < nseg; ++s)
+      acc = fmaf(Tst[tb + static_cast<size_t>(s) * m * ncol],
+                 expf(cseg[cb + static_cast<size_t>(s) * m] - cm), acc);
+    KV[(static_cast<size_t>(bh) * m + r) * ncol + c] = acc;
+    if (c == 0) cfin[static_cast<size_t>(bh) * m + r] = cm;
+  } else {
+    float rc = -INFINITY, run = 0.f;
+    for (int s = 0; s < nseg; ++s) {
+      const size_t ti = tb + static_cast<size_t>(s) * m * ncol;
+      const float ts = Tst[ti];
+      const float cs = cseg[cb + static_cast<size_t>(s) * m];
+      Tst[ti] = run;  // exclusive prefix of the segments before s
+      if (c == 0) cP[cb + static_cast<size_t>(s) * m] = rc;
+      const float nc = fmaxf(rc, cs);
+      run = run * expf(rc - nc) + ts * expf(cs - nc);
+      rc = nc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. Query side.  grid (ceil(L/kTT), BH).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void g_apply(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ W, const float* __restrict__ KVst, const float* __restrict__ cst,
+    const float* __restrict__ csg, T* __restrict__ O, int L, int d, int m, int seg, int nseg,
+    int causal) {
+  const int tile = blockIdx.x, bh = blockIdx.y;
+  const int t = threadIdx.x;
+  const int i0 = tile * kTT;
+  const int ncol = d + 1;
+  __shared__ float Qe[kTT][kMaxM];
+  __shared__ float Ke[kTT][kMaxM];
+  __shared__ float Xt[kTT][kMaxD + 1];
+  __shared__ float Vt[kTT][kMaxD + 1];
+  __shared__ float cstar[kMaxM];
+  __shared__ float cscale[kMaxM];
+  __shared__ float nrm[kTT];
+  __shared__ float Mrow[kTT];
+  __shared__ float Sij[kTT][kTT];
+  __shared__ float Num[kTT][kMaxD + 1];
+
+  const size_t base = static_cast<size_t>(bh) * L * d;
+  const int s = causal ? (i0 / seg) : 0;
+  const float* KVs;  // state rows [m][ncol]
+  if (causal) {
+    const size_t sb = static_cast<size_t>(bh) * nseg + s;
+    KVs = KVst + sb * m * ncol;
+    for (int r = t; r < m; r += kThreads) {
+      const float cp = cst[sb * m + r], cg = csg[sb * m + r];
+      const float cs = fmaxf(cp, cg);
+      cstar[r] = cs;
+      cscale[r] = expf(cp - cs);  // 0 for the first segment (cp = -inf)
+    }
+  } else {
+    KVs = KVst + static_cast<size_t>(bh) * m * ncol;
+    for (int r = t; r < m; r += kThreads) {
+      cstar[r] = cst[static_cast<size_t>(bh) * m + r];
+      cscale[r] = 1.f;
+    }
+  }
+  load_rows(Q, base, i0, L, d, Xt);
+  __syncthreads();
+
+  // Query exponents with the key references added; per-row maximum.
+  for (int r = t; r < m; r += kThreads) {
+    const float* w = W + static_cast<size_t>(r) * d;
+    float e[kTT];
+#pragma unroll
+    for (int i = 0; i < kTT; ++i) e[i] = 0.f;
+    for (int a = 0; a < d; ++a) {
+      const float wa = w[a];
+#pragma unroll
+      for (int i = 0; i < kTT; ++i) e[i] = fmaf(wa, Xt[i][a], e[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kTT; ++i) Qe[i][r] = e[i] + cstar[r];
+  }
+  __syncthreads();
+  {
+    // 32 lanes per row: lane k scans features k, k+32, ...; then a shuffle tree.
+    const int i = t / 32, k = t % 32;
+    float mx = -INFINITY;
+    for (int r = k; r < m; r += 32) mx = fmaxf(mx, Qe[i][r]);
+    for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+    if (k == 0) Mrow[i] = mx;
+  }
+  __syncthreads();
+  for (int p = t; p < kTT * m; p += kThreads) {
+    const int i = p / m, r = p - i * m;
+    Qe[i][r] = expf(Qe[i][r] - Mrow[i]);
+  }
+  __syncthreads();
+
+  // Carry / total term: num[i][c] = sum_r q~_ir * scale_r * KV[r][c].
+  constexpr int kAcc = (kTT * (kMaxD + 1) + kThreads - 1) / kThreads;
+  float acc[kAcc];
+#pragma unroll
+  for (int u = 0; u < kAcc; ++u) {
+    acc[u] = 0.f;
+    const int p = t + u * kThreads;
+    if (p < kTT * ncol) {
+      const int i = p / ncol, c = p - i * ncol;
+      float a = 0.f;
+      for (int r = 0; r < m; ++r) a = fmaf(Qe[i][r] * cscale[r], KVs[static_cast<size_t>(r) * ncol + c], a);
+      acc[u] = a;
+    }
+  }
+
+  if (causal) {
+    // Masked term over this segment's keys up to the end of the tile.
+    const int js = s * seg;
+    for (int jc = js; jc <= i0; jc += kTT) {
+      __syncthreads();
+      load_rows(K, base, jc, L, d, Xt);
+      for (int i = t; i < kTT * ncol; i += kThreads) {
+        const int j = i / ncol, c = i - j * ncol;
+        float v = 0.f;
+        if (jc + j < L) v = (c < d) ? load_x(V, base + static_cast<size_t>(jc + j) * d + c) : 1.f;
+        Vt[j][c] = v;
+      }
+      __syncthreads();
+      half_norms(Xt, d, nrm);
+      __syncthreads();
+      for (int r = t; r < m; r += kThreads) {
+        const float* w = W + static_cast<size_t>(r) * d;
+        float e[kTT];
+#pragma unroll
+        for (int j = 0; j < kTT; ++j) e[j] = 0.f;
+        for (int a = 0; a < d; ++a) {
+          const float wa = w[a];
+#pragma unroll
+          for (int j = 0; j < kTT; ++j) e[j] = fmaf(wa, Xt[j][a], e[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kTT; ++j) Ke[j][r] = expf(e[j] - nrm[j] - cstar[r]);
+      }
+      __syncthreads();
+      if (t < kTT * kTT * 4) {
+        const int pr = t / 4, part = t % 4;
+        const int i = pr / kTT, j = pr % kTT;
+        float a = 0.f;
+        for (int r = part; r < m; r += 4) a = fmaf(Qe[i][r], Ke[j][r], a);
+        a += __shfl_xor(a, 1, 4);
+        a += __shfl_xor(a, 2, 4);
+        const bool keep = (jc + j <= i0 + i) && (jc + j < L);
+        if (part == 0) Sij[i][j] = keep ? a : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kAcc; ++u) {
+        const int p = t + u * kThreads;
+        if (p < kTT * ncol) {
+          const int i = p / ncol, c = p - i * ncol;
+          float a = acc[u];
+          for (int j = 0; j < kTT; ++j) a = fmaf(Sij[i][j], Vt[j][c], a);
+          acc[u] = a;
+        }
+      }
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < kAcc; ++u) {
+    const int p = t + u * kThreads;
+    if (p < kTT * ncol) Num[p / ncol][p % ncol] = acc[u];
+  }
+  __syncthreads();
+  for (int p = t; p < kTT * d; p += kThreads) {
+    const int i = p / d, c = p - i * d;
+    if (i0 + i < L) store_x(O, base + static_cast<size_t>(i0 + i) * d + c, Num[i][c] / Num[i][d]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Feature map test kernel: Xp = exp(w . x - |x|^2/2) / sqrt(m), no shift.
+// grid (ceil(L/kTT), BH).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(kThreads) void g_feature_map(const T* __restrict__ X,
+                                                          const float* __restrict__ W,
+                                                          float* __restrict__ Xp, int L, int d,
+                                                          int m) {
+  const int tile = blockIdx.x, bh = blockIdx.y;
+  const int i0 = tile * kTT;
+  __shared__ float Xt[kTT][kMaxD + 1];
+  __shared__ float nrm[kTT];
+  const size_t base = static_cast<size_t>(bh) * L * d;
+  load_rows(X, base, i0, L, d, Xt);
+  __syncthreads();
+  half_norms(Xt, d, nrm);
+  __syncthreads();
+  const float inv_sqrt_m = 1.0f / sqrtf(static_cast<float>(m));
+  for (int r = threadIdx.x; r < m; r += kThreads) {
+    const float* w = W + static_cast<size_t>(r) * d;
+    for (int i = 0; i < kTT && i0 + i < L; ++i) {
+      const float e = dot_w(w, Xt[i], d) - nrm[i];
+      Xp[(static_cast<size_t>(bh) * L + i0 + i) * m + r] = expf(e) * inv_sqrt_m;
+    }
+  }
+}
+
+template <typename T>
+hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const float* W, T* O,
+                     char* ws, hipStream_t st) {
+  float* Tst = reinterpret_cast<float*>(ws + p.off_T);
+  float* cseg = reinterpret_cast<float*>(ws + p.off_cseg);
+  float* cP = reinterpret_cast<float*>(ws + p.off_cP);
+  float* KV = reinterpret_cast<float*>(ws + p.off_KV);
+  float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
+  g_state<T><<<dim3(p.nseg, (p.m + kFB - 1) / kFB, p.BH), kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.d,
+                                                                  p.m, p.seg, p.nseg);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nent = p.m * (p.d + 1);
+  g_combine<<<dim3((nent + kThreads - 1) / kThreads, p.BH), kThreads, 0, st>>>(
+      Tst, cseg, cP, KV, cfin, p.nseg, p.m, p.d, p.causal);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 ga((p.L + kTT - 1) / kTT, p.BH);
+  if (p.causal)
+    g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, Tst, cP, cseg, O, p.L, p.d, p.m, p.seg,
+                                        p.nseg, 1);
+  else
+    g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, KV, cfin, nullptr, O, p.L, p.d, p.m, p.seg,
+                                        p.nseg, 0);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const void* V,
+                           const float* W, void* O, void* ws, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  if (p.dtype == FAVOR_F32)
+    return forward_t<float>(p, static_cast<const float*>(Q), static_cast<const float*>(K),
+                            static_cast<const float*>(V), W, static_cast<float*>(O), w, stream);
+  return forward_t<uint16_t>(p, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                             static_cast<const uint16_t*>(V), W, static_cast<uint16_t*>(O), w,
+                             stream);
+}
+
+hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                               const void* X, const float* W, float* Xp, hipStream_t stream) {
+  const dim3 g((L + kTT - 1) / kTT, BH);
+  if (dtype == FAVOR_F32)
+    g_feature_map<float><<<g, kThreads, 0, stream>>>(static_cast<const float*>(X), W, Xp, L, d, m);
+  else
+    g_feature_map<uint16_t><<<g, kThreads, 0, stream>>>(static_cast<const uint16_t*>(X), W, Xp,
+                                                        L, d, m);
+  return hipGetLastError();
+}
+
+}  // namespace favor

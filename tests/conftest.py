@@ -9,3 +9,11 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
+
+
+def pytest_sessionstart(session):
+    # Load what is built; build only if nothing is (the library is git-ignored).
+    lib = os.path.join(ROOT, "linear_kernelized_attention_favor_amd", "libfavor.so")
+    if not os.path.exists(lib):
+        from linear_kernelized_attention_favor_amd import build_lib
+        build_lib.build()

@@ -1,0 +1,264 @@
+"""GPU parity: libfavor.so (through its C ABI) against the fp64 oracle.
+
+Metric: max over (b, h, row) of |gpu - oracle|_inf / |oracle|_inf per output
+row.  Bars: 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (bf16 output
+rounding alone is up to 2^-9 of a row's largest element).  The oracle and the
+GPU receive the same input values and the same fp32 W bytes; W comes from the
+oracle's draw, never from the library.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def fv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_kernelized_attention_favor_amd as m
+    return m
+
+
+def _w(seed, m, d):
+    return oracle.draw_w(seed, m, d).astype(np.float32)
+
+
+def _np64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def _run(fv, causal, q, k, v, W):
+    Wd = torch.from_numpy(W).cuda()
+    out = (fv.fwd_causal if causal else fv.fwd_bidir)(q.cuda(), k.cuda(), v.cuda(), Wd)
+    torch.cuda.synchronize()
+    return out
+
+
+def _ref(causal, q, k, v, W):
+    f = oracle.causal if causal else oracle.bidir
+    return f(_np64(q), _np64(k), _np64(v), W.astype(np.float64))
+
+
+def _case(B, H, L, d, m, dtype, seed, scale=None):
+    rng = np.random.default_rng(seed)
+    s = d ** -0.25 if scale is None else scale
+    q = rng.standard_normal((B, H, L, d), dtype=np.float32) * np.float32(s)
+    k = rng.standard_normal((B, H, L, d), dtype=np.float32) * np.float32(s)
+    v = rng.standard_normal((B, H, L, d), dtype=np.float32)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    return tuple(torch.from_numpy(x).to(td) for x in (q, k, v))
+
+
+# ---------------------------------------------------------------------------
+# Tiny fp32 workload: oracle, V = ones, brute force, exact-softmax trend.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_tiny_f32_workload(fv, causal):
+    w = workloads.workload("tiny_f32")
+    q, k, v = workloads.host_qkv(w)
+    W = _w(w.seed_w, w.m, w.d)
+    out = _run(fv, causal, q, k, v, W)
+    ref = _ref(causal, q, k, v, W)
+    err = oracle.row_rel_err(_np64(out), ref)
+    assert err <= TOL["f32"], err
+    brute = oracle.brute(_np64(q), _np64(k), _np64(v), W.astype(np.float64), causal)
+    assert oracle.row_rel_err(_np64(out), brute) <= TOL["f32"]
+    ones = torch.ones_like(v)
+    o1 = _run(fv, causal, q, k, ones, W)
+    assert np.max(np.abs(_np64(o1) - 1.0)) <= 1e-5
+
+
+def test_tiny_f32_approaches_softmax_like_the_oracle(fv):
+    # With many features the GPU's distance to exact softmax attention equals
+    # the oracle's (same W), at reduced input scale where the estimator
+    # converges quickly.
+    w = workloads.workload("tiny_f32")
+    q, k, v = workloads.host_qkv(w)
+    q, k = q * 0.5, k * 0.5
+    exact = oracle.softmax_attention(_np64(q), _np64(k), _np64(v))
+    errs = []
+    for m in (16, 1024):
+        W = _w(77 + m, m, w.d)
+        g = _np64(_run(fv, False, q, k, v, W))
+        o = _ref(False, q, k, v, W)
+        eg = np.linalg.norm(g - exact) / np.linalg.norm(exact)
+        eo = np.linalg.norm(o - exact) / np.linalg.norm(exact)
+        assert abs(eg - eo) <= 1e-4 * eo + 1e-6
+        errs.append(eg)
+    assert errs[1] < 0.5 * errs[0]
+
+
+# ---------------------------------------------------------------------------
+# Shape coverage, fp32 and bf16, with ragged tails.
+# ---------------------------------------------------------------------------
+SHAPES = [
+    # (B, H, L, d, m)
+    (1, 1, 1, 16, 16),
+    (1, 2, 17, 32, 48),
+    (2, 1, 255, 64, 256),
+    (1, 1, 600, 128, 1024),
+    (1, 3, 1000, 64, 128),
+    (1, 1, 4097, 16, 64),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_shapes(fv, shape, causal, dtype):
+    B, H, L, d, m = shape
+    q, k, v = _case(B, H, L, d, m, dtype, seed=sum(shape) + causal)
+    W = _w(31 * d + m, m, d)
+    out = _run(fv, causal, q, k, v, W)
+    err = oracle.row_rel_err(_np64(out), _ref(causal, q, k, v, W))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_text_shape_L128_brute_force(fv, causal):
+    # The text configuration's heads and features at L = 128, against the
+    # O(L^2) masked (or unmasked) feature attention.
+    w = workloads.workload("text_causal")
+    q, k, v = workloads.host_qkv(w, L=128)
+    W = _w(w.seed_w, w.m, w.d)
+    out = _run(fv, causal, q, k, v, W)
+    brute = oracle.brute(_np64(q), _np64(k), _np64(v), W.astype(np.float64), causal)
+    assert oracle.row_rel_err(_np64(out), brute) <= TOL["bf16"]
+    if causal:
+        # row 0 is v_0 (up to bf16 output rounding)
+        np.testing.assert_allclose(_np64(out)[..., 0, :], _np64(v)[..., 0, :], rtol=8e-3, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: the whole launch on the GPU, sampled heads on the oracle.
+# ---------------------------------------------------------------------------
+FULL = [("text_bidir", False), ("text_causal", True), ("protein_long", False),
+        ("protein_long", True), ("wide_many", False)]
+
+
+@pytest.mark.parametrize("name,causal", FULL, ids=[f"{n}-{'causal' if c else 'bidir'}" for n, c in FULL])
+def test_full_size_sampled(fv, name, causal):
+    w = workloads.workload(name)
+    torch.manual_seed(0)
+    q, k, v = workloads.device_qkv(w)
+    W = _w(w.seed_w, w.m, w.d)
+    out = (fv.fwd_causal if causal else fv.fwd_bidir)(q, k, v, torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    heads = [0, w.heads - 1]
+    qf, kf, vf, of = (x.reshape(w.heads, w.L, w.d) for x in (q, k, v, out))
+    for h in heads:
+        ref = _ref(causal, qf[h], kf[h], vf[h], W)
+        err = oracle.row_rel_err(_np64(of[h]), ref)
+        print(f"{name} causal={causal} head {h}: row-rel err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], (h, err)
+
+
+# ---------------------------------------------------------------------------
+# Feature map (projection and exponent arithmetic) and robustness.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_feature_map_closed_form_and_oracle(fv, dtype):
+    d, m = 64, 256
+    q, _, _ = _case(1, 2, 300, d, m, dtype, seed=5)
+    W = _w(9, m, d)
+    Wd = torch.from_numpy(W).cuda()
+    x = q.cuda()
+    p = fv.feature_map(x, Wd)
+    pm = fv.feature_map((-x.float()).to(x.dtype).contiguous(), Wd)
+    torch.cuda.synchronize()
+    lhs = (_np64(p) * _np64(pm)).sum(-1)
+    xx = _np64(q)
+    np.testing.assert_allclose(lhs, np.exp(-np.sum(xx * xx, -1)), rtol=2e-5)
+    np.testing.assert_allclose(_np64(p), oracle.phi(xx, W.astype(np.float64)), rtol=2e-5)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bitwise_deterministic(fv, causal):
+    q, k, v = (x.cuda() for x in _case(2, 4, 1500, 64, 256, "bf16", seed=3))
+    W = torch.from_numpy(_w(4, 256, 64)).cuda()
+    f = fv.fwd_causal if causal else fv.fwd_bidir
+    outs = [f(q, k, v, W).clone() for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_guard_bands_untouched(fv, causal):
+    B, H, L, d, m = 1, 2, 777, 64, 256
+    q, k, v = (x.cuda() for x in _case(B, H, L, d, m, "bf16", seed=8))
+    W = torch.from_numpy(_w(8, m, d)).cuda()
+    n = B * H * L * d
+    pad = 4096
+    obuf = torch.full((n + 2 * pad,), -12345, dtype=torch.int16, device="cuda")
+    out = obuf[pad:pad + n].view(torch.bfloat16).view(B, H, L, d)
+    need = fv.workspace_bytes(B, H, L, d, m, fv.BF16, causal)
+    wbuf = torch.full((need + 2 * 65536,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = wbuf[65536:65536 + need]
+    f = fv.fwd_causal if causal else fv.fwd_bidir
+    f(q, k, v, W, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:pad] == -12345) and torch.all(obuf[pad + n:] == -12345)
+    assert torch.all(wbuf[:65536] == 0xA5) and torch.all(wbuf[65536 + need:] == 0xA5)
+    ref = _ref(causal, q, k, v, W.cpu().numpy())
+    assert oracle.row_rel_err(_np64(out), ref) <= TOL["bf16"]
+
+
+def test_causal_prefix_property(fv):
+    B, H, L, d, m = 1, 2, 900, 64, 256
+    q, k, v = _case(B, H, L, d, m, "bf16", seed=12)
+    W = _w(12, m, d)
+    out = _np64(_run(fv, True, q, k, v, W))
+    i = 400
+    g = torch.Generator().manual_seed(1)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    for t in (q2, k2, v2):
+        t[..., i + 1:, :] += torch.randn(t[..., i + 1:, :].shape, generator=g).to(t.dtype)
+    out2 = _np64(_run(fv, True, q2, k2, v2, W))
+    ref = _ref(True, q, k, v, W)
+    assert oracle.row_rel_err(out2[..., :i + 1, :], ref[..., :i + 1, :]) <= TOL["bf16"]
+    assert np.max(np.abs(out2[..., i + 1:, :] - out[..., i + 1:, :])) > 1e-2
+
+
+def test_stabiliser_large_offsets(fv):
+    # Exponents far outside fp32's exp range without shifts: Q and K carry a
+    # large common offset (|x|^2/2 ~ 300); the oracle in fp64 still holds them.
+    B, H, L, d, m = 1, 2, 512, 64, 256
+    rng = np.random.default_rng(21)
+    mu = rng.standard_normal(d) * 3.0
+    q = torch.from_numpy((rng.standard_normal((B, H, L, d)) * 0.35 + mu).astype(np.float32))
+    k = torch.from_numpy((rng.standard_normal((B, H, L, d)) * 0.35 + mu).astype(np.float32))
+    v = torch.from_numpy(rng.standard_normal((B, H, L, d)).astype(np.float32))
+    W = _w(21, m, d)
+    for causal in (False, True):
+        for dt in (torch.float32, torch.bfloat16):
+            qq, kk, vv = q.to(dt), k.to(dt), v.to(dt)
+            out = _np64(_run(fv, causal, qq, kk, vv, W))
+            ref = _ref(causal, qq, kk, vv, W)
+            tol = TOL["f32"] if dt == torch.float32 else TOL["bf16"]
+            err = oracle.row_rel_err(out, ref)
+            print(f"offset case causal={causal} {dt}: {err:.3e}", flush=True)
+            assert err <= tol, (causal, dt, err)
+
+
+def test_redraw_changes_output_consistently(fv):
+    # Redrawing W (a new seed, uploaded between calls on the same buffers)
+    # gives the oracle's result for each W.
+    q, k, v = _case(1, 2, 256, 64, 256, "bf16", seed=2)
+    outs = []
+    for seed in (5002, 5003):
+        W = _w(seed, 256, 64)
+        out = _run(fv, False, q, k, v, W)
+        assert oracle.row_rel_err(_np64(out), _ref(False, q, k, v, W)) <= TOL["bf16"]
+        outs.append(_np64(out))
+    assert np.max(np.abs(outs[0] - outs[1])) > 1e-3

@@ -1,0 +1,151 @@
+"""Host-side checks of libfavor.so that need no GPU.
+
+* The library loads and exports every function include/favor.h declares.
+* Every validation error is returned before anything is enqueued (the calls
+  below never reach a HIP launch; the pointers are dummies).
+* The host projection draw (favor_draw_projection) matches the oracle's draw
+  of the same counter-based stream and has the properties the pages fix.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+import scipy.stats
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "favor.h")
+
+fv = pytest.importorskip("linear_kernelized_attention_favor_amd")
+lib = fv._binding.lib
+
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(favor_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) >= {"favor_fwd_bidir", "favor_fwd_causal", "favor_workspace_bytes",
+                          "favor_feature_map", "favor_draw_projection", "favor_status_string",
+                          "favor_last_hip_error"}
+    raw = ctypes.CDLL(fv.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_strings():
+    for s in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, 12345):
+        assert isinstance(fv.status_string(s), str) and fv.status_string(s)
+    assert lib.favor_last_hip_error() == 0
+
+
+# Dummy device addresses: aligned, never dereferenced (validation fails first).
+A = 0x10000
+MIS = 0x10008
+
+
+def call(fn, B=1, H=1, L=16, d=64, m=64, dtype=1, Q=A, K=A, V=A, W=A, O=A, ws=A, wsb=1 << 40):
+    return getattr(lib, fn)(B, H, L, d, m, dtype, Q, K, V, W, O, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["favor_fwd_bidir", "favor_fwd_causal"])
+def test_validation_errors(fn):
+    assert call(fn, B=0) == ESHAPE
+    assert call(fn, H=-1) == ESHAPE
+    assert call(fn, L=0) == ESHAPE
+    assert call(fn, B=1 << 16, H=1 << 10, L=1 << 10) == ESHAPE  # > 2^31 elements
+    for d in (0, 8, 48, 96, 256):
+        assert call(fn, d=d) == EUNSUP
+    for m in (0, 8, 24, 1040, 2048):
+        assert call(fn, m=m) == EUNSUP
+    assert call(fn, dtype=2) == EUNSUP
+    for k in ("Q", "K", "V", "W", "O", "ws"):
+        assert call(fn, **{k: None}) == ENULL
+    for k in ("Q", "K", "V", "W", "O"):
+        assert call(fn, **{k: MIS}) == EALIGN
+    assert call(fn, ws=A + 128) == EALIGN
+    need = fv.workspace_bytes(1, 1, 16, 64, 64, 1, fn.endswith("causal"))
+    assert call(fn, wsb=need - 1) == EWS
+    assert call(fn, wsb=0) == EWS
+    assert lib.favor_last_hip_error() == 0
+
+
+def test_feature_map_validation():
+    f = lib.favor_feature_map
+    assert f(1, 1, 0, 64, 64, 1, A, A, A, None) == ESHAPE
+    assert f(1, 1, 8, 24, 64, 1, A, A, A, None) == EUNSUP
+    assert f(1, 1, 8, 64, 64, 1, None, A, A, None) == ENULL
+    assert f(1, 1, 8, 64, 64, 1, A, A, None, None) == ENULL
+    assert f(1, 1, 8, 64, 64, 1, MIS, A, A, None) == EALIGN
+
+
+def test_workspace_bytes():
+    for causal in (False, True):
+        for (B, H, L, d, m) in [(1, 1, 1, 16, 16), (8, 8, 4096, 64, 256), (4, 32, 16384, 128, 512),
+                                (1, 16, 32768, 64, 256), (1, 1, 4097, 128, 1024)]:
+            n = fv.workspace_bytes(B, H, L, d, m, 1, causal)
+            # at least one key state [m, d+1] fp32 per head, and 256-byte granular
+            assert n >= B * H * m * (d + 1) * 4
+            assert n % 256 == 0
+    with pytest.raises(fv.FavorError):
+        fv.workspace_bytes(1, 1, 1, 24, 16)
+    out = ctypes.c_size_t(0)
+    assert lib.favor_workspace_bytes(1, 1, 1, 16, 16, 1, 0, None) == ENULL
+
+
+# ---------------------------------------------------------------------------
+# Host projection draw.
+# ---------------------------------------------------------------------------
+def test_draw_errors():
+    f = lib.favor_draw_projection
+    buf = (ctypes.c_float * 16)()
+    assert f(1, 4, 4, None) == ENULL
+    assert f(1, 0, 4, buf) == ESHAPE
+    assert f(1, 4, 0, buf) == ESHAPE
+
+
+@pytest.mark.parametrize("seed,m,d", [(1002, 16, 16), (2002, 256, 64), (5002, 512, 128),
+                                      (77, 40, 16), (2 ** 63 + 5, 64, 32)])
+def test_draw_matches_oracle_draw(seed, m, d):
+    # Both sides implement the same counter-based stream, Box-Muller and
+    # positive-diagonal orthogonalisation independently (Gram-Schmidt in the
+    # library, Householder QR with a sign fix in the oracle).
+    W = fv.draw_projection(seed, m, d).astype(np.float64)
+    Wo = oracle.draw_w(seed, m, d)
+    assert np.max(np.abs(W - Wo)) <= 1e-6 * np.max(np.abs(Wo))
+
+
+def test_draw_matches_golden_fixture():
+    rows = [l.split() for l in open(os.path.join(ROOT, "tests", "golden", "tiny_f32_W.txt"))
+            if not l.startswith("#")]
+    g = np.array(rows, dtype=np.float64).astype(np.float32)
+    W = fv.draw_projection(1002, 16, 16)
+    np.testing.assert_allclose(W, g, rtol=0, atol=2e-6 * np.abs(g).max())
+
+
+def test_draw_properties():
+    d = 64
+    W = fv.draw_projection(99, 64 * d, d).astype(np.float64)
+    for b0 in range(0, W.shape[0], d):
+        G = W[b0:b0 + d] @ W[b0:b0 + d].T
+        off = G - np.diag(np.diag(G))
+        assert np.max(np.abs(off)) <= 1e-6 * np.diag(G).mean()
+    s = np.linalg.norm(W, axis=1)
+    assert scipy.stats.kstest(s, scipy.stats.chi(d).cdf).pvalue > 1e-3
+    assert abs(np.mean(s ** 2) - d) < 5 * math.sqrt(2 * d / s.size)
+    assert np.max(np.abs(W.mean(axis=0))) < 5 / math.sqrt(W.shape[0])
+
+
+def test_draw_is_deterministic_and_seed_dependent():
+    a = fv.draw_projection(3, 32, 16)
+    np.testing.assert_array_equal(a, fv.draw_projection(3, 32, 16))
+    assert not np.array_equal(a, fv.draw_projection(4, 32, 16))
