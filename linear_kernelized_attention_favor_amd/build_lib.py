@@ -22,11 +22,15 @@ BUILD = os.path.join(CSRC, "_build")
 LIB = os.path.join(PKG, "libfavor.so")
 ARCH = "gfx950"
 
-COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-result",
+COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
 # Keep packed fp32 arithmetic out of the device code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-munsafe-fp-atomics"]
+
+
+def rocm() -> str:
+    return os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
 def hipcc() -> str:
@@ -41,7 +45,9 @@ def _compile(src: str, verbose: bool) -> str:
     if src.endswith(".hip"):
         cmd = [hipcc(), "-x", "hip", *DEVICE, *COMMON, "-c", src, "-o", obj]
     else:
-        cmd = [hipcc(), *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", src, "-o", obj]
+        # Host-only C++: the system compiler against the HIP headers.
+        cmd = [shutil.which("g++") or "g++", *COMMON, "-D__HIP_PLATFORM_AMD__",
+               f"-I{os.path.join(rocm(), 'include')}", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -38,8 +38,8 @@ int fail_hip(hipError_t e) {
 int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
             const void* Q, const void* K, const void* V, const float* W, void* O, void* ws,
             size_t ws_bytes, void* stream) {
-  int st = check_shape(B, H, L, d, m, dtype);
-  if (st != FAVOR_OK) return st;
+  const int status = check_shape(B, H, L, d, m, dtype);
+  if (status != FAVOR_OK) return status;
   if (!Q || !K || !V || !W || !O || !ws) return FAVOR_ERR_NULL;
   if (!is_aligned(Q, 16) || !is_aligned(K, 16) || !is_aligned(V, 16) || !is_aligned(W, 16) ||
       !is_aligned(O, 16) || !is_aligned(ws, 256))
@@ -47,7 +47,9 @@ int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype
   Plan p;
   make_plan(B, H, L, d, m, dtype, causal, &p);
   if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
-  hipError_t e = generic_forward(p, Q, K, V, W, O, ws, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = (p.path == kPathMfma) ? mfma_bidir_forward(p, Q, K, V, W, O, ws, st)
+                                             : generic_forward(p, Q, K, V, W, O, ws, st);
   if (e != hipSuccess) return fail_hip(e);
   return FAVOR_OK;
 }
@@ -59,14 +61,35 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
   std::memset(p, 0, sizeof(*p));
   p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
   p->BH = B * H;
+  const size_t ncol = static_cast<size_t>(d) + 1;
+  const size_t BH = static_cast<size_t>(p->BH);
+  size_t off = 0;
+  if (!causal && mfma_bidir_supported(d, m, dtype)) {
+    p->path = kPathMfma;
+    // Splits: about 512 key-side work-groups in total, at least 128 tokens each.
+    int ns = (512 + p->BH - 1) / p->BH;
+    const int maxs = (L + 127) / 128;
+    ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
+    p->seg = ((L + ns - 1) / ns + 31) / 32 * 32;
+    p->nseg = (L + p->seg - 1) / p->seg;
+    // Query blocks: about 512 work-groups, a multiple of 64 tokens, >= 256.
+    const int64_t want = (static_cast<int64_t>(L) * p->BH + 511) / 512;
+    int64_t qb = (want + 63) / 64 * 64;
+    if (qb < 256) qb = 256;
+    p->qblk = static_cast<int32_t>(qb);
+    p->off_T = off;    off = align256(off + BH * p->nseg * ncol * m * sizeof(float));
+    p->off_cseg = off; off = align256(off + BH * p->nseg * m * sizeof(float));
+    p->off_cP = off;   off = align256(off + static_cast<size_t>(m) * (d + 8) * 2);
+    p->off_KV = off;   off = align256(off + BH * (d + 16) * (static_cast<size_t>(m) + 8) * 2);
+    p->off_cfin = off; off = align256(off + BH * m * sizeof(float));
+    p->bytes = off;
+    return;
+  }
   p->path = kPathGeneric;
   // Sequence splits (bidirectional) and segments (causal); a multiple of the
   // 8-token tile of the generic kernels.
   p->seg = causal ? 256 : 512;
   p->nseg = (L + p->seg - 1) / p->seg;
-  const size_t ncol = static_cast<size_t>(d) + 1;
-  const size_t BH = static_cast<size_t>(p->BH);
-  size_t off = 0;
   p->off_T = off;    off = align256(off + BH * p->nseg * m * ncol * sizeof(float));
   p->off_cseg = off; off = align256(off + BH * p->nseg * m * sizeof(float));
   p->off_cP = off;   off = align256(off + (causal ? BH * p->nseg * m * sizeof(float) : 0));

@@ -24,6 +24,7 @@ struct Plan {
   int32_t path;
   int32_t seg;    // tokens per sequence split (bidirectional) or segment (causal)
   int32_t nseg;   // number of splits / segments per head
+  int32_t qblk;   // tokens per query-side work-group (MFMA path)
   // Generic-path workspace (all fp32):
   //   T    [BH][nseg][m][d+1]  per-segment key state, then (causal) its
   //                            exclusive prefix over earlier segments
@@ -31,6 +32,12 @@ struct Plan {
   //   cP   [BH][nseg][m]       reference of the exclusive prefix (causal)
   //   KV   [BH][m][d+1]        final key state (bidirectional)
   //   cfin [BH][m]             its per-feature reference
+  // MFMA bidirectional path:
+  //   T    [BH][nseg][d+1][m]  per-split partial state (row d = z), fp32
+  //   cseg [BH][nseg][m]       per-feature references of the partials
+  //   cP   [m][d+8]            W log2(e) in fp16 (query-side projection operand)
+  //   KV   [BH][d+16][m+8]     combined state, bf16, query-side operand order
+  //   cfin [BH][m]             combined per-feature references
   size_t off_T, off_cseg, off_cP, off_KV, off_cfin;
   size_t bytes;
 };
@@ -42,6 +49,11 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
 // Generic path: enqueue the whole forward pass on `stream`.
 hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const void* V,
                            const float* W, void* O, void* ws, hipStream_t stream);
+
+// MFMA path (bf16 inputs): shape support, and the bidirectional forward.
+bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype);
+hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
+                              const float* W, void* O, void* ws, hipStream_t stream);
 
 // Feature map test entry (generic fp32 arithmetic).
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
