@@ -51,6 +51,9 @@ constexpr float kTau = 20.0f;
 #ifndef FAVOR_QAPPLY_NTQ
 #define FAVOR_QAPPLY_NTQ 2      // 16-token tiles per query-side wave iteration
 #endif
+#ifndef FAVOR_QAPPLY_WPE
+#define FAVOR_QAPPLY_WPE 2      // query-side waves per SIMD the register budget targets
+#endif
 constexpr int kTT = 32;        // tokens per key tile
 
 template <int D>
@@ -78,15 +81,20 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
                                                  int L, int m, int SL, int nsplit) {
   using C = KCfg<D>;
   constexpr int NTH = NW * 64;
-  constexpr int CPT = (C::CH + NTH - 1) / NTH;
+  constexpr int KCH = kTT * D / 8;           // 16-byte K chunks per tile
+  constexpr int KPT = (KCH + NTH - 1) / NTH;
+  constexpr int VUN = (kTT / 2) * (D / 4);   // (token pair, 4-column group) units per tile
+  constexpr int VPT = (VUN + NTH - 1) / NTH;
   const int s = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int f0 = wave * C::FPW;
 
-  __shared__ __align__(16) _Float16 Ks[2][kTT][C::KROW];
-  __shared__ __align__(16) uint16_t Vt[2][D][C::VROW];
-  __shared__ __align__(16) float Ns[2][kTT];   // -|k|^2 log2(e) / 2 per token
+  // Three-stage ring: tile t's V^T, tile t+1's K (projection running ahead)
+  // and tile t+2 being written.
+  __shared__ __align__(16) _Float16 Ks[3][kTT][C::KROW];
+  __shared__ __align__(16) uint32_t Vt[3][D][C::VROW / 2];   // bf16 pairs, token order perm_of
+  __shared__ __align__(16) float Ns[3][kTT];                 // -|k|^2 log2(e) / 2 per token
 
   // Projection B operands, kept in registers: W'[f][32 ks + 8 g + u].
   f16x8 wb[C::NT][C::KS];
@@ -111,38 +119,44 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
   for (int i = 0; i <= C::MV; ++i)
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float cref[C::NT];   // per-feature reference (log2 units)
+  float cref[C::NT];   // per-feature reference (log2 units), set by the first tile
 #pragma unroll
   for (int nt = 0; nt < C::NT; ++nt) cref[nt] = 0.f;
-  bool fresh = true;   // no tile seen yet: the first tile sets the references
 
   const int j0 = s * SL, j1 = min(L, j0 + SL);
   const int ntiles = (j1 - j0 + kTT - 1) / kTT;
   const size_t base = static_cast<size_t>(bh) * L * D;
 
-  // Global loads of tile t+1 are in flight while tile t is computed.
-  uint4 kA[CPT], vA[CPT];
-  auto gload = [&](int t, uint4 (&kreg)[CPT], uint4 (&vreg)[CPT]) {
+  // Global loads of tile t+3 are in flight while tile t is consumed.  Loads
+  // past the split read nothing and stage zeros.
+  uint4 kreg[KPT];
+  uint2 vreg[VPT][2];
+  auto gload = [&](int t) {
     const int jt = j0 + t * kTT;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NTH;
-      const int j = c / C::CPR, ch = c % C::CPR;
-      const int tok = jt + j;
-      if (c < C::CH && tok < j1) {
-        const size_t off = base + static_cast<size_t>(tok) * D + ch * 8;
-        kreg[i] = *reinterpret_cast<const uint4*>(K + off);
-        vreg[i] = *reinterpret_cast<const uint4*>(V + off);
-      } else {
-        kreg[i] = make_uint4(0, 0, 0, 0);
-        vreg[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int tok = jt + c / C::CPR;
+      kreg[i] = make_uint4(0, 0, 0, 0);
+      if (c < KCH && tok < j1)
+        kreg[i] = *reinterpret_cast<const uint4*>(K + base + static_cast<size_t>(tok) * D +
+                                                  (c % C::CPR) * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * NTH;
+      const int tok = jt + 2 * (u % 16);
+      const size_t off = base + static_cast<size_t>(tok) * D + 4 * (u / 16);
+      vreg[i][0] = make_uint2(0, 0);
+      vreg[i][1] = make_uint2(0, 0);
+      if (u < VUN && tok < j1) vreg[i][0] = *reinterpret_cast<const uint2*>(V + off);
+      if (u < VUN && tok + 1 < j1) vreg[i][1] = *reinterpret_cast<const uint2*>(V + off + D);
     }
   };
-  auto lstore = [&](int buf, int t, const uint4 (&kreg)[CPT], const uint4 (&vreg)[CPT]) {
+  auto lstore = [&](int buf, int t) {
     const int jt = j0 + t * kTT;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
+    for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NTH;
       const int j = (c / C::CPR) % kTT, ch = c % C::CPR;
       const uint4 kv = kreg[i];
@@ -158,19 +172,27 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
       }
       // Sum of squares over the CPR threads holding one token (consecutive lanes).
       ss = group_sum<C::CPR>(ss);
-      if (c < C::CH) {
+      if (c < KCH) {
         uint4 h;
         h.x = bf16x2_to_f16x2(kv.x); h.y = bf16x2_to_f16x2(kv.y);
         h.z = bf16x2_to_f16x2(kv.z); h.w = bf16x2_to_f16x2(kv.w);
         *reinterpret_cast<uint4*>(&Ks[buf][j][ch * 8]) = h;
-        const uint32_t v4[4] = {vreg[i].x, vreg[i].y, vreg[i].z, vreg[i].w};
-        const int pj = perm_inv(j);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          Vt[buf][ch * 8 + 2 * q][pj] = static_cast<uint16_t>(v4[q] & 0xffffu);
-          Vt[buf][ch * 8 + 2 * q + 1][pj] = static_cast<uint16_t>(v4[q] >> 16);
-        }
         if (ch == 0) Ns[buf][j] = (jt + j < j1) ? -0.5f * kLog2e * ss : -INFINITY;
+      }
+    }
+    // V^T: two consecutive tokens share one 32-bit word (positions perm_of
+    // keep token pairs 2p, 2p+1 adjacent), four columns per unit.
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * NTH;
+      if (u < VUN) {
+        const int col = 4 * (u / 16);
+        const int w = perm_inv(2 * (u % 16)) >> 1;
+        const uint2 a = vreg[i][0], b = vreg[i][1];
+        Vt[buf][col + 0][w] = __builtin_amdgcn_perm(b.x, a.x, 0x05040100u);
+        Vt[buf][col + 1][w] = __builtin_amdgcn_perm(b.x, a.x, 0x07060302u);
+        Vt[buf][col + 2][w] = __builtin_amdgcn_perm(b.y, a.y, 0x05040100u);
+        Vt[buf][col + 3][w] = __builtin_amdgcn_perm(b.y, a.y, 0x07060302u);
       }
     }
   };
@@ -179,95 +201,116 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
 #pragma unroll
   for (int u = 0; u < 8; ++u) ones[u] = static_cast<__bf16>(1.0f);
 
-  auto compute = [&](const int buf) {
-    // S = K W'^T - n'  (rows: tokens 16 mt + 4 g + v; column: feature f0 + 16 nt + l16)
-    f32x4 S[2][C::NT];
-    {
-      f32x4 cinit[2];
-      f16x8 ka[2][C::KS];
+  using SArr = f32x4[2][C::NT];
+  // S = K W'^T - n'  (rows: tokens 16 mt + 4 g + v; column: feature f0 + 16 nt + l16)
+  auto proj = [&](int buf, SArr& S) {
+    f32x4 cinit[2];
+    f16x8 ka[2][C::KS];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        cinit[mt] = *reinterpret_cast<const f32x4*>(&Ns[buf][16 * mt + 4 * g]);
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          ka[mt][ks] = *reinterpret_cast<const f16x8*>(&Ks[buf][16 * mt + l16][32 * ks + 8 * g]);
-      }
-      // k-step outermost: consecutive MFMAs are independent.
+    for (int mt = 0; mt < 2; ++mt) {
+      cinit[mt] = *reinterpret_cast<const f32x4*>(&Ns[buf][16 * mt + 4 * g]);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < C::NT; ++nt)
-            S[mt][nt] = mma_f16(ka[mt][ks], wb[nt][ks], ks == 0 ? cinit[mt] : S[mt][nt]);
+        ka[mt][ks] = *reinterpret_cast<const f16x8*>(&Ks[buf][16 * mt + l16][32 * ks + 8 * g]);
     }
-
-    // Exponents relative to the per-feature reference, their tile maximum,
-    // and the lazy reference update (always on the work-group's first tile).
-    float e[C::NT][8];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt)
+          S[mt][nt] = mma_f16(ka[mt][ks], wb[nt][ks], ks == 0 ? cinit[mt] : S[mt][nt]);
+  };
+  // Exponents relative to the references, in place; true if any lane of the
+  // wave exceeds the headroom.
+  auto relative = [&](SArr& S, float (&lm)[C::NT]) {
     bool raise = false;
-    float tm[C::NT];
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        e[nt][v] = S[0][nt][v] - cref[nt];
-        e[nt][4 + v] = S[1][nt][v] - cref[nt];
-      }
-      const float a = max3(e[nt][0], e[nt][1], e[nt][2]);
-      const float b = max3(e[nt][3], e[nt][4], e[nt][5]);
-      tm[nt] = max3(a, b, fmaxf(e[nt][6], e[nt][7]));   // this lane's 8 tokens
-      raise |= tm[nt] > kTau;
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= cref[nt];
+      const float a = max3(S[0][nt][0], S[0][nt][1], S[0][nt][2]);
+      const float b = max3(S[0][nt][3], S[1][nt][0], S[1][nt][1]);
+      lm[nt] = max3(a, b, fmaxf(S[1][nt][2], S[1][nt][3]));   // this lane's 8 tokens
+      raise |= lm[nt] > kTau;
     }
-    // Only the first tile, or a lane above the headroom, needs the exact
-    // per-feature maximum (a column reduction) and a reference update.
-    if (__builtin_expect(fresh || __ballot(raise) != 0, 0)) {
+    return __ballot(raise) != 0;
+  };
+  // Reference update: exact per-feature maximum (column reduction); always
+  // on the first tile, otherwise only where a lane exceeded the headroom.
+  auto rebase = [&](SArr& S, float (&lm)[C::NT], bool first) {
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt) {
-        tm[nt] = colmax4(tm[nt]);
-        const float dlt = (fresh || tm[nt] > kTau) ? tm[nt] : 0.f;
-        if (!fresh) {   // accumulators are still zero on the first tile
-          const float f = fast_exp2(-dlt);
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const float tm = colmax4(lm[nt]);
+      const float dlt = (first || tm > kTau) ? tm : 0.f;
+      if (!first) {   // accumulators are still zero on the first tile
+        const float f = fast_exp2(-dlt);
 #pragma unroll
-          for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) e[nt][u] -= dlt;
-        cref[nt] += dlt;
+        for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
       }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= dlt;
+      cref[nt] += dlt;
     }
-    fresh = false;
-
-    // K~ = exp2(e) as the contraction's B operand (positions perm_of).
-    bf16x8 kb[C::NT];
+  };
+  // K~ = exp2(S) as the contraction's B operand (token positions perm_of).
+  auto features = [&](const SArr& S, bf16x8 (&kb)[C::NT]) {
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
       uint32_t p[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) p[q] = pack_bf16(fast_exp2(e[nt][2 * q]), fast_exp2(e[nt][2 * q + 1]));
+      for (int q = 0; q < 2; ++q) {
+        p[q] = pack_bf16(fast_exp2(S[0][nt][2 * q]), fast_exp2(S[0][nt][2 * q + 1]));
+        p[2 + q] = pack_bf16(fast_exp2(S[1][nt][2 * q]), fast_exp2(S[1][nt][2 * q + 1]));
+      }
       kb[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
     }
-
-    // [V | 1]^T K~ : rows = value columns, columns = features.
+  };
+  // [V | 1]^T K~ : rows = value columns, columns = features.
+  auto contract = [&](int buf, const bf16x8 (&kb)[C::NT]) {
 #pragma unroll
     for (int mv = 0; mv < C::MV; ++mv) {
-      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vt[buf][16 * mv + l16][8 * g]);
+      const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vt[buf][16 * mv + l16][4 * g]);
 #pragma unroll
       for (int nt = 0; nt < C::NT; ++nt) acc[mv][nt] = mma_bf16(va, kb[nt], acc[mv][nt]);
     }
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) acc[C::MV][nt] = mma_bf16(ones, kb[nt], acc[C::MV][nt]);
-
   };
 
-  gload(0, kA, vA);
-  lstore(0, 0, kA, vA);
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) gload(t + 1, kA, vA);
+  // Prologue: tiles 0 and 1 staged, tile 2 in flight, tile 0 projected.
+  gload(0);
+  lstore(0, 0);
+  gload(1);
+  lstore(1, 1);
+  gload(2);
+  lds_barrier();
+  SArr SA, SB;
+  float lm[C::NT];
+  proj(0, SA);
+  relative(SA, lm);
+  rebase(SA, lm, true);
+
+  // Iteration t: project tile t+1 while tile t's features are formed, then
+  // contract tile t, stage tile t+2, load tile t+3, and check tile t+1.
+  auto step = [&](int t, SArr& Scur, SArr& Snext) {
+    bf16x8 kb[C::NT];
+    proj((t + 1) % 3, Snext);
+    features(Scur, kb);
+    contract(t % 3, kb);
+    lstore((t + 2) % 3, t + 2);
+    gload(t + 3);
+    if (__builtin_expect(relative(Snext, lm), 0)) rebase(Snext, lm, false);
     lds_barrier();
-    compute(buf);
-    if (t + 1 < ntiles) lstore(buf ^ 1, t + 1, kA, vA);
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, SA, SB);
+    if (t + 1 >= ntiles) break;
+    step(t + 1, SB, SA);
   }
 
   // Partial state out: P[bh][s][row][f].
@@ -287,13 +330,13 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// kcombine: grid (ceil((D+16) * m / 256), BH), 256 threads, one thread per
-// (row, feature) entry of the combined state.  The splits are summed in split
-// order after rescaling to the largest per-feature reference.  Output Kz
-// [BH][D+16][m+8] bf16 in the query side's operand order (features permuted
-// within 32-blocks; row D = z, rows above D zero) and cfin [BH][m].  Head 0's
-// work-groups also write W16 [m][D+8]: W log2(e) in fp16, the query side's
-// projection operand.
+// kcombine: grid (ceil((D+16) * m / 1024), BH), 256 threads; each thread owns
+// four consecutive features of one row of the combined state.  The splits are
+// summed in split order after rescaling to the largest per-feature reference.
+// Output Kz [BH][D+16][m+8] bf16 in the query side's operand order (features
+// permuted within 32-blocks; row D = z, rows above D zero) and cfin [BH][m].
+// Head 0's work-groups also write W16 [m][D+8]: W log2(e) in fp16, the query
+// side's projection operand.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void kcombine(const float* __restrict__ P,
@@ -303,30 +346,45 @@ __global__ __launch_bounds__(256) void kcombine(const float* __restrict__ P,
                                                 float* __restrict__ cfin,
                                                 _Float16* __restrict__ W16, int m, int nsplit) {
   const int bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int e = blockIdx.x * 256 + threadIdx.x;   // (row, feature quad)
   if (bh == 0) {
     for (int i = e; i < m * D; i += gridDim.x * 256) {
       const int f = i / D, a = i - f * D;
       W16[static_cast<size_t>(f) * (D + 8) + a] = static_cast<_Float16>(W[i] * kLog2e);
     }
   }
-  if (e >= (D + 16) * m) return;
-  const int row = e / m, f = e - row * m;
-  const size_t cb = static_cast<size_t>(bh) * nsplit * m + f;
-  float cmax = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) cmax = fmaxf(cmax, cs[cb + static_cast<size_t>(s) * m]);
-  float a = 0.f;
+  const int mq = m / 4;
+  if (e >= (D + 16) * mq) return;
+  const int row = e / mq, f = 4 * (e - row * mq);
+  const float4* csq = reinterpret_cast<const float4*>(cs + static_cast<size_t>(bh) * nsplit * m + f);
+  float4 cmax = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  for (int s = 0; s < nsplit; ++s) {
+    const float4 c = csq[static_cast<size_t>(s) * mq];
+    cmax.x = fmaxf(cmax.x, c.x); cmax.y = fmaxf(cmax.y, c.y);
+    cmax.z = fmaxf(cmax.z, c.z); cmax.w = fmaxf(cmax.w, c.w);
+  }
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   if (row <= D) {
+    const float4* pq = reinterpret_cast<const float4*>(
+        P + (static_cast<size_t>(bh) * nsplit * (D + 1) + row) * m + f);
+    const size_t sstride = static_cast<size_t>(D + 1) * mq;
     for (int s = 0; s < nsplit; ++s) {
-      const float sc = fast_exp2(cs[cb + static_cast<size_t>(s) * m] - cmax);
-      a = fmaf(P[((static_cast<size_t>(bh) * nsplit + s) * (D + 1) + row) * m + f], sc, a);
+      const float4 c = csq[static_cast<size_t>(s) * mq];
+      const float4 v = pq[s * sstride];
+      a.x = fmaf(v.x, fast_exp2(c.x - cmax.x), a.x);
+      a.y = fmaf(v.y, fast_exp2(c.y - cmax.y), a.y);
+      a.z = fmaf(v.z, fast_exp2(c.z - cmax.z), a.z);
+      a.w = fmaf(v.w, fast_exp2(c.w - cmax.w), a.w);
     }
   }
-  const int kzrow = m + 8;
-  const int pos = (f & ~31) + perm_inv(f & 31);
-  Kz[(static_cast<size_t>(bh) * (D + 16) + row) * kzrow + pos] =
-      static_cast<uint16_t>(pack_bf16(a, 0.f) & 0xffffu);
-  if (row == 0) cfin[static_cast<size_t>(bh) * m + f] = cmax;
+  // Four features stay inside one 32-block; their permuted positions are
+  // scattered within it.
+  uint16_t* kzr = Kz + (static_cast<size_t>(bh) * (D + 16) + row) * (m + 8) + (f & ~31);
+  const float av[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    kzr[perm_inv((f & 31) + q)] = static_cast<uint16_t>(pack_bf16(av[q], 0.f) & 0xffffu);
+  if (row == 0) *reinterpret_cast<float4*>(cfin + static_cast<size_t>(bh) * m + f) = cmax;
 }
 
 // ---------------------------------------------------------------------------
@@ -349,59 +407,66 @@ size_t qapply_lds_bytes(int m) {
          static_cast<size_t>(m) * 4;
 }
 
-template <int D, int NW, int NTQ>
-__global__ __launch_bounds__(NW * 64, 2) void qapply(const uint16_t* __restrict__ Q,
+template <int D, int NW, int NTQ, int NCH>
+__global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16_t* __restrict__ Q,
                                                   const _Float16* __restrict__ W16,
                                                   const uint16_t* __restrict__ Kz,
                                                   const float* __restrict__ cfin,
-                                                  uint16_t* __restrict__ O, int L, int m, int QL) {
+                                                  uint16_t* __restrict__ O, int L, int QL) {
   using C = QCfg<D, NTQ>;
   constexpr int NTH = NW * 64;
+  constexpr int m = 64 * NCH;
+  constexpr int kzrow = m + 8;
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* Wl = reinterpret_cast<_Float16*>(smem);
   uint16_t* Kzl = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(m) * C::WROW * 2);
   float* cl = reinterpret_cast<float*>(smem + static_cast<size_t>(m) * C::WROW * 2 +
-                                       static_cast<size_t>(D + 16) * (m + 8) * 2);
+                                       static_cast<size_t>(D + 16) * kzrow * 2);
   const int qb = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int kzrow = m + 8;
 
   // Stage W' (fp16), Kz and c for this head.
   {
     const uint4* src = reinterpret_cast<const uint4*>(W16);
     uint4* dst = reinterpret_cast<uint4*>(Wl);
-    const int n16 = m * C::WROW / 8;
+    constexpr int n16 = m * C::WROW / 8;
     for (int i = tid; i < n16; i += NTH) dst[i] = src[i];
   }
   {
     const uint4* src = reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow);
     uint4* dst = reinterpret_cast<uint4*>(Kzl);
-    const int n16 = (D + 16) * kzrow / 8;
+    constexpr int n16 = (D + 16) * kzrow / 8;
     for (int i = tid; i < n16; i += NTH) dst[i] = src[i];
   }
   for (int i = tid; i < m; i += NTH) cl[i] = cfin[static_cast<size_t>(bh) * m + i];
-  __syncthreads();
+  __syncthreads();   // the only barrier: LDS is read-only from here on
 
   const size_t base = static_cast<size_t>(bh) * L * D;
   const int q0 = qb * QL, q1 = min(L, q0 + QL);
-  const int nch = m / 64;
+  const int step = NW * C::TQ;
+  const int tt0 = q0 + wave * C::TQ;
+  if (tt0 >= q1) return;
+  const int ntile = (q1 - tt0 + step - 1) / step;
 
-  // Q tiles: raw bf16 loads one tile ahead of their use, two register sets.
+  // Q tiles: raw bf16 loads one tile ahead of their use.
   using Raw = uint4[C::NTQ][C::KS];
+  using Qop = f16x8[C::NTQ][C::KS];
   auto qload = [&](int tt, Raw& raw) {
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
       const int tok = tt + 16 * nt + l16;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        raw[nt][ks] = (tok < q1) ? *reinterpret_cast<const uint4*>(
-                                       Q + base + static_cast<size_t>(tok) * D + 32 * ks + 8 * g)
-                                 : make_uint4(0, 0, 0, 0);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        raw[nt][ks] = make_uint4(0, 0, 0, 0);
+        if (tok < q1)
+          raw[nt][ks] = *reinterpret_cast<const uint4*>(Q + base + static_cast<size_t>(tok) * D +
+                                                        32 * ks + 8 * g);
+      }
     }
   };
   // Q^T operands: token tt + 16 nt + l16, dims 32 ks + 8 g .. +7, in fp16.
-  auto convert = [&](const Raw& raw, f16x8 (&qb_)[C::NTQ][C::KS]) {
+  auto convert = [&](const Raw& raw, Qop& qop) {
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt)
 #pragma unroll
@@ -410,104 +475,101 @@ __global__ __launch_bounds__(NW * 64, 2) void qapply(const uint16_t* __restrict_
         uint4 h;
         h.x = bf16x2_to_f16x2(x.x); h.y = bf16x2_to_f16x2(x.y);
         h.z = bf16x2_to_f16x2(x.z); h.w = bf16x2_to_f16x2(x.w);
-        qb_[nt][ks] = __builtin_bit_cast(f16x8, h);
+        qop[nt][ks] = __builtin_bit_cast(f16x8, h);
       }
   };
-  auto tile = [&](const int tt, const f16x8 (&qb_)[C::NTQ][C::KS]) {
-    f32x4 acc[C::MV + 1][C::NTQ];
-#pragma unroll
-    for (int i = 0; i <= C::MV; ++i)
-#pragma unroll
-      for (int nt = 0; nt < C::NTQ; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float M[C::NTQ];   // per-row reference (log2 units), set by the first chunk
-#pragma unroll
-    for (int nt = 0; nt < C::NTQ; ++nt) M[nt] = 0.f;
 
-    for (int ch = 0; ch < nch; ++ch) {
-      // S^T = W' Q^T + c  (rows: features 64 ch + 16 mt + 4 g + v; column: token)
-      f32x4 S[4][C::NTQ];
-      {
-        f32x4 cb[4];
-        f16x8 wa[4][C::KS];
+  f32x4 acc[C::MV + 1][C::NTQ];
+  float M[C::NTQ];   // per-row reference (log2 units), set by each tile's first chunk
+  using SArr = f32x4[4][C::NTQ];
+  // S^T = W' Q^T + c  (rows: features 64 ch + 16 mt + 4 g + v; column: token)
+  auto proj = [&](int ch, const Qop& qop, SArr& S) {
+    f32x4 cb[4];
+    f16x8 wa[4][C::KS];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int fr = 64 * ch + 16 * mt;
-          cb[mt] = *reinterpret_cast<const f32x4*>(&cl[fr + 4 * g]);
+    for (int mt = 0; mt < 4; ++mt) {
+      const int fr = 64 * ch + 16 * mt;
+      cb[mt] = *reinterpret_cast<const f32x4*>(&cl[fr + 4 * g]);
 #pragma unroll
-          for (int ks = 0; ks < C::KS; ++ks)
-            wa[mt][ks] = *reinterpret_cast<const f16x8*>(
-                &Wl[static_cast<size_t>(fr + l16) * C::WROW + 32 * ks + 8 * g]);
-        }
+      for (int ks = 0; ks < C::KS; ++ks)
+        wa[mt][ks] = *reinterpret_cast<const f16x8*>(
+            &Wl[static_cast<size_t>(fr + l16) * C::WROW + 32 * ks + 8 * g]);
+    }
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
+    for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < C::NTQ; ++nt)
-              S[mt][nt] = mma_f16(wa[mt][ks], qb_[nt][ks], ks == 0 ? cb[mt] : S[mt][nt]);
+        for (int nt = 0; nt < C::NTQ; ++nt)
+          S[mt][nt] = mma_f16(wa[mt][ks], qop[nt][ks], ks == 0 ? cb[mt] : S[mt][nt]);
+  };
+  // Exponents relative to the row references, in place; true if any lane of
+  // the wave exceeds the headroom.
+  float lm[C::NTQ];
+  auto relative = [&](SArr& S) {
+    bool raise = false;
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= M[nt];
+      const float a = max3(S[0][nt][0], S[0][nt][1], S[0][nt][2]);
+      const float b = max3(S[0][nt][3], S[1][nt][0], S[1][nt][1]);
+      const float c = max3(S[1][nt][2], S[1][nt][3], S[2][nt][0]);
+      const float d = max3(S[2][nt][1], S[2][nt][2], S[2][nt][3]);
+      const float e = max3(S[3][nt][0], S[3][nt][1], S[3][nt][2]);
+      lm[nt] = max3(max3(a, b, c), max3(d, e, S[3][nt][3]), a);   // this lane's 16 features
+      raise |= lm[nt] > kTau;
+    }
+    return __ballot(raise) != 0;
+  };
+  // Row reference update: exact row maximum (column reduction); always on a
+  // tile's first chunk, otherwise only where a lane exceeded the headroom.
+  auto rebase = [&](SArr& S, bool first) {
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      const float cm = colmax4(lm[nt]);
+      const float dlt = (first || cm > kTau) ? cm : 0.f;
+      if (!first) {   // accumulators are still zero on the first chunk
+        const float f = fast_exp2(-dlt);
+#pragma unroll
+        for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
       }
-      // Exponents relative to the row reference; the first chunk sets the
-      // reference to the chunk's row maximum, later chunks raise it lazily.
-      float e[4][C::NTQ][4];
-      bool raise = false;
-      float cm[C::NTQ];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= dlt;
+      M[nt] += dlt;
+    }
+  };
+  // Q~^T = exp2(S) (features at positions perm_of) times [KV | z]^T.
+  auto apply = [&](int ch, const SArr& S) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 qt[C::NTQ];
 #pragma unroll
       for (int nt = 0; nt < C::NTQ; ++nt) {
+        uint32_t p[4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) e[mt][nt][v] = S[mt][nt][v] - M[nt];
-        const float a = max3(e[0][nt][0], e[0][nt][1], e[0][nt][2]);
-        const float b = max3(e[0][nt][3], e[1][nt][0], e[1][nt][1]);
-        const float c = max3(e[1][nt][2], e[1][nt][3], e[2][nt][0]);
-        const float d = max3(e[2][nt][1], e[2][nt][2], e[2][nt][3]);
-        const float f = max3(e[3][nt][0], e[3][nt][1], e[3][nt][2]);
-        cm[nt] = max3(max3(a, b, c), max3(d, f, e[3][nt][3]), a);   // this lane's 16 features
-        raise |= cm[nt] > kTau;
+        for (int q = 0; q < 2; ++q) {
+          p[q] = pack_bf16(fast_exp2(S[2 * kb][nt][2 * q]), fast_exp2(S[2 * kb][nt][2 * q + 1]));
+          p[2 + q] = pack_bf16(fast_exp2(S[2 * kb + 1][nt][2 * q]),
+                               fast_exp2(S[2 * kb + 1][nt][2 * q + 1]));
+        }
+        qt[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
       }
-      // Only the first chunk, or a lane above the headroom, needs the exact
-      // row maximum (a column reduction) and a reference update.
-      if (__builtin_expect(ch == 0 || __ballot(raise) != 0, 0)) {
+      const int kcol = 64 * ch + 32 * kb + 8 * g;
 #pragma unroll
-        for (int nt = 0; nt < C::NTQ; ++nt) {
-          cm[nt] = colmax4(cm[nt]);
-          const float dlt = (ch == 0 || cm[nt] > kTau) ? cm[nt] : 0.f;
-          if (ch != 0) {   // accumulators are still zero on the first chunk
-            const float f = fast_exp2(-dlt);
+      for (int mv = 0; mv <= C::MV; ++mv) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kzl[(16 * mv + l16) * kzrow + kcol]);
 #pragma unroll
-            for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
-          }
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) e[mt][nt][v] -= dlt;
-          M[nt] += dlt;
-        }
-      }
-      // Q~^T operands (features at positions perm_of within each 32-block).
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 qt[C::NTQ];
-#pragma unroll
-        for (int nt = 0; nt < C::NTQ; ++nt) {
-          uint32_t p[4];
-          p[0] = pack_bf16(fast_exp2(e[2 * kb][nt][0]), fast_exp2(e[2 * kb][nt][1]));
-          p[1] = pack_bf16(fast_exp2(e[2 * kb][nt][2]), fast_exp2(e[2 * kb][nt][3]));
-          p[2] = pack_bf16(fast_exp2(e[2 * kb + 1][nt][0]), fast_exp2(e[2 * kb + 1][nt][1]));
-          p[3] = pack_bf16(fast_exp2(e[2 * kb + 1][nt][2]), fast_exp2(e[2 * kb + 1][nt][3]));
-          qt[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
-        }
-        const int kcol = 64 * ch + 32 * kb + 8 * g;
-#pragma unroll
-        for (int mv = 0; mv <= C::MV; ++mv) {
-          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kzl[static_cast<size_t>(16 * mv + l16) * kzrow + kcol]);
-#pragma unroll
-          for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[nt], acc[mv][nt]);
-        }
+        for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[nt], acc[mv][nt]);
       }
     }
-
-    // O = num / den; den is row 0 of the last tile (lanes with g = 0, v = 0).
+  };
+  // O = num / den for one tile; den is row 0 of the last tile (g = 0, v = 0).
+  auto finish = [&](int tt) {
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
       const float den = __shfl(acc[C::MV][nt][0], l16, 64);
@@ -525,21 +587,69 @@ __global__ __launch_bounds__(NW * 64, 2) void qapply(const uint16_t* __restrict_
       }
     }
   };
+  auto reset = [&]() {
+#pragma unroll
+    for (int i = 0; i <= C::MV; ++i)
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) M[nt] = 0.f;
+  };
 
-  const int step = NW * C::TQ;
-  Raw rA, rB;
-  int tt = q0 + wave * C::TQ;
-  if (tt < q1) qload(tt, rA);
-  if (tt + step < q1) qload(tt + step, rB);
-  for (; tt < q1; tt += 2 * step) {
-    f16x8 qa[C::NTQ][C::KS];
-    convert(rA, qa);
-    if (tt + 2 * step < q1) qload(tt + 2 * step, rA);
-    tile(tt, qa);
-    if (tt + step >= q1) break;
-    convert(rB, qa);
-    if (tt + 3 * step < q1) qload(tt + 3 * step, rB);
-    tile(tt + step, qa);
+  // Software pipeline over (tile, chunk): chunk k+1 is projected on the
+  // matrix cores while chunk k's features are formed and applied; a tile's
+  // last step projects the next tile's first chunk.
+  Raw raw;
+  Qop qcur;
+  qload(tt0, raw);
+  convert(raw, qcur);
+  if (ntile > 1) qload(tt0 + step, raw);
+  reset();
+  SArr SA, SB;
+  proj(0, qcur, SA);
+  relative(SA);
+  rebase(SA, true);
+  for (int ti = 0; ti < ntile; ++ti) {
+    const int tt = tt0 + ti * step;
+    const bool more = ti + 1 < ntile;
+    // Regular step: project chunk ch+1, apply chunk ch, check chunk ch+1.
+    auto regular = [&](const int ch, SArr& Scur, SArr& Snext) {
+      __builtin_amdgcn_sched_barrier(0);
+      proj(ch + 1, qcur, Snext);
+      apply(ch, Scur);
+      if (__builtin_expect(relative(Snext), 0)) rebase(Snext, false);
+    };
+    // Last step of a tile: project the next tile's first chunk, apply the
+    // last chunk, write the tile, start the next one.
+    auto last = [&](const int ch, SArr& Scur, SArr& Snext) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) convert(raw, qcur);   // the current tile's operands are done
+      proj(0, qcur, Snext);           // unused after the wave's last tile
+      apply(ch, Scur);
+      finish(tt);
+      reset();
+      if (more) {
+        if (ti + 2 < ntile) qload(tt + 2 * step, raw);
+        relative(Snext);
+        rebase(Snext, true);
+      }
+    };
+    int ch = 0;
+#pragma unroll 1
+    for (; ch + 2 < NCH; ch += 2) {
+      regular(ch, SA, SB);
+      regular(ch + 1, SB, SA);
+    }
+    if constexpr ((NCH % 2) == 0) {
+      regular(NCH - 2, SA, SB);
+      last(NCH - 1, SB, SA);
+    } else {
+      last(NCH - 1, SA, SB);   // the next tile's first chunk landed in SB
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < C::NTQ; ++nt) SA[mt][nt] = SB[mt][nt];
+    }
   }
 }
 
@@ -554,17 +664,20 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   kpart<D, NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg, p.nseg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  kcombine<D><<<dim3(((D + 16) * p.m + 255) / 256, p.BH), 256, 0, st>>>(P, cs, W, Kz, cfin, W16,
-                                                                        p.m, p.nseg);
+  kcombine<D><<<dim3(((D + 16) * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(P, cs, W, Kz, cfin,
+                                                                            W16, p.m, p.nseg);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = qapply_lds_bytes<D>(p.m);
+  const int nqb = (p.L + p.qblk - 1) / p.qblk;
   constexpr int NTQ = FAVOR_QAPPLY_NTQ;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&qapply<D, 4, NTQ>),
+  // m = 64 NCH; the key side runs m / FPW waves, so NCH follows from NW.
+  constexpr int NCH = NW * KCfg<D>::FPW / 64;
+  auto* kern = &qapply<D, 4, NTQ, NCH>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  const int nqb = (p.L + p.qblk - 1) / p.qblk;
-  qapply<D, 4, NTQ><<<dim3(nqb, p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.m, p.qblk);
+  kern<<<dim3(nqb, p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
   return hipGetLastError();
 }
 
