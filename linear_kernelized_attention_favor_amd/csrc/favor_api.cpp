@@ -48,8 +48,12 @@ int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype
   make_plan(B, H, L, d, m, dtype, causal, &p);
   if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  const hipError_t e = (p.path == kPathMfma) ? mfma_bidir_forward(p, Q, K, V, W, O, ws, st)
-                                             : generic_forward(p, Q, K, V, W, O, ws, st);
+  hipError_t e;
+  if (p.path == kPathMfma)
+    e = causal ? mfma_causal_forward(p, Q, K, V, W, O, ws, st)
+               : mfma_bidir_forward(p, Q, K, V, W, O, ws, st);
+  else
+    e = generic_forward(p, Q, K, V, W, O, ws, st);
   if (e != hipSuccess) return fail_hip(e);
   return FAVOR_OK;
 }
@@ -82,6 +86,23 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
     p->off_cP = off;   off = align256(off + static_cast<size_t>(m) * (d + 8) * 2);
     p->off_KV = off;   off = align256(off + BH * (d + 16) * (static_cast<size_t>(m) + 8) * 2);
     p->off_cfin = off; off = align256(off + BH * m * sizeof(float));
+    p->bytes = off;
+    return;
+  }
+  if (causal && mfma_causal_supported(d, m, dtype)) {
+    p->path = kPathMfma;
+    // Segments: about 512 scan work-groups in total, a multiple of the
+    // 32-token chunk, at least 256 tokens each.
+    int ns = (512 + p->BH - 1) / p->BH;
+    const int maxs = (L + 255) / 256;
+    ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
+    p->seg = ((L + ns - 1) / ns + 31) / 32 * 32;
+    p->nseg = (L + p->seg - 1) / p->seg;
+    p->off_T = off;    off = align256(off + BH * p->nseg * ncol * m * sizeof(float));
+    p->off_cseg = off; off = align256(off + BH * p->nseg * m * sizeof(float));
+    p->off_cP = off;   off = align256(off + BH * p->nseg * m * sizeof(float));
+    p->off_KV = off;
+    p->off_cfin = off;
     p->bytes = off;
     return;
   }

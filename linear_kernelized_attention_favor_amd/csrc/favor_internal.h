@@ -15,7 +15,7 @@ namespace favor {
 // ---------------------------------------------------------------------------
 enum Path : int32_t {
   kPathGeneric = 0,  // fp32 FMA kernels, any supported shape and dtype
-  kPathMfma = 1,     // bf16 MFMA kernels (d in {64, 128}, m % 64 == 0)
+  kPathMfma = 1,     // bf16 MFMA kernels (see mfma_*_supported)
 };
 
 struct Plan {
@@ -38,6 +38,11 @@ struct Plan {
   //   cP   [m][d+8]            W log2(e) in fp16 (query-side projection operand)
   //   KV   [BH][d+16][m+8]     combined state, bf16, query-side operand order
   //   cfin [BH][m]             combined per-feature references
+  // MFMA causal path:
+  //   T    [BH][nseg][d+1][m]  per-segment key state, then its exclusive
+  //                            prefix over earlier segments, fp32
+  //   cseg [BH][nseg][m]       per-feature references of the segment states
+  //   cP   [BH][nseg][m]       references of the prefixes (-inf: empty)
   size_t off_T, off_cseg, off_cP, off_KV, off_cfin;
   size_t bytes;
 };
@@ -54,6 +59,11 @@ hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const vo
 bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype);
 hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                               const float* W, void* O, void* ws, hipStream_t stream);
+
+// MFMA path (bf16 inputs): shape support, and the causal forward.
+bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype);
+hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, const void* V,
+                               const float* W, void* O, void* ws, hipStream_t stream);
 
 // Feature map test entry (generic fp32 arithmetic).
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,

@@ -653,6 +653,471 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
   }
 }
 
+// ---------------------------------------------------------------------------
+// Causal (masked) form, three launches:
+//   kpart    per (head, segment): the segment's key state, as above;
+//   kprefix  per head: exclusive prefix of the segment states in segment
+//            order (rescaled to a running per-feature reference), in place;
+//   cscan    per (head, segment): 32-token chunks in order, carrying the
+//            state [S | z] in registers from the prefix, with the masked
+//            in-chunk term on the matrix cores.
+// ---------------------------------------------------------------------------
+
+// kprefix: grid (ceil((D+1) m / 1024), BH), 256 threads; a thread owns four
+// features of one row.  P[bh][s] becomes the sum of segments before s and
+// cP[bh][s] its per-feature reference (-inf for the first segment).  The last
+// segment's own state is never needed, so kpart leaves it out.
+template <int D>
+__global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const float* __restrict__ cs,
+                                               float* __restrict__ cP, int m, int nseg) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int mq = m / 4;
+  if (e >= (D + 1) * mq) return;
+  const int row = e / mq, f = 4 * (e - row * mq);
+  float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 rc = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  for (int s = 0; s < nseg; ++s) {
+    const size_t ci = (static_cast<size_t>(bh) * nseg + s) * m + f;
+    float4* pp = reinterpret_cast<float4*>(P + ((static_cast<size_t>(bh) * nseg + s) * (D + 1) + row) * m + f);
+    if (row == 0) *reinterpret_cast<float4*>(cP + ci) = rc;
+    if (s + 1 == nseg) {
+      *pp = run;
+      break;
+    }
+    const float4 ts = *pp;
+    const float4 c = *reinterpret_cast<const float4*>(cs + ci);
+    *pp = run;
+    float4 nc;
+    nc.x = fmaxf(rc.x, c.x); nc.y = fmaxf(rc.y, c.y); nc.z = fmaxf(rc.z, c.z); nc.w = fmaxf(rc.w, c.w);
+    run.x = run.x * fast_exp2(rc.x - nc.x) + ts.x * fast_exp2(c.x - nc.x);
+    run.y = run.y * fast_exp2(rc.y - nc.y) + ts.y * fast_exp2(c.y - nc.y);
+    run.z = run.z * fast_exp2(rc.z - nc.z) + ts.z * fast_exp2(c.z - nc.z);
+    run.w = run.w * fast_exp2(rc.w - nc.w) + ts.w * fast_exp2(c.w - nc.w);
+    rc = nc;
+  }
+}
+
+// cscan: grid (nseg, BH), NW waves (d = 64; wave w owns features
+// [64 w, 64 w + 64)).  State per wave, in registers: st[mt][tv] with lane =
+// value column 16 tv + l16 (tv = 4: the ones column, z) and rows = features
+// 16 mt + 4 g + v; its per-feature references cref (log2 units).
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__ Q,
+                                                  const uint16_t* __restrict__ K,
+                                                  const uint16_t* __restrict__ V,
+                                                  const float* __restrict__ W,
+                                                  const float* __restrict__ P,
+                                                  const float* __restrict__ cP,
+                                                  uint16_t* __restrict__ O, int L, int m, int SEG,
+                                                  int nseg) {
+  constexpr int D = 64;
+  constexpr int NTH = NW * 64;
+  constexpr int KS = 2, NT = 4, TV = 5;
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int KCH = kTT * CPR;             // per tile and tensor
+  constexpr int KPT = (KCH + NTH - 1) / NTH;
+  constexpr int VUN = (kTT / 2) * (D / 4);
+  constexpr int VPT = (VUN + NTH - 1) / NTH;
+  constexpr int KROW = D + 8;
+  constexpr int RROW = kTT + 4;              // floats per (wave, column) row of partial outputs
+  const int s = blockIdx.x, bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int f0 = wave * 64;
+
+  __shared__ __align__(16) _Float16 Ks[2][kTT][KROW];
+  __shared__ __align__(16) _Float16 Qs[2][kTT][KROW];
+  __shared__ __align__(16) uint32_t Vt[2][D][kTT / 2 + 4];
+  __shared__ __align__(16) float Ns[2][kTT];
+  // Per wave, one region holds first this chunk's K~ over the wave's features
+  // (key rows; read only by the wave itself) and then the wave's partial
+  // outputs [column][query] (read by all after a barrier).
+  static_assert((D + 1) * RROW * 4 >= kTT * KROW * 2, "K~ tile fits the partial-output region");
+  __shared__ __align__(16) float ured[NW][(D + 1) * RROW];
+  __shared__ __align__(16) float cb[NW][64];                // per-feature references
+  __shared__ __align__(16) float fac[NW][64];               // per-feature rescale factors
+  __shared__ __align__(16) float mq[NW][kTT];               // per-wave row references
+  uint16_t* const Kt = reinterpret_cast<uint16_t*>(&ured[wave][0]);
+
+  // W' (fp16) operands of both projections: W'[f0 + 16 nt + l16][32 ks + 8 g + u].
+  f16x8 wreg[NT][KS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const float* wr = W + static_cast<size_t>(f0 + 16 * nt + l16) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float4 a = *reinterpret_cast<const float4*>(wr + 32 * ks);
+      const float4 b = *reinterpret_cast<const float4*>(wr + 32 * ks + 4);
+      f16x8 v;
+      v[0] = static_cast<_Float16>(a.x * kLog2e); v[1] = static_cast<_Float16>(a.y * kLog2e);
+      v[2] = static_cast<_Float16>(a.z * kLog2e); v[3] = static_cast<_Float16>(a.w * kLog2e);
+      v[4] = static_cast<_Float16>(b.x * kLog2e); v[5] = static_cast<_Float16>(b.y * kLog2e);
+      v[6] = static_cast<_Float16>(b.z * kLog2e); v[7] = static_cast<_Float16>(b.w * kLog2e);
+      wreg[nt][ks] = v;
+    }
+  }
+
+  // Carry-in: the prefix state of the segments before this one (none for
+  // the first segment: zero state, no reference yet).
+  f32x4 st[NT][TV];
+  float cref[NT];
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt) {
+    cref[mt] = -INFINITY;
+#pragma unroll
+    for (int tv = 0; tv < TV; ++tv) st[mt][tv] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (s > 0) {
+    const size_t pbase = (static_cast<size_t>(bh) * nseg + s) * (D + 1);
+    const size_t cbase = (static_cast<size_t>(bh) * nseg + s) * m;
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) {
+      const int f = f0 + 16 * mt + 4 * g;
+#pragma unroll
+      for (int tv = 0; tv < TV; ++tv) {
+        const int col = 16 * tv + l16;
+        if (col <= D) st[mt][tv] = *reinterpret_cast<const f32x4*>(P + (pbase + col) * m + f);
+      }
+      cref[mt] = cP[cbase + f0 + 16 * mt + l16];   // this lane's feature (S layout)
+    }
+  }
+
+  const int j0 = s * SEG, j1 = min(L, j0 + SEG);
+  const int nch = (j1 - j0 + kTT - 1) / kTT;
+  const size_t base = static_cast<size_t>(bh) * L * D;
+
+  uint4 kreg[KPT], qreg[KPT];
+  uint2 vreg[VPT][2];
+  auto gload = [&](int t) {
+    const int jt = j0 + t * kTT;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NTH;
+      const int tok = jt + c / CPR;
+      kreg[i] = make_uint4(0, 0, 0, 0);
+      qreg[i] = make_uint4(0, 0, 0, 0);
+      if (c < KCH && tok < j1) {
+        const size_t off = base + static_cast<size_t>(tok) * D + (c % CPR) * 8;
+        kreg[i] = *reinterpret_cast<const uint4*>(K + off);
+        qreg[i] = *reinterpret_cast<const uint4*>(Q + off);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * NTH;
+      const int tok = jt + 2 * (u % 16);
+      const size_t off = base + static_cast<size_t>(tok) * D + 4 * (u / 16);
+      vreg[i][0] = make_uint2(0, 0);
+      vreg[i][1] = make_uint2(0, 0);
+      if (u < VUN && tok < j1) vreg[i][0] = *reinterpret_cast<const uint2*>(V + off);
+      if (u < VUN && tok + 1 < j1) vreg[i][1] = *reinterpret_cast<const uint2*>(V + off + D);
+    }
+  };
+  auto lstore = [&](int buf, int t) {
+    const int jt = j0 + t * kTT;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + i * NTH;
+      const int j = (c / CPR) % kTT, ch = c % CPR;
+      const uint4 kv = kreg[i];
+      float ss = 0.f;
+      {
+        const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+      }
+      ss = group_sum<CPR>(ss);
+      if (c < KCH) {
+        uint4 h;
+        h.x = bf16x2_to_f16x2(kv.x); h.y = bf16x2_to_f16x2(kv.y);
+        h.z = bf16x2_to_f16x2(kv.z); h.w = bf16x2_to_f16x2(kv.w);
+        *reinterpret_cast<uint4*>(&Ks[buf][j][ch * 8]) = h;
+        const uint4 qv = qreg[i];
+        h.x = bf16x2_to_f16x2(qv.x); h.y = bf16x2_to_f16x2(qv.y);
+        h.z = bf16x2_to_f16x2(qv.z); h.w = bf16x2_to_f16x2(qv.w);
+        *reinterpret_cast<uint4*>(&Qs[buf][j][ch * 8]) = h;
+        if (ch == 0) Ns[buf][j] = (jt + j < j1) ? -0.5f * kLog2e * ss : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int u = tid + i * NTH;
+      if (u < VUN) {
+        const int col = 4 * (u / 16);
+        const int w = perm_inv(2 * (u % 16)) >> 1;
+        const uint2 a = vreg[i][0], b = vreg[i][1];
+        Vt[buf][col + 0][w] = __builtin_amdgcn_perm(b.x, a.x, 0x05040100u);
+        Vt[buf][col + 1][w] = __builtin_amdgcn_perm(b.x, a.x, 0x07060302u);
+        Vt[buf][col + 2][w] = __builtin_amdgcn_perm(b.y, a.y, 0x05040100u);
+        Vt[buf][col + 3][w] = __builtin_amdgcn_perm(b.y, a.y, 0x07060302u);
+      }
+    }
+  };
+
+  bf16x8 ones, onecol;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    ones[u] = static_cast<__bf16>(1.0f);
+    onecol[u] = static_cast<__bf16>(l16 == 0 ? 1.0f : 0.0f);   // [V | 1]'s last column
+  }
+  // B operand [V | 1] (tokens x value columns) for value-column tile tv.
+  auto vop = [&](int buf, int tv) -> bf16x8 {
+    if (tv < 4) return *reinterpret_cast<const bf16x8*>(&Vt[buf][16 * tv + l16][4 * g]);
+    return onecol;
+  };
+
+  auto chunk = [&](const int buf, const int jt) {
+    // (1) Key exponents S = K W'^T - n' (lane = feature, rows = tokens).
+    f32x4 SK[2][NT];
+    {
+      f32x4 cinit[2];
+      f16x8 ka[2][KS];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        cinit[mt] = *reinterpret_cast<const f32x4*>(&Ns[buf][16 * mt + 4 * g]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          ka[mt][ks] = *reinterpret_cast<const f16x8*>(&Ks[buf][16 * mt + l16][32 * ks + 8 * g]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            SK[mt][nt] = mma_f16(ka[mt][ks], wreg[nt][ks], ks == 0 ? cinit[mt] : SK[mt][nt]);
+    }
+    // Per-feature references: lazy raise, always on a segment with no carry.
+    bool raise = false;
+    float lm[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float c = cref[nt] == -INFINITY ? 0.f : cref[nt];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) SK[mt][nt][v] -= c;
+      const float a = max3(SK[0][nt][0], SK[0][nt][1], SK[0][nt][2]);
+      const float b = max3(SK[0][nt][3], SK[1][nt][0], SK[1][nt][1]);
+      lm[nt] = max3(a, b, fmaxf(SK[1][nt][2], SK[1][nt][3]));
+      raise |= (cref[nt] == -INFINITY) || lm[nt] > kTau;
+    }
+    if (__builtin_expect(__ballot(raise) != 0, 0)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const float tm = colmax4(lm[nt]);
+        const bool empty = cref[nt] == -INFINITY;
+        const float base_c = empty ? 0.f : cref[nt];
+        const float dlt = (empty || tm > kTau) ? tm : 0.f;
+        if (g == 0) fac[wave][16 * nt + l16] = empty ? 1.f : fast_exp2(-dlt);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) SK[mt][nt][v] -= dlt;
+        cref[nt] = base_c + dlt;
+      }
+      wave_lds_fence();
+      // The state's rows are features 16 mt + 4 g + v.
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const f32x4 fv = *reinterpret_cast<const f32x4*>(&fac[wave][16 * mt + 4 * g]);
+#pragma unroll
+        for (int tv = 0; tv < TV; ++tv) st[mt][tv] *= fv;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+      if (g == 0) cb[wave][16 * nt + l16] = cref[nt];
+    // K~ (lane = feature, 8 tokens at positions perm_of), and its transpose
+    // into Kt (key rows; features permuted within 32-blocks for the MFMA).
+    bf16x8 kb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      uint32_t p[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        p[q] = pack_bf16(fast_exp2(SK[0][nt][2 * q]), fast_exp2(SK[0][nt][2 * q + 1]));
+        p[2 + q] = pack_bf16(fast_exp2(SK[1][nt][2 * q]), fast_exp2(SK[1][nt][2 * q + 1]));
+      }
+      kb[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+      const int fl = 16 * nt + l16;                               // local feature
+      const int fc = (fl & ~31) + perm_inv(fl & 31);              // its column in Kt
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t w = p[u >> 1];
+        Kt[perm_of(8 * g + u) * KROW + fc] = static_cast<uint16_t>((u & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    }
+
+    wave_lds_fence();   // cb and K~ written above, read below by other lanes
+
+    // (2) Query exponents S^T = W' Q^T + c (lane = query, rows = features),
+    // with the wave's own row maximum as reference.
+    f32x4 SQ[NT][2];
+    {
+      f32x4 cq[NT];
+      f16x8 qa[2][KS];
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) cq[mt] = *reinterpret_cast<const f32x4*>(&cb[wave][16 * mt + 4 * g]);
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qa[nq][ks] = *reinterpret_cast<const f16x8*>(&Qs[buf][16 * nq + l16][32 * ks + 8 * g]);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt)
+#pragma unroll
+          for (int nq = 0; nq < 2; ++nq)
+            SQ[mt][nq] = mma_f16(wreg[mt][ks], qa[nq][ks], ks == 0 ? cq[mt] : SQ[mt][nq]);
+    }
+    bf16x8 qt[2][2];   // [kb][nq]: lane = query, 8 features (perm_of within 32-block kb)
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq) {
+      const float a = max3(SQ[0][nq][0], SQ[0][nq][1], SQ[0][nq][2]);
+      const float b = max3(SQ[0][nq][3], SQ[1][nq][0], SQ[1][nq][1]);
+      const float c = max3(SQ[1][nq][2], SQ[1][nq][3], SQ[2][nq][0]);
+      const float d = max3(SQ[2][nq][1], SQ[2][nq][2], SQ[2][nq][3]);
+      const float e = max3(SQ[3][nq][0], SQ[3][nq][1], SQ[3][nq][2]);
+      const float M = colmax4(max3(max3(a, b, c), max3(d, e, SQ[3][nq][3]), a));
+      if (g == 0) mq[wave][16 * nq + l16] = M;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        uint32_t p[4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          p[q] = pack_bf16(fast_exp2(SQ[2 * kb2][nq][2 * q] - M), fast_exp2(SQ[2 * kb2][nq][2 * q + 1] - M));
+          p[2 + q] = pack_bf16(fast_exp2(SQ[2 * kb2 + 1][nq][2 * q] - M),
+                               fast_exp2(SQ[2 * kb2 + 1][nq][2 * q + 1] - M));
+        }
+        qt[kb2][nq] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+      }
+    }
+
+    // (3) Partial output over the wave's features, num = Q~ [S|z] + A [V|1]
+    // (lane = value column, rows = queries); first the carried state, as bf16
+    // operands.
+    f32x4 num[2][TV];
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq)
+#pragma unroll
+      for (int tv = 0; tv < TV; ++tv) num[nq][tv] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int tv = 0; tv < TV; ++tv) {
+        const f32x4 lo = st[2 * kb2][tv], hi = st[2 * kb2 + 1][tv];
+        const bf16x8 sb = __builtin_bit_cast(
+            bf16x8, make_uint4(pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]),
+                               pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])));
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) num[nq][tv] = mma_bf16(qt[kb2][nq], sb, num[nq][tv]);
+      }
+    // (4) State update with this chunk's keys: [S|z] += K~^T [V|1].
+#pragma unroll
+    for (int tv = 0; tv < TV; ++tv) {
+      const bf16x8 vb = vop(buf, tv);
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) st[mt][tv] = mma_bf16(kb[mt], vb, st[mt][tv]);
+    }
+
+    // (5) In-chunk term A^T = K~ Q~^T over the wave's features (keys x
+    // queries), lower triangle only; masked, to bf16 as [key] operands.
+    bf16x8 ab[2];
+    {
+      f32x4 At[2][2];
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) At[mk][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int mk = 0; mk < 2; ++mk) {
+          const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kt[(16 * mk + l16) * KROW + 32 * kb2 + 8 * g]);
+#pragma unroll
+          for (int nq = mk; nq < 2; ++nq) At[mk][nq] = mma_bf16(ka, qt[kb2][nq], At[mk][nq]);
+        }
+      }
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) {
+        float x[8];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          // key 16 mk + 4 g + v against query 16 nq + l16 (the diagonal counts)
+          x[v] = (nq > 0 || 4 * g + v <= l16) ? At[0][nq][v] : 0.f;
+          x[4 + v] = (nq == 1 && 16 + 4 * g + v <= 16 + l16) ? At[1][nq][v] : 0.f;
+        }
+        ab[nq] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
+                                                       pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])));
+      }
+    }
+
+    // ... and the in-chunk term.
+#pragma unroll
+    for (int tv = 0; tv < TV; ++tv) {
+      const bf16x8 vb = vop(buf, tv);
+#pragma unroll
+      for (int nq = 0; nq < 2; ++nq) num[nq][tv] = mma_bf16(ab[nq], vb, num[nq][tv]);
+    }
+
+    wave_lds_fence();   // K~ tile read above; its region is overwritten next
+
+    // (6) Partial outputs to LDS, [wave][column][query], over the K~ tile
+    // (the wave's own step (3) is done with it).
+#pragma unroll
+    for (int nq = 0; nq < 2; ++nq)
+#pragma unroll
+      for (int tv = 0; tv < TV; ++tv) {
+        const int col = 16 * tv + l16;
+        if (col <= D) *reinterpret_cast<f32x4*>(&ured[wave][col * RROW + 16 * nq + 4 * g]) = num[nq][tv];
+      }
+    lds_barrier();
+    // Combine the waves' partials (row references differ per wave) and
+    // write O: thread -> (query, 8 columns).
+    for (int o = tid; o < kTT * (D / 8); o += NTH) {
+      const int i = o % kTT, c0 = 8 * (o / kTT);
+      float mw[NW], mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) { mw[w] = mq[w][i]; mx = fmaxf(mx, mw[w]); }
+      float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float sc = fast_exp2(mw[w] - mx);
+        den = fmaf(sc, ured[w][D * RROW + i], den);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc8[c] = fmaf(sc, ured[w][(c0 + c) * RROW + i], acc8[c]);
+      }
+      const float inv = 1.0f / den;
+      if (jt + i < j1) {
+        uint4 ov;
+        ov.x = pack_bf16(acc8[0] * inv, acc8[1] * inv);
+        ov.y = pack_bf16(acc8[2] * inv, acc8[3] * inv);
+        ov.z = pack_bf16(acc8[4] * inv, acc8[5] * inv);
+        ov.w = pack_bf16(acc8[6] * inv, acc8[7] * inv);
+        *reinterpret_cast<uint4*>(O + base + static_cast<size_t>(jt + i) * D + c0) = ov;
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0, 0);
+  for (int t = 0; t < nch; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nch) gload(t + 1);
+    lds_barrier();
+    chunk(buf, j0 + t * kTT);
+    if (t + 1 < nch) lstore(buf ^ 1, t + 1);
+  }
+}
+
 template <int D, int NW>
 hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                     const float* W, uint16_t* O, char* ws, hipStream_t st) {
@@ -681,7 +1146,52 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   return hipGetLastError();
 }
 
+template <int NW>
+hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                         const float* W, uint16_t* O, char* ws, hipStream_t st) {
+  float* P = reinterpret_cast<float*>(ws + p.off_T);
+  float* cs = reinterpret_cast<float*>(ws + p.off_cseg);
+  float* cP = reinterpret_cast<float*>(ws + p.off_cP);
+  hipError_t e;
+  if (p.nseg > 1) {
+    // Key states of every segment but the last (grid nseg - 1; the layout
+    // keeps nseg slots per head).
+    kpart<64, NW><<<dim3(p.nseg - 1, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
+                                                              p.nseg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kprefix<64><<<dim3((65 * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(P, cs, cP, p.m, p.nseg);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  cscan<NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype) {
+  return dtype == FAVOR_BF16 && d == 64 && m % 64 == 0 && m <= 256;
+}
+
+hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, const void* V,
+                               const float* W, void* O, void* ws, hipStream_t stream) {
+  const auto* q = static_cast<const uint16_t*>(Q);
+  const auto* k = static_cast<const uint16_t*>(K);
+  const auto* v = static_cast<const uint16_t*>(V);
+  auto* o = static_cast<uint16_t*>(O);
+  char* w = static_cast<char*>(ws);
+  if (p.d == 64) {
+    switch (p.m / 64) {
+      case 1: return launch_causal<1>(p, q, k, v, W, o, w, stream);
+      case 2: return launch_causal<2>(p, q, k, v, W, o, w, stream);
+      case 3: return launch_causal<3>(p, q, k, v, W, o, w, stream);
+      case 4: return launch_causal<4>(p, q, k, v, W, o, w, stream);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
 
 bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype) {
   if (dtype != FAVOR_BF16) return false;

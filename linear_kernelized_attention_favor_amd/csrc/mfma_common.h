@@ -93,5 +93,10 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Compiler-only ordering point for LDS data exchanged between the lanes of
+// one wave: a wave's LDS operations execute in issue order, so keeping the
+// compiler from moving accesses across this point is all that is needed.
+__device__ inline void wave_lds_fence() { asm volatile("" ::: "memory"); }
+
 }  // namespace mfma
 }  // namespace favor
