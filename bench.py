@@ -13,8 +13,14 @@ a device synchronisation on both sides.
 
 Prints one JSON line (rank 0 = the only rank).  Metric: tokens*heads/s of the
 forward pass at B8 H8 L4096 d64 m256 (the text-length bidirectional workload),
-with the roofline of the path and the fp64 CPU oracle timed on a bounded
-sample of the same workload beside it.
+with the roofline of the dominant kernel (its algorithmic bytes or flops per
+launch over its average duration from HIP events, in a second pass of the
+same K steps), the whole call's roofline, and the fp64 CPU oracle timed on a
+bounded sample of the same workload beside it.
+
+Measurement helpers: --copy-calibration runs a plain device copy of known size
+(the reference for the HBM byte counters); --pmc-summary DIR turns rocprofv3
+FETCH_SIZE / WRITE_SIZE passes into profiles/traffic.json.
 """
 from __future__ import annotations
 
@@ -45,6 +51,12 @@ def parse():
                     help="wall-clock budget of the CPU oracle sample")
     ap.add_argument("--cache-hot", action="store_true",
                     help="reuse one buffer set (a cache measurement, labelled as such)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain fp32 device copy of known size (the reference "
+                         "kernel that scales the HBM byte counters)")
+    ap.add_argument("--pmc-summary", metavar="DIR",
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE passes found under "
+                         "DIR/{fetch,write,copy_fetch,copy_write} into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -59,11 +71,11 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, causal: bool):
-    """HBM bytes per call from the committed rocprofv3 counter summary, or None.
+def measured_traffic(workload: str, causal: bool, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
 
-    None when no summary exists for this workload or when the kernel sources
-    changed since the counters were taken.
+    None when no summary exists for this workload and kernel, or when the
+    kernel sources changed since the counters were taken.
     """
     try:
         with open(TRAFFIC_FILE) as f:
@@ -74,7 +86,30 @@ def measured_traffic(workload: str, causal: bool):
     e = t.get(key)
     if not e or e.get("kernel_src_digest") != kernel_source_digest():
         return None
-    return e.get("bytes_per_call")
+    k = e.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
+    """Algorithmic (bytes, flops) of one launch of a kernel of the path.
+
+    The whole path moves 8 d bytes per token*head (Q, K, V read, O written
+    once) and does 8 d m flops (two projections and two m x (d+1)
+    contractions).  A key-side kernel owns the K and V reads and the key
+    projection and contraction (4 d bytes, 4 d m flops per token*head it
+    covers), a query-side kernel the Q read, O write, query projection and
+    contraction (the same), the causal scan both.  Combine and prefix kernels
+    only touch workspace: no algorithmic bytes or flops.
+    """
+    th = w.heads * w.L
+    if name == "kpart" and w.causal:
+        th = w.heads * min(w.L, (nseg - 1) * seg)     # the last segment is not summarised
+    half = (4 * w.d * elem * th, 4.0 * w.d * w.m * th)
+    if name in ("kpart", "qapply", "g_state") or (name == "g_apply" and not w.causal):
+        return half
+    if name in ("cscan",) or (name == "g_apply" and w.causal):
+        return (2 * half[0], 2 * half[1])
+    return (0, 0.0)
 
 
 def cpu_baseline(w, seconds: float):
@@ -108,8 +143,114 @@ def cpu_baseline(w, seconds: float):
                       f"{spent:.1f} s"}
 
 
+COPY_ELEMS = 1 << 28          # fp32 elements of the calibration copy (1 GiB read, 1 GiB written)
+
+
+def copy_calibration(steps: int):
+    """A plain device copy (dst = -src, fp32) of COPY_ELEMS elements, `steps` times."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_calibration": True, "bytes_read": 4 * COPY_ELEMS,
+                      "bytes_written": 4 * COPY_ELEMS, "ms": round(ms, 4),
+                      "GB_s": round(8 * COPY_ELEMS / ms / 1e6, 1)}), flush=True)
+
+
+FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "kprefix", "cscan", "g_state", "g_combine",
+                 "g_apply")
+
+
+def _pmc_rows(d):
+    """(kernel short name, counter, value) per dispatch from a rocprofv3 CSV tree."""
+    import csv
+    import glob
+    import re
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                n = r["Kernel_Name"]
+                m = re.search(r"favor::\(anonymous namespace\)::(\w+)<", n)
+                if m and m.group(1) in FAVOR_KERNELS:
+                    k = m.group(1)
+                elif "neg_kernel" in n or ("neg" in n and "elementwise" in n):
+                    k = "copy"
+                else:
+                    continue
+                out.append((k, r["Counter_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def _mean_by_kernel(rows, counter):
+    acc = {}
+    for k, c, v in rows:
+        if c == counter:
+            acc.setdefault(k, []).append(v)
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def pmc_summary(root: str, workload: str, causal: bool):
+    """Per-launch HBM bytes of each kernel, counters scaled by the copy kernel.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) come from separate passes;
+    each is multiplied by (known bytes of the calibration copy) / (what the
+    same counter reads for it), so the figures are in bytes as the copy
+    defines them.
+    """
+    fetch = _mean_by_kernel(_pmc_rows(os.path.join(root, "fetch")), "FETCH_SIZE")
+    write = _mean_by_kernel(_pmc_rows(os.path.join(root, "write")), "WRITE_SIZE")
+    cf = _mean_by_kernel(_pmc_rows(os.path.join(root, "copy_fetch")), "FETCH_SIZE")["copy"][0]
+    cw = _mean_by_kernel(_pmc_rows(os.path.join(root, "copy_write")), "WRITE_SIZE")["copy"][0]
+    f_scale = 4 * COPY_ELEMS / cf
+    w_scale = 4 * COPY_ELEMS / cw
+    kernels = {}
+    lines = [f"copy calibration: {4 * COPY_ELEMS} B read -> FETCH_SIZE {cf:.1f} "
+             f"(x{f_scale:.2f}), {4 * COPY_ELEMS} B written -> WRITE_SIZE {cw:.1f} "
+             f"(x{w_scale:.2f})",
+             f"{'kernel':10s} {'dispatches':>10s} {'FETCH_SIZE':>14s} {'WRITE_SIZE':>14s} "
+             f"{'fetch MB':>10s} {'write MB':>10s} {'total MB':>10s}"]
+    for k in FAVOR_KERNELS:
+        if k not in fetch or k not in write:
+            continue
+        fb = fetch[k][0] * f_scale
+        wb = write[k][0] * w_scale
+        kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                      "bytes_per_launch": round(fb + wb), "dispatches": fetch[k][1]}
+        lines.append(f"{k:10s} {fetch[k][1]:10d} {fetch[k][0]:14.1f} {write[k][0]:14.1f} "
+                     f"{fb / 1e6:10.2f} {wb / 1e6:10.2f} {(fb + wb) / 1e6:10.2f}")
+    key = f"{workload}{'-causal' if causal else ''}"
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        t = {}
+    t[key] = {"kernel_src_digest": kernel_source_digest(), "kernels": kernels,
+              "fetch_scale": f_scale, "write_scale": w_scale}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(t, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print("\n".join(lines), flush=True)
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.workload, args.causal)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "the forward pass is not sharded across GPUs in this build.", file=sys.stderr)
@@ -160,25 +301,49 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    # Per-kernel durations: the same K steps again, with the library
+    # recording a HIP event on `stream` before and after each of its kernel
+    # launches.  A second pass, because event records between kernels add a
+    # few microseconds of idle time per step that the whole-step figure above
+    # must not include.
+    torch.cuda.synchronize()
+    fv.timing_start()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kt = fv.timing_stop()
 
     tokens = w.heads * w.L
     value = tokens / (ms * 1e-3)
     alg_bytes = 4 * w.heads * w.L * w.d * elem                 # Q, K, V read + O written once
     alg_flops = 8.0 * w.heads * w.L * w.d * w.m
-    achieved_gbs = alg_bytes / (ms * 1e-3) / 1e9
     achieved_tflops = alg_flops / (ms * 1e-3) / 1e12
-    t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e9)
-    t_mfma = alg_flops / (BF16_PEAK_TFLOPS * 1e12)
-    bound = "hbm" if t_hbm >= t_mfma else "mfma"
-    if bound == "hbm":
-        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved_tflops / BF16_PEAK_TFLOPS, 4)}
-    tr = measured_traffic(w.name, w.causal)
-    roof["traffic"] = tr
-    roof["scope"] = "whole forward call (all kernels of one step)"
+
+    def roofline(nbytes, nflops, sec):
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        t_mfma = nflops / (BF16_PEAK_TFLOPS * 1e12)
+        if t_hbm >= t_mfma:
+            a = nbytes / sec / 1e9
+            return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(a / HBM_PEAK_GBS, 4)}
+        a = nflops / sec / 1e12
+        return {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(a / BF16_PEAK_TFLOPS, 4)}
+
+    _, nseg, seg = fv.plan_describe(w.B, w.H, w.L, w.d, w.m,
+                                    fv.BF16 if w.dtype == "bf16" else fv.F32, w.causal)
+    kernels = {}
+    for name, (tot_ms, launches) in kt.items():
+        kb, kf = kernel_work(name, w, nseg, seg, elem)
+        kernels[name] = {"avg_us": round(1e3 * tot_ms / launches, 3), "launches": launches,
+                         "alg_bytes": kb, "alg_flops": kf}
+    dom = max(kt, key=lambda n: kt[n][0])
+    dsec = kt[dom][0] / kt[dom][1] * 1e-3
+    roof = roofline(kernels[dom]["alg_bytes"], kernels[dom]["alg_flops"], dsec)
+    roof["traffic"] = measured_traffic(w.name, w.causal, dom)
+    roof["kernel"] = dom
+    roof["kernel_avg_us"] = kernels[dom]["avg_us"]
+    whole = roofline(alg_bytes, alg_flops, ms * 1e-3)
 
     out = {
         "metric": "FAVOR+ fwd tokens*heads/s + % of roofline, B8 H8 L4096 d64 m256",
@@ -199,6 +364,8 @@ def main():
         "tflops_alg": round(achieved_tflops, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
+        "roofline_whole_call": whole,
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -45,7 +45,7 @@
  *             favor_last_hip_error() (per thread).  NaN and Inf inputs are not
  *             checked; they propagate under IEEE rules.
  * Threads     Re-entrant; no global mutable state except the per-thread last
- *             HIP error.  Calls that share a workspace must be ordered on one
+ *             HIP error and the per-thread timing record (favor_timing_*).  Calls that share a workspace must be ordered on one
  *             stream.
  */
 #ifndef FAVOR_H
@@ -84,6 +84,16 @@ enum favor_status {
  */
 int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
                           int32_t dtype, int32_t causal, size_t* bytes);
+
+/*
+ * The execution plan a forward call with these arguments would use:
+ * *path = 0 (fp32 FMA kernels) or 1 (bf16 matrix-core kernels); *nseg and
+ * *seg = the number of sequence splits (bidirectional) or segments (causal)
+ * per head and their length in tokens.  Pure host function: no HIP call.
+ * Returns FAVOR_OK, a validation error or FAVOR_ERR_NULL.
+ */
+int favor_plan_describe(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                        int32_t causal, int32_t* path, int32_t* nseg, int32_t* seg);
 
 /*
  * Bidirectional FAVOR+ forward (FA-part equation of the method page):
@@ -135,6 +145,23 @@ const char* favor_status_string(int status);
 
 /* The hipError_t of this thread's last failed HIP call (0 if none). */
 int favor_last_hip_error(void);
+
+/*
+ * Per-kernel GPU time, for measurement harnesses (not part of the method).
+ * favor_timing_start() clears this host thread's record and turns recording
+ * on: every favor_fwd_bidir / favor_fwd_causal call made afterwards by this
+ * thread records a HIP event on its stream before and after each kernel it
+ * launches.  favor_timing_stop() turns recording off, waits for the recorded
+ * events, and reports up to max_kernels kernels in order of first launch:
+ * names[k] (static strings owned by the library), ms[k] (summed
+ * event-to-event milliseconds) and launches[k]; *n_kernels receives the
+ * number of distinct kernels recorded.  Events are created on first use and
+ * kept for reuse by this thread.  Returns FAVOR_OK, FAVOR_ERR_NULL (a NULL
+ * output with max_kernels > 0, or n_kernels NULL) or FAVOR_ERR_HIP.
+ */
+int favor_timing_start(void);
+int favor_timing_stop(int32_t max_kernels, const char** names, float* ms, int32_t* launches,
+                      int32_t* n_kernels);
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,9 @@ and causal, computed by hand-written HIP kernels in libfavor.so (C ABI in
 include/favor.h).  This package is the thin Python binding over that library.
 """
 from ._binding import (BF16, F32, LIB_PATH, FavorError, draw_projection, feature_map,  # noqa: F401
-                       fwd_bidir, fwd_causal, status_string, workspace_bytes)
+                       fwd_bidir, fwd_causal, plan_describe, status_string, timing_start, timing_stop,
+                       workspace_bytes)
 
 __all__ = ["fwd_bidir", "fwd_causal", "feature_map", "draw_projection", "workspace_bytes",
-           "status_string", "FavorError", "LIB_PATH", "F32", "BF16"]
+           "status_string", "plan_describe", "timing_start", "timing_stop", "FavorError", "LIB_PATH", "F32",
+           "BF16"]

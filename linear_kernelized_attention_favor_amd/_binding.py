@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 __all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
-           "feature_map", "draw_projection", "status_string", "F32", "BF16"]
+           "feature_map", "draw_projection", "status_string", "plan_describe", "timing_start", "timing_stop",
+           "F32", "BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfavor.so")
 
@@ -35,7 +36,7 @@ class FavorError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run "
-                          "python -m linear_kernelized_attention_favor_amd.build_lib")
+                          "python linear_kernelized_attention_favor_amd/build_lib.py")
     L = ctypes.CDLL(LIB_PATH)
     i32, sz, vp, fp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
     L.favor_workspace_bytes.argtypes = [i32] * 7 + [ctypes.POINTER(sz)]
@@ -52,6 +53,14 @@ def _load():
     L.favor_status_string.restype = ctypes.c_char_p
     L.favor_last_hip_error.argtypes = []
     L.favor_last_hip_error.restype = ctypes.c_int
+    L.favor_plan_describe.argtypes = [i32] * 7 + [ctypes.POINTER(i32)] * 3
+    L.favor_plan_describe.restype = ctypes.c_int
+    L.favor_timing_start.argtypes = []
+    L.favor_timing_start.restype = ctypes.c_int
+    L.favor_timing_stop.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p),
+                                    ctypes.POINTER(ctypes.c_float), ctypes.POINTER(i32),
+                                    ctypes.POINTER(i32)]
+    L.favor_timing_stop.restype = ctypes.c_int
     return L
 
 
@@ -72,6 +81,14 @@ def workspace_bytes(B, H, L, d, m, dtype=BF16, causal=False) -> int:
     _check(lib.favor_workspace_bytes(B, H, L, d, m, dtype, int(bool(causal)), ctypes.byref(out)),
            "favor_workspace_bytes")
     return out.value
+
+
+def plan_describe(B, H, L, d, m, dtype=BF16, causal=False):
+    """(path, nseg, seg) of the plan a forward call would use (favor_plan_describe)."""
+    a, b, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(lib.favor_plan_describe(B, H, L, d, m, dtype, int(bool(causal)), ctypes.byref(a),
+                                   ctypes.byref(b), ctypes.byref(c)), "favor_plan_describe")
+    return a.value, b.value, c.value
 
 
 def _shape_of(q, k, v, W):
@@ -144,3 +161,18 @@ def draw_projection(seed: int, m: int, d: int) -> np.ndarray:
     _check(lib.favor_draw_projection(ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), m, d,
                                      W.ctypes.data_as(ctypes.c_void_p)), "favor_draw_projection")
     return W
+
+
+def timing_start() -> None:
+    """Start recording per-kernel HIP events for this thread's forward calls."""
+    _check(lib.favor_timing_start(), "favor_timing_start")
+
+
+def timing_stop(max_kernels: int = 16) -> dict:
+    """Stop recording; {kernel name: (total ms, launches)} in order of first launch."""
+    names = (ctypes.c_char_p * max_kernels)()
+    ms = (ctypes.c_float * max_kernels)()
+    cnt = (ctypes.c_int32 * max_kernels)()
+    n = ctypes.c_int32(0)
+    _check(lib.favor_timing_stop(max_kernels, names, ms, cnt, ctypes.byref(n)), "favor_timing_stop")
+    return {names[k].decode(): (float(ms[k]), int(cnt[k])) for k in range(min(n.value, max_kernels))}

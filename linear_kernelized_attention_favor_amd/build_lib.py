@@ -1,6 +1,7 @@
 """Build libfavor.so in-tree with hipcc for gfx950.
 
-Usage: python -m linear_kernelized_attention_favor_amd.build_lib [-v]
+Usage: python linear_kernelized_attention_favor_amd/build_lib.py [-v]
+(this file imports nothing from the package, so it runs before a library exists)
 
 Every source under csrc/ is compiled to an object in csrc/_build/ (in
 parallel), then linked into linear_kernelized_attention_favor_amd/libfavor.so.

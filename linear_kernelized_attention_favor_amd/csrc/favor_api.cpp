@@ -30,10 +30,7 @@ int check_shape(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t d
   return FAVOR_OK;
 }
 
-int fail_hip(hipError_t e) {
-  g_last_hip_error = static_cast<int>(e);
-  return FAVOR_ERR_HIP;
-}
+int fail_hip(hipError_t e) { return record_hip_error(e); }
 
 int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
             const void* Q, const void* K, const void* V, const float* W, void* O, void* ws,
@@ -59,6 +56,11 @@ int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype
 }
 
 }  // namespace
+
+int record_hip_error(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return FAVOR_ERR_HIP;
+}
 
 void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                int32_t causal, Plan* p) {
@@ -131,6 +133,19 @@ int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
   favor::Plan p;
   favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p);
   *bytes = p.bytes;
+  return FAVOR_OK;
+}
+
+int favor_plan_describe(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                        int32_t causal, int32_t* path, int32_t* nseg, int32_t* seg) {
+  const int st = favor::check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  if (!path || !nseg || !seg) return FAVOR_ERR_NULL;
+  favor::Plan p;
+  favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p);
+  *path = p.path;
+  *nseg = p.nseg;
+  *seg = p.seg;
   return FAVOR_OK;
 }
 

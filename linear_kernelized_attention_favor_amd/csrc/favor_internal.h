@@ -65,6 +65,15 @@ bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype);
 hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, const void* V,
                                const float* W, void* O, void* ws, hipStream_t stream);
 
+// Measurement hooks behind favor_timing_*: each kernel launch is bracketed
+// by timing_before / timing_after (no-ops unless this thread is recording).
+// `kernel` must be a string literal.
+void timing_before(hipStream_t st);
+void timing_after(hipStream_t st, const char* kernel);
+
+// Records a failed HIP call for favor_last_hip_error(); returns FAVOR_ERR_HIP.
+int record_hip_error(hipError_t e);
+
 // Feature map test entry (generic fp32 arithmetic).
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
                                const void* X, const float* W, float* Xp, hipStream_t stream);

@@ -405,23 +405,30 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
   float* cP = reinterpret_cast<float*>(ws + p.off_cP);
   float* KV = reinterpret_cast<float*>(ws + p.off_KV);
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
+  timing_before(st);
   g_state<T><<<dim3(p.nseg, (p.m + kFB - 1) / kFB, p.BH), kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.d,
                                                                   p.m, p.seg, p.nseg);
   hipError_t e = hipGetLastError();
+  timing_after(st, "g_state");
   if (e != hipSuccess) return e;
   const int nent = p.m * (p.d + 1);
+  timing_before(st);
   g_combine<<<dim3((nent + kThreads - 1) / kThreads, p.BH), kThreads, 0, st>>>(
       Tst, cseg, cP, KV, cfin, p.nseg, p.m, p.d, p.causal);
   e = hipGetLastError();
+  timing_after(st, "g_combine");
   if (e != hipSuccess) return e;
   const dim3 ga((p.L + kTT - 1) / kTT, p.BH);
+  timing_before(st);
   if (p.causal)
     g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, Tst, cP, cseg, O, p.L, p.d, p.m, p.seg,
                                         p.nseg, 1);
   else
     g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, KV, cfin, nullptr, O, p.L, p.d, p.m, p.seg,
                                         p.nseg, 0);
-  return hipGetLastError();
+  e = hipGetLastError();
+  timing_after(st, "g_apply");
+  return e;
 }
 
 }  // namespace

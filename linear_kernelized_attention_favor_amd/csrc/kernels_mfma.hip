@@ -1126,12 +1126,16 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   uint16_t* Kz = reinterpret_cast<uint16_t*>(ws + p.off_KV);
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   _Float16* W16 = reinterpret_cast<_Float16*>(ws + p.off_cP);
+  timing_before(st);
   kpart<D, NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg, p.nseg);
   hipError_t e = hipGetLastError();
+  timing_after(st, "kpart");
   if (e != hipSuccess) return e;
+  timing_before(st);
   kcombine<D><<<dim3(((D + 16) * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(P, cs, W, Kz, cfin,
                                                                             W16, p.m, p.nseg);
   e = hipGetLastError();
+  timing_after(st, "kcombine");
   if (e != hipSuccess) return e;
   const size_t lds = qapply_lds_bytes<D>(p.m);
   const int nqb = (p.L + p.qblk - 1) / p.qblk;
@@ -1142,8 +1146,11 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
+  timing_before(st);
   kern<<<dim3(nqb, p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
-  return hipGetLastError();
+  e = hipGetLastError();
+  timing_after(st, "qapply");
+  return e;
 }
 
 template <int NW>
@@ -1156,16 +1163,23 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
   if (p.nseg > 1) {
     // Key states of every segment but the last (grid nseg - 1; the layout
     // keeps nseg slots per head).
+    timing_before(st);
     kpart<64, NW><<<dim3(p.nseg - 1, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
                                                               p.nseg);
     e = hipGetLastError();
+    timing_after(st, "kpart");
     if (e != hipSuccess) return e;
+    timing_before(st);
     kprefix<64><<<dim3((65 * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(P, cs, cP, p.m, p.nseg);
     e = hipGetLastError();
+    timing_after(st, "kprefix");
     if (e != hipSuccess) return e;
   }
+  timing_before(st);
   cscan<NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg);
-  return hipGetLastError();
+  e = hipGetLastError();
+  timing_after(st, "cscan");
+  return e;
 }
 
 }  // namespace

@@ -15,5 +15,9 @@ def pytest_sessionstart(session):
     # Load what is built; build only if nothing is (the library is git-ignored).
     lib = os.path.join(ROOT, "linear_kernelized_attention_favor_amd", "libfavor.so")
     if not os.path.exists(lib):
-        from linear_kernelized_attention_favor_amd import build_lib
-        build_lib.build()
+        import importlib.util
+        path = os.path.join(ROOT, "linear_kernelized_attention_favor_amd", "build_lib.py")
+        spec = importlib.util.spec_from_file_location("favor_build_lib", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()

@@ -108,6 +108,8 @@ SHAPES = [
     (1, 1, 600, 128, 1024),
     (1, 3, 1000, 64, 128),
     (1, 1, 4097, 16, 64),
+    (1, 1, 2049, 64, 64),     # causal: nine segments, the last one token long
+    (2, 2, 333, 64, 192),
 ]
 
 
@@ -262,3 +264,27 @@ def test_redraw_changes_output_consistently(fv):
         assert oracle.row_rel_err(_np64(out), _ref(False, q, k, v, W)) <= TOL["bf16"]
         outs.append(_np64(out))
     assert np.max(np.abs(outs[0] - outs[1])) > 1e-3
+
+
+def test_kernel_timing_records_each_launch(fv):
+    w = workloads.workload("text_causal").with_(B=1, H=4, L=3000)
+    q, k, v = workloads.host_qkv(w)
+    Wd = torch.from_numpy(_w(w.seed_w, w.m, w.d)).cuda()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    for causal, names in ((False, {"kpart", "kcombine", "qapply"}),
+                          (True, {"kpart", "kprefix", "cscan"})):
+        fwd = fv.fwd_causal if causal else fv.fwd_bidir
+        fwd(qd, kd, vd, Wd)
+        torch.cuda.synchronize()
+        fv.timing_start()
+        for _ in range(3):
+            fwd(qd, kd, vd, Wd)
+        rec = fv.timing_stop()
+        assert set(rec) == names, rec
+        for name, (ms, launches) in rec.items():
+            assert launches == 3 and 0.0 < ms < 1e3, (name, ms, launches)
+    # Recording is off after stop: later calls add nothing.
+    fv.fwd_bidir(qd, kd, vd, Wd)
+    torch.cuda.synchronize()
+    fv.timing_start()
+    assert fv.timing_stop() == {}

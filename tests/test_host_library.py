@@ -149,3 +149,31 @@ def test_draw_is_deterministic_and_seed_dependent():
     a = fv.draw_projection(3, 32, 16)
     np.testing.assert_array_equal(a, fv.draw_projection(3, 32, 16))
     assert not np.array_equal(a, fv.draw_projection(4, 32, 16))
+
+
+def test_plan_describe():
+    # Matrix-core path for the bf16 workloads, segments that tile the sequence.
+    for (B, H, L, d, m, causal) in [(8, 8, 4096, 64, 256, 0), (8, 8, 4096, 64, 256, 1),
+                                    (1, 16, 32768, 64, 256, 1), (1, 3, 1000, 64, 128, 1),
+                                    (2, 1, 255, 64, 256, 1)]:
+        path, nseg, seg = fv.plan_describe(B, H, L, d, m, fv.BF16, causal)
+        assert path == 1
+        assert seg % 32 == 0 and nseg == -(-L // seg) and (nseg - 1) * seg < L
+    # fp32 and shapes outside the matrix-core kernels take the generic path.
+    assert fv.plan_describe(1, 1, 256, 16, 16, fv.F32, 0)[0] == 0
+    assert fv.plan_describe(1, 1, 256, 64, 48, fv.BF16, 1)[0] == 0
+    with pytest.raises(fv.FavorError):
+        fv.plan_describe(1, 1, 0, 64, 64)
+    i = ctypes.c_int32()
+    assert lib.favor_plan_describe(1, 1, 16, 64, 64, 1, 0, None, ctypes.byref(i),
+                                   ctypes.byref(i)) == ENULL
+
+
+def test_timing_record_without_calls():
+    # Start/stop with no forward call in between records nothing and needs no GPU.
+    fv.timing_start()
+    assert fv.timing_stop() == {}
+    n = ctypes.c_int32(7)
+    assert lib.favor_timing_stop(0, None, None, None, ctypes.byref(n)) == OK and n.value == 0
+    assert lib.favor_timing_stop(4, None, None, None, ctypes.byref(n)) == ENULL
+    assert lib.favor_timing_stop(0, None, None, None, None) == ENULL
