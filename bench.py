@@ -170,19 +170,30 @@ FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "kprefix", "cscan", "g_state", "
                  "g_apply")
 
 
+def _favor_kernel(name: str):
+    """Short name of a libfavor kernel from a demangled or mangled symbol, else None."""
+    import re
+    m = re.search(r"favor::\(anonymous namespace\)::(\w+)<", name)
+    if m:
+        k = m.group(1)
+    else:   # _ZN5favor12_GLOBAL__N_1<len><name>I...
+        m = re.search(r"_ZN5favor12_GLOBAL__N_1(\d+)", name)
+        k = name[m.end():m.end() + int(m.group(1))] if m else None
+    return k if k in FAVOR_KERNELS else None
+
+
 def _pmc_rows(d):
     """(kernel short name, counter, value) per dispatch from a rocprofv3 CSV tree."""
     import csv
     import glob
-    import re
     out = []
     for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
         with open(f) as fh:
             for r in csv.DictReader(fh):
                 n = r["Kernel_Name"]
-                m = re.search(r"favor::\(anonymous namespace\)::(\w+)<", n)
-                if m and m.group(1) in FAVOR_KERNELS:
-                    k = m.group(1)
+                k = _favor_kernel(n)
+                if k:
+                    pass
                 elif "neg_kernel" in n or ("neg" in n and "elementwise" in n):
                     k = "copy"
                 else:

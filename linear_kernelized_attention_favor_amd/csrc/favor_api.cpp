@@ -72,9 +72,11 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
   size_t off = 0;
   if (!causal && mfma_bidir_supported(d, m, dtype)) {
     p->path = kPathMfma;
-    // Splits: about 512 key-side work-groups in total, at least 128 tokens each.
-    int ns = (512 + p->BH - 1) / p->BH;
-    const int maxs = (L + 127) / 128;
+    // Splits: about 512 key-side token groups in total (one or two per
+    // work-group), at least 128 tokens per group.
+    const int tg = mfma_bidir_token_groups(d, m);
+    int ns = (512 / tg + p->BH - 1) / p->BH;
+    const int maxs = (L + 128 * tg - 1) / (128 * tg);
     ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
     p->seg = ((L + ns - 1) / ns + 31) / 32 * 32;
     p->nseg = (L + p->seg - 1) / p->seg;

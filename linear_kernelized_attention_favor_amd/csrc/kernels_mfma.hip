@@ -73,28 +73,49 @@ struct KCfg {
 // [w FPW, (w+1) FPW).  Output: P [BH][nsplit][D+1][m] fp32 (row D = z) and
 // cs [BH][nsplit][m] fp32 (per-feature references, log2 units).
 // ---------------------------------------------------------------------------
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__ K,
+// TG token groups of NW waves each: group gi takes the split's tiles gi,
+// gi + TG, ... (every group runs the same number of steps; tiles past the
+// split are masked), and the groups' states are merged through LDS at the
+// end.  More groups per work-group mean fewer, longer splits for the same
+// number of waves, hence fewer partial states to write and combine.
+template <int D, int NW, int TG>
+struct KLds {
+  using C = KCfg<D>;
+  static constexpr int KS_BYTES = 3 * kTT * C::KROW * 2;
+  static constexpr int VT_BYTES = 3 * D * (C::VROW / 2) * 4;
+  static constexpr int NS_BYTES = 3 * kTT * 4;
+  static constexpr int RING = KS_BYTES + VT_BYTES + NS_BYTES;
+  static constexpr int M = NW * C::FPW;                          // features
+  static constexpr int XCH = (TG > 1) ? ((D + 1) * M + M) * 4 : 0;   // state + references
+  static constexpr int BYTES = (TG * RING > XCH) ? TG * RING : XCH;
+};
+
+template <int D, int NW, int TG>
+__global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V,
                                                  const float* __restrict__ W,
                                                  float* __restrict__ P, float* __restrict__ cs,
                                                  int L, int m, int SL, int nsplit) {
   using C = KCfg<D>;
-  constexpr int NTH = NW * 64;
+  using LD = KLds<D, NW, TG>;
+  constexpr int NTH = NW * 64;               // threads per token group
   constexpr int KCH = kTT * D / 8;           // 16-byte K chunks per tile
   constexpr int KPT = (KCH + NTH - 1) / NTH;
   constexpr int VUN = (kTT / 2) * (D / 4);   // (token pair, 4-column group) units per tile
   constexpr int VPT = (VUN + NTH - 1) / NTH;
   const int s = blockIdx.x, bh = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = threadIdx.x / NTH;
+  const int tid = threadIdx.x % NTH, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int f0 = wave * C::FPW;
 
-  // Three-stage ring: tile t's V^T, tile t+1's K (projection running ahead)
-  // and tile t+2 being written.
-  __shared__ __align__(16) _Float16 Ks[3][kTT][C::KROW];
-  __shared__ __align__(16) uint32_t Vt[3][D][C::VROW / 2];   // bf16 pairs, token order perm_of
-  __shared__ __align__(16) float Ns[3][kTT];                 // -|k|^2 log2(e) / 2 per token
+  // Per group, a three-stage ring: tile t's V^T, tile t+1's K (projection
+  // running ahead) and tile t+2 being written.
+  __shared__ __align__(16) unsigned char kp_smem[LD::BYTES];
+  unsigned char* const ring = kp_smem + grp * LD::RING;
+  auto Ks = reinterpret_cast<_Float16(*)[kTT][C::KROW]>(ring);
+  auto Vt = reinterpret_cast<uint32_t(*)[D][C::VROW / 2]>(ring + LD::KS_BYTES);   // bf16 pairs
+  auto Ns = reinterpret_cast<float(*)[kTT]>(ring + LD::KS_BYTES + LD::VT_BYTES);  // -|k|^2 log2e/2
 
   // Projection B operands, kept in registers: W'[f][32 ks + 8 g + u].
   f16x8 wb[C::NT][C::KS];
@@ -124,15 +145,17 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
   for (int nt = 0; nt < C::NT; ++nt) cref[nt] = 0.f;
 
   const int j0 = s * SL, j1 = min(L, j0 + SL);
-  const int ntiles = (j1 - j0 + kTT - 1) / kTT;
+  // Steps per group (the group's tile t is the split's tile t TG + grp).
+  const int ntiles = ((j1 - j0 + kTT - 1) / kTT + TG - 1) / TG;
   const size_t base = static_cast<size_t>(bh) * L * D;
+  auto tile0 = [&](int t) { return j0 + (t * TG + grp) * kTT; };
 
   // Global loads of tile t+3 are in flight while tile t is consumed.  Loads
   // past the split read nothing and stage zeros.
   uint4 kreg[KPT];
   uint2 vreg[VPT][2];
   auto gload = [&](int t) {
-    const int jt = j0 + t * kTT;
+    const int jt = tile0(t);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NTH;
@@ -154,7 +177,7 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
     }
   };
   auto lstore = [&](int buf, int t) {
-    const int jt = j0 + t * kTT;
+    const int jt = tile0(t);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NTH;
@@ -244,7 +267,8 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
       const float tm = colmax4(lm[nt]);
-      const float dlt = (first || tm > kTau) ? tm : 0.f;
+      // (a group whose first tile lies past the split keeps a finite reference)
+      const float dlt = first ? (tm == -INFINITY ? 0.f : tm) : (tm > kTau ? tm : 0.f);
       if (!first) {   // accumulators are still zero on the first tile
         const float f = fast_exp2(-dlt);
 #pragma unroll
@@ -311,6 +335,49 @@ __global__ __launch_bounds__(NW * 64, 2) void kpart(const uint16_t* __restrict__
     step(t, SA, SB);
     if (t + 1 >= ntiles) break;
     step(t + 1, SB, SA);
+  }
+
+  if constexpr (TG > 1) {
+    // Merge the groups' states into group 0's registers through LDS, one
+    // group at a time, each rescaled to the larger of the two references.
+    float* const xs = reinterpret_cast<float*>(kp_smem);      // [D+1][M]
+    float* const xc = xs + (D + 1) * LD::M;                   // [M]
+    for (int src = 1; src < TG; ++src) {
+      __syncthreads();
+      if (grp == src) {
+        const bool empty = tile0(0) >= j1;   // the group saw no token of the split
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+          const int f = f0 + 16 * nt + l16;
+#pragma unroll
+          for (int mv = 0; mv < C::MV; ++mv)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) xs[(16 * mv + 4 * g + v) * LD::M + f] = acc[mv][nt][v];
+          if (g == 0) {
+            xs[D * LD::M + f] = acc[C::MV][nt][0];
+            xc[f] = empty ? -INFINITY : cref[nt];
+          }
+        }
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+          const int f = f0 + 16 * nt + l16;
+          const float co = xc[f];
+          const float cn = fmaxf(cref[nt], co);
+          const float a = fast_exp2(cref[nt] - cn), b = fast_exp2(co - cn);
+#pragma unroll
+          for (int mv = 0; mv < C::MV; ++mv)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              acc[mv][nt][v] = acc[mv][nt][v] * a + xs[(16 * mv + 4 * g + v) * LD::M + f] * b;
+          acc[C::MV][nt][0] = acc[C::MV][nt][0] * a + xs[D * LD::M + f] * b;
+          cref[nt] = cn;
+        }
+      }
+    }
+    if (grp != 0) return;
   }
 
   // Partial state out: P[bh][s][row][f].
@@ -388,8 +455,8 @@ __global__ __launch_bounds__(256) void kcombine(const float* __restrict__ P,
 }
 
 // ---------------------------------------------------------------------------
-// qapply: grid (nqb, BH), NW waves; each wave takes 16*NTQ-token tiles of the
-// block [qb QL, (qb+1) QL).  LDS: W' fp16 [m][D+8], Kz bf16 [D+16][m+8],
+// qapply: grid (nqb * BH) in XCD-major item order, NW waves; each wave takes
+// 16*NTQ-token tiles of the block [qb QL, (qb+1) QL).  LDS: W' fp16 [m][D+8], Kz bf16 [D+16][m+8],
 // c [m] fp32 (dynamic).
 // ---------------------------------------------------------------------------
 template <int D, int NTQ_>
@@ -422,7 +489,10 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
   uint16_t* Kzl = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(m) * C::WROW * 2);
   float* cl = reinterpret_cast<float*>(smem + static_cast<size_t>(m) * C::WROW * 2 +
                                        static_cast<size_t>(D + 16) * kzrow * 2);
-  const int qb = blockIdx.x, bh = blockIdx.y;
+  // 1-D grid of (head, query block) items, one head's blocks on one XCD.
+  const int nqb = (L + QL - 1) / QL;
+  const int item = xcd_major(blockIdx.x, gridDim.x);
+  const int qb = item % nqb, bh = item / nqb;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
 
@@ -1127,7 +1197,10 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   _Float16* W16 = reinterpret_cast<_Float16*>(ws + p.off_cP);
   timing_before(st);
-  kpart<D, NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg, p.nseg);
+  // Two token groups while a work-group stays within 8 waves (two per SIMD).
+  constexpr int TG = (NW <= 4) ? 2 : 1;
+  kpart<D, NW, TG><<<dim3(p.nseg, p.BH), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
+                                                                p.nseg);
   hipError_t e = hipGetLastError();
   timing_after(st, "kpart");
   if (e != hipSuccess) return e;
@@ -1147,7 +1220,7 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   timing_before(st);
-  kern<<<dim3(nqb, p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
+  kern<<<dim3(nqb * p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
   e = hipGetLastError();
   timing_after(st, "qapply");
   return e;
@@ -1164,8 +1237,8 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     // Key states of every segment but the last (grid nseg - 1; the layout
     // keeps nseg slots per head).
     timing_before(st);
-    kpart<64, NW><<<dim3(p.nseg - 1, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
-                                                              p.nseg);
+    kpart<64, NW, 1><<<dim3(p.nseg - 1, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
+                                                                 p.seg, p.nseg);
     e = hipGetLastError();
     timing_after(st, "kpart");
     if (e != hipSuccess) return e;
@@ -1205,6 +1278,11 @@ hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, cons
     }
   }
   return hipErrorInvalidValue;
+}
+
+int mfma_bidir_token_groups(int32_t d, int32_t m) {
+  const int nw = m / KCfg<64>::FPW;   // key-side waves per token group at d = 64
+  return (d == 64 ? nw : m / KCfg<128>::FPW) <= 4 ? 2 : 1;
 }
 
 bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype) {

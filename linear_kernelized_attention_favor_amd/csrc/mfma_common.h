@@ -93,6 +93,15 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Work-group order across the chip's 8 accelerator dies (XCDs, each with its
+// own L2): the dispatcher hands linear work-group i to XCD i % 8.  Mapping
+// i to the work item (i % 8) (n / 8) + i / 8 gives every XCD a consecutive
+// run of items, so items that read the same data (the query blocks of one
+// head) share one L2.  Identity when n is not a multiple of 8.
+__device__ inline int xcd_major(int i, int n) {
+  return (n % 8) ? i : (i % 8) * (n / 8) + i / 8;
+}
+
 // Compiler-only ordering point for LDS data exchanged between the lanes of
 // one wave: a wave's LDS operations execute in issue order, so keeping the
 // compiler from moving accesses across this point is all that is needed.
