@@ -93,18 +93,19 @@ def measured_traffic(workload: str, causal: bool, kernel: str):
 def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     """Algorithmic (bytes, flops) of one launch of a kernel of the path.
 
-    The whole path moves 8 d bytes per token*head (Q, K, V read, O written
-    once) and does 8 d m flops (two projections and two m x (d+1)
-    contractions).  A key-side kernel owns the K and V reads and the key
-    projection and contraction (4 d bytes, 4 d m flops per token*head it
-    covers), a query-side kernel the Q read, O write, query projection and
-    contraction (the same), the causal scan both.  Combine and prefix kernels
-    only touch workspace: no algorithmic bytes or flops.
+    The whole path moves 4 d elements per token*head (Q, K, V read, O
+    written once: 8 d bytes in bf16) and does 8 d m flops (two projections
+    and two m x (d+1) contractions).  A key-side kernel owns the K and V
+    reads and the key projection and contraction (2 d elements, 4 d m flops
+    per token*head it covers), a query-side kernel the Q read, O write,
+    query projection and contraction (the same), the causal scan both.
+    Combine and prefix kernels only touch workspace: no algorithmic bytes or
+    flops.
     """
     th = w.heads * w.L
     if name == "kpart" and w.causal:
         th = w.heads * min(w.L, (nseg - 1) * seg)     # the last segment is not summarised
-    half = (4 * w.d * elem * th, 4.0 * w.d * w.m * th)
+    half = (2 * w.d * elem * th, 4.0 * w.d * w.m * th)
     if name in ("kpart", "qapply", "g_state") or (name == "g_apply" and not w.causal):
         return half
     if name in ("cscan",) or (name == "g_apply" and w.causal):
