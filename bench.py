@@ -106,7 +106,7 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     if name == "kpart" and w.causal:
         th = w.heads * min(w.L, (nseg - 1) * seg)     # the last segment is not summarised
     half = (2 * w.d * elem * th, 4.0 * w.d * w.m * th)
-    if name in ("kpart", "qapply", "g_state") or (name == "g_apply" and not w.causal):
+    if name in ("kpart", "qapply", "qstream", "g_state") or (name == "g_apply" and not w.causal):
         return half
     if name in ("cscan",) or (name == "g_apply" and w.causal):
         return (2 * half[0], 2 * half[1])
@@ -167,8 +167,8 @@ def copy_calibration(steps: int):
                       "GB_s": round(8 * COPY_ELEMS / ms / 1e6, 1)}), flush=True)
 
 
-FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "kprefix", "cscan", "g_state", "g_combine",
-                 "g_apply")
+FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "g_state",
+                 "g_combine", "g_apply")
 
 
 def _favor_kernel(name: str):

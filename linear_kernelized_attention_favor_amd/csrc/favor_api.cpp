@@ -73,16 +73,20 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
   if (!causal && mfma_bidir_supported(d, m, dtype)) {
     p->path = kPathMfma;
     // Splits: about 512 key-side token groups in total (one or two per
-    // work-group), at least 128 tokens per group.
+    // work-group, times the feature blocks), at least 128 tokens per group.
     const int tg = mfma_bidir_token_groups(d, m);
-    int ns = (512 / tg + p->BH - 1) / p->BH;
+    const int nfb = mfma_bidir_feature_blocks(d, m);
+    int ns = (512 / (tg * nfb) + p->BH - 1) / p->BH;
     const int maxs = (L + 128 * tg - 1) / (128 * tg);
     ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
     p->seg = ((L + ns - 1) / ns + 31) / 32 * 32;
     p->nseg = (L + p->seg - 1) / p->seg;
-    // Query blocks: about 512 work-groups, a multiple of 64 tokens, >= 256.
-    const int64_t want = (static_cast<int64_t>(L) * p->BH + 511) / 512;
-    int64_t qb = (want + 63) / 64 * 64;
+    // Query blocks: about 512 work-groups of 4 waves (qapply) or 256 of 8
+    // (qstream, one per compute unit); a multiple of 64 (256) tokens.
+    const bool stream = mfma_bidir_streams_queries(d, m);
+    const int64_t nwg = stream ? 256 : 512, unit = stream ? 256 : 64;
+    const int64_t want = (static_cast<int64_t>(L) * p->BH + nwg - 1) / nwg;
+    int64_t qb = (want + unit - 1) / unit * unit;
     if (qb < 256) qb = 256;
     p->qblk = static_cast<int32_t>(qb);
     p->off_T = off;    off = align256(off + BH * p->nseg * ncol * m * sizeof(float));

@@ -57,8 +57,12 @@ hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const vo
 
 // MFMA path (bf16 inputs): shape support, and the bidirectional forward.
 bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype);
-// Token groups per key-side work-group of the bidirectional MFMA path.
+// Key-side token groups per work-group and feature blocks of the
+// bidirectional MFMA path, and whether its query side streams the features
+// through LDS (qstream) instead of holding them (qapply).
 int mfma_bidir_token_groups(int32_t d, int32_t m);
+int mfma_bidir_feature_blocks(int32_t d, int32_t m);
+bool mfma_bidir_streams_queries(int32_t d, int32_t m);
 hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                               const float* W, void* O, void* ws, hipStream_t stream);
 

@@ -32,6 +32,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "favor.h"
 #include "favor_internal.h"
@@ -69,9 +70,10 @@ struct KCfg {
 };
 
 // ---------------------------------------------------------------------------
-// kpart: grid (nsplit, BH), NW waves of 64 threads, wave w owns features
-// [w FPW, (w+1) FPW).  Output: P [BH][nsplit][D+1][m] fp32 (row D = z) and
-// cs [BH][nsplit][m] fp32 (per-feature references, log2 units).
+// kpart: grid (nsplit, BH, m / (NW FPW)), TG x NW waves of 64 threads; wave
+// w of feature block z owns features [(z NW + w) FPW, (z NW + w + 1) FPW).
+// Output: P [BH][nsplit][D+1][m] fp32 (row D = z) and cs [BH][nsplit][m]
+// fp32 (per-feature references, log2 units).
 // ---------------------------------------------------------------------------
 // TG token groups of NW waves each: group gi takes the split's tiles gi,
 // gi + TG, ... (every group runs the same number of steps; tiles past the
@@ -104,10 +106,14 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   constexpr int VUN = (kTT / 2) * (D / 4);   // (token pair, 4-column group) units per tile
   constexpr int VPT = (VUN + NTH - 1) / NTH;
   const int s = blockIdx.x, bh = blockIdx.y;
-  const int grp = threadIdx.x / NTH;
+  // (wave-uniform: tells the compiler that per-group values are scalar)
+  const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / NTH);
   const int tid = threadIdx.x % NTH, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int f0 = wave * C::FPW;
+  // Feature block blockIdx.z: features [z NW FPW, (z+1) NW FPW) (several
+  // blocks when m needs more than 8 waves); f0 is global, fl0 block-local.
+  const int fl0 = wave * C::FPW;
+  const int f0 = static_cast<int>(blockIdx.z) * LD::M + fl0;
 
   // Per group, a three-stage ring: tile t's V^T, tile t+1's K (projection
   // running ahead) and tile t+2 being written.
@@ -150,30 +156,34 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   const size_t base = static_cast<size_t>(bh) * L * D;
   auto tile0 = [&](int t) { return j0 + (t * TG + grp) * kTT; };
 
-  // Global loads of tile t+3 are in flight while tile t is consumed.  Loads
-  // past the split read nothing and stage zeros.
+  // Global loads of tile t+3 are issued at the start of step t and consumed
+  // at the start of step t+1.  Buffer loads past the split's end return
+  // zeros (the tail needs no per-lane branch); per-thread byte offsets
+  // within a tile are fixed.
   uint4 kreg[KPT];
   uint2 vreg[VPT][2];
+  int kvo[KPT], vvo[VPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int c = tid + i * NTH;
+    kvo[i] = (c < KCH) ? ((c / C::CPR) * D + (c % C::CPR) * 8) * 2 : kBufOff;
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int u = tid + i * NTH;
+    vvo[i] = (u < VUN) ? (2 * (u % 16) * D + 4 * (u / 16)) * 2 : kBufOff;
+  }
   auto gload = [&](int t) {
     const int jt = tile0(t);
+    const int bytes = max(0, j1 - jt) * D * 2;
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(K + base + static_cast<size_t>(jt) * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(V + base + static_cast<size_t>(jt) * D, bytes);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NTH;
-      const int tok = jt + c / C::CPR;
-      kreg[i] = make_uint4(0, 0, 0, 0);
-      if (c < KCH && tok < j1)
-        kreg[i] = *reinterpret_cast<const uint4*>(K + base + static_cast<size_t>(tok) * D +
-                                                  (c % C::CPR) * 8);
-    }
+    for (int i = 0; i < KPT; ++i) kreg[i] = buffer_load16(rk, kvo[i]);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int u = tid + i * NTH;
-      const int tok = jt + 2 * (u % 16);
-      const size_t off = base + static_cast<size_t>(tok) * D + 4 * (u / 16);
-      vreg[i][0] = make_uint2(0, 0);
-      vreg[i][1] = make_uint2(0, 0);
-      if (u < VUN && tok < j1) vreg[i][0] = *reinterpret_cast<const uint2*>(V + off);
-      if (u < VUN && tok + 1 < j1) vreg[i][1] = *reinterpret_cast<const uint2*>(V + off + D);
+      vreg[i][0] = buffer_load8(rv, vvo[i]);
+      vreg[i][1] = buffer_load8(rv, vvo[i] + D * 2);
     }
   };
   auto lstore = [&](int buf, int t) {
@@ -319,22 +329,38 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   relative(SA, lm);
   rebase(SA, lm, true);
 
-  // Iteration t: project tile t+1 while tile t's features are formed, then
-  // contract tile t, stage tile t+2, load tile t+3, and check tile t+1.
-  auto step = [&](int t, SArr& Scur, SArr& Snext) {
+  // Step t: stage tile t+2 (loaded during step t-1), load tile t+3, project
+  // tile t+1 while tile t's features are formed, contract tile t, and check
+  // tile t+1.
+  // The loop body holds six steps (the ring's period 3 times the S double
+  // buffer's period 2), so every ring slot is a compile-time constant and
+  // LDS addresses fold into the instructions' offsets.
+  auto step = [&](auto R, int t, SArr& Scur, SArr& Snext) {
+    constexpr int r = decltype(R)::value;
     bf16x8 kb[C::NT];
-    proj((t + 1) % 3, Snext);
-    features(Scur, kb);
-    contract(t % 3, kb);
-    lstore((t + 2) % 3, t + 2);
+    lstore((r + 2) % 3, t + 2);
     gload(t + 3);
+    proj((r + 1) % 3, Snext);
+    features(Scur, kb);
+    contract(r % 3, kb);
     if (__builtin_expect(relative(Snext, lm), 0)) rebase(Snext, lm, false);
     lds_barrier();
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, SA, SB);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  for (int t = 0; t < ntiles; t += 6) {
+    step(I0{}, t, SA, SB);
     if (t + 1 >= ntiles) break;
-    step(t + 1, SB, SA);
+    step(I1{}, t + 1, SB, SA);
+    if (t + 2 >= ntiles) break;
+    step(I2{}, t + 2, SA, SB);
+    if (t + 3 >= ntiles) break;
+    step(I0{}, t + 3, SB, SA);
+    if (t + 4 >= ntiles) break;
+    step(I1{}, t + 4, SA, SB);
+    if (t + 5 >= ntiles) break;
+    step(I2{}, t + 5, SB, SA);
   }
 
   if constexpr (TG > 1) {
@@ -348,7 +374,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
         const bool empty = tile0(0) >= j1;   // the group saw no token of the split
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
-          const int f = f0 + 16 * nt + l16;
+          const int f = fl0 + 16 * nt + l16;   // block-local
 #pragma unroll
           for (int mv = 0; mv < C::MV; ++mv)
 #pragma unroll
@@ -363,7 +389,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
       if (grp == 0) {
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
-          const int f = f0 + 16 * nt + l16;
+          const int f = fl0 + 16 * nt + l16;   // block-local
           const float co = xc[f];
           const float cn = fmaxf(cref[nt], co);
           const float a = fast_exp2(cref[nt] - cn), b = fast_exp2(co - cn);
@@ -720,6 +746,262 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
 #pragma unroll
         for (int nt = 0; nt < C::NTQ; ++nt) SA[mt][nt] = SB[mt][nt];
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// qstream: the query side when W' and [KV | z] do not fit in LDS together
+// (m (d+8) + (d+16)(m+8) halves over 160 KB, e.g. d = 128 with m = 512).
+// Grid as qapply.  The NW waves take their 16*NTQ-token tiles in lockstep
+// rounds, and each round streams the features through LDS in 64-feature
+// chunks, double buffered (chunk k+1 is loaded while chunk k is used).  Per
+// chunk buffer: W' rows [64][D+8] fp16, [KV | z] columns [D+16][64+8] bf16
+// and c [64] fp32.
+// ---------------------------------------------------------------------------
+template <int D>
+struct QsLds {
+  static constexpr int WROW = D + 8;
+  static constexpr int KROWS = D + 16;
+  static constexpr int KCOL = 64 + 8;
+  static constexpr int W_BYTES = 64 * WROW * 2;
+  static constexpr int K_BYTES = KROWS * KCOL * 2;
+  static constexpr int BUF = W_BYTES + K_BYTES + 64 * 4;
+  static constexpr int W16 = 64 * WROW / 8;     // 16-byte units per chunk
+  static constexpr int K16 = KROWS * 8;
+  static constexpr int C16 = 16;
+  static constexpr int ALL16 = W16 + K16 + C16;
+};
+
+template <int D, int NW, int NTQ, int NCH>
+__global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict__ Q,
+                                                   const _Float16* __restrict__ W16,
+                                                   const uint16_t* __restrict__ Kz,
+                                                   const float* __restrict__ cfin,
+                                                   uint16_t* __restrict__ O, int L, int QL) {
+  using C = QCfg<D, NTQ>;
+  using LS = QsLds<D>;
+  constexpr int NTH = NW * 64;
+  constexpr int m = 64 * NCH;
+  constexpr int kzrow = m + 8;
+  constexpr int SPT = (LS::ALL16 + NTH - 1) / NTH;
+  __shared__ __align__(16) unsigned char qs_smem[2 * LS::BUF];
+  const int nqb = (L + QL - 1) / QL;
+  const int item = xcd_major(blockIdx.x, gridDim.x);
+  const int qb = item % nqb, bh = item / nqb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g = lane >> 4;
+  const size_t base = static_cast<size_t>(bh) * L * D;
+  const int q0 = qb * QL, q1 = min(L, q0 + QL);
+  const int nround = (q1 - q0 + NW * C::TQ - 1) / (NW * C::TQ);
+
+  auto Wl = [&](int b) { return reinterpret_cast<_Float16*>(qs_smem + b * LS::BUF); };
+  auto Kzl = [&](int b) {
+    return reinterpret_cast<uint16_t*>(qs_smem + b * LS::BUF + LS::W_BYTES);
+  };
+  auto cl = [&](int b) {
+    return reinterpret_cast<float*>(qs_smem + b * LS::BUF + LS::W_BYTES + LS::K_BYTES);
+  };
+
+  // Chunk staging through registers: global loads of chunk k+1 are issued
+  // before chunk k is used and written to the other buffer after it.
+  uint4 sreg[SPT];
+  const uint4* const wsrc = reinterpret_cast<const uint4*>(W16);
+  const uint4* const ksrc = reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow);
+  const uint4* const csrc = reinterpret_cast<const uint4*>(cfin + static_cast<size_t>(bh) * m);
+  auto sload = [&](int ch) {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int e = tid + k * NTH;
+      if (e < LS::W16) {
+        sreg[k] = wsrc[ch * LS::W16 + e];
+      } else if (e < LS::W16 + LS::K16) {
+        const int e2 = e - LS::W16, row = e2 >> 3, c8 = e2 & 7;
+        sreg[k] = ksrc[(row * kzrow + 64 * ch) / 8 + c8];
+      } else if (e < LS::ALL16) {
+        sreg[k] = csrc[16 * ch + (e - LS::W16 - LS::K16)];
+      }
+    }
+  };
+  auto sstore = [&](int b) {
+#pragma unroll
+    for (int k = 0; k < SPT; ++k) {
+      const int e = tid + k * NTH;
+      if (e < LS::W16) {
+        reinterpret_cast<uint4*>(Wl(b))[e] = sreg[k];
+      } else if (e < LS::W16 + LS::K16) {
+        const int e2 = e - LS::W16, row = e2 >> 3, c8 = e2 & 7;
+        reinterpret_cast<uint4*>(Kzl(b))[row * (LS::KCOL / 8) + c8] = sreg[k];
+      } else if (e < LS::ALL16) {
+        reinterpret_cast<uint4*>(cl(b))[e - LS::W16 - LS::K16] = sreg[k];
+      }
+    }
+  };
+
+  using Qop = f16x8[C::NTQ][C::KS];
+  auto qload = [&](int tt, Qop& qop) {
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      const int tok = tt + 16 * nt + l16;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        uint4 x = make_uint4(0, 0, 0, 0);
+        if (tok < q1)
+          x = *reinterpret_cast<const uint4*>(Q + base + static_cast<size_t>(tok) * D + 32 * ks +
+                                              8 * g);
+        uint4 h;
+        h.x = bf16x2_to_f16x2(x.x); h.y = bf16x2_to_f16x2(x.y);
+        h.z = bf16x2_to_f16x2(x.z); h.w = bf16x2_to_f16x2(x.w);
+        qop[nt][ks] = __builtin_bit_cast(f16x8, h);
+      }
+    }
+  };
+
+  f32x4 acc[C::MV + 1][C::NTQ];
+  float M[C::NTQ], lm[C::NTQ];
+  using SArr = f32x4[4][C::NTQ];
+  // S^T = W' Q^T + c for the chunk in buffer b (rows: chunk features).
+  // (W' operands one 16-feature tile ahead: bounded registers, LDS latency
+  // covered by the previous tile's products)
+  auto proj = [&](int b, const Qop& qop, SArr& S) {
+    const _Float16* w = Wl(b);
+    const float* c = cl(b);
+    f16x8 wa[2][C::KS];
+    auto wload = [&](int mt, f16x8 (&dst)[C::KS]) {
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        dst[ks] = *reinterpret_cast<const f16x8*>(&w[(16 * mt + l16) * LS::WROW + 32 * ks + 8 * g]);
+    };
+    wload(0, wa[0]);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (mt + 1 < 4) wload(mt + 1, wa[(mt + 1) & 1]);
+      const f32x4 cb = *reinterpret_cast<const f32x4*>(&c[16 * mt + 4 * g]);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < C::NTQ; ++nt)
+          S[mt][nt] = mma_f16(wa[mt & 1][ks], qop[nt][ks], ks == 0 ? cb : S[mt][nt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto relative = [&](SArr& S) {
+    bool raise = false;
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= M[nt];
+      const float a = max3(S[0][nt][0], S[0][nt][1], S[0][nt][2]);
+      const float b = max3(S[0][nt][3], S[1][nt][0], S[1][nt][1]);
+      const float c = max3(S[1][nt][2], S[1][nt][3], S[2][nt][0]);
+      const float d = max3(S[2][nt][1], S[2][nt][2], S[2][nt][3]);
+      const float e = max3(S[3][nt][0], S[3][nt][1], S[3][nt][2]);
+      lm[nt] = max3(max3(a, b, c), max3(d, e, S[3][nt][3]), a);
+      raise |= lm[nt] > kTau;
+    }
+    return __ballot(raise) != 0;
+  };
+  auto rebase = [&](SArr& S, bool first) {
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      const float cm = colmax4(lm[nt]);
+      const float dlt = (first || cm > kTau) ? cm : 0.f;
+      if (!first) {
+        const float f = fast_exp2(-dlt);
+#pragma unroll
+        for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= dlt;
+      M[nt] += dlt;
+    }
+  };
+  auto apply = [&](int b, const SArr& S) {
+    const uint16_t* kz = Kzl(b);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 qt[C::NTQ];
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt) {
+        uint32_t p[4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          p[q] = pack_bf16(fast_exp2(S[2 * kb][nt][2 * q]), fast_exp2(S[2 * kb][nt][2 * q + 1]));
+          p[2 + q] = pack_bf16(fast_exp2(S[2 * kb + 1][nt][2 * q]),
+                               fast_exp2(S[2 * kb + 1][nt][2 * q + 1]));
+        }
+        qt[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+      }
+#pragma unroll
+      for (int mv = 0; mv <= C::MV; ++mv) {
+        const bf16x8 ka =
+            *reinterpret_cast<const bf16x8*>(&kz[(16 * mv + l16) * LS::KCOL + 32 * kb + 8 * g]);
+#pragma unroll
+        for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[nt], acc[mv][nt]);
+        if (mv % 3 == 2) __builtin_amdgcn_sched_barrier(0);   // bounded operand lookahead
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto finish = [&](int tt) {
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      const float den = __shfl(acc[C::MV][nt][0], l16, 64);
+      const float inv = 1.0f / den;
+      const int tok = tt + 16 * nt + l16;
+      if (tok < q1) {
+        uint16_t* orow = O + base + static_cast<size_t>(tok) * D + 4 * g;
+#pragma unroll
+        for (int mv = 0; mv < C::MV; ++mv) {
+          uint2 o;
+          o.x = pack_bf16(acc[mv][nt][0] * inv, acc[mv][nt][1] * inv);
+          o.y = pack_bf16(acc[mv][nt][2] * inv, acc[mv][nt][3] * inv);
+          *reinterpret_cast<uint2*>(orow + 16 * mv) = o;
+        }
+      }
+    }
+  };
+
+  // Every wave runs every round and chunk (tiles past the block compute on
+  // zeros and store nothing), so the work-group barriers always match.
+  sload(0);
+  sstore(0);
+  __syncthreads();
+  int b = 0;
+  Qop qcur;
+  for (int r = 0; r < nround; ++r) {
+    const int tt = q0 + (r * NW + wave) * C::TQ;
+    qload(tt, qcur);
+#pragma unroll
+    for (int i = 0; i <= C::MV; ++i)
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) M[nt] = 0.f;
+#pragma unroll 1
+    for (int ch = 0; ch < NCH; ++ch) {
+      const bool more = (ch + 1 < NCH) || (r + 1 < nround);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) sload((ch + 1) % NCH);
+      SArr S;
+      proj(b, qcur, S);
+      // (the other buffer was last read before the previous barrier)
+      if (more) sstore(b ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ch == 0) {
+        relative(S);
+        rebase(S, true);
+      } else if (__builtin_expect(relative(S), 0)) {
+        rebase(S, false);
+      }
+      apply(b, S);
+      __syncthreads();
+      b ^= 1;
+    }
+    finish(tt);
   }
 }
 
@@ -1188,7 +1470,10 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   }
 }
 
-template <int D, int NW>
+// The bidirectional path for m = NFB NW FPW features: kpart in NFB feature
+// blocks of NW waves, kcombine, then qapply (W', [KV | z] and c resident in
+// LDS) or, when they do not fit, qstream.
+template <int D, int NW, int NFB>
 hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                     const float* W, uint16_t* O, char* ws, hipStream_t st) {
   float* P = reinterpret_cast<float*>(ws + p.off_T);
@@ -1196,11 +1481,11 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   uint16_t* Kz = reinterpret_cast<uint16_t*>(ws + p.off_KV);
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   _Float16* W16 = reinterpret_cast<_Float16*>(ws + p.off_cP);
-  timing_before(st);
   // Two token groups while a work-group stays within 8 waves (two per SIMD).
   constexpr int TG = (NW <= 4) ? 2 : 1;
-  kpart<D, NW, TG><<<dim3(p.nseg, p.BH), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
-                                                                p.nseg);
+  timing_before(st);
+  kpart<D, NW, TG><<<dim3(p.nseg, p.BH, NFB), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
+                                                                     p.seg, p.nseg);
   hipError_t e = hipGetLastError();
   timing_after(st, "kpart");
   if (e != hipSuccess) return e;
@@ -1210,19 +1495,25 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   e = hipGetLastError();
   timing_after(st, "kcombine");
   if (e != hipSuccess) return e;
-  const size_t lds = qapply_lds_bytes<D>(p.m);
   const int nqb = (p.L + p.qblk - 1) / p.qblk;
   constexpr int NTQ = FAVOR_QAPPLY_NTQ;
-  // m = 64 NCH; the key side runs m / FPW waves, so NCH follows from NW.
-  constexpr int NCH = NW * KCfg<D>::FPW / 64;
-  auto* kern = &qapply<D, 4, NTQ, NCH>;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  if (e != hipSuccess) return e;
-  timing_before(st);
-  kern<<<dim3(nqb * p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
-  e = hipGetLastError();
-  timing_after(st, "qapply");
+  constexpr int NCH = NFB * NW * KCfg<D>::FPW / 64;   // m / 64
+  const size_t lds = qapply_lds_bytes<D>(p.m);
+  if (lds <= 160 * 1024) {
+    auto* kern = &qapply<D, 4, NTQ, NCH>;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    timing_before(st);
+    kern<<<dim3(nqb * p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
+    e = hipGetLastError();
+    timing_after(st, "qapply");
+  } else {
+    timing_before(st);
+    qstream<D, 8, NTQ, NCH><<<dim3(nqb * p.BH), 512, 0, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
+    e = hipGetLastError();
+    timing_after(st, "qstream");
+  }
   return e;
 }
 
@@ -1280,21 +1571,43 @@ hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, cons
   return hipErrorInvalidValue;
 }
 
+namespace {
+// Waves of the key side per feature block, and feature blocks, for (d, m);
+// 0 waves when the MFMA path does not take the shape.
+void bidir_blocks(int32_t d, int32_t m, int* nw, int* nfb) {
+  *nw = 0;
+  *nfb = 1;
+  if (m % 64 != 0 || m > 1024 || (d != 64 && d != 128)) return;
+  const int total = m / (d == 64 ? KCfg<64>::FPW : KCfg<128>::FPW);
+  if (total <= 8) {
+    *nw = total;
+  } else if (total % 2 == 0 && total <= 16) {
+    *nw = total / 2;
+    *nfb = 2;
+  }
+}
+}  // namespace
+
 int mfma_bidir_token_groups(int32_t d, int32_t m) {
-  const int nw = m / KCfg<64>::FPW;   // key-side waves per token group at d = 64
-  return (d == 64 ? nw : m / KCfg<128>::FPW) <= 4 ? 2 : 1;
+  int nw, nfb;
+  bidir_blocks(d, m, &nw, &nfb);
+  return (nw > 0 && nw <= 4) ? 2 : 1;
+}
+
+int mfma_bidir_feature_blocks(int32_t d, int32_t m) {
+  int nw, nfb;
+  bidir_blocks(d, m, &nw, &nfb);
+  return nfb;
 }
 
 bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype) {
-  if (dtype != FAVOR_BF16) return false;
-  if (m % 64 != 0) return false;
-  if (d == 64) return m <= 1024 && qapply_lds_bytes<64>(m) <= 160 * 1024;
-  if (d == 128) return m <= 512 && qapply_lds_bytes<128>(m) <= 160 * 1024;
-  return false;
+  int nw, nfb;
+  bidir_blocks(d, m, &nw, &nfb);
+  return dtype == FAVOR_BF16 && nw > 0;
 }
 
-size_t mfma_bidir_lds_bytes(int32_t d, int32_t m) {
-  return d == 64 ? qapply_lds_bytes<64>(m) : qapply_lds_bytes<128>(m);
+bool mfma_bidir_streams_queries(int32_t d, int32_t m) {
+  return (d == 64 ? qapply_lds_bytes<64>(m) : qapply_lds_bytes<128>(m)) > 160 * 1024;
 }
 
 hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
@@ -1304,27 +1617,16 @@ hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const
   const auto* v = static_cast<const uint16_t*>(V);
   auto* o = static_cast<uint16_t*>(O);
   char* w = static_cast<char*>(ws);
-  if (p.d == 64) {
-    switch (p.m / 64) {
-      case 1: return launch_d<64, 1>(p, q, k, v, W, o, w, stream);
-      case 2: return launch_d<64, 2>(p, q, k, v, W, o, w, stream);
-      case 3: return launch_d<64, 3>(p, q, k, v, W, o, w, stream);
-      case 4: return launch_d<64, 4>(p, q, k, v, W, o, w, stream);
-      case 5: return launch_d<64, 5>(p, q, k, v, W, o, w, stream);
-      case 6: return launch_d<64, 6>(p, q, k, v, W, o, w, stream);
-      case 7: return launch_d<64, 7>(p, q, k, v, W, o, w, stream);
-      case 8: return launch_d<64, 8>(p, q, k, v, W, o, w, stream);
-      default: break;
-    }
-  } else if (p.d == 128) {
-    switch (p.m / 32) {
-      case 2: return launch_d<128, 2>(p, q, k, v, W, o, w, stream);
-      case 4: return launch_d<128, 4>(p, q, k, v, W, o, w, stream);
-      case 6: return launch_d<128, 6>(p, q, k, v, W, o, w, stream);
-      case 8: return launch_d<128, 8>(p, q, k, v, W, o, w, stream);
-      default: break;
-    }
-  }
+  int nw, nfb;
+  bidir_blocks(p.d, p.m, &nw, &nfb);
+#define FAVOR_CASE(D, NW, NFB) \
+  if (p.d == D && nw == NW && nfb == NFB) return launch_d<D, NW, NFB>(p, q, k, v, W, o, w, stream);
+  FAVOR_CASE(64, 1, 1) FAVOR_CASE(64, 2, 1) FAVOR_CASE(64, 3, 1) FAVOR_CASE(64, 4, 1)
+  FAVOR_CASE(64, 5, 1) FAVOR_CASE(64, 6, 1) FAVOR_CASE(64, 7, 1) FAVOR_CASE(64, 8, 1)
+  FAVOR_CASE(64, 5, 2) FAVOR_CASE(64, 6, 2) FAVOR_CASE(64, 7, 2) FAVOR_CASE(64, 8, 2)
+  FAVOR_CASE(128, 2, 1) FAVOR_CASE(128, 4, 1) FAVOR_CASE(128, 6, 1) FAVOR_CASE(128, 8, 1)
+  FAVOR_CASE(128, 5, 2) FAVOR_CASE(128, 6, 2) FAVOR_CASE(128, 7, 2) FAVOR_CASE(128, 8, 2)
+#undef FAVOR_CASE
   return hipErrorInvalidValue;
 }
 

@@ -102,6 +102,28 @@ __device__ inline int xcd_major(int i, int n) {
   return (n % 8) ? i : (i % 8) * (n / 8) + i / 8;
 }
 
+// Raw buffer access (gfx9 buffer resource: base, stride 0, size in bytes).
+// A load whose byte offset (VGPR offset plus the instruction's immediate) is
+// at or past `bytes` returns zeros without touching memory, which masks the
+// tail of a token range with no per-lane branch.  The resource is built from
+// wave-uniform values, so it lives in scalar registers.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBufFlags = 0x00020000;   // 32-bit data format, as every gfx9 raw buffer uses
+constexpr int kBufOff = 0x40000000;     // an offset past any valid size: always reads zero
+
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufFlags);
+}
+__device__ inline uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ inline uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
+
 // Compiler-only ordering point for LDS data exchanged between the lanes of
 // one wave: a wave's LDS operations execute in issue order, so keeping the
 // compiler from moving accesses across this point is all that is needed.

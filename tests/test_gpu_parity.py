@@ -110,6 +110,8 @@ SHAPES = [
     (1, 1, 4097, 16, 64),
     (1, 1, 2049, 64, 64),     # causal: nine segments, the last one token long
     (2, 2, 333, 64, 192),
+    (1, 2, 700, 128, 512),    # bidirectional: two key feature blocks, streamed query side
+    (1, 1, 500, 64, 768),     # bidirectional: two key feature blocks, streamed query side
 ]
 
 

@@ -159,6 +159,9 @@ def test_plan_describe():
         path, nseg, seg = fv.plan_describe(B, H, L, d, m, fv.BF16, causal)
         assert path == 1
         assert seg % 32 == 0 and nseg == -(-L // seg) and (nseg - 1) * seg < L
+    assert fv.plan_describe(4, 32, 16384, 128, 512, fv.BF16, 0)[0] == 1
+    assert fv.plan_describe(1, 1, 500, 64, 768, fv.BF16, 0)[0] == 1
+    assert fv.plan_describe(1, 1, 500, 64, 576, fv.BF16, 0)[0] == 0   # 9 key waves: generic
     # fp32 and shapes outside the matrix-core kernels take the generic path.
     assert fv.plan_describe(1, 1, 256, 16, 16, fv.F32, 0)[0] == 0
     assert fv.plan_describe(1, 1, 256, 64, 48, fv.BF16, 1)[0] == 0
