@@ -754,22 +754,25 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
 // (m (d+8) + (d+16)(m+8) halves over 160 KB, e.g. d = 128 with m = 512).
 // Grid as qapply.  The NW waves take their 16*NTQ-token tiles in lockstep
 // rounds, and each round streams the features through LDS in 64-feature
-// chunks, double buffered (chunk k+1 is loaded while chunk k is used).  Per
-// chunk buffer: W' rows [64][D+8] fp16, [KV | z] columns [D+16][64+8] bf16
-// and c [64] fp32.
+// chunks, double buffered: chunk k+1 travels from global memory straight
+// into LDS (global_load_lds, no registers) while chunk k is used.  Per chunk
+// buffer: W' rows [64][D+8] fp16 (as laid out in the workspace), [KV | z]
+// columns [D+16][64] bf16 with the 16-byte units of row r XOR-swizzled by
+// (r >> 1) & 7 (conflict-free operand reads without padding), c [64] fp32.
 // ---------------------------------------------------------------------------
 template <int D>
 struct QsLds {
   static constexpr int WROW = D + 8;
   static constexpr int KROWS = D + 16;
-  static constexpr int KCOL = 64 + 8;
   static constexpr int W_BYTES = 64 * WROW * 2;
-  static constexpr int K_BYTES = KROWS * KCOL * 2;
+  static constexpr int K_BYTES = KROWS * 64 * 2;
   static constexpr int BUF = W_BYTES + K_BYTES + 64 * 4;
   static constexpr int W16 = 64 * WROW / 8;     // 16-byte units per chunk
   static constexpr int K16 = KROWS * 8;
-  static constexpr int C16 = 16;
-  static constexpr int ALL16 = W16 + K16 + C16;
+  static constexpr int WJOBS = W16 / 64;        // one wave instruction moves 64 units
+  static constexpr int KJOBS = K16 / 64;
+  static constexpr int JOBS = WJOBS + KJOBS + 1;   // + c (16 units)
+  static_assert(W16 % 64 == 0 && K16 % 64 == 0, "whole waves per staging job");
 };
 
 template <int D, int NW, int NTQ, int NCH>
@@ -780,15 +783,14 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
                                                    uint16_t* __restrict__ O, int L, int QL) {
   using C = QCfg<D, NTQ>;
   using LS = QsLds<D>;
-  constexpr int NTH = NW * 64;
   constexpr int m = 64 * NCH;
   constexpr int kzrow = m + 8;
-  constexpr int SPT = (LS::ALL16 + NTH - 1) / NTH;
   __shared__ __align__(16) unsigned char qs_smem[2 * LS::BUF];
   const int nqb = (L + QL - 1) / QL;
   const int item = xcd_major(blockIdx.x, gridDim.x);
   const int qb = item % nqb, bh = item / nqb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   const size_t base = static_cast<size_t>(bh) * L * D;
   const int q0 = qb * QL, q1 = min(L, q0 + QL);
@@ -802,40 +804,28 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
     return reinterpret_cast<float*>(qs_smem + b * LS::BUF + LS::W_BYTES + LS::K_BYTES);
   };
 
-  // Chunk staging through registers: global loads of chunk k+1 are issued
-  // before chunk k is used and written to the other buffer after it.
-  uint4 sreg[SPT];
+  // Chunk staging: job j (one wave instruction, 64 units of 16 bytes, lane i
+  // landing at unit i) goes to wave j % NW.
   const uint4* const wsrc = reinterpret_cast<const uint4*>(W16);
-  const uint4* const ksrc = reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow);
+  const uint4* const ksrc =
+      reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow);
   const uint4* const csrc = reinterpret_cast<const uint4*>(cfin + static_cast<size_t>(bh) * m);
-  auto sload = [&](int ch) {
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-      const int e = tid + k * NTH;
-      if (e < LS::W16) {
-        sreg[k] = wsrc[ch * LS::W16 + e];
-      } else if (e < LS::W16 + LS::K16) {
-        const int e2 = e - LS::W16, row = e2 >> 3, c8 = e2 & 7;
-        sreg[k] = ksrc[(row * kzrow + 64 * ch) / 8 + c8];
-      } else if (e < LS::ALL16) {
-        sreg[k] = csrc[16 * ch + (e - LS::W16 - LS::K16)];
+  auto stage = [&](int ch, int b) {
+    for (int j = wave; j < LS::JOBS; j += NW) {
+      if (j < LS::WJOBS) {
+        lds_dma16(wsrc + ch * LS::W16 + 64 * j + lane, reinterpret_cast<uint4*>(Wl(b)) + 64 * j);
+      } else if (j < LS::WJOBS + LS::KJOBS) {
+        const int u = 64 * (j - LS::WJOBS) + lane;      // destination unit
+        const int row = u >> 3, c8 = (u & 7) ^ ((row >> 1) & 7);
+        lds_dma16(ksrc + (row * kzrow + 64 * ch) / 8 + c8,
+                  reinterpret_cast<uint4*>(Kzl(b)) + 64 * (j - LS::WJOBS));
+      } else if (lane < 16) {
+        lds_dma16(csrc + 16 * ch + lane, cl(b));
       }
     }
   };
-  auto sstore = [&](int b) {
-#pragma unroll
-    for (int k = 0; k < SPT; ++k) {
-      const int e = tid + k * NTH;
-      if (e < LS::W16) {
-        reinterpret_cast<uint4*>(Wl(b))[e] = sreg[k];
-      } else if (e < LS::W16 + LS::K16) {
-        const int e2 = e - LS::W16, row = e2 >> 3, c8 = e2 & 7;
-        reinterpret_cast<uint4*>(Kzl(b))[row * (LS::KCOL / 8) + c8] = sreg[k];
-      } else if (e < LS::ALL16) {
-        reinterpret_cast<uint4*>(cl(b))[e - LS::W16 - LS::K16] = sreg[k];
-      }
-    }
-  };
+  // This wave's staging loads have landed in LDS (then a barrier publishes).
+  auto staged = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
 
   using Qop = f16x8[C::NTQ][C::KS];
   auto qload = [&](int tt, Qop& qop) {
@@ -937,8 +927,8 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
       }
 #pragma unroll
       for (int mv = 0; mv <= C::MV; ++mv) {
-        const bf16x8 ka =
-            *reinterpret_cast<const bf16x8*>(&kz[(16 * mv + l16) * LS::KCOL + 32 * kb + 8 * g]);
+        const int row = 16 * mv + l16, c8 = (4 * kb + g) ^ ((row >> 1) & 7);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kz[row * 64 + 8 * c8]);
 #pragma unroll
         for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[nt], acc[mv][nt]);
         if (mv % 3 == 2) __builtin_amdgcn_sched_barrier(0);   // bounded operand lookahead
@@ -967,8 +957,8 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
 
   // Every wave runs every round and chunk (tiles past the block compute on
   // zeros and store nothing), so the work-group barriers always match.
-  sload(0);
-  sstore(0);
+  stage(0, 0);
+  staged();
   __syncthreads();
   int b = 0;
   Qop qcur;
@@ -984,13 +974,10 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
 #pragma unroll 1
     for (int ch = 0; ch < NCH; ++ch) {
       const bool more = (ch + 1 < NCH) || (r + 1 < nround);
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) sload((ch + 1) % NCH);
+      // (the other buffer was last read before the previous barrier)
+      if (more) stage((ch + 1) % NCH, b ^ 1);
       SArr S;
       proj(b, qcur, S);
-      // (the other buffer was last read before the previous barrier)
-      if (more) sstore(b ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
       if (ch == 0) {
         relative(S);
         rebase(S, true);
@@ -998,6 +985,7 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
         rebase(S, false);
       }
       apply(b, S);
+      staged();
       __syncthreads();
       b ^= 1;
     }

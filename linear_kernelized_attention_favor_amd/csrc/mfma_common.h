@@ -124,6 +124,13 @@ __device__ inline uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int off) {
   return make_uint2(v.x, v.y);
 }
 
+// 16 bytes per lane from global memory straight into LDS (gfx950
+// global_load_lds_dwordx4): lane i's data lands at lds_dst + 16 i, where
+// lds_dst is the same for the whole wave.  Completion is tracked by vmcnt.
+__device__ inline void lds_dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+}
+
 // Compiler-only ordering point for LDS data exchanged between the lanes of
 // one wave: a wave's LDS operations execute in issue order, so keeping the
 // compiler from moving accesses across this point is all that is needed.
