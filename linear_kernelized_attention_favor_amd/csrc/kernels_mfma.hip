@@ -4,14 +4,17 @@
 // D = diag(Q' ((K')^T 1_L)), with phi(x) = exp(w . x - |x|^2/2)/sqrt(m).
 // Three launches:
 //
-//   kpart    per (head, sequence split): for each 32-token tile the feature
-//            exponents S = K W'^T - |k|^2/2 (fp16 MFMA; W' = W log2 e so the
-//            exponentials are exp2), a per-feature running reference c_r (the
-//            maximum exponent seen so far, raised only when a tile exceeds it
-//            by more than kTau), K~ = exp2(S - c_r) in bf16, and the
-//            contraction [V | 1]^T K~ accumulated in fp32 (bf16 MFMA).  Each
-//            wave owns a slice of features; the 32-token tile is staged once
-//            per work-group in LDS (K in fp16, V transposed).
+//   kpart    per (head, sequence split): for each 32-token tile the relative
+//            feature exponents S = K W'^T - |k|^2/2 - c_r (fp16 MFMA; W' =
+//            W log2 e so the exponentials are exp2; the norm and the
+//            per-feature reference c_r enter through one extra MFMA k-step
+//            whose operands hold them as fp16 hi/lo pairs), K~ = exp2(S) in
+//            bf16, and the contraction [V | 1]^T K~ accumulated in fp32 (bf16
+//            MFMA).  c_r sits kKeyBias above the largest exponent seen when it
+//            was set and is raised only when some K~ reaches 2 (the top bit of
+//            a bf16 exponent, tested on the packed features).  Each wave owns
+//            a slice of features; the 32-token tile is staged once per
+//            work-group in LDS (K in fp16, V transposed).
 //   kcombine per head: the splits' partial states, rescaled to the largest
 //            per-feature reference, summed in split order; written as the
 //            bf16 operand of the query side.
@@ -49,6 +52,13 @@ using namespace mfma;
 // raises (which rescale the accumulators) are rare.
 constexpr float kTau = 20.0f;
 
+// Key-side reference placement: after a (re)set, a feature's largest
+// exponent sits kKeyBias below its reference, so K~ <= 2^-kKeyBias; a tile is
+// re-referenced only when some K~ >= 2 (kKeyBias + 1 log2 units of headroom),
+// and values more than 126 - kKeyBias below the maximum flush to zero (bf16
+// normal range), where they are far below fp32 resolution of the sums.
+constexpr float kKeyBias = 40.0f;
+
 #ifndef FAVOR_QAPPLY_NTQ
 #define FAVOR_QAPPLY_NTQ 2      // 16-token tiles per query-side wave iteration
 #endif
@@ -85,8 +95,9 @@ struct KLds {
   using C = KCfg<D>;
   static constexpr int KS_BYTES = 3 * kTT * C::KROW * 2;
   static constexpr int VT_BYTES = 3 * D * (C::VROW / 2) * 4;
-  static constexpr int NS_BYTES = 3 * kTT * 4;
-  static constexpr int RING = KS_BYTES + VT_BYTES + NS_BYTES;
+  static constexpr int NAROW = 40;                    // halves per token row (32 + pad)
+  static constexpr int NA_BYTES = 3 * kTT * NAROW * 2;   // per token: 1, 1, n_hi, n_lo, 0 ...
+  static constexpr int RING = KS_BYTES + VT_BYTES + NA_BYTES;
   static constexpr int M = NW * C::FPW;                          // features
   static constexpr int XCH = (TG > 1) ? ((D + 1) * M + M) * 4 : 0;   // state + references
   static constexpr int BYTES = (TG * RING > XCH) ? TG * RING : XCH;
@@ -121,7 +132,14 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   unsigned char* const ring = kp_smem + grp * LD::RING;
   auto Ks = reinterpret_cast<_Float16(*)[kTT][C::KROW]>(ring);
   auto Vt = reinterpret_cast<uint32_t(*)[D][C::VROW / 2]>(ring + LD::KS_BYTES);   // bf16 pairs
-  auto Ns = reinterpret_cast<float(*)[kTT]>(ring + LD::KS_BYTES + LD::VT_BYTES);  // -|k|^2 log2e/2
+  // Per token the A operand of the extra k-step: [1, 1, n_hi, n_lo, 0 x 28]
+  // with n = |k|^2 log2(e) / 2 (lanes of the upper k rows read the zeros).
+  // (A full k=32 step: chaining a k=16 product into a k=32 accumulation was
+  // seen to read the accumulator too early on this part.)
+  auto Na = reinterpret_cast<_Float16(*)[kTT][LD::NAROW]>(ring + LD::KS_BYTES + LD::VT_BYTES);
+  for (int i = tid; i < LD::NA_BYTES / 16; i += NTH)
+    reinterpret_cast<uint4*>(Na)[i] = make_uint4(0, 0, 0, 0);
+  lds_barrier();
 
   // Projection B operands, kept in registers: W'[f][32 ks + 8 g + u].
   f16x8 wb[C::NT][C::KS];
@@ -147,8 +165,18 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float cref[C::NT];   // per-feature reference (log2 units), set by the first tile
+  f16x8 baug[C::NT];   // B operand of the extra step: [-c_hi, -c_lo, -1, -1] on k rows 0..3
+  auto set_baug = [&](int nt) {
+    const _Float16 hi = static_cast<_Float16>(cref[nt]);
+    const _Float16 lo = static_cast<_Float16>(cref[nt] - static_cast<float>(hi));
+    const _Float16 z = static_cast<_Float16>(0.f), m1 = static_cast<_Float16>(-1.f);
+    baug[nt] = (g == 0) ? f16x8{-hi, -lo, m1, m1, z, z, z, z} : f16x8{z, z, z, z, z, z, z, z};
+  };
 #pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt) cref[nt] = 0.f;
+  for (int nt = 0; nt < C::NT; ++nt) {
+    cref[nt] = 0.f;
+    set_baug(nt);
+  }
 
   const int j0 = s * SL, j1 = min(L, j0 + SL);
   // Steps per group (the group's tile t is the split's tile t TG + grp).
@@ -210,7 +238,18 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
         h.x = bf16x2_to_f16x2(kv.x); h.y = bf16x2_to_f16x2(kv.y);
         h.z = bf16x2_to_f16x2(kv.z); h.w = bf16x2_to_f16x2(kv.w);
         *reinterpret_cast<uint4*>(&Ks[buf][j][ch * 8]) = h;
-        if (ch == 0) Ns[buf][j] = (jt + j < j1) ? -0.5f * kLog2e * ss : -INFINITY;
+        if (ch == 0) {
+          // n as an fp16 hi/lo pair (clamped: a larger norm underflows K~ anyway);
+          // a token past the split gets n = +inf, i.e. K~ = 0.
+          const float n = fminf(0.5f * kLog2e * ss, 65504.f);
+          const _Float16 nh = static_cast<_Float16>(n);
+          const _Float16 nl = static_cast<_Float16>(n - static_cast<float>(nh));
+          const _Float16 one = static_cast<_Float16>(1.f);
+          const bool live = jt + j < j1;
+          *reinterpret_cast<f16x4*>(&Na[buf][j][0]) =
+              f16x4{one, one, live ? nh : static_cast<_Float16>(INFINITY),
+                    live ? nl : static_cast<_Float16>(0.f)};
+        }
       }
     }
     // V^T: two consecutive tokens share one 32-bit word (positions perm_of
@@ -235,51 +274,53 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   for (int u = 0; u < 8; ++u) ones[u] = static_cast<__bf16>(1.0f);
 
   using SArr = f32x4[2][C::NT];
-  // S = K W'^T - n'  (rows: tokens 16 mt + 4 g + v; column: feature f0 + 16 nt + l16)
+  // S = K W'^T - n - c  (rows: tokens 16 mt + 4 g + v; column: feature f0 + 16 nt + l16)
   auto proj = [&](int buf, SArr& S) {
-    f32x4 cinit[2];
+    f16x8 aa[2];
     f16x8 ka[2][C::KS];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      cinit[mt] = *reinterpret_cast<const f32x4*>(&Ns[buf][16 * mt + 4 * g]);
+      aa[mt] = *reinterpret_cast<const f16x8*>(&Na[buf][16 * mt + l16][8 * g]);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
         ka[mt][ks] = *reinterpret_cast<const f16x8*>(&Ks[buf][16 * mt + l16][32 * ks + 8 * g]);
     }
 #pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < C::NT; ++nt)
+        S[mt][nt] = mma_f16(aa[mt], baug[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < C::NT; ++nt)
-          S[mt][nt] = mma_f16(ka[mt][ks], wb[nt][ks], ks == 0 ? cinit[mt] : S[mt][nt]);
+        for (int nt = 0; nt < C::NT; ++nt) S[mt][nt] = mma_f16(ka[mt][ks], wb[nt][ks], S[mt][nt]);
   };
-  // Exponents relative to the references, in place; true if any lane of the
-  // wave exceeds the headroom.
-  auto relative = [&](SArr& S, float (&lm)[C::NT]) {
-    bool raise = false;
+  // True if some feature of the tile reached 2 (or is not finite): the top
+  // exponent bit of a packed bf16 value, ORed over the wave's features.
+  auto overflow = [&](const bf16x8 (&kb)[C::NT]) {
+    uint32_t o = 0;
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
+      const uint4 w = __builtin_bit_cast(uint4, kb[nt]);
+      o |= w.x | w.y | w.z | w.w;
+    }
+    return __ballot((o & 0x40004000u) != 0) != 0;
+  };
+  // Reference update from the exact per-feature maximum tm of S (relative to
+  // the current reference): raise by tm + kKeyBias where that is positive
+  // (always reset on the first tile, whose accumulators are still zero).
+  // S and any tile already projected with the old reference move along.
+  auto rebase = [&](SArr& S, bool first, float (&dl)[C::NT]) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= cref[nt];
+    for (int nt = 0; nt < C::NT; ++nt) {
       const float a = max3(S[0][nt][0], S[0][nt][1], S[0][nt][2]);
       const float b = max3(S[0][nt][3], S[1][nt][0], S[1][nt][1]);
-      lm[nt] = max3(a, b, fmaxf(S[1][nt][2], S[1][nt][3]));   // this lane's 8 tokens
-      raise |= lm[nt] > kTau;
-    }
-    return __ballot(raise) != 0;
-  };
-  // Reference update: exact per-feature maximum (column reduction); always
-  // on the first tile, otherwise only where a lane exceeded the headroom.
-  auto rebase = [&](SArr& S, float (&lm)[C::NT], bool first) {
-#pragma unroll
-    for (int nt = 0; nt < C::NT; ++nt) {
-      const float tm = colmax4(lm[nt]);
+      const float tm = colmax4(max3(a, b, fmaxf(S[1][nt][2], S[1][nt][3])));
       // (a group whose first tile lies past the split keeps a finite reference)
-      const float dlt = first ? (tm == -INFINITY ? 0.f : tm) : (tm > kTau ? tm : 0.f);
-      if (!first) {   // accumulators are still zero on the first tile
+      const float dlt = (tm == -INFINITY) ? 0.f : (first ? tm + kKeyBias : fmaxf(tm + kKeyBias, 0.f));
+      if (!first) {
         const float f = fast_exp2(-dlt);
 #pragma unroll
         for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
@@ -289,6 +330,8 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
 #pragma unroll
         for (int v = 0; v < 4; ++v) S[mt][nt][v] -= dlt;
       cref[nt] += dlt;
+      set_baug(nt);
+      dl[nt] = dlt;
     }
   };
   // K~ = exp2(S) as the contraction's B operand (token positions perm_of).
@@ -316,51 +359,60 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
     for (int nt = 0; nt < C::NT; ++nt) acc[C::MV][nt] = mma_bf16(ones, kb[nt], acc[C::MV][nt]);
   };
 
-  // Prologue: tiles 0 and 1 staged, tile 2 in flight, tile 0 projected.
+  // Prologue: tiles 0 and 1 staged, tile 2 in flight, tile 0's features
+  // formed (its reference set from the exact maximum).
   gload(0);
   lstore(0, 0);
   gload(1);
   lstore(1, 1);
   gload(2);
   lds_barrier();
-  SArr SA, SB;
-  float lm[C::NT];
-  proj(0, SA);
-  relative(SA, lm);
-  rebase(SA, lm, true);
+  bf16x8 kbA[C::NT], kbB[C::NT];
+  {
+    SArr S;
+    float dl[C::NT];
+    proj(0, S);
+    rebase(S, true, dl);
+    features(S, kbA);
+  }
 
   // Step t: stage tile t+2 (loaded during step t-1), load tile t+3, project
-  // tile t+1 while tile t's features are formed, contract tile t, and check
-  // tile t+1.
-  // The loop body holds six steps (the ring's period 3 times the S double
-  // buffer's period 2), so every ring slot is a compile-time constant and
-  // LDS addresses fold into the instructions' offsets.
-  auto step = [&](auto R, int t, SArr& Scur, SArr& Snext) {
+  // tile t+1 on the matrix cores while tile t is contracted, then form and
+  // check tile t+1's features (so every projection is consumed in its own
+  // step).  The loop body holds six steps (the ring's period 3 times the
+  // feature double buffer's period 2), so every ring slot is a compile-time
+  // constant and LDS addresses fold into the instructions' offsets.
+  auto step = [&](auto R, int t, const bf16x8 (&kcur)[C::NT], bf16x8 (&knext)[C::NT]) {
     constexpr int r = decltype(R)::value;
-    bf16x8 kb[C::NT];
+    __builtin_amdgcn_sched_barrier(0);   // keep the scheduler within one step
     lstore((r + 2) % 3, t + 2);
     gload(t + 3);
-    proj((r + 1) % 3, Snext);
-    features(Scur, kb);
-    contract(r % 3, kb);
-    if (__builtin_expect(relative(Snext, lm), 0)) rebase(Snext, lm, false);
+    SArr S;
+    proj((r + 1) % 3, S);
+    contract(r % 3, kcur);
+    features(S, knext);
+    if (__builtin_expect(overflow(knext), 0)) {
+      float dl[C::NT];
+      rebase(S, false, dl);
+      features(S, knext);
+    }
     lds_barrier();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   for (int t = 0; t < ntiles; t += 6) {
-    step(I0{}, t, SA, SB);
+    step(I0{}, t, kbA, kbB);
     if (t + 1 >= ntiles) break;
-    step(I1{}, t + 1, SB, SA);
+    step(I1{}, t + 1, kbB, kbA);
     if (t + 2 >= ntiles) break;
-    step(I2{}, t + 2, SA, SB);
+    step(I2{}, t + 2, kbA, kbB);
     if (t + 3 >= ntiles) break;
-    step(I0{}, t + 3, SB, SA);
+    step(I0{}, t + 3, kbB, kbA);
     if (t + 4 >= ntiles) break;
-    step(I1{}, t + 4, SA, SB);
+    step(I1{}, t + 4, kbA, kbB);
     if (t + 5 >= ntiles) break;
-    step(I2{}, t + 5, SB, SA);
+    step(I2{}, t + 5, kbB, kbA);
   }
 
   if constexpr (TG > 1) {
