@@ -84,7 +84,7 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
     // Query blocks: about 512 work-groups of 4 waves (qapply) or 256 of 8
     // (qstream, one per compute unit); a multiple of 64 (256) tokens.
     const bool stream = mfma_bidir_streams_queries(d, m);
-    const int64_t nwg = stream ? 256 : 512, unit = stream ? 256 : 64;
+    const int64_t nwg = stream ? 256 : mfma_bidir_query_workgroups(), unit = stream ? 256 : 64;
     const int64_t want = (static_cast<int64_t>(L) * p->BH + nwg - 1) / nwg;
     int64_t qb = (want + unit - 1) / unit * unit;
     if (qb < 256) qb = 256;

@@ -63,6 +63,7 @@ bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype);
 int mfma_bidir_token_groups(int32_t d, int32_t m);
 int mfma_bidir_feature_blocks(int32_t d, int32_t m);
 bool mfma_bidir_streams_queries(int32_t d, int32_t m);
+int mfma_bidir_query_workgroups();   // query-side work-groups the plan aims for (qapply)
 hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                               const float* W, void* O, void* ws, hipStream_t stream);
 

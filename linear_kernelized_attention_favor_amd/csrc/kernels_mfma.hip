@@ -58,12 +58,21 @@ constexpr float kTau = 20.0f;
 // and values more than 126 - kKeyBias below the maximum flush to zero (bf16
 // normal range), where they are far below fp32 resolution of the sums.
 constexpr float kKeyBias = 40.0f;
+// The same for the query side's per-row reference (the products of query and
+// key features stay above 2^-(kKeyBias + kQBias), far inside fp32).
+constexpr float kQBias = 20.0f;
 
 #ifndef FAVOR_QAPPLY_NTQ
 #define FAVOR_QAPPLY_NTQ 2      // 16-token tiles per query-side wave iteration
 #endif
 #ifndef FAVOR_QAPPLY_WPE
 #define FAVOR_QAPPLY_WPE 2      // query-side waves per SIMD the register budget targets
+#endif
+#ifndef FAVOR_QAPPLY_NW
+#define FAVOR_QAPPLY_NW 4       // waves per query-side work-group
+#endif
+#ifndef FAVOR_QAPPLY_WGS
+#define FAVOR_QAPPLY_WGS 512    // query-side work-groups per call the plan aims for
 #endif
 constexpr int kTT = 32;        // tokens per key tile
 
@@ -534,8 +543,13 @@ __global__ __launch_bounds__(256) void kcombine(const float* __restrict__ P,
 
 // ---------------------------------------------------------------------------
 // qapply: grid (nqb * BH) in XCD-major item order, NW waves; each wave takes
-// 16*NTQ-token tiles of the block [qb QL, (qb+1) QL).  LDS: W' fp16 [m][D+8], Kz bf16 [D+16][m+8],
-// c [m] fp32 (dynamic).
+// 16*NTQ-token tiles of the block [qb QL, (qb+1) QL).  LDS (dynamic): W'
+// fp16 [m][D+8], Kz bf16 [D+16][m+8], c [m] as fp16 hi/lo pairs.  The query
+// exponents relative to the row reference, S^T = W' Q^T + c - M, come out of
+// the matrix cores directly: an extra k-step multiplies [c_hi, c_lo, 1, 1]
+// per feature by [1, 1, -M_hi, -M_lo] per token.  M sits kQBias above the
+// row's largest exponent when set (first chunk of a tile) and is raised only
+// when some feature reaches 2 (the bf16 exponent's top bit).
 // ---------------------------------------------------------------------------
 template <int D, int NTQ_>
 struct QCfg {
@@ -565,8 +579,8 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* Wl = reinterpret_cast<_Float16*>(smem);
   uint16_t* Kzl = reinterpret_cast<uint16_t*>(smem + static_cast<size_t>(m) * C::WROW * 2);
-  float* cl = reinterpret_cast<float*>(smem + static_cast<size_t>(m) * C::WROW * 2 +
-                                       static_cast<size_t>(D + 16) * kzrow * 2);
+  uint32_t* chl = reinterpret_cast<uint32_t*>(smem + static_cast<size_t>(m) * C::WROW * 2 +
+                                              static_cast<size_t>(D + 16) * kzrow * 2);
   // 1-D grid of (head, query block) items, one head's blocks on one XCD.
   const int nqb = (L + QL - 1) / QL;
   const int item = xcd_major(blockIdx.x, gridDim.x);
@@ -574,20 +588,27 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
 
-  // Stage W' (fp16), Kz and c for this head.
+  // Stage W' (fp16), Kz and c (as fp16 hi/lo pairs) for this head.  W' and
+  // Kz go global -> LDS directly (each wave instruction moves 64 16-byte
+  // units), all issued before the first wait: one memory round trip.
   {
-    const uint4* src = reinterpret_cast<const uint4*>(W16);
-    uint4* dst = reinterpret_cast<uint4*>(Wl);
-    constexpr int n16 = m * C::WROW / 8;
-    for (int i = tid; i < n16; i += NTH) dst[i] = src[i];
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    auto copy = [&](const uint4* src, uint4* dst, int n16) {
+      for (int j = wv; 64 * j < n16; j += NW)
+        if (64 * j + lane < n16) lds_dma16(src + 64 * j + lane, dst + 64 * j);
+    };
+    copy(reinterpret_cast<const uint4*>(W16), reinterpret_cast<uint4*>(Wl), m * C::WROW / 8);
+    copy(reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow),
+         reinterpret_cast<uint4*>(Kzl), (D + 16) * kzrow / 8);
   }
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow);
-    uint4* dst = reinterpret_cast<uint4*>(Kzl);
-    constexpr int n16 = (D + 16) * kzrow / 8;
-    for (int i = tid; i < n16; i += NTH) dst[i] = src[i];
+  for (int i = tid; i < m; i += NTH) {
+    const float c = cfin[static_cast<size_t>(bh) * m + i];
+    const _Float16 hi = static_cast<_Float16>(c);
+    const _Float16 lo = static_cast<_Float16>(c - static_cast<float>(hi));
+    chl[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) << 16);
   }
-  for (int i = tid; i < m; i += NTH) cl[i] = cfin[static_cast<size_t>(bh) * m + i];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's staging has landed
   __syncthreads();   // the only barrier: LDS is read-only from here on
 
   const size_t base = static_cast<size_t>(bh) * L * D;
@@ -628,74 +649,45 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
   };
 
   f32x4 acc[C::MV + 1][C::NTQ];
-  float M[C::NTQ];   // per-row reference (log2 units), set by each tile's first chunk
+  float M[C::NTQ];     // per-row reference (log2 units)
+  f16x8 baug[C::NTQ];  // B operand of the extra step: [1, 1, -M_hi, -M_lo] on k rows 0..3
+  auto set_baug = [&](int nt) {
+    const _Float16 hi = static_cast<_Float16>(M[nt]);
+    const _Float16 lo = static_cast<_Float16>(M[nt] - static_cast<float>(hi));
+    const _Float16 z = static_cast<_Float16>(0.f), one = static_cast<_Float16>(1.f);
+    baug[nt] = (g == 0) ? f16x8{one, one, -hi, -lo, z, z, z, z} : f16x8{z, z, z, z, z, z, z, z};
+  };
   using SArr = f32x4[4][C::NTQ];
-  // S^T = W' Q^T + c  (rows: features 64 ch + 16 mt + 4 g + v; column: token)
+  using Feat = bf16x8[2][C::NTQ];   // [kb][nt]: lane = token, 8 features (perm_of)
+  // S^T = W' Q^T + c - M  (rows: features 64 ch + 16 mt + 4 g + v; column: token)
   auto proj = [&](int ch, const Qop& qop, SArr& S) {
-    f32x4 cb[4];
-    f16x8 wa[4][C::KS];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int fr = 64 * ch + 16 * mt;
-      cb[mt] = *reinterpret_cast<const f32x4*>(&cl[fr + 4 * g]);
+      const uint32_t cw = chl[64 * ch + 16 * mt + l16];
+      const f16x8 aa = __builtin_bit_cast(
+          f16x8, (g == 0) ? make_uint4(cw, 0x3C003C00u, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        wa[mt][ks] = *reinterpret_cast<const f16x8*>(
-            &Wl[static_cast<size_t>(fr + l16) * C::WROW + 32 * ks + 8 * g]);
+      for (int nt = 0; nt < C::NTQ; ++nt)
+        S[mt][nt] = mma_f16(aa, baug[nt], f32x4{0.f, 0.f, 0.f, 0.f});
     }
+    // (W' operands one k-step at a time: bounded registers at d = 128)
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
+    for (int ks = 0; ks < C::KS; ++ks) {
+      f16x8 wa[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        wa[mt] = *reinterpret_cast<const f16x8*>(
+            &Wl[static_cast<size_t>(64 * ch + 16 * mt + l16) * C::WROW + 32 * ks + 8 * g]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < C::NTQ; ++nt)
-          S[mt][nt] = mma_f16(wa[mt][ks], qop[nt][ks], ks == 0 ? cb[mt] : S[mt][nt]);
-  };
-  // Exponents relative to the row references, in place; true if any lane of
-  // the wave exceeds the headroom.
-  float lm[C::NTQ];
-  auto relative = [&](SArr& S) {
-    bool raise = false;
-#pragma unroll
-    for (int nt = 0; nt < C::NTQ; ++nt) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= M[nt];
-      const float a = max3(S[0][nt][0], S[0][nt][1], S[0][nt][2]);
-      const float b = max3(S[0][nt][3], S[1][nt][0], S[1][nt][1]);
-      const float c = max3(S[1][nt][2], S[1][nt][3], S[2][nt][0]);
-      const float d = max3(S[2][nt][1], S[2][nt][2], S[2][nt][3]);
-      const float e = max3(S[3][nt][0], S[3][nt][1], S[3][nt][2]);
-      lm[nt] = max3(max3(a, b, c), max3(d, e, S[3][nt][3]), a);   // this lane's 16 features
-      raise |= lm[nt] > kTau;
-    }
-    return __ballot(raise) != 0;
-  };
-  // Row reference update: exact row maximum (column reduction); always on a
-  // tile's first chunk, otherwise only where a lane exceeded the headroom.
-  auto rebase = [&](SArr& S, bool first) {
-#pragma unroll
-    for (int nt = 0; nt < C::NTQ; ++nt) {
-      const float cm = colmax4(lm[nt]);
-      const float dlt = (first || cm > kTau) ? cm : 0.f;
-      if (!first) {   // accumulators are still zero on the first chunk
-        const float f = fast_exp2(-dlt);
-#pragma unroll
-        for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= dlt;
-      M[nt] += dlt;
+        for (int nt = 0; nt < C::NTQ; ++nt) S[mt][nt] = mma_f16(wa[mt], qop[nt][ks], S[mt][nt]);
     }
   };
-  // Q~^T = exp2(S) (features at positions perm_of) times [KV | z]^T.
-  auto apply = [&](int ch, const SArr& S) {
+  // Q~^T = exp2(S) in bf16 as the contraction's B operand.
+  auto features = [&](const SArr& S, Feat& qt) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 qt[C::NTQ];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int nt = 0; nt < C::NTQ; ++nt) {
         uint32_t p[4];
@@ -705,14 +697,57 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
           p[2 + q] = pack_bf16(fast_exp2(S[2 * kb + 1][nt][2 * q]),
                                fast_exp2(S[2 * kb + 1][nt][2 * q + 1]));
         }
-        qt[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+        qt[kb][nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
       }
+  };
+  // True if some feature reached 2 (or is not finite), as in the key kernel.
+  auto overflow = [&](const Feat& qt) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt) {
+        const uint4 w = __builtin_bit_cast(uint4, qt[kb][nt]);
+        o |= w.x | w.y | w.z | w.w;
+      }
+    return __ballot((o & 0x40004000u) != 0) != 0;
+  };
+  // Row reference update from the exact row maximum of S (over the chunk's
+  // features): reset on a tile's first chunk, otherwise raised where
+  // positive, with the accumulators rescaled.
+  auto rebase = [&](SArr& S, bool first) {
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      const float a = max3(S[0][nt][0], S[0][nt][1], S[0][nt][2]);
+      const float b = max3(S[0][nt][3], S[1][nt][0], S[1][nt][1]);
+      const float c = max3(S[1][nt][2], S[1][nt][3], S[2][nt][0]);
+      const float d = max3(S[2][nt][1], S[2][nt][2], S[2][nt][3]);
+      const float e = max3(S[3][nt][0], S[3][nt][1], S[3][nt][2]);
+      const float tm = colmax4(max3(max3(a, b, c), max3(d, e, S[3][nt][3]), a));
+      const float dlt = first ? tm + kQBias : fmaxf(tm + kQBias, 0.f);
+      if (!first) {
+        const float f = fast_exp2(-dlt);
+#pragma unroll
+        for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= dlt;
+      M[nt] += dlt;
+      set_baug(nt);
+    }
+  };
+  // [KV | z]^T Q~^T accumulated over the chunk's features.
+  auto apply = [&](int ch, const Feat& qt) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       const int kcol = 64 * ch + 32 * kb + 8 * g;
 #pragma unroll
       for (int mv = 0; mv <= C::MV; ++mv) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kzl[(16 * mv + l16) * kzrow + kcol]);
 #pragma unroll
-        for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[nt], acc[mv][nt]);
+        for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[kb][nt], acc[mv][nt]);
       }
     }
   };
@@ -741,62 +776,75 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
 #pragma unroll
       for (int nt = 0; nt < C::NTQ; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int nt = 0; nt < C::NTQ; ++nt) M[nt] = 0.f;
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      M[nt] = 0.f;
+      set_baug(nt);
+    }
   };
 
   // Software pipeline over (tile, chunk): chunk k+1 is projected on the
-  // matrix cores while chunk k's features are formed and applied; a tile's
-  // last step projects the next tile's first chunk.
+  // matrix cores while chunk k is applied, then its features are formed and
+  // checked in the same step; a tile's last step projects the next tile's
+  // first chunk.
   Raw raw;
   Qop qcur;
   qload(tt0, raw);
   convert(raw, qcur);
   if (ntile > 1) qload(tt0 + step, raw);
   reset();
-  SArr SA, SB;
-  proj(0, qcur, SA);
-  relative(SA);
-  rebase(SA, true);
+  Feat FA, FB;
+  {
+    SArr S;
+    proj(0, qcur, S);
+    rebase(S, true);
+    features(S, FA);
+  }
   for (int ti = 0; ti < ntile; ++ti) {
     const int tt = tt0 + ti * step;
     const bool more = ti + 1 < ntile;
-    // Regular step: project chunk ch+1, apply chunk ch, check chunk ch+1.
-    auto regular = [&](const int ch, SArr& Scur, SArr& Snext) {
+    // Regular step: project chunk ch+1, apply chunk ch, form chunk ch+1.
+    auto regular = [&](const int ch, const Feat& Fcur, Feat& Fnext) {
       __builtin_amdgcn_sched_barrier(0);
-      proj(ch + 1, qcur, Snext);
-      apply(ch, Scur);
-      if (__builtin_expect(relative(Snext), 0)) rebase(Snext, false);
+      SArr S;
+      proj(ch + 1, qcur, S);
+      apply(ch, Fcur);
+      features(S, Fnext);
+      if (__builtin_expect(overflow(Fnext), 0)) {
+        rebase(S, false);
+        features(S, Fnext);
+      }
     };
-    // Last step of a tile: project the next tile's first chunk, apply the
-    // last chunk, write the tile, start the next one.
-    auto last = [&](const int ch, SArr& Scur, SArr& Snext) {
+    // Last step of a tile: apply the last chunk, write the tile, then project
+    // and form the next tile's first chunk.
+    auto last = [&](const int ch, const Feat& Fcur, Feat& Fnext) {
       __builtin_amdgcn_sched_barrier(0);
       if (more) convert(raw, qcur);   // the current tile's operands are done
-      proj(0, qcur, Snext);           // unused after the wave's last tile
-      apply(ch, Scur);
+      apply(ch, Fcur);
       finish(tt);
       reset();
       if (more) {
         if (ti + 2 < ntile) qload(tt + 2 * step, raw);
-        relative(Snext);
-        rebase(Snext, true);
+        SArr S;
+        proj(0, qcur, S);
+        rebase(S, true);
+        features(S, Fnext);
       }
     };
     int ch = 0;
 #pragma unroll 1
     for (; ch + 2 < NCH; ch += 2) {
-      regular(ch, SA, SB);
-      regular(ch + 1, SB, SA);
+      regular(ch, FA, FB);
+      regular(ch + 1, FB, FA);
     }
     if constexpr ((NCH % 2) == 0) {
-      regular(NCH - 2, SA, SB);
-      last(NCH - 1, SB, SA);
+      regular(NCH - 2, FA, FB);
+      last(NCH - 1, FB, FA);
     } else {
-      last(NCH - 1, SA, SB);   // the next tile's first chunk landed in SB
+      last(NCH - 1, FA, FB);   // the next tile's first chunk landed in FB
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int nt = 0; nt < C::NTQ; ++nt) SA[mt][nt] = SB[mt][nt];
+        for (int nt = 0; nt < C::NTQ; ++nt) FA[kb][nt] = FB[kb][nt];
     }
   }
 }
@@ -1540,12 +1588,13 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   constexpr int NCH = NFB * NW * KCfg<D>::FPW / 64;   // m / 64
   const size_t lds = qapply_lds_bytes<D>(p.m);
   if (lds <= 160 * 1024) {
-    auto* kern = &qapply<D, 4, NTQ, NCH>;
+    constexpr int QNW = FAVOR_QAPPLY_NW;
+    auto* kern = &qapply<D, QNW, NTQ, NCH>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
     timing_before(st);
-    kern<<<dim3(nqb * p.BH), 256, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
+    kern<<<dim3(nqb * p.BH), QNW * 64, lds, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
     e = hipGetLastError();
     timing_after(st, "qapply");
   } else {
@@ -1645,6 +1694,8 @@ bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype) {
   bidir_blocks(d, m, &nw, &nfb);
   return dtype == FAVOR_BF16 && nw > 0;
 }
+
+int mfma_bidir_query_workgroups() { return FAVOR_QAPPLY_WGS; }
 
 bool mfma_bidir_streams_queries(int32_t d, int32_t m) {
   return (d == 64 ? qapply_lds_bytes<64>(m) : qapply_lds_bytes<128>(m)) > 160 * 1024;

@@ -112,6 +112,7 @@ SHAPES = [
     (2, 2, 333, 64, 192),
     (1, 2, 700, 128, 512),    # bidirectional: two key feature blocks, streamed query side
     (1, 1, 500, 64, 768),     # bidirectional: two key feature blocks, streamed query side
+    (1, 2, 300, 128, 256),    # bidirectional: wide heads, query operands resident in LDS
 ]
 
 
