@@ -325,6 +325,33 @@ def main():
     torch.cuda.synchronize()
     kt = fv.timing_stop()
 
+    # Projection redraw (workloads that redraw W every k calls): the same K
+    # steps again with a fresh host draw (favor_draw_projection, seed
+    # s_W + call // k) uploaded synchronously before every k-th call.
+    redraw = None
+    if w.redraw_every:
+        Wn = torch.empty_like(W)
+        t_draw = 0.0
+        torch.cuda.synchronize()
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for i in range(args.steps):
+            if i % w.redraw_every == 0:
+                td = time.perf_counter()
+                Wh = torch.from_numpy(fv.draw_projection(w.seed_w + i // w.redraw_every, w.m, w.d))
+                t_draw += time.perf_counter() - td
+                Wn.copy_(Wh)           # host -> device, ordered on the stream
+            q, k, v, o = sets[i % nsets]
+            fwd(q, k, v, Wn, out=o, workspace=ws, stream=stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        ms_r = r0.elapsed_time(r1) / args.steps
+        ndraw = -(-args.steps // w.redraw_every)
+        redraw = {"every": w.redraw_every, "ms_per_step": round(ms_r, 5),
+                  "overhead_ms_per_step": round(ms_r - ms, 5),
+                  "host_draw_ms": round(1e3 * t_draw / ndraw, 3)}
+
     tokens = w.heads * w.L
     value = tokens / (ms * 1e-3)
     alg_bytes = 4 * w.heads * w.L * w.d * elem                 # Q, K, V read + O written once
@@ -379,6 +406,8 @@ def main():
         "roofline_whole_call": whole,
         "kernels": kernels,
     }
+    if redraw:
+        out["redraw"] = redraw
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

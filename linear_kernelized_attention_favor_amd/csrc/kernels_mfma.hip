@@ -89,8 +89,10 @@ struct KCfg {
 };
 
 // ---------------------------------------------------------------------------
-// kpart: grid (nsplit, BH, m / (NW FPW)), TG x NW waves of 64 threads; wave
-// w of feature block z owns features [(z NW + w) FPW, (z NW + w + 1) FPW).
+// kpart: grid (BH x nsplit_run x m / (NW FPW)) items, TG x NW waves of 64
+// threads; wave w of feature block z owns features [(z NW + w) FPW,
+// (z NW + w + 1) FPW).  nsplit_run <= nsplit splits are computed (the causal
+// form skips the last segment); the layout keeps nsplit slots per head.
 // Output: P [BH][nsplit][D+1][m] fp32 (row D = z) and cs [BH][nsplit][m]
 // fp32 (per-feature references, log2 units).
 // ---------------------------------------------------------------------------
@@ -117,7 +119,8 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
                                                  const uint16_t* __restrict__ V,
                                                  const float* __restrict__ W,
                                                  float* __restrict__ P, float* __restrict__ cs,
-                                                 int L, int m, int SL, int nsplit) {
+                                                 int L, int m, int SL, int nsplit,
+                                                 int nsplit_run) {
   using C = KCfg<D>;
   using LD = KLds<D, NW, TG>;
   constexpr int NTH = NW * 64;               // threads per token group
@@ -125,15 +128,20 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   constexpr int KPT = (KCH + NTH - 1) / NTH;
   constexpr int VUN = (kTT / 2) * (D / 4);   // (token pair, 4-column group) units per tile
   constexpr int VPT = (VUN + NTH - 1) / NTH;
-  const int s = blockIdx.x, bh = blockIdx.y;
+  // 1-D grid of (head, split, feature block) items in XCD-major order, the
+  // feature block fastest: the blocks of one split read the same K and V
+  // tiles on one XCD at about the same time (one HBM read, L2 hits after).
+  const int nfb = m / LD::M;
+  const int item = xcd_major(blockIdx.x, gridDim.x);
+  const int fb = item % nfb, s = (item / nfb) % nsplit_run, bh = item / (nfb * nsplit_run);
   // (wave-uniform: tells the compiler that per-group values are scalar)
   const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / NTH);
   const int tid = threadIdx.x % NTH, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  // Feature block blockIdx.z: features [z NW FPW, (z+1) NW FPW) (several
-  // blocks when m needs more than 8 waves); f0 is global, fl0 block-local.
+  // Feature block fb: features [fb NW FPW, (fb+1) NW FPW) (several blocks
+  // when m needs more than 8 waves); f0 is global, fl0 block-local.
   const int fl0 = wave * C::FPW;
-  const int f0 = static_cast<int>(blockIdx.z) * LD::M + fl0;
+  const int f0 = fb * LD::M + fl0;
 
   // Per group, a three-stage ring: tile t's V^T, tile t+1's K (projection
   // running ahead) and tile t+2 being written.
@@ -1572,8 +1580,8 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   // Two token groups while a work-group stays within 8 waves (two per SIMD).
   constexpr int TG = (NW <= 4) ? 2 : 1;
   timing_before(st);
-  kpart<D, NW, TG><<<dim3(p.nseg, p.BH, NFB), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
-                                                                     p.seg, p.nseg);
+  kpart<D, NW, TG><<<dim3(p.nseg * p.BH * NFB), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
+                                                                       p.seg, p.nseg, p.nseg);
   hipError_t e = hipGetLastError();
   timing_after(st, "kpart");
   if (e != hipSuccess) return e;
@@ -1617,8 +1625,8 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     // Key states of every segment but the last (grid nseg - 1; the layout
     // keeps nseg slots per head).
     timing_before(st);
-    kpart<64, NW, 1><<<dim3(p.nseg - 1, p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
-                                                                 p.seg, p.nseg);
+    kpart<64, NW, 1><<<dim3((p.nseg - 1) * p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
+                                                                    p.seg, p.nseg, p.nseg - 1);
     e = hipGetLastError();
     timing_after(st, "kpart");
     if (e != hipSuccess) return e;
