@@ -291,3 +291,34 @@ def test_kernel_timing_records_each_launch(fv):
     torch.cuda.synchronize()
     fv.timing_start()
     assert fv.timing_stop() == {}
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 1000, 64, 256), (1, 1, 700, 128, 512), (1, 1, 3000, 64, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_late_exponent_spikes_force_rereferencing(fv, shape):
+    # A few keys and queries late in the sequence lie exactly along one
+    # projection row: their exponent for that feature, |w|^2 / 2 (about 46
+    # log2 units at d = 64), exceeds everything in the first tile or chunk by
+    # far more than the kernels' headroom, so the mid-stream re-reference
+    # paths (accumulator rescale, already-projected tiles shifted) run.
+    B, H, L, d, m = shape
+    rng = np.random.default_rng(sum(shape))
+    s = d ** -0.25
+    q = rng.standard_normal((B, H, L, d)) * s
+    k = rng.standard_normal((B, H, L, d)) * s
+    v = rng.standard_normal((B, H, L, d))
+    W = _w(99 + d + m, m, d)
+    # the longest rows give the largest exponents (|w|^2 / 2); queries use
+    # rows outside the first 64-feature chunk
+    big = np.argsort(-(W.astype(np.float64) ** 2).sum(1))
+    late = [f for f in big if f >= 64][:3]
+    for j, fk, fq in zip((L // 3, L // 2, L - 3), big[:3], late):
+        k[:, :, j, :] = W[fk]
+        q[:, :, j + 1, :] = W[fq]
+    qt, kt, vt = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16) for x in (q, k, v))
+    for causal in ((False, True) if d == 64 else (False,)):
+        out = _np64(_run(fv, causal, qt, kt, vt, W))
+        ref = _ref(causal, qt, kt, vt, W)
+        err = oracle.row_rel_err(out, ref)
+        print(f"spikes {shape} causal={causal}: {err:.3e}", flush=True)
+        assert np.isfinite(out).all() and err <= TOL["bf16"], (causal, err)
