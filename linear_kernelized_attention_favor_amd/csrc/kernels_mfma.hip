@@ -110,8 +110,7 @@ struct KLds {
   static constexpr int NA_BYTES = 3 * kTT * NAROW * 2;   // per token: 1, 1, n_hi, n_lo, 0 ...
   static constexpr int RING = KS_BYTES + VT_BYTES + NA_BYTES;
   static constexpr int M = NW * C::FPW;                          // features
-  static constexpr int XCH = (TG > 1) ? ((D + 1) * M + M) * 4 : 0;   // state + references
-  static constexpr int BYTES = (TG * RING > XCH) ? TG * RING : XCH;
+  static constexpr int BYTES = TG * RING;
 };
 
 template <int D, int NW, int TG>
@@ -158,23 +157,26 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
     reinterpret_cast<uint4*>(Na)[i] = make_uint4(0, 0, 0, 0);
   lds_barrier();
 
-  // Projection B operands, kept in registers: W'[f][32 ks + 8 g + u].
+  // Projection B operands, kept in registers: W'[f][32 ks + 8 g + u]
+  // (loaded in the prologue, together with the first tiles).
   f16x8 wb[C::NT][C::KS];
+  auto load_w = [&]() {
 #pragma unroll
-  for (int nt = 0; nt < C::NT; ++nt) {
-    const float* wr = W + static_cast<size_t>(f0 + 16 * nt + l16) * D + 8 * g;
+    for (int nt = 0; nt < C::NT; ++nt) {
+      const float* wr = W + static_cast<size_t>(f0 + 16 * nt + l16) * D + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const float4 a = *reinterpret_cast<const float4*>(wr + 32 * ks);
-      const float4 b = *reinterpret_cast<const float4*>(wr + 32 * ks + 4);
-      f16x8 v;
-      v[0] = static_cast<_Float16>(a.x * kLog2e); v[1] = static_cast<_Float16>(a.y * kLog2e);
-      v[2] = static_cast<_Float16>(a.z * kLog2e); v[3] = static_cast<_Float16>(a.w * kLog2e);
-      v[4] = static_cast<_Float16>(b.x * kLog2e); v[5] = static_cast<_Float16>(b.y * kLog2e);
-      v[6] = static_cast<_Float16>(b.z * kLog2e); v[7] = static_cast<_Float16>(b.w * kLog2e);
-      wb[nt][ks] = v;
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const float4 a = *reinterpret_cast<const float4*>(wr + 32 * ks);
+        const float4 b = *reinterpret_cast<const float4*>(wr + 32 * ks + 4);
+        f16x8 v;
+        v[0] = static_cast<_Float16>(a.x * kLog2e); v[1] = static_cast<_Float16>(a.y * kLog2e);
+        v[2] = static_cast<_Float16>(a.z * kLog2e); v[3] = static_cast<_Float16>(a.w * kLog2e);
+        v[4] = static_cast<_Float16>(b.x * kLog2e); v[5] = static_cast<_Float16>(b.y * kLog2e);
+        v[6] = static_cast<_Float16>(b.z * kLog2e); v[7] = static_cast<_Float16>(b.w * kLog2e);
+        wb[nt][ks] = v;
+      }
     }
-  }
+  };
 
   f32x4 acc[C::MV + 1][C::NT];
 #pragma unroll
@@ -205,8 +207,10 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   // at the start of step t+1.  Buffer loads past the split's end return
   // zeros (the tail needs no per-lane branch); per-thread byte offsets
   // within a tile are fixed.
-  uint4 kreg[KPT];
-  uint2 vreg[VPT][2];
+  using KRegs = uint4[KPT];
+  using VRegs = uint2[VPT][2];
+  KRegs kreg;
+  VRegs vreg;
   int kvo[KPT], vvo[VPT];
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
@@ -218,26 +222,27 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
     const int u = tid + i * NTH;
     vvo[i] = (u < VUN) ? (2 * (u % 16) * D + 4 * (u / 16)) * 2 : kBufOff;
   }
-  auto gload = [&](int t) {
+  auto gload_to = [&](int t, KRegs& kr, VRegs& vr) {
     const int jt = tile0(t);
     const int bytes = max(0, j1 - jt) * D * 2;
     const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(K + base + static_cast<size_t>(jt) * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(V + base + static_cast<size_t>(jt) * D, bytes);
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) kreg[i] = buffer_load16(rk, kvo[i]);
+    for (int i = 0; i < KPT; ++i) kr[i] = buffer_load16(rk, kvo[i]);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      vreg[i][0] = buffer_load8(rv, vvo[i]);
-      vreg[i][1] = buffer_load8(rv, vvo[i] + D * 2);
+      vr[i][0] = buffer_load8(rv, vvo[i]);
+      vr[i][1] = buffer_load8(rv, vvo[i] + D * 2);
     }
   };
-  auto lstore = [&](int buf, int t) {
+  auto gload = [&](int t) { gload_to(t, kreg, vreg); };
+  auto lstore_from = [&](int buf, int t, const KRegs& kr, const VRegs& vr) {
     const int jt = tile0(t);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + i * NTH;
       const int j = (c / C::CPR) % kTT, ch = c % C::CPR;
-      const uint4 kv = kreg[i];
+      const uint4 kv = kr[i];
       float ss = 0.f;
       {
         const uint32_t w4[4] = {kv.x, kv.y, kv.z, kv.w};
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
       if (u < VUN) {
         const int col = 4 * (u / 16);
         const int w = perm_inv(2 * (u % 16)) >> 1;
-        const uint2 a = vreg[i][0], b = vreg[i][1];
+        const uint2 a = vr[i][0], b = vr[i][1];
         Vt[buf][col + 0][w] = __builtin_amdgcn_perm(b.x, a.x, 0x05040100u);
         Vt[buf][col + 1][w] = __builtin_amdgcn_perm(b.x, a.x, 0x07060302u);
         Vt[buf][col + 2][w] = __builtin_amdgcn_perm(b.y, a.y, 0x05040100u);
@@ -285,6 +290,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
       }
     }
   };
+  auto lstore = [&](int buf, int t) { lstore_from(buf, t, kreg, vreg); };
 
   bf16x8 ones;
 #pragma unroll
@@ -377,12 +383,26 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   };
 
   // Prologue: tiles 0 and 1 staged, tile 2 in flight, tile 0's features
-  // formed (its reference set from the exact maximum).
-  gload(0);
-  lstore(0, 0);
-  gload(1);
-  lstore(1, 1);
-  gload(2);
+  // formed (its reference set from the exact maximum).  The loads of tiles
+  // 0..2 and of W' are all issued before the first wait (when a thread's
+  // share of a tile is one load of each kind: the registers are there).
+  if constexpr (KPT == 1 && VPT == 1) {
+    KRegs k0, k1;
+    VRegs v0, v1;
+    gload_to(0, k0, v0);
+    gload_to(1, k1, v1);
+    gload(2);
+    load_w();
+    lstore_from(0, 0, k0, v0);
+    lstore_from(1, 1, k1, v1);
+  } else {
+    load_w();
+    gload(0);
+    lstore(0, 0);
+    gload(1);
+    lstore(1, 1);
+    gload(2);
+  }
   lds_barrier();
   bf16x8 kbA[C::NT], kbB[C::NT];
   {
@@ -435,39 +455,40 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   if constexpr (TG > 1) {
     // Merge the groups' states into group 0's registers through LDS, one
     // group at a time, each rescaled to the larger of the two references.
-    float* const xs = reinterpret_cast<float*>(kp_smem);      // [D+1][M]
-    float* const xc = xs + (D + 1) * LD::M;                   // [M]
+    // Each lane moves its own registers (16-byte slots, lane-major, one
+    // slot row per accumulator tile, then z and the references): wave w of
+    // every group holds the same features in the same lanes.
+    constexpr int SL = NW * 64;
+    constexpr int NSLOT = C::MV * C::NT + 2;
+    static_assert(C::NT <= 4, "z and the references of a lane fit one slot each");
+    static_assert(NSLOT * SL * 16 <= LD::BYTES, "merge slots fit in the block's LDS");
+    f32x4* const xv = reinterpret_cast<f32x4*>(kp_smem) + wave * 64 + lane;
     for (int src = 1; src < TG; ++src) {
       __syncthreads();
       if (grp == src) {
         const bool empty = tile0(0) >= j1;   // the group saw no token of the split
+        f32x4 z4 = f32x4{0.f, 0.f, 0.f, 0.f}, c4 = z4;
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
-          const int f = fl0 + 16 * nt + l16;   // block-local
 #pragma unroll
-          for (int mv = 0; mv < C::MV; ++mv)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) xs[(16 * mv + 4 * g + v) * LD::M + f] = acc[mv][nt][v];
-          if (g == 0) {
-            xs[D * LD::M + f] = acc[C::MV][nt][0];
-            xc[f] = empty ? -INFINITY : cref[nt];
-          }
+          for (int mv = 0; mv < C::MV; ++mv) xv[(mv * C::NT + nt) * SL] = acc[mv][nt];
+          z4[nt] = acc[C::MV][nt][0];
+          c4[nt] = empty ? -INFINITY : cref[nt];
         }
+        xv[(C::MV * C::NT) * SL] = z4;
+        xv[(C::MV * C::NT + 1) * SL] = c4;
       }
       __syncthreads();
       if (grp == 0) {
+        const f32x4 z4 = xv[(C::MV * C::NT) * SL], c4 = xv[(C::MV * C::NT + 1) * SL];
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
-          const int f = fl0 + 16 * nt + l16;   // block-local
-          const float co = xc[f];
+          const float co = c4[nt];
           const float cn = fmaxf(cref[nt], co);
           const float a = fast_exp2(cref[nt] - cn), b = fast_exp2(co - cn);
 #pragma unroll
-          for (int mv = 0; mv < C::MV; ++mv)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              acc[mv][nt][v] = acc[mv][nt][v] * a + xs[(16 * mv + 4 * g + v) * LD::M + f] * b;
-          acc[C::MV][nt][0] = acc[C::MV][nt][0] * a + xs[D * LD::M + f] * b;
+          for (int mv = 0; mv < C::MV; ++mv) acc[mv][nt] = acc[mv][nt] * a + xv[(mv * C::NT + nt) * SL] * b;
+          acc[C::MV][nt][0] = acc[C::MV][nt][0] * a + z4[nt] * b;
           cref[nt] = cn;
         }
       }
@@ -1168,7 +1189,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   constexpr int VUN = (kTT / 2) * (D / 4);
   constexpr int VPT = (VUN + NTH - 1) / NTH;
   constexpr int KROW = D + 8;
-  constexpr int RROW = kTT + 4;              // floats per (wave, column) row of partial outputs
+  constexpr int CROW = D + 4;                // floats per (wave, query) row of partial outputs
   const int s = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
@@ -1180,9 +1201,10 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   __shared__ __align__(16) float Ns[2][kTT];
   // Per wave, one region holds first this chunk's K~ over the wave's features
   // (key rows; read only by the wave itself) and then the wave's partial
-  // outputs [column][query] (read by all after a barrier).
-  static_assert((D + 1) * RROW * 4 >= kTT * KROW * 2, "K~ tile fits the partial-output region");
-  __shared__ __align__(16) float ured[NW][(D + 1) * RROW];
+  // outputs [query][column], columns 0..D-1 the numerator, D the
+  // denominator (read by all after a barrier).
+  static_assert(kTT * CROW * 4 >= kTT * KROW * 2, "K~ tile fits the partial-output region");
+  __shared__ __align__(16) float ured[NW][kTT * CROW];
   __shared__ __align__(16) float cb[NW][64];                // per-feature references
   __shared__ __align__(16) float fac[NW][64];               // per-feature rescale factors
   __shared__ __align__(16) float mq[NW][kTT];               // per-wave row references
@@ -1448,14 +1470,15 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       }
     }
 
-    // (3) Partial output over the wave's features, num = Q~ [S|z] + A [V|1]
-    // (lane = value column, rows = queries); first the carried state, as bf16
-    // operands.
-    f32x4 num[2][TV];
+    // (3) Partial output over the wave's features, transposed:
+    // num^T = [S|z]^T Q~^T + [V|1]^T A^T (lane = query, rows = value columns
+    // 16 tv + 4 g + v); first the carried state, as bf16 operands (the same
+    // registers serve as the A operand [column][feature]).
+    f32x4 num[TV][2];
 #pragma unroll
-    for (int nq = 0; nq < 2; ++nq)
+    for (int tv = 0; tv < TV; ++tv)
 #pragma unroll
-      for (int tv = 0; tv < TV; ++tv) num[nq][tv] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int nq = 0; nq < 2; ++nq) num[tv][nq] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -1465,7 +1488,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
             bf16x8, make_uint4(pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]),
                                pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])));
 #pragma unroll
-        for (int nq = 0; nq < 2; ++nq) num[nq][tv] = mma_bf16(qt[kb2][nq], sb, num[nq][tv]);
+        for (int nq = 0; nq < 2; ++nq) num[tv][nq] = mma_bf16(sb, qt[kb2][nq], num[tv][nq]);
       }
     // (4) State update with this chunk's keys: [S|z] += K~^T [V|1].
 #pragma unroll
@@ -1507,30 +1530,30 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       }
     }
 
-    // ... and the in-chunk term.
+    // ... and the in-chunk term ([V|1]^T as the A operand: same registers).
 #pragma unroll
     for (int tv = 0; tv < TV; ++tv) {
       const bf16x8 vb = vop(buf, tv);
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq) num[nq][tv] = mma_bf16(ab[nq], vb, num[nq][tv]);
+      for (int nq = 0; nq < 2; ++nq) num[tv][nq] = mma_bf16(vb, ab[nq], num[tv][nq]);
     }
 
     wave_lds_fence();   // K~ tile read above; its region is overwritten next
 
-    // (6) Partial outputs to LDS, [wave][column][query], over the K~ tile
-    // (the wave's own step (3) is done with it).
+    // (6) Partial outputs to LDS, [wave][query][column], over the K~ tile
+    // (the wave's own step (3) is done with it); of the last column tile only
+    // the denominator's quad (g = 0: columns D..D+3).
 #pragma unroll
-    for (int nq = 0; nq < 2; ++nq)
+    for (int tv = 0; tv < TV; ++tv)
 #pragma unroll
-      for (int tv = 0; tv < TV; ++tv) {
-        const int col = 16 * tv + l16;
-        if (col <= D) *reinterpret_cast<f32x4*>(&ured[wave][col * RROW + 16 * nq + 4 * g]) = num[nq][tv];
-      }
+      for (int nq = 0; nq < 2; ++nq)
+        if (tv < TV - 1 || g == 0)
+          *reinterpret_cast<f32x4*>(&ured[wave][(16 * nq + l16) * CROW + 16 * tv + 4 * g]) = num[tv][nq];
     lds_barrier();
     // Combine the waves' partials (row references differ per wave) and
-    // write O: thread -> (query, 8 columns).
+    // write O: thread -> (query, 8 columns); eight threads cover one row.
     for (int o = tid; o < kTT * (D / 8); o += NTH) {
-      const int i = o % kTT, c0 = 8 * (o / kTT);
+      const int i = o / (D / 8), c0 = 8 * (o % (D / 8));
       float mw[NW], mx = -INFINITY;
 #pragma unroll
       for (int w = 0; w < NW; ++w) { mw[w] = mq[w][i]; mx = fmaxf(mx, mw[w]); }
@@ -1539,9 +1562,15 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const float sc = fast_exp2(mw[w] - mx);
-        den = fmaf(sc, ured[w][D * RROW + i], den);
+        const float* row = &ured[w][i * CROW];
+        den = fmaf(sc, row[D], den);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(row + c0);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(row + c0 + 4);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc8[c] = fmaf(sc, ured[w][(c0 + c) * RROW + i], acc8[c]);
+        for (int c = 0; c < 4; ++c) {
+          acc8[c] = fmaf(sc, a[c], acc8[c]);
+          acc8[4 + c] = fmaf(sc, b[c], acc8[4 + c]);
+        }
       }
       const float inv = 1.0f / den;
       if (jt + i < j1) {
