@@ -540,25 +540,45 @@ __global__ __launch_bounds__(256) void kcombine(const float* __restrict__ P,
   if (e >= (D + 16) * mq) return;
   const int row = e / mq, f = 4 * (e - row * mq);
   const float4* csq = reinterpret_cast<const float4*>(cs + static_cast<size_t>(bh) * nsplit * m + f);
+  const float4* pq = reinterpret_cast<const float4*>(
+      P + (static_cast<size_t>(bh) * nsplit * (D + 1) + (row <= D ? row : 0)) * m + f);
+  const size_t sstride = static_cast<size_t>(D + 1) * mq;
+  // Splits in batches of KB, every load of a batch issued before the first
+  // use (one memory round trip per batch); the running sum is rescaled when
+  // a later batch raises the reference.
+  constexpr int KB = 8;
   float4 cmax = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-  for (int s = 0; s < nsplit; ++s) {
-    const float4 c = csq[static_cast<size_t>(s) * mq];
-    cmax.x = fmaxf(cmax.x, c.x); cmax.y = fmaxf(cmax.y, c.y);
-    cmax.z = fmaxf(cmax.z, c.z); cmax.w = fmaxf(cmax.w, c.w);
-  }
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (row <= D) {
-    const float4* pq = reinterpret_cast<const float4*>(
-        P + (static_cast<size_t>(bh) * nsplit * (D + 1) + row) * m + f);
-    const size_t sstride = static_cast<size_t>(D + 1) * mq;
-    for (int s = 0; s < nsplit; ++s) {
-      const float4 c = csq[static_cast<size_t>(s) * mq];
-      const float4 v = pq[s * sstride];
-      a.x = fmaf(v.x, fast_exp2(c.x - cmax.x), a.x);
-      a.y = fmaf(v.y, fast_exp2(c.y - cmax.y), a.y);
-      a.z = fmaf(v.z, fast_exp2(c.z - cmax.z), a.z);
-      a.w = fmaf(v.w, fast_exp2(c.w - cmax.w), a.w);
+  for (int s0 = 0; s0 < nsplit; s0 += KB) {
+    float4 c[KB], v[KB];
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      const bool in = s0 + j < nsplit;
+      c[j] = in ? csq[static_cast<size_t>(s0 + j) * mq]
+                : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      v[j] = (in && row <= D) ? pq[(s0 + j) * sstride] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    float4 nm = cmax;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      nm.x = fmaxf(nm.x, c[j].x); nm.y = fmaxf(nm.y, c[j].y);
+      nm.z = fmaxf(nm.z, c[j].z); nm.w = fmaxf(nm.w, c[j].w);
+    }
+    // (a reference still at -inf means no split so far: its sum is zero)
+    a.x *= (cmax.x == -INFINITY) ? 0.f : fast_exp2(cmax.x - nm.x);
+    a.y *= (cmax.y == -INFINITY) ? 0.f : fast_exp2(cmax.y - nm.y);
+    a.z *= (cmax.z == -INFINITY) ? 0.f : fast_exp2(cmax.z - nm.z);
+    a.w *= (cmax.w == -INFINITY) ? 0.f : fast_exp2(cmax.w - nm.w);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+      if (s0 + j < nsplit) {
+        a.x = fmaf(v[j].x, fast_exp2(c[j].x - nm.x), a.x);
+        a.y = fmaf(v[j].y, fast_exp2(c[j].y - nm.y), a.y);
+        a.z = fmaf(v[j].z, fast_exp2(c[j].z - nm.z), a.z);
+        a.w = fmaf(v[j].w, fast_exp2(c[j].w - nm.w), a.w);
+      }
+    }
+    cmax = nm;
   }
   // Four features stay inside one 32-block; their permuted positions are
   // scattered within it.
