@@ -40,9 +40,9 @@ struct Plan {
   //   cfin [BH][m]             combined per-feature references
   // MFMA causal path:
   //   T    [BH][nseg][d+1][m]  per-segment key state, then its exclusive
-  //                            prefix over earlier segments, fp32
+  //                            prefix over earlier segments (s >= 1), fp32
   //   cseg [BH][nseg][m]       per-feature references of the segment states
-  //   cP   [BH][nseg][m]       references of the prefixes (-inf: empty)
+  //   cP   [BH][nseg][m]       references of the prefixes (s >= 1)
   size_t off_T, off_cseg, off_cP, off_KV, off_cfin;
   size_t bytes;
 };

@@ -650,21 +650,10 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
     copy(reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow),
          reinterpret_cast<uint4*>(Kzl), (D + 16) * kzrow / 8);
   }
-  for (int i = tid; i < m; i += NTH) {
-    const float c = cfin[static_cast<size_t>(bh) * m + i];
-    const _Float16 hi = static_cast<_Float16>(c);
-    const _Float16 lo = static_cast<_Float16>(c - static_cast<float>(hi));
-    chl[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) |
-             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) << 16);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's staging has landed
-  __syncthreads();   // the only barrier: LDS is read-only from here on
-
   const size_t base = static_cast<size_t>(bh) * L * D;
   const int q0 = qb * QL, q1 = min(L, q0 + QL);
   const int step = NW * C::TQ;
   const int tt0 = q0 + wave * C::TQ;
-  if (tt0 >= q1) return;
   const int ntile = (q1 - tt0 + step - 1) / step;
 
   // Q tiles: raw bf16 loads one tile ahead of their use.
@@ -683,6 +672,21 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
       }
     }
   };
+  // The wave's first tile is loaded while the staging is in flight.
+  Raw raw;
+  qload(tt0, raw);
+
+  for (int i = tid; i < m; i += NTH) {
+    const float c = cfin[static_cast<size_t>(bh) * m + i];
+    const _Float16 hi = static_cast<_Float16>(c);
+    const _Float16 lo = static_cast<_Float16>(c - static_cast<float>(hi));
+    chl[i] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) |
+             (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) << 16);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's staging has landed
+  __syncthreads();   // the only barrier: LDS is read-only from here on
+  if (tt0 >= q1) return;
+
   // Q^T operands: token tt + 16 nt + l16, dims 32 ks + 8 g .. +7, in fp16.
   auto convert = [&](const Raw& raw, Qop& qop) {
 #pragma unroll
@@ -835,9 +839,7 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
   // matrix cores while chunk k is applied, then its features are formed and
   // checked in the same step; a tile's last step projects the next tile's
   // first chunk.
-  Raw raw;
   Qop qcur;
-  qload(tt0, raw);
   convert(raw, qcur);
   if (ntile > 1) qload(tt0 + step, raw);
   reset();
@@ -1154,8 +1156,9 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
 
 // kprefix: grid (ceil((D+1) m / 1024), BH), 256 threads; a thread owns four
 // features of one row.  P[bh][s] becomes the sum of segments before s and
-// cP[bh][s] its per-feature reference (-inf for the first segment).  The last
-// segment's own state is never needed, so kpart leaves it out.
+// cP[bh][s] its per-feature reference, for s >= 1 (the scan starts the first
+// segment from a zero state and reads neither).  The last segment's own
+// state is never needed, so kpart leaves it out.
 template <int D>
 __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const float* __restrict__ cs,
                                                float* __restrict__ cP, int m, int nseg) {
@@ -1169,14 +1172,14 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
   for (int s = 0; s < nseg; ++s) {
     const size_t ci = (static_cast<size_t>(bh) * nseg + s) * m + f;
     float4* pp = reinterpret_cast<float4*>(P + ((static_cast<size_t>(bh) * nseg + s) * (D + 1) + row) * m + f);
-    if (row == 0) *reinterpret_cast<float4*>(cP + ci) = rc;
+    if (row == 0 && s > 0) *reinterpret_cast<float4*>(cP + ci) = rc;
     if (s + 1 == nseg) {
-      *pp = run;
+      if (s > 0) *pp = run;
       break;
     }
     const float4 ts = *pp;
     const float4 c = *reinterpret_cast<const float4*>(cs + ci);
-    *pp = run;
+    if (s > 0) *pp = run;
     float4 nc;
     nc.x = fmaxf(rc.x, c.x); nc.y = fmaxf(rc.y, c.y); nc.z = fmaxf(rc.z, c.z); nc.w = fmaxf(rc.w, c.w);
     run.x = run.x * fast_exp2(rc.x - nc.x) + ts.x * fast_exp2(c.x - nc.x);
