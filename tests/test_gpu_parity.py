@@ -143,6 +143,57 @@ def test_text_shape_L128_brute_force(fv, causal):
         np.testing.assert_allclose(_np64(out)[..., 0, :], _np64(v)[..., 0, :], rtol=8e-3, atol=1e-6)
 
 
+def test_long_single_head_many_splits(fv):
+    # One head of 20000 tokens: 79 key-side splits, the combine's batches of
+    # eight splits with a ragged last batch.
+    B, H, L, d, m = 1, 1, 20000, 64, 256
+    q, k, v = _case(B, H, L, d, m, "bf16", seed=5)
+    W = _w(7, m, d)
+    out = _run(fv, False, q, k, v, W)
+    err = oracle.row_rel_err(_np64(out), _ref(False, q, k, v, W))
+    assert err <= TOL["bf16"], err
+
+
+def test_workspace_reuse_and_garbage(fv):
+    # Whatever the workspace holds before a call (never-written memory, an
+    # earlier call's partial states) must not change the result.
+    B, H, L, d, m = 2, 2, 1500, 64, 256
+    q, k, v = _case(B, H, L, d, m, "bf16", seed=3)
+    W = torch.from_numpy(_w(11, m, d)).cuda()
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    need = fv.workspace_bytes(B, H, L, d, m, 1, False)
+    ref = fv.fwd_bidir(qd, kd, vd, W)
+    for fill in (0x00, 0xFF, 0x01):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        for _ in range(3):   # the later calls see the counters of the earlier ones
+            out = fv.fwd_bidir(qd, kd, vd, W, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), fill
+
+
+def test_graph_replays_match_eager(fv):
+    # The forward pass captured once in a HIP graph and replayed on new
+    # inputs gives the eager results, replay after replay.
+    B, H, L, d, m = 1, 4, 3000, 64, 256
+    W = torch.from_numpy(_w(13, m, d)).cuda()
+    cases = [[x.cuda() for x in _case(B, H, L, d, m, "bf16", seed=40 + i)] for i in range(4)]
+    qs, ks, vs = (x.clone() for x in cases[0])
+    ws = torch.zeros(fv.workspace_bytes(B, H, L, d, m, 1, False), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(qs)
+    fv.fwd_bidir(qs, ks, vs, W, out=out, workspace=ws)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fv.fwd_bidir(qs, ks, vs, W, out=out, workspace=ws)
+    for q, k, v in cases[1:] + cases[:1]:
+        qs.copy_(q); ks.copy_(k); vs.copy_(v)
+        g.replay()
+        torch.cuda.synchronize()
+        eager = fv.fwd_bidir(q, k, v, W)
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads: the whole launch on the GPU, sampled heads on the oracle.
 # ---------------------------------------------------------------------------
