@@ -42,8 +42,10 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # (a few hundred untimed calls first: the clocks settle within ~10 ms of
+    # continuous work; 500 timed calls of the text workload take ~35 ms)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="text_bidir")
     ap.add_argument("--causal", action="store_true", help="time the causal form of the workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
