@@ -73,6 +73,20 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def measured_counters(workload: str, causal: bool, kernel: str):
+    """Executed-MFMA fraction of the bf16 peak of `kernel` from the committed
+    counter summary (its own rocprofv3 duration), or None (absent or stale)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(f"{workload}{'-causal' if causal else ''}")
+    if not e or e.get("kernel_src_digest") != kernel_source_digest():
+        return None
+    return e.get("kernels", {}).get(kernel, {}).get("mfma_frac")
+
+
 def measured_traffic(workload: str, causal: bool, kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or None.
 
@@ -139,7 +153,14 @@ def cpu_baseline(w, seconds: float):
         spent += time.perf_counter() - t0
         heads += 1
     tok = heads * w.L
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": tok / spent, "unit": "tokens*heads/s", "cores": int(threads),
+            "host_cores": len(os.sched_getaffinity(0)), "cpu_model": model,
             "kind": "oracle",
             "sample": f"{heads} of {w.heads} heads of {w.name} (L={w.L}, d={w.d}, m={w.m}, "
                       f"{'causal' if w.causal else 'bidirectional'}), fp64 numpy, "
@@ -205,6 +226,20 @@ def _pmc_rows(d):
     return out
 
 
+def _kernel_avg_ns(stats_dir):
+    """Average duration (ns) of each libfavor kernel from a rocprofv3 --stats tree."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                k = _favor_kernel(r["Name"])
+                if k:
+                    out[k] = float(r["AverageNs"])
+    return out
+
+
 def _mean_by_kernel(rows, counter):
     acc = {}
     for k, c, v in rows:
@@ -242,6 +277,33 @@ def pmc_summary(root: str, workload: str, causal: bool):
                       "bytes_per_launch": round(fb + wb), "dispatches": fetch[k][1]}
         lines.append(f"{k:10s} {fetch[k][1]:10d} {fetch[k][0]:14.1f} {write[k][0]:14.1f} "
                      f"{fb / 1e6:10.2f} {wb / 1e6:10.2f} {(fb + wb) / 1e6:10.2f}")
+    # Matrix-core and transcendental work from a third pass (when present):
+    # SQ_INSTS_VALU_MFMA_MOPS_* count 512-flop units of executed MFMA work,
+    # SQ_INSTS_VALU_TRANS_F32 wave-level transcendental instructions (the
+    # exponentials); rates use each kernel's average duration from the
+    # kernel-trace pass in the same directory.
+    mfma_dir = os.path.join(root, "mfma")
+    if os.path.isdir(mfma_dir):
+        rows = _pmc_rows(mfma_dir)
+        bf = _mean_by_kernel(rows, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        hf = _mean_by_kernel(rows, "SQ_INSTS_VALU_MFMA_MOPS_F16")
+        tr = _mean_by_kernel(rows, "SQ_INSTS_VALU_TRANS_F32")
+        dur = _kernel_avg_ns(os.path.join(root, "stats"))
+        lines.append(f"{'kernel':10s} {'MFMA GFLOP':>11s} {'avg us':>8s} {'TFLOP/s':>9s} "
+                     f"{'of 2.5 PF':>9s} {'exp insts':>10s}")
+        for k, e in kernels.items():
+            if k not in bf:
+                continue
+            fl = 512.0 * (bf[k][0] + hf.get(k, (0.0, 0))[0])
+            e["mfma_flops_executed"] = round(fl)
+            e["trans_insts"] = round(tr.get(k, (0.0, 0))[0])
+            if k in dur:
+                tf = fl / dur[k] / 1e3
+                e["avg_us"] = round(dur[k] / 1e3, 3)
+                e["mfma_tflops_executed"] = round(tf, 1)
+                e["mfma_frac"] = round(tf / BF16_PEAK_TFLOPS, 4)
+                lines.append(f"{k:10s} {fl / 1e9:11.2f} {dur[k] / 1e3:8.2f} {tf:9.1f} "
+                             f"{tf / BF16_PEAK_TFLOPS:9.3f} {e['trans_insts']:10d}")
     key = f"{workload}{'-causal' if causal else ''}"
     try:
         with open(TRAFFIC_FILE) as fh:
@@ -315,6 +377,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+
+    def timed(calls, pick):
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(calls):
+            pick(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / calls
+
+    # Spread: the same K calls timed five more times (min, median, max), and
+    # the cache-hot figure (one buffer set, the inputs resident in the
+    # 256 MB last-level cache where they fit), labelled as such.
+    reps = sorted(timed(args.steps, step) for _ in range(5))
+    q0, k0, v0, o0 = sets[0]
+    hot = timed(args.steps, lambda i: fwd(q0, k0, v0, W, out=o0, workspace=ws, stream=stream))
     # Per-kernel durations: the same K steps again, with the library
     # recording a HIP event on `stream` before and after each of its kernel
     # launches.  A second pass, because event records between kernels add a
@@ -350,9 +430,46 @@ def main():
         torch.cuda.synchronize()
         ms_r = r0.elapsed_time(r1) / args.steps
         ndraw = -(-args.steps // w.redraw_every)
+        # Overlapped: a host thread draws the next window's W while the
+        # current window's calls run; each draw lands in pinned host memory
+        # and goes up with a non-blocking copy into the other of two device
+        # W buffers, ordered on the stream before the window's first call.
+        import concurrent.futures as cf
+        Wd = [torch.empty_like(W), torch.empty_like(W)]
+        Wp = [torch.empty(W.shape, dtype=W.dtype, pin_memory=True) for _ in range(2)]
+        upl = [torch.cuda.Event(), torch.cuda.Event()]
+        seed_of = lambda win: w.seed_w + win
+        draw = lambda win: fv.draw_projection(seed_of(win), w.m, w.d)
+        o0_ = torch.cuda.Event(enable_timing=True)
+        o1_ = torch.cuda.Event(enable_timing=True)
+        with cf.ThreadPoolExecutor(max_workers=1) as pool:
+            # window 0's W is in place before the timed region, window 1's
+            # draw already running
+            Wp[0].copy_(torch.from_numpy(draw(0)))
+            Wd[0].copy_(Wp[0])
+            nxt = pool.submit(draw, 1)
+            torch.cuda.synchronize()
+            o0_.record(stream)
+            for i in range(args.steps):
+                win = i // w.redraw_every
+                if i % w.redraw_every == 0 and win > 0:
+                    slot = win % 2
+                    upl[slot].synchronize()          # the pinned buffer's last upload is done
+                    Wp[slot].copy_(torch.from_numpy(nxt.result()))
+                    Wd[slot].copy_(Wp[slot], non_blocking=True)
+                    upl[slot].record(stream)
+                    nxt = pool.submit(draw, win + 1)
+                q, k, v, o = sets[i % nsets]
+                fwd(q, k, v, Wd[win % 2], out=o, workspace=ws, stream=stream)
+            o1_.record(stream)
+            torch.cuda.synchronize()
+            nxt.result()
+        ms_o = o0_.elapsed_time(o1_) / args.steps
         redraw = {"every": w.redraw_every, "ms_per_step": round(ms_r, 5),
                   "overhead_ms_per_step": round(ms_r - ms, 5),
-                  "host_draw_ms": round(1e3 * t_draw / ndraw, 3)}
+                  "host_draw_ms": round(1e3 * t_draw / ndraw, 3),
+                  "overlapped_ms_per_step": round(ms_o, 5),
+                  "overlapped_overhead_ms_per_step": round(ms_o - ms, 5)}
 
     tokens = w.heads * w.L
     value = tokens / (ms * 1e-3)
@@ -382,6 +499,9 @@ def main():
     dsec = kt[dom][0] / kt[dom][1] * 1e-3
     roof = roofline(kernels[dom]["alg_bytes"], kernels[dom]["alg_flops"], dsec)
     roof["traffic"] = measured_traffic(w.name, w.causal, dom)
+    mf = measured_counters(w.name, w.causal, dom)
+    if mf is not None:
+        roof["mfma_executed_frac"] = mf
     roof["kernel"] = dom
     roof["kernel_avg_us"] = kernels[dom]["avg_us"]
     whole = roofline(alg_bytes, alg_flops, ms * 1e-3)
@@ -402,6 +522,9 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m,
                    "causal": w.causal, "buffer_sets": nsets,
                    "cache": "hot" if args.cache_hot else "rotating >= 1 GiB"},
+        "repeats": {"n": len(reps), "min_ms": round(reps[0], 5),
+                    "median_ms": round(reps[len(reps) // 2], 5), "max_ms": round(reps[-1], 5)},
+        "cache_hot_ms_per_step": round(hot, 5),
         "tflops_alg": round(achieved_tflops, 2),
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
