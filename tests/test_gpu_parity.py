@@ -113,6 +113,10 @@ SHAPES = [
     (1, 2, 700, 128, 512),    # bidirectional: two key feature blocks, streamed query side
     (1, 1, 500, 64, 768),     # bidirectional: two key feature blocks, streamed query side
     (1, 2, 300, 128, 256),    # bidirectional: wide heads, query operands resident in LDS
+    (1, 1, 1, 64, 256),       # matrix-core path with one token (every tile ragged)
+    (1, 3, 31, 64, 256),      # one partial 32-token tile per head
+    (1, 1, 33, 128, 512),     # streamed query side with a 1-token second tile
+    (3, 1, 257, 64, 128),     # odd head count, one token past a tile boundary
 ]
 
 
