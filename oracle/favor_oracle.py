@@ -36,6 +36,12 @@ design notes):
   norms are drawn independently from chi(d), so each row is marginally
   N(0, I_d).
 * The masked form includes the diagonal: token i attends to tokens j <= i.
+* The method page says the mechanism approximates softmax and Gaussian
+  kernels but prints the features of neither.  For the Gaussian kernel
+  ``exp(-|x-y|^2/2) = exp(-|x|^2/2) exp(-|y|^2/2) exp(x^T y)`` the features
+  are read as the softmax-kernel features times ``exp(-|x|^2/2)``:
+  ``phi_G(x) = exp(w_r^T x - |x|^2) / sqrt(m)``, positive, with expectation
+  exactly ``exp(-|x-y|^2/2)``.
 * The random stream is a counter-based SplitMix64 (Steele, Lea & Flood,
   "Fast splittable pseudorandom number generators", OOPSLA 2014) feeding the
   Box-Muller transform; the pages name no generator.
@@ -60,12 +66,14 @@ __all__ = [
     "draw_w",
     "draw_w_iid",
     "phi",
+    "phi_gaussian",
     "attend_bidir",
     "attend_causal",
     "bidir",
     "causal",
     "brute",
     "softmax_attention",
+    "gaussian_attention",
     "row_rel_err",
 ]
 
@@ -174,6 +182,31 @@ def phi(X: np.ndarray, W: np.ndarray) -> np.ndarray:
     return out
 
 
+def phi_gaussian(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Positive random features of the Gaussian kernel exp(-|x - y|^2 / 2).
+
+    phi_G(x) = exp(W x - |x|^2) / sqrt(m): the softmax-kernel features times
+    exp(-|x|^2 / 2), so that E[phi_G(x)^T phi_G(y)] = exp(-|x - y|^2 / 2).
+    Shapes as phi.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    m = W.shape[0]
+    s = X @ W.T - np.sum(X * X, axis=-1, keepdims=True)
+    out = np.exp(s) / math.sqrt(m)
+    assert np.all(np.isfinite(out)), "feature exponent out of fp64 range"
+    return out
+
+
+def _features(kernel: str):
+    """The feature map of `kernel` ("softmax" or "gaussian"), looked up at call time."""
+    if kernel == "softmax":
+        return phi
+    if kernel == "gaussian":
+        return phi_gaussian
+    raise ValueError(f"unknown kernel {kernel!r}")
+
+
 def attend_bidir(Qp: np.ndarray, Kp: np.ndarray, V: np.ndarray) -> np.ndarray:
     """FA-part with given features: D^-1 (Q' ((K')^T V)), D = diag(Q' ((K')^T 1_L)).
 
@@ -219,19 +252,22 @@ def attend_causal(Qp: np.ndarray, Kp: np.ndarray, V: np.ndarray) -> np.ndarray:
     return out
 
 
-def bidir(Q, K, V, W) -> np.ndarray:
+def bidir(Q, K, V, W, kernel: str = "softmax") -> np.ndarray:
     """Bidirectional FAVOR+ forward: attend_bidir(phi(Q), phi(K), V) in fp64."""
-    return attend_bidir(phi(Q, W), phi(K, W), np.asarray(V, dtype=np.float64))
+    f = _features(kernel)
+    return attend_bidir(f(Q, W), f(K, W), np.asarray(V, dtype=np.float64))
 
 
-def causal(Q, K, V, W) -> np.ndarray:
+def causal(Q, K, V, W, kernel: str = "softmax") -> np.ndarray:
     """Masked (causal) FAVOR+ forward in prefix-sum form, fp64."""
-    return attend_causal(phi(Q, W), phi(K, W), np.asarray(V, dtype=np.float64))
+    f = _features(kernel)
+    return attend_causal(f(Q, W), f(K, W), np.asarray(V, dtype=np.float64))
 
 
-def brute(Q, K, V, W, is_causal: bool) -> np.ndarray:
+def brute(Q, K, V, W, is_causal: bool, kernel: str = "softmax") -> np.ndarray:
     """O(L^2) form: A = Q' K'^T (lower-triangular if masked), out = A V / A 1_L."""
-    A = phi(Q, W) @ np.swapaxes(phi(K, W), -1, -2)
+    f = _features(kernel)
+    A = f(Q, W) @ np.swapaxes(f(K, W), -1, -2)
     if is_causal:
         L = A.shape[-1]
         A = A * np.tril(np.ones((L, L)))
@@ -250,6 +286,26 @@ def softmax_attention(Q, K, V, is_causal: bool = False) -> np.ndarray:
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     s = Q @ np.swapaxes(K, -1, -2)
+    if is_causal:
+        L = s.shape[-1]
+        s = np.where(np.tril(np.ones((L, L), dtype=bool)), s, -np.inf)
+    s = s - s.max(axis=-1, keepdims=True)
+    A = np.exp(s)
+    return (A @ V) / A.sum(axis=-1)[..., None]
+
+
+def gaussian_attention(Q, K, V, is_causal: bool = False) -> np.ndarray:
+    """Exact kernel attention with K(x,y) = exp(-|x - y|^2 / 2), no further scale.
+
+    The Gaussian kernel the features phi_G estimate, written from its
+    definition: A_ij = exp(-|q_i - k_j|^2 / 2), out = A V / A 1_L (each row
+    shifted by its largest exponent, which cancels).
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    diff = Q[..., :, None, :] - K[..., None, :, :]
+    s = -0.5 * np.sum(diff * diff, axis=-1)
     if is_causal:
         L = s.shape[-1]
         s = np.where(np.tril(np.ones((L, L), dtype=bool)), s, -np.inf)

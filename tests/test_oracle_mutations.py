@@ -14,7 +14,8 @@ import oracle.favor_oracle as fo
 import test_oracle_pins as pins
 
 # the real functions, saved before any patching, for mutants built on them
-_REAL = {n: getattr(fo, n) for n in ("draw_w", "attend_causal", "softmax_attention")}
+_REAL = {n: getattr(fo, n) for n in ("draw_w", "attend_causal", "softmax_attention",
+                                     "gaussian_attention")}
 
 
 def _phi_no_norm(X, W):
@@ -81,6 +82,25 @@ def _attend_causal_off_by_one(Qp, Kp, V):
     return out2
 
 
+def _phi_gaussian_half_norm(X, W):
+    # the softmax-kernel features under the Gaussian name
+    X = np.asarray(X, float)
+    s = X @ np.asarray(W, float).T - 0.5 * np.sum(X * X, axis=-1, keepdims=True)
+    return np.exp(s) / math.sqrt(W.shape[0])
+
+
+def _phi_gaussian_double_norm(X, W):
+    X = np.asarray(X, float)
+    s = X @ np.asarray(W, float).T - 2.0 * np.sum(X * X, axis=-1, keepdims=True)
+    return np.exp(s) / math.sqrt(W.shape[0])
+
+
+def _gaussian_attention_no_half(Q, K, V, is_causal=False):
+    # exp(-|q-k|^2) instead of exp(-|q-k|^2/2)
+    return _REAL["gaussian_attention"](np.asarray(Q) * math.sqrt(2), np.asarray(K) * math.sqrt(2),
+                                       V, is_causal)
+
+
 def _softmax_with_scale(Q, K, V, is_causal=False):
     return _REAL["softmax_attention"](np.asarray(Q) / math.sqrt(Q.shape[-1]), K, V, is_causal)
 
@@ -114,6 +134,11 @@ BIDIR_PINS = [
     (pins.test_P10_single_feature_closed_form, {}),
     (pins.test_bidir_is_a_convex_combination_of_values, {}),
 ]
+GAUSS_PINS = [
+    (pins.test_G1_gaussian_phi_x_dot_phi_minus_x, dict(m=16, d=16)),
+    (pins.test_G1_gaussian_phi_of_zero_and_positivity, {}),
+    (pins.test_G3_equal_key_norms_make_the_kernels_agree, {}),
+]
 CAUSAL_PINS = [
     (pins.test_P13_causal_first_and_last_rows, {}),
     (pins.test_causal_mask_includes_diagonal, {}),
@@ -131,6 +156,12 @@ CAUSAL_PINS = [
     ("bidir drops the normaliser", "attend_bidir", _attend_bidir_no_normaliser, BIDIR_PINS),
     ("causal excludes the diagonal", "attend_causal", _attend_causal_strict, CAUSAL_PINS),
     ("causal output lags one token", "attend_causal", _attend_causal_off_by_one, CAUSAL_PINS),
+    ("Gaussian features keep the softmax norm term", "phi_gaussian", _phi_gaussian_half_norm,
+     GAUSS_PINS),
+    ("Gaussian features double the norm term", "phi_gaussian", _phi_gaussian_double_norm,
+     GAUSS_PINS),
+    ("Gaussian attention drops the 1/2", "gaussian_attention", _gaussian_attention_no_half,
+     [(pins.test_G2_gaussian_attention_matches_library_softmax, {})]),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, target, mutant, pinset):
     monkeypatch.setattr(fo, target, mutant)
@@ -145,5 +176,5 @@ def test_softmax_scale_mistake_is_caught(monkeypatch):
 
 
 def test_real_oracle_passes_the_same_pins():
-    for pinset in (PHI_PINS, DRAW_PINS, BIDIR_PINS, CAUSAL_PINS):
+    for pinset in (PHI_PINS, DRAW_PINS, BIDIR_PINS, CAUSAL_PINS, GAUSS_PINS):
         assert _run_pins(pinset) == 0

@@ -404,3 +404,104 @@ def test_row_rel_err_metric():
     ref = np.array([[1.0, -2.0], [0.5, 0.25]])
     got = ref + np.array([[0.02, 0.0], [0.0, 0.01]])
     assert math.isclose(oracle.row_rel_err(got, ref), 0.02, rel_tol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The Gaussian kernel (FAVOR+ method page: the mechanism approximates softmax
+# and Gaussian kernels).  G1-G5 pin phi_gaussian and gaussian_attention the
+# way P4-P15 pin the softmax side.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,d", [(16, 16), (256, 64), (37, 8)])
+def test_G1_gaussian_phi_x_dot_phi_minus_x(m, d):
+    # exp(w.x - |x|^2) exp(-w.x - |x|^2) = exp(-2|x|^2) per feature, for every W
+    rng = _rng(7 * m + d)
+    W = rng.standard_normal((m, d)) * 1.3
+    X = rng.standard_normal((50, d)) * 0.6
+    lhs = np.sum(oracle.phi_gaussian(X, W) * oracle.phi_gaussian(-X, W), axis=1)
+    np.testing.assert_allclose(lhs, np.exp(-2 * np.sum(X * X, axis=1)), rtol=1e-13, atol=0)
+
+
+def test_G1_gaussian_phi_of_zero_and_positivity():
+    W = _rng(3).standard_normal((64, 8))
+    np.testing.assert_allclose(oracle.phi_gaussian(np.zeros((1, 8)), W), 1 / 8.0, rtol=1e-15)
+    assert np.all(oracle.phi_gaussian(_rng(4).standard_normal((20, 8)) * 2, W) > 0)
+
+
+def test_G2_gaussian_attention_matches_library_softmax():
+    # exp(-|q-k|^2/2) = exp(-|q|^2/2) exp(q.k - |k|^2/2): the query factor
+    # cancels per row, so the exact Gaussian attention is a softmax over
+    # q.k - |k|^2/2 (library routine)
+    rng = _rng(21)
+    Q = rng.standard_normal((2, 30, 8))
+    K = rng.standard_normal((2, 30, 8))
+    V = rng.standard_normal((2, 30, 8))
+    logits = Q @ np.swapaxes(K, -1, -2) - 0.5 * np.sum(K * K, axis=-1)[..., None, :]
+    A = scipy.special.softmax(logits, axis=-1)
+    np.testing.assert_allclose(oracle.gaussian_attention(Q, K, V), A @ V, rtol=1e-12)
+    mask = np.tril(np.ones((30, 30))) > 0
+    Ac = scipy.special.softmax(np.where(mask, logits, -np.inf), axis=-1)
+    np.testing.assert_allclose(oracle.gaussian_attention(Q, K, V, True), Ac @ V, rtol=1e-12)
+
+
+def test_G3_equal_key_norms_make_the_kernels_agree():
+    # with every key of the same norm the key factors exp(-|k|^2/2) are one
+    # common scalar and the query factors cancel per row: the Gaussian and the
+    # softmax FAVOR+ outputs coincide (same W); with unequal norms they differ
+    Q, K, V, W = _inputs(1, 2, 48, 16, 64, 23)
+    Ku = K / np.linalg.norm(K, axis=-1, keepdims=True) * 0.9
+    for f in (oracle.bidir, oracle.causal):
+        np.testing.assert_allclose(f(Q, Ku, V, W, kernel="gaussian"), f(Q, Ku, V, W),
+                                   rtol=1e-11, atol=1e-13)
+        assert np.max(np.abs(f(Q, K * 2, V, W, kernel="gaussian") - f(Q, K * 2, V, W))) > 1e-3
+
+
+def test_G3_gaussian_ones_rebracketing_and_brute_force():
+    Q, K, V, W = _inputs(2, 2, 64, 16, 32, 24)
+    ones = np.ones_like(V)
+    np.testing.assert_allclose(oracle.bidir(Q, K, ones, W, kernel="gaussian"), 1.0, atol=1e-14)
+    np.testing.assert_allclose(oracle.causal(Q, K, ones, W, kernel="gaussian"), 1.0, atol=1e-14)
+    np.testing.assert_allclose(oracle.bidir(Q, K, V, W, kernel="gaussian"),
+                               oracle.brute(Q, K, V, W, False, kernel="gaussian"), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oracle.causal(Q, K, V, W, kernel="gaussian"),
+                               oracle.brute(Q, K, V, W, True, kernel="gaussian"), rtol=1e-12, atol=1e-13)
+
+
+def _gauss_block_estimates(W, x, y, d):
+    nb = W.shape[0] // d
+    px = oracle.phi_gaussian(x[None, :], W)[0].reshape(nb, d) * math.sqrt(W.shape[0] / d)
+    py = oracle.phi_gaussian(y[None, :], W)[0].reshape(nb, d) * math.sqrt(W.shape[0] / d)
+    return np.sum(px * py, axis=1)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("norm2", [0.25, 1.0])
+def test_G4_unbiased_gaussian_kernel(norm2):
+    d, N = 16, 20_000
+    x, y = _pair(norm2, 61 + int(norm2 * 4))
+    W = oracle.draw_w(5151 + int(norm2 * 100), d * N, d)
+    est = _gauss_block_estimates(W, x, y, d)
+    target = math.exp(-0.5 * np.sum((x - y) ** 2))
+    # the softmax-kernel iid variance times the square of exp(-(|x|^2+|y|^2)/2)
+    var = ((math.exp(np.sum((x + y) ** 2)) - 1) * math.exp(2 * x @ y) / d
+           * math.exp(-(x @ x + y @ y)))
+    z = (est.mean() - target) / math.sqrt(var / N)
+    assert abs(z) < 4, z
+
+
+@pytest.mark.slow
+def test_G5_convergence_to_gaussian_attention():
+    # the Gaussian FAVOR+ output approaches the exact Gaussian attention as m grows
+    errs = []
+    for m in (16, 1024):
+        e = []
+        for s in range(6):
+            rng = _rng(900 + s)
+            Q = rng.standard_normal((128, 16)) * 16 ** -0.25 * 0.5
+            K = rng.standard_normal((128, 16)) * 16 ** -0.25 * 0.5
+            V = rng.standard_normal((128, 16))
+            W = oracle.draw_w(9500 + 13 * s + m, m, 16)
+            ref = oracle.gaussian_attention(Q, K, V)
+            e.append(np.linalg.norm(oracle.bidir(Q, K, V, W, kernel="gaussian") - ref)
+                     / np.linalg.norm(ref))
+        errs.append(np.mean(e))
+    assert errs[1] < 0.25 * errs[0], errs
