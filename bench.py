@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="text_bidir")
     ap.add_argument("--causal", action="store_true", help="time the causal form of the workload")
+    ap.add_argument("--kernel", choices=("softmax", "gaussian"), default="softmax",
+                    help="attention kernel the features estimate (default softmax)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -129,7 +131,7 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     return (0, 0.0)
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, kernel: str = "softmax"):
     """Time the fp64 oracle on whole heads of the same workload (host cores)."""
     import numpy as np
     import oracle
@@ -149,7 +151,7 @@ def cpu_baseline(w, seconds: float):
     q, k, v = (t.double().numpy()[0, 0] for t in workloads.host_qkv(w, heads=[0]))
     while spent < seconds and heads < w.heads:
         t0 = time.perf_counter()
-        f(q, k, v, W)
+        f(q, k, v, W, kernel=kernel)
         spent += time.perf_counter() - t0
         heads += 1
     tok = heads * w.L
@@ -162,7 +164,7 @@ def cpu_baseline(w, seconds: float):
     return {"value": tok / spent, "unit": "tokens*heads/s", "cores": int(threads),
             "host_cores": len(os.sched_getaffinity(0)), "cpu_model": model,
             "kind": "oracle",
-            "sample": f"{heads} of {w.heads} heads of {w.name} (L={w.L}, d={w.d}, m={w.m}, "
+            "sample": f"{heads} of {w.heads} heads of {w.name} ({kernel} kernel, L={w.L}, d={w.d}, m={w.m}, "
                       f"{'causal' if w.causal else 'bidirectional'}), fp64 numpy, "
                       f"{spent:.1f} s"}
 
@@ -357,7 +359,8 @@ def main():
         sets.append((q, k, v, torch.empty_like(q)))
     ws = torch.empty(fv.workspace_bytes(w.B, w.H, w.L, w.d, w.m, fv.BF16 if w.dtype == "bf16"
                                         else fv.F32, w.causal), dtype=torch.uint8, device=dev)
-    fwd = fv.fwd_causal if w.causal else fv.fwd_bidir
+    fwd_ = fv.fwd_causal if w.causal else fv.fwd_bidir
+    fwd = lambda *a, **kw: fwd_(*a, kernel=args.kernel, **kw)
     stream = torch.cuda.current_stream(dev)
 
     def step(i):
@@ -498,8 +501,9 @@ def main():
     dom = max(kt, key=lambda n: kt[n][0])
     dsec = kt[dom][0] / kt[dom][1] * 1e-3
     roof = roofline(kernels[dom]["alg_bytes"], kernels[dom]["alg_flops"], dsec)
-    roof["traffic"] = measured_traffic(w.name, w.causal, dom)
-    mf = measured_counters(w.name, w.causal, dom)
+    # (counter summaries exist for the softmax-kernel runs only)
+    roof["traffic"] = measured_traffic(w.name, w.causal, dom) if args.kernel == "softmax" else None
+    mf = measured_counters(w.name, w.causal, dom) if args.kernel == "softmax" else None
     if mf is not None:
         roof["mfma_executed_frac"] = mf
     roof["kernel"] = dom
@@ -520,7 +524,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian Q, K, V; orthogonal Gaussian W)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m,
-                   "causal": w.causal, "buffer_sets": nsets,
+                   "causal": w.causal, "attn_kernel": args.kernel, "buffer_sets": nsets,
                    "cache": "hot" if args.cache_hot else "rotating >= 1 GiB"},
         "repeats": {"n": len(reps), "min_ms": round(reps[0], 5),
                     "median_ms": round(reps[len(reps) // 2], 5), "max_ms": round(reps[-1], 5)},
@@ -534,7 +538,7 @@ def main():
     if redraw:
         out["redraw"] = redraw
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.kernel)
     print(json.dumps(out), flush=True)
 
 

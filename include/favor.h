@@ -63,11 +63,25 @@ enum favor_dtype {
   FAVOR_BF16 = 1
 };
 
+/*
+ * Attention kernel the features estimate (method page, section "FAVOR+": the
+ * mechanism approximates softmax and Gaussian kernels).  The features are
+ * phi(x)_r = exp(w_r . x - c |x|^2) / sqrt(m) with c = 1/2 for the softmax
+ * kernel exp(x . y) and c = 1 for the Gaussian kernel exp(-|x - y|^2 / 2)
+ * (the softmax features times exp(-|x|^2 / 2); the method page prints
+ * neither feature map, this is the reading taken).
+ */
+enum favor_attn_kernel {
+  FAVOR_SOFTMAX = 0,
+  FAVOR_GAUSSIAN = 1
+};
+
 enum favor_status {
   FAVOR_OK = 0,
   FAVOR_ERR_NULL = -1,        /* a required pointer is NULL                     */
   FAVOR_ERR_SHAPE = -2,       /* B, H or L < 1, or the tensor is too large      */
-  FAVOR_ERR_UNSUPPORTED = -3, /* d, m or dtype outside the supported set        */
+  FAVOR_ERR_UNSUPPORTED = -3, /* d, m, dtype or attention kernel outside the
+                                 supported set                                  */
   FAVOR_ERR_ALIGN = -4,       /* a tensor base is not 16-byte aligned, or the
                                  workspace base is not 256-byte aligned         */
   FAVOR_ERR_WORKSPACE = -5,   /* workspace_bytes below favor_workspace_bytes()  */
@@ -116,6 +130,20 @@ int favor_fwd_causal(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int3
                      void* O, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Either form with either attention kernel: favor_fwd_bidir (causal = 0) or
+ * favor_fwd_causal (causal != 0) with the features of `attn_kernel`
+ * (FAVOR_SOFTMAX: exactly those entry points; FAVOR_GAUSSIAN: the key
+ * features carry exp(-|k|^2), the query features' norm term cancels per
+ * row).  Arguments, workspace (favor_workspace_bytes does not depend on the
+ * kernel) and errors as favor_fwd_bidir; an unknown attn_kernel gives
+ * FAVOR_ERR_UNSUPPORTED before anything is enqueued.
+ */
+int favor_fwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                   int32_t causal, int32_t attn_kernel, const void* Q, const void* K,
+                   const void* V, const float* W, void* O, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * The feature map alone, for testing the projection and exponent arithmetic:
  * Xp[b,h,l,r] = exp(w_r . x_{b,h,l} - |x_{b,h,l}|^2 / 2) / sqrt(m), fp32
  * [B,H,L,m] in device memory, with no exponent shift (the caller keeps the
@@ -124,6 +152,16 @@ int favor_fwd_causal(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int3
  */
 int favor_feature_map(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                       const void* X, const float* W, float* Xp, void* stream);
+
+/*
+ * favor_feature_map with the features of `attn_kernel`:
+ * Xp[b,h,l,r] = exp(w_r . x - c |x|^2) / sqrt(m), c = 1/2 (FAVOR_SOFTMAX, the
+ * same as favor_feature_map) or 1 (FAVOR_GAUSSIAN).  Unknown attn_kernel:
+ * FAVOR_ERR_UNSUPPORTED.
+ */
+int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                           int32_t attn_kernel, const void* X, const float* W, float* Xp,
+                           void* stream);
 
 /*
  * Draw the projection W [m, d] (fp32, row-major, host memory) from `seed`:

@@ -16,12 +16,15 @@ import torch
 
 __all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
            "feature_map", "draw_projection", "status_string", "plan_describe", "timing_start", "timing_stop",
-           "F32", "BF16"]
+           "F32", "BF16", "SOFTMAX", "GAUSSIAN"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfavor.so")
 
 F32, BF16 = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+# attention kernel the features estimate (enum favor_attn_kernel)
+SOFTMAX, GAUSSIAN = 0, 1
+_KERNELS = {"softmax": SOFTMAX, "gaussian": GAUSSIAN, SOFTMAX: SOFTMAX, GAUSSIAN: GAUSSIAN}
 
 
 class FavorError(RuntimeError):
@@ -45,8 +48,12 @@ def _load():
         f = getattr(L, name)
         f.argtypes = [i32] * 6 + [vp, vp, vp, fp, vp, vp, sz, vp]
         f.restype = ctypes.c_int
+    L.favor_fwd_attn.argtypes = [i32] * 8 + [vp, vp, vp, fp, vp, vp, sz, vp]
+    L.favor_fwd_attn.restype = ctypes.c_int
     L.favor_feature_map.argtypes = [i32] * 6 + [vp, fp, vp, vp]
     L.favor_feature_map.restype = ctypes.c_int
+    L.favor_feature_map_attn.argtypes = [i32] * 7 + [vp, fp, vp, vp]
+    L.favor_feature_map_attn.restype = ctypes.c_int
     L.favor_draw_projection.argtypes = [ctypes.c_uint64, i32, i32, ctypes.c_void_p]
     L.favor_draw_projection.restype = ctypes.c_int
     L.favor_status_string.argtypes = [ctypes.c_int]
@@ -118,7 +125,15 @@ def _stream(q, stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _forward(name, causal, q, k, v, W, out, workspace, stream):
+def _kernel(kernel):
+    try:
+        return _KERNELS[kernel]
+    except KeyError:
+        raise ValueError(f"kernel must be 'softmax' or 'gaussian', not {kernel!r}") from None
+
+
+def _forward(name, causal, q, k, v, W, out, workspace, stream, kernel="softmax"):
+    ak = _kernel(kernel)
     B, H, L, d, m, dt = _shape_of(q, k, v, W)
     need = workspace_bytes(B, H, L, d, m, dt, causal)
     if out is None:
@@ -127,31 +142,43 @@ def _forward(name, causal, q, k, v, W, out, workspace, stream):
         raise ValueError("out must be a contiguous tensor like Q")
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
-    st = getattr(lib, name)(B, H, L, d, m, dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                            W.data_ptr(), out.data_ptr(), workspace.data_ptr(),
-                            workspace.numel() * workspace.element_size(), _stream(q, stream))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), out.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q, stream))
+    if ak == SOFTMAX:
+        st = getattr(lib, name)(B, H, L, d, m, dt, *ptrs)
+    else:
+        name = "favor_fwd_attn"
+        st = lib.favor_fwd_attn(B, H, L, d, m, dt, int(causal), ak, *ptrs)
     _check(st, name)
     return out
 
 
-def fwd_bidir(q, k, v, W, out=None, workspace=None, stream=None):
-    """Bidirectional FAVOR+ forward, favor_fwd_bidir (enqueued on the current stream)."""
-    return _forward("favor_fwd_bidir", False, q, k, v, W, out, workspace, stream)
+def fwd_bidir(q, k, v, W, out=None, workspace=None, stream=None, kernel="softmax"):
+    """Bidirectional FAVOR+ forward (enqueued on the current stream): favor_fwd_bidir,
+    or favor_fwd_attn for kernel="gaussian" (features of exp(-|x-y|^2/2))."""
+    return _forward("favor_fwd_bidir", False, q, k, v, W, out, workspace, stream, kernel)
 
 
-def fwd_causal(q, k, v, W, out=None, workspace=None, stream=None):
-    """Causal FAVOR+ forward in prefix-sum form, favor_fwd_causal."""
-    return _forward("favor_fwd_causal", True, q, k, v, W, out, workspace, stream)
+def fwd_causal(q, k, v, W, out=None, workspace=None, stream=None, kernel="softmax"):
+    """Causal FAVOR+ forward in prefix-sum form: favor_fwd_causal, or favor_fwd_attn
+    for kernel="gaussian"."""
+    return _forward("favor_fwd_causal", True, q, k, v, W, out, workspace, stream, kernel)
 
 
-def feature_map(x, W, out=None, stream=None):
-    """phi(x) = exp(W x - |x|^2/2)/sqrt(m) as fp32 [B, H, L, m], favor_feature_map."""
+def feature_map(x, W, out=None, stream=None, kernel="softmax"):
+    """phi(x) = exp(W x - c |x|^2)/sqrt(m) as fp32 [B, H, L, m], c = 1/2 (softmax,
+    favor_feature_map) or 1 (gaussian, favor_feature_map_attn)."""
+    ak = _kernel(kernel)
     B, H, L, d, m, dt = _shape_of(x, x, x, W)
     if out is None:
         out = torch.empty((B, H, L, m), dtype=torch.float32, device=x.device)
-    st = lib.favor_feature_map(B, H, L, d, m, dt, x.data_ptr(), W.data_ptr(), out.data_ptr(),
-                               _stream(x, stream))
-    _check(st, "favor_feature_map")
+    args = (x.data_ptr(), W.data_ptr(), out.data_ptr(), _stream(x, stream))
+    if ak == SOFTMAX:
+        st = lib.favor_feature_map(B, H, L, d, m, dt, *args)
+        _check(st, "favor_feature_map")
+    else:
+        st = lib.favor_feature_map_attn(B, H, L, d, m, dt, ak, *args)
+        _check(st, "favor_feature_map_attn")
     return out
 
 

@@ -32,11 +32,23 @@ int check_shape(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t d
 
 int fail_hip(hipError_t e) { return record_hip_error(e); }
 
+// Norm coefficient of the features of an attention kernel, or a negative
+// value for an unknown kernel.
+float norm_coefficient(int32_t attn_kernel) {
+  switch (attn_kernel) {
+    case FAVOR_SOFTMAX: return 0.5f;
+    case FAVOR_GAUSSIAN: return 1.0f;
+    default: return -1.0f;
+  }
+}
+
 int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
-            const void* Q, const void* K, const void* V, const float* W, void* O, void* ws,
-            size_t ws_bytes, void* stream) {
+            int32_t attn_kernel, const void* Q, const void* K, const void* V, const float* W,
+            void* O, void* ws, size_t ws_bytes, void* stream) {
   const int status = check_shape(B, H, L, d, m, dtype);
   if (status != FAVOR_OK) return status;
+  const float knorm = norm_coefficient(attn_kernel);
+  if (knorm < 0.f) return FAVOR_ERR_UNSUPPORTED;
   if (!Q || !K || !V || !W || !O || !ws) return FAVOR_ERR_NULL;
   if (!is_aligned(Q, 16) || !is_aligned(K, 16) || !is_aligned(V, 16) || !is_aligned(W, 16) ||
       !is_aligned(O, 16) || !is_aligned(ws, 256))
@@ -44,6 +56,7 @@ int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype
   Plan p;
   make_plan(B, H, L, d, m, dtype, causal, &p);
   if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
+  p.knorm = knorm;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p.path == kPathMfma)
@@ -158,28 +171,44 @@ int favor_plan_describe(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, i
 int favor_fwd_bidir(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                     const void* Q, const void* K, const void* V, const float* W, void* O,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return favor::forward(B, H, L, d, m, dtype, 0, Q, K, V, W, O, workspace, workspace_bytes,
-                        stream);
+  return favor::forward(B, H, L, d, m, dtype, 0, FAVOR_SOFTMAX, Q, K, V, W, O, workspace,
+                        workspace_bytes, stream);
 }
 
 int favor_fwd_causal(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                      const void* Q, const void* K, const void* V, const float* W, void* O,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return favor::forward(B, H, L, d, m, dtype, 1, Q, K, V, W, O, workspace, workspace_bytes,
-                        stream);
+  return favor::forward(B, H, L, d, m, dtype, 1, FAVOR_SOFTMAX, Q, K, V, W, O, workspace,
+                        workspace_bytes, stream);
+}
+
+int favor_fwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                   int32_t causal, int32_t attn_kernel, const void* Q, const void* K,
+                   const void* V, const float* W, void* O, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return favor::forward(B, H, L, d, m, dtype, causal ? 1 : 0, attn_kernel, Q, K, V, W, O,
+                        workspace, workspace_bytes, stream);
+}
+
+int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                           int32_t attn_kernel, const void* X, const float* W, float* Xp,
+                           void* stream) {
+  const int st = favor::check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  const float knorm = favor::norm_coefficient(attn_kernel);
+  if (knorm < 0.f) return FAVOR_ERR_UNSUPPORTED;
+  if (!X || !W || !Xp) return FAVOR_ERR_NULL;
+  if (!favor::is_aligned(X, 16) || !favor::is_aligned(W, 16) || !favor::is_aligned(Xp, 16))
+    return FAVOR_ERR_ALIGN;
+  const hipError_t e = favor::generic_feature_map(B * H, L, d, m, dtype, knorm, X, W, Xp,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return favor::fail_hip(e);
+  return FAVOR_OK;
 }
 
 int favor_feature_map(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                       const void* X, const float* W, float* Xp, void* stream) {
-  const int st = favor::check_shape(B, H, L, d, m, dtype);
-  if (st != FAVOR_OK) return st;
-  if (!X || !W || !Xp) return FAVOR_ERR_NULL;
-  if (!favor::is_aligned(X, 16) || !favor::is_aligned(W, 16) || !favor::is_aligned(Xp, 16))
-    return FAVOR_ERR_ALIGN;
-  const hipError_t e = favor::generic_feature_map(B * H, L, d, m, dtype, X, W, Xp,
-                                                  static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return favor::fail_hip(e);
-  return FAVOR_OK;
+  return favor_feature_map_attn(B, H, L, d, m, dtype, FAVOR_SOFTMAX, X, W, Xp, stream);
 }
 
 const char* favor_status_string(int status) {
@@ -189,7 +218,8 @@ const char* favor_status_string(int status) {
     case FAVOR_ERR_SHAPE: return "invalid shape (B, H or L below 1, or tensor too large)";
     case FAVOR_ERR_UNSUPPORTED:
       return "unsupported configuration (d must be 16, 32, 64 or 128; m a multiple of 16 in "
-             "[16, 1024]; dtype FAVOR_F32 or FAVOR_BF16)";
+             "[16, 1024]; dtype FAVOR_F32 or FAVOR_BF16; attention kernel FAVOR_SOFTMAX or "
+             "FAVOR_GAUSSIAN)";
     case FAVOR_ERR_ALIGN:
       return "misaligned pointer (tensors need 16-byte, the workspace 256-byte alignment)";
     case FAVOR_ERR_WORKSPACE: return "workspace smaller than favor_workspace_bytes()";

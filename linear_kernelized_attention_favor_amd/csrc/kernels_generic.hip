@@ -63,12 +63,13 @@ __device__ inline void load_rows(const T* __restrict__ X, size_t base, int j0, i
   }
 }
 
-// Half squared norms of the kTT rows in `rows` (first kTT threads).
-__device__ inline void half_norms(const float (*rows)[kMaxD + 1], int d, float* nrm) {
+// Norm terms knorm |x|^2 of the kTT rows in `rows` (first kTT threads):
+// knorm = 1/2 for the softmax kernel's features, 1 for the Gaussian's.
+__device__ inline void norm_terms(const float (*rows)[kMaxD + 1], int d, float knorm, float* nrm) {
   if (threadIdx.x < kTT) {
     float acc = 0.f;
     for (int a = 0; a < d; ++a) acc = fmaf(rows[threadIdx.x][a], rows[threadIdx.x][a], acc);
-    nrm[threadIdx.x] = 0.5f * acc;
+    nrm[threadIdx.x] = knorm * acc;
   }
 }
 
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
                                                     const float* __restrict__ W,
                                                     float* __restrict__ Tout,
                                                     float* __restrict__ cseg, int L, int d, int m,
-                                                    int seg, int nseg) {
+                                                    int seg, int nseg, float knorm) {
   const int s = blockIdx.x, fb = blockIdx.y, bh = blockIdx.z;
   const int t = threadIdx.x;
   const int r = t % kFB, jj = t / kFB;  // this thread's feature and tile row
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
     __syncthreads();
     load_rows(K, base, jt, j1, d, Kt);
     __syncthreads();
-    half_norms(Kt, d, nrm);
+    norm_terms(Kt, d, knorm, nrm);
     __syncthreads();
     if (rv && jt + jj < j1) mx = fmaxf(mx, dot_w(wrow, Kt[jj], d) - nrm[jj]);
   }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
       Vt[j][c] = v;
     }
     __syncthreads();
-    half_norms(Kt, d, nrm);
+    norm_terms(Kt, d, knorm, nrm);
     __syncthreads();
     E[jj][r] = (rv && jt + jj < j1) ? expf(dot_w(wrow, Kt[jj], d) - nrm[jj] - cref[r]) : 0.f;
     __syncthreads();
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void g_apply(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ W, const float* __restrict__ KVst, const float* __restrict__ cst,
     const float* __restrict__ csg, T* __restrict__ O, int L, int d, int m, int seg, int nseg,
-    int causal) {
+    int causal, float knorm) {
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
   const int i0 = tile * kTT;
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void g_apply(
         Vt[j][c] = v;
       }
       __syncthreads();
-      half_norms(Xt, d, nrm);
+      norm_terms(Xt, d, knorm, nrm);
       __syncthreads();
       for (int r = t; r < m; r += kThreads) {
         const float* w = W + static_cast<size_t>(r) * d;
@@ -370,14 +371,14 @@ __global__ __launch_bounds__(kThreads) void g_apply(
 }
 
 // ---------------------------------------------------------------------------
-// Feature map test kernel: Xp = exp(w . x - |x|^2/2) / sqrt(m), no shift.
+// Feature map test kernel: Xp = exp(w . x - knorm |x|^2) / sqrt(m), no shift.
 // grid (ceil(L/kTT), BH).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void g_feature_map(const T* __restrict__ X,
                                                           const float* __restrict__ W,
                                                           float* __restrict__ Xp, int L, int d,
-                                                          int m) {
+                                                          int m, float knorm) {
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int i0 = tile * kTT;
   __shared__ float Xt[kTT][kMaxD + 1];
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void g_feature_map(const T* __restrict__ 
   const size_t base = static_cast<size_t>(bh) * L * d;
   load_rows(X, base, i0, L, d, Xt);
   __syncthreads();
-  half_norms(Xt, d, nrm);
+  norm_terms(Xt, d, knorm, nrm);
   __syncthreads();
   const float inv_sqrt_m = 1.0f / sqrtf(static_cast<float>(m));
   for (int r = threadIdx.x; r < m; r += kThreads) {
@@ -407,7 +408,7 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   timing_before(st);
   g_state<T><<<dim3(p.nseg, (p.m + kFB - 1) / kFB, p.BH), kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.d,
-                                                                  p.m, p.seg, p.nseg);
+                                                                  p.m, p.seg, p.nseg, p.knorm);
   hipError_t e = hipGetLastError();
   timing_after(st, "g_state");
   if (e != hipSuccess) return e;
@@ -422,10 +423,10 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
   timing_before(st);
   if (p.causal)
     g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, Tst, cP, cseg, O, p.L, p.d, p.m, p.seg,
-                                        p.nseg, 1);
+                                        p.nseg, 1, p.knorm);
   else
     g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, KV, cfin, nullptr, O, p.L, p.d, p.m, p.seg,
-                                        p.nseg, 0);
+                                        p.nseg, 0, p.knorm);
   e = hipGetLastError();
   timing_after(st, "g_apply");
   return e;
@@ -445,13 +446,15 @@ hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const vo
 }
 
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
-                               const void* X, const float* W, float* Xp, hipStream_t stream) {
+                               float knorm, const void* X, const float* W, float* Xp,
+                               hipStream_t stream) {
   const dim3 g((L + kTT - 1) / kTT, BH);
   if (dtype == FAVOR_F32)
-    g_feature_map<float><<<g, kThreads, 0, stream>>>(static_cast<const float*>(X), W, Xp, L, d, m);
+    g_feature_map<float><<<g, kThreads, 0, stream>>>(static_cast<const float*>(X), W, Xp, L, d, m,
+                                                     knorm);
   else
     g_feature_map<uint16_t><<<g, kThreads, 0, stream>>>(static_cast<const uint16_t*>(X), W, Xp,
-                                                        L, d, m);
+                                                        L, d, m, knorm);
   return hipGetLastError();
 }
 

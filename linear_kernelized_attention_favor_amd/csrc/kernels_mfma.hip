@@ -5,7 +5,9 @@
 // Three launches:
 //
 //   kpart    per (head, sequence split): for each 32-token tile the relative
-//            feature exponents S = K W'^T - |k|^2/2 - c_r (fp16 MFMA; W' =
+//            feature exponents S = K W'^T - knorm |k|^2 - c_r (knorm = 1/2
+//            for the softmax kernel's features, 1 for the Gaussian kernel's;
+//            the query side's norm term cancels per row) (fp16 MFMA; W' =
 //            W log2 e so the exponentials are exp2; the norm and the
 //            per-feature reference c_r enter through one extra MFMA k-step
 //            whose operands hold them as fp16 hi/lo pairs), K~ = exp2(S) in
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
                                                  const float* __restrict__ W,
                                                  float* __restrict__ P, float* __restrict__ cs,
                                                  int L, int m, int SL, int nsplit,
-                                                 int nsplit_run) {
+                                                 int nsplit_run, float knorm) {
   using C = KCfg<D>;
   using LD = KLds<D, NW, TG>;
   constexpr int NTH = NW * 64;               // threads per token group
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
   auto Ks = reinterpret_cast<_Float16(*)[kTT][C::KROW]>(ring);
   auto Vt = reinterpret_cast<uint32_t(*)[D][C::VROW / 2]>(ring + LD::KS_BYTES);   // bf16 pairs
   // Per token the A operand of the extra k-step: [1, 1, n_hi, n_lo, 0 x 28]
-  // with n = |k|^2 log2(e) / 2 (lanes of the upper k rows read the zeros).
+  // with n = knorm |k|^2 log2(e) (lanes of the upper k rows read the zeros).
   // (A full k=32 step: chaining a k=16 product into a k=32 accumulation was
   // seen to read the accumulator too early on this part.)
   auto Na = reinterpret_cast<_Float16(*)[kTT][LD::NAROW]>(ring + LD::KS_BYTES + LD::VT_BYTES);
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
         if (ch == 0) {
           // n as an fp16 hi/lo pair (clamped: a larger norm underflows K~ anyway);
           // a token past the split gets n = +inf, i.e. K~ = 0.
-          const float n = fminf(0.5f * kLog2e * ss, 65504.f);
+          const float n = fminf(knorm * kLog2e * ss, 65504.f);
           const _Float16 nh = static_cast<_Float16>(n);
           const _Float16 nl = static_cast<_Float16>(n - static_cast<float>(nh));
           const _Float16 one = static_cast<_Float16>(1.f);
@@ -1202,7 +1204,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
                                                   const float* __restrict__ P,
                                                   const float* __restrict__ cP,
                                                   uint16_t* __restrict__ O, int L, int m, int SEG,
-                                                  int nseg) {
+                                                  int nseg, float knorm) {
   constexpr int D = 64;
   constexpr int NTH = NW * 64;
   constexpr int KS = 2, NT = 4, TV = 5;
@@ -1334,7 +1336,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
         h.x = bf16x2_to_f16x2(qv.x); h.y = bf16x2_to_f16x2(qv.y);
         h.z = bf16x2_to_f16x2(qv.z); h.w = bf16x2_to_f16x2(qv.w);
         *reinterpret_cast<uint4*>(&Qs[buf][j][ch * 8]) = h;
-        if (ch == 0) Ns[buf][j] = (jt + j < j1) ? -0.5f * kLog2e * ss : -INFINITY;
+        if (ch == 0) Ns[buf][j] = (jt + j < j1) ? -knorm * kLog2e * ss : -INFINITY;
       }
     }
 #pragma unroll
@@ -1633,7 +1635,8 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   constexpr int TG = (NW <= 4) ? 2 : 1;
   timing_before(st);
   kpart<D, NW, TG><<<dim3(p.nseg * p.BH * NFB), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
-                                                                       p.seg, p.nseg, p.nseg);
+                                                                       p.seg, p.nseg, p.nseg,
+                                                                       p.knorm);
   hipError_t e = hipGetLastError();
   timing_after(st, "kpart");
   if (e != hipSuccess) return e;
@@ -1678,7 +1681,8 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     // keeps nseg slots per head).
     timing_before(st);
     kpart<64, NW, 1><<<dim3((p.nseg - 1) * p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
-                                                                    p.seg, p.nseg, p.nseg - 1);
+                                                                    p.seg, p.nseg, p.nseg - 1,
+                                                                    p.knorm);
     e = hipGetLastError();
     timing_after(st, "kpart");
     if (e != hipSuccess) return e;
@@ -1689,7 +1693,8 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     if (e != hipSuccess) return e;
   }
   timing_before(st);
-  cscan<NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg);
+  cscan<NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg,
+                                                     p.knorm);
   e = hipGetLastError();
   timing_after(st, "cscan");
   return e;

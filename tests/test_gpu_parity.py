@@ -377,3 +377,80 @@ def test_late_exponent_spikes_force_rereferencing(fv, shape):
         err = oracle.row_rel_err(out, ref)
         print(f"spikes {shape} causal={causal}: {err:.3e}", flush=True)
         assert np.isfinite(out).all() and err <= TOL["bf16"], (causal, err)
+
+
+# ---------------------------------------------------------------------------
+# The Gaussian kernel exp(-|x-y|^2/2) (method page: FAVOR+ approximates
+# softmax and Gaussian kernels): the same kernels with key features
+# exp(w.k - |k|^2), against the oracle's Gaussian features.
+# ---------------------------------------------------------------------------
+GAUSS_SHAPES = [
+    (1, 2, 17, 32, 48),       # generic path
+    (2, 1, 255, 64, 256),     # matrix-core path
+    (1, 3, 1000, 64, 128),
+    (1, 1, 2049, 64, 64),     # causal: nine segments, the last one token long
+    (1, 2, 700, 128, 512),    # streamed query side
+    (1, 1, 1, 64, 256),
+]
+
+
+def _gauss_ref(causal, q, k, v, W):
+    f = oracle.causal if causal else oracle.bidir
+    return f(_np64(q), _np64(k), _np64(v), W.astype(np.float64), kernel="gaussian")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", GAUSS_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gaussian_shapes(fv, shape, causal, dtype):
+    B, H, L, d, m = shape
+    q, k, v = _case(B, H, L, d, m, dtype, seed=sum(shape) + 77 + causal)
+    W = _w(41 * d + m, m, d)
+    f = fv.fwd_causal if causal else fv.fwd_bidir
+    out = f(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(W).cuda(), kernel="gaussian")
+    torch.cuda.synchronize()
+    err = oracle.row_rel_err(_np64(out), _gauss_ref(causal, q, k, v, W))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gaussian_feature_map_closed_form_and_oracle(fv, dtype):
+    d, m = 64, 256
+    q, _, _ = _case(1, 2, 300, d, m, dtype, seed=15)
+    W = _w(19, m, d)
+    Wd = torch.from_numpy(W).cuda()
+    x = q.cuda()
+    p = fv.feature_map(x, Wd, kernel="gaussian")
+    pm = fv.feature_map((-x.float()).to(x.dtype).contiguous(), Wd, kernel="gaussian")
+    torch.cuda.synchronize()
+    xx = _np64(q)
+    np.testing.assert_allclose((_np64(p) * _np64(pm)).sum(-1), np.exp(-2 * np.sum(xx * xx, -1)),
+                               rtol=2e-5)
+    np.testing.assert_allclose(_np64(p), oracle.phi_gaussian(xx, W.astype(np.float64)), rtol=2e-5)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gaussian_ones_in_ones_out(fv, causal):
+    q, k, _ = _case(1, 4, 1500, 64, 256, "bf16", seed=17)
+    ones = torch.ones_like(q)
+    f = fv.fwd_causal if causal else fv.fwd_bidir
+    out = f(q.cuda(), k.cuda(), ones.cuda(), torch.from_numpy(_w(17, 256, 64)).cuda(),
+            kernel="gaussian")
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 1.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gaussian_text_shape_sampled(fv, causal):
+    w = workloads.workload("text_causal" if causal else "text_bidir")
+    torch.manual_seed(0)
+    q, k, v = workloads.device_qkv(w)
+    W = _w(w.seed_w, w.m, w.d)
+    f = fv.fwd_causal if causal else fv.fwd_bidir
+    out = f(q, k, v, torch.from_numpy(W).cuda(), kernel="gaussian")
+    torch.cuda.synchronize()
+    qf, kf, vf, of = (x.reshape(w.heads, w.L, w.d) for x in (q, k, v, out))
+    for h in (0, w.heads - 1):
+        err = oracle.row_rel_err(_np64(of[h]), _gauss_ref(causal, qf[h], kf[h], vf[h], W))
+        print(f"gaussian {w.name} causal={causal} head {h}: row-rel err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], (h, err)

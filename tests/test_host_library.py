@@ -79,6 +79,36 @@ def test_validation_errors(fn):
     assert lib.favor_last_hip_error() == 0
 
 
+def call_attn(causal=0, attn=0, **kw):
+    a = dict(B=1, H=1, L=16, d=64, m=64, dtype=1, Q=A, K=A, V=A, W=A, O=A, ws=A, wsb=1 << 40)
+    a.update(kw)
+    return lib.favor_fwd_attn(a["B"], a["H"], a["L"], a["d"], a["m"], a["dtype"], causal, attn,
+                              a["Q"], a["K"], a["V"], a["W"], a["O"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("attn", [0, 1])
+def test_attn_entry_validation(causal, attn):
+    # favor_fwd_attn validates as favor_fwd_bidir / favor_fwd_causal do
+    assert call_attn(causal, attn, B=0) == ESHAPE
+    assert call_attn(causal, attn, d=48) == EUNSUP
+    assert call_attn(causal, attn, Q=None) == ENULL
+    assert call_attn(causal, attn, O=MIS) == EALIGN
+    need = fv.workspace_bytes(1, 1, 16, 64, 64, 1, bool(causal))
+    assert call_attn(causal, attn, wsb=need - 1) == EWS
+
+
+def test_attn_entry_rejects_unknown_kernels():
+    for attn in (-1, 2, 7):
+        assert call_attn(0, attn) == EUNSUP
+        assert call_attn(1, attn) == EUNSUP
+        assert lib.favor_feature_map_attn(1, 1, 8, 64, 64, 1, attn, A, A, A, None) == EUNSUP
+    assert lib.favor_feature_map_attn(1, 1, 8, 64, 64, 1, 1, None, A, A, None) == ENULL
+    with pytest.raises(ValueError):
+        fv._binding._kernel("laplace")
+    assert lib.favor_last_hip_error() == 0
+
+
 def test_feature_map_validation():
     f = lib.favor_feature_map
     assert f(1, 1, 0, 64, 64, 1, A, A, A, None) == ESHAPE
