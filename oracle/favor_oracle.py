@@ -42,6 +42,12 @@ design notes):
   are read as the softmax-kernel features times ``exp(-|x|^2/2)``:
   ``phi_G(x) = exp(w_r^T x - |x|^2) / sqrt(m)``, positive, with expectation
   exactly ``exp(-|x-y|^2/2)``.
+* The pages also name generalized kernelizable attention, features
+  ``f(W x) / sqrt(m)`` for some f they do not name.  The one built is
+  f = ReLU: ``phi_R(x) = max(W x, 0) / sqrt(m)``, non-negative; its
+  expectation over w ~ N(0, I_d) is the first-order arc-cosine kernel
+  ``|x| |y| (sin t + (pi - t) cos t) / (2 pi)``, t the angle between x and y.
+  A query whose features are all zero (e.g. q = 0) has no defined output.
 * The random stream is a counter-based SplitMix64 (Steele, Lea & Flood,
   "Fast splittable pseudorandom number generators", OOPSLA 2014) feeding the
   Box-Muller transform; the pages name no generator.
@@ -67,6 +73,7 @@ __all__ = [
     "draw_w_iid",
     "phi",
     "phi_gaussian",
+    "phi_relu",
     "attend_bidir",
     "attend_causal",
     "bidir",
@@ -74,6 +81,8 @@ __all__ = [
     "brute",
     "softmax_attention",
     "gaussian_attention",
+    "arccos_kernel",
+    "arccos_attention",
     "row_rel_err",
 ]
 
@@ -198,12 +207,24 @@ def phi_gaussian(X: np.ndarray, W: np.ndarray) -> np.ndarray:
     return out
 
 
+def phi_relu(X: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Generalized (f = ReLU) random features phi_R(x) = max(W x, 0) / sqrt(m).
+
+    Shapes as phi.  E[phi_R(x)^T phi_R(y)] is arccos_kernel(x, y).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    return np.maximum(X @ W.T, 0.0) / math.sqrt(W.shape[0])
+
+
 def _features(kernel: str):
-    """The feature map of `kernel` ("softmax" or "gaussian"), looked up at call time."""
+    """The feature map of `kernel` ("softmax", "gaussian" or "relu"), looked up at call time."""
     if kernel == "softmax":
         return phi
     if kernel == "gaussian":
         return phi_gaussian
+    if kernel == "relu":
+        return phi_relu
     raise ValueError(f"unknown kernel {kernel!r}")
 
 
@@ -312,6 +333,35 @@ def gaussian_attention(Q, K, V, is_causal: bool = False) -> np.ndarray:
     s = s - s.max(axis=-1, keepdims=True)
     A = np.exp(s)
     return (A @ V) / A.sum(axis=-1)[..., None]
+
+
+def arccos_kernel(X, Y) -> np.ndarray:
+    """First-order arc-cosine kernel |x| |y| (sin t + (pi - t) cos t) / (2 pi).
+
+    X is [..., n, d], Y is [..., p, d]; the result is [..., n, p].  It is
+    E[max(w.x, 0) max(w.y, 0)] for w ~ N(0, I_d) (the half-space integral of
+    the Gaussian measure, Cho and Saul 2009), written from its closed form.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    Y = np.asarray(Y, dtype=np.float64)
+    nx = np.linalg.norm(X, axis=-1)[..., :, None]
+    ny = np.linalg.norm(Y, axis=-1)[..., None, :]
+    cos = np.clip((X @ np.swapaxes(Y, -1, -2)) / np.maximum(nx * ny, 1e-300), -1.0, 1.0)
+    t = np.arccos(cos)
+    return nx * ny * (np.sin(t) + (math.pi - t) * cos) / (2 * math.pi)
+
+
+def arccos_attention(Q, K, V, is_causal: bool = False) -> np.ndarray:
+    """Exact kernel attention with the arc-cosine kernel: the large-m limit of
+    the ReLU features.  A = arccos_kernel(Q, K) (lower-triangular if masked),
+    out = A V / A 1_L."""
+    A = arccos_kernel(Q, K)
+    if is_causal:
+        L = A.shape[-1]
+        A = A * np.tril(np.ones((L, L)))
+    den = A.sum(axis=-1)
+    assert np.all(den > 0)
+    return (A @ np.asarray(V, dtype=np.float64)) / den[..., None]
 
 
 def row_rel_err(got, ref) -> float:

@@ -15,7 +15,7 @@ import test_oracle_pins as pins
 
 # the real functions, saved before any patching, for mutants built on them
 _REAL = {n: getattr(fo, n) for n in ("draw_w", "attend_causal", "softmax_attention",
-                                     "gaussian_attention")}
+                                     "gaussian_attention", "arccos_kernel")}
 
 
 def _phi_no_norm(X, W):
@@ -101,6 +101,30 @@ def _gaussian_attention_no_half(Q, K, V, is_causal=False):
                                        V, is_causal)
 
 
+def _phi_relu_abs(X, W):
+    # |W x| instead of max(W x, 0)
+    return np.abs(np.asarray(X, float) @ np.asarray(W, float).T) / math.sqrt(W.shape[0])
+
+
+def _phi_relu_no_sqrt_m(X, W):
+    return np.maximum(np.asarray(X, float) @ np.asarray(W, float).T, 0.0)
+
+
+def _phi_relu_with_bias(X, W):
+    # a small positive floor on every feature (not on the pages)
+    return (np.maximum(np.asarray(X, float) @ np.asarray(W, float).T, 0.0) + 1e-3) / math.sqrt(W.shape[0])
+
+
+def _arccos_t_for_pi_minus_t(X, Y):
+    X = np.asarray(X, float)
+    Y = np.asarray(Y, float)
+    nx = np.linalg.norm(X, axis=-1)[..., :, None]
+    ny = np.linalg.norm(Y, axis=-1)[..., None, :]
+    cos = np.clip((X @ np.swapaxes(Y, -1, -2)) / (nx * ny), -1.0, 1.0)
+    t = np.arccos(cos)
+    return nx * ny * (np.sin(t) + t * cos) / (2 * math.pi)
+
+
 def _softmax_with_scale(Q, K, V, is_causal=False):
     return _REAL["softmax_attention"](np.asarray(Q) / math.sqrt(Q.shape[-1]), K, V, is_causal)
 
@@ -139,6 +163,10 @@ GAUSS_PINS = [
     (pins.test_G1_gaussian_phi_of_zero_and_positivity, {}),
     (pins.test_G3_equal_key_norms_make_the_kernels_agree, {}),
 ]
+RELU_PINS = [
+    (pins.test_R1_relu_features_split_the_projection, dict(m=16, d=16)),
+    (pins.test_R3_relu_attention_is_scale_free, {}),
+]
 CAUSAL_PINS = [
     (pins.test_P13_causal_first_and_last_rows, {}),
     (pins.test_causal_mask_includes_diagonal, {}),
@@ -162,6 +190,11 @@ CAUSAL_PINS = [
      GAUSS_PINS),
     ("Gaussian attention drops the 1/2", "gaussian_attention", _gaussian_attention_no_half,
      [(pins.test_G2_gaussian_attention_matches_library_softmax, {})]),
+    ("ReLU features take |W x|", "phi_relu", _phi_relu_abs, RELU_PINS),
+    ("ReLU features drop 1/sqrt(m)", "phi_relu", _phi_relu_no_sqrt_m, RELU_PINS),
+    ("ReLU features get a positive floor", "phi_relu", _phi_relu_with_bias, RELU_PINS),
+    ("arc-cosine kernel with t for pi - t", "arccos_kernel", _arccos_t_for_pi_minus_t,
+     [(pins.test_R2_arccos_kernel_special_cases_and_monte_carlo, {})]),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, target, mutant, pinset):
     monkeypatch.setattr(fo, target, mutant)
@@ -176,5 +209,5 @@ def test_softmax_scale_mistake_is_caught(monkeypatch):
 
 
 def test_real_oracle_passes_the_same_pins():
-    for pinset in (PHI_PINS, DRAW_PINS, BIDIR_PINS, CAUSAL_PINS, GAUSS_PINS):
+    for pinset in (PHI_PINS, DRAW_PINS, BIDIR_PINS, CAUSAL_PINS, GAUSS_PINS, RELU_PINS):
         assert _run_pins(pinset) == 0

@@ -505,3 +505,81 @@ def test_G5_convergence_to_gaussian_attention():
                      / np.linalg.norm(ref))
         errs.append(np.mean(e))
     assert errs[1] < 0.25 * errs[0], errs
+
+
+# ---------------------------------------------------------------------------
+# Generalized kernelizable attention with f = ReLU (FAVOR+ method page and
+# the paper's abstract name generalized kernelizable attention; f unnamed,
+# ReLU is the reading taken).  R1-R5 pin phi_relu, arccos_kernel and
+# arccos_attention.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("m,d", [(16, 16), (256, 64), (37, 8)])
+def test_R1_relu_features_split_the_projection(m, d):
+    # max(s,0) - max(-s,0) = s and max(s,0) max(-s,0) = 0, for every W
+    rng = _rng(11 * m + d)
+    W = rng.standard_normal((m, d))
+    X = rng.standard_normal((40, d))
+    p, n = oracle.phi_relu(X, W), oracle.phi_relu(-X, W)
+    np.testing.assert_allclose(p - n, X @ W.T / math.sqrt(m), rtol=1e-14, atol=1e-15)
+    assert np.all(p * n == 0) and np.all(p >= 0)
+
+
+def test_R2_arccos_kernel_special_cases_and_monte_carlo():
+    rng = _rng(33)
+    x = rng.standard_normal(8)
+    u = rng.standard_normal(8)
+    y = u - (u @ x) / (x @ x) * x               # orthogonal to x
+    k = lambda a, b: oracle.arccos_kernel(a[None], b[None])[0, 0]
+    assert math.isclose(k(x, x), 0.5 * (x @ x), rel_tol=1e-12)          # E[relu(g)^2] = 1/2
+    assert math.isclose(k(x, y), np.linalg.norm(x) * np.linalg.norm(y) / (2 * math.pi), rel_tol=1e-9)
+    assert abs(k(x, -x)) < 1e-12
+    # against a plain Monte Carlo average over iid Gaussian w (numpy's generator)
+    z = rng.standard_normal(8)
+    Wmc = np.random.default_rng(34).standard_normal((2_000_000, 8))
+    prod = np.maximum(Wmc @ x, 0) * np.maximum(Wmc @ z, 0)
+    se = prod.std() / math.sqrt(len(prod))
+    assert abs(prod.mean() - k(x, z)) < 4 * se
+
+
+def test_R3_relu_attention_is_scale_free():
+    # phi_R is positively homogeneous: scaling Q or K by a positive factor
+    # cancels in D^-1 (a plausible exp- or bias-based feature would not)
+    Q, K, V, W = _inputs(1, 2, 48, 16, 64, 31)
+    for f in (oracle.bidir, oracle.causal):
+        ref = f(Q, K, V, W, kernel="relu")
+        np.testing.assert_allclose(f(3.7 * Q, 0.2 * K, V, W, kernel="relu"), ref, rtol=1e-12, atol=1e-13)
+    ones = np.ones_like(V)
+    np.testing.assert_allclose(oracle.bidir(Q, K, ones, W, kernel="relu"), 1.0, atol=1e-14)
+    np.testing.assert_allclose(oracle.causal(Q, K, V, W, kernel="relu"),
+                               oracle.brute(Q, K, V, W, True, kernel="relu"), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.slow
+def test_R4_unbiased_arccos_kernel():
+    d, N = 16, 20_000
+    rng = _rng(71)
+    x, y = rng.standard_normal(d) * 0.7, rng.standard_normal(d) * 0.7
+    W = oracle.draw_w(6161, d * N, d)
+    px = oracle.phi_relu(x[None, :], W)[0].reshape(N, d) * math.sqrt(N)
+    py = oracle.phi_relu(y[None, :], W)[0].reshape(N, d) * math.sqrt(N)
+    est = np.sum(px * py, axis=1)                      # one m = d estimator per block
+    target = oracle.arccos_kernel(x[None], y[None])[0, 0]
+    z = (est.mean() - target) / (est.std() / math.sqrt(N))
+    assert abs(z) < 4, z
+
+
+@pytest.mark.slow
+def test_R5_convergence_to_arccos_attention():
+    errs = []
+    for m in (16, 2048):
+        e = []
+        for s in range(6):
+            rng = _rng(1300 + s)
+            Q = rng.standard_normal((128, 16))
+            K = rng.standard_normal((128, 16))
+            V = rng.standard_normal((128, 16))
+            W = oracle.draw_w(9700 + 13 * s + m, m, 16)
+            ref = oracle.arccos_attention(Q, K, V)
+            e.append(np.linalg.norm(oracle.bidir(Q, K, V, W, kernel="relu") - ref) / np.linalg.norm(ref))
+        errs.append(np.mean(e))
+    assert errs[1] < 0.25 * errs[0], errs
