@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="text_bidir")
     ap.add_argument("--causal", action="store_true", help="time the causal form of the workload")
-    ap.add_argument("--kernel", choices=("softmax", "gaussian"), default="softmax",
+    ap.add_argument("--kernel", choices=("softmax", "gaussian", "relu"), default="softmax",
                     help="attention kernel the features estimate (default softmax)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,

@@ -65,15 +65,21 @@ enum favor_dtype {
 
 /*
  * Attention kernel the features estimate (method page, section "FAVOR+": the
- * mechanism approximates softmax and Gaussian kernels).  The features are
+ * mechanism approximates softmax and Gaussian kernels; the paper's abstract
+ * also names generalized kernelizable attention).  The features are
  * phi(x)_r = exp(w_r . x - c |x|^2) / sqrt(m) with c = 1/2 for the softmax
  * kernel exp(x . y) and c = 1 for the Gaussian kernel exp(-|x - y|^2 / 2)
- * (the softmax features times exp(-|x|^2 / 2); the method page prints
- * neither feature map, this is the reading taken).
+ * (the softmax features times exp(-|x|^2 / 2)), and, for generalized
+ * attention with f = ReLU (f is not named on the pages; this is the one
+ * built), phi(x)_r = max(w_r . x, 0) / sqrt(m), whose expectation is the
+ * first-order arc-cosine kernel.  The pages print none of the feature maps;
+ * these are the readings taken.  With ReLU features a query whose features
+ * are all zero (e.g. q = 0) has no defined output (0/0).
  */
 enum favor_attn_kernel {
   FAVOR_SOFTMAX = 0,
-  FAVOR_GAUSSIAN = 1
+  FAVOR_GAUSSIAN = 1,
+  FAVOR_RELU = 2
 };
 
 enum favor_status {
@@ -130,12 +136,13 @@ int favor_fwd_causal(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int3
                      void* O, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Either form with either attention kernel: favor_fwd_bidir (causal = 0) or
+ * Either form with any attention kernel: favor_fwd_bidir (causal = 0) or
  * favor_fwd_causal (causal != 0) with the features of `attn_kernel`
  * (FAVOR_SOFTMAX: exactly those entry points; FAVOR_GAUSSIAN: the key
  * features carry exp(-|k|^2), the query features' norm term cancels per
- * row).  Arguments, workspace (favor_workspace_bytes does not depend on the
- * kernel) and errors as favor_fwd_bidir; an unknown attn_kernel gives
+ * row; FAVOR_RELU: max(w . x, 0) features, no exponent references).
+ * Arguments, workspace (favor_workspace_bytes does not depend on the kernel)
+ * and errors as favor_fwd_bidir; an unknown attn_kernel gives
  * FAVOR_ERR_UNSUPPORTED before anything is enqueued.
  */
 int favor_fwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
@@ -156,8 +163,8 @@ int favor_feature_map(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int
 /*
  * favor_feature_map with the features of `attn_kernel`:
  * Xp[b,h,l,r] = exp(w_r . x - c |x|^2) / sqrt(m), c = 1/2 (FAVOR_SOFTMAX, the
- * same as favor_feature_map) or 1 (FAVOR_GAUSSIAN).  Unknown attn_kernel:
- * FAVOR_ERR_UNSUPPORTED.
+ * same as favor_feature_map) or 1 (FAVOR_GAUSSIAN), or max(w_r . x, 0) /
+ * sqrt(m) (FAVOR_RELU).  Unknown attn_kernel: FAVOR_ERR_UNSUPPORTED.
  */
 int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                            int32_t attn_kernel, const void* X, const float* W, float* Xp,

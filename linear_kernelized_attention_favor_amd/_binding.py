@@ -16,15 +16,16 @@ import torch
 
 __all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
            "feature_map", "draw_projection", "status_string", "plan_describe", "timing_start", "timing_stop",
-           "F32", "BF16", "SOFTMAX", "GAUSSIAN"]
+           "F32", "BF16", "SOFTMAX", "GAUSSIAN", "RELU"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfavor.so")
 
 F32, BF16 = 0, 1
 _DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 # attention kernel the features estimate (enum favor_attn_kernel)
-SOFTMAX, GAUSSIAN = 0, 1
-_KERNELS = {"softmax": SOFTMAX, "gaussian": GAUSSIAN, SOFTMAX: SOFTMAX, GAUSSIAN: GAUSSIAN}
+SOFTMAX, GAUSSIAN, RELU = 0, 1, 2
+_KERNELS = {"softmax": SOFTMAX, "gaussian": GAUSSIAN, "relu": RELU,
+            SOFTMAX: SOFTMAX, GAUSSIAN: GAUSSIAN, RELU: RELU}
 
 
 class FavorError(RuntimeError):
@@ -129,7 +130,7 @@ def _kernel(kernel):
     try:
         return _KERNELS[kernel]
     except KeyError:
-        raise ValueError(f"kernel must be 'softmax' or 'gaussian', not {kernel!r}") from None
+        raise ValueError(f"kernel must be 'softmax', 'gaussian' or 'relu', not {kernel!r}") from None
 
 
 def _forward(name, causal, q, k, v, W, out, workspace, stream, kernel="softmax"):
@@ -155,19 +156,21 @@ def _forward(name, causal, q, k, v, W, out, workspace, stream, kernel="softmax")
 
 def fwd_bidir(q, k, v, W, out=None, workspace=None, stream=None, kernel="softmax"):
     """Bidirectional FAVOR+ forward (enqueued on the current stream): favor_fwd_bidir,
-    or favor_fwd_attn for kernel="gaussian" (features of exp(-|x-y|^2/2))."""
+    or favor_fwd_attn for kernel="gaussian" (features of exp(-|x-y|^2/2)) or
+    kernel="relu" (features max(W x, 0)/sqrt(m), generalized attention)."""
     return _forward("favor_fwd_bidir", False, q, k, v, W, out, workspace, stream, kernel)
 
 
 def fwd_causal(q, k, v, W, out=None, workspace=None, stream=None, kernel="softmax"):
     """Causal FAVOR+ forward in prefix-sum form: favor_fwd_causal, or favor_fwd_attn
-    for kernel="gaussian"."""
+    for kernel="gaussian" or "relu"."""
     return _forward("favor_fwd_causal", True, q, k, v, W, out, workspace, stream, kernel)
 
 
 def feature_map(x, W, out=None, stream=None, kernel="softmax"):
     """phi(x) = exp(W x - c |x|^2)/sqrt(m) as fp32 [B, H, L, m], c = 1/2 (softmax,
-    favor_feature_map) or 1 (gaussian, favor_feature_map_attn)."""
+    favor_feature_map) or 1 (gaussian, favor_feature_map_attn), or
+    max(W x, 0)/sqrt(m) (relu, favor_feature_map_attn)."""
     ak = _kernel(kernel)
     B, H, L, d, m, dt = _shape_of(x, x, x, W)
     if out is None:

@@ -32,12 +32,14 @@ int check_shape(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t d
 
 int fail_hip(hipError_t e) { return record_hip_error(e); }
 
-// Norm coefficient of the features of an attention kernel, or a negative
-// value for an unknown kernel.
+// Norm coefficient of the features of an attention kernel (0 for the ReLU
+// features, which have no norm term), or a negative value for an unknown
+// kernel.
 float norm_coefficient(int32_t attn_kernel) {
   switch (attn_kernel) {
     case FAVOR_SOFTMAX: return 0.5f;
     case FAVOR_GAUSSIAN: return 1.0f;
+    case FAVOR_RELU: return 0.0f;
     default: return -1.0f;
   }
 }
@@ -57,6 +59,7 @@ int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype
   make_plan(B, H, L, d, m, dtype, causal, &p);
   if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
   p.knorm = knorm;
+  p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (p.path == kPathMfma)
@@ -200,7 +203,8 @@ int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m
   if (!X || !W || !Xp) return FAVOR_ERR_NULL;
   if (!favor::is_aligned(X, 16) || !favor::is_aligned(W, 16) || !favor::is_aligned(Xp, 16))
     return FAVOR_ERR_ALIGN;
-  const hipError_t e = favor::generic_feature_map(B * H, L, d, m, dtype, knorm, X, W, Xp,
+  const hipError_t e = favor::generic_feature_map(B * H, L, d, m, dtype, knorm,
+                                                  attn_kernel == FAVOR_RELU ? 1 : 0, X, W, Xp,
                                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return favor::fail_hip(e);
   return FAVOR_OK;
@@ -218,8 +222,8 @@ const char* favor_status_string(int status) {
     case FAVOR_ERR_SHAPE: return "invalid shape (B, H or L below 1, or tensor too large)";
     case FAVOR_ERR_UNSUPPORTED:
       return "unsupported configuration (d must be 16, 32, 64 or 128; m a multiple of 16 in "
-             "[16, 1024]; dtype FAVOR_F32 or FAVOR_BF16; attention kernel FAVOR_SOFTMAX or "
-             "FAVOR_GAUSSIAN)";
+             "[16, 1024]; dtype FAVOR_F32 or FAVOR_BF16; attention kernel FAVOR_SOFTMAX, "
+             "FAVOR_GAUSSIAN or FAVOR_RELU)";
     case FAVOR_ERR_ALIGN:
       return "misaligned pointer (tensors need 16-byte, the workspace 256-byte alignment)";
     case FAVOR_ERR_WORKSPACE: return "workspace smaller than favor_workspace_bytes()";

@@ -45,9 +45,11 @@ struct Plan {
   //   cP   [BH][nseg][m]       references of the prefixes (s >= 1)
   size_t off_T, off_cseg, off_cP, off_KV, off_cfin;
   size_t bytes;
-  // Norm coefficient of the key features, exp(w.k - knorm |k|^2): 1/2 for
-  // the softmax kernel, 1 for the Gaussian kernel (set per call).
+  // Features (set per call): exp(w.k - knorm |k|^2) with knorm = 1/2 (softmax
+  // kernel) or 1 (Gaussian kernel), or, with relu = 1, max(w.x, 0)
+  // (generalized attention; knorm = 0).
   float knorm;
+  int32_t relu;
 };
 
 // Fills *p for a validated shape (the C-ABI layer validates first).
@@ -86,7 +88,7 @@ int record_hip_error(hipError_t e);
 
 // Feature map test entry (generic fp32 arithmetic).
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
-                               float knorm, const void* X, const float* W, float* Xp,
-                               hipStream_t stream);
+                               float knorm, int32_t relu, const void* X, const float* W,
+                               float* Xp, hipStream_t stream);
 
 }  // namespace favor

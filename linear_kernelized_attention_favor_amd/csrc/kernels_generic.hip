@@ -73,6 +73,11 @@ __device__ inline void norm_terms(const float (*rows)[kMaxD + 1], int d, float k
   }
 }
 
+// The feature of exponent (or, for ReLU features, projection) e: exp(e), or
+// max(e, 0) when relu is set.  ReLU features take no norm term and no
+// reference (knorm = 0 and every reference 0).
+__device__ inline float feat(float e, int relu) { return relu ? fmaxf(e, 0.f) : expf(e); }
+
 // w . x over d coordinates, w from global memory (row of W), x from LDS.
 __device__ inline float dot_w(const float* __restrict__ w, const float* x, int d) {
   float acc = 0.f;
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
                                                     const float* __restrict__ W,
                                                     float* __restrict__ Tout,
                                                     float* __restrict__ cseg, int L, int d, int m,
-                                                    int seg, int nseg, float knorm) {
+                                                    int seg, int nseg, float knorm, int relu) {
   const int s = blockIdx.x, fb = blockIdx.y, bh = blockIdx.z;
   const int t = threadIdx.x;
   const int r = t % kFB, jj = t / kFB;  // this thread's feature and tile row
@@ -112,9 +117,9 @@ __global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
   const int j0 = s * seg, j1 = min(L, j0 + seg);
   const float* wrow = W + static_cast<size_t>(fb * kFB + (rv ? r : 0)) * d;
 
-  // Pass 1: per-feature maximum exponent over the segment.
-  float mx = -INFINITY;
-  for (int jt = j0; jt < j1; jt += kTT) {
+  // Pass 1: per-feature maximum exponent over the segment (0 for ReLU).
+  float mx = relu ? 0.f : -INFINITY;
+  for (int jt = j0; jt < j1 && !relu; jt += kTT) {
     __syncthreads();
     load_rows(K, base, jt, j1, d, Kt);
     __syncthreads();
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
     __syncthreads();
     norm_terms(Kt, d, knorm, nrm);
     __syncthreads();
-    E[jj][r] = (rv && jt + jj < j1) ? expf(dot_w(wrow, Kt[jj], d) - nrm[jj] - cref[r]) : 0.f;
+    E[jj][r] = (rv && jt + jj < j1) ? feat(dot_w(wrow, Kt[jj], d) - nrm[jj] - cref[r], relu) : 0.f;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kAcc; ++u) {
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void g_apply(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ W, const float* __restrict__ KVst, const float* __restrict__ cst,
     const float* __restrict__ csg, T* __restrict__ O, int L, int d, int m, int seg, int nseg,
-    int causal, float knorm) {
+    int causal, float knorm, int relu) {
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
   const int i0 = tile * kTT;
@@ -281,12 +286,12 @@ __global__ __launch_bounds__(kThreads) void g_apply(
     float mx = -INFINITY;
     for (int r = k; r < m; r += 32) mx = fmaxf(mx, Qe[i][r]);
     for (int off = 16; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 32));
-    if (k == 0) Mrow[i] = mx;
+    if (k == 0) Mrow[i] = relu ? 0.f : mx;
   }
   __syncthreads();
   for (int p = t; p < kTT * m; p += kThreads) {
     const int i = p / m, r = p - i * m;
-    Qe[i][r] = expf(Qe[i][r] - Mrow[i]);
+    Qe[i][r] = feat(Qe[i][r] - Mrow[i], relu);
   }
   __syncthreads();
 
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kThreads) void g_apply(
           for (int j = 0; j < kTT; ++j) e[j] = fmaf(wa, Xt[j][a], e[j]);
         }
 #pragma unroll
-        for (int j = 0; j < kTT; ++j) Ke[j][r] = expf(e[j] - nrm[j] - cstar[r]);
+        for (int j = 0; j < kTT; ++j) Ke[j][r] = feat(e[j] - nrm[j] - cstar[r], relu);
       }
       __syncthreads();
       if (t < kTT * kTT * 4) {
@@ -371,14 +376,15 @@ __global__ __launch_bounds__(kThreads) void g_apply(
 }
 
 // ---------------------------------------------------------------------------
-// Feature map test kernel: Xp = exp(w . x - knorm |x|^2) / sqrt(m), no shift.
+// Feature map test kernel: Xp = exp(w . x - knorm |x|^2) / sqrt(m), no shift,
+// or max(w . x, 0) / sqrt(m) when relu is set.
 // grid (ceil(L/kTT), BH).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kThreads) void g_feature_map(const T* __restrict__ X,
                                                           const float* __restrict__ W,
                                                           float* __restrict__ Xp, int L, int d,
-                                                          int m, float knorm) {
+                                                          int m, float knorm, int relu) {
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int i0 = tile * kTT;
   __shared__ float Xt[kTT][kMaxD + 1];
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void g_feature_map(const T* __restrict__ 
     const float* w = W + static_cast<size_t>(r) * d;
     for (int i = 0; i < kTT && i0 + i < L; ++i) {
       const float e = dot_w(w, Xt[i], d) - nrm[i];
-      Xp[(static_cast<size_t>(bh) * L + i0 + i) * m + r] = expf(e) * inv_sqrt_m;
+      Xp[(static_cast<size_t>(bh) * L + i0 + i) * m + r] = feat(e, relu) * inv_sqrt_m;
     }
   }
 }
@@ -408,7 +414,7 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   timing_before(st);
   g_state<T><<<dim3(p.nseg, (p.m + kFB - 1) / kFB, p.BH), kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.d,
-                                                                  p.m, p.seg, p.nseg, p.knorm);
+                                                                  p.m, p.seg, p.nseg, p.knorm, p.relu);
   hipError_t e = hipGetLastError();
   timing_after(st, "g_state");
   if (e != hipSuccess) return e;
@@ -423,10 +429,10 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
   timing_before(st);
   if (p.causal)
     g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, Tst, cP, cseg, O, p.L, p.d, p.m, p.seg,
-                                        p.nseg, 1, p.knorm);
+                                        p.nseg, 1, p.knorm, p.relu);
   else
     g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, KV, cfin, nullptr, O, p.L, p.d, p.m, p.seg,
-                                        p.nseg, 0, p.knorm);
+                                        p.nseg, 0, p.knorm, p.relu);
   e = hipGetLastError();
   timing_after(st, "g_apply");
   return e;
@@ -446,15 +452,15 @@ hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const vo
 }
 
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
-                               float knorm, const void* X, const float* W, float* Xp,
+                               float knorm, int32_t relu, const void* X, const float* W, float* Xp,
                                hipStream_t stream) {
   const dim3 g((L + kTT - 1) / kTT, BH);
   if (dtype == FAVOR_F32)
     g_feature_map<float><<<g, kThreads, 0, stream>>>(static_cast<const float*>(X), W, Xp, L, d, m,
-                                                     knorm);
+                                                     knorm, relu);
   else
     g_feature_map<uint16_t><<<g, kThreads, 0, stream>>>(static_cast<const uint16_t*>(X), W, Xp,
-                                                        L, d, m, knorm);
+                                                        L, d, m, knorm, relu);
   return hipGetLastError();
 }
 

@@ -29,6 +29,11 @@
 // The shifts cancel exactly: sum_r e^{s_ir + c_r - M_i} sum_j e^{e_jr - c_r}
 // [v_j | 1] = e^{-M_i} sum_r e^{s_ir} sum_j e^{e_jr} [v_j | 1].
 //
+// ReLU features (generalized attention, template flag RELU): the same
+// kernels with max(s, 0) in place of exp2(s), no norm term, every reference
+// 0 and no row reference.  s is then w . x log2 e; the common factor
+// (log2 e)^2 of numerator and denominator cancels in the division.
+//
 // Numerics: Q and K are converted to fp16 for the projection (exact for
 // |x| < 65504 outside fp16's subnormal range), W' is rounded to fp16, the
 // features and [KV | z] are rounded to bf16 (full fp32 exponent range), all
@@ -115,7 +120,7 @@ struct KLds {
   static constexpr int BYTES = TG * RING;
 };
 
-template <int D, int NW, int TG>
+template <int D, int NW, int TG, bool RELU>
 __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restrict__ K,
                                                  const uint16_t* __restrict__ V,
                                                  const float* __restrict__ W,
@@ -313,8 +318,15 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < C::NT; ++nt)
-        S[mt][nt] = mma_f16(aa[mt], baug[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int nt = 0; nt < C::NT; ++nt) {
+        // ReLU: no norm term and no reference.  The extra step is kept where
+        // TG = 1 (it adds exact zeros there: knorm = 0 and the reference stays
+        // 0), again for the register allocation.
+        if constexpr (RELU && TG > 1)
+          S[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        else
+          S[mt][nt] = mma_f16(aa[mt], baug[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
@@ -366,8 +378,8 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
       uint32_t p[4];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        p[q] = pack_bf16(fast_exp2(S[0][nt][2 * q]), fast_exp2(S[0][nt][2 * q + 1]));
-        p[2 + q] = pack_bf16(fast_exp2(S[1][nt][2 * q]), fast_exp2(S[1][nt][2 * q + 1]));
+        p[q] = pack_bf16(feature<RELU>(S[0][nt][2 * q]), feature<RELU>(S[0][nt][2 * q + 1]));
+        p[2 + q] = pack_bf16(feature<RELU>(S[1][nt][2 * q]), feature<RELU>(S[1][nt][2 * q + 1]));
       }
       kb[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
     }
@@ -411,7 +423,7 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
     SArr S;
     float dl[C::NT];
     proj(0, S);
-    rebase(S, true, dl);
+    if constexpr (!RELU) rebase(S, true, dl);
     features(S, kbA);
   }
 
@@ -430,7 +442,11 @@ __global__ __launch_bounds__(TG * NW * 64, 2) void kpart(const uint16_t* __restr
     proj((r + 1) % 3, S);
     contract(r % 3, kcur);
     features(S, knext);
-    if (__builtin_expect(overflow(knext), 0)) {
+    // ReLU features take no reference: for them the check below is compiled
+    // but never taken (knorm is 0), because the branch keeps the register
+    // allocation of the exponential features (without it the compiler spills
+    // the accumulators).
+    if (__builtin_expect((RELU ? knorm < 0.f : true) && overflow(knext), 0)) {
       float dl[C::NT];
       rebase(S, false, dl);
       features(S, knext);
@@ -617,7 +633,7 @@ size_t qapply_lds_bytes(int m) {
          static_cast<size_t>(m) * 4;
 }
 
-template <int D, int NW, int NTQ, int NCH>
+template <int D, int NW, int NTQ, int NCH, bool RELU>
 __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16_t* __restrict__ Q,
                                                   const _Float16* __restrict__ W16,
                                                   const uint16_t* __restrict__ Kz,
@@ -722,8 +738,12 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
       const f16x8 aa = __builtin_bit_cast(
           f16x8, (g == 0) ? make_uint4(cw, 0x3C003C00u, 0u, 0u) : make_uint4(0u, 0u, 0u, 0u));
 #pragma unroll
-      for (int nt = 0; nt < C::NTQ; ++nt)
-        S[mt][nt] = mma_f16(aa, baug[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int nt = 0; nt < C::NTQ; ++nt) {
+        if constexpr (RELU)   // (no reference on either side)
+          S[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        else
+          S[mt][nt] = mma_f16(aa, baug[nt], f32x4{0.f, 0.f, 0.f, 0.f});
+      }
     }
     // (W' operands one k-step at a time: bounded registers at d = 128)
 #pragma unroll
@@ -748,9 +768,10 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
         uint32_t p[4];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          p[q] = pack_bf16(fast_exp2(S[2 * kb][nt][2 * q]), fast_exp2(S[2 * kb][nt][2 * q + 1]));
-          p[2 + q] = pack_bf16(fast_exp2(S[2 * kb + 1][nt][2 * q]),
-                               fast_exp2(S[2 * kb + 1][nt][2 * q + 1]));
+          p[q] = pack_bf16(feature<RELU>(S[2 * kb][nt][2 * q]),
+                           feature<RELU>(S[2 * kb][nt][2 * q + 1]));
+          p[2 + q] = pack_bf16(feature<RELU>(S[2 * kb + 1][nt][2 * q]),
+                               feature<RELU>(S[2 * kb + 1][nt][2 * q + 1]));
         }
         qt[kb][nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
       }
@@ -849,7 +870,7 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
   {
     SArr S;
     proj(0, qcur, S);
-    rebase(S, true);
+    if constexpr (!RELU) rebase(S, true);
     features(S, FA);
   }
   for (int ti = 0; ti < ntile; ++ti) {
@@ -862,9 +883,11 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
       proj(ch + 1, qcur, S);
       apply(ch, Fcur);
       features(S, Fnext);
-      if (__builtin_expect(overflow(Fnext), 0)) {
-        rebase(S, false);
-        features(S, Fnext);
+      if constexpr (!RELU) {
+        if (__builtin_expect(overflow(Fnext), 0)) {
+          rebase(S, false);
+          features(S, Fnext);
+        }
       }
     };
     // Last step of a tile: apply the last chunk, write the tile, then project
@@ -879,7 +902,7 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
         if (ti + 2 < ntile) qload(tt + 2 * step, raw);
         SArr S;
         proj(0, qcur, S);
-        rebase(S, true);
+        if constexpr (!RELU) rebase(S, true);
         features(S, Fnext);
       }
     };
@@ -928,7 +951,7 @@ struct QsLds {
   static_assert(W16 % 64 == 0 && K16 % 64 == 0, "whole waves per staging job");
 };
 
-template <int D, int NW, int NTQ, int NCH>
+template <int D, int NW, int NTQ, int NCH, bool RELU>
 __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict__ Q,
                                                    const _Float16* __restrict__ W16,
                                                    const uint16_t* __restrict__ Kz,
@@ -1072,9 +1095,10 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
         uint32_t p[4];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          p[q] = pack_bf16(fast_exp2(S[2 * kb][nt][2 * q]), fast_exp2(S[2 * kb][nt][2 * q + 1]));
-          p[2 + q] = pack_bf16(fast_exp2(S[2 * kb + 1][nt][2 * q]),
-                               fast_exp2(S[2 * kb + 1][nt][2 * q + 1]));
+          p[q] = pack_bf16(feature<RELU>(S[2 * kb][nt][2 * q]),
+                           feature<RELU>(S[2 * kb][nt][2 * q + 1]));
+          p[2 + q] = pack_bf16(feature<RELU>(S[2 * kb + 1][nt][2 * q]),
+                               feature<RELU>(S[2 * kb + 1][nt][2 * q + 1]));
         }
         qt[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
       }
@@ -1131,11 +1155,13 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
       if (more) stage((ch + 1) % NCH, b ^ 1);
       SArr S;
       proj(b, qcur, S);
-      if (ch == 0) {
-        relative(S);
-        rebase(S, true);
-      } else if (__builtin_expect(relative(S), 0)) {
-        rebase(S, false);
+      if constexpr (!RELU) {
+        if (ch == 0) {
+          relative(S);
+          rebase(S, true);
+        } else if (__builtin_expect(relative(S), 0)) {
+          rebase(S, false);
+        }
       }
       apply(b, S);
       staged();
@@ -1196,7 +1222,7 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
 // [64 w, 64 w + 64)).  State per wave, in registers: st[mt][tv] with lane =
 // value column 16 tv + l16 (tv = 4: the ones column, z) and rows = features
 // 16 mt + 4 g + v; its per-feature references cref (log2 units).
-template <int NW>
+template <int NW, bool RELU>
 __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__ Q,
                                                   const uint16_t* __restrict__ K,
                                                   const uint16_t* __restrict__ V,
@@ -1387,11 +1413,12 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
           for (int nt = 0; nt < NT; ++nt)
             SK[mt][nt] = mma_f16(ka[mt][ks], wreg[nt][ks], ks == 0 ? cinit[mt] : SK[mt][nt]);
     }
-    // Per-feature references: lazy raise, always on a segment with no carry.
+    // Per-feature references: lazy raise, always on a segment with no carry
+    // (none for ReLU features).
     bool raise = false;
     float lm[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
+    for (int nt = 0; nt < NT && !RELU; ++nt) {
       const float c = cref[nt] == -INFINITY ? 0.f : cref[nt];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -1402,7 +1429,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       lm[nt] = max3(a, b, fmaxf(SK[1][nt][2], SK[1][nt][3]));
       raise |= (cref[nt] == -INFINITY) || lm[nt] > kTau;
     }
-    if (__builtin_expect(__ballot(raise) != 0, 0)) {
+    if (!RELU && __builtin_expect(__ballot(raise) != 0, 0)) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float tm = colmax4(lm[nt]);
@@ -1427,7 +1454,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
     }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
-      if (g == 0) cb[wave][16 * nt + l16] = cref[nt];
+      if (g == 0) cb[wave][16 * nt + l16] = RELU ? 0.f : cref[nt];
     // K~ (lane = feature, 8 tokens at positions perm_of), and its transpose
     // into Kt (key rows; features permuted within 32-blocks for the MFMA).
     bf16x8 kb[NT];
@@ -1436,8 +1463,8 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       uint32_t p[4];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        p[q] = pack_bf16(fast_exp2(SK[0][nt][2 * q]), fast_exp2(SK[0][nt][2 * q + 1]));
-        p[2 + q] = pack_bf16(fast_exp2(SK[1][nt][2 * q]), fast_exp2(SK[1][nt][2 * q + 1]));
+        p[q] = pack_bf16(feature<RELU>(SK[0][nt][2 * q]), feature<RELU>(SK[0][nt][2 * q + 1]));
+        p[2 + q] = pack_bf16(feature<RELU>(SK[1][nt][2 * q]), feature<RELU>(SK[1][nt][2 * q + 1]));
       }
       kb[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
       const int fl = 16 * nt + l16;                               // local feature
@@ -1480,16 +1507,17 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       const float c = max3(SQ[1][nq][2], SQ[1][nq][3], SQ[2][nq][0]);
       const float d = max3(SQ[2][nq][1], SQ[2][nq][2], SQ[2][nq][3]);
       const float e = max3(SQ[3][nq][0], SQ[3][nq][1], SQ[3][nq][2]);
-      const float M = colmax4(max3(max3(a, b, c), max3(d, e, SQ[3][nq][3]), a));
+      const float M = RELU ? 0.f : colmax4(max3(max3(a, b, c), max3(d, e, SQ[3][nq][3]), a));
       if (g == 0) mq[wave][16 * nq + l16] = M;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         uint32_t p[4];
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-          p[q] = pack_bf16(fast_exp2(SQ[2 * kb2][nq][2 * q] - M), fast_exp2(SQ[2 * kb2][nq][2 * q + 1] - M));
-          p[2 + q] = pack_bf16(fast_exp2(SQ[2 * kb2 + 1][nq][2 * q] - M),
-                               fast_exp2(SQ[2 * kb2 + 1][nq][2 * q + 1] - M));
+          p[q] = pack_bf16(feature<RELU>(SQ[2 * kb2][nq][2 * q] - M),
+                           feature<RELU>(SQ[2 * kb2][nq][2 * q + 1] - M));
+          p[2 + q] = pack_bf16(feature<RELU>(SQ[2 * kb2 + 1][nq][2 * q] - M),
+                               feature<RELU>(SQ[2 * kb2 + 1][nq][2 * q + 1] - M));
         }
         qt[kb2][nq] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
       }
@@ -1623,7 +1651,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
 // The bidirectional path for m = NFB NW FPW features: kpart in NFB feature
 // blocks of NW waves, kcombine, then qapply (W', [KV | z] and c resident in
 // LDS) or, when they do not fit, qstream.
-template <int D, int NW, int NFB>
+template <int D, int NW, int NFB, bool RELU>
 hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                     const float* W, uint16_t* O, char* ws, hipStream_t st) {
   float* P = reinterpret_cast<float*>(ws + p.off_T);
@@ -1634,7 +1662,7 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   // Two token groups while a work-group stays within 8 waves (two per SIMD).
   constexpr int TG = (NW <= 4) ? 2 : 1;
   timing_before(st);
-  kpart<D, NW, TG><<<dim3(p.nseg * p.BH * NFB), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
+  kpart<D, NW, TG, RELU><<<dim3(p.nseg * p.BH * NFB), TG * NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
                                                                        p.seg, p.nseg, p.nseg,
                                                                        p.knorm);
   hipError_t e = hipGetLastError();
@@ -1652,7 +1680,7 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   const size_t lds = qapply_lds_bytes<D>(p.m);
   if (lds <= 160 * 1024) {
     constexpr int QNW = FAVOR_QAPPLY_NW;
-    auto* kern = &qapply<D, QNW, NTQ, NCH>;
+    auto* kern = &qapply<D, QNW, NTQ, NCH, RELU>;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
@@ -1662,14 +1690,15 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
     timing_after(st, "qapply");
   } else {
     timing_before(st);
-    qstream<D, 8, NTQ, NCH><<<dim3(nqb * p.BH), 512, 0, st>>>(Q, W16, Kz, cfin, O, p.L, p.qblk);
+    qstream<D, 8, NTQ, NCH, RELU><<<dim3(nqb * p.BH), 512, 0, st>>>(Q, W16, Kz, cfin, O, p.L,
+                                                                    p.qblk);
     e = hipGetLastError();
     timing_after(st, "qstream");
   }
   return e;
 }
 
-template <int NW>
+template <int NW, bool RELU>
 hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                          const float* W, uint16_t* O, char* ws, hipStream_t st) {
   float* P = reinterpret_cast<float*>(ws + p.off_T);
@@ -1680,7 +1709,7 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     // Key states of every segment but the last (grid nseg - 1; the layout
     // keeps nseg slots per head).
     timing_before(st);
-    kpart<64, NW, 1><<<dim3((p.nseg - 1) * p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
+    kpart<64, NW, 1, RELU><<<dim3((p.nseg - 1) * p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m,
                                                                     p.seg, p.nseg, p.nseg - 1,
                                                                     p.knorm);
     e = hipGetLastError();
@@ -1693,7 +1722,7 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     if (e != hipSuccess) return e;
   }
   timing_before(st);
-  cscan<NW><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg,
+  cscan<NW, RELU><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg,
                                                      p.knorm);
   e = hipGetLastError();
   timing_after(st, "cscan");
@@ -1714,13 +1743,15 @@ hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, cons
   auto* o = static_cast<uint16_t*>(O);
   char* w = static_cast<char*>(ws);
   if (p.d == 64) {
+#define FAVOR_CCASE(NW)                                                            \
+  case NW:                                                                         \
+    return p.relu ? launch_causal<NW, true>(p, q, k, v, W, o, w, stream)           \
+                  : launch_causal<NW, false>(p, q, k, v, W, o, w, stream);
     switch (p.m / 64) {
-      case 1: return launch_causal<1>(p, q, k, v, W, o, w, stream);
-      case 2: return launch_causal<2>(p, q, k, v, W, o, w, stream);
-      case 3: return launch_causal<3>(p, q, k, v, W, o, w, stream);
-      case 4: return launch_causal<4>(p, q, k, v, W, o, w, stream);
+      FAVOR_CCASE(1) FAVOR_CCASE(2) FAVOR_CCASE(3) FAVOR_CCASE(4)
       default: break;
     }
+#undef FAVOR_CCASE
   }
   return hipErrorInvalidValue;
 }
@@ -1775,8 +1806,10 @@ hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const
   char* w = static_cast<char*>(ws);
   int nw, nfb;
   bidir_blocks(p.d, p.m, &nw, &nfb);
-#define FAVOR_CASE(D, NW, NFB) \
-  if (p.d == D && nw == NW && nfb == NFB) return launch_d<D, NW, NFB>(p, q, k, v, W, o, w, stream);
+#define FAVOR_CASE(D, NW, NFB)                                                       \
+  if (p.d == D && nw == NW && nfb == NFB)                                            \
+    return p.relu ? launch_d<D, NW, NFB, true>(p, q, k, v, W, o, w, stream)          \
+                  : launch_d<D, NW, NFB, false>(p, q, k, v, W, o, w, stream);
   FAVOR_CASE(64, 1, 1) FAVOR_CASE(64, 2, 1) FAVOR_CASE(64, 3, 1) FAVOR_CASE(64, 4, 1)
   FAVOR_CASE(64, 5, 1) FAVOR_CASE(64, 6, 1) FAVOR_CASE(64, 7, 1) FAVOR_CASE(64, 8, 1)
   FAVOR_CASE(64, 5, 2) FAVOR_CASE(64, 6, 2) FAVOR_CASE(64, 7, 2) FAVOR_CASE(64, 8, 2)

@@ -63,6 +63,16 @@ __device__ inline float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// A feature from its (relative) projection s: 2^s for the exponential
+// features of the softmax and Gaussian kernels, max(s, 0) for the ReLU
+// features of generalized attention (no reference needed: they cannot
+// overflow, and a constant factor on every feature cancels).
+template <bool RELU>
+__device__ inline float feature(float s) {
+  if constexpr (RELU) return fmaxf(s, 0.f);
+  else return fast_exp2(s);
+}
+
 // fmaxf trees over values produced by ordinary arithmetic (already
 // canonical) lower to v_max3_f32 without extra canonicalisation.
 __device__ inline float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }

@@ -454,3 +454,106 @@ def test_gaussian_text_shape_sampled(fv, causal):
         err = oracle.row_rel_err(_np64(of[h]), _gauss_ref(causal, qf[h], kf[h], vf[h], W))
         print(f"gaussian {w.name} causal={causal} head {h}: row-rel err {err:.3e}", flush=True)
         assert err <= TOL["bf16"], (h, err)
+
+
+# ---------------------------------------------------------------------------
+# Generalized attention with f = ReLU (paper abstract: generalized kernelizable
+# attention): features max(W x, 0)/sqrt(m), the same kernels with no norm term
+# and no exponent references, against the oracle's ReLU features.
+# ---------------------------------------------------------------------------
+RELU_SHAPES = [
+    (1, 2, 17, 32, 48),       # generic path
+    (2, 1, 255, 64, 256),     # matrix-core path, two token groups per work-group
+    (1, 3, 1000, 64, 128),
+    (1, 2, 900, 64, 512),     # one token group, 8 waves
+    (1, 1, 2049, 64, 64),     # causal: nine segments, the last one token long
+    (1, 2, 700, 128, 512),    # streamed query side
+    (1, 1, 1, 64, 256),
+]
+
+
+def _relu_ref(causal, q, k, v, W):
+    f = oracle.causal if causal else oracle.bidir
+    return f(_np64(q), _np64(k), _np64(v), W.astype(np.float64), kernel="relu")
+
+
+def _relu_run(fv, causal, q, k, v, W):
+    f = fv.fwd_causal if causal else fv.fwd_bidir
+    out = f(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(W).cuda(), kernel="relu")
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", RELU_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_relu_shapes(fv, shape, causal, dtype):
+    B, H, L, d, m = shape
+    q, k, v = _case(B, H, L, d, m, dtype, seed=sum(shape) + 91 + causal)
+    W = _w(43 * d + m, m, d)
+    out = _relu_run(fv, causal, q, k, v, W)
+    err = oracle.row_rel_err(_np64(out), _relu_ref(causal, q, k, v, W))
+    assert err <= TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_relu_feature_map_split_identity_and_oracle(fv, dtype):
+    # max(s, 0) - max(-s, 0) = s: phi(x) - phi(-x) = W x / sqrt(m) for every W
+    d, m = 64, 256
+    q, _, _ = _case(1, 2, 300, d, m, dtype, seed=16)
+    W = _w(23, m, d)
+    Wd = torch.from_numpy(W).cuda()
+    x = q.cuda()
+    p = fv.feature_map(x, Wd, kernel="relu")
+    pm = fv.feature_map((-x.float()).to(x.dtype).contiguous(), Wd, kernel="relu")
+    torch.cuda.synchronize()
+    xx = _np64(q)
+    W64 = W.astype(np.float64)
+    lin = xx @ W64.T / math.sqrt(m)
+    scale = np.abs(lin).max()
+    assert np.abs(_np64(p) - _np64(pm) - lin).max() <= 1e-5 * scale
+    assert np.all(_np64(p) >= 0) and np.all(_np64(p) * _np64(pm) == 0)
+    assert np.abs(_np64(p) - oracle.phi_relu(xx, W64)).max() <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_relu_scale_free(fv, causal):
+    # phi_R is positively homogeneous, so O(a q, b k) = O(q, k) for a, b > 0.
+    # fp32 (generic path): powers of two scale every step exactly -> bitwise.
+    q, k, v = _case(1, 2, 300, 64, 128, "f32", seed=24)
+    W = _w(24, 128, 64)
+    o1 = _relu_run(fv, causal, q, k, v, W)
+    o2 = _relu_run(fv, causal, q * 4, k * 0.5, v, W)
+    assert torch.equal(o1, o2)
+    # bf16 (matrix cores): equal to well inside the bar (fp16 subnormals of
+    # the projection's operands round differently after scaling)
+    q, k, v = _case(2, 2, 1500, 64, 256, "bf16", seed=25)
+    W = _w(25, 256, 64)
+    o1 = _relu_run(fv, causal, q, k, v, W)
+    o2 = _relu_run(fv, causal, q * 4, k * 0.5, v, W)
+    err = oracle.row_rel_err(_np64(o2), _np64(o1))
+    assert err <= 4e-3, err
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_relu_ones_in_ones_out(fv, causal):
+    q, k, _ = _case(1, 4, 1500, 64, 256, "bf16", seed=18)
+    ones = torch.ones_like(q)
+    out = _relu_run(fv, causal, q, k, ones, _w(18, 256, 64))
+    assert torch.all(out.float() == 1.0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_relu_text_shape_sampled(fv, causal):
+    w = workloads.workload("text_causal" if causal else "text_bidir")
+    torch.manual_seed(0)
+    q, k, v = workloads.device_qkv(w)
+    W = _w(w.seed_w, w.m, w.d)
+    f = fv.fwd_causal if causal else fv.fwd_bidir
+    out = f(q, k, v, torch.from_numpy(W).cuda(), kernel="relu")
+    torch.cuda.synchronize()
+    qf, kf, vf, of = (x.reshape(w.heads, w.L, w.d) for x in (q, k, v, out))
+    for h in (0, w.heads - 1):
+        err = oracle.row_rel_err(_np64(of[h]), _relu_ref(causal, qf[h], kf[h], vf[h], W))
+        print(f"relu {w.name} causal={causal} head {h}: row-rel err {err:.3e}", flush=True)
+        assert err <= TOL["bf16"], (h, err)

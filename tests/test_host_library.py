@@ -87,7 +87,7 @@ def call_attn(causal=0, attn=0, **kw):
 
 
 @pytest.mark.parametrize("causal", [0, 1])
-@pytest.mark.parametrize("attn", [0, 1])
+@pytest.mark.parametrize("attn", [0, 1, 2])
 def test_attn_entry_validation(causal, attn):
     # favor_fwd_attn validates as favor_fwd_bidir / favor_fwd_causal do
     assert call_attn(causal, attn, B=0) == ESHAPE
@@ -99,7 +99,7 @@ def test_attn_entry_validation(causal, attn):
 
 
 def test_attn_entry_rejects_unknown_kernels():
-    for attn in (-1, 2, 7):
+    for attn in (-1, 3, 7):
         assert call_attn(0, attn) == EUNSUP
         assert call_attn(1, attn) == EUNSUP
         assert lib.favor_feature_map_attn(1, 1, 8, 64, 64, 1, attn, A, A, A, None) == EUNSUP

@@ -164,8 +164,8 @@ GAUSS_PINS = [
     (pins.test_G3_equal_key_norms_make_the_kernels_agree, {}),
 ]
 RELU_PINS = [
-    (pins.test_R1_relu_features_split_the_projection, dict(m=16, d=16)),
-    (pins.test_R3_relu_attention_is_scale_free, {}),
+    (pins.test_U1_relu_features_split_the_projection, dict(m=16, d=16)),
+    (pins.test_U3_relu_attention_is_scale_free, {}),
 ]
 CAUSAL_PINS = [
     (pins.test_P13_causal_first_and_last_rows, {}),
@@ -194,7 +194,7 @@ CAUSAL_PINS = [
     ("ReLU features drop 1/sqrt(m)", "phi_relu", _phi_relu_no_sqrt_m, RELU_PINS),
     ("ReLU features get a positive floor", "phi_relu", _phi_relu_with_bias, RELU_PINS),
     ("arc-cosine kernel with t for pi - t", "arccos_kernel", _arccos_t_for_pi_minus_t,
-     [(pins.test_R2_arccos_kernel_special_cases_and_monte_carlo, {})]),
+     [(pins.test_U2_arccos_kernel_special_cases_and_monte_carlo, {})]),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, target, mutant, pinset):
     monkeypatch.setattr(fo, target, mutant)

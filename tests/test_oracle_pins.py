@@ -510,11 +510,11 @@ def test_G5_convergence_to_gaussian_attention():
 # ---------------------------------------------------------------------------
 # Generalized kernelizable attention with f = ReLU (FAVOR+ method page and
 # the paper's abstract name generalized kernelizable attention; f unnamed,
-# ReLU is the reading taken).  R1-R5 pin phi_relu, arccos_kernel and
+# ReLU is the reading taken).  U1-U5 pin phi_relu, arccos_kernel and
 # arccos_attention.
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("m,d", [(16, 16), (256, 64), (37, 8)])
-def test_R1_relu_features_split_the_projection(m, d):
+def test_U1_relu_features_split_the_projection(m, d):
     # max(s,0) - max(-s,0) = s and max(s,0) max(-s,0) = 0, for every W
     rng = _rng(11 * m + d)
     W = rng.standard_normal((m, d))
@@ -524,7 +524,7 @@ def test_R1_relu_features_split_the_projection(m, d):
     assert np.all(p * n == 0) and np.all(p >= 0)
 
 
-def test_R2_arccos_kernel_special_cases_and_monte_carlo():
+def test_U2_arccos_kernel_special_cases_and_monte_carlo():
     rng = _rng(33)
     x = rng.standard_normal(8)
     u = rng.standard_normal(8)
@@ -541,7 +541,7 @@ def test_R2_arccos_kernel_special_cases_and_monte_carlo():
     assert abs(prod.mean() - k(x, z)) < 4 * se
 
 
-def test_R3_relu_attention_is_scale_free():
+def test_U3_relu_attention_is_scale_free():
     # phi_R is positively homogeneous: scaling Q or K by a positive factor
     # cancels in D^-1 (a plausible exp- or bias-based feature would not)
     Q, K, V, W = _inputs(1, 2, 48, 16, 64, 31)
@@ -555,7 +555,7 @@ def test_R3_relu_attention_is_scale_free():
 
 
 @pytest.mark.slow
-def test_R4_unbiased_arccos_kernel():
+def test_U4_unbiased_arccos_kernel():
     d, N = 16, 20_000
     rng = _rng(71)
     x, y = rng.standard_normal(d) * 0.7, rng.standard_normal(d) * 0.7
@@ -569,7 +569,7 @@ def test_R4_unbiased_arccos_kernel():
 
 
 @pytest.mark.slow
-def test_R5_convergence_to_arccos_attention():
+def test_U5_convergence_to_arccos_attention():
     errs = []
     for m in (16, 2048):
         e = []
