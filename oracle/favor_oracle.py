@@ -48,6 +48,10 @@ design notes):
   expectation over w ~ N(0, I_d) is the first-order arc-cosine kernel
   ``|x| |y| (sin t + (pi - t) cos t) / (2 pi)``, t the angle between x and y.
   A query whose features are all zero (e.g. q = 0) has no defined output.
+* The backward pass (gradients of the outputs with respect to Q, K and V for
+  an upstream gradient dO) is not printed on the pages; it is the plain chain
+  rule through the definitions above, with W held fixed (it is redrawn, not
+  trained).  The ReLU derivative at exactly 0 is taken as 0.
 * The random stream is a counter-based SplitMix64 (Steele, Lea & Flood,
   "Fast splittable pseudorandom number generators", OOPSLA 2014) feeding the
   Box-Muller transform; the pages name no generator.
@@ -79,6 +83,11 @@ __all__ = [
     "bidir",
     "causal",
     "brute",
+    "phi_vjp",
+    "attend_bidir_vjp",
+    "attend_causal_vjp",
+    "bidir_backward",
+    "causal_backward",
     "softmax_attention",
     "gaussian_attention",
     "arccos_kernel",
@@ -295,6 +304,113 @@ def brute(Q, K, V, W, is_causal: bool, kernel: str = "softmax") -> np.ndarray:
     den = A.sum(axis=-1)
     assert np.all(den > 0)
     return (A @ np.asarray(V, dtype=np.float64)) / den[..., None]
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: vector-Jacobian products by the chain rule through the
+# definitions above (the pages print no backward pass).  For an upstream
+# gradient dO of the outputs, each function returns the gradients of
+# <dO, O> with respect to its inputs.  W is held fixed.
+# ---------------------------------------------------------------------------
+def phi_vjp(X, W, G, kernel: str = "softmax") -> np.ndarray:
+    """Gradient with respect to X of <G, phi(X)> for the features of `kernel`.
+
+    X is [..., L, d], W [m, d], G [..., L, m].  With Phi = phi(X):
+      softmax  d phi_r / dx = phi_r (w_r - x)      -> (G*Phi) W - sum_r(G*Phi) x
+      gaussian d phi_r / dx = phi_r (w_r - 2 x)    -> (G*Phi) W - 2 sum_r(G*Phi) x
+      relu     d phi_r / dx = [w_r . x > 0] w_r / sqrt(m)
+    """
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    if kernel == "relu":
+        gate = (X @ W.T > 0).astype(np.float64)
+        return ((G * gate) @ W) / math.sqrt(W.shape[0])
+    c = {"softmax": 1.0, "gaussian": 2.0}[kernel]
+    P = G * _features(kernel)(X, W)
+    return P @ W - c * np.sum(P, axis=-1, keepdims=True) * X
+
+
+def attend_bidir_vjp(Qp, Kp, V, dO):
+    """Gradients (dQ', dK', dV) of <dO, attend_bidir(Q', K', V)>.
+
+    Forward in the page's bracketing: S = (K')^T V, z = (K')^T 1_L,
+    num = Q' S, den = Q' z, out = num / den.  Backward, step by step:
+      dnum = dO / den,  dden = -sum_c dO num / den^2,
+      dQ' = dnum S^T + dden z^T,  dS = (Q')^T dnum,  dz = (Q')^T dden,
+      dK' = V dS^T + 1_L dz^T,  dV = K' dS.
+    """
+    Qp, Kp, V, dO = (np.asarray(x, dtype=np.float64) for x in (Qp, Kp, V, dO))
+    S = np.swapaxes(Kp, -1, -2) @ V
+    z = np.sum(Kp, axis=-2)
+    num = Qp @ S
+    den = np.einsum("...lm,...m->...l", Qp, z)
+    assert np.all(den > 0), "non-positive normaliser"
+    dnum = dO / den[..., None]
+    dden = -np.sum(dO * num, axis=-1) / den ** 2
+    dQp = dnum @ np.swapaxes(S, -1, -2) + dden[..., :, None] * z[..., None, :]
+    dS = np.swapaxes(Qp, -1, -2) @ dnum
+    dz = np.einsum("...lm,...l->...m", Qp, dden)
+    dKp = V @ np.swapaxes(dS, -1, -2) + dz[..., None, :]
+    dV = Kp @ dS
+    return dQp, dKp, dV
+
+
+def attend_causal_vjp(Qp, Kp, V, dO):
+    """Gradients (dQ', dK', dV) of <dO, attend_causal(Q', K', V)>, token by token.
+
+    A forward sweep rebuilds the prefix states S_i, z_i and gives
+    dq'_i = S_i dnum_i + z_i dden_i; a backward sweep over i = L-1 .. 0 keeps
+    the suffix sums R_j = sum_{i>=j} q'_i dnum_i^T and r_j = sum_{i>=j} q'_i dden_i,
+    which give dk'_j = R_j v_j + r_j and dv_j = R_j^T k'_j.
+    """
+    Qp, Kp, V, dO = (np.asarray(x, dtype=np.float64) for x in (Qp, Kp, V, dO))
+    lead = Qp.shape[:-2]
+    L, m = Qp.shape[-2:]
+    dv = V.shape[-1]
+    dnum = np.empty(lead + (L, dv))
+    dden = np.empty(lead + (L,))
+    dQp = np.empty(lead + (L, m))
+    S = np.zeros(lead + (m, dv))
+    z = np.zeros(lead + (m,))
+    for i in range(L):
+        k = Kp[..., i, :]
+        S += k[..., :, None] * V[..., i, None, :]
+        z += k
+        q = Qp[..., i, :]
+        num = np.einsum("...m,...md->...d", q, S)
+        den = np.einsum("...m,...m->...", q, z)
+        assert np.all(den > 0), "non-positive normaliser"
+        dnum[..., i, :] = dO[..., i, :] / den[..., None]
+        dden[..., i] = -np.sum(dO[..., i, :] * num, axis=-1) / den ** 2
+        dQp[..., i, :] = np.einsum("...md,...d->...m", S, dnum[..., i, :]) + z * dden[..., i, None]
+    dKp = np.empty(lead + (L, m))
+    dV = np.empty(lead + (L, dv))
+    R = np.zeros(lead + (m, dv))
+    r = np.zeros(lead + (m,))
+    for j in range(L - 1, -1, -1):
+        q = Qp[..., j, :]
+        R += q[..., :, None] * dnum[..., j, None, :]
+        r += q * dden[..., j, None]
+        dKp[..., j, :] = np.einsum("...md,...d->...m", R, V[..., j, :]) + r
+        dV[..., j, :] = np.einsum("...md,...m->...d", R, Kp[..., j, :])
+    return dQp, dKp, dV
+
+
+def _backward(attend_vjp, Q, K, V, W, dO, kernel):
+    f = _features(kernel)
+    dQp, dKp, dV = attend_vjp(f(Q, W), f(K, W), V, dO)
+    return phi_vjp(Q, W, dQp, kernel), phi_vjp(K, W, dKp, kernel), dV
+
+
+def bidir_backward(Q, K, V, W, dO, kernel: str = "softmax"):
+    """(dQ, dK, dV) of <dO, bidir(Q, K, V, W, kernel)>, fp64."""
+    return _backward(attend_bidir_vjp, Q, K, V, W, dO, kernel)
+
+
+def causal_backward(Q, K, V, W, dO, kernel: str = "softmax"):
+    """(dQ, dK, dV) of <dO, causal(Q, K, V, W, kernel)>, fp64."""
+    return _backward(attend_causal_vjp, Q, K, V, W, dO, kernel)
 
 
 def softmax_attention(Q, K, V, is_causal: bool = False) -> np.ndarray:

@@ -15,7 +15,8 @@ import test_oracle_pins as pins
 
 # the real functions, saved before any patching, for mutants built on them
 _REAL = {n: getattr(fo, n) for n in ("draw_w", "attend_causal", "softmax_attention",
-                                     "gaussian_attention", "arccos_kernel")}
+                                     "gaussian_attention", "arccos_kernel", "phi_vjp",
+                                     "attend_bidir_vjp", "attend_causal_vjp")}
 
 
 def _phi_no_norm(X, W):
@@ -174,6 +175,88 @@ CAUSAL_PINS = [
 ]
 
 
+def _phi_vjp_norm_sign(X, W, G, kernel="softmax"):
+    # the norm term's derivative added instead of subtracted
+    if kernel == "relu":
+        return _REAL["phi_vjp"](X, W, G, kernel)
+    X = np.asarray(X, float)
+    P = np.asarray(G, float) * fo._features(kernel)(X, W)
+    c = {"softmax": 1.0, "gaussian": 2.0}[kernel]
+    return P @ np.asarray(W, float) + c * np.sum(P, -1, keepdims=True) * X
+
+
+def _phi_vjp_relu_no_sqrt_m(X, W, G, kernel="softmax"):
+    out = _REAL["phi_vjp"](X, W, G, kernel)
+    return out * math.sqrt(W.shape[0]) if kernel == "relu" else out
+
+
+def _phi_vjp_relu_no_gate(X, W, G, kernel="softmax"):
+    if kernel != "relu":
+        return _REAL["phi_vjp"](X, W, G, kernel)
+    return (np.asarray(G, float) @ np.asarray(W, float)) / math.sqrt(W.shape[0])
+
+
+def _bidir_vjp_no_dden(Qp, Kp, V, dO):
+    # forgets that the normaliser depends on the features too
+    S = np.swapaxes(Kp, -1, -2) @ V
+    z = np.sum(Kp, axis=-2)
+    den = np.einsum("...lm,...m->...l", Qp, z)
+    dnum = dO / den[..., None]
+    dS = np.swapaxes(Qp, -1, -2) @ dnum
+    return dnum @ np.swapaxes(S, -1, -2), V @ np.swapaxes(dS, -1, -2), Kp @ dS
+
+
+def _bidir_vjp_no_dz(Qp, Kp, V, dO):
+    dQp, _, dV = _REAL["attend_bidir_vjp"](Qp, Kp, V, dO)
+    S = np.swapaxes(Kp, -1, -2) @ V
+    den = np.einsum("...lm,...m->...l", Qp, np.sum(Kp, axis=-2))
+    dS = np.swapaxes(Qp, -1, -2) @ (dO / den[..., None])
+    return dQp, V @ np.swapaxes(dS, -1, -2), dV
+
+
+def _causal_vjp_prefix_for_suffix(Qp, Kp, V, dO):
+    # the key side sums over earlier queries instead of later ones
+    dQp, _, _ = _REAL["attend_causal_vjp"](Qp, Kp, V, dO)
+    f = lambda x: np.flip(x, axis=-2)
+    _, dKr, dVr = _REAL["attend_causal_vjp"](f(Qp), f(Kp), f(V), f(dO))
+    return dQp, f(dKr), f(dVr)
+
+
+def _causal_vjp_strict_suffix(Qp, Kp, V, dO):
+    # the key side skips the diagonal query (i > j instead of i >= j)
+    dQp, dKp, dV = _REAL["attend_causal_vjp"](Qp, Kp, V, dO)
+    L = Qp.shape[-2]
+    Kp2 = np.array(Kp, dtype=float)
+    S = np.cumsum(Kp2[..., :, :, None] * np.asarray(V, float)[..., :, None, :], axis=-3)
+    z = np.cumsum(Kp2, axis=-2)
+    num = np.einsum("...lm,...lmd->...ld", Qp, S)
+    den = np.einsum("...lm,...lm->...l", Qp, z)
+    dnum = dO / den[..., None]
+    dden = -np.sum(dO * num, -1) / den ** 2
+    corr_k = Qp * (np.einsum("...ld,...ld->...l", dnum, V) + dden)[..., None]
+    corr_v = np.einsum("...lm,...lm->...l", Qp, Kp2)[..., None] * dnum
+    return dQp, dKp - corr_k, dV - corr_v
+
+
+BWD_PINS = [(pins.test_B1_gradients_match_central_differences, dict(kernel=k, causal=c))
+            for k, c in pins._BWD_CASES] + [
+            (pins.test_B3_gradient_invariants, dict(kernel=k, causal=c)) for k, c in pins._BWD_CASES]
+
+
+@pytest.mark.parametrize("name,target,mutant", [
+    ("feature gradient adds the norm term", "phi_vjp", _phi_vjp_norm_sign),
+    ("ReLU feature gradient drops 1/sqrt(m)", "phi_vjp", _phi_vjp_relu_no_sqrt_m),
+    ("ReLU feature gradient ignores the gate", "phi_vjp", _phi_vjp_relu_no_gate),
+    ("bidirectional gradient drops the normaliser's term", "attend_bidir_vjp", _bidir_vjp_no_dden),
+    ("bidirectional key gradient drops dz", "attend_bidir_vjp", _bidir_vjp_no_dz),
+    ("causal key side sums over earlier queries", "attend_causal_vjp", _causal_vjp_prefix_for_suffix),
+    ("causal key side skips the diagonal", "attend_causal_vjp", _causal_vjp_strict_suffix),
+])
+def test_planted_backward_mistake_is_caught(monkeypatch, name, target, mutant):
+    monkeypatch.setattr(fo, target, mutant)
+    assert _run_pins(BWD_PINS) >= 1, f"no pin caught: {name}"
+
+
 @pytest.mark.parametrize("name,target,mutant,pinset", [
     ("phi drops the norm term", "phi", _phi_no_norm, PHI_PINS),
     ("phi adds the norm term", "phi", _phi_plus_norm, PHI_PINS),
@@ -209,5 +292,5 @@ def test_softmax_scale_mistake_is_caught(monkeypatch):
 
 
 def test_real_oracle_passes_the_same_pins():
-    for pinset in (PHI_PINS, DRAW_PINS, BIDIR_PINS, CAUSAL_PINS, GAUSS_PINS, RELU_PINS):
+    for pinset in (PHI_PINS, DRAW_PINS, BIDIR_PINS, CAUSAL_PINS, GAUSS_PINS, RELU_PINS, BWD_PINS):
         assert _run_pins(pinset) == 0

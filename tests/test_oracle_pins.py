@@ -583,3 +583,111 @@ def test_U5_convergence_to_arccos_attention():
             e.append(np.linalg.norm(oracle.bidir(Q, K, V, W, kernel="relu") - ref) / np.linalg.norm(ref))
         errs.append(np.mean(e))
     assert errs[1] < 0.25 * errs[0], errs
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (chain rule through the definitions; the pages print none).
+# B1-B4 pin phi_vjp, attend_bidir_vjp, attend_causal_vjp and the composed
+# bidir_backward / causal_backward.
+# ---------------------------------------------------------------------------
+_BWD_CASES = [(k, c) for k in ("softmax", "gaussian", "relu") for c in (False, True)]
+
+
+def _bwd_inputs(kernel, seed, L=20, d=8):
+    m = 64 if kernel == "relu" else 16     # (ReLU: no all-zero first causal row)
+    Q, K, V, W = _inputs(1, 2, L, d, m, seed, scale=0.6)
+    dO = _rng(seed + 7).standard_normal(V.shape)
+    return Q, K, V, W, dO
+
+
+def _fwd_bwd(causal):
+    return ((oracle.causal, oracle.causal_backward) if causal
+            else (oracle.bidir, oracle.bidir_backward))
+
+
+@pytest.mark.parametrize("kernel,causal", _BWD_CASES)
+def test_B1_gradients_match_central_differences(kernel, causal):
+    # directional derivative of <dO, O> along random directions, h = 1e-6
+    Q, K, V, W, dO = _bwd_inputs(kernel, 101 + 2 * causal)
+    fwd, bwd = _fwd_bwd(causal)
+    grads = bwd(Q, K, V, W, dO, kernel)
+    rng = _rng(55)
+    h = 1e-6
+    for idx in range(3):
+        for _ in range(2):
+            D = rng.standard_normal(Q.shape)
+            plus, minus = [Q, K, V], [Q, K, V]
+            plus[idx] = plus[idx] + h * D
+            minus[idx] = minus[idx] - h * D
+            fd = (np.sum(dO * fwd(*plus, W, kernel)) - np.sum(dO * fwd(*minus, W, kernel))) / (2 * h)
+            an = np.sum(grads[idx] * D)
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (idx, fd, an)
+
+
+@pytest.mark.parametrize("kernel,causal", _BWD_CASES)
+def test_B2_gradients_match_torch_autograd_of_the_quadratic_form(kernel, causal):
+    # an independent forward in torch fp64 (features and A = Q'K'^T, masked,
+    # O = A V / A 1), differentiated by torch's autograd
+    torch = pytest.importorskip("torch")
+    Q, K, V, W, dO = _bwd_inputs(kernel, 202 + causal, L=24)
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (Q, K, V)]
+    Wt = torch.tensor(W, dtype=torch.float64)
+    m = W.shape[0]
+
+    def feat(x):
+        s = x @ Wt.T
+        if kernel == "relu":
+            return torch.relu(s) / math.sqrt(m)
+        c = 0.5 if kernel == "softmax" else 1.0
+        return torch.exp(s - c * (x * x).sum(-1, keepdim=True)) / math.sqrt(m)
+
+    A = feat(t[0]) @ feat(t[1]).transpose(-1, -2)
+    if causal:
+        A = torch.tril(A)
+    O = (A @ t[2]) / A.sum(-1, keepdim=True)
+    (O * torch.tensor(dO)).sum().backward()
+    grads = _fwd_bwd(causal)[1](Q, K, V, W, dO, kernel)
+    for g, x in zip(grads, t):
+        np.testing.assert_allclose(g, x.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+@pytest.mark.parametrize("kernel,causal", _BWD_CASES)
+def test_B3_gradient_invariants(kernel, causal):
+    Q, K, V, W, dO = _bwd_inputs(kernel, 303 + causal)
+    dQ, dK, dV = _fwd_bwd(causal)[1](Q, K, V, W, dO, kernel)
+    # each output row is a convex combination of value rows: sum_j dv_j = sum_i dO_i
+    np.testing.assert_allclose(dV.sum(-2), dO.sum(-2), rtol=1e-12, atol=1e-12)
+    if causal:
+        # row 0 is v_0 whatever q_0 is
+        assert np.abs(dQ[..., 0, :]).max() <= 1e-14 * np.abs(dQ).max()
+    # V with identical rows: O is constant, so Q and K get no gradient
+    Vc = np.broadcast_to(V[..., :1, :], V.shape).copy()
+    dQc, dKc, _ = _fwd_bwd(causal)[1](Q, K, Vc, W, dO, kernel)
+    assert np.abs(dQc).max() <= 1e-12 and np.abs(dKc).max() <= 1e-12
+    if kernel == "relu":
+        # positive homogeneity: rescaling one query, or every key, leaves O
+        np.testing.assert_allclose(np.sum(dQ * Q, -1), 0, atol=1e-12)
+        np.testing.assert_allclose(np.sum(dK * K, (-1, -2)), 0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_B4_single_feature_has_no_query_gradient(causal):
+    # m = 1: q' is a positive scalar per row and cancels in the division, so
+    # O does not depend on Q; dK and dV follow from O_i = sum_j k'_j v_j / sum_j k'_j
+    Q, K, V, _ = _inputs(1, 1, 12, 4, 16, 404, scale=0.7)
+    W = oracle.draw_w(405, 1, 4)
+    dO = _rng(406).standard_normal(V.shape)
+    dQ, dK, dV = _fwd_bwd(causal)[1](Q, K, V, W, dO)
+    assert np.abs(dQ).max() <= 1e-13
+    k = np.exp(K[0, 0] @ W[0] - 0.5 * np.sum(K[0, 0] ** 2, -1))      # (1/sqrt(m) = 1)
+    L = len(k)
+    mask = np.tril(np.ones((L, L))) if causal else np.ones((L, L))
+    Z = mask @ k                                                        # per row i
+    O = (mask * k) @ V[0, 0] / Z[:, None]
+    # dV_j = sum_i mask_ij k_j dO_i / Z_i ; dk'_j = sum_i mask_ij (v_j - O_i).dO_i / Z_i
+    dV_ref = k[:, None] * (mask.T @ (dO[0, 0] / Z[:, None]))
+    dkp = np.sum(mask.T[:, :, None] * (V[0, 0][:, None, :] - O[None, :, :]) * (dO[0, 0] / Z[:, None])[None],
+                 axis=(1, 2))
+    dK_ref = (dkp * k)[:, None] * (W[0][None, :] - K[0, 0])
+    np.testing.assert_allclose(dV[0, 0], dV_ref, rtol=1e-12)
+    np.testing.assert_allclose(dK[0, 0], dK_ref, rtol=1e-10, atol=1e-13)
