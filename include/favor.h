@@ -151,6 +151,34 @@ int favor_fwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
                    size_t workspace_bytes, void* stream);
 
 /*
+ * Workspace size, in bytes, of favor_bwd_attn for this shape (written to
+ * *bytes): the forward's key state and references plus, per query, the
+ * scaled upstream gradient [dO/den | -(dO . O)/den] and its row reference,
+ * and the per-segment query state.  Returns FAVOR_OK or a validation error
+ * (bytes untouched).  Pure host function: no HIP call.
+ */
+int favor_bwd_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
+                              int32_t dtype, int32_t causal, size_t* bytes);
+
+/*
+ * Backward pass of favor_fwd_attn (the pages print none; it is the chain rule
+ * through the same definitions, with W held fixed -- the pages redraw W, they
+ * do not train it): for an upstream gradient dO [B,H,L,d] of the output,
+ * writes dQ, dK, dV [B,H,L,d], the gradients of <dO, O> with respect to Q, K
+ * and V, for either form (causal = 0 or 1) and any attn_kernel (the ReLU
+ * derivative at exactly 0 is taken as 0).  Inputs and outputs share the
+ * dtype; every buffer is in device memory, 16-byte aligned; the outputs may
+ * not alias any input or each other.  The forward is recomputed inside the
+ * call (no forward output is taken).  Workspace of at least
+ * favor_bwd_workspace_bytes() bytes, 256-byte aligned.  Errors as
+ * favor_fwd_attn.
+ */
+int favor_bwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                   int32_t causal, int32_t attn_kernel, const void* Q, const void* K,
+                   const void* V, const float* W, const void* dO, void* dQ, void* dK, void* dV,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The feature map alone, for testing the projection and exponent arithmetic:
  * Xp[b,h,l,r] = exp(w_r . x_{b,h,l} - |x_{b,h,l}|^2 / 2) / sqrt(m), fp32
  * [B,H,L,m] in device memory, with no exponent shift (the caller keeps the

@@ -1,13 +1,14 @@
-"""FAVOR+ attention forward pass for AMD Instinct MI355X (gfx950).
+"""FAVOR+ attention for AMD Instinct MI355X (gfx950): forward and backward passes.
 
 Positive orthogonal random features and linear-time attention, bidirectional
-and causal, computed by hand-written HIP kernels in libfavor.so (C ABI in
+and causal, with their gradients, computed by hand-written HIP kernels in libfavor.so (C ABI in
 include/favor.h).  This package is the thin Python binding over that library.
 """
 from ._binding import (BF16, F32, GAUSSIAN, LIB_PATH, RELU, SOFTMAX, FavorError,  # noqa: F401
-                       draw_projection, feature_map, fwd_bidir, fwd_causal, plan_describe,
+                       bwd, bwd_workspace_bytes, draw_projection, feature_map, fwd_bidir,
+                       fwd_causal, plan_describe,
                        status_string, timing_start, timing_stop, workspace_bytes)
 
-__all__ = ["fwd_bidir", "fwd_causal", "feature_map", "draw_projection", "workspace_bytes",
+__all__ = ["fwd_bidir", "fwd_causal", "bwd", "bwd_workspace_bytes", "feature_map", "draw_projection", "workspace_bytes",
            "status_string", "plan_describe", "timing_start", "timing_stop", "FavorError", "LIB_PATH", "F32",
            "BF16", "SOFTMAX", "GAUSSIAN", "RELU"]

@@ -15,6 +15,7 @@ import numpy as np
 import torch
 
 __all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
+           "bwd", "bwd_workspace_bytes",
            "feature_map", "draw_projection", "status_string", "plan_describe", "timing_start", "timing_stop",
            "F32", "BF16", "SOFTMAX", "GAUSSIAN", "RELU"]
 
@@ -51,6 +52,10 @@ def _load():
         f.restype = ctypes.c_int
     L.favor_fwd_attn.argtypes = [i32] * 8 + [vp, vp, vp, fp, vp, vp, sz, vp]
     L.favor_fwd_attn.restype = ctypes.c_int
+    L.favor_bwd_workspace_bytes.argtypes = [i32] * 7 + [ctypes.POINTER(sz)]
+    L.favor_bwd_workspace_bytes.restype = ctypes.c_int
+    L.favor_bwd_attn.argtypes = [i32] * 8 + [vp, vp, vp, fp, vp, vp, vp, vp, vp, sz, vp]
+    L.favor_bwd_attn.restype = ctypes.c_int
     L.favor_feature_map.argtypes = [i32] * 6 + [vp, fp, vp, vp]
     L.favor_feature_map.restype = ctypes.c_int
     L.favor_feature_map_attn.argtypes = [i32] * 7 + [vp, fp, vp, vp]
@@ -88,6 +93,13 @@ def workspace_bytes(B, H, L, d, m, dtype=BF16, causal=False) -> int:
     out = ctypes.c_size_t(0)
     _check(lib.favor_workspace_bytes(B, H, L, d, m, dtype, int(bool(causal)), ctypes.byref(out)),
            "favor_workspace_bytes")
+    return out.value
+
+
+def bwd_workspace_bytes(B, H, L, d, m, dtype=BF16, causal=False) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.favor_bwd_workspace_bytes(B, H, L, d, m, dtype, int(bool(causal)),
+                                         ctypes.byref(out)), "favor_bwd_workspace_bytes")
     return out.value
 
 
@@ -151,6 +163,30 @@ def _forward(name, causal, q, k, v, W, out, workspace, stream, kernel="softmax")
         name = "favor_fwd_attn"
         st = lib.favor_fwd_attn(B, H, L, d, m, dt, int(causal), ak, *ptrs)
     _check(st, name)
+    return out
+
+
+def bwd(q, k, v, W, do, causal=False, kernel="softmax", out=None, workspace=None, stream=None):
+    """Backward pass (favor_bwd_attn): (dQ, dK, dV), the gradients of <do, O> for the
+    forward fwd_causal (causal=True) or fwd_bidir with the same kernel; W is held fixed.
+    out, if given, is a tuple of three contiguous tensors like Q."""
+    ak = _kernel(kernel)
+    B, H, L, d, m, dt = _shape_of(q, k, v, W)
+    if do.shape != q.shape or do.dtype != q.dtype or not do.is_contiguous() or not do.is_cuda:
+        raise ValueError("do must be a contiguous GPU tensor like Q")
+    need = bwd_workspace_bytes(B, H, L, d, m, dt, causal)
+    if out is None:
+        out = tuple(torch.empty_like(q) for _ in range(3))
+    elif len(out) != 3 or any(o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous()
+                              for o in out):
+        raise ValueError("out must be three contiguous tensors like Q")
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.favor_bwd_attn(B, H, L, d, m, dt, int(bool(causal)), ak, q.data_ptr(), k.data_ptr(),
+                            v.data_ptr(), W.data_ptr(), do.data_ptr(), out[0].data_ptr(),
+                            out[1].data_ptr(), out[2].data_ptr(), workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(q, stream))
+    _check(st, "favor_bwd_attn")
     return out
 
 

@@ -71,7 +71,35 @@ int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype
   return FAVOR_OK;
 }
 
+int backward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
+             int32_t attn_kernel, const void* Q, const void* K, const void* V, const float* W,
+             const void* dO, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
+             void* stream) {
+  const int status = check_shape(B, H, L, d, m, dtype);
+  if (status != FAVOR_OK) return status;
+  const float knorm = norm_coefficient(attn_kernel);
+  if (knorm < 0.f) return FAVOR_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !W || !dO || !dQ || !dK || !dV || !ws) return FAVOR_ERR_NULL;
+  for (const void* x : {Q, K, V, static_cast<const void*>(W), dO,
+                        static_cast<const void*>(dQ), static_cast<const void*>(dK),
+                        static_cast<const void*>(dV)})
+    if (!is_aligned(x, 16)) return FAVOR_ERR_ALIGN;
+  if (!is_aligned(ws, 256)) return FAVOR_ERR_ALIGN;
+  Plan p;
+  BwdPlan b;
+  make_bwd_plan(B, H, L, d, m, dtype, causal, &p, &b);
+  if (ws_bytes < b.bytes) return FAVOR_ERR_WORKSPACE;
+  p.knorm = knorm;
+  p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
+  const hipError_t e = generic_backward(p, b, Q, K, V, W, dO, dQ, dK, dV, ws,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail_hip(e);
+  return FAVOR_OK;
+}
+
 }  // namespace
+
+void make_generic_plan(Plan* p);
 
 int record_hip_error(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -130,6 +158,15 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
     p->bytes = off;
     return;
   }
+  make_generic_plan(p);
+}
+
+void make_generic_plan(Plan* p) {
+  const size_t ncol = static_cast<size_t>(p->d) + 1;
+  const size_t BH = static_cast<size_t>(p->BH);
+  const size_t m = static_cast<size_t>(p->m);
+  const int32_t causal = p->causal, L = p->L;
+  size_t off = 0;
   p->path = kPathGeneric;
   // Sequence splits (bidirectional) and segments (causal); a multiple of the
   // 8-token tile of the generic kernels.
@@ -141,6 +178,22 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
   p->off_KV = off;   off = align256(off + (causal ? 0 : BH * m * ncol * sizeof(float)));
   p->off_cfin = off; off = align256(off + (causal ? 0 : BH * m * sizeof(float)));
   p->bytes = off;
+}
+
+void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                   int32_t causal, Plan* p, BwdPlan* b) {
+  std::memset(p, 0, sizeof(*p));
+  p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
+  p->BH = B * H;
+  make_generic_plan(p);
+  const size_t ncol = static_cast<size_t>(d) + 1;
+  const size_t BH = static_cast<size_t>(p->BH);
+  size_t off = p->bytes;
+  b->off_U = off;    off = align256(off + BH * L * ncol * sizeof(float));
+  b->off_M = off;    off = align256(off + BH * L * sizeof(float));
+  b->off_G = off;    off = align256(off + BH * p->nseg * m * ncol * sizeof(float));
+  b->off_Gfin = off; off = align256(off + (causal ? 0 : BH * m * ncol * sizeof(float)));
+  b->bytes = off;
 }
 
 }  // namespace favor
@@ -193,6 +246,26 @@ int favor_fwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
                         workspace, workspace_bytes, stream);
 }
 
+int favor_bwd_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
+                              int32_t dtype, int32_t causal, size_t* bytes) {
+  const int st = favor::check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  if (!bytes) return FAVOR_ERR_NULL;
+  favor::Plan p;
+  favor::BwdPlan b;
+  favor::make_bwd_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p, &b);
+  *bytes = b.bytes;
+  return FAVOR_OK;
+}
+
+int favor_bwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                   int32_t causal, int32_t attn_kernel, const void* Q, const void* K,
+                   const void* V, const float* W, const void* dO, void* dQ, void* dK, void* dV,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  return favor::backward(B, H, L, d, m, dtype, causal ? 1 : 0, attn_kernel, Q, K, V, W, dO, dQ,
+                         dK, dV, workspace, workspace_bytes, stream);
+}
+
 int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                            int32_t attn_kernel, const void* X, const float* W, float* Xp,
                            void* stream) {
@@ -226,7 +299,9 @@ const char* favor_status_string(int status) {
              "FAVOR_GAUSSIAN or FAVOR_RELU)";
     case FAVOR_ERR_ALIGN:
       return "misaligned pointer (tensors need 16-byte, the workspace 256-byte alignment)";
-    case FAVOR_ERR_WORKSPACE: return "workspace smaller than favor_workspace_bytes()";
+    case FAVOR_ERR_WORKSPACE:
+      return "workspace smaller than favor_workspace_bytes() (favor_bwd_workspace_bytes() for "
+             "the backward pass)";
     case FAVOR_ERR_HIP: return "a HIP runtime call failed (see favor_last_hip_error)";
     default: return "unknown status";
   }

@@ -56,9 +56,30 @@ struct Plan {
 void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                int32_t causal, Plan* p);
 
+// Backward pass: the generic path's key-state layout (Plan, path forced to
+// kPathGeneric) followed by
+//   U    [BH][L][d+1]         Ucat_i = [dO_i / den_i | -(dO_i . O_i) / den_i]
+//   M    [BH][L]              the query rows' references
+//   G    [BH][nseg][m][d+1]   per-segment query state sum_i Q~_ir Ucat_i, then
+//                             (causal) its exclusive suffix over later segments
+//   Gfin [BH][m][d+1]         bidirectional total of G
+struct BwdPlan {
+  size_t off_U, off_M, off_G, off_Gfin;
+  size_t bytes;
+};
+void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                   int32_t causal, Plan* p, BwdPlan* b);
+
 // Generic path: enqueue the whole forward pass on `stream`.
 hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const void* V,
                            const float* W, void* O, void* ws, hipStream_t stream);
+// Its first two steps alone: the key state and references in the workspace.
+hipError_t generic_key_state(const Plan& p, const void* K, const void* V, const float* W,
+                             void* ws, hipStream_t stream);
+// Generic backward: dQ, dK, dV of <dO, O> (same dtype as the inputs).
+hipError_t generic_backward(const Plan& p, const BwdPlan& b, const void* Q, const void* K,
+                            const void* V, const float* W, const void* dO, void* dQ, void* dK,
+                            void* dV, void* ws, hipStream_t stream);
 
 // MFMA path (bf16 inputs): shape support, and the bidirectional forward.
 bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype);

@@ -28,68 +28,12 @@
 
 #include "favor.h"
 #include "favor_internal.h"
+#include "generic_common.h"
 
 namespace favor {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kFB = 32;   // features per g_state block
-constexpr int kTT = 8;    // tokens per tile
-constexpr int kMaxD = 128;
-constexpr int kMaxM = 1024;
-
-__device__ inline float load_x(const float* p, size_t i) { return p[i]; }
-__device__ inline float load_x(const uint16_t* p, size_t i) {
-  return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
-}
-
-// fp32 -> bf16, round to nearest even; NaN stays NaN.
-__device__ inline uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-__device__ inline void store_x(float* p, size_t i, float v) { p[i] = v; }
-__device__ inline void store_x(uint16_t* p, size_t i, float v) { p[i] = to_bf16(v); }
-
-// Loads kTT rows [j0, j0+kTT) of a [L, d] matrix into LDS (zero past L).
-template <typename T>
-__device__ inline void load_rows(const T* __restrict__ X, size_t base, int j0, int jend, int d,
-                                 float (*dst)[kMaxD + 1]) {
-  for (int i = threadIdx.x; i < kTT * d; i += kThreads) {
-    const int j = i / d, a = i - j * d;
-    dst[j][a] = (j0 + j < jend) ? load_x(X, base + static_cast<size_t>(j0 + j) * d + a) : 0.f;
-  }
-}
-
-// Norm terms knorm |x|^2 of the kTT rows in `rows` (first kTT threads):
-// knorm = 1/2 for the softmax kernel's features, 1 for the Gaussian's.
-__device__ inline void norm_terms(const float (*rows)[kMaxD + 1], int d, float knorm, float* nrm) {
-  if (threadIdx.x < kTT) {
-    float acc = 0.f;
-    for (int a = 0; a < d; ++a) acc = fmaf(rows[threadIdx.x][a], rows[threadIdx.x][a], acc);
-    nrm[threadIdx.x] = knorm * acc;
-  }
-}
-
-// The feature of exponent (or, for ReLU features, projection) e: exp(e), or
-// max(e, 0) when relu is set.  ReLU features take no norm term and no
-// reference (knorm = 0 and every reference 0).
-__device__ inline float feat(float e, int relu) { return relu ? fmaxf(e, 0.f) : expf(e); }
-
-// w . x over d coordinates, w from global memory (row of W), x from LDS.
-__device__ inline float dot_w(const float* __restrict__ w, const float* x, int d) {
-  float acc = 0.f;
-  for (int a = 0; a < d; a += 4) {
-    const float4 wv = *reinterpret_cast<const float4*>(w + a);
-    acc = fmaf(wv.x, x[a], acc);
-    acc = fmaf(wv.y, x[a + 1], acc);
-    acc = fmaf(wv.z, x[a + 2], acc);
-    acc = fmaf(wv.w, x[a + 3], acc);
-  }
-  return acc;
-}
+using namespace generic_detail;
 
 // ---------------------------------------------------------------------------
 // 1. Per-segment key state.  grid (nseg, ceil(m / kFB), BH).
@@ -404,9 +348,11 @@ __global__ __launch_bounds__(kThreads) void g_feature_map(const T* __restrict__ 
   }
 }
 
+// Steps 1 and 2: the key state (bidirectional: KV and cfin; causal: the
+// exclusive prefixes in T with references cP, and the segment references).
 template <typename T>
-hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const float* W, T* O,
-                     char* ws, hipStream_t st) {
+hipError_t key_state_t(const Plan& p, const T* K, const T* V, const float* W, char* ws,
+                       hipStream_t st) {
   float* Tst = reinterpret_cast<float*>(ws + p.off_T);
   float* cseg = reinterpret_cast<float*>(ws + p.off_cseg);
   float* cP = reinterpret_cast<float*>(ws + p.off_cP);
@@ -424,7 +370,19 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
       Tst, cseg, cP, KV, cfin, p.nseg, p.m, p.d, p.causal);
   e = hipGetLastError();
   timing_after(st, "g_combine");
+  return e;
+}
+
+template <typename T>
+hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const float* W, T* O,
+                     char* ws, hipStream_t st) {
+  hipError_t e = key_state_t(p, K, V, W, ws, st);
   if (e != hipSuccess) return e;
+  float* Tst = reinterpret_cast<float*>(ws + p.off_T);
+  float* cseg = reinterpret_cast<float*>(ws + p.off_cseg);
+  float* cP = reinterpret_cast<float*>(ws + p.off_cP);
+  float* KV = reinterpret_cast<float*>(ws + p.off_KV);
+  float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   const dim3 ga((p.L + kTT - 1) / kTT, p.BH);
   timing_before(st);
   if (p.causal)
@@ -449,6 +407,16 @@ hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const vo
   return forward_t<uint16_t>(p, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
                              static_cast<const uint16_t*>(V), W, static_cast<uint16_t*>(O), w,
                              stream);
+}
+
+hipError_t generic_key_state(const Plan& p, const void* K, const void* V, const float* W,
+                             void* ws, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  if (p.dtype == FAVOR_F32)
+    return key_state_t<float>(p, static_cast<const float*>(K), static_cast<const float*>(V), W, w,
+                              stream);
+  return key_state_t<uint16_t>(p, static_cast<const uint16_t*>(K), static_cast<const uint16_t*>(V),
+                               W, w, stream);
 }
 
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,

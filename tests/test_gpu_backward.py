@@ -1,0 +1,189 @@
+"""GPU parity of the backward pass: favor_bwd_attn (through the C ABI) against
+the fp64 oracle's bidir_backward / causal_backward.
+
+Metric: per (b, h), max |gpu - oracle| over the head's gradient divided by the
+largest |oracle| entry of that head's gradient, maximised over heads (a
+per-row bar does not fit gradients: causal dq_0 is exactly 0).  Bars: 1e-4
+for fp32 inputs, 2e-2 for bf16 inputs (bf16 output rounding alone is up to
+2^-9 of an entry).  The GPU and the oracle get the same input values and the
+same fp32 W bytes.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def fv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_kernelized_attention_favor_amd as m
+    return m
+
+
+def _np64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def grad_err(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    num = np.abs(got - ref).max(axis=(-1, -2))
+    den = np.abs(ref).max(axis=(-1, -2))
+    return float(np.max(num / den))
+
+
+def _relu_gate_check(name, got, ref, X, W, dXp, tol):
+    """ReLU gradients with the gate decided where the pages leave it open.
+
+    The gate [w_r . x > 0] is a floating-point decision: where |w_r . x| is
+    within the fp32 projection's rounding of 0, the GPU and the oracle may
+    decide it differently, and both answers are gradients of the same
+    function (one-sided derivatives at the kink).  Rows within the bar are
+    accepted; a row outside it passes only if flipping some of its ambiguous
+    gates (|w_r . x| <= 1e-5 |x| |w_r|, at most 3) in the oracle's gradient
+    dx = sum_r [w_r . x > 0] dX'_r w_r / sqrt(m) brings it within the bar.
+    """
+    m = W.shape[0]
+    S = X @ W.T
+    amb = np.abs(S) <= 1e-5 * np.linalg.norm(X, axis=-1, keepdims=True) * np.linalg.norm(W, axis=-1)
+    scale = np.abs(ref).max(axis=(-1, -2), keepdims=True)
+    row_err = np.abs(got - ref).max(-1) / scale[..., 0]
+    for idx in zip(*np.nonzero(row_err > tol)):
+        rs = np.nonzero(amb[idx])[0]
+        assert 0 < len(rs) <= 3, (name, idx, float(row_err[idx]), len(rs))
+        best = np.inf
+        for flips in itertools.product((0, 1), repeat=len(rs)):
+            alt = ref[idx].copy()
+            for r, f in zip(rs, flips):
+                if f:
+                    sign = -1.0 if S[idx + (r,)] > 0 else 1.0
+                    alt += sign * dXp[idx + (r,)] * W[r] / math.sqrt(m)
+            best = min(best, np.abs(got[idx] - alt).max() / scale[idx[:-1]][0, 0])
+        assert best <= tol, (name, idx, best)
+
+
+def _case(shape, dtype, seed, kernel):
+    B, H, L, d, m = shape
+    rng = np.random.default_rng(seed)
+    s = d ** -0.25
+    q, k, v, do = (rng.standard_normal((B, H, L, d), dtype=np.float32) for _ in range(4))
+    q *= np.float32(s)
+    k *= np.float32(s)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    W = oracle.draw_w(seed + 3, m, d).astype(np.float32)
+    return tuple(torch.from_numpy(x).to(td) for x in (q, k, v, do)) + (W,)
+
+
+def _gpu(fv, q, k, v, W, do, causal, kernel):
+    out = fv.bwd(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(W).cuda(), do.cuda(),
+                 causal=causal, kernel=kernel)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle(q, k, v, W, do, causal, kernel):
+    f = oracle.causal_backward if causal else oracle.bidir_backward
+    return f(_np64(q), _np64(k), _np64(v), W.astype(np.float64), _np64(do), kernel)
+
+
+SHAPES = [
+    (1, 1, 1, 16, 16),
+    (1, 2, 17, 32, 48),
+    (2, 1, 255, 64, 256),
+    (1, 3, 600, 64, 128),      # causal: three segments, the last one partial
+    (1, 1, 1030, 16, 64),      # causal: five segments, the last six tokens
+    (1, 1, 300, 128, 1024),
+]
+
+
+@pytest.mark.parametrize("kernel", ["softmax", "gaussian", "relu"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_shapes(fv, shape, causal, dtype, kernel):
+    if kernel == "relu" and shape[4] < 64:
+        shape = shape[:4] + (64,)          # (no all-zero ReLU feature rows)
+    q, k, v, do, W = _case(shape, dtype, sum(shape) + 7 * causal, kernel)
+    got = _gpu(fv, q, k, v, W, do, causal, kernel)
+    ref = _oracle(q, k, v, W, do, causal, kernel)
+    if kernel == "relu":
+        W64 = W.astype(np.float64)
+        vjp = oracle.attend_causal_vjp if causal else oracle.attend_bidir_vjp
+        dQp, dKp, _ = vjp(oracle.phi_relu(_np64(q), W64), oracle.phi_relu(_np64(k), W64),
+                          _np64(v), _np64(do))
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        if name in ("dQ", "dK") and shape[2] == 1:
+            # one token: O = v_0 whatever q and k are, so dQ = dK = 0 up to rounding
+            assert np.abs(_np64(g)).max() <= 1e-5 * np.abs(ref[2]).max()
+            continue
+        if kernel == "relu" and name != "dV":
+            X, dXp = (q, dQp) if name == "dQ" else (k, dKp)
+            _relu_gate_check(name, _np64(g), r, _np64(X), W64, dXp, TOL[dtype])
+            continue
+        err = grad_err(_np64(g), r)
+        assert err <= TOL[dtype], (name, err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_value_gradient_sums_and_causal_first_row(fv, causal):
+    # sum_j dv_j = sum_i dO_i (each output row is a convex combination of
+    # value rows); causal dq_0 = 0 (row 0 is v_0); at a size the oracle
+    # would take long on
+    q, k, v, do, W = _case((1, 2, 4096, 64, 256), "f32", 61 + causal, "softmax")
+    dq, dk, dv = _gpu(fv, q, k, v, W, do, causal, "softmax")
+    s_dv = _np64(dv).sum(-2)
+    s_do = _np64(do).sum(-2)
+    assert np.abs(s_dv - s_do).max() <= 1e-4 * np.abs(s_do).max()
+    if causal:
+        assert np.abs(_np64(dq)[..., 0, :]).max() <= 1e-6 * np.abs(_np64(dq)).max()
+
+
+def test_backward_constant_values_give_no_query_or_key_gradient(fv):
+    q, k, v, do, W = _case((1, 2, 700, 64, 256), "f32", 71, "softmax")
+    vc = v[..., :1, :].expand_as(v).contiguous()
+    for causal in (False, True):
+        dq, dk, _ = _gpu(fv, q, k, vc, W, do, causal, "softmax")
+        _, _, dv = _gpu(fv, q, k, v, W, do, causal, "softmax")
+        scale = np.abs(_np64(dv)).max()
+        assert np.abs(_np64(dq)).max() <= 1e-5 * scale
+        assert np.abs(_np64(dk)).max() <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_bitwise_deterministic(fv, causal):
+    q, k, v, do, W = _case((2, 2, 777, 64, 128), "bf16", 81, "softmax")
+    a = _gpu(fv, q, k, v, W, do, causal, "softmax")
+    b = _gpu(fv, q, k, v, W, do, causal, "softmax")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_text_shape_sampled(fv, causal):
+    w = workloads.workload("text_causal" if causal else "text_bidir")
+    torch.manual_seed(0)
+    q, k, v = workloads.device_qkv(w)
+    do = torch.randn_like(q, dtype=torch.float32).to(q.dtype)
+    W = oracle.draw_w(w.seed_w, w.m, w.d).astype(np.float32)
+    got = fv.bwd(q, k, v, torch.from_numpy(W).cuda(), do, causal=causal)
+    torch.cuda.synchronize()
+    shp = (w.heads, w.L, w.d)
+    qf, kf, vf, df = (x.reshape(shp) for x in (q, k, v, do))
+    gf = [g.reshape(shp) for g in got]
+    for h in (0, w.heads - 1):
+        ref = _oracle(qf[h], kf[h], vf[h], W, df[h], causal, "softmax")
+        for name, g, r in zip(("dQ", "dK", "dV"), gf, ref):
+            err = grad_err(_np64(g[h])[None], r[None])
+            print(f"backward {w.name} head {h} {name}: {err:.3e}", flush=True)
+            assert err <= TOL["bf16"], (h, name, err)

@@ -109,6 +109,47 @@ def test_attn_entry_rejects_unknown_kernels():
     assert lib.favor_last_hip_error() == 0
 
 
+def call_bwd(causal=0, attn=0, **kw):
+    a = dict(B=1, H=1, L=16, d=64, m=64, dtype=1, Q=A, K=A, V=A, W=A, dO=A, dQ=A, dK=A, dV=A,
+             ws=A, wsb=1 << 40)
+    a.update(kw)
+    return lib.favor_bwd_attn(a["B"], a["H"], a["L"], a["d"], a["m"], a["dtype"], causal, attn,
+                              a["Q"], a["K"], a["V"], a["W"], a["dO"], a["dQ"], a["dK"], a["dV"],
+                              a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("causal", [0, 1])
+@pytest.mark.parametrize("attn", [0, 1, 2])
+def test_bwd_entry_validation(causal, attn):
+    assert call_bwd(causal, attn, B=0) == ESHAPE
+    assert call_bwd(causal, attn, L=0) == ESHAPE
+    assert call_bwd(causal, attn, d=48) == EUNSUP
+    assert call_bwd(causal, attn, m=8) == EUNSUP
+    assert call_bwd(causal, attn, dtype=3) == EUNSUP
+    for k in ("Q", "K", "V", "W", "dO", "dQ", "dK", "dV", "ws"):
+        assert call_bwd(causal, attn, **{k: None}) == ENULL
+    for k in ("Q", "K", "V", "W", "dO", "dQ", "dK", "dV"):
+        assert call_bwd(causal, attn, **{k: MIS}) == EALIGN
+    assert call_bwd(causal, attn, ws=A + 128) == EALIGN
+    need = fv.bwd_workspace_bytes(1, 1, 16, 64, 64, 1, bool(causal))
+    assert call_bwd(causal, attn, wsb=need - 1) == EWS
+    assert lib.favor_last_hip_error() == 0
+
+
+def test_bwd_rejects_unknown_kernels_and_sizes_its_workspace():
+    for attn in (-1, 3):
+        assert call_bwd(0, attn) == EUNSUP
+        assert call_bwd(1, attn) == EUNSUP
+    for causal in (False, True):
+        for (B, H, L, d, m) in [(1, 1, 1, 16, 16), (8, 8, 4096, 64, 256), (1, 1, 4097, 128, 1024)]:
+            n = fv.bwd_workspace_bytes(B, H, L, d, m, 1, causal)
+            # the key state, and per query (d + 2) floats: Ucat and the row reference
+            assert n >= B * H * (m * (d + 1) + L * (d + 2)) * 4
+            assert n % 256 == 0
+    with pytest.raises(fv.FavorError):
+        fv.bwd_workspace_bytes(1, 1, 1, 24, 16)
+
+
 def test_feature_map_validation():
     f = lib.favor_feature_map
     assert f(1, 1, 0, 64, 64, 1, A, A, A, None) == ESHAPE
