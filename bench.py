@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Throughput of the FAVOR+ forward pass on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload text_bidir]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload text_bidir] [--pass bwd]
 
 A step is one forward call (favor_fwd_bidir or favor_fwd_causal) over one
 batch of synthetic inputs of the workload's shape, inputs already resident in
-HBM.  Calls rotate over several input/output buffer sets (>= 1 GiB in total,
+HBM; with --pass bwd, one backward call (favor_bwd_attn: dQ, dK, dV for a
+seeded upstream gradient dO, the forward's state recomputed inside).  Calls rotate over several input/output buffer sets (>= 1 GiB in total,
 four times the 256 MiB last-level cache) so that the timing is an HBM
 measurement, not a cache one.  W steps are run untimed, then exactly K steps
 are timed between two events recorded on the stream the kernels run on, with
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector FMA, published (256 CUs at 2.4 GHz)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -50,6 +52,8 @@ def parse():
     ap.add_argument("--causal", action="store_true", help="time the causal form of the workload")
     ap.add_argument("--kernel", choices=("softmax", "gaussian", "relu"), default="softmax",
                     help="attention kernel the features estimate (default softmax)")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward pass")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -121,6 +125,15 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     flops.
     """
     th = w.heads * w.L
+    # Backward (favor_bwd_attn): Q, K, V, dO read and dQ, dK, dV written once
+    # (7 d elements per token*head); 22 d m flops: the key state (4 d m),
+    # the query side (projection, [num | den], T, dq: 8 d m), the query
+    # state from the features (2 d m) and the key side (projection, H, dk,
+    # dv: 8 d m).
+    bwd = {"gb_query": (3, 8.0), "gb_gstate": (0, 2.0), "gb_key": (2, 8.0)}
+    if name in bwd:
+        nb, nf = bwd[name]
+        return (nb * w.d * elem * th, nf * w.d * w.m * th)
     if name == "kpart" and w.causal:
         th = w.heads * min(w.L, (nseg - 1) * seg)     # the last segment is not summarised
     half = (2 * w.d * elem * th, 4.0 * w.d * w.m * th)
@@ -131,7 +144,7 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     return (0, 0.0)
 
 
-def cpu_baseline(w, seconds: float, kernel: str = "softmax"):
+def cpu_baseline(w, seconds: float, kernel: str = "softmax", backward: bool = False):
     """Time the fp64 oracle on whole heads of the same workload (host cores)."""
     import numpy as np
     import oracle
@@ -143,6 +156,11 @@ def cpu_baseline(w, seconds: float, kernel: str = "softmax"):
         threads = len(os.sched_getaffinity(0))
     W = oracle.draw_w(w.seed_w, w.m, w.d)
     f = oracle.causal if w.causal else oracle.bidir
+    if backward:
+        fb = oracle.causal_backward if w.causal else oracle.bidir_backward
+        rng = np.random.default_rng(w.seed_in + 5)
+        dO = rng.standard_normal((w.L, w.d))
+        f = lambda q, k, v, W, kernel: fb(q, k, v, W, dO, kernel)
     heads = 0
     spent = 0.0
     # One head's inputs from the host generator (drawn outside the timing);
@@ -164,7 +182,8 @@ def cpu_baseline(w, seconds: float, kernel: str = "softmax"):
     return {"value": tok / spent, "unit": "tokens*heads/s", "cores": int(threads),
             "host_cores": len(os.sched_getaffinity(0)), "cpu_model": model,
             "kind": "oracle",
-            "sample": f"{heads} of {w.heads} heads of {w.name} ({kernel} kernel, L={w.L}, d={w.d}, m={w.m}, "
+            "sample": f"{heads} of {w.heads} heads of {w.name} ({'backward, ' if backward else ''}"
+                      f"{kernel} kernel, L={w.L}, d={w.d}, m={w.m}, "
                       f"{'causal' if w.causal else 'bidirectional'}), fp64 numpy, "
                       f"{spent:.1f} s"}
 
@@ -351,17 +370,31 @@ def main():
     W = torch.from_numpy(fv.draw_projection(w.seed_w, w.m, w.d)).to(dev)
 
     elem = 2 if w.dtype == "bf16" else 4
-    set_bytes = 4 * w.heads * w.L * w.d * elem
+    backward = args.pass_ == "bwd"
+    set_bytes = (8 if backward else 4) * w.heads * w.L * w.d * elem
     nsets = 1 if args.cache_hot else max(1, -(-(1 << 30) // set_bytes))
     sets = []
     for i in range(nsets):
         q, k, v = workloads.device_qkv(w, seed=w.seed_in + 7919 * i)
-        sets.append((q, k, v, torch.empty_like(q)))
-    ws = torch.empty(fv.workspace_bytes(w.B, w.H, w.L, w.d, w.m, fv.BF16 if w.dtype == "bf16"
-                                        else fv.F32, w.causal), dtype=torch.uint8, device=dev)
+        if backward:
+            g = torch.Generator(device=dev).manual_seed(w.seed_in + 5 + i)
+            do = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+            sets.append((q, k, v, do, tuple(torch.empty_like(q) for _ in range(3))))
+        else:
+            sets.append((q, k, v, torch.empty_like(q)))
+    dt_code = fv.BF16 if w.dtype == "bf16" else fv.F32
+    ws_bytes = (fv.bwd_workspace_bytes if backward else fv.workspace_bytes)(
+        w.B, w.H, w.L, w.d, w.m, dt_code, w.causal)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     fwd_ = fv.fwd_causal if w.causal else fv.fwd_bidir
-    fwd = lambda *a, **kw: fwd_(*a, kernel=args.kernel, **kw)
     stream = torch.cuda.current_stream(dev)
+    if backward:
+        def fwd(q, k, v, W, out, workspace, stream):
+            return fv.bwd(q, k, v, W, out[0], causal=w.causal, kernel=args.kernel, out=out[1],
+                          workspace=workspace, stream=stream)
+        sets = [(q, k, v, (do, outs)) for (q, k, v, do, outs) in sets]
+    else:
+        fwd = lambda *a, **kw: fwd_(*a, kernel=args.kernel, **kw)
 
     def step(i):
         q, k, v, o = sets[i % nsets]
@@ -476,20 +509,23 @@ def main():
 
     tokens = w.heads * w.L
     value = tokens / (ms * 1e-3)
-    alg_bytes = 4 * w.heads * w.L * w.d * elem                 # Q, K, V read + O written once
-    alg_flops = 8.0 * w.heads * w.L * w.d * w.m
+    alg_bytes = (7 if backward else 4) * w.heads * w.L * w.d * elem   # inputs read + outputs written once
+    alg_flops = (22.0 if backward else 8.0) * w.heads * w.L * w.d * w.m
     achieved_tflops = alg_flops / (ms * 1e-3) / 1e12
 
-    def roofline(nbytes, nflops, sec):
+    def roofline(nbytes, nflops, sec, alu=False):
+        # alu: fp32 FMA kernels (the generic path), priced against the fp32
+        # vector peak instead of the matrix cores'
+        peak = FP32_VALU_PEAK_TFLOPS if alu else BF16_PEAK_TFLOPS
         t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-        t_mfma = nflops / (BF16_PEAK_TFLOPS * 1e12)
+        t_mfma = nflops / (peak * 1e12)
         if t_hbm >= t_mfma:
             a = nbytes / sec / 1e9
             return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(a / HBM_PEAK_GBS, 4)}
         a = nflops / sec / 1e12
-        return {"bound": "mfma", "achieved": round(a, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(a / BF16_PEAK_TFLOPS, 4)}
+        return {"bound": "alu" if alu else "mfma", "achieved": round(a, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(a / peak, 4)}
 
     _, nseg, seg = fv.plan_describe(w.B, w.H, w.L, w.d, w.m,
                                     fv.BF16 if w.dtype == "bf16" else fv.F32, w.causal)
@@ -500,18 +536,21 @@ def main():
                          "alg_bytes": kb, "alg_flops": kf}
     dom = max(kt, key=lambda n: kt[n][0])
     dsec = kt[dom][0] / kt[dom][1] * 1e-3
-    roof = roofline(kernels[dom]["alg_bytes"], kernels[dom]["alg_flops"], dsec)
+    generic = dom.startswith("g_") or dom.startswith("gb_")
+    roof = roofline(kernels[dom]["alg_bytes"], kernels[dom]["alg_flops"], dsec, alu=generic)
     # (counter summaries exist for the softmax-kernel runs only)
-    roof["traffic"] = measured_traffic(w.name, w.causal, dom) if args.kernel == "softmax" else None
-    mf = measured_counters(w.name, w.causal, dom) if args.kernel == "softmax" else None
+    counted = args.kernel == "softmax" and not backward
+    roof["traffic"] = measured_traffic(w.name, w.causal, dom) if counted else None
+    mf = measured_counters(w.name, w.causal, dom) if counted else None
     if mf is not None:
         roof["mfma_executed_frac"] = mf
     roof["kernel"] = dom
     roof["kernel_avg_us"] = kernels[dom]["avg_us"]
-    whole = roofline(alg_bytes, alg_flops, ms * 1e-3)
+    whole = roofline(alg_bytes, alg_flops, ms * 1e-3, alu=generic)
 
     out = {
-        "metric": "FAVOR+ fwd tokens*heads/s + % of roofline, B8 H8 L4096 d64 m256",
+        "metric": ("FAVOR+ bwd tokens*heads/s, B8 H8 L4096 d64 m256" if backward else
+                   "FAVOR+ fwd tokens*heads/s + % of roofline, B8 H8 L4096 d64 m256"),
         "value": round(value, 1),
         "unit": "tokens*heads/s",
         "n_gpus": 1,
@@ -524,7 +563,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded Gaussian Q, K, V; orthogonal Gaussian W)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m,
-                   "causal": w.causal, "attn_kernel": args.kernel, "buffer_sets": nsets,
+                   "causal": w.causal, "attn_kernel": args.kernel, "pass": args.pass_,
+                   "buffer_sets": nsets,
                    "cache": "hot" if args.cache_hot else "rotating >= 1 GiB"},
         "repeats": {"n": len(reps), "min_ms": round(reps[0], 5),
                     "median_ms": round(reps[len(reps) // 2], 5), "max_ms": round(reps[-1], 5)},
@@ -538,7 +578,7 @@ def main():
     if redraw:
         out["redraw"] = redraw
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.kernel)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.kernel, backward)
     print(json.dumps(out), flush=True)
 
 

@@ -169,8 +169,8 @@ void make_generic_plan(Plan* p) {
   size_t off = 0;
   p->path = kPathGeneric;
   // Sequence splits (bidirectional) and segments (causal); a multiple of the
-  // 8-token tile of the generic kernels.
-  p->seg = causal ? 256 : 512;
+  // 8-token tile of the generic kernels (a caller may preset a segment length).
+  if (p->seg <= 0) p->seg = causal ? 256 : 512;
   p->nseg = (L + p->seg - 1) / p->seg;
   p->off_T = off;    off = align256(off + BH * p->nseg * m * ncol * sizeof(float));
   p->off_cseg = off; off = align256(off + BH * p->nseg * m * sizeof(float));
@@ -185,6 +185,9 @@ void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
   std::memset(p, 0, sizeof(*p));
   p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
   p->BH = B * H;
+  // Causal: 64-token segments (the masked in-segment terms of the backward
+  // cost O(segment) per token; the forward's 256 would quadruple them).
+  p->seg = causal ? 64 : 0;
   make_generic_plan(p);
   const size_t ncol = static_cast<size_t>(d) + 1;
   const size_t BH = static_cast<size_t>(p->BH);

@@ -101,8 +101,8 @@ SHAPES = [
     (1, 1, 1, 16, 16),
     (1, 2, 17, 32, 48),
     (2, 1, 255, 64, 256),
-    (1, 3, 600, 64, 128),      # causal: three segments, the last one partial
-    (1, 1, 1030, 16, 64),      # causal: five segments, the last six tokens
+    (1, 3, 600, 64, 128),      # causal: ten 64-token segments, the last one partial
+    (1, 1, 1030, 16, 64),      # causal: seventeen segments, the last six tokens
     (1, 1, 300, 128, 1024),
 ]
 
