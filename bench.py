@@ -6,7 +6,10 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload text_bidir] [--p
 A step is one forward call (favor_fwd_bidir or favor_fwd_causal) over one
 batch of synthetic inputs of the workload's shape, inputs already resident in
 HBM; with --pass bwd, one backward call (favor_bwd_attn: dQ, dK, dV for a
-seeded upstream gradient dO, the forward's state recomputed inside).  Calls rotate over several input/output buffer sets (>= 1 GiB in total,
+seeded upstream gradient dO, the forward's state recomputed inside); with
+--pass prefill, one causal favor_prefill call exporting the state; with
+--pass decode, one favor_decode call (one new token for each of the B*H heads,
+the state updated in place).  Calls rotate over several input/output buffer sets (>= 1 GiB in total,
 four times the 256 MiB last-level cache) so that the timing is an HBM
 measurement, not a cache one.  W steps are run untimed, then exactly K steps
 are timed between two events recorded on the stream the kernels run on, with
@@ -52,8 +55,10 @@ def parse():
     ap.add_argument("--causal", action="store_true", help="time the causal form of the workload")
     ap.add_argument("--kernel", choices=("softmax", "gaussian", "relu"), default="softmax",
                     help="attention kernel the features estimate (default softmax)")
-    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd"), default="fwd",
-                    help="time the forward (default) or the backward pass")
+    ap.add_argument("--pass", dest="pass_", choices=("fwd", "bwd", "prefill", "decode"),
+                    default="fwd",
+                    help="time the forward (default), the backward pass, the causal prefill "
+                         "that exports its state, or one decoding step per head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -131,6 +136,11 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     # state from the features (2 d m) and the key side (projection, H, dk,
     # dv: 8 d m).
     bwd = {"gb_query": (3, 8.0), "gb_gstate": (0, 2.0), "gb_key": (2, 8.0)}
+    if name == "g_decode":
+        # one token per head: the state [m][d+4] fp32 read and written, q, k,
+        # v read and o written; two projections, the state update and the
+        # contraction (8 d m flops)
+        return (w.heads * (2 * w.m * (w.d + 4) * 4 + 4 * w.d * elem), 8.0 * w.d * w.m * w.heads)
     if name in bwd:
         nb, nf = bwd[name]
         return (nb * w.d * elem * th, nf * w.d * w.m * th)
@@ -340,6 +350,59 @@ def pmc_summary(root: str, workload: str, causal: bool):
     print("\n".join(lines), flush=True)
 
 
+def decode_bench(args, w, fv, W, dev, elem):
+    """--pass decode: K favor_decode calls (one token per head each) on a
+    state filled by the warmup calls; one JSON line like the forward's."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev).manual_seed(w.seed_in)
+    td = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    n = 64                                   # token slots cycled through
+    toks = [tuple((torch.randn((w.B, w.H, w.d), generator=g, device=dev) * s).to(td)
+                  for s in (w.d ** -0.25, w.d ** -0.25, 1.0)) for _ in range(n)]
+    outs = [torch.empty((w.B, w.H, w.d), dtype=td, device=dev) for _ in range(n)]
+    st = fv.state_new(w.B, w.H, w.d, w.m)
+
+    def step(i):
+        q, k, v = toks[i % n]
+        fv.decode(q, k, v, W, st, kernel=args.kernel, out=outs[i % n], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    fv.timing_start()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    kt = fv.timing_stop()
+    tot, launches = kt["g_decode"]
+    sec = tot / launches * 1e-3
+    nb, nf = kernel_work("g_decode", w, 1, w.L, elem)
+    a = nb / sec / 1e9
+    out = {
+        "metric": "FAVOR+ causal decode tokens*heads/s, B8 H8 d64 m256",
+        "value": round(w.heads / (ms * 1e-3), 1), "unit": "tokens*heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian q, k, v per step; orthogonal Gaussian W)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "m": w.m,
+                   "attn_kernel": args.kernel, "pass": "decode"},
+        "roofline": {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "g_decode",
+                     "kernel_avg_us": round(sec * 1e6, 3)},
+        "kernels": {"g_decode": {"avg_us": round(sec * 1e6, 3), "launches": launches,
+                                 "alg_bytes": nb, "alg_flops": nf}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -370,6 +433,11 @@ def main():
     W = torch.from_numpy(fv.draw_projection(w.seed_w, w.m, w.d)).to(dev)
 
     elem = 2 if w.dtype == "bf16" else 4
+    if args.pass_ in ("prefill", "decode"):
+        w = w.with_(causal=True)
+    if args.pass_ == "decode":
+        decode_bench(args, w, fv, W, dev, elem)
+        return
     backward = args.pass_ == "bwd"
     set_bytes = (8 if backward else 4) * w.heads * w.L * w.d * elem
     nsets = 1 if args.cache_hot else max(1, -(-(1 << 30) // set_bytes))
@@ -388,7 +456,15 @@ def main():
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     fwd_ = fv.fwd_causal if w.causal else fv.fwd_bidir
     stream = torch.cuda.current_stream(dev)
-    if backward:
+    if args.pass_ == "prefill":
+        ws_bytes = fv._binding.prefill_workspace_bytes(w.B, w.H, w.L, w.d, w.m, dt_code)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        st_out = fv.state_new(w.B, w.H, w.d, w.m)
+
+        def fwd(q, k, v, W, out, workspace, stream):
+            return fv.prefill(q, k, v, W, state_in=None, state_out=st_out, kernel=args.kernel,
+                              out=out, workspace=workspace, stream=stream)
+    elif backward:
         def fwd(q, k, v, W, out, workspace, stream):
             return fv.bwd(q, k, v, W, out[0], causal=w.causal, kernel=args.kernel, out=out[1],
                           workspace=workspace, stream=stream)
@@ -550,6 +626,8 @@ def main():
 
     out = {
         "metric": ("FAVOR+ bwd tokens*heads/s, B8 H8 L4096 d64 m256" if backward else
+                   "FAVOR+ causal prefill tokens*heads/s, B8 H8 L4096 d64 m256"
+                   if args.pass_ == "prefill" else
                    "FAVOR+ fwd tokens*heads/s + % of roofline, B8 H8 L4096 d64 m256"),
         "value": round(value, 1),
         "unit": "tokens*heads/s",

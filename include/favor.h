@@ -179,6 +179,57 @@ int favor_bwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Incremental causal state (masked form in prefix-sum order; thesis record
+ * "Random Features for Efficient Attention Approximation", abstract: masked
+ * attention in linear time): the running sums S = sum_j phi(k_j) v_j^T and
+ * z = sum_j phi(k_j) of the tokens seen so far, for streaming and
+ * token-by-token decoding.
+ *
+ * Layout   fp32 [B*H][m][d+4] in device memory (16-byte aligned), one row
+ *          per feature r: [S~_r (d values) | z~_r | c_r | 0 | 0], the true state
+ *          [S | z]_r = exp(c_r) sqrt(m)^-1 [S~_r | z~_r] (c_r a per-feature
+ *          exponent reference that keeps S~ in fp32 range; for FAVOR_RELU
+ *          c_r = 0 once a token was added).  Empty state: S~ = z~ = 0,
+ *          c = -inf.  The buffer is the export/import format: copy it to keep
+ *          a stream's state, pass it back to continue it.  A state is tied to
+ *          its (d, m, W, attn_kernel).
+ */
+/* Bytes of the states of B*H heads (B*H*m*(d+4)*4).  Pure host function. */
+int favor_state_bytes(int32_t B, int32_t H, int32_t d, int32_t m, size_t* bytes);
+
+/* Empty states for B*H heads (a fill kernel on `stream`, no memset node). */
+int favor_state_reset(int32_t B, int32_t H, int32_t d, int32_t m, float* state, void* stream);
+
+/* Workspace bytes of favor_prefill for this shape.  Pure host function. */
+int favor_prefill_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
+                                  int32_t dtype, size_t* bytes);
+
+/*
+ * Causal forward over L new tokens that continues a state: O (as
+ * favor_fwd_attn with causal = 1) where token i attends to the carried
+ * tokens of state_in and to the new tokens j <= i.  state_in (NULL: empty)
+ * and state_out (NULL: not written) are states as above and may not alias;
+ * state_out receives the state after the last new token.  Runs on the fp32
+ * FMA kernels for every shape and dtype.  Workspace of at least
+ * favor_prefill_workspace_bytes() bytes, 256-byte aligned.  Errors as
+ * favor_fwd_attn.
+ */
+int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                  int32_t attn_kernel, const void* Q, const void* K, const void* V,
+                  const float* W, void* O, const float* state_in, float* state_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One decoding step for every head: the new token's k, v ([B,H,d] in
+ * `dtype`) are added to `state` in place, then o = the causal output of the
+ * new token's q over every token in the state (itself included).  One
+ * work-group per head; no workspace.  Errors as favor_fwd_attn (L is 1).
+ */
+int favor_decode(int32_t B, int32_t H, int32_t d, int32_t m, int32_t dtype, int32_t attn_kernel,
+                 const void* q, const void* k, const void* v, const float* W, void* o,
+                 float* state, void* stream);
+
+/*
  * The feature map alone, for testing the projection and exponent arithmetic:
  * Xp[b,h,l,r] = exp(w_r . x_{b,h,l} - |x_{b,h,l}|^2 / 2) / sqrt(m), fp32
  * [B,H,L,m] in device memory, with no exponent shift (the caller keeps the

@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 __all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
-           "bwd", "bwd_workspace_bytes",
+           "bwd", "bwd_workspace_bytes", "state_bytes", "state_new", "state_reset", "prefill", "prefill_workspace_bytes",
+           "decode",
            "feature_map", "draw_projection", "status_string", "plan_describe", "timing_start", "timing_stop",
            "F32", "BF16", "SOFTMAX", "GAUSSIAN", "RELU"]
 
@@ -56,6 +57,16 @@ def _load():
     L.favor_bwd_workspace_bytes.restype = ctypes.c_int
     L.favor_bwd_attn.argtypes = [i32] * 8 + [vp, vp, vp, fp, vp, vp, vp, vp, vp, sz, vp]
     L.favor_bwd_attn.restype = ctypes.c_int
+    L.favor_state_bytes.argtypes = [i32] * 4 + [ctypes.POINTER(sz)]
+    L.favor_state_bytes.restype = ctypes.c_int
+    L.favor_state_reset.argtypes = [i32] * 4 + [vp, vp]
+    L.favor_state_reset.restype = ctypes.c_int
+    L.favor_prefill_workspace_bytes.argtypes = [i32] * 6 + [ctypes.POINTER(sz)]
+    L.favor_prefill_workspace_bytes.restype = ctypes.c_int
+    L.favor_prefill.argtypes = [i32] * 7 + [vp, vp, vp, fp, vp, vp, vp, vp, sz, vp]
+    L.favor_prefill.restype = ctypes.c_int
+    L.favor_decode.argtypes = [i32] * 6 + [vp, vp, vp, fp, vp, vp, vp]
+    L.favor_decode.restype = ctypes.c_int
     L.favor_feature_map.argtypes = [i32] * 6 + [vp, fp, vp, vp]
     L.favor_feature_map.restype = ctypes.c_int
     L.favor_feature_map_attn.argtypes = [i32] * 7 + [vp, fp, vp, vp]
@@ -187,6 +198,82 @@ def bwd(q, k, v, W, do, causal=False, kernel="softmax", out=None, workspace=None
                             out[1].data_ptr(), out[2].data_ptr(), workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(q, stream))
     _check(st, "favor_bwd_attn")
+    return out
+
+
+def state_bytes(B, H, d, m) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib.favor_state_bytes(B, H, d, m, ctypes.byref(out)), "favor_state_bytes")
+    return out.value
+
+
+def state_reset(state, stream=None):
+    """Empty the causal states in `state` (fp32 [B, H, m, d+4]) on the GPU."""
+    if state.dim() != 4 or state.dtype != torch.float32 or not state.is_contiguous():
+        raise ValueError("state must be a contiguous fp32 [B, H, m, d+4] tensor")
+    B, H, m, d4 = state.shape
+    _check(lib.favor_state_reset(B, H, d4 - 4, m, state.data_ptr(), _stream(state, stream)),
+           "favor_state_reset")
+    return state
+
+
+def state_new(B, H, d, m, device="cuda"):
+    """A new empty causal state for B*H heads: fp32 [B, H, m, d+4] rows [S~ | z~ | c]."""
+    st = torch.empty((B, H, m, d + 4), dtype=torch.float32, device=device)
+    return state_reset(st)
+
+
+def _check_state(st, B, H, d, m, what):
+    if st is not None and (st.shape != (B, H, m, d + 4) or st.dtype != torch.float32
+                           or not st.is_contiguous() or not st.is_cuda):
+        raise ValueError(f"{what} must be a contiguous fp32 GPU tensor [B, H, m, d+4]")
+
+
+def prefill_workspace_bytes(B, H, L, d, m, dtype=BF16) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.favor_prefill_workspace_bytes(B, H, L, d, m, dtype, ctypes.byref(n)),
+           "favor_prefill_workspace_bytes")
+    return n.value
+
+
+def prefill(q, k, v, W, state_in=None, state_out=None, kernel="softmax", out=None,
+            workspace=None, stream=None):
+    """Causal forward over new tokens continuing state_in (None: empty) (favor_prefill).
+
+    Returns (O, state_out); state_out is allocated when not given."""
+    ak = _kernel(kernel)
+    B, H, L, d, m, dt = _shape_of(q, k, v, W)
+    _check_state(state_in, B, H, d, m, "state_in")
+    if state_out is None:
+        state_out = torch.empty((B, H, m, d + 4), dtype=torch.float32, device=q.device)
+    _check_state(state_out, B, H, d, m, "state_out")
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        need = prefill_workspace_bytes(B, H, L, d, m, dt)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    st = lib.favor_prefill(B, H, L, d, m, dt, ak, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           W.data_ptr(), out.data_ptr(),
+                           None if state_in is None else state_in.data_ptr(),
+                           state_out.data_ptr(), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), _stream(q, stream))
+    _check(st, "favor_prefill")
+    return out, state_out
+
+
+def decode(q, k, v, W, state, kernel="softmax", out=None, stream=None):
+    """One decoding step (favor_decode): q, k, v [B, H, d] (one new token per head);
+    `state` is updated in place; returns o [B, H, d]."""
+    ak = _kernel(kernel)
+    if q.dim() != 3:
+        raise ValueError("q, k, v must be [B, H, d]")
+    B, H, L, d, m, dt = _shape_of(q[:, :, None], k[:, :, None], v[:, :, None], W)
+    _check_state(state, B, H, d, m, "state")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib.favor_decode(B, H, d, m, dt, ak, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            W.data_ptr(), out.data_ptr(), state.data_ptr(), _stream(q, stream)),
+           "favor_decode")
     return out
 
 

@@ -97,9 +97,29 @@ int backward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtyp
   return FAVOR_OK;
 }
 
+// Prefill segments: 64 tokens (the masked in-segment term of the generic
+// causal kernels costs O(segment) per token).
+constexpr int32_t kPrefillSeg = 64;
+
+// Incremental causal state: shape checks shared by its entry points.
+int check_state(int32_t B, int32_t H, int32_t d, int32_t m, int32_t attn_kernel) {
+  const int st = check_shape(B, H, 1, d, m, FAVOR_F32);
+  if (st != FAVOR_OK) return st;
+  return norm_coefficient(attn_kernel) < 0.f ? FAVOR_ERR_UNSUPPORTED : FAVOR_OK;
+}
+
 }  // namespace
 
 void make_generic_plan(Plan* p);
+
+void make_generic_only_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                            int32_t causal, int32_t seg, Plan* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
+  p->BH = B * H;
+  p->seg = seg;
+  make_generic_plan(p);
+}
 
 int record_hip_error(hipError_t e) {
   g_last_hip_error = static_cast<int>(e);
@@ -182,13 +202,9 @@ void make_generic_plan(Plan* p) {
 
 void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                    int32_t causal, Plan* p, BwdPlan* b) {
-  std::memset(p, 0, sizeof(*p));
-  p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
-  p->BH = B * H;
   // Causal: 64-token segments (the masked in-segment terms of the backward
   // cost O(segment) per token; the forward's 256 would quadruple them).
-  p->seg = causal ? 64 : 0;
-  make_generic_plan(p);
+  make_generic_only_plan(B, H, L, d, m, dtype, causal, causal ? 64 : 0, p);
   const size_t ncol = static_cast<size_t>(d) + 1;
   const size_t BH = static_cast<size_t>(p->BH);
   size_t off = p->bytes;
@@ -267,6 +283,78 @@ int favor_bwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
                    void* workspace, size_t workspace_bytes, void* stream) {
   return favor::backward(B, H, L, d, m, dtype, causal ? 1 : 0, attn_kernel, Q, K, V, W, dO, dQ,
                          dK, dV, workspace, workspace_bytes, stream);
+}
+
+int favor_state_bytes(int32_t B, int32_t H, int32_t d, int32_t m, size_t* bytes) {
+  const int st = favor::check_state(B, H, d, m, FAVOR_SOFTMAX);
+  if (st != FAVOR_OK) return st;
+  if (!bytes) return FAVOR_ERR_NULL;
+  *bytes = static_cast<size_t>(B) * H * m * (d + 4) * sizeof(float);
+  return FAVOR_OK;
+}
+
+int favor_state_reset(int32_t B, int32_t H, int32_t d, int32_t m, float* state, void* stream) {
+  const int st = favor::check_state(B, H, d, m, FAVOR_SOFTMAX);
+  if (st != FAVOR_OK) return st;
+  if (!state) return FAVOR_ERR_NULL;
+  if (!favor::is_aligned(state, 16)) return FAVOR_ERR_ALIGN;
+  const hipError_t e = favor::generic_state_reset(B * H, d, m, state,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return favor::fail_hip(e);
+  return FAVOR_OK;
+}
+
+int favor_prefill_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
+                                  int32_t dtype, size_t* bytes) {
+  const int st = favor::check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  if (!bytes) return FAVOR_ERR_NULL;
+  favor::Plan p;
+  favor::make_generic_only_plan(B, H, L, d, m, dtype, 1, favor::kPrefillSeg, &p);
+  *bytes = p.bytes;
+  return FAVOR_OK;
+}
+
+int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                  int32_t attn_kernel, const void* Q, const void* K, const void* V,
+                  const float* W, void* O, const float* state_in, float* state_out,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = favor::check_shape(B, H, L, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  const float knorm = favor::norm_coefficient(attn_kernel);
+  if (knorm < 0.f) return FAVOR_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !W || !O || !workspace) return FAVOR_ERR_NULL;
+  for (const void* x : {Q, K, V, static_cast<const void*>(W), static_cast<const void*>(O),
+                        static_cast<const void*>(state_in), static_cast<const void*>(state_out)})
+    if (x && !favor::is_aligned(x, 16)) return FAVOR_ERR_ALIGN;
+  if (!favor::is_aligned(workspace, 256)) return FAVOR_ERR_ALIGN;
+  favor::Plan p;
+  favor::make_generic_only_plan(B, H, L, d, m, dtype, 1, favor::kPrefillSeg, &p);
+  if (workspace_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
+  p.knorm = knorm;
+  p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
+  const hipError_t e = favor::generic_prefill(p, Q, K, V, W, O, state_in, state_out, workspace,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return favor::fail_hip(e);
+  return FAVOR_OK;
+}
+
+int favor_decode(int32_t B, int32_t H, int32_t d, int32_t m, int32_t dtype, int32_t attn_kernel,
+                 const void* q, const void* k, const void* v, const float* W, void* o,
+                 float* state, void* stream) {
+  int st = favor::check_shape(B, H, 1, d, m, dtype);
+  if (st != FAVOR_OK) return st;
+  const float knorm = favor::norm_coefficient(attn_kernel);
+  if (knorm < 0.f) return FAVOR_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !W || !o || !state) return FAVOR_ERR_NULL;
+  for (const void* x : {q, k, v, static_cast<const void*>(W), static_cast<const void*>(o),
+                        static_cast<const void*>(state)})
+    if (!favor::is_aligned(x, 16)) return FAVOR_ERR_ALIGN;
+  const hipError_t e = favor::generic_decode(B * H, d, m, dtype, knorm,
+                                             attn_kernel == FAVOR_RELU ? 1 : 0, q, k, v, W, o,
+                                             state, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return favor::fail_hip(e);
+  return FAVOR_OK;
 }
 
 int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,

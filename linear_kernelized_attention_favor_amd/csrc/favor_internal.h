@@ -67,12 +67,28 @@ struct BwdPlan {
   size_t off_U, off_M, off_G, off_Gfin;
   size_t bytes;
 };
+// A generic-path plan whatever the shape (seg <= 0: the default segment length).
+void make_generic_only_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                            int32_t causal, int32_t seg, Plan* p);
 void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                    int32_t causal, Plan* p, BwdPlan* b);
 
 // Generic path: enqueue the whole forward pass on `stream`.
 hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const void* V,
                            const float* W, void* O, void* ws, hipStream_t stream);
+// Causal forward on the generic kernels carrying a state across calls:
+// st_in (nullable) is the state before token 0, st_out (nullable) receives
+// the state after token L-1; both fp32 [BH][m][d+4] rows [S~ | z~ | c | 0 | 0].
+hipError_t generic_prefill(const Plan& p, const void* Q, const void* K, const void* V,
+                           const float* W, void* O, const float* st_in, float* st_out, void* ws,
+                           hipStream_t stream);
+// Empty states (S~ = z~ = 0, c = -inf) for BH heads.
+hipError_t generic_state_reset(int32_t BH, int32_t d, int32_t m, float* state,
+                               hipStream_t stream);
+// One decode step per head (q, k, v, o: [BH][d]); the state is updated in place.
+hipError_t generic_decode(int32_t BH, int32_t d, int32_t m, int32_t dtype, float knorm,
+                          int32_t relu, const void* q, const void* k, const void* v,
+                          const float* W, void* o, float* state, hipStream_t stream);
 // Its first two steps alone: the key state and references in the workspace.
 hipError_t generic_key_state(const Plan& p, const void* K, const void* V, const float* W,
                              void* ws, hipStream_t stream);

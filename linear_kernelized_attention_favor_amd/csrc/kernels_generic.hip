@@ -23,6 +23,7 @@
 // are bitwise reproducible.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -131,7 +132,9 @@ __global__ __launch_bounds__(kThreads) void g_combine(float* __restrict__ Tst,
                                                       float* __restrict__ cP,
                                                       float* __restrict__ KV,
                                                       float* __restrict__ cfin, int nseg, int m,
-                                                      int d, int causal) {
+                                                      int d, int causal,
+                                                      const float* __restrict__ st_in,
+                                                      float* __restrict__ st_out) {
   const int bh = blockIdx.y;
   const int ncol = d + 1;
   const int e = blockIdx.x * kThreads + threadIdx.x;
@@ -149,7 +152,14 @@ __global__ __launch_bounds__(kThreads) void g_combine(float* __restrict__ Tst,
     KV[(static_cast<size_t>(bh) * m + r) * ncol + c] = acc;
     if (c == 0) cfin[static_cast<size_t>(bh) * m + r] = cm;
   } else {
+    // (st_in: a carried state [S~ | z~ | c] per head and feature row, the
+    // prefix before the first segment; st_out: the total after the last)
+    const size_t sr = (static_cast<size_t>(bh) * m + r) * (d + 4);
     float rc = -INFINITY, run = 0.f;
+    if (st_in) {
+      run = st_in[sr + c];
+      rc = st_in[sr + d + 1];
+    }
     for (int s = 0; s < nseg; ++s) {
       const size_t ti = tb + static_cast<size_t>(s) * m * ncol;
       const float ts = Tst[ti];
@@ -159,6 +169,14 @@ __global__ __launch_bounds__(kThreads) void g_combine(float* __restrict__ Tst,
       const float nc = fmaxf(rc, cs);
       run = run * expf(rc - nc) + ts * expf(cs - nc);
       rc = nc;
+    }
+    if (st_out) {
+      st_out[sr + c] = run;
+      if (c == 0) {
+        st_out[sr + d + 1] = rc;
+        st_out[sr + d + 2] = 0.f;
+        st_out[sr + d + 3] = 0.f;
+      }
     }
   }
 }
@@ -352,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void g_feature_map(const T* __restrict__ 
 // exclusive prefixes in T with references cP, and the segment references).
 template <typename T>
 hipError_t key_state_t(const Plan& p, const T* K, const T* V, const float* W, char* ws,
-                       hipStream_t st) {
+                       hipStream_t st, const float* st_in = nullptr, float* st_out = nullptr) {
   float* Tst = reinterpret_cast<float*>(ws + p.off_T);
   float* cseg = reinterpret_cast<float*>(ws + p.off_cseg);
   float* cP = reinterpret_cast<float*>(ws + p.off_cP);
@@ -367,7 +385,7 @@ hipError_t key_state_t(const Plan& p, const T* K, const T* V, const float* W, ch
   const int nent = p.m * (p.d + 1);
   timing_before(st);
   g_combine<<<dim3((nent + kThreads - 1) / kThreads, p.BH), kThreads, 0, st>>>(
-      Tst, cseg, cP, KV, cfin, p.nseg, p.m, p.d, p.causal);
+      Tst, cseg, cP, KV, cfin, p.nseg, p.m, p.d, p.causal, st_in, st_out);
   e = hipGetLastError();
   timing_after(st, "g_combine");
   return e;
@@ -375,8 +393,9 @@ hipError_t key_state_t(const Plan& p, const T* K, const T* V, const float* W, ch
 
 template <typename T>
 hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const float* W, T* O,
-                     char* ws, hipStream_t st) {
-  hipError_t e = key_state_t(p, K, V, W, ws, st);
+                     char* ws, hipStream_t st, const float* st_in = nullptr,
+                     float* st_out = nullptr) {
+  hipError_t e = key_state_t(p, K, V, W, ws, st, st_in, st_out);
   if (e != hipSuccess) return e;
   float* Tst = reinterpret_cast<float*>(ws + p.off_T);
   float* cseg = reinterpret_cast<float*>(ws + p.off_cseg);
@@ -396,7 +415,165 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
   return e;
 }
 
+// ---------------------------------------------------------------------------
+// Incremental causal state.  A head's state is fp32 [m][d+4]: row r holds
+// [S~_r | z~_r | c_r | 0 | 0] (16-byte rows) with the true state [S | z]_r = e^{c_r} [S~_r | z~_r]
+// (the features' 1/sqrt(m) left out, as everywhere on this path; ReLU: c_r is
+// 0 once a token has been added).  Empty: S~ = z~ = 0, c = -inf.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void g_state_reset(float* __restrict__ st, size_t rows,
+                                                          int d) {
+  const int sw = d + 4;
+  const size_t n = rows * sw;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * kThreads)
+    st[i] = (static_cast<int>(i % sw) == d + 1) ? -INFINITY : 0.f;
+}
+
+// One token per head: add (k, v) to the state (the reference of each feature
+// raised to cover the new key), then o = q~ [S | z] -> num / den with the
+// query's own row reference.  grid (BH), one work-group per head; the state
+// rows move as float4 quads, a quad column per thread and the rows split
+// over groups of threads.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void g_decode(const T* __restrict__ q,
+                                                     const T* __restrict__ k,
+                                                     const T* __restrict__ v,
+                                                     const float* __restrict__ W,
+                                                     T* __restrict__ o, float* __restrict__ st,
+                                                     int d, int m, float knorm, int relu) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  const int sw = d + 4, nq = sw / 4;
+  const int ng = kThreads / nq;                  // row groups
+  __shared__ float xq[kMaxD], xk[kMaxD], xv[kMaxD + 4];
+  __shared__ float kt[kMaxM], sc[kMaxM], qt[kMaxM];
+  __shared__ float part[kThreads / 5][kMaxD + 4];  // (nq >= 5)
+  __shared__ float wred[kThreads / 64];
+  __shared__ float nk;
+  const size_t base = static_cast<size_t>(bh) * d;
+  for (int a = t; a < d; a += kThreads) {
+    xq[a] = load_x(q, base + a);
+    xk[a] = load_x(k, base + a);
+    xv[a] = load_x(v, base + a);
+  }
+  if (t < 4) xv[d + t] = (t == 0) ? 1.f : 0.f;
+  __syncthreads();
+  if (t < 64) {
+    float acc = 0.f;
+    for (int a = t; a < d; a += 64) acc = fmaf(xk[a], xk[a], acc);
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (t == 0) nk = knorm * acc;
+  }
+  __syncthreads();
+  float* S = st + static_cast<size_t>(bh) * m * sw;
+  float mx = -INFINITY;
+  for (int r = t; r < m; r += kThreads) {
+    const float* w = W + static_cast<size_t>(r) * d;
+    const float e = dot_w(w, xk, d) - nk;
+    const float c = S[static_cast<size_t>(r) * sw + d + 1];
+    float cn;
+    if (relu) {
+      cn = 0.f;
+      sc[r] = 1.f;
+      kt[r] = fmaxf(e, 0.f);
+    } else {
+      cn = fmaxf(c, e);
+      sc[r] = expf(c - cn);     // 0 for an empty row (c = -inf)
+      kt[r] = expf(e - cn);
+    }
+    S[static_cast<size_t>(r) * sw + d + 1] = cn;
+    const float s = dot_w(w, xq, d);
+    qt[r] = relu ? fmaxf(s, 0.f) : s + cn;
+    mx = fmaxf(mx, qt[r]);
+  }
+  // row reference of the query (ReLU: none)
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((t & 63) == 0) wred[t >> 6] = mx;
+  __syncthreads();
+  if (!relu) {
+    float M = wred[0];
+    for (int i = 1; i < kThreads / 64; ++i) M = fmaxf(M, wred[i]);
+    for (int r = t; r < m; r += kThreads) qt[r] = expf(qt[r] - M);
+  }
+  __syncthreads();
+  // State update and the query's contraction: thread (quad j, group g) owns
+  // columns 4j..4j+3 of rows g, g+ng, ...  Columns above d (the reference
+  // and the padding) pass through unchanged.
+  const int j = t % nq, g = t / nq;
+  if (g < ng) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    const int c0 = 4 * j;
+    const float v0 = xv[c0], v1 = xv[c0 + 1], v2 = xv[c0 + 2], v3 = xv[c0 + 3];
+    const bool up1 = c0 + 1 <= d, up2 = c0 + 2 <= d, up3 = c0 + 3 <= d;
+    float4* S4 = reinterpret_cast<float4*>(S);
+    for (int r = g; r < m; r += ng) {
+      float4 x = S4[static_cast<size_t>(r) * nq + j];
+      const float a = sc[r], b = kt[r], qr = qt[r];
+      x.x = fmaf(x.x, a, b * v0);
+      if (up1) x.y = fmaf(x.y, a, b * v1);
+      if (up2) x.z = fmaf(x.z, a, b * v2);
+      if (up3) x.w = fmaf(x.w, a, b * v3);
+      S4[static_cast<size_t>(r) * nq + j] = x;
+      acc.x = fmaf(qr, x.x, acc.x);
+      acc.y = fmaf(qr, x.y, acc.y);
+      acc.z = fmaf(qr, x.z, acc.z);
+      acc.w = fmaf(qr, x.w, acc.w);
+    }
+    part[g][c0] = acc.x;
+    part[g][c0 + 1] = acc.y;
+    part[g][c0 + 2] = acc.z;
+    part[g][c0 + 3] = acc.w;
+  }
+  __syncthreads();
+  if (t <= d) {
+    float a = 0.f;
+    for (int i = 0; i < ng; ++i) a += part[i][t];
+    xv[t] = a;     // (xv no longer needed: reused for [num | den])
+  }
+  __syncthreads();
+  for (int c = t; c < d; c += kThreads) store_x(o, base + c, xv[c] / xv[d]);
+}
+
 }  // namespace
+
+hipError_t generic_state_reset(int32_t BH, int32_t d, int32_t m, float* state,
+                               hipStream_t stream) {
+  const size_t rows = static_cast<size_t>(BH) * m;
+  const size_t n = rows * (d + 4);
+  const int blocks = static_cast<int>(std::min<size_t>((n + kThreads - 1) / kThreads, 4096));
+  g_state_reset<<<blocks, kThreads, 0, stream>>>(state, rows, d);
+  return hipGetLastError();
+}
+
+hipError_t generic_decode(int32_t BH, int32_t d, int32_t m, int32_t dtype, float knorm,
+                          int32_t relu, const void* q, const void* k, const void* v,
+                          const float* W, void* o, float* state, hipStream_t stream) {
+  timing_before(stream);
+  if (dtype == FAVOR_F32)
+    g_decode<float><<<BH, kThreads, 0, stream>>>(
+        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+        W, static_cast<float*>(o), state, d, m, knorm, relu);
+  else
+    g_decode<uint16_t><<<BH, kThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+        static_cast<const uint16_t*>(v), W, static_cast<uint16_t*>(o), state, d, m, knorm, relu);
+  const hipError_t e = hipGetLastError();
+  timing_after(stream, "g_decode");
+  return e;
+}
+
+hipError_t generic_prefill(const Plan& p, const void* Q, const void* K, const void* V,
+                           const float* W, void* O, const float* st_in, float* st_out, void* ws,
+                           hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  if (p.dtype == FAVOR_F32)
+    return forward_t<float>(p, static_cast<const float*>(Q), static_cast<const float*>(K),
+                            static_cast<const float*>(V), W, static_cast<float*>(O), w, stream,
+                            st_in, st_out);
+  return forward_t<uint16_t>(p, static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                             static_cast<const uint16_t*>(V), W, static_cast<uint16_t*>(O), w,
+                             stream, st_in, st_out);
+}
 
 hipError_t generic_forward(const Plan& p, const void* Q, const void* K, const void* V,
                            const float* W, void* O, void* ws, hipStream_t stream) {

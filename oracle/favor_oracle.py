@@ -83,6 +83,7 @@ __all__ = [
     "bidir",
     "causal",
     "brute",
+    "causal_state",
     "phi_vjp",
     "attend_bidir_vjp",
     "attend_causal_vjp",
@@ -292,6 +293,17 @@ def causal(Q, K, V, W, kernel: str = "softmax") -> np.ndarray:
     """Masked (causal) FAVOR+ forward in prefix-sum form, fp64."""
     f = _features(kernel)
     return attend_causal(f(Q, W), f(K, W), np.asarray(V, dtype=np.float64))
+
+
+def causal_state(K, V, W, kernel: str = "softmax"):
+    """The masked form's running sums after every given token, fp64.
+
+    S = sum_j phi(k_j) v_j^T ([..., m, dv]) and z = sum_j phi(k_j) ([..., m]):
+    the state from which the next token's output q'^T S / q'^T z follows.
+    """
+    Kp = _features(kernel)(K, W)
+    V = np.asarray(V, dtype=np.float64)
+    return np.swapaxes(Kp, -1, -2) @ V, np.sum(Kp, axis=-2)
 
 
 def brute(Q, K, V, W, is_causal: bool, kernel: str = "softmax") -> np.ndarray:

@@ -1,0 +1,179 @@
+"""GPU parity of the incremental causal state: favor_prefill, favor_decode and
+favor_state_reset (through the C ABI) against the fp64 oracle's causal form
+and its running state (oracle.causal_state).
+
+Outputs: per-row relative error as in the forward's parity tests (1e-4 for
+fp32 inputs, 2e-2 for bf16).  States: the true state exp(c) [S~ | z~] / sqrt(m)
+against the oracle's (S, z) per head, max abs error over the largest entry,
+1e-4 for both dtypes (the state is fp32 arithmetic on the same input values).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def fv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_kernelized_attention_favor_amd as m
+    return m
+
+
+def _np64(t):
+    return t.detach().cpu().double().numpy()
+
+
+def _case(shape, dtype, seed):
+    B, H, L, d, m = shape
+    rng = np.random.default_rng(seed)
+    s = d ** -0.25
+    q, k, v = (rng.standard_normal((B, H, L, d), dtype=np.float32) for _ in range(3))
+    q *= np.float32(s)
+    k *= np.float32(s)
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    W = oracle.draw_w(seed + 5, m, d).astype(np.float32)
+    return tuple(torch.from_numpy(x).to(td) for x in (q, k, v)) + (W,)
+
+
+def _true_state(st):
+    # rows [S~ (d) | z~ | c | 0 | 0]
+    st = _np64(st)
+    m, d = st.shape[-2], st.shape[-1] - 4
+    assert np.all(st[..., d + 2:] == 0)
+    scale = np.exp(st[..., d + 1]) / math.sqrt(m)          # [B, H, m]
+    return st[..., :d] * scale[..., None], st[..., d] * scale
+
+
+def _state_err(st, K, V, W, kernel):
+    S, z = _true_state(st)
+    Sr, zr = oracle.causal_state(_np64(K), _np64(V), W.astype(np.float64), kernel)
+    got = np.concatenate([S, z[..., None]], -1)
+    ref = np.concatenate([Sr, zr[..., None]], -1)
+    return float(np.max(np.abs(got - ref).max(axis=(-1, -2)) / np.abs(ref).max(axis=(-1, -2))))
+
+
+def _ref_out(q, k, v, W, kernel):
+    return oracle.causal(_np64(q), _np64(k), _np64(v), W.astype(np.float64), kernel)
+
+
+SHAPES = [(1, 2, 300, 64, 256), (2, 1, 77, 32, 48), (1, 1, 600, 128, 1024), (1, 3, 1, 16, 64)]
+KERNELS = ["softmax", "gaussian", "relu"]
+
+
+def _m(shape, kernel):
+    # (ReLU: enough features that no first row has an all-zero normaliser)
+    return shape if kernel != "relu" or shape[4] >= 64 else shape[:4] + (64,)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_output_and_state(fv, shape, dtype, kernel):
+    shape = _m(shape, kernel)
+    q, k, v, W = _case(shape, dtype, sum(shape) + 11)
+    Wd = torch.from_numpy(W).cuda()
+    o, st = fv.prefill(q.cuda(), k.cuda(), v.cuda(), Wd, kernel=kernel)
+    torch.cuda.synchronize()
+    assert oracle.row_rel_err(_np64(o), _ref_out(q, k, v, W, kernel)) <= TOL[dtype]
+    assert _state_err(st, k, v, W, kernel) <= 1e-4
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chunked_prefill_continues_the_state(fv, dtype, kernel):
+    shape = (2, 2, 700, 64, 128)
+    q, k, v, W = _case(shape, dtype, 23)
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    cut = 333
+    o1, st1 = fv.prefill(qc[:, :, :cut].contiguous(), kc[:, :, :cut].contiguous(),
+                         vc[:, :, :cut].contiguous(), Wd, kernel=kernel)
+    o2, st2 = fv.prefill(qc[:, :, cut:].contiguous(), kc[:, :, cut:].contiguous(),
+                         vc[:, :, cut:].contiguous(), Wd, state_in=st1, kernel=kernel)
+    torch.cuda.synchronize()
+    ref = _ref_out(q, k, v, W, kernel)
+    assert oracle.row_rel_err(_np64(o1), ref[:, :, :cut]) <= TOL[dtype]
+    assert oracle.row_rel_err(_np64(o2), ref[:, :, cut:]) <= TOL[dtype]
+    assert _state_err(st1, k[:, :, :cut], v[:, :, :cut], W, kernel) <= 1e-4
+    assert _state_err(st2, k, v, W, kernel) <= 1e-4
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_continues_prefill(fv, dtype, kernel):
+    shape = (2, 3, 260, 64, 256)
+    q, k, v, W = _case(shape, dtype, 29)
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    L0 = 240
+    _, st = fv.prefill(qc[:, :, :L0].contiguous(), kc[:, :, :L0].contiguous(),
+                       vc[:, :, :L0].contiguous(), Wd, kernel=kernel)
+    outs = []
+    for t in range(L0, shape[2]):
+        outs.append(fv.decode(qc[:, :, t].contiguous(), kc[:, :, t].contiguous(),
+                              vc[:, :, t].contiguous(), Wd, st, kernel=kernel))
+    torch.cuda.synchronize()
+    got = torch.stack(outs, 2)
+    ref = _ref_out(q, k, v, W, kernel)[:, :, L0:]
+    assert oracle.row_rel_err(_np64(got), ref) <= TOL[dtype]
+    assert _state_err(st, k, v, W, kernel) <= 1e-4
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_from_an_empty_state(fv, kernel):
+    shape = (1, 2, 40, 32, 64)
+    q, k, v, W = _case(shape, "f32", 31)
+    Wd = torch.from_numpy(W).cuda()
+    st = fv.state_new(1, 2, 32, 64)
+    got = torch.stack([fv.decode(q[:, :, t].contiguous().cuda(), k[:, :, t].contiguous().cuda(),
+                                 v[:, :, t].contiguous().cuda(), Wd, st, kernel=kernel)
+                       for t in range(shape[2])], 2)
+    torch.cuda.synchronize()
+    assert oracle.row_rel_err(_np64(got), _ref_out(q, k, v, W, kernel)) <= TOL["f32"]
+    # the same stream through the prefill path, after a reset of the state
+    fv.state_reset(st)
+    o, st2 = fv.prefill(q.cuda(), k.cuda(), v.cuda(), Wd, kernel=kernel)
+    torch.cuda.synchronize()
+    assert oracle.row_rel_err(_np64(o), _np64(got)) <= TOL["f32"]
+
+
+def test_state_reset_layout(fv):
+    st = torch.full((2, 3, 48, 20), 7.0, device="cuda")     # d = 16
+    fv.state_reset(st)
+    torch.cuda.synchronize()
+    s = st.cpu()
+    assert torch.all(s[..., :17] == 0) and torch.all(s[..., 17] == -math.inf)
+    assert torch.all(s[..., 18:] == 0)
+    assert fv.state_bytes(2, 3, 16, 48) == st.numel() * 4
+
+
+def test_decode_large_offsets_stay_finite(fv):
+    # keys whose exponents grow along the stream: the per-feature references
+    # follow them, so the state stays finite and the outputs match the oracle
+    B, H, L, d, m = 1, 1, 64, 32, 64
+    rng = np.random.default_rng(37)
+    mu = rng.standard_normal(d).astype(np.float32)
+    ramp = np.linspace(0, 6, L, dtype=np.float32)[:, None]
+    k = (rng.standard_normal((B, H, L, d)).astype(np.float32) * 0.3 + ramp * mu / np.linalg.norm(mu))
+    q = rng.standard_normal((B, H, L, d)).astype(np.float32) * 0.3
+    v = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    W = oracle.draw_w(38, m, d).astype(np.float32)
+    Wd = torch.from_numpy(W).cuda()
+    st = fv.state_new(B, H, d, m)
+    qt, kt, vt = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    got = torch.stack([fv.decode(qt[:, :, t].contiguous(), kt[:, :, t].contiguous(),
+                                 vt[:, :, t].contiguous(), Wd, st) for t in range(L)], 2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(st).all()
+    ref = oracle.causal(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
+                        W.astype(np.float64))
+    assert oracle.row_rel_err(_np64(got), ref) <= TOL["f32"]

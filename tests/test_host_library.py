@@ -150,6 +150,47 @@ def test_bwd_rejects_unknown_kernels_and_sizes_its_workspace():
         fv.bwd_workspace_bytes(1, 1, 1, 24, 16)
 
 
+def test_state_entry_validation():
+    sb = ctypes.c_size_t(0)
+    assert lib.favor_state_bytes(2, 3, 64, 256, ctypes.byref(sb)) == 0
+    assert sb.value == 2 * 3 * 256 * 68 * 4
+    assert lib.favor_state_bytes(0, 3, 64, 256, ctypes.byref(sb)) == ESHAPE
+    assert lib.favor_state_bytes(1, 1, 48, 256, ctypes.byref(sb)) == EUNSUP
+    assert lib.favor_state_bytes(1, 1, 64, 256, None) == ENULL
+    assert lib.favor_state_reset(1, 1, 64, 64, None, None) == ENULL
+    assert lib.favor_state_reset(1, 1, 64, 64, MIS, None) == EALIGN
+    assert lib.favor_prefill_workspace_bytes(1, 1, 16, 64, 64, 1, ctypes.byref(sb)) == 0
+    need = sb.value
+
+    def pre(**kw):
+        a = dict(B=1, H=1, L=16, d=64, m=64, dtype=1, attn=0, Q=A, K=A, V=A, W=A, O=A, si=None,
+                 so=A, ws=A, wsb=1 << 40)
+        a.update(kw)
+        return lib.favor_prefill(a["B"], a["H"], a["L"], a["d"], a["m"], a["dtype"], a["attn"],
+                                 a["Q"], a["K"], a["V"], a["W"], a["O"], a["si"], a["so"], a["ws"],
+                                 a["wsb"], None)
+    assert pre(L=0) == ESHAPE
+    assert pre(d=24) == EUNSUP
+    assert pre(attn=3) == EUNSUP
+    assert pre(Q=None) == ENULL
+    assert pre(ws=None) == ENULL
+    assert pre(si=MIS) == EALIGN
+    assert pre(so=MIS) == EALIGN
+    assert pre(wsb=need - 1) == EWS
+
+    def dec(**kw):
+        a = dict(B=1, H=1, d=64, m=64, dtype=1, attn=0, q=A, k=A, v=A, W=A, o=A, st=A)
+        a.update(kw)
+        return lib.favor_decode(a["B"], a["H"], a["d"], a["m"], a["dtype"], a["attn"], a["q"],
+                                a["k"], a["v"], a["W"], a["o"], a["st"], None)
+    assert dec(H=0) == ESHAPE
+    assert dec(m=20) == EUNSUP
+    assert dec(attn=-1) == EUNSUP
+    assert dec(st=None) == ENULL
+    assert dec(o=MIS) == EALIGN
+    assert lib.favor_last_hip_error() == 0
+
+
 def test_feature_map_validation():
     f = lib.favor_feature_map
     assert f(1, 1, 0, 64, 64, 1, A, A, A, None) == ESHAPE

@@ -691,3 +691,30 @@ def test_B4_single_feature_has_no_query_gradient(causal):
     dK_ref = (dkp * k)[:, None] * (W[0][None, :] - K[0, 0])
     np.testing.assert_allclose(dV[0, 0], dV_ref, rtol=1e-12)
     np.testing.assert_allclose(dK[0, 0], dK_ref, rtol=1e-10, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# The masked form's running state (S, z) after a prefix: S1-S2 pin
+# causal_state.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("kernel", ["softmax", "gaussian", "relu"])
+def test_S1_state_gives_the_last_causal_row(kernel):
+    # the output of the last token is q'^T S / q'^T z with the state over
+    # every token up to it (the prefix-sum form, computed independently)
+    Q, K, V, W = _inputs(1, 2, 30, 8, 64, 91)
+    S, z = oracle.causal_state(K, V, W, kernel)
+    qp = {"softmax": oracle.phi, "gaussian": oracle.phi_gaussian, "relu": oracle.phi_relu}[kernel](
+        Q[..., -1, :], W)
+    last = np.einsum("...m,...md->...d", qp, S) / np.einsum("...m,...m->...", qp, z)[..., None]
+    np.testing.assert_allclose(last, oracle.causal(Q, K, V, W, kernel)[..., -1, :], rtol=1e-12)
+
+
+def test_S2_state_is_additive_and_z_is_the_ones_column():
+    Q, K, V, W = _inputs(2, 1, 25, 8, 32, 92)
+    S, z = oracle.causal_state(K, V, W)
+    S1, z1 = oracle.causal_state(K[..., :11, :], V[..., :11, :], W)
+    S2, z2 = oracle.causal_state(K[..., 11:, :], V[..., 11:, :], W)
+    np.testing.assert_allclose(S, S1 + S2, rtol=1e-13)
+    np.testing.assert_allclose(z, z1 + z2, rtol=1e-13)
+    Sones, _ = oracle.causal_state(K, np.ones_like(V), W)
+    np.testing.assert_allclose(Sones, np.broadcast_to(z[..., None], Sones.shape), rtol=1e-13)
