@@ -577,11 +577,65 @@ def main():
             torch.cuda.synchronize()
             nxt.result()
         ms_o = o0_.elapsed_time(o1_) / args.steps
+        # On the device: favor_draw_projection_device enqueued on the stream
+        # before every k-th call (no host work, no copy).
+        torch.cuda.synchronize()
+        d0_ = torch.cuda.Event(enable_timing=True)
+        d1_ = torch.cuda.Event(enable_timing=True)
+        d0_.record(stream)
+        for i in range(args.steps):
+            if i % w.redraw_every == 0:
+                fv.draw_projection_device(w.seed_w + i // w.redraw_every, w.m, w.d, out=Wn,
+                                          stream=stream)
+            q, k, v, o = sets[i % nsets]
+            fwd(q, k, v, Wn, out=o, workspace=ws, stream=stream)
+        d1_.record(stream)
+        torch.cuda.synchronize()
+        ms_d = d0_.elapsed_time(d1_) / args.steps
+        # On the device, overlapped: the next window's W drawn on a second
+        # stream (default priority) into the other of two buffers while the
+        # current window's calls run; the main stream waits for that draw
+        # only at the window switch.
+        side = torch.cuda.Stream(dev)
+        ready = [torch.cuda.Event(), torch.cuda.Event()]
+        used = [torch.cuda.Event(), torch.cuda.Event()]
+        fv.draw_projection_device(seed_of(0), w.m, w.d, out=Wd[0], stream=stream)
+        torch.cuda.synchronize()
+        d0_.record(stream)
+        for i in range(args.steps):
+            win = i // w.redraw_every
+            if i % w.redraw_every == 0:
+                if win > 0:
+                    stream.wait_event(ready[win % 2])
+                nxt_slot = (win + 1) % 2
+                if win > 0:
+                    used[nxt_slot].record(stream)      # the last call that read that buffer
+                side.wait_event(used[nxt_slot])
+                fv.draw_projection_device(seed_of(win + 1), w.m, w.d, out=Wd[nxt_slot],
+                                          stream=side)
+                ready[nxt_slot].record(side)
+            q, k, v, o = sets[i % nsets]
+            fwd(q, k, v, Wd[win % 2], out=o, workspace=ws, stream=stream)
+        d1_.record(stream)
+        torch.cuda.synchronize()
+        ms_do = d0_.elapsed_time(d1_) / args.steps
+        ndd = 50
+        d0_.record(stream)
+        for i in range(ndd):
+            fv.draw_projection_device(w.seed_w + i, w.m, w.d, out=Wn, stream=stream)
+        d1_.record(stream)
+        torch.cuda.synchronize()
+        draw_dev_ms = d0_.elapsed_time(d1_) / ndd
         redraw = {"every": w.redraw_every, "ms_per_step": round(ms_r, 5),
                   "overhead_ms_per_step": round(ms_r - ms, 5),
                   "host_draw_ms": round(1e3 * t_draw / ndraw, 3),
                   "overlapped_ms_per_step": round(ms_o, 5),
-                  "overlapped_overhead_ms_per_step": round(ms_o - ms, 5)}
+                  "overlapped_overhead_ms_per_step": round(ms_o - ms, 5),
+                  "device_draw_ms": round(draw_dev_ms, 4),
+                  "device_ms_per_step": round(ms_d, 5),
+                  "device_overhead_ms_per_step": round(ms_d - ms, 5),
+                  "device_overlapped_ms_per_step": round(ms_do, 5),
+                  "device_overlapped_overhead_ms_per_step": round(ms_do - ms, 5)}
 
     tokens = w.heads * w.L
     value = tokens / (ms * 1e-3)

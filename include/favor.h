@@ -264,6 +264,18 @@ int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m
  */
 int favor_draw_projection(uint64_t seed, int32_t m, int32_t d, float* W_host);
 
+/*
+ * favor_draw_projection on the GPU: the same distribution, random stream and
+ * stream order, written to W (fp32 [m, d], device memory, 16-byte aligned)
+ * on `stream` (one work-group per block of d rows; no host work, no copy),
+ * so that a redraw can be queued between forward calls.  The directions are
+ * made orthonormal in fp64 by classical Gram-Schmidt applied twice, the host
+ * by the one-at-a-time form: the two agree to fp64 rounding, and W to fp32
+ * rounding.  1 <= d <= 128 and 1 <= m.  Returns FAVOR_OK, FAVOR_ERR_NULL,
+ * FAVOR_ERR_SHAPE, FAVOR_ERR_ALIGN or FAVOR_ERR_HIP.
+ */
+int favor_draw_projection_device(uint64_t seed, int32_t m, int32_t d, float* W, void* stream);
+
 /* Static English text for a favor_status value (never NULL). */
 const char* favor_status_string(int status);
 

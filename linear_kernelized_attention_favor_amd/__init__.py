@@ -5,12 +5,14 @@ and causal, with their gradients, computed by hand-written HIP kernels in libfav
 include/favor.h).  This package is the thin Python binding over that library.
 """
 from ._binding import (BF16, F32, GAUSSIAN, LIB_PATH, RELU, SOFTMAX, FavorError,  # noqa: F401
-                       bwd, bwd_workspace_bytes, decode, draw_projection, feature_map,
+                       bwd, bwd_workspace_bytes, decode, draw_projection,
+                       draw_projection_device, feature_map,
                        fwd_bidir, fwd_causal, plan_describe, prefill, state_bytes, state_new,
                        state_reset,
                        status_string, timing_start, timing_stop, workspace_bytes)
 
 __all__ = ["fwd_bidir", "fwd_causal", "bwd", "bwd_workspace_bytes", "prefill", "decode",
+           "draw_projection_device",
            "state_bytes", "state_new", "state_reset", "feature_map", "draw_projection", "workspace_bytes",
            "status_string", "plan_describe", "timing_start", "timing_stop", "FavorError", "LIB_PATH", "F32",
            "BF16", "SOFTMAX", "GAUSSIAN", "RELU"]

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 __all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
-           "bwd", "bwd_workspace_bytes", "state_bytes", "state_new", "state_reset", "prefill", "prefill_workspace_bytes",
+           "bwd", "bwd_workspace_bytes", "draw_projection_device", "state_bytes", "state_new", "state_reset", "prefill", "prefill_workspace_bytes",
            "decode",
            "feature_map", "draw_projection", "status_string", "plan_describe", "timing_start", "timing_stop",
            "F32", "BF16", "SOFTMAX", "GAUSSIAN", "RELU"]
@@ -73,6 +73,8 @@ def _load():
     L.favor_feature_map_attn.restype = ctypes.c_int
     L.favor_draw_projection.argtypes = [ctypes.c_uint64, i32, i32, ctypes.c_void_p]
     L.favor_draw_projection.restype = ctypes.c_int
+    L.favor_draw_projection_device.argtypes = [ctypes.c_uint64, i32, i32, vp, vp]
+    L.favor_draw_projection_device.restype = ctypes.c_int
     L.favor_status_string.argtypes = [ctypes.c_int]
     L.favor_status_string.restype = ctypes.c_char_p
     L.favor_last_hip_error.argtypes = []
@@ -314,6 +316,20 @@ def draw_projection(seed: int, m: int, d: int) -> np.ndarray:
     _check(lib.favor_draw_projection(ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), m, d,
                                      W.ctypes.data_as(ctypes.c_void_p)), "favor_draw_projection")
     return W
+
+
+def draw_projection_device(seed: int, m: int, d: int, out=None, device="cuda", stream=None):
+    """On-device draw of W [m, d] (fp32 GPU tensor), favor_draw_projection_device: the
+    host draw's distribution and random stream, enqueued on the current stream."""
+    if out is None:
+        out = torch.empty((m, d), dtype=torch.float32, device=device)
+    elif out.shape != (m, d) or out.dtype != torch.float32 or not out.is_contiguous() \
+            or not out.is_cuda:
+        raise ValueError("out must be a contiguous fp32 GPU tensor [m, d]")
+    _check(lib.favor_draw_projection_device(ctypes.c_uint64(seed & 0xFFFFFFFFFFFFFFFF), m, d,
+                                            out.data_ptr(), _stream(out, stream)),
+           "favor_draw_projection_device")
+    return out
 
 
 def timing_start() -> None:

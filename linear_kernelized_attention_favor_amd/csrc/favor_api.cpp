@@ -357,6 +357,15 @@ int favor_decode(int32_t B, int32_t H, int32_t d, int32_t m, int32_t dtype, int3
   return FAVOR_OK;
 }
 
+int favor_draw_projection_device(uint64_t seed, int32_t m, int32_t d, float* W, void* stream) {
+  if (!W) return FAVOR_ERR_NULL;
+  if (m < 1 || d < 1 || d > 128) return FAVOR_ERR_SHAPE;
+  if (!favor::is_aligned(W, 16)) return FAVOR_ERR_ALIGN;
+  const hipError_t e = favor::device_draw(seed, m, d, W, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return favor::fail_hip(e);
+  return FAVOR_OK;
+}
+
 int favor_feature_map_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                            int32_t attn_kernel, const void* X, const float* W, float* Xp,
                            void* stream) {

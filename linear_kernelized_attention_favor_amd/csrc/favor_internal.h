@@ -123,6 +123,10 @@ void timing_after(hipStream_t st, const char* kernel);
 // Records a failed HIP call for favor_last_hip_error(); returns FAVOR_ERR_HIP.
 int record_hip_error(hipError_t e);
 
+// On-device draw of W [m, d] (fp32, device memory; 1 <= d <= 128), the host
+// draw's distribution and random stream.
+hipError_t device_draw(uint64_t seed, int32_t m, int32_t d, float* W, hipStream_t stream);
+
 // Feature map test entry (generic fp32 arithmetic).
 hipError_t generic_feature_map(int32_t BH, int32_t L, int32_t d, int32_t m, int32_t dtype,
                                float knorm, int32_t relu, const void* X, const float* W,

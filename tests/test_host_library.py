@@ -191,6 +191,16 @@ def test_state_entry_validation():
     assert lib.favor_last_hip_error() == 0
 
 
+def test_device_draw_validation():
+    f = lib.favor_draw_projection_device
+    assert f(1, 256, 64, None, None) == ENULL
+    assert f(1, 0, 64, A, None) == ESHAPE
+    assert f(1, 256, 0, A, None) == ESHAPE
+    assert f(1, 256, 129, A, None) == ESHAPE
+    assert f(1, 256, 64, MIS, None) == EALIGN
+    assert lib.favor_last_hip_error() == 0
+
+
 def test_feature_map_validation():
     f = lib.favor_feature_map
     assert f(1, 1, 0, 64, 64, 1, A, A, A, None) == ESHAPE
