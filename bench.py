@@ -135,7 +135,10 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     # the query side (projection, [num | den], T, dq: 8 d m), the query
     # state from the features (2 d m) and the key side (projection, H, dk,
     # dv: 8 d m).
-    bwd = {"gb_query": (3, 8.0), "gb_gstate": (0, 2.0), "gb_key": (2, 8.0)}
+    bwd = {"gb_query": (3, 8.0), "gb_gstate": (0, 2.0), "gb_key": (2, 8.0),
+           # matrix-core backward: bquery forms the features, [num | den], T, dq
+           # and the query state G (10 d m); bkey the key features, H, dk, dv
+           "bquery": (3, 10.0), "bkey": (2, 8.0)}
     if name == "g_decode":
         # one token per head: the state [m][d+4] fp32 read and written, q, k,
         # v read and o written; two projections, the state update and the

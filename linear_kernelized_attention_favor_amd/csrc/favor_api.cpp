@@ -91,8 +91,10 @@ int backward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtyp
   if (ws_bytes < b.bytes) return FAVOR_ERR_WORKSPACE;
   p.knorm = knorm;
   p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
-  const hipError_t e = generic_backward(p, b, Q, K, V, W, dO, dQ, dK, dV, ws,
-                                        static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = b.path == kPathMfma
+                           ? mfma_backward(p, b, Q, K, V, W, dO, dQ, dK, dV, ws, st)
+                           : generic_backward(p, b, Q, K, V, W, dO, dQ, dK, dV, ws, st);
   if (e != hipSuccess) return fail_hip(e);
   return FAVOR_OK;
 }
@@ -202,6 +204,33 @@ void make_generic_plan(Plan* p) {
 
 void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                    int32_t causal, Plan* p, BwdPlan* b) {
+  std::memset(b, 0, sizeof(*b));
+  if (mfma_bwd_supported(d, m, dtype, causal)) {
+    make_plan(B, H, L, d, m, dtype, causal, p);   // the forward's key partials
+    b->path = kPathMfma;
+    const size_t BH = static_cast<size_t>(p->BH), mm = static_cast<size_t>(m);
+    // Query blocks: about 512 work-groups in total, a multiple of 64 tokens.
+    const int want = (512 + p->BH - 1) / p->BH;
+    const int ntile = (L + 63) / 64;
+    int nqb = want < ntile ? want : ntile;
+    if (nqb < 1) nqb = 1;
+    b->qblk = ((ntile + nqb - 1) / nqb) * 64;
+    b->nqb = (L + b->qblk - 1) / b->qblk;
+    size_t off = p->bytes;
+    b->off_W16 = off; off = align256(off + mm * 64 * 2);
+    b->off_WT = off;  off = align256(off + mm * 64 * 2);
+    b->off_KzT = off; off = align256(off + BH * 2 * 80 * mm * 2);
+    b->off_KzF = off; off = align256(off + BH * 2 * mm * 64 * 2);
+    b->off_zf = off;  off = align256(off + BH * mm * 4);
+    b->off_cf = off;  off = align256(off + BH * mm * 4);
+    b->off_G = off;   off = align256(off + BH * b->nqb * mm * 65 * 4);
+    b->off_GF = off;  off = align256(off + BH * 2 * mm * 64 * 2);
+    b->off_GT = off;  off = align256(off + BH * mm * 64 * 2);
+    b->off_Gz = off;  off = align256(off + BH * mm * 4);
+    b->bytes = off;
+    return;
+  }
+  b->path = kPathGeneric;
   // Causal: 64-token segments (the masked in-segment terms of the backward
   // cost O(segment) per token; the forward's 256 would quadruple them).
   make_generic_only_plan(B, H, L, d, m, dtype, causal, causal ? 64 : 0, p);

@@ -64,7 +64,16 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
 //                             (causal) its exclusive suffix over later segments
 //   Gfin [BH][m][d+1]         bidirectional total of G
 struct BwdPlan {
+  int32_t path;   // kPathGeneric, or kPathMfma (bidirectional bf16, d = 64)
   size_t off_U, off_M, off_G, off_Gfin;
+  // Matrix-core path (after the forward plan's key partials T, cseg):
+  //   W16 [m][64] fp16 (W log2 e), WT [64][m] bf16 (W^T), KzT [BH][2][80][m]
+  //   bf16 (state^T hi, lo; row 64 = z), KzF [BH][2][m][64] bf16 (state hi,
+  //   lo), zf, cf [BH][m] fp32 (z and the references), G [BH][nqb][m][65]
+  //   fp32 (per query block), GF [BH][2][m][64] (hi, lo), GT [BH][64][m] bf16
+  //   and Gz [BH][m] fp32 (their sum).
+  size_t off_W16, off_WT, off_KzT, off_KzF, off_zf, off_cf, off_GF, off_GT, off_Gz;
+  int32_t nqb, qblk;   // query blocks per head and their length (multiple of 64)
   size_t bytes;
 };
 // A generic-path plan whatever the shape (seg <= 0: the default segment length).
@@ -92,6 +101,14 @@ hipError_t generic_decode(int32_t BH, int32_t d, int32_t m, int32_t dtype, float
 // Its first two steps alone: the key state and references in the workspace.
 hipError_t generic_key_state(const Plan& p, const void* K, const void* V, const float* W,
                              void* ws, hipStream_t stream);
+// Matrix-core backward (bidirectional, bf16, d = 64, m in {64, 128, 192, 256}).
+bool mfma_bwd_supported(int32_t d, int32_t m, int32_t dtype, int32_t causal);
+hipError_t mfma_backward(const Plan& p, const BwdPlan& b, const void* Q, const void* K,
+                         const void* V, const float* W, const void* dO, void* dQ, void* dK,
+                         void* dV, void* ws, hipStream_t stream);
+// The bidirectional matrix-core path's key partials alone (kpart).
+hipError_t mfma_bidir_key_partials(const Plan& p, const void* K, const void* V, const float* W,
+                                   void* ws, hipStream_t stream);
 // Generic backward: dQ, dK, dV of <dO, O> (same dtype as the inputs).
 hipError_t generic_backward(const Plan& p, const BwdPlan& b, const void* Q, const void* K,
                             const void* V, const float* W, const void* dO, void* dQ, void* dK,

@@ -1797,6 +1797,39 @@ bool mfma_bidir_streams_queries(int32_t d, int32_t m) {
   return (d == 64 ? qapply_lds_bytes<64>(m) : qapply_lds_bytes<128>(m)) > 160 * 1024;
 }
 
+namespace {
+// kpart alone, with the bidirectional plan's configuration.
+template <int D, int NW, int NFB, bool RELU>
+hipError_t launch_kpart(const Plan& p, const uint16_t* K, const uint16_t* V, const float* W,
+                        char* ws, hipStream_t st) {
+  float* P = reinterpret_cast<float*>(ws + p.off_T);
+  float* cs = reinterpret_cast<float*>(ws + p.off_cseg);
+  constexpr int TG = (NW <= 4) ? 2 : 1;
+  timing_before(st);
+  kpart<D, NW, TG, RELU><<<dim3(p.nseg * p.BH * NFB), TG * NW * 64, 0, st>>>(
+      K, V, W, P, cs, p.L, p.m, p.seg, p.nseg, p.nseg, p.knorm);
+  const hipError_t e = hipGetLastError();
+  timing_after(st, "kpart");
+  return e;
+}
+}  // namespace
+
+hipError_t mfma_bidir_key_partials(const Plan& p, const void* K, const void* V, const float* W,
+                                   void* ws, hipStream_t stream) {
+  const auto* k = static_cast<const uint16_t*>(K);
+  const auto* v = static_cast<const uint16_t*>(V);
+  char* w = static_cast<char*>(ws);
+  int nw, nfb;
+  bidir_blocks(p.d, p.m, &nw, &nfb);
+#define FAVOR_CASE(D, NW, NFB)                                                       \
+  if (p.d == D && nw == NW && nfb == NFB)                                            \
+    return p.relu ? launch_kpart<D, NW, NFB, true>(p, k, v, W, w, stream)            \
+                  : launch_kpart<D, NW, NFB, false>(p, k, v, W, w, stream);
+  FAVOR_CASE(64, 1, 1) FAVOR_CASE(64, 2, 1) FAVOR_CASE(64, 3, 1) FAVOR_CASE(64, 4, 1)
+#undef FAVOR_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                               const float* W, void* O, void* ws, hipStream_t stream) {
   const auto* q = static_cast<const uint16_t*>(Q);

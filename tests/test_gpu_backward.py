@@ -43,25 +43,26 @@ def grad_err(got, ref):
     return float(np.max(num / den))
 
 
-def _relu_gate_check(name, got, ref, X, W, dXp, tol):
+def _relu_gate_check(name, got, ref, X, W, dXp, tol, tau):
     """ReLU gradients with the gate decided where the pages leave it open.
 
     The gate [w_r . x > 0] is a floating-point decision: where |w_r . x| is
-    within the fp32 projection's rounding of 0, the GPU and the oracle may
-    decide it differently, and both answers are gradients of the same
-    function (one-sided derivatives at the kink).  Rows within the bar are
-    accepted; a row outside it passes only if flipping some of its ambiguous
-    gates (|w_r . x| <= 1e-5 |x| |w_r|, at most 3) in the oracle's gradient
+    within the projection's rounding of 0 (tau |x| |w_r|: 1e-5 for the fp32
+    projection of the generic kernels, 2e-3 for the fp16 operands of the
+    matrix cores), the GPU and the oracle may decide it differently, and both
+    answers are gradients of the same function (one-sided derivatives at the
+    kink).  Rows within the bar are accepted; a row outside it passes only if
+    flipping some of its ambiguous gates (at most 10) in the oracle's gradient
     dx = sum_r [w_r . x > 0] dX'_r w_r / sqrt(m) brings it within the bar.
     """
     m = W.shape[0]
     S = X @ W.T
-    amb = np.abs(S) <= 1e-5 * np.linalg.norm(X, axis=-1, keepdims=True) * np.linalg.norm(W, axis=-1)
+    amb = np.abs(S) <= tau * np.linalg.norm(X, axis=-1, keepdims=True) * np.linalg.norm(W, axis=-1)
     scale = np.abs(ref).max(axis=(-1, -2), keepdims=True)
     row_err = np.abs(got - ref).max(-1) / scale[..., 0]
     for idx in zip(*np.nonzero(row_err > tol)):
         rs = np.nonzero(amb[idx])[0]
-        assert 0 < len(rs) <= 3, (name, idx, float(row_err[idx]), len(rs))
+        assert 0 < len(rs) <= 10, (name, idx, float(row_err[idx]), len(rs))
         best = np.inf
         for flips in itertools.product((0, 1), repeat=len(rs)):
             alt = ref[idx].copy()
@@ -124,15 +125,39 @@ def test_backward_shapes(fv, shape, causal, dtype, kernel):
                           _np64(v), _np64(do))
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         if name in ("dQ", "dK") and shape[2] == 1:
-            # one token: O = v_0 whatever q and k are, so dQ = dK = 0 up to rounding
-            assert np.abs(_np64(g)).max() <= 1e-5 * np.abs(ref[2]).max()
+            # one token: O = v_0 whatever q and k are, so dQ = dK = 0 up to
+            # rounding (bf16: the features and T rounded as matrix-core
+            # operands leave ~2^-9 of the terms, which cancel exactly here)
+            bound = 1e-5 if dtype == "f32" else 1e-2
+            assert np.abs(_np64(g)).max() <= bound * np.abs(ref[2]).max()
             continue
         if kernel == "relu" and name != "dV":
             X, dXp = (q, dQp) if name == "dQ" else (k, dKp)
-            _relu_gate_check(name, _np64(g), r, _np64(X), W64, dXp, TOL[dtype])
+            _relu_gate_check(name, _np64(g), r, _np64(X), W64, dXp, TOL[dtype],
+                             1e-5 if dtype == "f32" else 2e-3)
             continue
         err = grad_err(_np64(g), r)
         assert err <= TOL[dtype], (name, err)
+
+
+# Shapes of the matrix-core backward (bidirectional, bf16, d = 64, m up to
+# 256): single tokens, ragged 64-token tiles, every supported m, many query
+# blocks per head.
+MFMA_SHAPES = [
+    (1, 1, 1, 64, 64),
+    (1, 2, 65, 64, 192),
+    (3, 1, 130, 64, 64),
+    (1, 1, 4097, 64, 256),
+    (2, 3, 500, 64, 128),
+]
+
+
+@pytest.mark.parametrize("kernel", ["softmax", "gaussian", "relu"])
+@pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_backward_matrix_core_shapes(fv, shape, kernel):
+    B, H, L, d, m = shape
+    assert fv.plan_describe(B, H, L, d, m, fv.BF16, False)[0] == 1   # the matrix-core plan
+    test_backward_shapes(fv, shape, False, "bf16", kernel)
 
 
 @pytest.mark.parametrize("causal", [False, True])
