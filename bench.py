@@ -138,7 +138,13 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     bwd = {"gb_query": (3, 8.0), "gb_gstate": (0, 2.0), "gb_key": (2, 8.0),
            # matrix-core backward: bquery forms the features, [num | den], T, dq
            # and the query state G (10 d m); bkey the key features, H, dk, dv
-           "bquery": (3, 10.0), "bkey": (2, 8.0)}
+           "bquery": (3, 10.0), "bkey": (2, 8.0),
+           # the same work split into passes that each rebuild the features:
+           # 1/den and u0 (projection, [num | den]), dq (projection, T, dq),
+           # the query state (projection, G); dk (projection, H, dk), dv
+           # (projection, dv)
+           "bq_den": (2, 4.0), "bq_dq": (1, 6.0), "bq_g": (0, 4.0),
+           "bkey_dk": (1, 6.0), "bkey_dv": (1, 4.0)}
     if name == "g_decode":
         # one token per head: the state [m][d+4] fp32 read and written, q, k,
         # v read and o written; two projections, the state update and the

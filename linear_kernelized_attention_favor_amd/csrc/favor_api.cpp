@@ -215,7 +215,14 @@ void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
     int nqb = want < ntile ? want : ntile;
     if (nqb < 1) nqb = 1;
     b->qblk = ((ntile + nqb - 1) / nqb) * 64;
+    b->qblk = (b->qblk + 127) / 128 * 128;   // whole 128-query steps
     b->nqb = (L + b->qblk - 1) / b->qblk;
+    // Key blocks: about 512 work-groups, a multiple of 128 keys.
+    const int nstep = (L + 127) / 128;
+    int nkb = want < nstep ? want : nstep;
+    if (nkb < 1) nkb = 1;
+    b->kblk = ((nstep + nkb - 1) / nkb) * 128;
+    b->nkb = (L + b->kblk - 1) / b->kblk;
     size_t off = p->bytes;
     b->off_W16 = off; off = align256(off + mm * 64 * 2);
     b->off_WT = off;  off = align256(off + mm * 64 * 2);
@@ -227,6 +234,7 @@ void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
     b->off_GF = off;  off = align256(off + BH * 2 * mm * 64 * 2);
     b->off_GT = off;  off = align256(off + BH * mm * 64 * 2);
     b->off_Gz = off;  off = align256(off + BH * mm * 4);
+    b->off_ru = off;  off = align256(off + BH * static_cast<size_t>(L) * 2 * 4);
     b->bytes = off;
     return;
   }

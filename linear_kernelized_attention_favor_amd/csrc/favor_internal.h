@@ -72,8 +72,10 @@ struct BwdPlan {
   //   lo), zf, cf [BH][m] fp32 (z and the references), G [BH][nqb][m][65]
   //   fp32 (per query block), GF [BH][2][m][64] (hi, lo), GT [BH][64][m] bf16
   //   and Gz [BH][m] fp32 (their sum).
-  size_t off_W16, off_WT, off_KzT, off_KzF, off_zf, off_cf, off_GF, off_GT, off_Gz;
+  //   ru [BH][L][2] fp32 (1/den and u0 per query).
+  size_t off_W16, off_WT, off_KzT, off_KzF, off_zf, off_cf, off_GF, off_GT, off_Gz, off_ru;
   int32_t nqb, qblk;   // query blocks per head and their length (multiple of 64)
+  int32_t nkb, kblk;   // key blocks per head and their length (multiple of 128)
   size_t bytes;
 };
 // A generic-path plan whatever the shape (seg <= 0: the default segment length).

@@ -21,14 +21,16 @@
 // references are opposite, and e^{-M_i} divides out through den~ in U.
 //
 // Launches: kpart (the forward's key partials), bprep (W' in fp16 and W^T in
-// bf16), bcombine (the split partials summed into the operand layouts),
-// bquery (per query block: dq and the block's G partial), gcombine (the
-// blocks' G summed in block order), bkey (per 64-key tile: dk, dv).
+// bf16), bcombine (the split partials summed into the operand layouts), bqr
+// in three passes (1/den and u0; dq; the query blocks' G partials), gcombine
+// (the blocks' G summed in block order), bkeyr in two passes (dk; dv).
 //
-// Matrix products run as 16x16x32 MFMAs on 64-token tiles, one wave per 16
-// tokens; every product reads its operands k-contiguous (from LDS for the
-// per-tile values, from global memory -- L2-resident per head -- for W', W^T,
-// the state and G).  Values change layout between products through LDS.
+// Matrix products run as 16x16x32 MFMAs, each wave on two 16-token column
+// tiles; a work-group keeps the per-head operands it needs (W', W^T, the
+// state, G) resident in LDS and walks a block of tokens.  A product's output
+// tile feeds the next product's k-slice straight from registers where the
+// other operand stores its features in the order feat_pos; Q~^T and Ucat^T
+// for the query state go through LDS.
 // Numerics: projections in fp16 (Q, K exact, W' rounded); features, P and R
 // rounded to bf16 as operands; the state, U (with u0) and G, whose products
 // cancel against a ones-column term (T = S~ U + z~ u0 and H = G v + G_z vanish
@@ -49,17 +51,31 @@ namespace {
 using namespace mfma;
 
 constexpr int kD = 64;          // head dimension of this path
-constexpr int kTok = 64;        // tokens per tile (4 waves x 16)
-constexpr int kQRow = kD + 8;   // fp16 / bf16 per row of [token][d] LDS tiles
-constexpr int kUTRow = kTok + 8;
 
 __device__ inline uint16_t bf16_bits(float x) {
   return static_cast<uint16_t>(pack_bf16(x, 0.f) & 0xffffu);
 }
 
+// Feature order of the operands contracted over features.  A product's
+// 16x16 output tile holds, per lane (g, l16), rows 4g..4g+3 of one column;
+// two such tiles (features 32p + [0, 16) and 32p + [16, 32)) give a lane the
+// eight features {32p + 4g + j, 32p + 16 + 4g + j : j < 4} of its column,
+// which serve directly as the lane's 8-value k-slice of the next product if
+// the other operand stores its features in the same order: position
+// 32p + 8g + j holds feature 32p + 4g + j (j < 4) or 32p + 16 + 4g + j - 4.
+__device__ inline int feat_pos(int f) {
+  const int p = f & ~31, i = f & 31;
+  return p + 8 * ((i & 15) >> 2) + (i & 3) + (i >= 16 ? 4 : 0);
+}
+// Eight bf16 of column l16 from the output tiles ft = 2p and 2p + 1, in that order.
+__device__ inline bf16x8 pack_k8(const f32x4& lo, const f32x4& hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]),
+                                               pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])));
+}
+
 // ---------------------------------------------------------------------------
-// bprep: W' = W log2 e as fp16 [m][64] and W^T as bf16 [64][m] (true W).
-// grid (ceil(m*64/256)).
+// bprep: W' = W log2 e as fp16 [m][64] and W^T as bf16 [64][m] (true W,
+// features in the contraction order feat_pos).  grid (ceil(m*64/256)).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bprep(const float* __restrict__ W,
                                              _Float16* __restrict__ W16,
@@ -69,13 +85,14 @@ __global__ __launch_bounds__(256) void bprep(const float* __restrict__ W,
   const int r = i / kD, a = i - r * kD;
   const float w = W[i];
   W16[i] = static_cast<_Float16>(w * kLog2e);
-  WT[static_cast<size_t>(a) * m + r] = bf16_bits(w);
+  WT[static_cast<size_t>(a) * m + feat_pos(r)] = bf16_bits(w);
 }
 
 // ---------------------------------------------------------------------------
 // bcombine: per head and feature, the splits' partial states rescaled to the
 // largest reference and summed in split order.  Writes KzT [2][80][m] bf16
-// (hi, lo; rows 0..63 S~^T, row 64 z~, rows 65..79 zero), KzF [2][m][64] bf16
+// (hi, lo; rows 0..63 S~^T, row 64 z~, rows 65..79 zero; features in the
+// contraction order feat_pos), KzF [2][m][64] bf16
 // (S~ hi, lo), zf [m] fp32 (z~) and cf [m] fp32 (the reference).  grid
 // (ceil(m/64), BH), 256 threads: 64 features x 4 column groups.
 // ---------------------------------------------------------------------------
@@ -101,8 +118,8 @@ __global__ __launch_bounds__(256) void bcombine(const float* __restrict__ P,
     }
     const uint16_t hi = bf16_bits(acc);
     const uint16_t lo = bf16_bits(acc - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-    KzT[(static_cast<size_t>(bh) * 160 + c) * m + f] = hi;
-    KzT[(static_cast<size_t>(bh) * 160 + 80 + c) * m + f] = lo;
+    KzT[(static_cast<size_t>(bh) * 160 + c) * m + feat_pos(f)] = hi;
+    KzT[(static_cast<size_t>(bh) * 160 + 80 + c) * m + feat_pos(f)] = lo;
     if (c < kD) {
       KzF[(static_cast<size_t>(bh) * 2 * m + f) * kD + c] = hi;
       KzF[((static_cast<size_t>(bh) * 2 + 1) * m + f) * kD + c] = lo;
@@ -111,17 +128,12 @@ __global__ __launch_bounds__(256) void bcombine(const float* __restrict__ P,
     }
   }
   for (int c = kD + 1 + cg; c < 80; c += 4) {
-    KzT[(static_cast<size_t>(bh) * 160 + c) * m + f] = 0;
-    KzT[(static_cast<size_t>(bh) * 160 + 80 + c) * m + f] = 0;
+    KzT[(static_cast<size_t>(bh) * 160 + c) * m + feat_pos(f)] = 0;
+    KzT[(static_cast<size_t>(bh) * 160 + 80 + c) * m + feat_pos(f)] = 0;
   }
   if (cg == 0) cf[static_cast<size_t>(bh) * m + f] = cm;
 }
 
-// 16-byte operand loads.
-__device__ inline f16x8 ld_f16x8(const _Float16* p) { return *reinterpret_cast<const f16x8*>(p); }
-__device__ inline bf16x8 ld_bf16x8(const uint16_t* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
 // Four bf16 values (8 bytes) at p, as floats.
 __device__ inline void ld_bf16x4(const uint16_t* p, float (&x)[4]) {
   const uint2 u = *reinterpret_cast<const uint2*>(p);
@@ -134,276 +146,10 @@ __device__ inline void st_bf16x4(uint16_t* p, float a, float b, float c, float d
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16(a, b), pack_bf16(c, d));
 }
 
-// Stages a 64-token tile of X [L][64] bf16 (rows past L zero) into an LDS
-// tile [64][kQRow] as fp16 (exact for bf16 values in fp16's normal range);
-// with nrm, also writes knorm log2(e) |x|^2 per token.  256 threads.
-__device__ inline void stage_f16(const uint16_t* __restrict__ X, size_t base, int t0, int L,
-                                 _Float16 (*dst)[kQRow], float* nrm, float ncoef) {
-  const int t = threadIdx.x;
-  // 64 tokens x 8 chunks of 8 values; thread t takes chunks t and t + 256
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = t + 256 * h;
-    const int tok = c / 8, ch = c % 8;
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (t0 + tok < L) u = *reinterpret_cast<const uint4*>(X + base + static_cast<size_t>(t0 + tok) * kD + 8 * ch);
-    float ss = 0.f;
-    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
-      ss = fmaf(lo, lo, ss);
-      ss = fmaf(hi, hi, ss);
-    }
-    uint4 hv;
-    hv.x = bf16x2_to_f16x2(u.x);
-    hv.y = bf16x2_to_f16x2(u.y);
-    hv.z = bf16x2_to_f16x2(u.z);
-    hv.w = bf16x2_to_f16x2(u.w);
-    *reinterpret_cast<uint4*>(&dst[tok][8 * ch]) = hv;
-    if (nrm) {
-      ss = group_sum<8>(ss);
-      if (ch == 0) nrm[tok] = ncoef * ss;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// bquery: grid (BH * nqb), 256 threads.  Work-group (bh, qb) takes tokens
-// [qb qblk, (qb+1) qblk) in 64-token tiles; wave w owns tokens 16w..16w+15 of
-// a tile for the per-token products and features [w m/4, (w+1) m/4) for the
-// block's G partial, written to Gp [BH][nqb][m][65] fp32 at the end.
-// ---------------------------------------------------------------------------
-template <int M, bool RELU>
-__global__ __launch_bounds__(256, 1) void bquery(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
-    const _Float16* __restrict__ W16, const uint16_t* __restrict__ WT,
-    const uint16_t* __restrict__ KzT, const uint16_t* __restrict__ KzF,
-    const float* __restrict__ zf, const float* __restrict__ cf, uint16_t* __restrict__ dQ,
-    float* __restrict__ Gp, int L, int qblk, int nqb, float knorm) {
-  constexpr int FT = M / 16;        // feature tiles (per token, all features)
-  constexpr int KF = M / 32;        // k-steps over features
-  constexpr int GFT = M / 64;       // feature tiles of this wave's G rows
-  constexpr int QFRow = M + 8;
-  const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int l16 = lane % 16, g = lane / 16;
-  __shared__ _Float16 Qs[kTok][kQRow];
-  __shared__ uint16_t QF[kTok][QFRow];     // Q~ [token][feature], then P
-  __shared__ uint16_t QT[M][kUTRow];       // Q~^T [feature][token]
-  __shared__ uint16_t Ds[kTok][kQRow];     // dO [token][column] (bf16, as given)
-  __shared__ uint16_t UT[2][80][kUTRow];   // Ucat^T hi, lo [column][token] (row 64 = u0)
-
-  const size_t base = static_cast<size_t>(bh) * L * kD;
-  const uint16_t* kzt0 = KzT + static_cast<size_t>(bh) * 160 * M;       // hi; lo at + 80 M
-  const uint16_t* kzf0 = KzF + static_cast<size_t>(bh) * 2 * M * kD;    // hi; lo at + M kD
-  const float* zfh0 = zf + static_cast<size_t>(bh) * M;
-  const float* cfh0 = cf + static_cast<size_t>(bh) * M;
-  for (int i = tid; i < 2 * 15 * kUTRow; i += 256) {
-    const int h = i / (15 * kUTRow), j = i % (15 * kUTRow);
-    UT[h][65 + j / kUTRow][j % kUTRow] = 0;
-  }
-
-  f32x4 G[GFT][5];
-#pragma unroll
-  for (int a = 0; a < GFT; ++a)
-#pragma unroll
-    for (int c = 0; c < 5; ++c) G[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int i_beg = qb * qblk, i_end = min(L, i_beg + qblk);
-  const int tl = 16 * wave + l16;            // this lane's token within the tile
-  for (int t0 = i_beg; t0 < i_end; t0 += kTok) {
-    // The per-head operands are re-read from memory (L2) every tile: made
-    // opaque here so that the compiler does not hoist every one of their
-    // loads out of the loop into registers.
-    int z = 0;
-    asm volatile("" : "+v"(z));
-    const _Float16* w16 = W16 + z;
-    const uint16_t* wt = WT + z;
-    const uint16_t* kzt = kzt0 + z;
-    const uint16_t* kzf = kzf0 + z;
-    const float* zfh = zfh0 + z;
-    const float* cfh = cfh0 + z;
-    __syncthreads();                          // previous tile's QT / UT reads done
-    stage_f16(Q, base, t0, L, Qs, nullptr, 0.f);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {            // dO rows as given (zero past L)
-      const int c = tid + 256 * h;
-      const int tok = c / 8, ch = c % 8;
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (t0 + tok < L) u = *reinterpret_cast<const uint4*>(dO + base + static_cast<size_t>(t0 + tok) * kD + 8 * ch);
-      *reinterpret_cast<uint4*>(&Ds[tok][8 * ch]) = u;
-    }
-    __syncthreads();
-    const bool live = t0 + tl < L;
-    // (1) S^T = W' Q^T (rows: features 16 ft + 4 g + v; column: token tl).
-    f32x4 S[FT];
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      S[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        S[ft] = mma_f16(ld_f16x8(w16 + (16 * ft + l16) * kD + 32 * ks + 8 * g),
-                        ld_f16x8(&Qs[tl][32 * ks + 8 * g]), S[ft]);
-      if (ft % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bounded operand lookahead
-    }
-    // Query features: + c, row reference M (ReLU: none).
-    float Mrow = 0.f;
-    if constexpr (!RELU) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        const float4 c4 = *reinterpret_cast<const float4*>(cfh + 16 * ft + 4 * g);
-        S[ft][0] += c4.x; S[ft][1] += c4.y; S[ft][2] += c4.z; S[ft][3] += c4.w;
-        mx = fmaxf(mx, max3(S[ft][0], S[ft][1], fmaxf(S[ft][2], S[ft][3])));
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      Mrow = mx;
-    }
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) S[ft][v] = feature<RELU>(S[ft][v] - Mrow);
-    // Q~ to QF [token][feature] (4 features per lane) and QT [feature][token].
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      st_bf16x4(&QF[tl][16 * ft + 4 * g], S[ft][0], S[ft][1], S[ft][2], S[ft][3]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) QT[16 * ft + 4 * g + v][tl] = bf16_bits(S[ft][v]);
-    }
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    // (2) [num | den]^T = KzT Q~^T (rows: columns 16 ct + 4 g + v; column: token tl).
-    f32x4 N[5];
-#pragma unroll
-    for (int ct = 0; ct < 5; ++ct) {
-      N[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KF; ++ks) {
-        const bf16x8 qb = ld_bf16x8(&QF[tl][32 * ks + 8 * g]);
-        N[ct] = mma_bf16(ld_bf16x8(kzt + (16 * ct + l16) * M + 32 * ks + 8 * g), qb, N[ct]);
-        N[ct] = mma_bf16(ld_bf16x8(kzt + (80 + 16 * ct + l16) * M + 32 * ks + 8 * g), qb, N[ct]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // den (column 64: ct 4, g 0, v 0) to every lane of the token
-    const float den = __shfl(N[4][0], l16);
-    // U = dO / den, u0 = -(dO . num) / den^2; dO rows past L are zero.
-    float dov[4][4];
-    float dot = 0.f;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      ld_bf16x4(&Ds[tl][16 * ct + 4 * g], dov[ct]);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) dot = fmaf(dov[ct][v], N[ct][v], dot);
-    }
-    dot += __shfl_xor(dot, 16);
-    dot += __shfl_xor(dot, 32);
-    const float rden = live ? 1.f / den : 0.f;
-    const float u0 = -dot * rden * rden;
-    // Ucat^T as bf16 hi + lo
-    auto put = [&](int row, float x) {
-      const uint16_t hi = bf16_bits(x);
-      UT[0][row][tl] = hi;
-      UT[1][row][tl] = bf16_bits(x - __uint_as_float(static_cast<uint32_t>(hi) << 16));
-    };
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) put(16 * ct + 4 * g + v, dov[ct][v] * rden);
-    if (g == 0) put(64, u0);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    // (3) T^T = S~ U^T + z~ u0 (rows: features; column: token tl), P = Q~ T
-    // (Q~ read back from QF as the bf16 operand the products used, then P
-    // written in its place).
-    float psum = 0.f;
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      float qf[4];
-      ld_bf16x4(&QF[tl][16 * ft + 4 * g], qf);
-      f32x4 T = f32x4{0.f, 0.f, 0.f, 0.f};   // S~ . dO (hi + lo), scaled by 1/den below
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 db = ld_bf16x8(&Ds[tl][32 * ks + 8 * g]);
-        T = mma_bf16(ld_bf16x8(kzf + (16 * ft + l16) * kD + 32 * ks + 8 * g), db, T);
-        T = mma_bf16(ld_bf16x8(kzf + (M + 16 * ft + l16) * kD + 32 * ks + 8 * g), db, T);
-      }
-      const float4 z4 = *reinterpret_cast<const float4*>(zfh + 16 * ft + 4 * g);
-      const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
-      float p[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float tv = fmaf(zz[v], u0, T[v] * rden);
-        p[v] = RELU ? (qf[v] > 0.f ? tv : 0.f) : qf[v] * tv;
-        psum += p[v];
-      }
-      st_bf16x4(&QF[tl][16 * ft + 4 * g], p[0], p[1], p[2], p[3]);
-      if (ft % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-    }
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    // (4) dq^T = W^T P^T (rows: d columns 16 at + 4 g + v; column: token tl).
-    // (Every lane takes part in the products; only live tokens are stored.)
-    {
-#pragma unroll
-      for (int at = 0; at < 4; ++at) {
-        f32x4 Dq = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KF; ++ks)
-          Dq = mma_bf16(ld_bf16x8(wt + (16 * at + l16) * M + 32 * ks + 8 * g),
-                        ld_bf16x8(&QF[tl][32 * ks + 8 * g]), Dq);
-        const int a0 = 16 * at + 4 * g;
-        float o[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float qv = static_cast<float>(Qs[tl][a0 + v]);
-          o[v] = RELU ? Dq[v] * kLog2e : fmaf(-2.f * knorm * psum, qv, Dq[v]);
-        }
-        if (live)
-          st_bf16x4(dQ + base + static_cast<size_t>(t0 + tl) * kD + a0, o[0], o[1], o[2], o[3]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // (5) G (this wave's feature rows) += Q~^T Ucat over the tile's 64 tokens.
-#pragma unroll
-    for (int a = 0; a < GFT; ++a) {
-      const int f = wave * (M / 4) + 16 * a + l16;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 qa = ld_bf16x8(&QT[f][32 * ks + 8 * g]);
-#pragma unroll
-        for (int ct = 0; ct < 5; ++ct) {
-          G[a][ct] = mma_bf16(qa, ld_bf16x8(&UT[0][16 * ct + l16][32 * ks + 8 * g]), G[a][ct]);
-          G[a][ct] = mma_bf16(qa, ld_bf16x8(&UT[1][16 * ct + l16][32 * ks + 8 * g]), G[a][ct]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // Block partial: Gp [bh][qb][f][c], rows f = wave m/4 + 16 a + 4 g + v, column 16 ct + l16.
-  float* gp = Gp + (static_cast<size_t>(bh) * nqb + qb) * M * (kD + 1);
-#pragma unroll
-  for (int a = 0; a < GFT; ++a)
-#pragma unroll
-    for (int ct = 0; ct < 5; ++ct) {
-      const int c = 16 * ct + l16;
-      if (c > kD) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int f = wave * (M / 4) + 16 * a + 4 * g + v;
-        gp[static_cast<size_t>(f) * (kD + 1) + c] = G[a][ct][v];
-      }
-    }
-}
-
 // ---------------------------------------------------------------------------
 // gcombine: G = sum over query blocks (block order) -> GF [2][m][64] bf16
-// (hi, lo), GT [64][m] bf16, Gz [m] fp32 (the ones column).
+// (hi, lo), GT [64][m] bf16 (features in the order feat_pos), Gz [m] fp32
+// (the ones column).
 // grid (ceil(m*65/256), BH).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gcombine(const float* __restrict__ Gp,
@@ -421,123 +167,500 @@ __global__ __launch_bounds__(256) void gcombine(const float* __restrict__ Gp,
     GF[(static_cast<size_t>(bh) * 2 * m + f) * kD + c] = x;
     GF[((static_cast<size_t>(bh) * 2 + 1) * m + f) * kD + c] =
         bf16_bits(acc - __uint_as_float(static_cast<uint32_t>(x) << 16));
-    GT[(static_cast<size_t>(bh) * kD + c) * m + f] = x;
+    GT[(static_cast<size_t>(bh) * kD + c) * m + feat_pos(f)] = x;
   } else {
     Gz[static_cast<size_t>(bh) * m + f] = acc;
   }
 }
 
 // ---------------------------------------------------------------------------
-// bkey: grid (BH * ceil(L/64)), 256 threads, one 64-key tile per work-group,
-// wave w owns keys 16w..16w+15.
+// bkeyr: the key side with its per-head operands resident in LDS.  grid
+// (BH * nkb), 256 threads; work-group (bh, kb) takes keys [kb kblk,
+// (kb+1) kblk) in steps of 128, wave w owning keys 32w..32w+31 of a step
+// (two 16-key column tiles, so every operand fragment read from LDS feeds two
+// products).  MODE 0: dk (operands W' [M][64] fp16, G hi/lo [2][M][64] bf16,
+// W^T [64][M] bf16: 128 KB); MODE 1: dv (W', G^T [64][M]: 64 KB).  K and V
+// fragments come straight from global memory as the products' B operands.
+// LDS rows are XOR-swizzled in 16-byte chunks (chunk ^ (row & 7)).
 // ---------------------------------------------------------------------------
-template <int M, bool RELU>
-__global__ __launch_bounds__(256, 1) void bkey(
+template <int C>
+__device__ inline int swz(int row, int col) {   // element offset in a [rows][C] tile
+  return row * C + ((((col >> 3) ^ (row & 7))) << 3) + (col & 7);
+}
+
+// Copies a [rows][C] 16-bit matrix from global memory into a swizzled LDS tile.
+template <int C>
+__device__ inline void stage_swz(const uint16_t* __restrict__ src, uint16_t* dst, int rows) {
+  const int nch = rows * (C / 8);
+  for (int i = threadIdx.x; i < nch; i += 256) {
+    const int r = i / (C / 8), c = (i % (C / 8)) * 8;
+    *reinterpret_cast<uint4*>(dst + swz<C>(r, c)) =
+        *reinterpret_cast<const uint4*>(src + static_cast<size_t>(r) * C + c);
+  }
+}
+
+template <int M, bool RELU, int MODE>
+__global__ __launch_bounds__(256, 1) void bkeyr(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const _Float16* __restrict__ W16, const uint16_t* __restrict__ WT,
     const uint16_t* __restrict__ GF, const uint16_t* __restrict__ GT,
     const float* __restrict__ Gz, const float* __restrict__ cf, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int L, int ntile, float knorm) {
+    uint16_t* __restrict__ dV, int L, int kblk, int nkb, float knorm) {
   constexpr int FT = M / 16;
   constexpr int KF = M / 32;
-  constexpr int FRow = M + 8;
-  const int bh = blockIdx.x / ntile, t0 = (blockIdx.x % ntile) * kTok;
+  const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int l16 = lane % 16, g = lane / 16;
-  __shared__ _Float16 Ks[kTok][kQRow];
-  __shared__ uint16_t Vs[kTok][kQRow];
-  __shared__ uint16_t RF[kTok][FRow];     // R [key][feature]
-  __shared__ uint16_t KF_[kTok][FRow];    // K~ [key][feature]
-  __shared__ float nk[kTok];
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* Wl = lds;                               // W' [M][64]
+  uint16_t* Gl = lds + M * kD;                      // MODE 0: G hi, lo [2][M][64]
+  uint16_t* Tl = lds + (MODE == 0 ? 3 : 1) * M * kD;   // W^T (MODE 0) or G^T (MODE 1) [64][M]
+
+  stage_swz<kD>(reinterpret_cast<const uint16_t*>(W16), Wl, M);
+  if constexpr (MODE == 0) {
+    stage_swz<kD>(GF + static_cast<size_t>(bh) * 2 * M * kD, Gl, 2 * M);
+    stage_swz<M>(WT, Tl, kD);
+  } else {
+    stage_swz<M>(GT + static_cast<size_t>(bh) * kD * M, Tl, kD);
+  }
+  __syncthreads();
 
   const size_t base = static_cast<size_t>(bh) * L * kD;
-  const uint16_t* gf = GF + static_cast<size_t>(bh) * 2 * M * kD;   // hi; lo at + M kD
-  const uint16_t* gt = GT + static_cast<size_t>(bh) * kD * M;
   const float* gz = Gz + static_cast<size_t>(bh) * M;
   const float* cfh = cf + static_cast<size_t>(bh) * M;
-  stage_f16(K, base, t0, L, Ks, nk, knorm * kLog2e);
-  {
-    // V rows as bf16 (as stored)
+  const int j_beg = kb * kblk, j_end = min(L, j_beg + kblk);
+  for (int t0 = j_beg + 32 * wave; t0 < j_end; t0 += 128) {
+    // Key fragments of the two column tiles (B operands, k = d), as fp16;
+    // norm terms n_j = knorm log2(e) |k_j|^2.
+    f16x8 kf[2][2];
+    float nrm[2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = tid + 256 * h;
-      const int tok = c / 8, ch = c % 8;
-      uint4 u = make_uint4(0u, 0u, 0u, 0u);
-      if (t0 + tok < L) u = *reinterpret_cast<const uint4*>(V + base + static_cast<size_t>(t0 + tok) * kD + 8 * ch);
-      *reinterpret_cast<uint4*>(&Vs[tok][8 * ch]) = u;
+    for (int nt = 0; nt < 2; ++nt) {
+      const int j = t0 + 16 * nt + l16;
+      float ss = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (j < L) u = *reinterpret_cast<const uint4*>(K + base + static_cast<size_t>(j) * kD + 32 * ks + 8 * g);
+        const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
+          ss = fmaf(lo, lo, ss);
+          ss = fmaf(hi, hi, ss);
+        }
+        kf[nt][ks] = __builtin_bit_cast(f16x8, make_uint4(bf16x2_to_f16x2(u.x), bf16x2_to_f16x2(u.y),
+                                                         bf16x2_to_f16x2(u.z), bf16x2_to_f16x2(u.w)));
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      nrm[nt] = knorm * kLog2e * ss;
+    }
+    // (1) E^T = W' K^T - n - c, K~ = exp2(E) (rows: features; columns: keys).
+    f32x4 E[2][FT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      float c4[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (!RELU) {
+        const float4 cv = *reinterpret_cast<const float4*>(cfh + 16 * ft + 4 * g);
+        c4[0] = cv.x; c4[1] = cv.y; c4[2] = cv.z; c4[3] = cv.w;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) E[nt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f16x8 wa = *reinterpret_cast<const f16x8*>(Wl + swz<kD>(16 * ft + l16, 32 * ks + 8 * g));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) E[nt][ft] = mma_f16(wa, kf[nt][ks], E[nt][ft]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          E[nt][ft][v] = feature<RELU>(RELU ? E[nt][ft][v] : E[nt][ft][v] - nrm[nt] - c4[v]);
+      __builtin_amdgcn_sched_barrier(0);   // bounded operand lookahead
+    }
+    if constexpr (MODE == 0) {
+      // (2) H^T = G V^T + G_z (G hi + lo), R = K~ H in place of K~.
+      bf16x8 vf[2][2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int j = t0 + 16 * nt + l16;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          uint4 u = make_uint4(0u, 0u, 0u, 0u);
+          if (j < L) u = *reinterpret_cast<const uint4*>(V + base + static_cast<size_t>(j) * kD + 32 * ks + 8 * g);
+          vf[nt][ks] = __builtin_bit_cast(bf16x8, u);
+        }
+      }
+      float rsum[2] = {0.f, 0.f};
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        f32x4 H[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 ghi = *reinterpret_cast<const bf16x8*>(Gl + swz<kD>(16 * ft + l16, 32 * ks + 8 * g));
+          const bf16x8 glo = *reinterpret_cast<const bf16x8*>(Gl + swz<kD>(M + 16 * ft + l16, 32 * ks + 8 * g));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            H[nt] = mma_bf16(ghi, vf[nt][ks], H[nt]);
+            H[nt] = mma_bf16(glo, vf[nt][ks], H[nt]);
+          }
+        }
+        const float4 z4 = *reinterpret_cast<const float4*>(gz + 16 * ft + 4 * g);
+        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float hv = H[nt][v] + zz[v];
+            const float r = RELU ? (E[nt][ft][v] > 0.f ? hv : 0.f) : E[nt][ft][v] * hv;
+            E[nt][ft][v] = r;
+            rsum[nt] += r;
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        rsum[nt] += __shfl_xor(rsum[nt], 16);
+        rsum[nt] += __shfl_xor(rsum[nt], 32);
+      }
+      // (3) dk^T = W^T R^T - 2 knorm (sum_r R) k.
+#pragma unroll
+      for (int at = 0; at < 4; ++at) {
+        f32x4 Dk[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KF; ++ks) {
+          const bf16x8 wa = *reinterpret_cast<const bf16x8*>(Tl + swz<M>(16 * at + l16, 32 * ks + 8 * g));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) Dk[nt] = mma_bf16(wa, pack_k8(E[nt][2 * ks], E[nt][2 * ks + 1]), Dk[nt]);
+        }
+        const int a0 = 16 * at + 4 * g;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int j = t0 + 16 * nt + l16;
+          if (j < L) {
+            float kv[4];
+            ld_bf16x4(K + base + static_cast<size_t>(j) * kD + a0, kv);
+            float o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              o[v] = RELU ? Dk[nt][v] * kLog2e : fmaf(-2.f * knorm * rsum[nt], kv[v], Dk[nt][v]);
+            st_bf16x4(dK + base + static_cast<size_t>(j) * kD + a0, o[0], o[1], o[2], o[3]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // (4) dv^T = G^T K~^T.
+#pragma unroll
+      for (int at = 0; at < 4; ++at) {
+        f32x4 Dv[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KF; ++ks) {
+          const bf16x8 ga = *reinterpret_cast<const bf16x8*>(Tl + swz<M>(16 * at + l16, 32 * ks + 8 * g));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) Dv[nt] = mma_bf16(ga, pack_k8(E[nt][2 * ks], E[nt][2 * ks + 1]), Dv[nt]);
+        }
+        const int a0 = 16 * at + 4 * g;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int j = t0 + 16 * nt + l16;
+          if (j < L) st_bf16x4(dV + base + static_cast<size_t>(j) * kD + a0, Dv[nt][0], Dv[nt][1], Dv[nt][2], Dv[nt][3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bqr: the query side with its per-head operands resident in LDS, in three
+// passes that each rebuild the query features Q~ (cheaper than the operand
+// traffic of one pass holding every operand).  grid (BH * nqb), 256 threads;
+// work-group (bh, qb) takes queries [qb qblk, (qb+1) qblk) in steps of 128,
+// wave w owning queries 32w..32w+31 of a step (two 16-query column tiles).
+//   MODE 0: [num | den] = Q~ [S~ | z~] (state hi + lo) -> ru[i] = (1/den~_i, u0_i)
+//           (operands W' and KzT: 112 KB)
+//   MODE 1: T = S~ dO / den~ + z~ u0 (state hi + lo), P = Q~ T, dq = P W -
+//           2 knorm (sum_r P) q (operands W', KzF, W^T: 128 KB)
+//   MODE 2: G += Q~^T Ucat over the step's 128 queries (Ucat hi + lo), the
+//           block's partial written at the end (operand W' and the step's
+//           Q~^T / Ucat^T tiles: 144 KB at m = 256)
+// ---------------------------------------------------------------------------
+template <int M, bool RELU, int MODE>
+__global__ __launch_bounds__(256, 1) void bqr(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
+    const _Float16* __restrict__ W16, const uint16_t* __restrict__ WT,
+    const uint16_t* __restrict__ KzT, const uint16_t* __restrict__ KzF,
+    const float* __restrict__ zf, const float* __restrict__ cf, float* __restrict__ ru,
+    uint16_t* __restrict__ dQ, float* __restrict__ Gp, int L, int qblk, int nqb, float knorm) {
+  constexpr int FT = M / 16;
+  constexpr int KF = M / 32;
+  constexpr int GFT = M / 64;
+  constexpr int kStep = 128;
+  constexpr int kTRow = kStep + 8;
+  const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int l16 = lane % 16, g = lane / 16;
+  extern __shared__ __align__(16) uint16_t lds[];
+  uint16_t* Wl = lds;                       // W' [M][64]
+  uint16_t* Xl = lds + M * kD;              // MODE 0: KzT hi, lo [160][M]; MODE 1: KzF hi, lo
+                                            // [2M][64] then W^T [64][M]; MODE 2: QT, UT
+  stage_swz<kD>(reinterpret_cast<const uint16_t*>(W16), Wl, M);
+  if constexpr (MODE == 0) {
+    stage_swz<M>(KzT + static_cast<size_t>(bh) * 160 * M, Xl, 160);
+  } else if constexpr (MODE == 1) {
+    stage_swz<kD>(KzF + static_cast<size_t>(bh) * 2 * M * kD, Xl, 2 * M);
+    stage_swz<M>(WT, Xl + 2 * M * kD, kD);
+  } else {
+    // rows 65..79 of both Ucat^T halves are zero
+    uint16_t* UT = Xl + M * kTRow;
+    for (int i = tid; i < 2 * 15 * kTRow; i += 256) {
+      const int h = i / (15 * kTRow), r = i % (15 * kTRow);
+      UT[(h * 80 + 65 + r / kTRow) * kTRow + r % kTRow] = 0;
     }
   }
   __syncthreads();
-  const int tl = 16 * wave + l16;
-  const bool live = t0 + tl < L;
-  // (1) E^T = W' K^T - n - c (rows: features; column: key tl), K~ = exp2(E).
-  f32x4 E[FT];
-  const float ntok = nk[tl];
+
+  const size_t base = static_cast<size_t>(bh) * L * kD;
+  const float* cfh = cf + static_cast<size_t>(bh) * M;
+  const float* zfh = zf + static_cast<size_t>(bh) * M;
+  float* ruh = ru + static_cast<size_t>(bh) * L * 2;
+  f32x4 G[MODE == 2 ? GFT : 1][5];
+  if constexpr (MODE == 2) {
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    E[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < GFT; ++a)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      E[ft] = mma_f16(ld_f16x8(W16 + (16 * ft + l16) * kD + 32 * ks + 8 * g),
-                      ld_f16x8(&Ks[tl][32 * ks + 8 * g]), E[ft]);
-    if constexpr (!RELU) {
-      const float4 c4 = *reinterpret_cast<const float4*>(cfh + 16 * ft + 4 * g);
-      E[ft][0] -= ntok + c4.x; E[ft][1] -= ntok + c4.y;
-      E[ft][2] -= ntok + c4.z; E[ft][3] -= ntok + c4.w;
-    }
-#pragma unroll
-    for (int v = 0; v < 4; ++v) E[ft][v] = feature<RELU>(E[ft][v]);
-    st_bf16x4(&KF_[tl][16 * ft + 4 * g], E[ft][0], E[ft][1], E[ft][2], E[ft][3]);
+      for (int c = 0; c < 5; ++c) G[a][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // (2) H^T = G V^T + Gz (rows: features; column: key tl), R = K~ H.
-  float rsum = 0.f;
+  const int i_beg = qb * qblk, i_end = min(L, i_beg + qblk);
+  for (int s0 = i_beg; s0 < i_end; s0 += kStep) {
+    const int t0 = s0 + 32 * wave;
+    // Query fragments (B operands, k = d) as fp16.
+    f16x8 qf[2][2];
 #pragma unroll
-  for (int ft = 0; ft < FT; ++ft) {
-    f32x4 H = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 2; ++nt) {
+      const int i = t0 + 16 * nt + l16;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 vb = ld_bf16x8(&Vs[tl][32 * ks + 8 * g]);
-      H = mma_bf16(ld_bf16x8(gf + (16 * ft + l16) * kD + 32 * ks + 8 * g), vb, H);
-      H = mma_bf16(ld_bf16x8(gf + (M + 16 * ft + l16) * kD + 32 * ks + 8 * g), vb, H);
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 u = make_uint4(0u, 0u, 0u, 0u);
+        if (i < L) u = *reinterpret_cast<const uint4*>(Q + base + static_cast<size_t>(i) * kD + 32 * ks + 8 * g);
+        qf[nt][ks] = __builtin_bit_cast(f16x8, make_uint4(bf16x2_to_f16x2(u.x), bf16x2_to_f16x2(u.y),
+                                                         bf16x2_to_f16x2(u.z), bf16x2_to_f16x2(u.w)));
+      }
     }
-    const float4 z4 = *reinterpret_cast<const float4*>(gz + 16 * ft + 4 * g);
-    const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
-    float r[4];
+    // (1) S^T = W' Q^T + c; Q~ = exp2(S - M) with the row reference M (the
+    // same arithmetic in every pass, so every pass rebuilds the same Q~).
+    f32x4 S[2][FT];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float hv = H[v] + zz[v];
-      r[v] = RELU ? (E[ft][v] > 0.f ? hv : 0.f) : E[ft][v] * hv;
-      rsum += r[v];
+    for (int ft = 0; ft < FT; ++ft) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) S[nt][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f16x8 wa = *reinterpret_cast<const f16x8*>(Wl + swz<kD>(16 * ft + l16, 32 * ks + 8 * g));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) S[nt][ft] = mma_f16(wa, qf[nt][ks], S[nt][ft]);
+      }
+      if constexpr (!RELU) {
+        const float4 c4 = *reinterpret_cast<const float4*>(cfh + 16 * ft + 4 * g);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          S[nt][ft][0] += c4.x; S[nt][ft][1] += c4.y; S[nt][ft][2] += c4.z; S[nt][ft][3] += c4.w;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    st_bf16x4(&RF[tl][16 * ft + 4 * g], r[0], r[1], r[2], r[3]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float Mrow = 0.f;
+      if constexpr (!RELU) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+          mx = fmaxf(mx, max3(S[nt][ft][0], S[nt][ft][1], fmaxf(S[nt][ft][2], S[nt][ft][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        Mrow = mx;
+      }
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) S[nt][ft][v] = feature<RELU>(S[nt][ft][v] - Mrow);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    if constexpr (MODE == 0) {
+      // (2) [num | den]^T = KzT Q~^T (hi + lo); den, dO . num -> (1/den, u0).
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int i = t0 + 16 * nt + l16;
+        f32x4 N[5];
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct) {
+          N[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KF; ++ks) {
+            const bf16x8 qb8 = pack_k8(S[nt][2 * ks], S[nt][2 * ks + 1]);
+            N[ct] = mma_bf16(*reinterpret_cast<const bf16x8*>(Xl + swz<M>(16 * ct + l16, 32 * ks + 8 * g)), qb8, N[ct]);
+            N[ct] = mma_bf16(*reinterpret_cast<const bf16x8*>(Xl + swz<M>(80 + 16 * ct + l16, 32 * ks + 8 * g)), qb8, N[ct]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const float den = __shfl(N[4][0], l16);
+        float dot = 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          float dv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (i < L) ld_bf16x4(dO + base + static_cast<size_t>(i) * kD + 16 * ct + 4 * g, dv);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) dot = fmaf(dv[v], N[ct][v], dot);
+        }
+        dot += __shfl_xor(dot, 16);
+        dot += __shfl_xor(dot, 32);
+        if (g == 0 && i < L) {
+          const float rden = 1.f / den;
+          *reinterpret_cast<float2*>(ruh + 2 * static_cast<size_t>(i)) = make_float2(rden, -dot * rden * rden);
+        }
+      }
+    } else if constexpr (MODE == 1) {
+      // (3) T^T = S~ dO^T / den + z~ u0 (hi + lo), P = Q~ T in place of Q~.
+      const uint16_t* Kl = Xl;                 // KzF hi, lo [2M][64]
+      const uint16_t* Tl = Xl + 2 * M * kD;    // W^T [64][M]
+      bf16x8 df[2][2];
+      float rden[2], u0[2], psum[2] = {0.f, 0.f};
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int i = t0 + 16 * nt + l16;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          uint4 u = make_uint4(0u, 0u, 0u, 0u);
+          if (i < L) u = *reinterpret_cast<const uint4*>(dO + base + static_cast<size_t>(i) * kD + 32 * ks + 8 * g);
+          df[nt][ks] = __builtin_bit_cast(bf16x8, u);
+        }
+        float2 r2 = make_float2(0.f, 0.f);
+        if (i < L) r2 = *reinterpret_cast<const float2*>(ruh + 2 * static_cast<size_t>(i));
+        rden[nt] = r2.x;
+        u0[nt] = r2.y;
+      }
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        f32x4 T[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const bf16x8 hi = *reinterpret_cast<const bf16x8*>(Kl + swz<kD>(16 * ft + l16, 32 * ks + 8 * g));
+          const bf16x8 lo = *reinterpret_cast<const bf16x8*>(Kl + swz<kD>(M + 16 * ft + l16, 32 * ks + 8 * g));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            T[nt] = mma_bf16(hi, df[nt][ks], T[nt]);
+            T[nt] = mma_bf16(lo, df[nt][ks], T[nt]);
+          }
+        }
+        const float4 z4 = *reinterpret_cast<const float4*>(zfh + 16 * ft + 4 * g);
+        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float tv = fmaf(zz[v], u0[nt], T[nt][v] * rden[nt]);
+            const float p = RELU ? (S[nt][ft][v] > 0.f ? tv : 0.f) : S[nt][ft][v] * tv;
+            S[nt][ft][v] = p;
+            psum[nt] += p;
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        psum[nt] += __shfl_xor(psum[nt], 16);
+        psum[nt] += __shfl_xor(psum[nt], 32);
+      }
+      // (4) dq^T = W^T P^T - 2 knorm (sum_r P) q.
+#pragma unroll
+      for (int at = 0; at < 4; ++at) {
+        f32x4 Dq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int ks = 0; ks < KF; ++ks) {
+          const bf16x8 wa = *reinterpret_cast<const bf16x8*>(Tl + swz<M>(16 * at + l16, 32 * ks + 8 * g));
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) Dq[nt] = mma_bf16(wa, pack_k8(S[nt][2 * ks], S[nt][2 * ks + 1]), Dq[nt]);
+        }
+        const int a0 = 16 * at + 4 * g;
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int i = t0 + 16 * nt + l16;
+          if (i < L) {
+            float qv[4];
+            ld_bf16x4(Q + base + static_cast<size_t>(i) * kD + a0, qv);
+            float o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              o[v] = RELU ? Dq[nt][v] * kLog2e : fmaf(-2.f * knorm * psum[nt], qv[v], Dq[nt][v]);
+            st_bf16x4(dQ + base + static_cast<size_t>(i) * kD + a0, o[0], o[1], o[2], o[3]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // (5) Q~^T and Ucat^T (hi, lo) of the step's 128 queries into LDS, then
+      // G (this wave's feature rows) += Q~^T Ucat.
+      uint16_t* QT = Xl;                    // [M][kTRow]
+      uint16_t* UT = Xl + M * kTRow;        // [2][80][kTRow]
+      __syncthreads();                      // the previous step's reads are done
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int il = 32 * wave + 16 * nt + l16, i = s0 + il;
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) QT[(16 * ft + 4 * g + v) * kTRow + il] = bf16_bits(S[nt][ft][v]);
+        float2 r2 = make_float2(0.f, 0.f);
+        if (i < L) r2 = *reinterpret_cast<const float2*>(ruh + 2 * static_cast<size_t>(i));
+        auto put = [&](int row, float x) {
+          const uint16_t hi = bf16_bits(x);
+          UT[row * kTRow + il] = hi;
+          UT[(80 + row) * kTRow + il] = bf16_bits(x - __uint_as_float(static_cast<uint32_t>(hi) << 16));
+        };
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          float dv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (i < L) ld_bf16x4(dO + base + static_cast<size_t>(i) * kD + 16 * ct + 4 * g, dv);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) put(16 * ct + 4 * g + v, dv[v] * r2.x);
+        }
+        if (g == 0) put(64, r2.y);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int a = 0; a < GFT; ++a) {
+        const int f = wave * (M / 4) + 16 * a + l16;
+#pragma unroll
+        for (int ks = 0; ks < kStep / 32; ++ks) {
+          const bf16x8 qa = *reinterpret_cast<const bf16x8*>(QT + f * kTRow + 32 * ks + 8 * g);
+#pragma unroll
+          for (int ct = 0; ct < 5; ++ct) {
+            G[a][ct] = mma_bf16(qa, *reinterpret_cast<const bf16x8*>(UT + (16 * ct + l16) * kTRow + 32 * ks + 8 * g), G[a][ct]);
+            G[a][ct] = mma_bf16(qa, *reinterpret_cast<const bf16x8*>(UT + (80 + 16 * ct + l16) * kTRow + 32 * ks + 8 * g), G[a][ct]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
-  rsum += __shfl_xor(rsum, 16);
-  rsum += __shfl_xor(rsum, 32);
-  __syncthreads();
-  // (3) dk^T = W^T R^T - 2 knorm (sum_r R) k; (4) dv^T = G^T K~^T (every lane
-  // takes part in the products; only live keys are stored).
+  if constexpr (MODE == 2) {
+    float* gp = Gp + (static_cast<size_t>(bh) * nqb + qb) * M * (kD + 1);
 #pragma unroll
-  for (int at = 0; at < 4; ++at) {
-    f32x4 Dk = f32x4{0.f, 0.f, 0.f, 0.f}, Dv = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int a = 0; a < GFT; ++a)
 #pragma unroll
-    for (int ks = 0; ks < KF; ++ks) {
-      Dk = mma_bf16(ld_bf16x8(WT + (16 * at + l16) * M + 32 * ks + 8 * g),
-                    ld_bf16x8(&RF[tl][32 * ks + 8 * g]), Dk);
-      Dv = mma_bf16(ld_bf16x8(gt + (16 * at + l16) * M + 32 * ks + 8 * g),
-                    ld_bf16x8(&KF_[tl][32 * ks + 8 * g]), Dv);
-    }
-    const int a0 = 16 * at + 4 * g;
-    float o[4];
+      for (int ct = 0; ct < 5; ++ct) {
+        const int c = 16 * ct + l16;
+        if (c > kD) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float kv = static_cast<float>(Ks[tl][a0 + v]);
-      o[v] = RELU ? Dk[v] * kLog2e : fmaf(-2.f * knorm * rsum, kv, Dk[v]);
-    }
-    if (live) {
-      const size_t row = base + static_cast<size_t>(t0 + tl) * kD + a0;
-      st_bf16x4(dK + row, o[0], o[1], o[2], o[3]);
-      st_bf16x4(dV + row, Dv[0], Dv[1], Dv[2], Dv[3]);
-    }
+        for (int v = 0; v < 4; ++v) {
+          const int f = wave * (M / 4) + 16 * a + 4 * g + v;
+          gp[static_cast<size_t>(f) * (kD + 1) + c] = G[a][ct][v];
+        }
+      }
   }
 }
 
@@ -569,23 +692,66 @@ hipError_t launch_bwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const 
   e = hipGetLastError();
   timing_after(st, "bcombine");
   if (e != hipSuccess) return e;
-  timing_before(st);
-  bquery<M, RELU><<<dim3(p.BH * b.nqb), 256, 0, st>>>(Q, dO, W16, WT, KzT, KzF, zf, cf, dQ, Gp,
-                                                       p.L, b.qblk, b.nqb, p.knorm);
-  e = hipGetLastError();
-  timing_after(st, "bquery");
-  if (e != hipSuccess) return e;
+  auto* ru = reinterpret_cast<float*>(ws + b.off_ru);
+  {
+    constexpr int kq0 = (M * kD + 160 * M) * 2;
+    constexpr int kq1 = (M * kD + 2 * M * kD + kD * M) * 2;
+    constexpr int kq2 = (M * kD + M * 136 + 160 * 136) * 2;
+    const void* fns[3] = {reinterpret_cast<const void*>(&bqr<M, RELU, 0>),
+                          reinterpret_cast<const void*>(&bqr<M, RELU, 1>),
+                          reinterpret_cast<const void*>(&bqr<M, RELU, 2>)};
+    const int lds[3] = {kq0, kq1, kq2};
+    for (int i = 0; i < 3; ++i) {
+      e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
+      if (e != hipSuccess) return e;
+    }
+    const dim3 grid(p.BH * b.nqb);
+    timing_before(st);
+    bqr<M, RELU, 0><<<grid, 256, kq0, st>>>(Q, dO, W16, WT, KzT, KzF, zf, cf, ru, dQ, Gp, p.L,
+                                            b.qblk, b.nqb, p.knorm);
+    e = hipGetLastError();
+    timing_after(st, "bq_den");
+    if (e != hipSuccess) return e;
+    timing_before(st);
+    bqr<M, RELU, 1><<<grid, 256, kq1, st>>>(Q, dO, W16, WT, KzT, KzF, zf, cf, ru, dQ, Gp, p.L,
+                                            b.qblk, b.nqb, p.knorm);
+    e = hipGetLastError();
+    timing_after(st, "bq_dq");
+    if (e != hipSuccess) return e;
+    timing_before(st);
+    bqr<M, RELU, 2><<<grid, 256, kq2, st>>>(Q, dO, W16, WT, KzT, KzF, zf, cf, ru, dQ, Gp, p.L,
+                                            b.qblk, b.nqb, p.knorm);
+    e = hipGetLastError();
+    timing_after(st, "bq_g");
+    if (e != hipSuccess) return e;
+  }
   timing_before(st);
   gcombine<<<dim3((M * (kD + 1) + 255) / 256, p.BH), 256, 0, st>>>(Gp, GF, GT, Gz, M, b.nqb);
   e = hipGetLastError();
   timing_after(st, "gcombine");
   if (e != hipSuccess) return e;
-  const int ntile = (p.L + kTok - 1) / kTok;
-  timing_before(st);
-  bkey<M, RELU><<<dim3(p.BH * ntile), 256, 0, st>>>(K, V, W16, WT, GF, GT, Gz, cf, dK, dV, p.L,
-                                                     ntile, p.knorm);
-  e = hipGetLastError();
-  timing_after(st, "bkey");
+  {
+    auto* k0 = &bkeyr<M, RELU, 0>;
+    auto* k1 = &bkeyr<M, RELU, 1>;
+    const int lds0 = 4 * M * kD * 2, lds1 = 2 * M * kD * 2;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k0),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds0);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(k1),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds1);
+    if (e != hipSuccess) return e;
+    timing_before(st);
+    k0<<<dim3(p.BH * b.nkb), 256, lds0, st>>>(K, V, W16, WT, GF, GT, Gz, cf, dK, dV, p.L, b.kblk,
+                                              b.nkb, p.knorm);
+    e = hipGetLastError();
+    timing_after(st, "bkey_dk");
+    if (e != hipSuccess) return e;
+    timing_before(st);
+    k1<<<dim3(p.BH * b.nkb), 256, lds1, st>>>(K, V, W16, WT, GF, GT, Gz, cf, dK, dV, p.L, b.kblk,
+                                              b.nkb, p.knorm);
+    e = hipGetLastError();
+    timing_after(st, "bkey_dv");
+  }
   return e;
 }
 
