@@ -209,8 +209,11 @@ int favor_prefill_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, in
  * favor_fwd_attn with causal = 1) where token i attends to the carried
  * tokens of state_in and to the new tokens j <= i.  state_in (NULL: empty)
  * and state_out (NULL: not written) are states as above and may not alias;
- * state_out receives the state after the last new token.  Runs on the fp32
- * FMA kernels for every shape and dtype.  Workspace of at least
+ * state_out receives the state after the last new token.  A fresh prefill
+ * (state_in NULL) of bf16 inputs with d = 64 and m a multiple of 64 up to
+ * 256 runs on the matrix cores (the causal forward, and the final state as
+ * the sum over every key); every other case on the fp32 FMA kernels.
+ * Workspace of at least
  * favor_prefill_workspace_bytes() bytes, 256-byte aligned.  Errors as
  * favor_fwd_attn.
  */

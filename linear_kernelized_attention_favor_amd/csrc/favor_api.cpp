@@ -103,6 +103,23 @@ int backward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtyp
 // causal kernels costs O(segment) per token).
 constexpr int32_t kPrefillSeg = 64;
 
+// A fresh prefill (no carried state) on the matrix cores: the causal forward's
+// plan, then the bidirectional key partials (the final state is the sum over
+// every key) at the next 256-byte boundary.  False when the shape is not
+// covered (the generic kernels run it).
+bool mfma_prefill_plans(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                        Plan* pc, Plan* pb, size_t* off_b, size_t* bytes) {
+  if (!mfma_causal_supported(d, m, dtype) || !mfma_bidir_supported(d, m, dtype) || d != 64 ||
+      m > 256)
+    return false;
+  make_plan(B, H, L, d, m, dtype, 1, pc);
+  make_plan(B, H, L, d, m, dtype, 0, pb);
+  if (pc->path != kPathMfma || pb->path != kPathMfma) return false;
+  *off_b = align256(pc->bytes);
+  *bytes = *off_b + pb->bytes;
+  return true;
+}
+
 // Incremental causal state: shape checks shared by its entry points.
 int check_state(int32_t B, int32_t H, int32_t d, int32_t m, int32_t attn_kernel) {
   const int st = check_shape(B, H, 1, d, m, FAVOR_F32);
@@ -348,7 +365,12 @@ int favor_prefill_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, in
   if (!bytes) return FAVOR_ERR_NULL;
   favor::Plan p;
   favor::make_generic_only_plan(B, H, L, d, m, dtype, 1, favor::kPrefillSeg, &p);
-  *bytes = p.bytes;
+  size_t need = p.bytes;
+  favor::Plan pc, pb;
+  size_t off_b = 0, mb = 0;
+  if (favor::mfma_prefill_plans(B, H, L, d, m, dtype, &pc, &pb, &off_b, &mb) && mb > need)
+    need = mb;
+  *bytes = need;
   return FAVOR_OK;
 }
 
@@ -367,9 +389,28 @@ int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t
   if (!favor::is_aligned(workspace, 256)) return FAVOR_ERR_ALIGN;
   favor::Plan p;
   favor::make_generic_only_plan(B, H, L, d, m, dtype, 1, favor::kPrefillSeg, &p);
-  if (workspace_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
+  size_t need = 0;
+  if (favor_prefill_workspace_bytes(B, H, L, d, m, dtype, &need) != FAVOR_OK) return FAVOR_ERR_SHAPE;
+  if (workspace_bytes < need) return FAVOR_ERR_WORKSPACE;
   p.knorm = knorm;
   p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
+  favor::Plan pc, pb;
+  size_t off_b = 0, mb = 0;
+  if (!state_in && favor::mfma_prefill_plans(B, H, L, d, m, dtype, &pc, &pb, &off_b, &mb)) {
+    // A fresh prefill on the matrix cores: the causal forward, then (if the
+    // state is wanted) the final state as the sum over every key.
+    pc.knorm = pb.knorm = knorm;
+    pc.relu = pb.relu = p.relu;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = favor::mfma_causal_forward(pc, Q, K, V, W, O, workspace, st);
+    if (e == hipSuccess && state_out) {
+      char* wb = static_cast<char*>(workspace) + off_b;
+      e = favor::mfma_bidir_key_partials(pb, K, V, W, wb, st);
+      if (e == hipSuccess) e = favor::mfma_state_export(pb, wb, state_out, st);
+    }
+    if (e != hipSuccess) return favor::fail_hip(e);
+    return FAVOR_OK;
+  }
   const hipError_t e = favor::generic_prefill(p, Q, K, V, W, O, state_in, state_out, workspace,
                                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return favor::fail_hip(e);

@@ -108,6 +108,9 @@ bool mfma_bwd_supported(int32_t d, int32_t m, int32_t dtype, int32_t causal);
 hipError_t mfma_backward(const Plan& p, const BwdPlan& b, const void* Q, const void* K,
                          const void* V, const float* W, const void* dO, void* dQ, void* dK,
                          void* dV, void* ws, hipStream_t stream);
+// The exported causal state after every key (fp32 [BH][m][d+4], natural-log
+// references) from the bidirectional key partials in `ws` (plan p).
+hipError_t mfma_state_export(const Plan& p, const void* ws, float* state, hipStream_t stream);
 // The bidirectional matrix-core path's key partials alone (kpart).
 hipError_t mfma_bidir_key_partials(const Plan& p, const void* K, const void* V, const float* W,
                                    void* ws, hipStream_t stream);

@@ -755,7 +755,53 @@ hipError_t launch_bwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const 
   return e;
 }
 
+// ---------------------------------------------------------------------------
+// sexport: the causal state after every key of the sequence -- the sum over
+// all keys, i.e. the bidirectional key state -- from the splits' partials, in
+// the exported layout [BH][m][d+4]: [S~ | z~ | c | 0 | 0] with c in natural-log
+// units (the features here are exp2 of log2-unit exponents, the same values;
+// ReLU features here are max(w' . k, 0) = log2(e) max(w . k, 0), so the state
+// is scaled back by ln 2).
+// grid (ceil(m/64), BH), 256 threads: 64 features x 4 column groups.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void sexport(const float* __restrict__ P,
+                                               const float* __restrict__ cs,
+                                               float* __restrict__ st, int m, int nseg,
+                                               int relu) {
+  const int bh = blockIdx.y;
+  const int fl = threadIdx.x % 64, cg = threadIdx.x / 64;
+  const int f = blockIdx.x * 64 + fl;
+  if (f >= m) return;
+  const size_t cb = static_cast<size_t>(bh) * nseg * m + f;
+  float cm = -INFINITY;
+  for (int s = 0; s < nseg; ++s) cm = fmaxf(cm, cs[cb + static_cast<size_t>(s) * m]);
+  float* row = st + (static_cast<size_t>(bh) * m + f) * (kD + 4);
+  for (int c = cg; c <= kD; c += 4) {
+    float acc = 0.f;
+    for (int s = 0; s < nseg; ++s)
+      acc = fmaf(P[((static_cast<size_t>(bh) * nseg + s) * (kD + 1) + c) * m + f],
+                 fast_exp2(cs[cb + static_cast<size_t>(s) * m] - cm), acc);
+    row[c] = relu ? acc * 0.6931471805599453f : acc;
+  }
+  if (cg == 0) {
+    row[kD + 1] = cm * 0.6931471805599453f;
+    row[kD + 2] = 0.f;
+    row[kD + 3] = 0.f;
+  }
+}
+
 }  // namespace
+
+hipError_t mfma_state_export(const Plan& p, const void* ws, float* state, hipStream_t stream) {
+  const char* w = static_cast<const char*>(ws);
+  timing_before(stream);
+  sexport<<<dim3((p.m + 63) / 64, p.BH), 256, 0, stream>>>(
+      reinterpret_cast<const float*>(w + p.off_T), reinterpret_cast<const float*>(w + p.off_cseg),
+      state, p.m, p.nseg, p.relu);
+  const hipError_t e = hipGetLastError();
+  timing_after(stream, "sexport");
+  return e;
+}
 
 bool mfma_bwd_supported(int32_t d, int32_t m, int32_t dtype, int32_t causal) {
   return dtype == FAVOR_BF16 && !causal && d == kD && (m == 64 || m == 128 || m == 192 ||

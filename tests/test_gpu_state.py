@@ -4,8 +4,10 @@ and its running state (oracle.causal_state).
 
 Outputs: per-row relative error as in the forward's parity tests (1e-4 for
 fp32 inputs, 2e-2 for bf16).  States: the true state exp(c) [S~ | z~] / sqrt(m)
-against the oracle's (S, z) per head, max abs error over the largest entry,
-1e-4 for both dtypes (the state is fp32 arithmetic on the same input values).
+against the oracle's (S, z) per head, max abs error over the largest entry:
+1e-4 where the state is fp32 arithmetic on the same input values (the generic
+kernels, either dtype), 1e-2 where a fresh bf16 prefill runs on the matrix
+cores (features rounded to bf16 as the products' operands).
 """
 import math
 
@@ -61,6 +63,12 @@ def _state_err(st, K, V, W, kernel):
     return float(np.max(np.abs(got - ref).max(axis=(-1, -2)) / np.abs(ref).max(axis=(-1, -2))))
 
 
+def _state_tol(shape, dtype, fresh=True):
+    d, m = shape[3], shape[4]
+    mfma = fresh and dtype == "bf16" and d == 64 and m % 64 == 0 and m <= 256
+    return 1e-2 if mfma else 1e-4
+
+
 def _ref_out(q, k, v, W, kernel):
     return oracle.causal(_np64(q), _np64(k), _np64(v), W.astype(np.float64), kernel)
 
@@ -84,7 +92,7 @@ def test_prefill_output_and_state(fv, shape, dtype, kernel):
     o, st = fv.prefill(q.cuda(), k.cuda(), v.cuda(), Wd, kernel=kernel)
     torch.cuda.synchronize()
     assert oracle.row_rel_err(_np64(o), _ref_out(q, k, v, W, kernel)) <= TOL[dtype]
-    assert _state_err(st, k, v, W, kernel) <= 1e-4
+    assert _state_err(st, k, v, W, kernel) <= _state_tol(shape, dtype)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -103,8 +111,10 @@ def test_chunked_prefill_continues_the_state(fv, dtype, kernel):
     ref = _ref_out(q, k, v, W, kernel)
     assert oracle.row_rel_err(_np64(o1), ref[:, :, :cut]) <= TOL[dtype]
     assert oracle.row_rel_err(_np64(o2), ref[:, :, cut:]) <= TOL[dtype]
-    assert _state_err(st1, k[:, :, :cut], v[:, :, :cut], W, kernel) <= 1e-4
-    assert _state_err(st2, k, v, W, kernel) <= 1e-4
+    assert _state_err(st1, k[:, :, :cut], v[:, :, :cut], W, kernel) <= _state_tol(shape, dtype)
+    # (the second call continues a state: generic kernels, on the first
+    # call's state, so the first call's error carries over)
+    assert _state_err(st2, k, v, W, kernel) <= _state_tol(shape, dtype)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -125,7 +135,7 @@ def test_decode_continues_prefill(fv, dtype, kernel):
     got = torch.stack(outs, 2)
     ref = _ref_out(q, k, v, W, kernel)[:, :, L0:]
     assert oracle.row_rel_err(_np64(got), ref) <= TOL[dtype]
-    assert _state_err(st, k, v, W, kernel) <= 1e-4
+    assert _state_err(st, k, v, W, kernel) <= _state_tol(shape, dtype)
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
