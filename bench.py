@@ -73,14 +73,18 @@ def parse():
     return ap.parse_args()
 
 
+# The sources the forward pass's counted kernels are compiled from: a change
+# to any of them voids the committed counter summary.
+FORWARD_SOURCES = ("kernels_mfma.hip", "mfma_common.h", "favor_internal.h")
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_kernelized_attention_favor_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".cpp", ".h")):
-            h.update(f.encode())
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+    for f in sorted(FORWARD_SOURCES):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -231,18 +235,26 @@ def copy_calibration(steps: int):
 
 
 FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "g_state",
-                 "g_combine", "g_apply")
+                 "g_combine", "g_apply", "gb_query", "gb_gstate", "gb_gcombine", "gb_key",
+                 "bprep", "bcombine", "bqr", "gcombine", "bkeyr", "sexport", "g_decode",
+                 "g_state_reset", "draw_block", "g_feature_map")
+# passes of the templated backward kernels, by their last template argument
+_PASSES = {"bqr": ("bq_den", "bq_dq", "bq_g"), "bkeyr": ("bkey_dk", "bkey_dv")}
 
 
 def _favor_kernel(name: str):
     """Short name of a libfavor kernel from a demangled or mangled symbol, else None."""
     import re
-    m = re.search(r"favor::\(anonymous namespace\)::(\w+)<", name)
+    m = re.search(r"favor::\(anonymous namespace\)::(\w+)(?:<([^>]*)>)?\(", name)
     if m:
-        k = m.group(1)
+        k, targs = m.group(1), m.group(2) or ""
+        mode = re.search(r"(\d+)\s*$", targs)
     else:   # _ZN5favor12_GLOBAL__N_1<len><name>I...
         m = re.search(r"_ZN5favor12_GLOBAL__N_1(\d+)", name)
         k = name[m.end():m.end() + int(m.group(1))] if m else None
+        mode = re.search(r"ELi(\d+)EE", name[m.end():]) if m else None
+    if k in _PASSES and mode is not None:
+        return _PASSES[k][int(mode.group(1))]
     return k if k in FAVOR_KERNELS else None
 
 
