@@ -212,3 +212,44 @@ def test_backward_text_shape_sampled(fv, causal):
             err = grad_err(_np64(g[h])[None], r[None])
             print(f"backward {w.name} head {h} {name}: {err:.3e}", flush=True)
             assert err <= TOL["bf16"], (h, name, err)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_workspace_reuse_and_garbage(fv, causal):
+    # Whatever the workspace holds before a call must not change the result.
+    q, k, v, do, W = _case((2, 2, 700, 64, 256), "bf16", 91 + causal, "softmax")
+    qd, kd, vd, dd = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    Wd = torch.from_numpy(W).cuda()
+    ref = fv.bwd(qd, kd, vd, Wd, dd, causal=causal)
+    need = fv.bwd_workspace_bytes(2, 2, 700, 64, 256, fv.BF16, causal)
+    for fill in (0x00, 0xFF, 0x7F):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        for _ in range(2):
+            got = fv.bwd(qd, kd, vd, Wd, dd, causal=causal, workspace=ws)
+            torch.cuda.synchronize()
+            for a, b in zip(got, ref):
+                assert torch.equal(a, b), fill
+
+
+def test_backward_graph_replays_match_eager(fv):
+    # The matrix-core backward captured once and replayed on new inputs.
+    shape = (1, 4, 1500, 64, 256)
+    cases = [[x.cuda() for x in _case(shape, "bf16", 100 + i, "softmax")[:4]] for i in range(3)]
+    W = torch.from_numpy(_case(shape, "bf16", 100, "softmax")[4]).cuda()
+    qs, ks, vs, ds = (x.clone() for x in cases[0])
+    ws = torch.zeros(fv.bwd_workspace_bytes(1, 4, 1500, 64, 256, fv.BF16, False),
+                     dtype=torch.uint8, device="cuda")
+    outs = tuple(torch.empty_like(qs) for _ in range(3))
+    fv.bwd(qs, ks, vs, W, ds, out=outs, workspace=ws)   # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fv.bwd(qs, ks, vs, W, ds, out=outs, workspace=ws)
+    for q, k, v, d in cases[1:] + cases[:1]:
+        qs.copy_(q); ks.copy_(k); vs.copy_(v); ds.copy_(d)
+        g.replay()
+        torch.cuda.synchronize()
+        eager = fv.bwd(q, k, v, W, d)
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b)

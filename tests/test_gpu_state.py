@@ -187,3 +187,31 @@ def test_decode_large_offsets_stay_finite(fv):
     ref = oracle.causal(q.astype(np.float64), k.astype(np.float64), v.astype(np.float64),
                         W.astype(np.float64))
     assert oracle.row_rel_err(_np64(got), ref) <= TOL["f32"]
+
+
+def test_decode_graph_replays_match_eager(fv):
+    # One decode step captured in a HIP graph and replayed token after token
+    # (the serving loop's form) follows the eager steps on a second state.
+    B, H, L, d, m = 2, 3, 12, 64, 256
+    q, k, v, W = _case((B, H, L, d, m), "bf16", 41)
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    st_g = fv.state_new(B, H, d, m)
+    st_e = fv.state_new(B, H, d, m)
+    qs, ks, vs = (x[:, :, 0].contiguous() for x in (qc, kc, vc))
+    out = torch.empty_like(qs)
+    g = torch.cuda.CUDAGraph()
+    warm = fv.state_new(B, H, d, m)
+    fv.decode(qs, ks, vs, Wd, warm, out=out)          # warm-up outside the capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fv.decode(qs, ks, vs, Wd, st_g, out=out)
+    for t in range(L):
+        qs.copy_(qc[:, :, t]); ks.copy_(kc[:, :, t]); vs.copy_(vc[:, :, t])
+        g.replay()
+        torch.cuda.synchronize()
+        e = fv.decode(qc[:, :, t].contiguous(), kc[:, :, t].contiguous(), vc[:, :, t].contiguous(),
+                      Wd, st_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out, e), t
+        assert torch.equal(st_g, st_e), t
