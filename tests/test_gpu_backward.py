@@ -194,9 +194,19 @@ def test_backward_bitwise_deterministic(fv, causal):
         assert torch.equal(x, y)
 
 
-@pytest.mark.parametrize("causal", [False, True])
-def test_backward_text_shape_sampled(fv, causal):
-    w = workloads.workload("text_causal" if causal else "text_bidir")
+FULL_BWD = [("text_bidir", False), ("text_causal", True), ("protein_long", False),
+            ("wide_many", False)]
+
+
+@pytest.mark.parametrize("name,causal", FULL_BWD,
+                         ids=[f"{n}-{'causal' if c else 'bidir'}" for n, c in FULL_BWD])
+def test_backward_full_size_sampled(fv, name, causal):
+    # The whole workload's backward on the GPU (matrix cores for the d = 64
+    # bidirectional shapes, generic kernels for the causal and d = 128 ones);
+    # the first and last heads against the oracle.
+    w = workloads.workload(name)
+    if causal:
+        w = w.with_(causal=True)
     torch.manual_seed(0)
     q, k, v = workloads.device_qkv(w)
     do = torch.randn_like(q, dtype=torch.float32).to(q.dtype)
@@ -208,10 +218,10 @@ def test_backward_text_shape_sampled(fv, causal):
     gf = [g.reshape(shp) for g in got]
     for h in (0, w.heads - 1):
         ref = _oracle(qf[h], kf[h], vf[h], W, df[h], causal, "softmax")
-        for name, g, r in zip(("dQ", "dK", "dV"), gf, ref):
+        for gname, g, r in zip(("dQ", "dK", "dV"), gf, ref):
             err = grad_err(_np64(g[h])[None], r[None])
-            print(f"backward {w.name} head {h} {name}: {err:.3e}", flush=True)
-            assert err <= TOL["bf16"], (h, name, err)
+            print(f"backward {w.name} head {h} {gname}: {err:.3e}", flush=True)
+            assert err <= TOL["bf16"], (h, gname, err)
 
 
 @pytest.mark.parametrize("causal", [False, True])
