@@ -7,7 +7,8 @@ A step is one forward call (favor_fwd_bidir or favor_fwd_causal) over one
 batch of synthetic inputs of the workload's shape, inputs already resident in
 HBM; with --pass bwd, one backward call (favor_bwd_attn: dQ, dK, dV for a
 seeded upstream gradient dO, the forward's state recomputed inside); with
---pass prefill, one causal favor_prefill call exporting the state; with
+--pass prefill, one causal favor_prefill call exporting the state (--carry:
+continuing a carried state); with
 --pass decode, one favor_decode call (one new token for each of the B*H heads,
 the state updated in place).  Calls rotate over several input/output buffer sets (>= 1 GiB in total,
 four times the 256 MiB last-level cache) so that the timing is an HBM
@@ -59,6 +60,9 @@ def parse():
                     default="fwd",
                     help="time the forward (default), the backward pass, the causal prefill "
                          "that exports its state, or one decoding step per head")
+    ap.add_argument("--carry", action="store_true",
+                    help="with --pass prefill: continue a carried state (the state a prefill "
+                         "of the same shape exported) instead of starting empty")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle sample")
@@ -481,9 +485,15 @@ def main():
         ws_bytes = fv._binding.prefill_workspace_bytes(w.B, w.H, w.L, w.d, w.m, dt_code)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         st_out = fv.state_new(w.B, w.H, w.d, w.m)
+        st_in = None
+        if args.carry:
+            q0, k0, v0, o0 = sets[0]
+            st_in = fv.state_new(w.B, w.H, w.d, w.m)
+            fv.prefill(q0, k0, v0, W, state_out=st_in, kernel=args.kernel, out=o0,
+                       workspace=ws, stream=stream)
 
         def fwd(q, k, v, W, out, workspace, stream):
-            return fv.prefill(q, k, v, W, state_in=None, state_out=st_out, kernel=args.kernel,
+            return fv.prefill(q, k, v, W, state_in=st_in, state_out=st_out, kernel=args.kernel,
                               out=out, workspace=workspace, stream=stream)
     elif backward:
         def fwd(q, k, v, W, out, workspace, stream):
@@ -717,6 +727,7 @@ def main():
         "data": "synthetic (seeded Gaussian Q, K, V; orthogonal Gaussian W)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "m": w.m,
                    "causal": w.causal, "attn_kernel": args.kernel, "pass": args.pass_,
+                   **({"carried_state": True} if args.carry and args.pass_ == "prefill" else {}),
                    "buffer_sets": nsets,
                    "cache": "hot" if args.cache_hot else "rotating >= 1 GiB"},
         "repeats": {"n": len(reps), "min_ms": round(reps[0], 5),

@@ -209,13 +209,14 @@ int favor_prefill_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, in
  * favor_fwd_attn with causal = 1) where token i attends to the carried
  * tokens of state_in and to the new tokens j <= i.  state_in (NULL: empty)
  * and state_out (NULL: not written) are states as above and may not alias;
- * state_out receives the state after the last new token.  A fresh prefill
- * (state_in NULL) of bf16 inputs with d = 64 and m a multiple of 64 up to
- * 256 runs on the matrix cores (the causal forward, and the final state as
- * the sum over every key); every other case on the fp32 FMA kernels.
- * Workspace of at least
+ * state_out receives the state after the last new token.  A prefill of
+ * bf16 inputs with d = 64 and m a multiple of 64 up to 256 runs on the
+ * matrix cores (the causal forward with state_in as the first segment's
+ * carry, and the final state as state_in plus the sum over every key);
+ * every other case on the fp32 FMA kernels.  Workspace of at least
  * favor_prefill_workspace_bytes() bytes, 256-byte aligned.  Errors as
- * favor_fwd_attn.
+ * favor_fwd_attn, and FAVOR_ERR_UNSUPPORTED when state_in and state_out
+ * overlap.
  */
 int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                   int32_t attn_kernel, const void* Q, const void* K, const void* V,

@@ -103,10 +103,11 @@ int backward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtyp
 // causal kernels costs O(segment) per token).
 constexpr int32_t kPrefillSeg = 64;
 
-// A fresh prefill (no carried state) on the matrix cores: the causal forward's
-// plan, then the bidirectional key partials (the final state is the sum over
-// every key) at the next 256-byte boundary.  False when the shape is not
-// covered (the generic kernels run it).
+// A prefill on the matrix cores: the causal forward's plan (a carried state
+// enters as the first segment's carry), then the bidirectional key partials
+// (the final state is the carried state plus the sum over every key) at the
+// next 256-byte boundary.  False when the shape is not covered (the generic
+// kernels run it).
 bool mfma_prefill_plans(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                         Plan* pc, Plan* pb, size_t* off_b, size_t* bytes) {
   if (!mfma_causal_supported(d, m, dtype) || !mfma_bidir_supported(d, m, dtype) || d != 64 ||
@@ -387,6 +388,13 @@ int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t
                         static_cast<const void*>(state_in), static_cast<const void*>(state_out)})
     if (x && !favor::is_aligned(x, 16)) return FAVOR_ERR_ALIGN;
   if (!favor::is_aligned(workspace, 256)) return FAVOR_ERR_ALIGN;
+  if (state_in && state_out) {
+    size_t sb = 0;
+    favor_state_bytes(B, H, d, m, &sb);
+    const auto* a = reinterpret_cast<const char*>(state_in);
+    const auto* b = reinterpret_cast<const char*>(state_out);
+    if (a < b + sb && b < a + sb) return FAVOR_ERR_UNSUPPORTED;
+  }
   favor::Plan p;
   favor::make_generic_only_plan(B, H, L, d, m, dtype, 1, favor::kPrefillSeg, &p);
   size_t need = 0;
@@ -396,17 +404,17 @@ int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t
   p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
   favor::Plan pc, pb;
   size_t off_b = 0, mb = 0;
-  if (!state_in && favor::mfma_prefill_plans(B, H, L, d, m, dtype, &pc, &pb, &off_b, &mb)) {
-    // A fresh prefill on the matrix cores: the causal forward, then (if the
-    // state is wanted) the final state as the sum over every key.
+  if (favor::mfma_prefill_plans(B, H, L, d, m, dtype, &pc, &pb, &off_b, &mb)) {
+    // On the matrix cores: the causal forward from the carried state, then
+    // (if the state is wanted) the carried state plus the sum over every key.
     pc.knorm = pb.knorm = knorm;
     pc.relu = pb.relu = p.relu;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = favor::mfma_causal_forward(pc, Q, K, V, W, O, workspace, st);
+    hipError_t e = favor::mfma_causal_forward(pc, Q, K, V, W, O, workspace, st, state_in);
     if (e == hipSuccess && state_out) {
       char* wb = static_cast<char*>(workspace) + off_b;
       e = favor::mfma_bidir_key_partials(pb, K, V, W, wb, st);
-      if (e == hipSuccess) e = favor::mfma_state_export(pb, wb, state_out, st);
+      if (e == hipSuccess) e = favor::mfma_state_export(pb, wb, state_in, state_out, st);
     }
     if (e != hipSuccess) return favor::fail_hip(e);
     return FAVOR_OK;

@@ -109,8 +109,10 @@ hipError_t mfma_backward(const Plan& p, const BwdPlan& b, const void* Q, const v
                          const void* V, const float* W, const void* dO, void* dQ, void* dK,
                          void* dV, void* ws, hipStream_t stream);
 // The exported causal state after every key (fp32 [BH][m][d+4], natural-log
-// references) from the bidirectional key partials in `ws` (plan p).
-hipError_t mfma_state_export(const Plan& p, const void* ws, float* state, hipStream_t stream);
+// references) from the bidirectional key partials in `ws` (plan p), added to
+// the imported state state_in (nullptr: empty; may not alias state).
+hipError_t mfma_state_export(const Plan& p, const void* ws, const float* state_in, float* state,
+                             hipStream_t stream);
 // The bidirectional matrix-core path's key partials alone (kpart).
 hipError_t mfma_bidir_key_partials(const Plan& p, const void* K, const void* V, const float* W,
                                    void* ws, hipStream_t stream);
@@ -133,8 +135,11 @@ hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const
 
 // MFMA path (bf16 inputs): shape support, and the causal forward.
 bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype);
+// state_in (exported layout, nullptr: none) is a carried state that every
+// query also attends to.
 hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, const void* V,
-                               const float* W, void* O, void* ws, hipStream_t stream);
+                               const float* W, void* O, void* ws, hipStream_t stream,
+                               const float* state_in = nullptr);
 
 // Measurement hooks behind favor_timing_*: each kernel launch is bracketed
 // by timing_before / timing_after (no-ops unless this thread is recording).

@@ -1186,10 +1186,13 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
 // features of one row.  P[bh][s] becomes the sum of segments before s and
 // cP[bh][s] its per-feature reference, for s >= 1 (the scan starts the first
 // segment from a zero state and reads neither).  The last segment's own
-// state is never needed, so kpart leaves it out.
+// state is never needed, so kpart leaves it out.  With an imported state Sin
+// (the exported layout [BH][m][D+4], reference in natural-log units) the sum
+// starts from it, and every segment, the first included, gets a carry.
 template <int D>
 __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const float* __restrict__ cs,
-                                               float* __restrict__ cP, int m, int nseg) {
+                                               float* __restrict__ cP, const float* __restrict__ Sin,
+                                               int m, int nseg, float sin_scale) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int mq = m / 4;
@@ -1197,17 +1200,28 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
   const int row = e / mq, f = 4 * (e - row * mq);
   float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 rc = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+  const bool carry = Sin != nullptr;
+  if (carry) {
+    // exported values: log2-unit reference c log2(e); ReLU states in the
+    // features' log2(e) scale (sin_scale)
+    const float* sr = Sin + (static_cast<size_t>(bh) * m + f) * (D + 4);
+    run = make_float4(sr[row] * sin_scale, sr[(D + 4) + row] * sin_scale,
+                      sr[2 * (D + 4) + row] * sin_scale, sr[3 * (D + 4) + row] * sin_scale);
+    rc = make_float4(sr[D + 1] * kLog2e, sr[(D + 4) + D + 1] * kLog2e,
+                     sr[2 * (D + 4) + D + 1] * kLog2e, sr[3 * (D + 4) + D + 1] * kLog2e);
+  }
   for (int s = 0; s < nseg; ++s) {
     const size_t ci = (static_cast<size_t>(bh) * nseg + s) * m + f;
     float4* pp = reinterpret_cast<float4*>(P + ((static_cast<size_t>(bh) * nseg + s) * (D + 1) + row) * m + f);
-    if (row == 0 && s > 0) *reinterpret_cast<float4*>(cP + ci) = rc;
+    const bool put = s > 0 || carry;
+    if (row == 0 && put) *reinterpret_cast<float4*>(cP + ci) = rc;
     if (s + 1 == nseg) {
-      if (s > 0) *pp = run;
+      if (put) *pp = run;
       break;
     }
     const float4 ts = *pp;
     const float4 c = *reinterpret_cast<const float4*>(cs + ci);
-    if (s > 0) *pp = run;
+    if (put) *pp = run;
     float4 nc;
     nc.x = fmaxf(rc.x, c.x); nc.y = fmaxf(rc.y, c.y); nc.z = fmaxf(rc.z, c.z); nc.w = fmaxf(rc.w, c.w);
     run.x = run.x * fast_exp2(rc.x - nc.x) + ts.x * fast_exp2(c.x - nc.x);
@@ -1230,7 +1244,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
                                                   const float* __restrict__ P,
                                                   const float* __restrict__ cP,
                                                   uint16_t* __restrict__ O, int L, int m, int SEG,
-                                                  int nseg, float knorm) {
+                                                  int nseg, float knorm, int carry0) {
   constexpr int D = 64;
   constexpr int NTH = NW * 64;
   constexpr int KS = 2, NT = 4, TV = 5;
@@ -1280,7 +1294,8 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   }
 
   // Carry-in: the prefix state of the segments before this one (none for
-  // the first segment: zero state, no reference yet).
+  // the first segment unless a state was imported: zero state, no reference
+  // yet).
   f32x4 st[NT][TV];
   float cref[NT];
 #pragma unroll
@@ -1289,7 +1304,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
 #pragma unroll
     for (int tv = 0; tv < TV; ++tv) st[mt][tv] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (s > 0) {
+  if (s > 0 || carry0) {
     const size_t pbase = (static_cast<size_t>(bh) * nseg + s) * (D + 1);
     const size_t cbase = (static_cast<size_t>(bh) * nseg + s) * m;
 #pragma unroll
@@ -1700,7 +1715,8 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
 
 template <int NW, bool RELU>
 hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
-                         const float* W, uint16_t* O, char* ws, hipStream_t st) {
+                         const float* W, uint16_t* O, char* ws, const float* Sin,
+                         hipStream_t st) {
   float* P = reinterpret_cast<float*>(ws + p.off_T);
   float* cs = reinterpret_cast<float*>(ws + p.off_cseg);
   float* cP = reinterpret_cast<float*>(ws + p.off_cP);
@@ -1715,15 +1731,18 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     e = hipGetLastError();
     timing_after(st, "kpart");
     if (e != hipSuccess) return e;
+  }
+  if (p.nseg > 1 || Sin) {
     timing_before(st);
-    kprefix<64><<<dim3((65 * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(P, cs, cP, p.m, p.nseg);
+    kprefix<64><<<dim3((65 * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(
+        P, cs, cP, Sin, p.m, p.nseg, RELU ? kLog2e : 1.f);
     e = hipGetLastError();
     timing_after(st, "kprefix");
     if (e != hipSuccess) return e;
   }
   timing_before(st);
   cscan<NW, RELU><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg,
-                                                     p.knorm);
+                                                     p.knorm, Sin ? 1 : 0);
   e = hipGetLastError();
   timing_after(st, "cscan");
   return e;
@@ -1736,7 +1755,8 @@ bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype) {
 }
 
 hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, const void* V,
-                               const float* W, void* O, void* ws, hipStream_t stream) {
+                               const float* W, void* O, void* ws, hipStream_t stream,
+                               const float* state_in) {
   const auto* q = static_cast<const uint16_t*>(Q);
   const auto* k = static_cast<const uint16_t*>(K);
   const auto* v = static_cast<const uint16_t*>(V);
@@ -1745,8 +1765,8 @@ hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, cons
   if (p.d == 64) {
 #define FAVOR_CCASE(NW)                                                            \
   case NW:                                                                         \
-    return p.relu ? launch_causal<NW, true>(p, q, k, v, W, o, w, stream)           \
-                  : launch_causal<NW, false>(p, q, k, v, W, o, w, stream);
+    return p.relu ? launch_causal<NW, true>(p, q, k, v, W, o, w, state_in, stream) \
+                  : launch_causal<NW, false>(p, q, k, v, W, o, w, state_in, stream);
     switch (p.m / 64) {
       FAVOR_CCASE(1) FAVOR_CCASE(2) FAVOR_CCASE(3) FAVOR_CCASE(4)
       default: break;

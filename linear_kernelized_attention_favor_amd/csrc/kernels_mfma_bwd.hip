@@ -761,11 +761,13 @@ hipError_t launch_bwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const 
 // the exported layout [BH][m][d+4]: [S~ | z~ | c | 0 | 0] with c in natural-log
 // units (the features here are exp2 of log2-unit exponents, the same values;
 // ReLU features here are max(w' . k, 0) = log2(e) max(w . k, 0), so the state
-// is scaled back by ln 2).
+// is scaled back by ln 2).  With an imported state Sin (same layout, not
+// aliasing st) the result is Sin plus every key's contribution.
 // grid (ceil(m/64), BH), 256 threads: 64 features x 4 column groups.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void sexport(const float* __restrict__ P,
                                                const float* __restrict__ cs,
+                                               const float* __restrict__ Sin,
                                                float* __restrict__ st, int m, int nseg,
                                                int relu) {
   const int bh = blockIdx.y;
@@ -775,9 +777,15 @@ __global__ __launch_bounds__(256) void sexport(const float* __restrict__ P,
   const size_t cb = static_cast<size_t>(bh) * nseg * m + f;
   float cm = -INFINITY;
   for (int s = 0; s < nseg; ++s) cm = fmaxf(cm, cs[cb + static_cast<size_t>(s) * m]);
+  const float* srow = Sin ? Sin + (static_cast<size_t>(bh) * m + f) * (kD + 4) : nullptr;
+  // the imported state in the features' units: log2-unit reference, ReLU
+  // values times log2(e)
+  const float cin = srow ? srow[kD + 1] * kLog2e : -INFINITY;
+  cm = fmaxf(cm, cin);
+  const float sin_scale = srow ? (relu ? kLog2e : 1.f) * fast_exp2(cin - cm) : 0.f;
   float* row = st + (static_cast<size_t>(bh) * m + f) * (kD + 4);
   for (int c = cg; c <= kD; c += 4) {
-    float acc = 0.f;
+    float acc = srow ? srow[c] * sin_scale : 0.f;
     for (int s = 0; s < nseg; ++s)
       acc = fmaf(P[((static_cast<size_t>(bh) * nseg + s) * (kD + 1) + c) * m + f],
                  fast_exp2(cs[cb + static_cast<size_t>(s) * m] - cm), acc);
@@ -792,12 +800,13 @@ __global__ __launch_bounds__(256) void sexport(const float* __restrict__ P,
 
 }  // namespace
 
-hipError_t mfma_state_export(const Plan& p, const void* ws, float* state, hipStream_t stream) {
+hipError_t mfma_state_export(const Plan& p, const void* ws, const float* state_in, float* state,
+                             hipStream_t stream) {
   const char* w = static_cast<const char*>(ws);
   timing_before(stream);
   sexport<<<dim3((p.m + 63) / 64, p.BH), 256, 0, stream>>>(
       reinterpret_cast<const float*>(w + p.off_T), reinterpret_cast<const float*>(w + p.off_cseg),
-      state, p.m, p.nseg, p.relu);
+      state_in, state, p.m, p.nseg, p.relu);
   const hipError_t e = hipGetLastError();
   timing_after(stream, "sexport");
   return e;

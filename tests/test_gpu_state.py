@@ -6,8 +6,8 @@ Outputs: per-row relative error as in the forward's parity tests (1e-4 for
 fp32 inputs, 2e-2 for bf16).  States: the true state exp(c) [S~ | z~] / sqrt(m)
 against the oracle's (S, z) per head, max abs error over the largest entry:
 1e-4 where the state is fp32 arithmetic on the same input values (the generic
-kernels, either dtype), 1e-2 where a fresh bf16 prefill runs on the matrix
-cores (features rounded to bf16 as the products' operands).
+kernels, either dtype), 1e-2 where a bf16 prefill runs on the matrix cores
+(features rounded to bf16 as the products' operands).
 """
 import math
 
@@ -63,9 +63,9 @@ def _state_err(st, K, V, W, kernel):
     return float(np.max(np.abs(got - ref).max(axis=(-1, -2)) / np.abs(ref).max(axis=(-1, -2))))
 
 
-def _state_tol(shape, dtype, fresh=True):
+def _state_tol(shape, dtype):
     d, m = shape[3], shape[4]
-    mfma = fresh and dtype == "bf16" and d == 64 and m % 64 == 0 and m <= 256
+    mfma = dtype == "bf16" and d == 64 and m % 64 == 0 and m <= 256
     return 1e-2 if mfma else 1e-4
 
 
@@ -112,8 +112,7 @@ def test_chunked_prefill_continues_the_state(fv, dtype, kernel):
     assert oracle.row_rel_err(_np64(o1), ref[:, :, :cut]) <= TOL[dtype]
     assert oracle.row_rel_err(_np64(o2), ref[:, :, cut:]) <= TOL[dtype]
     assert _state_err(st1, k[:, :, :cut], v[:, :, :cut], W, kernel) <= _state_tol(shape, dtype)
-    # (the second call continues a state: generic kernels, on the first
-    # call's state, so the first call's error carries over)
+    # (the second call continues the first call's state, whose error carries over)
     assert _state_err(st2, k, v, W, kernel) <= _state_tol(shape, dtype)
 
 
@@ -215,3 +214,70 @@ def test_decode_graph_replays_match_eager(fv):
         torch.cuda.synchronize()
         assert torch.equal(out, e), t
         assert torch.equal(st_g, st_e), t
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_prefill_from_an_empty_state_equals_a_fresh_prefill(fv, kernel):
+    # An imported empty state (reference -inf) is the fresh prefill's zero
+    # carry: the same outputs and exported state, bit for bit.
+    shape = (2, 3, 530, 64, 192)
+    q, k, v, W = _case(shape, "bf16", 43)
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    o1, st1 = fv.prefill(qc, kc, vc, Wd, kernel=kernel)
+    empty = fv.state_new(2, 3, 64, 192)
+    o2, st2 = fv.prefill(qc, kc, vc, Wd, state_in=empty, kernel=kernel)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(st1, st2)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("cuts", [(1000, 17), (64, 1200), (500, 500, 260)], ids=str)
+def test_prefill_chain_on_the_matrix_cores(fv, kernel, cuts):
+    # Prefills chained through exported states: every piece (a short tail of
+    # one partial segment, or many segments) continues the previous state.
+    L = sum(cuts)
+    shape = (1, 4, L, 64, 256)
+    q, k, v, W = _case(shape, "bf16", L + 7)
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    ref = _ref_out(q, k, v, W, kernel)
+    st, a = None, 0
+    for n in cuts:
+        sl = slice(a, a + n)
+        o, st = fv.prefill(qc[:, :, sl].contiguous(), kc[:, :, sl].contiguous(),
+                           vc[:, :, sl].contiguous(), Wd, state_in=st, kernel=kernel)
+        torch.cuda.synchronize()
+        assert oracle.row_rel_err(_np64(o), ref[:, :, sl]) <= TOL["bf16"], (a, n)
+        a += n
+        assert _state_err(st, k[:, :, :a], v[:, :, :a], W, kernel) <= 1e-2, a
+
+
+def test_prefill_continues_a_state_with_large_references(fv):
+    # Keys whose exponents grow along the stream, split over two prefills:
+    # the imported references are large and the continuation raises them.
+    # (along the first feature's direction: its exponent |w_0| t - t^2 / 2
+    # climbs from 0 to about 27 over the stream)
+    B, H, L, d, m = 1, 2, 900, 64, 128
+    rng = np.random.default_rng(47)
+    W = oracle.draw_w(48, m, d).astype(np.float32)
+    mu = W[0] / np.linalg.norm(W[0])
+    ramp = np.linspace(0, 5, L, dtype=np.float32)[:, None]
+    k = rng.standard_normal((B, H, L, d)).astype(np.float32) * 0.1 + ramp * mu
+    q = rng.standard_normal((B, H, L, d)).astype(np.float32) * 0.3
+    v = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    cut = 450
+    o1, st1 = fv.prefill(qc[:, :, :cut].contiguous(), kc[:, :, :cut].contiguous(),
+                         vc[:, :, :cut].contiguous(), Wd)
+    o2, st2 = fv.prefill(qc[:, :, cut:].contiguous(), kc[:, :, cut:].contiguous(),
+                         vc[:, :, cut:].contiguous(), Wd, state_in=st1)
+    torch.cuda.synchronize()
+    assert torch.isfinite(st2).all()
+    ref = _ref_out(q, k, v, W, "softmax")
+    assert oracle.row_rel_err(_np64(o1), ref[:, :, :cut]) <= TOL["bf16"]
+    assert oracle.row_rel_err(_np64(o2), ref[:, :, cut:]) <= TOL["bf16"]
+    assert _state_err(st2, k, v, W, "softmax") <= 1e-2

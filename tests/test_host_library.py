@@ -182,6 +182,10 @@ def test_state_entry_validation():
     assert pre(si=MIS) == EALIGN
     assert pre(so=MIS) == EALIGN
     assert pre(wsb=need - 1) == EWS
+    # state_in and state_out may not overlap (1 x 1 x 64 x 68 floats = 17408 bytes)
+    assert pre(si=A, so=A) == EUNSUP
+    assert pre(si=A, so=A + 17408 - 16) == EUNSUP
+    assert pre(si=A + 17392, so=A) == EUNSUP
 
     def dec(**kw):
         a = dict(B=1, H=1, d=64, m=64, dtype=1, attn=0, q=A, k=A, v=A, W=A, o=A, st=A)
