@@ -227,6 +227,15 @@ void make_bwd_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
     make_plan(B, H, L, d, m, dtype, causal, p);   // the forward's key partials
     b->path = kPathMfma;
     const size_t BH = static_cast<size_t>(p->BH), mm = static_cast<size_t>(m);
+    if (causal) {
+      // The causal forward's segments; per query (L_i, p_i), and per
+      // segment a query state of 66 rows.
+      size_t off = p->bytes;
+      b->off_ru = off; off = align256(off + BH * static_cast<size_t>(L) * 2 * 4);
+      b->off_G = off;  off = align256(off + BH * p->nseg * 66 * mm * 4);
+      b->bytes = off;
+      return;
+    }
     // Query blocks: about 512 work-groups in total, a multiple of 64 tokens.
     const int want = (512 + p->BH - 1) / p->BH;
     const int ntile = (L + 63) / 64;

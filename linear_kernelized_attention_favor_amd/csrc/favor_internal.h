@@ -103,11 +103,22 @@ hipError_t generic_decode(int32_t BH, int32_t d, int32_t m, int32_t dtype, float
 // Its first two steps alone: the key state and references in the workspace.
 hipError_t generic_key_state(const Plan& p, const void* K, const void* V, const float* W,
                              void* ws, hipStream_t stream);
-// Matrix-core backward (bidirectional, bf16, d = 64, m in {64, 128, 192, 256}).
+// Matrix-core backward (bf16, d = 64, m in {64, 128, 192, 256}; both forms).
 bool mfma_bwd_supported(int32_t d, int32_t m, int32_t dtype, int32_t causal);
 hipError_t mfma_backward(const Plan& p, const BwdPlan& b, const void* Q, const void* K,
                          const void* V, const float* W, const void* dO, void* dQ, void* dK,
                          void* dV, void* ws, hipStream_t stream);
+// Causal backward on the matrix cores (bf16, d = 64, m a multiple of 64 up
+// to 256; the causal forward's plan p, workspace offsets off_ru (the
+// per-query (L_i, p_i)) and off_G (the segments' query states) of b).
+hipError_t mfma_causal_backward(const Plan& p, const BwdPlan& b, const void* Q, const void* K,
+                                const void* V, const float* W, const void* dO, void* dQ, void* dK,
+                                void* dV, void* ws, hipStream_t stream);
+// Its first launches: every segment's key state and reference, the prefix
+// states, and per query (L_i, p_i) as float pairs in lp (BH L pairs).
+hipError_t mfma_causal_rowstats(const Plan& p, const void* Q, const void* K, const void* V,
+                                const float* W, const void* dO, float* lp, void* ws,
+                                hipStream_t stream);
 // The exported causal state after every key (fp32 [BH][m][d+4], natural-log
 // references) from the bidirectional key partials in `ws` (plan p), added to
 // the imported state state_in (nullptr: empty; may not alias state).

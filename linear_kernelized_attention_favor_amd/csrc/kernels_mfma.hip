@@ -1236,7 +1236,12 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
 // [64 w, 64 w + 64)).  State per wave, in registers: st[mt][tv] with lane =
 // value column 16 tv + l16 (tv = 4: the ones column, z) and rows = features
 // 16 mt + 4 g + v; its per-feature references cref (log2 units).
-template <int NW, bool RELU>
+//
+// BWD: the same scan for the backward pass; instead of O it writes, per
+// query, lp[i] = (L_i, p_i) with L_i = log2 of the denominator taken with no
+// reference (log2 sum_{j <= i} sum_r 2^(s_ir + e_jr), the same in every
+// frame of references) and p_i = dO_i . O_i in fp32.
+template <int NW, bool RELU, bool BWD = false>
 __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__ Q,
                                                   const uint16_t* __restrict__ K,
                                                   const uint16_t* __restrict__ V,
@@ -1244,7 +1249,9 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
                                                   const float* __restrict__ P,
                                                   const float* __restrict__ cP,
                                                   uint16_t* __restrict__ O, int L, int m, int SEG,
-                                                  int nseg, float knorm, int carry0) {
+                                                  int nseg, float knorm, int carry0,
+                                                  const uint16_t* __restrict__ dO = nullptr,
+                                                  float2* __restrict__ lp = nullptr) {
   constexpr int D = 64;
   constexpr int NTH = NW * 64;
   constexpr int KS = 2, NT = 4, TV = 5;
@@ -1641,7 +1648,22 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
         }
       }
       const float inv = 1.0f / den;
-      if (jt + i < j1) {
+      if constexpr (BWD) {
+        // (the eight threads of a row are consecutive lanes of one wave)
+        float pd = 0.f;
+        if (jt + i < j1) {
+          const uint4 gv = *reinterpret_cast<const uint4*>(dO + base + static_cast<size_t>(jt + i) * D + c0);
+          const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            pd = fmaf(bf16_lo(g4[q]), acc8[2 * q] * inv, pd);
+            pd = fmaf(bf16_hi(g4[q]), acc8[2 * q + 1] * inv, pd);
+          }
+        }
+        pd = group_sum<8>(pd);
+        if (c0 == 0 && jt + i < j1)
+          lp[static_cast<size_t>(bh) * L + jt + i] = make_float2(log2f(den) + mx, pd);
+      } else if (jt + i < j1) {
         uint4 ov;
         ov.x = pack_bf16(acc8[0] * inv, acc8[1] * inv);
         ov.y = pack_bf16(acc8[2] * inv, acc8[3] * inv);
@@ -1748,7 +1770,60 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
   return e;
 }
 
+// The backward's first launches: every segment's key state (the last one's
+// reference is needed too), the exclusive prefix, and the scan's per-query
+// (L_i, p_i).
+template <int NW, bool RELU>
+hipError_t launch_rowstats(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                           const float* W, const uint16_t* dO, float2* lp, char* ws,
+                           hipStream_t st) {
+  float* P = reinterpret_cast<float*>(ws + p.off_T);
+  float* cs = reinterpret_cast<float*>(ws + p.off_cseg);
+  float* cP = reinterpret_cast<float*>(ws + p.off_cP);
+  timing_before(st);
+  kpart<64, NW, 1, RELU><<<dim3(p.nseg * p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
+                                                                  p.nseg, p.nseg, p.knorm);
+  hipError_t e = hipGetLastError();
+  timing_after(st, "kpart");
+  if (e != hipSuccess) return e;
+  if (p.nseg > 1) {
+    timing_before(st);
+    kprefix<64><<<dim3((65 * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(P, cs, cP, nullptr, p.m,
+                                                                         p.nseg, 1.f);
+    e = hipGetLastError();
+    timing_after(st, "kprefix");
+    if (e != hipSuccess) return e;
+  }
+  timing_before(st);
+  cscan<NW, RELU, true><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(
+      Q, K, V, W, P, cP, nullptr, p.L, p.m, p.seg, p.nseg, p.knorm, 0, dO, lp);
+  e = hipGetLastError();
+  timing_after(st, "cscan_lp");
+  return e;
+}
+
 }  // namespace
+
+hipError_t mfma_causal_rowstats(const Plan& p, const void* Q, const void* K, const void* V,
+                                const float* W, const void* dO, float* lp, void* ws,
+                                hipStream_t stream) {
+  const auto* q = static_cast<const uint16_t*>(Q);
+  const auto* k = static_cast<const uint16_t*>(K);
+  const auto* v = static_cast<const uint16_t*>(V);
+  const auto* g = static_cast<const uint16_t*>(dO);
+  auto* l2 = reinterpret_cast<float2*>(lp);
+  char* w = static_cast<char*>(ws);
+#define FAVOR_RCASE(NW)                                                                   \
+  case NW:                                                                                \
+    return p.relu ? launch_rowstats<NW, true>(p, q, k, v, W, g, l2, w, stream)            \
+                  : launch_rowstats<NW, false>(p, q, k, v, W, g, l2, w, stream);
+  switch (p.d == 64 ? p.m / 64 : 0) {
+    FAVOR_RCASE(1) FAVOR_RCASE(2) FAVOR_RCASE(3) FAVOR_RCASE(4)
+    default: break;
+  }
+#undef FAVOR_RCASE
+  return hipErrorInvalidValue;
+}
 
 bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype) {
   return dtype == FAVOR_BF16 && d == 64 && m % 64 == 0 && m <= 256;

@@ -813,9 +813,8 @@ hipError_t mfma_state_export(const Plan& p, const void* ws, const float* state_i
 }
 
 bool mfma_bwd_supported(int32_t d, int32_t m, int32_t dtype, int32_t causal) {
-  return dtype == FAVOR_BF16 && !causal && d == kD && (m == 64 || m == 128 || m == 192 ||
-                                                       m == 256) &&
-         mfma_bidir_supported(d, m, dtype);
+  const bool shape = dtype == FAVOR_BF16 && d == kD && (m == 64 || m == 128 || m == 192 || m == 256);
+  return shape && (causal ? mfma_causal_supported(d, m, dtype) : mfma_bidir_supported(d, m, dtype));
 }
 
 hipError_t mfma_backward(const Plan& p, const BwdPlan& b, const void* Q, const void* K,
@@ -829,6 +828,7 @@ hipError_t mfma_backward(const Plan& p, const BwdPlan& b, const void* Q, const v
   auto* dk = static_cast<uint16_t*>(dK);
   auto* dv = static_cast<uint16_t*>(dV);
   char* w = static_cast<char*>(ws);
+  if (p.causal) return mfma_causal_backward(p, b, Q, K, V, W, dO, dQ, dK, dV, ws, stream);
 #define FAVOR_BCASE(M)                                                                   \
   if (p.m == M)                                                                          \
     return p.relu ? launch_bwd<M, true>(p, b, q, k, v, W, g, dq, dk, dv, w, stream)      \

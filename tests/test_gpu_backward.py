@@ -140,24 +140,27 @@ def test_backward_shapes(fv, shape, causal, dtype, kernel):
         assert err <= TOL[dtype], (name, err)
 
 
-# Shapes of the matrix-core backward (bidirectional, bf16, d = 64, m up to
-# 256): single tokens, ragged 64-token tiles, every supported m, many query
-# blocks per head.
+# Shapes of the matrix-core backward (bf16, d = 64, m up to 256): single
+# tokens, ragged 32- and 64-token tiles, every supported m, many query blocks
+# per head (bidirectional) and many segments with a partial last one (causal:
+# at least 256 tokens per segment).
 MFMA_SHAPES = [
     (1, 1, 1, 64, 64),
     (1, 2, 65, 64, 192),
     (3, 1, 130, 64, 64),
     (1, 1, 4097, 64, 256),
     (2, 3, 500, 64, 128),
+    (1, 2, 1000, 64, 256),
 ]
 
 
 @pytest.mark.parametrize("kernel", ["softmax", "gaussian", "relu"])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", MFMA_SHAPES, ids=lambda s: "x".join(map(str, s)))
-def test_backward_matrix_core_shapes(fv, shape, kernel):
+def test_backward_matrix_core_shapes(fv, shape, causal, kernel):
     B, H, L, d, m = shape
-    assert fv.plan_describe(B, H, L, d, m, fv.BF16, False)[0] == 1   # the matrix-core plan
-    test_backward_shapes(fv, shape, False, "bf16", kernel)
+    assert fv.plan_describe(B, H, L, d, m, fv.BF16, causal)[0] == 1   # the matrix-core plan
+    test_backward_shapes(fv, shape, causal, "bf16", kernel)
 
 
 @pytest.mark.parametrize("causal", [False, True])
