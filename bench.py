@@ -152,7 +152,16 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
            # the query state (projection, G); dk (projection, H, dk), dv
            # (projection, dv)
            "bq_den": (2, 4.0), "bq_dq": (1, 6.0), "bq_g": (0, 4.0),
-           "bkey_dk": (1, 6.0), "bkey_dv": (1, 4.0)}
+           "bkey_dk": (1, 6.0), "bkey_dv": (1, 4.0),
+           # causal matrix-core backward (kpart owns the K, V reads and the
+           # key state): the scan for (L, p) reads Q and dO (both
+           # projections, [num | den], the state update: 8 d m); dq (both
+           # projections, T, state update, dq: 10 d m); the segments' query
+           # states (projection, G: 4 d m); dk (both projections, H, G
+           # update, dk: 10 d m); dv (key projection, the query projection
+           # twice, dv, G update: 10 d m); masked in-chunk terms uncounted
+           "cscan_lp": (2, 8.0), "cbq": (1, 10.0), "cbg": (0, 4.0),
+           "cbk_dk": (1, 10.0), "cbk_dv": (1, 10.0)}
     if name == "g_decode":
         # one token per head: the state [m][d+4] fp32 read and written, q, k,
         # v read and o written; two projections, the state update and the
@@ -241,9 +250,10 @@ def copy_calibration(steps: int):
 FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "g_state",
                  "g_combine", "g_apply", "gb_query", "gb_gstate", "gb_gcombine", "gb_key",
                  "bprep", "bcombine", "bqr", "gcombine", "bkeyr", "sexport", "g_decode",
-                 "g_state_reset", "draw_block", "g_feature_map")
+                 "g_state_reset", "draw_block", "g_feature_map", "cbq", "cbg", "cbsuffix")
 # passes of the templated backward kernels, by their last template argument
-_PASSES = {"bqr": ("bq_den", "bq_dq", "bq_g"), "bkeyr": ("bkey_dk", "bkey_dv")}
+_PASSES = {"bqr": ("bq_den", "bq_dq", "bq_g"), "bkeyr": ("bkey_dk", "bkey_dv"),
+           "cbk": ("cbk_dk", "cbk_dv")}
 
 
 def _favor_kernel(name: str):
@@ -259,6 +269,10 @@ def _favor_kernel(name: str):
         mode = re.search(r"ELi(\d+)EE", name[m.end():]) if m else None
     if k in _PASSES and mode is not None:
         return _PASSES[k][int(mode.group(1))]
+    if k == "cscan":   # the backward's variant (last template argument true)
+        tail = (m.group(2) or "") if "(anonymous namespace)" in name else name[m.end():]
+        if re.search(r"true\s*$", tail) or re.search(r"ELb1EE", tail):
+            return "cscan_lp"
     return k if k in FAVOR_KERNELS else None
 
 
