@@ -143,10 +143,15 @@ def test_bwd_rejects_unknown_kernels_and_sizes_its_workspace():
     for causal in (False, True):
         for (B, H, L, d, m) in [(1, 1, 1, 16, 16), (8, 8, 4096, 64, 256), (1, 1, 4097, 128, 1024)]:
             n = fv.bwd_workspace_bytes(B, H, L, d, m, 1, causal)
-            mfma = not causal and d == 64 and m <= 256
-            if mfma:
+            mfma = d == 64 and m <= 256
+            if mfma and not causal:
                 # the key state, its operand copies and the query blocks' G partials
                 assert n >= B * H * m * (d + 1) * 4 * 2
+            elif mfma:
+                # every segment's key state and query state (66 rows), and per
+                # query (L_i, p_i)
+                nseg = fv.plan_describe(B, H, L, d, m, 1, True)[1]
+                assert n >= B * H * (nseg * m * (d + 1 + 66) + 2 * L) * 4
             else:
                 # the key state, and per query (d + 2) floats: Ucat and the row reference
                 assert n >= B * H * (m * (d + 1) + L * (d + 2)) * 4
