@@ -186,6 +186,109 @@ __device__ inline void stage_chunk(Stage& st, const uint16_t* __restrict__ Q,
   }
 }
 
+// The same chunk load split in two for a work-group of 256 threads (one row
+// unit and one transpose unit per thread): the global loads into registers,
+// issued a chunk ahead, and the LDS stores.
+struct ChunkRegs {
+  uint4 k, q, v, g;        // row unit (token tid / 8, values 8 (tid % 8) ..)
+  uint2 va, vb, ga, gb;    // transpose unit: tokens t, t + 1, columns col ..
+  float2 l;                // (L, p) of token tid (tid < 32)
+};
+__device__ inline void gload_chunk(ChunkRegs& r, const uint16_t* __restrict__ Q,
+                                   const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                   const uint16_t* __restrict__ dO, const float2* __restrict__ lp,
+                                   size_t base, size_t lbase, int jt, int j1) {
+  const int tid = threadIdx.x;
+  {
+    const int t = tid / 8, ch = tid % 8;
+    const size_t off = base + static_cast<size_t>(jt + t) * kD + 8 * ch;
+    r.k = r.q = r.v = r.g = make_uint4(0, 0, 0, 0);
+    if (jt + t < j1) {
+      r.k = *reinterpret_cast<const uint4*>(K + off);
+      r.q = *reinterpret_cast<const uint4*>(Q + off);
+      r.v = *reinterpret_cast<const uint4*>(V + off);
+      r.g = *reinterpret_cast<const uint4*>(dO + off);
+    }
+  }
+  {
+    const int t = 2 * (tid % (kC / 2)), col = 4 * (tid / (kC / 2));
+    const size_t off = base + static_cast<size_t>(jt + t) * kD + col;
+    r.va = r.vb = r.ga = r.gb = make_uint2(0, 0);
+    if (jt + t < j1) {
+      r.va = *reinterpret_cast<const uint2*>(V + off);
+      r.ga = *reinterpret_cast<const uint2*>(dO + off);
+    }
+    if (jt + t + 1 < j1) {
+      r.vb = *reinterpret_cast<const uint2*>(V + off + kD);
+      r.gb = *reinterpret_cast<const uint2*>(dO + off + kD);
+    }
+  }
+  r.l = make_float2(INFINITY, 0.f);
+  if (tid < kC && jt + tid < j1) r.l = lp[lbase + jt + tid];
+}
+__device__ inline void lstore_chunk(Stage& st, const ChunkRegs& r, int jt, int j1, float knorm) {
+  const int tid = threadIdx.x;
+  {
+    const int t = tid / 8, ch = tid % 8;
+    float ss = 0.f;
+    const uint32_t w4[4] = {r.k.x, r.k.y, r.k.z, r.k.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ss = fmaf(bf16_lo(w4[q]), bf16_lo(w4[q]), ss);
+      ss = fmaf(bf16_hi(w4[q]), bf16_hi(w4[q]), ss);
+    }
+    ss = group_sum<8>(ss);
+    *reinterpret_cast<uint4*>(&st.Kh[t][8 * ch]) =
+        make_uint4(bf16x2_to_f16x2(r.k.x), bf16x2_to_f16x2(r.k.y), bf16x2_to_f16x2(r.k.z),
+                   bf16x2_to_f16x2(r.k.w));
+    *reinterpret_cast<uint4*>(&st.Qh[t][8 * ch]) =
+        make_uint4(bf16x2_to_f16x2(r.q.x), bf16x2_to_f16x2(r.q.y), bf16x2_to_f16x2(r.q.z),
+                   bf16x2_to_f16x2(r.q.w));
+    *reinterpret_cast<uint4*>(&st.Vr[t][8 * ch]) = r.v;
+    *reinterpret_cast<uint4*>(&st.Gr[t][8 * ch]) = r.g;
+    if (ch == 0) st.nk[t] = (jt + t < j1) ? -knorm * kLog2e * ss : -INFINITY;
+  }
+  {
+    const int t = 2 * (tid % (kC / 2)), col = 4 * (tid / (kC / 2));
+    const int w = perm_inv(t) >> 1;
+    st.Vt[col + 0][w] = __builtin_amdgcn_perm(r.vb.x, r.va.x, 0x05040100u);
+    st.Vt[col + 1][w] = __builtin_amdgcn_perm(r.vb.x, r.va.x, 0x07060302u);
+    st.Vt[col + 2][w] = __builtin_amdgcn_perm(r.vb.y, r.va.y, 0x05040100u);
+    st.Vt[col + 3][w] = __builtin_amdgcn_perm(r.vb.y, r.va.y, 0x07060302u);
+    st.Gt[col + 0][w] = __builtin_amdgcn_perm(r.gb.x, r.ga.x, 0x05040100u);
+    st.Gt[col + 1][w] = __builtin_amdgcn_perm(r.gb.x, r.ga.x, 0x07060302u);
+    st.Gt[col + 2][w] = __builtin_amdgcn_perm(r.gb.y, r.ga.y, 0x05040100u);
+    st.Gt[col + 3][w] = __builtin_amdgcn_perm(r.gb.y, r.ga.y, 0x07060302u);
+  }
+  if (tid < kC) {
+    st.Lq[tid] = r.l.x;
+    st.pq[tid] = r.l.y;
+    const uint16_t hi = bf16_bits(-r.l.y);
+    st.pn[0][perm_inv(tid)] = hi;
+    st.pn[1][perm_inv(tid)] = bf16_bits(-r.l.y - bf16_val(hi));
+  }
+}
+
+// Chunk loads of a sweep: with 256 threads, each chunk's global loads are
+// issued one chunk ahead (next()) and stored to LDS at the start of its turn
+// (put()); otherwise loaded and stored at once.
+template <int NTH>
+struct ChunkLoader {
+  ChunkRegs r;
+  const uint16_t *Q, *K, *V, *dO;
+  const float2* lp;
+  size_t base, lbase;
+  int j1;
+  float knorm;
+  __device__ void next(int jt) {
+    if constexpr (NTH == 256) gload_chunk(r, Q, K, V, dO, lp, base, lbase, jt, j1);
+  }
+  __device__ void put(Stage& st, int jt) {
+    if constexpr (NTH == 256) lstore_chunk(st, r, jt, j1, knorm);
+    else stage_chunk<NTH>(st, Q, K, V, dO, lp, base, lbase, jt, j1, knorm);
+  }
+};
+
 // W' (fp16) of the wave's features as the projections' operand:
 // W'[f0 + 16 nt + l16][32 ks + 8 g + u].
 __device__ inline void load_wreg(const float* __restrict__ W, int f0, int l16, int g,
@@ -370,9 +473,12 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
   const size_t lbase = static_cast<size_t>(bh) * L;
   __syncthreads();
 
+  ChunkLoader<NTH> ld{ChunkRegs{}, Q, K, V, dO, lp, base, lbase, j1, RELU ? 0.f : knorm};
+  ld.next(j0);
   for (int jt = j0; jt < j1; jt += kC) {
-    stage_chunk<NTH>(st, Q, K, V, dO, lp, base, lbase, jt, j1, RELU ? 0.f : knorm);
+    ld.put(st, jt);
     lds_barrier();
+    if (jt + kC < j1) ld.next(jt + kC);
 
     // (1) key features K~ (E orientation) -> kb[nt]: lane = feature, the
     // chunk's 8 keys at positions 8 g ..
@@ -525,7 +631,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
     }
     // (7) sum over the waves, norm term, store.
     reduce_store<NW, RELU>(red, Dq, ps, st.Qh, wave, l16, g, knorm, dQ, base, jt, j1, true);
-    __syncthreads();
+    lds_barrier();   // (LDS only: the next chunk's loads stay in flight)
   }
 }
 
@@ -585,9 +691,12 @@ __global__ __launch_bounds__(NW * 64, 1) void cbg(
   const size_t base = static_cast<size_t>(bh) * L * kD;
   const size_t lbase = static_cast<size_t>(bh) * L;
   __syncthreads();
+  ChunkLoader<NTH> ld{ChunkRegs{}, Q, K, V, dO, lp, base, lbase, j1, 0.f};
+  ld.next(j0);
   for (int jt = j0; jt < j1; jt += kC) {
-    stage_chunk<NTH>(st, Q, K, V, dO, lp, base, lbase, jt, j1, 0.f);
+    ld.put(st, jt);
     lds_barrier();
+    if (jt + kC < j1) ld.next(jt + kC);
     bf16x8 qb[4];
     query_factors_e<NW, RELU>(st, wreg, cst, f0, l16, g, qb);
 #pragma unroll
@@ -596,7 +705,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbg(
 #pragma unroll
       for (int ft = 0; ft < 4; ++ft) gT[ct][ft] = mma_bf16(a, qb[ft], gT[ct][ft]);
     }
-    __syncthreads();
+    lds_barrier();
   }
   float* gs = Gs + (static_cast<size_t>(bh) * nseg + s) * kGRows * M;
 #pragma unroll
@@ -702,10 +811,13 @@ __global__ __launch_bounds__(NW * 64, 1) void cbk(
   const size_t lbase = static_cast<size_t>(bh) * L;
   __syncthreads();
 
+  ChunkLoader<NTH> ld{ChunkRegs{}, Q, K, V, dO, lp, base, lbase, j1, RELU ? 0.f : knorm};
+  ld.next(j0 + kC * (nch - 1));
   for (int t = nch - 1; t >= 0; --t) {
     const int jt = j0 + kC * t;
-    stage_chunk<NTH>(st, Q, K, V, dO, lp, base, lbase, jt, j1, RELU ? 0.f : knorm);
+    ld.put(st, jt);
     lds_barrier();
+    if (t > 0) ld.next(jt - kC);
 
     // (1) key features K~^T (E^T orientation: lane = key 16 nk + l16, rows =
     // features 16 ft + 4 g + v).
@@ -902,7 +1014,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbk(
       const float zs[2] = {0.f, 0.f};
       reduce_store<NW, RELU>(red, Dv, zs, st.Kh, wave, l16, g, knorm, dV, base, jt, j1, false);
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
