@@ -198,15 +198,15 @@ def test_backward_bitwise_deterministic(fv, causal):
 
 
 FULL_BWD = [("text_bidir", False), ("text_causal", True), ("protein_long", False),
-            ("wide_many", False)]
+            ("protein_long", True), ("wide_many", False)]
 
 
 @pytest.mark.parametrize("name,causal", FULL_BWD,
                          ids=[f"{n}-{'causal' if c else 'bidir'}" for n, c in FULL_BWD])
 def test_backward_full_size_sampled(fv, name, causal):
     # The whole workload's backward on the GPU (matrix cores for the d = 64
-    # bidirectional shapes, generic kernels for the causal and d = 128 ones);
-    # the first and last heads against the oracle.
+    # shapes, both forms; generic kernels for d = 128); the first and last
+    # heads against the oracle.
     w = workloads.workload(name)
     if causal:
         w = w.with_(causal=True)
