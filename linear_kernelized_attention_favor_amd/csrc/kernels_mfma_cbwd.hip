@@ -666,7 +666,7 @@ __device__ inline void query_factors_e(const Stage& st, const f16x8 (&wreg)[4][2
 }
 
 template <int NW, bool RELU>
-__global__ __launch_bounds__(NW * 64, 1) void cbg(
+__global__ __launch_bounds__(NW * 64, 2) void cbg(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ cs,
     const float* __restrict__ cP, const float2* __restrict__ lp, float* __restrict__ Gs, int L,
@@ -756,7 +756,7 @@ __global__ __launch_bounds__(256) void cbsuffix(float* __restrict__ Gs, const fl
 //           sc_ij = Q'_i . K~_j for i >= j (over the wave's features).
 // ---------------------------------------------------------------------------
 template <int NW, bool RELU, int MODE>
-__global__ __launch_bounds__(NW * 64, 1) void cbk(
+__global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ cs,
     const float* __restrict__ cP, const float2* __restrict__ lp, const float* __restrict__ Gs,
