@@ -281,3 +281,28 @@ def test_prefill_continues_a_state_with_large_references(fv):
     assert oracle.row_rel_err(_np64(o1), ref[:, :, :cut]) <= TOL["bf16"]
     assert oracle.row_rel_err(_np64(o2), ref[:, :, cut:]) <= TOL["bf16"]
     assert _state_err(st2, k, v, W, "softmax") <= 1e-2
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_prefill_decode_prefill_chain(fv, kernel):
+    # A stream served in turns: a matrix-core prefill, decode steps on the
+    # generic kernel updating that state in place, then a matrix-core prefill
+    # continuing the decoded state (the export/import format read by both
+    # paths, in both directions).
+    shape = (2, 2, 700, 64, 256)
+    q, k, v, W = _case(shape, "bf16", 53)
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    a, b = 300, 310
+    o1, st = fv.prefill(qc[:, :, :a].contiguous(), kc[:, :, :a].contiguous(),
+                        vc[:, :, :a].contiguous(), Wd, kernel=kernel)
+    dec = [fv.decode(qc[:, :, t].contiguous(), kc[:, :, t].contiguous(), vc[:, :, t].contiguous(),
+                     Wd, st, kernel=kernel) for t in range(a, b)]
+    o3, st3 = fv.prefill(qc[:, :, b:].contiguous(), kc[:, :, b:].contiguous(),
+                         vc[:, :, b:].contiguous(), Wd, state_in=st, kernel=kernel)
+    torch.cuda.synchronize()
+    ref = _ref_out(q, k, v, W, kernel)
+    assert oracle.row_rel_err(_np64(o1), ref[:, :, :a]) <= TOL["bf16"]
+    assert oracle.row_rel_err(_np64(torch.stack(dec, 2)), ref[:, :, a:b]) <= TOL["bf16"]
+    assert oracle.row_rel_err(_np64(o3), ref[:, :, b:]) <= TOL["bf16"]
+    assert _state_err(st3, k, v, W, kernel) <= 1e-2
