@@ -269,9 +269,9 @@ __device__ inline void lstore_chunk(Stage& st, const ChunkRegs& r, int jt, int j
   }
 }
 
-// Chunk loads of a sweep: with 256 threads, each chunk's global loads are
-// issued one chunk ahead (next()) and stored to LDS at the start of its turn
-// (put()); otherwise loaded and stored at once.
+// Chunk loads of a sweep: with at least 256 threads, each chunk's global
+// loads are issued one chunk ahead by the first 256 (next()) and stored to
+// LDS at the start of its turn (put()); otherwise loaded and stored at once.
 template <int NTH>
 struct ChunkLoader {
   ChunkRegs r;
@@ -281,20 +281,25 @@ struct ChunkLoader {
   int j1;
   float knorm;
   __device__ void next(int jt) {
-    if constexpr (NTH == 256) gload_chunk(r, Q, K, V, dO, lp, base, lbase, jt, j1);
+    if constexpr (NTH >= 256)
+      if (threadIdx.x < 256) gload_chunk(r, Q, K, V, dO, lp, base, lbase, jt, j1);
   }
   __device__ void put(Stage& st, int jt) {
-    if constexpr (NTH == 256) lstore_chunk(st, r, jt, j1, knorm);
-    else stage_chunk<NTH>(st, Q, K, V, dO, lp, base, lbase, jt, j1, knorm);
+    if constexpr (NTH >= 256) {
+      if (threadIdx.x < 256) lstore_chunk(st, r, jt, j1, knorm);
+    } else {
+      stage_chunk<NTH>(st, Q, K, V, dO, lp, base, lbase, jt, j1, knorm);
+    }
   }
 };
 
 // W' (fp16) of the wave's features as the projections' operand:
 // W'[f0 + 16 nt + l16][32 ks + 8 g + u].
+template <int FT = 4>
 __device__ inline void load_wreg(const float* __restrict__ W, int f0, int l16, int g,
-                                 f16x8 (&wreg)[4][2]) {
+                                 f16x8 (&wreg)[FT][2]) {
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < FT; ++nt) {
     const float* wr = W + static_cast<size_t>(f0 + 16 * nt + l16) * kD + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -327,8 +332,9 @@ __device__ inline void load_wt(const float* __restrict__ W, int m, uint16_t* wt)
 
 // Projections of the chunk's rows X (fp16 in LDS) on the wave's features.
 // E orientation (lane = feature 16 nt + l16, rows = tokens 16 mt + 4 g + v):
-__device__ inline void proj_e(const _Float16 (*X)[kRow], const f16x8 (&wreg)[4][2], int l16,
-                              int g, const f32x4 (&init)[2], f32x4 (&E)[2][4]) {
+template <int FT = 4>
+__device__ inline void proj_e(const _Float16 (*X)[kRow], const f16x8 (&wreg)[FT][2], int l16,
+                              int g, const f32x4 (&init)[2], f32x4 (&E)[2][FT]) {
   f16x8 xa[2][2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -339,11 +345,12 @@ __device__ inline void proj_e(const _Float16 (*X)[kRow], const f16x8 (&wreg)[4][
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) E[mt][nt] = mma_f16(xa[mt][ks], wreg[nt][ks], ks == 0 ? init[mt] : E[mt][nt]);
+      for (int nt = 0; nt < FT; ++nt) E[mt][nt] = mma_f16(xa[mt][ks], wreg[nt][ks], ks == 0 ? init[mt] : E[mt][nt]);
 }
 // E^T orientation (lane = token 16 nt + l16, rows = features 16 mt + 4 g + v):
-__device__ inline void proj_et(const _Float16 (*X)[kRow], const f16x8 (&wreg)[4][2], int l16,
-                               int g, const f32x4 (&init)[4], f32x4 (&E)[4][2]) {
+template <int FT = 4>
+__device__ inline void proj_et(const _Float16 (*X)[kRow], const f16x8 (&wreg)[FT][2], int l16,
+                               int g, const f32x4 (&init)[FT], f32x4 (&E)[FT][2]) {
   f16x8 xb[2][2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
@@ -352,7 +359,7 @@ __device__ inline void proj_et(const _Float16 (*X)[kRow], const f16x8 (&wreg)[4]
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < FT; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) E[mt][nt] = mma_f16(wreg[mt][ks], xb[nt][ks], ks == 0 ? init[mt] : E[mt][nt]);
 }
@@ -418,18 +425,18 @@ __device__ inline bf16x8 dop_t(const Stage& st, int ct, int l16, int g) {
 // State per wave: stT[ct][ft], S^T tiles (lane = feature f0 + 16 ft + l16,
 // rows = columns 16 ct + 4 g + v of [S~ | z~ | z~]), in the frame c*(s).
 // ---------------------------------------------------------------------------
-template <int NW, bool RELU>
+template <int NW, bool RELU, int FT>
 __global__ __launch_bounds__(NW * 64, 1) void cbq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ P,
     const float* __restrict__ cs, const float* __restrict__ cP, const float2* __restrict__ lp,
     uint16_t* __restrict__ dQ, int L, int SEG, int nseg, float knorm) {
   constexpr int NTH = NW * 64;
-  constexpr int M = NW * 64;
+  constexpr int M = NW * 16 * FT;   // FT feature tiles of 16 per wave
   const int s = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int f0 = 64 * wave;
+  const int f0 = 16 * FT * wave;
   __shared__ Stage st;
   __shared__ __align__(16) uint16_t wt[kD * (M + 8)];
   __shared__ __align__(16) float red[NW][kC][kRedRow];
@@ -437,19 +444,19 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
 
   for (int r = tid; r < M; r += NTH) cst[r] = RELU ? 0.f : seg_ref(cs, cP, bh, s, nseg, M, r);
   load_wt<NTH>(W, M, wt);
-  f16x8 wreg[4][2];
-  load_wreg(W, f0, l16, g, wreg);
+  f16x8 wreg[FT][2];
+  load_wreg<FT>(W, f0, l16, g, wreg);
 
   // Carry-in: the prefix state (at cP) moved to c*(s); column 65 repeats z~.
-  f32x4 stT[5][4];
+  f32x4 stT[5][FT];
 #pragma unroll
   for (int ct = 0; ct < 5; ++ct)
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft) stT[ct][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ft = 0; ft < FT; ++ft) stT[ct][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (s > 0) {
     const size_t pb = (static_cast<size_t>(bh) * nseg + s) * (kD + 1);
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft) {
+    for (int ft = 0; ft < FT; ++ft) {
       const int f = f0 + 16 * ft + l16;
       const size_t ci = (static_cast<size_t>(bh) * nseg + s) * M + f;
       const float sc = RELU ? 1.f : fast_exp2(cP[ci] - fmaxf(cP[ci], cs[ci]));
@@ -482,14 +489,14 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
 
     // (1) key features K~ (E orientation) -> kb[nt]: lane = feature, the
     // chunk's 8 keys at positions 8 g ..
-    bf16x8 kb[4];
+    bf16x8 kb[FT];
     {
-      f32x4 SK[2][4];
+      f32x4 SK[2][FT];
       const f32x4 init[2] = {*reinterpret_cast<const f32x4*>(&st.nk[4 * g]),
                              *reinterpret_cast<const f32x4*>(&st.nk[16 + 4 * g])};
-      proj_e(st.Kh, wreg, l16, g, init, SK);
+      proj_e<FT>(st.Kh, wreg, l16, g, init, SK);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < FT; ++nt) {
         const float c = cst[f0 + 16 * nt + l16];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
@@ -500,19 +507,19 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
     }
     // (2) query factors Q' (E^T orientation: lane = query 16 nq + l16, rows
     // = features 16 mt + 4 g + v).
-    f32x4 SQ[4][2];
+    f32x4 SQ[FT][2];
     float rl[2];
     {
-      f32x4 init[4];
+      f32x4 init[FT];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
-      proj_et(st.Qh, wreg, l16, g, init, SQ);
+      for (int mt = 0; mt < FT; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
+      proj_et<FT>(st.Qh, wreg, l16, g, init, SQ);
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) {
         const float Lq = st.Lq[16 * nq + l16];
         rl[nq] = fast_exp2(-Lq);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int mt = 0; mt < FT; ++mt)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
             SQ[mt][nq][v] = RELU ? SQ[mt][nq][v] : fast_exp2(SQ[mt][nq][v] - Lq);
@@ -520,9 +527,9 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
     }
     // (3) T^T = S [dO | -p]^T from the carried state (hi + lo), then (4) the
     // masked in-chunk term K~^T a, a_ji = v_j . dO_i - p_i for j <= i.
-    f32x4 T[4][2];
+    f32x4 T[FT][2];
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
+    for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq) T[ft][nq] = zero4;
 #pragma unroll
@@ -544,7 +551,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
         }
       }
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) {
+      for (int ft = 0; ft < FT; ++ft) {
         bf16x8 ah, al;
         split8(stT[2 * p][ft], p < 2 ? stT[2 * p + 1][ft] : zero4, ah, al);
 #pragma unroll
@@ -585,7 +592,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
         bf16x8 ah, al;
         split8(A[0][nq], A[1][nq], ah, al);
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) {
+        for (int ft = 0; ft < FT; ++ft) {
           T[ft][nq] = mma_bf16(kb[ft], ah, T[ft][nq]);
           T[ft][nq] = mma_bf16(kb[ft], al, T[ft][nq]);
         }
@@ -594,7 +601,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
     // (5) P = Q' T (ReLU: [s > 0] T 2^-L), in place of Q'; per-query sums.
     float ps[2] = {0.f, 0.f};
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
+    for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq)
 #pragma unroll
@@ -616,7 +623,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
       Dq[at][0] = zero4;
       Dq[at][1] = zero4;
 #pragma unroll
-      for (int kf = 0; kf < 2; ++kf) {
+      for (int kf = 0; kf < FT / 2; ++kf) {
         const bf16x8 wa = *reinterpret_cast<const bf16x8*>(&wt[(16 * at + l16) * (M + 8) + f0 + 32 * kf + 8 * g]);
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq) Dq[at][nq] = mma_bf16(wa, pack8(SQ[2 * kf][nq], SQ[2 * kf + 1][nq]), Dq[at][nq]);
@@ -627,7 +634,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
     for (int ct = 0; ct < 5; ++ct) {
       const bf16x8 va = ct < 4 ? *reinterpret_cast<const bf16x8*>(&st.Vt[16 * ct + l16][4 * g]) : ones;
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) stT[ct][ft] = mma_bf16(va, kb[ft], stT[ct][ft]);
+      for (int ft = 0; ft < FT; ++ft) stT[ct][ft] = mma_bf16(va, kb[ft], stT[ct][ft]);
     }
     // (7) sum over the waves, norm term, store.
     reduce_store<NW, RELU>(red, Dq, ps, st.Qh, wave, l16, g, knorm, dQ, base, jt, j1, true);
@@ -1032,8 +1039,9 @@ hipError_t launch_cbwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const
   float* Gs = reinterpret_cast<float*>(ws + b.off_G);
   const dim3 grid(p.nseg, p.BH);
   timing_before(st);
-  cbq<NW, RELU><<<grid, NW * 64, 0, st>>>(Q, K, V, dO, W, P, cs, cP, lp, dQ, p.L, p.seg, p.nseg,
-                                          p.knorm);
+  // dq: 32 features per wave (twice the waves, half the registers each)
+  cbq<2 * NW, RELU, 2><<<grid, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, P, cs, cP, lp, dQ, p.L, p.seg,
+                                                     p.nseg, p.knorm);
   e = hipGetLastError();
   timing_after(st, "cbq");
   if (e != hipSuccess) return e;
