@@ -647,16 +647,16 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
 // G^T = sum_i [dO_i | -p_hi,i | -p_lo,i]^T Q'_i in the frame c*(s), written
 // as Gs[bh][s][66][m] fp32 (row = column of [dO | -p_hi | -p_lo]).
 // ---------------------------------------------------------------------------
-template <int NW, bool RELU>
-__device__ inline void query_factors_e(const Stage& st, const f16x8 (&wreg)[4][2], const float* cst,
-                                       int f0, int l16, int g, bf16x8 (&qb)[4]) {
-  f32x4 E[2][4];
+template <bool RELU, int FT = 4>
+__device__ inline void query_factors_e(const Stage& st, const f16x8 (&wreg)[FT][2], const float* cst,
+                                       int f0, int l16, int g, bf16x8 (&qb)[FT]) {
+  f32x4 E[2][FT];
   const f32x4 init[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  proj_e(st.Qh, wreg, l16, g, init, E);
+  proj_e<FT>(st.Qh, wreg, l16, g, init, E);
   const f32x4 L0 = *reinterpret_cast<const f32x4*>(&st.Lq[4 * g]);
   const f32x4 L1 = *reinterpret_cast<const f32x4*>(&st.Lq[16 + 4 * g]);
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
+  for (int nt = 0; nt < FT; ++nt) {
     const float c = cst[f0 + 16 * nt + l16];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -672,28 +672,28 @@ __device__ inline void query_factors_e(const Stage& st, const f16x8 (&wreg)[4][2
   }
 }
 
-template <int NW, bool RELU>
+template <int NW, bool RELU, int FT>
 __global__ __launch_bounds__(NW * 64, 2) void cbg(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ cs,
     const float* __restrict__ cP, const float2* __restrict__ lp, float* __restrict__ Gs, int L,
     int SEG, int nseg) {
   constexpr int NTH = NW * 64;
-  constexpr int M = NW * 64;
+  constexpr int M = NW * 16 * FT;
   const int s = blockIdx.x + 1, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int f0 = 64 * wave;
+  const int f0 = 16 * FT * wave;
   __shared__ Stage st;
   __shared__ __align__(16) float cst[M];
   for (int r = tid; r < M; r += NTH) cst[r] = RELU ? 0.f : seg_ref(cs, cP, bh, s, nseg, M, r);
-  f16x8 wreg[4][2];
-  load_wreg(W, f0, l16, g, wreg);
-  f32x4 gT[5][4];
+  f16x8 wreg[FT][2];
+  load_wreg<FT>(W, f0, l16, g, wreg);
+  f32x4 gT[5][FT];
 #pragma unroll
   for (int ct = 0; ct < 5; ++ct)
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft) gT[ct][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ft = 0; ft < FT; ++ft) gT[ct][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int j0 = s * SEG, j1 = min(L, j0 + SEG);
   const size_t base = static_cast<size_t>(bh) * L * kD;
   const size_t lbase = static_cast<size_t>(bh) * L;
@@ -704,13 +704,13 @@ __global__ __launch_bounds__(NW * 64, 2) void cbg(
     ld.put(st, jt);
     lds_barrier();
     if (jt + kC < j1) ld.next(jt + kC);
-    bf16x8 qb[4];
-    query_factors_e<NW, RELU>(st, wreg, cst, f0, l16, g, qb);
+    bf16x8 qb[FT];
+    query_factors_e<RELU, FT>(st, wreg, cst, f0, l16, g, qb);
 #pragma unroll
     for (int ct = 0; ct < 5; ++ct) {
       const bf16x8 a = dop_t(st, ct, l16, g);
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) gT[ct][ft] = mma_bf16(a, qb[ft], gT[ct][ft]);
+      for (int ft = 0; ft < FT; ++ft) gT[ct][ft] = mma_bf16(a, qb[ft], gT[ct][ft]);
     }
     lds_barrier();
   }
@@ -722,7 +722,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cbg(
       const int col = 16 * ct + 4 * g + v;
       if (col < kGRows) {
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) gs[static_cast<size_t>(col) * M + f0 + 16 * ft + l16] = gT[ct][ft][v];
+        for (int ft = 0; ft < FT; ++ft) gs[static_cast<size_t>(col) * M + f0 + 16 * ft + l16] = gT[ct][ft][v];
       }
     }
 }
@@ -762,7 +762,7 @@ __global__ __launch_bounds__(256) void cbsuffix(float* __restrict__ Gs, const fl
 //           features); dv^T = G^T K~^T plus the masked term dO^T sc,
 //           sc_ij = Q'_i . K~_j for i >= j (over the wave's features).
 // ---------------------------------------------------------------------------
-template <int NW, bool RELU, int MODE>
+template <int NW, bool RELU, int MODE, int FT>
 __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ cs,
@@ -770,11 +770,11 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int L, int SEG, int nseg,
     float knorm) {
   constexpr int NTH = NW * 64;
-  constexpr int M = NW * 64;
+  constexpr int M = NW * 16 * FT;   // FT feature tiles of 16 per wave
   const int s = blockIdx.x, bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
-  const int f0 = 64 * wave;
+  const int f0 = 16 * FT * wave;
   __shared__ Stage st;
   __shared__ __align__(16) uint16_t wt[MODE == 0 ? kD * (M + 8) : 8];
   __shared__ __align__(16) float red[NW][kC][kRedRow];
@@ -782,19 +782,19 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
 
   for (int r = tid; r < M; r += NTH) cst[r] = RELU ? 0.f : seg_ref(cs, cP, bh, s, nseg, M, r);
   if constexpr (MODE == 0) load_wt<NTH>(W, M, wt);
-  f16x8 wreg[4][2];
-  load_wreg(W, f0, l16, g, wreg);
+  f16x8 wreg[FT][2];
+  load_wreg<FT>(W, f0, l16, g, wreg);
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Carry-in: the suffix state of the later segments.
   const float* gs = Gs + (static_cast<size_t>(bh) * nseg + s) * kGRows * M;
-  f32x4 gT[MODE == 0 ? 5 : 1][4];
-  f32x4 gF[MODE == 1 ? 4 : 1][4];
+  f32x4 gT[MODE == 0 ? 5 : 1][FT];
+  f32x4 gF[MODE == 1 ? FT : 1][4];
   if constexpr (MODE == 0) {
 #pragma unroll
     for (int ct = 0; ct < 5; ++ct)
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft)
+      for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int col = 16 * ct + 4 * g + v;
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
         }
   } else {
 #pragma unroll
-    for (int ft = 0; ft < 4; ++ft)
+    for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
       for (int at = 0; at < 4; ++at) {
         const int col = 16 * at + l16;
@@ -828,34 +828,34 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
 
     // (1) key features K~^T (E^T orientation: lane = key 16 nk + l16, rows =
     // features 16 ft + 4 g + v).
-    f32x4 EK[4][2];
+    f32x4 EK[FT][2];
     {
-      f32x4 init[4];
+      f32x4 init[FT];
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) {
+      for (int ft = 0; ft < FT; ++ft) {
         const f32x4 c = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * ft + 4 * g]);
         init[ft] = -c;
       }
-      proj_et(st.Kh, wreg, l16, g, init, EK);
+      proj_et<FT>(st.Kh, wreg, l16, g, init, EK);
 #pragma unroll
       for (int nk = 0; nk < 2; ++nk) {
         const float n = st.nk[16 * nk + l16];
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft)
+        for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
           for (int v = 0; v < 4; ++v) EK[ft][nk][v] = feature<RELU>(EK[ft][nk][v] + n);
       }
     }
     // Query factors Q' (E orientation, lane = feature): the state update's
     // operand and, for dk, the masked term's.
-    bf16x8 qb[4];
-    query_factors_e<NW, RELU>(st, wreg, cst, f0, l16, g, qb);
+    bf16x8 qb[FT];
+    query_factors_e<RELU, FT>(st, wreg, cst, f0, l16, g, qb);
 
     if constexpr (MODE == 0) {
       // (2) H^T = G [v | 1 | 1]^T (G hi + lo).
-      f32x4 H[4][2];
+      f32x4 H[FT][2];
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) H[ft][0] = H[ft][1] = zero4;
+      for (int ft = 0; ft < FT; ++ft) H[ft][0] = H[ft][1] = zero4;
 #pragma unroll
       for (int p = 0; p < 3; ++p) {
         bf16x8 vb[2];
@@ -871,7 +871,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
           }
         }
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) {
+        for (int ft = 0; ft < FT; ++ft) {
           bf16x8 ah, al;
           split8(gT[2 * p][ft], p < 2 ? gT[2 * p + 1][ft] : zero4, ah, al);
 #pragma unroll
@@ -913,7 +913,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
           bf16x8 bh_, bl_;
           split8(Bm[0][nk], Bm[1][nk], bh_, bl_);
 #pragma unroll
-          for (int ft = 0; ft < 4; ++ft) {
+          for (int ft = 0; ft < FT; ++ft) {
             H[ft][nk] = mma_bf16(qb[ft], bh_, H[ft][nk]);
             H[ft][nk] = mma_bf16(qb[ft], bl_, H[ft][nk]);
           }
@@ -922,7 +922,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
       // (4) R = K~ H (ReLU: [e > 0] H), per-key sums.
       float rs[2] = {0.f, 0.f};
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft)
+      for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int nk = 0; nk < 2; ++nk)
 #pragma unroll
@@ -942,7 +942,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
       for (int at = 0; at < 4; ++at) {
         Dk[at][0] = Dk[at][1] = zero4;
 #pragma unroll
-        for (int kf = 0; kf < 2; ++kf) {
+        for (int kf = 0; kf < FT / 2; ++kf) {
           const bf16x8 wa = *reinterpret_cast<const bf16x8*>(&wt[(16 * at + l16) * (M + 8) + f0 + 32 * kf + 8 * g]);
 #pragma unroll
           for (int nk = 0; nk < 2; ++nk) Dk[at][nk] = mma_bf16(wa, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Dk[at][nk]);
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
       for (int ct = 0; ct < 5; ++ct) {
         const bf16x8 a = dop_t(st, ct, l16, g);
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) gT[ct][ft] = mma_bf16(a, qb[ft], gT[ct][ft]);
+        for (int ft = 0; ft < FT; ++ft) gT[ct][ft] = mma_bf16(a, qb[ft], gT[ct][ft]);
       }
       reduce_store<NW, RELU>(red, Dk, rs, st.Kh, wave, l16, g, knorm, dK, base, jt, j1, true);
     } else {
@@ -963,7 +963,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
       for (int at = 0; at < 4; ++at) {
         Dv[at][0] = Dv[at][1] = zero4;
 #pragma unroll
-        for (int kf = 0; kf < 2; ++kf) {
+        for (int kf = 0; kf < FT / 2; ++kf) {
           const bf16x8 ga = pack8(gF[2 * kf][at], gF[2 * kf + 1][at]);
 #pragma unroll
           for (int nk = 0; nk < 2; ++nk) Dv[at][nk] = mma_bf16(ga, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Dv[at][nk]);
@@ -972,16 +972,16 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
       // (3) masked term: sc (queries x keys) = Q' K~^T over the wave's
       // features for i >= j, then dv^T += dO^T sc.
       {
-        f32x4 SQ[4][2];   // Q' in the E^T orientation (lane = query)
-        f32x4 init[4];
+        f32x4 SQ[FT][2];   // Q' in the E^T orientation (lane = query)
+        f32x4 init[FT];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
-        proj_et(st.Qh, wreg, l16, g, init, SQ);
+        for (int mt = 0; mt < FT; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
+        proj_et<FT>(st.Qh, wreg, l16, g, init, SQ);
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq) {
           const float Lq = st.Lq[16 * nq + l16];
 #pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
+          for (int mt = 0; mt < FT; ++mt)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
               SQ[mt][nq][v] = RELU ? fmaxf(SQ[mt][nq][v], 0.f) * fast_exp2(-Lq) : fast_exp2(SQ[mt][nq][v] - Lq);
@@ -990,7 +990,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
 #pragma unroll
         for (int mi = 0; mi < 2; ++mi) Sc[mi][0] = Sc[mi][1] = zero4;
 #pragma unroll
-        for (int kf = 0; kf < 2; ++kf)
+        for (int kf = 0; kf < FT / 2; ++kf)
 #pragma unroll
           for (int mi = 0; mi < 2; ++mi) {
             const bf16x8 qa = pack8(SQ[2 * kf][mi], SQ[2 * kf + 1][mi]);
@@ -1016,7 +1016,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
       for (int at = 0; at < 4; ++at) {
         const bf16x8 b = *reinterpret_cast<const bf16x8*>(&st.Gt[16 * at + l16][4 * g]);
 #pragma unroll
-        for (int ft = 0; ft < 4; ++ft) gF[ft][at] = mma_bf16(qb[ft], b, gF[ft][at]);
+        for (int ft = 0; ft < FT; ++ft) gF[ft][at] = mma_bf16(qb[ft], b, gF[ft][at]);
       }
       const float zs[2] = {0.f, 0.f};
       reduce_store<NW, RELU>(red, Dv, zs, st.Kh, wave, l16, g, knorm, dV, base, jt, j1, false);
@@ -1047,7 +1047,7 @@ hipError_t launch_cbwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const
   if (e != hipSuccess) return e;
   if (p.nseg > 1) {
     timing_before(st);
-    cbg<NW, RELU><<<dim3(p.nseg - 1, p.BH), NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, p.L,
+    cbg<NW, RELU, 4><<<dim3(p.nseg - 1, p.BH), NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, p.L,
                                                               p.seg, p.nseg);
     e = hipGetLastError();
     timing_after(st, "cbg");
@@ -1059,14 +1059,14 @@ hipError_t launch_cbwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const
   timing_after(st, "cbsuffix");
   if (e != hipSuccess) return e;
   timing_before(st);
-  cbk<NW, RELU, 0><<<grid, NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK, dV, p.L, p.seg,
-                                             p.nseg, p.knorm);
+  cbk<2 * NW, RELU, 0, 2><<<grid, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK, dV, p.L,
+                                                        p.seg, p.nseg, p.knorm);
   e = hipGetLastError();
   timing_after(st, "cbk_dk");
   if (e != hipSuccess) return e;
   timing_before(st);
-  cbk<NW, RELU, 1><<<grid, NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK, dV, p.L, p.seg,
-                                             p.nseg, p.knorm);
+  cbk<NW, RELU, 1, 4><<<grid, NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK, dV, p.L, p.seg,
+                                                p.nseg, p.knorm);
   e = hipGetLastError();
   timing_after(st, "cbk_dv");
   return e;
