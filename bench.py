@@ -256,7 +256,7 @@ FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "
                  "g_combine", "g_apply", "gb_query", "gb_gstate", "gb_gcombine", "gb_key",
                  "bprep", "bcombine", "bqr", "gcombine", "bkeyr", "sexport", "g_decode",
                  "g_state_reset", "draw_block", "g_feature_map", "cbq", "cbg", "cbsuffix")
-# passes of the templated backward kernels, by their last template argument
+# passes of the templated backward kernels, by their third template argument
 _PASSES = {"bqr": ("bq_den", "bq_dq", "bq_g"), "bkeyr": ("bkey_dk", "bkey_dv"),
            "cbk": ("cbk_dk", "cbk_dv")}
 
@@ -267,13 +267,14 @@ def _favor_kernel(name: str):
     m = re.search(r"favor::\(anonymous namespace\)::(\w+)(?:<([^>]*)>)?\(", name)
     if m:
         k, targs = m.group(1), m.group(2) or ""
-        mode = re.search(r"(\d+)\s*$", targs)
-    else:   # _ZN5favor12_GLOBAL__N_1<len><name>I...
+        args = [a.strip() for a in targs.split(",")] if targs else []
+    else:   # _ZN5favor12_GLOBAL__N_1<len><name>I<L..E>...E
         m = re.search(r"_ZN5favor12_GLOBAL__N_1(\d+)", name)
         k = name[m.end():m.end() + int(m.group(1))] if m else None
-        mode = re.search(r"ELi(\d+)EE", name[m.end():]) if m else None
-    if k in _PASSES and mode is not None:
-        return _PASSES[k][int(mode.group(1))]
+        rest = name[m.end() + int(m.group(1)):] if m else ""
+        args = re.findall(r"L[a-z](\d+)E", rest.split("EEv")[0] + "E") if rest.startswith("I") else []
+    if k in _PASSES and len(args) >= 3 and args[2].isdigit():
+        return _PASSES[k][int(args[2])]
     if k == "cscan":   # the backward's variant (last template argument true)
         tail = (m.group(2) or "") if "(anonymous namespace)" in name else name[m.end():]
         if re.search(r"true\s*$", tail) or re.search(r"ELb1EE", tail):
