@@ -39,8 +39,9 @@
 //                     (G tiles)
 // Within a chunk the masked terms pair the chunk's keys and queries
 // directly (32 x 32 products); every reduction over features is split across
-// the waves (wave w owns features [64 w, 64 w + 64)) and summed through LDS
-// in wave order, so results are bitwise reproducible.
+// the waves (wave w owns features [16 FT w, 16 FT (w + 1)), FT = 2 or 4
+// feature tiles of 16) and summed through LDS in wave order, so results are
+// bitwise reproducible.
 //
 // Numerics as the bidirectional backward: projections in fp16 (Q, K exact,
 // W' rounded); features rounded to bf16 as operands; the carried states and
@@ -421,7 +422,7 @@ __device__ inline bf16x8 dop_t(const Stage& st, int ct, int l16, int g) {
 }
 
 // ---------------------------------------------------------------------------
-// cbq: grid (nseg, BH), NW = m / 64 waves.  dq of the segment's queries.
+// cbq: grid (nseg, BH), NW = m / (16 FT) waves.  dq of the segment's queries.
 // State per wave: stT[ct][ft], S^T tiles (lane = feature f0 + 16 ft + l16,
 // rows = columns 16 ct + 4 g + v of [S~ | z~ | z~]), in the frame c*(s).
 // ---------------------------------------------------------------------------
@@ -752,7 +753,7 @@ __global__ __launch_bounds__(256) void cbsuffix(float* __restrict__ Gs, const fl
 }
 
 // ---------------------------------------------------------------------------
-// cbk: grid (nseg, BH), NW waves; the segment's chunks in reverse order with
+// cbk: grid (nseg, BH), NW = m / (16 FT) waves; the segment's chunks in reverse order with
 // the suffix query state carried in registers (queries of later chunks and
 // segments), in the frame c*(s).
 //   MODE 0: dk.  G^T tiles gT[ct][ft] (lane = feature, rows = columns of
@@ -1058,6 +1059,8 @@ hipError_t launch_cbwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const
   e = hipGetLastError();
   timing_after(st, "cbsuffix");
   if (e != hipSuccess) return e;
+  // dk: 32 features per wave, as dq; dv: 64 per wave, two work-groups per
+  // compute unit
   timing_before(st);
   cbk<2 * NW, RELU, 0, 2><<<grid, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK, dV, p.L,
                                                         p.seg, p.nseg, p.knorm);
