@@ -266,3 +266,28 @@ def test_backward_graph_replays_match_eager(fv):
         torch.cuda.synchronize()
         for a, b in zip(outs, eager):
             assert torch.equal(a, b)
+
+
+def test_causal_backward_with_key_exponents_climbing_through_a_segment(fv):
+    # Keys along the first feature's direction with a growing length: that
+    # feature's exponent |w_0| t - t^2 / 2 climbs by ~27 (natural units) over
+    # the sequence, so a segment's frame sits far above its first keys and
+    # the early queries' factors 2^(s + c - L) are large; the gradients must
+    # still match the oracle (matrix cores, bf16).
+    B, H, L, d, m = 1, 2, 1200, 64, 128
+    rng = np.random.default_rng(71)
+    W = oracle.draw_w(72, m, d).astype(np.float32)
+    mu = W[0] / np.linalg.norm(W[0])
+    ramp = np.linspace(0, 5, L, dtype=np.float32)[:, None]
+    k = rng.standard_normal((B, H, L, d)).astype(np.float32) * 0.1 + ramp * mu
+    q = rng.standard_normal((B, H, L, d)).astype(np.float32) * 0.3
+    v = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    do = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    q, k, v, do = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v, do))
+    assert fv.plan_describe(B, H, L, d, m, fv.BF16, True)[0] == 1
+    got = _gpu(fv, q, k, v, W, do, True, "softmax")
+    ref = _oracle(q, k, v, W, do, True, "softmax")
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert torch.isfinite(g).all(), name
+        err = grad_err(_np64(g), r)
+        assert err <= TOL["bf16"], (name, err)
