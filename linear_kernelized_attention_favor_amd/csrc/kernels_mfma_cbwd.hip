@@ -422,19 +422,21 @@ __device__ inline bf16x8 dop_t(const Stage& st, int ct, int l16, int g) {
 }
 
 // ---------------------------------------------------------------------------
-// cbq: grid (nseg, BH), NW = m / (16 FT) waves.  dq of the segment's queries.
-// State per wave: stT[ct][ft], S^T tiles (lane = feature f0 + 16 ft + l16,
-// rows = columns 16 ct + 4 g + v of [S~ | z~ | z~]), in the frame c*(s).
+// cbq: grid (ceil(nseg / spw), BH), NW = m / (16 FT) waves.  dq of the
+// queries of spw consecutive segments, in order.  State per wave: stT[ct][ft],
+// S^T tiles (lane = feature f0 + 16 ft + l16, rows = columns 16 ct + 4 g + v
+// of [S~ | z~ | z~]), in the frame c*(s) of the segment being swept (moved to
+// the next segment's frame at its start, factors 2^(c*(s) - c*(s+1)) <= 1).
 // ---------------------------------------------------------------------------
 template <int NW, bool RELU, int FT>
 __global__ __launch_bounds__(NW * 64, 1) void cbq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ P,
     const float* __restrict__ cs, const float* __restrict__ cP, const float2* __restrict__ lp,
-    uint16_t* __restrict__ dQ, int L, int SEG, int nseg, float knorm) {
+    uint16_t* __restrict__ dQ, int L, int SEG, int nseg, int spw, float knorm) {
   constexpr int NTH = NW * 64;
   constexpr int M = NW * 16 * FT;   // FT feature tiles of 16 per wave
-  const int s = blockIdx.x, bh = blockIdx.y;
+  const int sA = blockIdx.x * spw, sB = min(nseg, sA + spw), bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int f0 = 16 * FT * wave;
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
   __shared__ __align__(16) float red[NW][kC][kRedRow];
   __shared__ __align__(16) float cst[M];
 
-  for (int r = tid; r < M; r += NTH) cst[r] = RELU ? 0.f : seg_ref(cs, cP, bh, s, nseg, M, r);
+  for (int r = tid; r < M; r += NTH) cst[r] = RELU ? 0.f : seg_ref(cs, cP, bh, sA, nseg, M, r);
   load_wt<NTH>(W, M, wt);
   f16x8 wreg[FT][2];
   load_wreg<FT>(W, f0, l16, g, wreg);
@@ -454,12 +456,12 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
   for (int ct = 0; ct < 5; ++ct)
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) stT[ct][ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (s > 0) {
-    const size_t pb = (static_cast<size_t>(bh) * nseg + s) * (kD + 1);
+  if (sA > 0) {
+    const size_t pb = (static_cast<size_t>(bh) * nseg + sA) * (kD + 1);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const int f = f0 + 16 * ft + l16;
-      const size_t ci = (static_cast<size_t>(bh) * nseg + s) * M + f;
+      const size_t ci = (static_cast<size_t>(bh) * nseg + sA) * M + f;
       const float sc = RELU ? 1.f : fast_exp2(cP[ci] - fmaxf(cP[ci], cs[ci]));
 #pragma unroll
       for (int ct = 0; ct < 5; ++ct)
@@ -476,170 +478,189 @@ __global__ __launch_bounds__(NW * 64, 1) void cbq(
   const bf16x8 ones = (l16 < 2) ? __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u))
                                 : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 
-  const int j0 = s * SEG, j1 = min(L, j0 + SEG);
   const size_t base = static_cast<size_t>(bh) * L * kD;
   const size_t lbase = static_cast<size_t>(bh) * L;
   __syncthreads();
 
-  ChunkLoader<NTH> ld{ChunkRegs{}, Q, K, V, dO, lp, base, lbase, j1, RELU ? 0.f : knorm};
-  ld.next(j0);
-  for (int jt = j0; jt < j1; jt += kC) {
-    ld.put(st, jt);
-    lds_barrier();
-    if (jt + kC < j1) ld.next(jt + kC);
-
-    // (1) key features K~ (E orientation) -> kb[nt]: lane = feature, the
-    // chunk's 8 keys at positions 8 g ..
-    bf16x8 kb[FT];
-    {
-      f32x4 SK[2][FT];
-      const f32x4 init[2] = {*reinterpret_cast<const f32x4*>(&st.nk[4 * g]),
-                             *reinterpret_cast<const f32x4*>(&st.nk[16 + 4 * g])};
-      proj_e<FT>(st.Kh, wreg, l16, g, init, SK);
-#pragma unroll
-      for (int nt = 0; nt < FT; ++nt) {
-        const float c = cst[f0 + 16 * nt + l16];
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) SK[mt][nt][v] = feature<RELU>(SK[mt][nt][v] - c);
-        kb[nt] = pack8(SK[0][nt], SK[1][nt]);
-      }
-    }
-    // (2) query factors Q' (E^T orientation: lane = query 16 nq + l16, rows
-    // = features 16 mt + 4 g + v).
-    f32x4 SQ[FT][2];
-    float rl[2];
-    {
-      f32x4 init[FT];
-#pragma unroll
-      for (int mt = 0; mt < FT; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
-      proj_et<FT>(st.Qh, wreg, l16, g, init, SQ);
-#pragma unroll
-      for (int nq = 0; nq < 2; ++nq) {
-        const float Lq = st.Lq[16 * nq + l16];
-        rl[nq] = fast_exp2(-Lq);
-#pragma unroll
-        for (int mt = 0; mt < FT; ++mt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            SQ[mt][nq][v] = RELU ? SQ[mt][nq][v] : fast_exp2(SQ[mt][nq][v] - Lq);
-      }
-    }
-    // (3) T^T = S [dO | -p]^T from the carried state (hi + lo), then (4) the
-    // masked in-chunk term K~^T a, a_ji = v_j . dO_i - p_i for j <= i.
-    f32x4 T[FT][2];
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int nq = 0; nq < 2; ++nq) T[ft][nq] = zero4;
-#pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      bf16x8 db[2];
-#pragma unroll
-      for (int nq = 0; nq < 2; ++nq) {
-        const int q = 16 * nq + l16;
-        if (p < 2) {
-          const uint2 a = *reinterpret_cast<const uint2*>(&st.Gr[q][32 * p + 4 * g]);
-          const uint2 b = *reinterpret_cast<const uint2*>(&st.Gr[q][32 * p + 16 + 4 * g]);
-          db[nq] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-        } else {
-          const float pv = -st.pq[q];
-          const uint16_t hi = bf16_bits(pv);
-          const uint16_t lo = bf16_bits(pv - bf16_val(hi));
-          db[nq] = __builtin_bit_cast(
-              bf16x8, make_uint4(g == 0 ? (static_cast<uint32_t>(lo) << 16) | hi : 0u, 0u, 0u, 0u));
-        }
-      }
+  ChunkLoader<NTH> ld{ChunkRegs{}, Q, K, V, dO, lp, base, lbase, 0, RELU ? 0.f : knorm};
+  for (int s = sA; s < sB; ++s) {
+    if (!RELU && s > sA) {
+      // the carried state into segment s's frame
+      float fac[FT];
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
-        bf16x8 ah, al;
-        split8(stT[2 * p][ft], p < 2 ? stT[2 * p + 1][ft] : zero4, ah, al);
+        const int f = f0 + 16 * ft + l16;
+        fac[ft] = fast_exp2(cst[f] - seg_ref(cs, cP, bh, s, nseg, M, f));
+      }
+      lds_barrier();   // every wave has read the previous frame
+      for (int r = tid; r < M; r += NTH) cst[r] = seg_ref(cs, cP, bh, s, nseg, M, r);
+#pragma unroll
+      for (int ct = 0; ct < 5; ++ct)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) stT[ct][ft] *= fac[ft];
+      lds_barrier();
+    }
+    const int j0 = s * SEG, j1 = min(L, j0 + SEG);
+    ld.j1 = j1;
+    ld.next(j0);
+    for (int jt = j0; jt < j1; jt += kC) {
+      ld.put(st, jt);
+      lds_barrier();
+      if (jt + kC < j1) ld.next(jt + kC);
+
+      // (1) key features K~ (E orientation) -> kb[nt]: lane = feature, the
+      // chunk's 8 keys at positions 8 g ..
+      bf16x8 kb[FT];
+      {
+        f32x4 SK[2][FT];
+        const f32x4 init[2] = {*reinterpret_cast<const f32x4*>(&st.nk[4 * g]),
+                               *reinterpret_cast<const f32x4*>(&st.nk[16 + 4 * g])};
+        proj_e<FT>(st.Kh, wreg, l16, g, init, SK);
+#pragma unroll
+        for (int nt = 0; nt < FT; ++nt) {
+          const float c = cst[f0 + 16 * nt + l16];
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) SK[mt][nt][v] = feature<RELU>(SK[mt][nt][v] - c);
+          kb[nt] = pack8(SK[0][nt], SK[1][nt]);
+        }
+      }
+      // (2) query factors Q' (E^T orientation: lane = query 16 nq + l16, rows
+      // = features 16 mt + 4 g + v).
+      f32x4 SQ[FT][2];
+      float rl[2];
+      {
+        f32x4 init[FT];
+#pragma unroll
+        for (int mt = 0; mt < FT; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
+        proj_et<FT>(st.Qh, wreg, l16, g, init, SQ);
 #pragma unroll
         for (int nq = 0; nq < 2; ++nq) {
-          T[ft][nq] = mma_bf16(ah, db[nq], T[ft][nq]);
-          T[ft][nq] = mma_bf16(al, db[nq], T[ft][nq]);
+          const float Lq = st.Lq[16 * nq + l16];
+          rl[nq] = fast_exp2(-Lq);
+#pragma unroll
+          for (int mt = 0; mt < FT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              SQ[mt][nq][v] = RELU ? SQ[mt][nq][v] : fast_exp2(SQ[mt][nq][v] - Lq);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    {
-      f32x4 A[2][2];   // [mk][nq]: lane = query 16 nq + l16, rows = keys 16 mk + 4 g + v
+      // (3) T^T = S [dO | -p]^T from the carried state (hi + lo), then (4) the
+      // masked in-chunk term K~^T a, a_ji = v_j . dO_i - p_i for j <= i.
+      f32x4 T[FT][2];
 #pragma unroll
-      for (int mk = 0; mk < 2; ++mk)
+      for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-        for (int nq = 0; nq < 2; ++nq) A[mk][nq] = zero4;
+        for (int nq = 0; nq < 2; ++nq) T[ft][nq] = zero4;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 va[2], ga[2];
+      for (int p = 0; p < 3; ++p) {
+        bf16x8 db[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          va[i] = *reinterpret_cast<const bf16x8*>(&st.Vr[16 * i + l16][32 * ks + 8 * g]);
-          ga[i] = *reinterpret_cast<const bf16x8*>(&st.Gr[16 * i + l16][32 * ks + 8 * g]);
+        for (int nq = 0; nq < 2; ++nq) {
+          const int q = 16 * nq + l16;
+          if (p < 2) {
+            const uint2 a = *reinterpret_cast<const uint2*>(&st.Gr[q][32 * p + 4 * g]);
+            const uint2 b = *reinterpret_cast<const uint2*>(&st.Gr[q][32 * p + 16 + 4 * g]);
+            db[nq] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+          } else {
+            const float pv = -st.pq[q];
+            const uint16_t hi = bf16_bits(pv);
+            const uint16_t lo = bf16_bits(pv - bf16_val(hi));
+            db[nq] = __builtin_bit_cast(
+                bf16x8, make_uint4(g == 0 ? (static_cast<uint32_t>(lo) << 16) | hi : 0u, 0u, 0u, 0u));
+          }
         }
-#pragma unroll
-        for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-          for (int nq = 0; nq < 2; ++nq) A[mk][nq] = mma_bf16(va[mk], ga[nq], A[mk][nq]);
-      }
-#pragma unroll
-      for (int nq = 0; nq < 2; ++nq) {
-        const int q = 16 * nq + l16;
-        const float pv = st.pq[q];
-#pragma unroll
-        for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) A[mk][nq][v] = (16 * mk + 4 * g + v <= q) ? A[mk][nq][v] - pv : 0.f;
-        bf16x8 ah, al;
-        split8(A[0][nq], A[1][nq], ah, al);
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) {
-          T[ft][nq] = mma_bf16(kb[ft], ah, T[ft][nq]);
-          T[ft][nq] = mma_bf16(kb[ft], al, T[ft][nq]);
+          bf16x8 ah, al;
+          split8(stT[2 * p][ft], p < 2 ? stT[2 * p + 1][ft] : zero4, ah, al);
+#pragma unroll
+          for (int nq = 0; nq < 2; ++nq) {
+            T[ft][nq] = mma_bf16(ah, db[nq], T[ft][nq]);
+            T[ft][nq] = mma_bf16(al, db[nq], T[ft][nq]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {
+        f32x4 A[2][2];   // [mk][nq]: lane = query 16 nq + l16, rows = keys 16 mk + 4 g + v
+#pragma unroll
+        for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+          for (int nq = 0; nq < 2; ++nq) A[mk][nq] = zero4;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 va[2], ga[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            va[i] = *reinterpret_cast<const bf16x8*>(&st.Vr[16 * i + l16][32 * ks + 8 * g]);
+            ga[i] = *reinterpret_cast<const bf16x8*>(&st.Gr[16 * i + l16][32 * ks + 8 * g]);
+          }
+#pragma unroll
+          for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+            for (int nq = 0; nq < 2; ++nq) A[mk][nq] = mma_bf16(va[mk], ga[nq], A[mk][nq]);
+        }
+#pragma unroll
+        for (int nq = 0; nq < 2; ++nq) {
+          const int q = 16 * nq + l16;
+          const float pv = st.pq[q];
+#pragma unroll
+          for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) A[mk][nq][v] = (16 * mk + 4 * g + v <= q) ? A[mk][nq][v] - pv : 0.f;
+          bf16x8 ah, al;
+          split8(A[0][nq], A[1][nq], ah, al);
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) {
+            T[ft][nq] = mma_bf16(kb[ft], ah, T[ft][nq]);
+            T[ft][nq] = mma_bf16(kb[ft], al, T[ft][nq]);
+          }
         }
       }
-    }
-    // (5) P = Q' T (ReLU: [s > 0] T 2^-L), in place of Q'; per-query sums.
-    float ps[2] = {0.f, 0.f};
+      // (5) P = Q' T (ReLU: [s > 0] T 2^-L), in place of Q'; per-query sums.
+      float ps[2] = {0.f, 0.f};
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
+      for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-      for (int nq = 0; nq < 2; ++nq)
+        for (int nq = 0; nq < 2; ++nq)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float x = RELU ? (SQ[ft][nq][v] > 0.f ? T[ft][nq][v] * rl[nq] : 0.f)
-                               : SQ[ft][nq][v] * T[ft][nq][v];
-          SQ[ft][nq][v] = x;
-          ps[nq] += x;
-        }
+          for (int v = 0; v < 4; ++v) {
+            const float x = RELU ? (SQ[ft][nq][v] > 0.f ? T[ft][nq][v] * rl[nq] : 0.f)
+                                 : SQ[ft][nq][v] * T[ft][nq][v];
+            SQ[ft][nq][v] = x;
+            ps[nq] += x;
+          }
 #pragma unroll
-    for (int nq = 0; nq < 2; ++nq) {
-      ps[nq] += __shfl_xor(ps[nq], 16);
-      ps[nq] += __shfl_xor(ps[nq], 32);
-    }
-    // (6) dq^T partial = W^T P^T over the wave's features.
-    f32x4 Dq[4][2];
-#pragma unroll
-    for (int at = 0; at < 4; ++at) {
-      Dq[at][0] = zero4;
-      Dq[at][1] = zero4;
-#pragma unroll
-      for (int kf = 0; kf < FT / 2; ++kf) {
-        const bf16x8 wa = *reinterpret_cast<const bf16x8*>(&wt[(16 * at + l16) * (M + 8) + f0 + 32 * kf + 8 * g]);
-#pragma unroll
-        for (int nq = 0; nq < 2; ++nq) Dq[at][nq] = mma_bf16(wa, pack8(SQ[2 * kf][nq], SQ[2 * kf + 1][nq]), Dq[at][nq]);
+      for (int nq = 0; nq < 2; ++nq) {
+        ps[nq] += __shfl_xor(ps[nq], 16);
+        ps[nq] += __shfl_xor(ps[nq], 32);
       }
-    }
-    // (8) state update with the chunk's keys: S^T += [V | 1 | 1]^T K~.
+      // (6) dq^T partial = W^T P^T over the wave's features.
+      f32x4 Dq[4][2];
 #pragma unroll
-    for (int ct = 0; ct < 5; ++ct) {
-      const bf16x8 va = ct < 4 ? *reinterpret_cast<const bf16x8*>(&st.Vt[16 * ct + l16][4 * g]) : ones;
+      for (int at = 0; at < 4; ++at) {
+        Dq[at][0] = zero4;
+        Dq[at][1] = zero4;
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) stT[ct][ft] = mma_bf16(va, kb[ft], stT[ct][ft]);
+        for (int kf = 0; kf < FT / 2; ++kf) {
+          const bf16x8 wa = *reinterpret_cast<const bf16x8*>(&wt[(16 * at + l16) * (M + 8) + f0 + 32 * kf + 8 * g]);
+#pragma unroll
+          for (int nq = 0; nq < 2; ++nq) Dq[at][nq] = mma_bf16(wa, pack8(SQ[2 * kf][nq], SQ[2 * kf + 1][nq]), Dq[at][nq]);
+        }
+      }
+      // (8) state update with the chunk's keys: S^T += [V | 1 | 1]^T K~.
+#pragma unroll
+      for (int ct = 0; ct < 5; ++ct) {
+        const bf16x8 va = ct < 4 ? *reinterpret_cast<const bf16x8*>(&st.Vt[16 * ct + l16][4 * g]) : ones;
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) stT[ct][ft] = mma_bf16(va, kb[ft], stT[ct][ft]);
+      }
+      // (7) sum over the waves, norm term, store.
+      reduce_store<NW, RELU>(red, Dq, ps, st.Qh, wave, l16, g, knorm, dQ, base, jt, j1, true);
+      lds_barrier();   // (LDS only: the next chunk's loads stay in flight)
     }
-    // (7) sum over the waves, norm term, store.
-    reduce_store<NW, RELU>(red, Dq, ps, st.Qh, wave, l16, g, knorm, dQ, base, jt, j1, true);
-    lds_barrier();   // (LDS only: the next chunk's loads stay in flight)
   }
 }
 
@@ -753,7 +774,9 @@ __global__ __launch_bounds__(256) void cbsuffix(float* __restrict__ Gs, const fl
 }
 
 // ---------------------------------------------------------------------------
-// cbk: grid (nseg, BH), NW = m / (16 FT) waves; the segment's chunks in reverse order with
+// cbk: grid (ceil(nseg / SPW), BH), NW = m / (16 FT) waves; the chunks of SPW
+// consecutive segments in reverse order (the state moved to each earlier
+// segment's frame, factors 2^(c*(s) - c*(s+1)) <= 1) with
 // the suffix query state carried in registers (queries of later chunks and
 // segments), in the frame c*(s).
 //   MODE 0: dk.  G^T tiles gT[ct][ft] (lane = feature, rows = columns of
@@ -763,8 +786,8 @@ __global__ __launch_bounds__(256) void cbsuffix(float* __restrict__ Gs, const fl
 //           features); dv^T = G^T K~^T plus the masked term dO^T sc,
 //           sc_ij = Q'_i . K~_j for i >= j (over the wave's features).
 // ---------------------------------------------------------------------------
-template <int NW, bool RELU, int MODE, int FT>
-__global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
+template <int NW, bool RELU, int MODE, int FT, int SPW>
+__global__ __launch_bounds__(NW * 64, (MODE == 1 && FT == 4) ? 2 : 1) void cbk(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ cs,
     const float* __restrict__ cP, const float2* __restrict__ lp, const float* __restrict__ Gs,
@@ -772,7 +795,7 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
     float knorm) {
   constexpr int NTH = NW * 64;
   constexpr int M = NW * 16 * FT;   // FT feature tiles of 16 per wave
-  const int s = blockIdx.x, bh = blockIdx.y;
+  const int sA = blockIdx.x * SPW, sB = min(nseg, sA + SPW), bh = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, g = lane >> 4;
   const int f0 = 16 * FT * wave;
@@ -781,14 +804,14 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
   __shared__ __align__(16) float red[NW][kC][kRedRow];
   __shared__ __align__(16) float cst[M];
 
-  for (int r = tid; r < M; r += NTH) cst[r] = RELU ? 0.f : seg_ref(cs, cP, bh, s, nseg, M, r);
+  for (int r = tid; r < M; r += NTH) cst[r] = RELU ? 0.f : seg_ref(cs, cP, bh, sB - 1, nseg, M, r);
   if constexpr (MODE == 0) load_wt<NTH>(W, M, wt);
   f16x8 wreg[FT][2];
   load_wreg<FT>(W, f0, l16, g, wreg);
   const f32x4 zero4 = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Carry-in: the suffix state of the later segments.
-  const float* gs = Gs + (static_cast<size_t>(bh) * nseg + s) * kGRows * M;
+  // Carry-in: the suffix state of the segments after the last one swept.
+  const float* gs = Gs + (static_cast<size_t>(bh) * nseg + sB - 1) * kGRows * M;
   f32x4 gT[MODE == 0 ? 5 : 1][FT];
   f32x4 gF[MODE == 1 ? FT : 1][4];
   if constexpr (MODE == 0) {
@@ -813,216 +836,247 @@ __global__ __launch_bounds__(NW * 64, MODE == 1 ? 2 : 1) void cbk(
   const bf16x8 ones = (g == 0) ? __builtin_bit_cast(bf16x8, make_uint4(0x3f803f80u, 0u, 0u, 0u))
                                : __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
 
-  const int j0 = s * SEG, j1 = min(L, j0 + SEG);
-  const int nch = (j1 - j0 + kC - 1) / kC;
   const size_t base = static_cast<size_t>(bh) * L * kD;
   const size_t lbase = static_cast<size_t>(bh) * L;
   __syncthreads();
 
-  ChunkLoader<NTH> ld{ChunkRegs{}, Q, K, V, dO, lp, base, lbase, j1, RELU ? 0.f : knorm};
-  ld.next(j0 + kC * (nch - 1));
-  for (int t = nch - 1; t >= 0; --t) {
-    const int jt = j0 + kC * t;
-    ld.put(st, jt);
-    lds_barrier();
-    if (t > 0) ld.next(jt - kC);
-
-    // (1) key features K~^T (E^T orientation: lane = key 16 nk + l16, rows =
-    // features 16 ft + 4 g + v).
-    f32x4 EK[FT][2];
-    {
-      f32x4 init[FT];
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        const f32x4 c = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * ft + 4 * g]);
-        init[ft] = -c;
-      }
-      proj_et<FT>(st.Kh, wreg, l16, g, init, EK);
-#pragma unroll
-      for (int nk = 0; nk < 2; ++nk) {
-        const float n = st.nk[16 * nk + l16];
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) EK[ft][nk][v] = feature<RELU>(EK[ft][nk][v] + n);
-      }
-    }
-    // Query factors Q' (E orientation, lane = feature): the state update's
-    // operand and, for dk, the masked term's.
-    bf16x8 qb[FT];
-    query_factors_e<RELU, FT>(st, wreg, cst, f0, l16, g, qb);
-
-    if constexpr (MODE == 0) {
-      // (2) H^T = G [v | 1 | 1]^T (G hi + lo).
-      f32x4 H[FT][2];
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) H[ft][0] = H[ft][1] = zero4;
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        bf16x8 vb[2];
-#pragma unroll
-        for (int nk = 0; nk < 2; ++nk) {
-          const int k = 16 * nk + l16;
-          if (p < 2) {
-            const uint2 a = *reinterpret_cast<const uint2*>(&st.Vr[k][32 * p + 4 * g]);
-            const uint2 b = *reinterpret_cast<const uint2*>(&st.Vr[k][32 * p + 16 + 4 * g]);
-            vb[nk] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
-          } else {
-            vb[nk] = ones;
-          }
-        }
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) {
-          bf16x8 ah, al;
-          split8(gT[2 * p][ft], p < 2 ? gT[2 * p + 1][ft] : zero4, ah, al);
-#pragma unroll
-          for (int nk = 0; nk < 2; ++nk) {
-            H[ft][nk] = mma_bf16(ah, vb[nk], H[ft][nk]);
-            H[ft][nk] = mma_bf16(al, vb[nk], H[ft][nk]);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // (3) masked term: b (queries x keys) = dO V^T - p, i >= j.
-      {
-        f32x4 Bm[2][2];   // [mi][nk]: lane = key 16 nk + l16, rows = queries 16 mi + 4 g + v
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) Bm[mi][0] = Bm[mi][1] = zero4;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 ga[2], vbk[2];
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            ga[i] = *reinterpret_cast<const bf16x8*>(&st.Gr[16 * i + l16][32 * ks + 8 * g]);
-            vbk[i] = *reinterpret_cast<const bf16x8*>(&st.Vr[16 * i + l16][32 * ks + 8 * g]);
-          }
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-            for (int nk = 0; nk < 2; ++nk) Bm[mi][nk] = mma_bf16(ga[mi], vbk[nk], Bm[mi][nk]);
-        }
-        const f32x4 p0 = *reinterpret_cast<const f32x4*>(&st.pq[4 * g]);
-        const f32x4 p1 = *reinterpret_cast<const f32x4*>(&st.pq[16 + 4 * g]);
-#pragma unroll
-        for (int nk = 0; nk < 2; ++nk) {
-          const int k = 16 * nk + l16;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            Bm[0][nk][v] = (4 * g + v >= k) ? Bm[0][nk][v] - p0[v] : 0.f;
-            Bm[1][nk][v] = (16 + 4 * g + v >= k) ? Bm[1][nk][v] - p1[v] : 0.f;
-          }
-          bf16x8 bh_, bl_;
-          split8(Bm[0][nk], Bm[1][nk], bh_, bl_);
-#pragma unroll
-          for (int ft = 0; ft < FT; ++ft) {
-            H[ft][nk] = mma_bf16(qb[ft], bh_, H[ft][nk]);
-            H[ft][nk] = mma_bf16(qb[ft], bl_, H[ft][nk]);
-          }
-        }
-      }
-      // (4) R = K~ H (ReLU: [e > 0] H), per-key sums.
-      float rs[2] = {0.f, 0.f};
+  ChunkLoader<NTH> ld{ChunkRegs{}, Q, K, V, dO, lp, base, lbase, 0, RELU ? 0.f : knorm};
+  for (int s = sB - 1; s >= sA; --s) {
+    if (!RELU && SPW > 1 && s < sB - 1) {
+      // the carried state into segment s's frame (factors 2^(c*(s) - c*(s+1)) <= 1)
+      float fac[FT][4];
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-        for (int nk = 0; nk < 2; ++nk)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float x = RELU ? (EK[ft][nk][v] > 0.f ? H[ft][nk][v] : 0.f) : EK[ft][nk][v] * H[ft][nk][v];
-            EK[ft][nk][v] = x;
-            rs[nk] += x;
-          }
-#pragma unroll
-      for (int nk = 0; nk < 2; ++nk) {
-        rs[nk] += __shfl_xor(rs[nk], 16);
-        rs[nk] += __shfl_xor(rs[nk], 32);
-      }
-      // (5) dk^T partial = W^T R^T.
-      f32x4 Dk[4][2];
-#pragma unroll
-      for (int at = 0; at < 4; ++at) {
-        Dk[at][0] = Dk[at][1] = zero4;
-#pragma unroll
-        for (int kf = 0; kf < FT / 2; ++kf) {
-          const bf16x8 wa = *reinterpret_cast<const bf16x8*>(&wt[(16 * at + l16) * (M + 8) + f0 + 32 * kf + 8 * g]);
-#pragma unroll
-          for (int nk = 0; nk < 2; ++nk) Dk[at][nk] = mma_bf16(wa, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Dk[at][nk]);
+        for (int v = 0; v < 4; ++v) {
+          // MODE 0: the lane's feature; MODE 1: the tile rows' features
+          const int f = MODE == 0 ? f0 + 16 * ft + l16 : f0 + 16 * ft + 4 * g + v;
+          fac[ft][v] = fast_exp2(seg_ref(cs, cP, bh, s, nseg, M, f) - cst[f]);
         }
-      }
-      // (6) state update with the chunk's queries: G^T += [dO | -p]^T Q'.
+      lds_barrier();   // every wave has read the previous frame
+      for (int r = tid; r < M; r += NTH) cst[r] = seg_ref(cs, cP, bh, s, nseg, M, r);
+      if constexpr (MODE == 0) {
 #pragma unroll
-      for (int ct = 0; ct < 5; ++ct) {
-        const bf16x8 a = dop_t(st, ct, l16, g);
+        for (int ct = 0; ct < 5; ++ct)
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) gT[ct][ft] = mma_bf16(a, qb[ft], gT[ct][ft]);
-      }
-      reduce_store<NW, RELU>(red, Dk, rs, st.Kh, wave, l16, g, knorm, dK, base, jt, j1, true);
-    } else {
-      // (2) dv^T = G^T K~^T from the carried state.
-      f32x4 Dv[4][2];
+          for (int ft = 0; ft < FT; ++ft) gT[ct][ft] *= fac[ft][0];
+      } else {
 #pragma unroll
-      for (int at = 0; at < 4; ++at) {
-        Dv[at][0] = Dv[at][1] = zero4;
-#pragma unroll
-        for (int kf = 0; kf < FT / 2; ++kf) {
-          const bf16x8 ga = pack8(gF[2 * kf][at], gF[2 * kf + 1][at]);
-#pragma unroll
-          for (int nk = 0; nk < 2; ++nk) Dv[at][nk] = mma_bf16(ga, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Dv[at][nk]);
-        }
-      }
-      // (3) masked term: sc (queries x keys) = Q' K~^T over the wave's
-      // features for i >= j, then dv^T += dO^T sc.
-      {
-        f32x4 SQ[FT][2];   // Q' in the E^T orientation (lane = query)
-        f32x4 init[FT];
-#pragma unroll
-        for (int mt = 0; mt < FT; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
-        proj_et<FT>(st.Qh, wreg, l16, g, init, SQ);
-#pragma unroll
-        for (int nq = 0; nq < 2; ++nq) {
-          const float Lq = st.Lq[16 * nq + l16];
-#pragma unroll
-          for (int mt = 0; mt < FT; ++mt)
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              SQ[mt][nq][v] = RELU ? fmaxf(SQ[mt][nq][v], 0.f) * fast_exp2(-Lq) : fast_exp2(SQ[mt][nq][v] - Lq);
-        }
-        f32x4 Sc[2][2];   // [mi][nk]: lane = key, rows = queries 16 mi + 4 g + v
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) Sc[mi][0] = Sc[mi][1] = zero4;
-#pragma unroll
-        for (int kf = 0; kf < FT / 2; ++kf)
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi) {
-            const bf16x8 qa = pack8(SQ[2 * kf][mi], SQ[2 * kf + 1][mi]);
-#pragma unroll
-            for (int nk = 0; nk < 2; ++nk) Sc[mi][nk] = mma_bf16(qa, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Sc[mi][nk]);
-          }
-#pragma unroll
-        for (int nk = 0; nk < 2; ++nk) {
-          const int k = 16 * nk + l16;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            if (4 * g + v < k) Sc[0][nk][v] = 0.f;
-            if (16 + 4 * g + v < k) Sc[1][nk][v] = 0.f;
-          }
-          const bf16x8 sb = pack8(Sc[0][nk], Sc[1][nk]);
+        for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
           for (int at = 0; at < 4; ++at)
-            Dv[at][nk] = mma_bf16(*reinterpret_cast<const bf16x8*>(&st.Gt[16 * at + l16][4 * g]), sb, Dv[at][nk]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) gF[ft][at][v] *= fac[ft][v];
+      }
+      lds_barrier();
+    }
+    const int j0 = s * SEG, j1 = min(L, j0 + SEG);
+    const int nch = (j1 - j0 + kC - 1) / kC;
+    ld.j1 = j1;
+    ld.next(j0 + kC * (nch - 1));
+    for (int t = nch - 1; t >= 0; --t) {
+      const int jt = j0 + kC * t;
+      ld.put(st, jt);
+      lds_barrier();
+      if (t > 0) ld.next(jt - kC);
+
+      // (1) key features K~^T (E^T orientation: lane = key 16 nk + l16, rows =
+      // features 16 ft + 4 g + v).
+      f32x4 EK[FT][2];
+      {
+        f32x4 init[FT];
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          const f32x4 c = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * ft + 4 * g]);
+          init[ft] = -c;
+        }
+        proj_et<FT>(st.Kh, wreg, l16, g, init, EK);
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk) {
+          const float n = st.nk[16 * nk + l16];
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) EK[ft][nk][v] = feature<RELU>(EK[ft][nk][v] + n);
         }
       }
-      // (4) state update with the chunk's queries: G += Q'^T dO.
+      // Query factors Q' (E orientation, lane = feature): the state update's
+      // operand and, for dk, the masked term's.
+      bf16x8 qb[FT];
+      query_factors_e<RELU, FT>(st, wreg, cst, f0, l16, g, qb);
+
+      if constexpr (MODE == 0) {
+        // (2) H^T = G [v | 1 | 1]^T (G hi + lo).
+        f32x4 H[FT][2];
 #pragma unroll
-      for (int at = 0; at < 4; ++at) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&st.Gt[16 * at + l16][4 * g]);
+        for (int ft = 0; ft < FT; ++ft) H[ft][0] = H[ft][1] = zero4;
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) gF[ft][at] = mma_bf16(qb[ft], b, gF[ft][at]);
+        for (int p = 0; p < 3; ++p) {
+          bf16x8 vb[2];
+#pragma unroll
+          for (int nk = 0; nk < 2; ++nk) {
+            const int k = 16 * nk + l16;
+            if (p < 2) {
+              const uint2 a = *reinterpret_cast<const uint2*>(&st.Vr[k][32 * p + 4 * g]);
+              const uint2 b = *reinterpret_cast<const uint2*>(&st.Vr[k][32 * p + 16 + 4 * g]);
+              vb[nk] = __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+            } else {
+              vb[nk] = ones;
+            }
+          }
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) {
+            bf16x8 ah, al;
+            split8(gT[2 * p][ft], p < 2 ? gT[2 * p + 1][ft] : zero4, ah, al);
+#pragma unroll
+            for (int nk = 0; nk < 2; ++nk) {
+              H[ft][nk] = mma_bf16(ah, vb[nk], H[ft][nk]);
+              H[ft][nk] = mma_bf16(al, vb[nk], H[ft][nk]);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // (3) masked term: b (queries x keys) = dO V^T - p, i >= j.
+        {
+          f32x4 Bm[2][2];   // [mi][nk]: lane = key 16 nk + l16, rows = queries 16 mi + 4 g + v
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi) Bm[mi][0] = Bm[mi][1] = zero4;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            bf16x8 ga[2], vbk[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              ga[i] = *reinterpret_cast<const bf16x8*>(&st.Gr[16 * i + l16][32 * ks + 8 * g]);
+              vbk[i] = *reinterpret_cast<const bf16x8*>(&st.Vr[16 * i + l16][32 * ks + 8 * g]);
+            }
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+              for (int nk = 0; nk < 2; ++nk) Bm[mi][nk] = mma_bf16(ga[mi], vbk[nk], Bm[mi][nk]);
+          }
+          const f32x4 p0 = *reinterpret_cast<const f32x4*>(&st.pq[4 * g]);
+          const f32x4 p1 = *reinterpret_cast<const f32x4*>(&st.pq[16 + 4 * g]);
+#pragma unroll
+          for (int nk = 0; nk < 2; ++nk) {
+            const int k = 16 * nk + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              Bm[0][nk][v] = (4 * g + v >= k) ? Bm[0][nk][v] - p0[v] : 0.f;
+              Bm[1][nk][v] = (16 + 4 * g + v >= k) ? Bm[1][nk][v] - p1[v] : 0.f;
+            }
+            bf16x8 bh_, bl_;
+            split8(Bm[0][nk], Bm[1][nk], bh_, bl_);
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) {
+              H[ft][nk] = mma_bf16(qb[ft], bh_, H[ft][nk]);
+              H[ft][nk] = mma_bf16(qb[ft], bl_, H[ft][nk]);
+            }
+          }
+        }
+        // (4) R = K~ H (ReLU: [e > 0] H), per-key sums.
+        float rs[2] = {0.f, 0.f};
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+          for (int nk = 0; nk < 2; ++nk)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float x = RELU ? (EK[ft][nk][v] > 0.f ? H[ft][nk][v] : 0.f) : EK[ft][nk][v] * H[ft][nk][v];
+              EK[ft][nk][v] = x;
+              rs[nk] += x;
+            }
+#pragma unroll
+        for (int nk = 0; nk < 2; ++nk) {
+          rs[nk] += __shfl_xor(rs[nk], 16);
+          rs[nk] += __shfl_xor(rs[nk], 32);
+        }
+        // (5) dk^T partial = W^T R^T.
+        f32x4 Dk[4][2];
+#pragma unroll
+        for (int at = 0; at < 4; ++at) {
+          Dk[at][0] = Dk[at][1] = zero4;
+#pragma unroll
+          for (int kf = 0; kf < FT / 2; ++kf) {
+            const bf16x8 wa = *reinterpret_cast<const bf16x8*>(&wt[(16 * at + l16) * (M + 8) + f0 + 32 * kf + 8 * g]);
+#pragma unroll
+            for (int nk = 0; nk < 2; ++nk) Dk[at][nk] = mma_bf16(wa, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Dk[at][nk]);
+          }
+        }
+        // (6) state update with the chunk's queries: G^T += [dO | -p]^T Q'.
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct) {
+          const bf16x8 a = dop_t(st, ct, l16, g);
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) gT[ct][ft] = mma_bf16(a, qb[ft], gT[ct][ft]);
+        }
+        reduce_store<NW, RELU>(red, Dk, rs, st.Kh, wave, l16, g, knorm, dK, base, jt, j1, true);
+      } else {
+        // (2) dv^T = G^T K~^T from the carried state.
+        f32x4 Dv[4][2];
+#pragma unroll
+        for (int at = 0; at < 4; ++at) {
+          Dv[at][0] = Dv[at][1] = zero4;
+#pragma unroll
+          for (int kf = 0; kf < FT / 2; ++kf) {
+            const bf16x8 ga = pack8(gF[2 * kf][at], gF[2 * kf + 1][at]);
+#pragma unroll
+            for (int nk = 0; nk < 2; ++nk) Dv[at][nk] = mma_bf16(ga, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Dv[at][nk]);
+          }
+        }
+        // (3) masked term: sc (queries x keys) = Q' K~^T over the wave's
+        // features for i >= j, then dv^T += dO^T sc.
+        {
+          f32x4 SQ[FT][2];   // Q' in the E^T orientation (lane = query)
+          f32x4 init[FT];
+#pragma unroll
+          for (int mt = 0; mt < FT; ++mt) init[mt] = *reinterpret_cast<const f32x4*>(&cst[f0 + 16 * mt + 4 * g]);
+          proj_et<FT>(st.Qh, wreg, l16, g, init, SQ);
+#pragma unroll
+          for (int nq = 0; nq < 2; ++nq) {
+            const float Lq = st.Lq[16 * nq + l16];
+#pragma unroll
+            for (int mt = 0; mt < FT; ++mt)
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                SQ[mt][nq][v] = RELU ? fmaxf(SQ[mt][nq][v], 0.f) * fast_exp2(-Lq) : fast_exp2(SQ[mt][nq][v] - Lq);
+          }
+          f32x4 Sc[2][2];   // [mi][nk]: lane = key, rows = queries 16 mi + 4 g + v
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi) Sc[mi][0] = Sc[mi][1] = zero4;
+#pragma unroll
+          for (int kf = 0; kf < FT / 2; ++kf)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi) {
+              const bf16x8 qa = pack8(SQ[2 * kf][mi], SQ[2 * kf + 1][mi]);
+#pragma unroll
+              for (int nk = 0; nk < 2; ++nk) Sc[mi][nk] = mma_bf16(qa, pack8(EK[2 * kf][nk], EK[2 * kf + 1][nk]), Sc[mi][nk]);
+            }
+#pragma unroll
+          for (int nk = 0; nk < 2; ++nk) {
+            const int k = 16 * nk + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              if (4 * g + v < k) Sc[0][nk][v] = 0.f;
+              if (16 + 4 * g + v < k) Sc[1][nk][v] = 0.f;
+            }
+            const bf16x8 sb = pack8(Sc[0][nk], Sc[1][nk]);
+#pragma unroll
+            for (int at = 0; at < 4; ++at)
+              Dv[at][nk] = mma_bf16(*reinterpret_cast<const bf16x8*>(&st.Gt[16 * at + l16][4 * g]), sb, Dv[at][nk]);
+          }
+        }
+        // (4) state update with the chunk's queries: G += Q'^T dO.
+#pragma unroll
+        for (int at = 0; at < 4; ++at) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8*>(&st.Gt[16 * at + l16][4 * g]);
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) gF[ft][at] = mma_bf16(qb[ft], b, gF[ft][at]);
+        }
+        const float zs[2] = {0.f, 0.f};
+        reduce_store<NW, RELU>(red, Dv, zs, st.Kh, wave, l16, g, knorm, dV, base, jt, j1, false);
       }
-      const float zs[2] = {0.f, 0.f};
-      reduce_store<NW, RELU>(red, Dv, zs, st.Kh, wave, l16, g, knorm, dV, base, jt, j1, false);
+      lds_barrier();
     }
-    lds_barrier();
   }
 }
 
@@ -1038,11 +1092,13 @@ hipError_t launch_cbwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const
   const float* cP = reinterpret_cast<const float*>(ws + p.off_cP);
   const auto* lp = reinterpret_cast<const float2*>(lpf);
   float* Gs = reinterpret_cast<float*>(ws + b.off_G);
-  const dim3 grid(p.nseg, p.BH);
   timing_before(st);
   // dq: 32 features per wave (twice the waves, half the registers each)
-  cbq<2 * NW, RELU, 2><<<grid, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, P, cs, cP, lp, dQ, p.L, p.seg,
-                                                     p.nseg, p.knorm);
+  // (two segments per work-group: 8-wave work-groups, one per compute unit)
+  constexpr int kSpw = 2;
+  const dim3 grid2((p.nseg + kSpw - 1) / kSpw, p.BH);
+  cbq<2 * NW, RELU, 2><<<grid2, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, P, cs, cP, lp, dQ, p.L, p.seg,
+                                                      p.nseg, kSpw, p.knorm);
   e = hipGetLastError();
   timing_after(st, "cbq");
   if (e != hipSuccess) return e;
@@ -1059,17 +1115,16 @@ hipError_t launch_cbwd(const Plan& p, const BwdPlan& b, const uint16_t* Q, const
   e = hipGetLastError();
   timing_after(st, "cbsuffix");
   if (e != hipSuccess) return e;
-  // dk: 32 features per wave, as dq; dv: 64 per wave, two work-groups per
-  // compute unit
+  // dk and dv: 32 features per wave and two segments per work-group, as dq
   timing_before(st);
-  cbk<2 * NW, RELU, 0, 2><<<grid, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK, dV, p.L,
-                                                        p.seg, p.nseg, p.knorm);
+  cbk<2 * NW, RELU, 0, 2, kSpw><<<grid2, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK,
+                                                               dV, p.L, p.seg, p.nseg, p.knorm);
   e = hipGetLastError();
   timing_after(st, "cbk_dk");
   if (e != hipSuccess) return e;
   timing_before(st);
-  cbk<NW, RELU, 1, 4><<<grid, NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK, dV, p.L, p.seg,
-                                                p.nseg, p.knorm);
+  cbk<2 * NW, RELU, 1, 2, kSpw><<<grid2, 2 * NW * 64, 0, st>>>(Q, K, V, dO, W, cs, cP, lp, Gs, dK,
+                                                               dV, p.L, p.seg, p.nseg, p.knorm);
   e = hipGetLastError();
   timing_after(st, "cbk_dv");
   return e;
