@@ -787,7 +787,7 @@ __global__ __launch_bounds__(256) void cbsuffix(float* __restrict__ Gs, const fl
 //           sc_ij = Q'_i . K~_j for i >= j (over the wave's features).
 // ---------------------------------------------------------------------------
 template <int NW, bool RELU, int MODE, int FT, int SPW>
-__global__ __launch_bounds__(NW * 64, (MODE == 1 && FT == 4) ? 2 : 1) void cbk(
+__global__ __launch_bounds__(NW * 64, 1) void cbk(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ W, const float* __restrict__ cs,
     const float* __restrict__ cP, const float2* __restrict__ lp, const float* __restrict__ Gs,
