@@ -125,7 +125,7 @@ def measured_traffic(workload: str, causal: bool, kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
+def kernel_work(name: str, w, nseg: int, seg: int, elem: int, backward: bool = False):
     """Algorithmic (bytes, flops) of one launch of a kernel of the path.
 
     The whole path moves 4 d elements per token*head (Q, K, V read, O
@@ -170,13 +170,21 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int):
     if name in bwd:
         nb, nf = bwd[name]
         return (nb * w.d * elem * th, nf * w.d * w.m * th)
-    if name == "kpart" and w.causal:
-        th = w.heads * min(w.L, (nseg - 1) * seg)     # the last segment is not summarised
     half = (2 * w.d * elem * th, 4.0 * w.d * w.m * th)
-    if name in ("kpart", "qapply", "qstream", "g_state") or (name == "g_apply" and not w.causal):
+    if backward:
+        # the backward's key state: kpart (or g_state) reads K and V once
+        return half if name in ("kpart", "g_state") else (0, 0.0)
+    if w.causal:
+        # The causal scan reads Q, K, V and writes O and does both projections
+        # and both contractions: the whole path's algorithmic work.  The
+        # segment-state pass before it (kpart, g_state) re-reads K and V and
+        # recomputes the key side: overhead, credited nothing, so that the
+        # kernels' bytes sum to 4 d elements per token*head.
+        if name in ("cscan", "g_apply"):
+            return (2 * half[0], 2 * half[1])
+        return (0, 0.0)
+    if name in ("kpart", "qapply", "qstream", "g_state", "g_apply"):
         return half
-    if name in ("cscan",) or (name == "g_apply" and w.causal):
-        return (2 * half[0], 2 * half[1])
     return (0, 0.0)
 
 
@@ -230,6 +238,33 @@ def cpu_baseline(w, seconds: float, kernel: str = "softmax", backward: bool = Fa
 
 
 COPY_ELEMS = 1 << 28          # fp32 elements of the calibration copy (1 GiB read, 1 GiB written)
+
+
+def copy_ceiling(reps: int = 20):
+    """Measured HBM ceiling: a plain device copy (dst = -src, fp32, 1 GiB read and
+    1 GiB written) timed with events over `reps` back-to-back launches, outside
+    any profiler.  Returns {"GB_s", "ms", "bytes", "kernel"}."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 8 * COPY_ELEMS
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"GB_s": round(nbytes / ms / 1e6, 1), "ms": round(ms, 4), "bytes": nbytes,
+            "kernel": "torch.neg fp32, 1 GiB read + 1 GiB written, 20 launches"}
 
 
 def copy_calibration(steps: int):
@@ -712,7 +747,7 @@ def main():
                                     fv.BF16 if w.dtype == "bf16" else fv.F32, w.causal)
     kernels = {}
     for name, (tot_ms, launches) in kt.items():
-        kb, kf = kernel_work(name, w, nseg, seg, elem)
+        kb, kf = kernel_work(name, w, nseg, seg, elem, backward)
         kernels[name] = {"avg_us": round(1e3 * tot_ms / launches, 3), "launches": launches,
                          "alg_bytes": kb, "alg_flops": kf}
     dom = max(kt, key=lambda n: kt[n][0])
@@ -728,6 +763,11 @@ def main():
     roof["kernel"] = dom
     roof["kernel_avg_us"] = kernels[dom]["avg_us"]
     whole = roofline(alg_bytes, alg_flops, ms * 1e-3, alu=generic)
+    # Secondary fractions against the measured copy ceiling (HBM-bound only).
+    ceiling = copy_ceiling()
+    for r in (roof, whole):
+        if r["bound"] == "hbm":
+            r["frac_vs_copy"] = round(r["achieved"] / ceiling["GB_s"], 4)
 
     out = {
         "metric": ("FAVOR+ bwd tokens*heads/s, B8 H8 L4096 d64 m256" if backward else
@@ -757,6 +797,7 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roof,
         "roofline_whole_call": whole,
+        "copy_ceiling": ceiling,
         "kernels": kernels,
     }
     if redraw:

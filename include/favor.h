@@ -91,7 +91,8 @@ enum favor_status {
   FAVOR_ERR_ALIGN = -4,       /* a tensor base is not 16-byte aligned, or the
                                  workspace base is not 256-byte aligned         */
   FAVOR_ERR_WORKSPACE = -5,   /* workspace_bytes below favor_workspace_bytes()  */
-  FAVOR_ERR_HIP = -6          /* a HIP runtime call failed                      */
+  FAVOR_ERR_HIP = -6,         /* a HIP runtime call failed                      */
+  FAVOR_ERR_ALIAS = -7        /* two buffers that must be distinct overlap      */
 };
 
 /*
@@ -107,7 +108,9 @@ int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
 
 /*
  * The execution plan a forward call with these arguments would use:
- * *path = 0 (fp32 FMA kernels) or 1 (bf16 matrix-core kernels); *nseg and
+ * *path = 0 (fp32 FMA kernels), 1 (bf16 matrix-core kernels) or 2 (bf16
+ * matrix-core kernels, the bidirectional form in one persistent launch after
+ * a small preparation launch: d = 64, m = 256, at least 64 heads); *nseg and
  * *seg = the number of sequence splits (bidirectional) or segments (causal)
  * per head and their length in tokens.  Pure host function: no HIP call.
  * Returns FAVOR_OK, a validation error or FAVOR_ERR_NULL.
@@ -215,8 +218,8 @@ int favor_prefill_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, in
  * carry, and the final state as state_in plus the sum over every key);
  * every other case on the fp32 FMA kernels.  Workspace of at least
  * favor_prefill_workspace_bytes() bytes, 256-byte aligned.  Errors as
- * favor_fwd_attn, and FAVOR_ERR_UNSUPPORTED when state_in and state_out
- * overlap.
+ * favor_fwd_attn, and FAVOR_ERR_ALIAS when state_in and state_out
+ * overlap (chunked prefill alternates two state buffers).
  */
 int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                   int32_t attn_kernel, const void* Q, const void* K, const void* V,

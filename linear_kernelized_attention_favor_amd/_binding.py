@@ -158,14 +158,20 @@ def _kernel(kernel):
         raise ValueError(f"kernel must be 'softmax', 'gaussian' or 'relu', not {kernel!r}") from None
 
 
+def _check_out(out, shape, dtype, device, what):
+    if (tuple(out.shape) != tuple(shape) or out.dtype != dtype or not out.is_contiguous()
+            or not out.is_cuda or out.device != device):
+        raise ValueError(f"{what} must be a contiguous {dtype} GPU tensor of shape "
+                         f"{list(shape)} on {device}")
+
+
 def _forward(name, causal, q, k, v, W, out, workspace, stream, kernel="softmax"):
     ak = _kernel(kernel)
     B, H, L, d, m, dt = _shape_of(q, k, v, W)
     need = workspace_bytes(B, H, L, d, m, dt, causal)
     if out is None:
         out = torch.empty_like(q)
-    elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like Q")
+    _check_out(out, q.shape, q.dtype, q.device, "out")
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), out.data_ptr(),
@@ -190,9 +196,10 @@ def bwd(q, k, v, W, do, causal=False, kernel="softmax", out=None, workspace=None
     need = bwd_workspace_bytes(B, H, L, d, m, dt, causal)
     if out is None:
         out = tuple(torch.empty_like(q) for _ in range(3))
-    elif len(out) != 3 or any(o.shape != q.shape or o.dtype != q.dtype or not o.is_contiguous()
-                              for o in out):
+    elif len(out) != 3:
         raise ValueError("out must be three contiguous tensors like Q")
+    for o in out:
+        _check_out(o, q.shape, q.dtype, q.device, "each of out")
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     st = lib.favor_bwd_attn(B, H, L, d, m, dt, int(bool(causal)), ak, q.data_ptr(), k.data_ptr(),
@@ -231,6 +238,11 @@ def _check_state(st, B, H, d, m, what):
         raise ValueError(f"{what} must be a contiguous fp32 GPU tensor [B, H, m, d+4]")
 
 
+def _overlap(a, b) -> bool:
+    a0, b0 = a.data_ptr(), b.data_ptr()
+    return a0 < b0 + b.numel() * b.element_size() and b0 < a0 + a.numel() * a.element_size()
+
+
 def prefill_workspace_bytes(B, H, L, d, m, dtype=BF16) -> int:
     n = ctypes.c_size_t(0)
     _check(lib.favor_prefill_workspace_bytes(B, H, L, d, m, dtype, ctypes.byref(n)),
@@ -249,8 +261,13 @@ def prefill(q, k, v, W, state_in=None, state_out=None, kernel="softmax", out=Non
     if state_out is None:
         state_out = torch.empty((B, H, m, d + 4), dtype=torch.float32, device=q.device)
     _check_state(state_out, B, H, d, m, "state_out")
+    if state_in is not None and _overlap(state_in, state_out):
+        raise ValueError("state_out must not overlap state_in: the library reads the imported "
+                         "state while it writes the exported one (pass a second state buffer "
+                         "and swap the two between chunks)")
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q.shape, q.dtype, q.device, "out")
     if workspace is None:
         need = prefill_workspace_bytes(B, H, L, d, m, dt)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
@@ -273,6 +290,7 @@ def decode(q, k, v, W, state, kernel="softmax", out=None, stream=None):
     _check_state(state, B, H, d, m, "state")
     if out is None:
         out = torch.empty_like(q)
+    _check_out(out, q.shape, q.dtype, q.device, "out")
     _check(lib.favor_decode(B, H, d, m, dt, ak, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             W.data_ptr(), out.data_ptr(), state.data_ptr(), _stream(q, stream)),
            "favor_decode")
@@ -300,6 +318,7 @@ def feature_map(x, W, out=None, stream=None, kernel="softmax"):
     B, H, L, d, m, dt = _shape_of(x, x, x, W)
     if out is None:
         out = torch.empty((B, H, L, m), dtype=torch.float32, device=x.device)
+    _check_out(out, (B, H, L, m), torch.float32, x.device, "out")
     args = (x.data_ptr(), W.data_ptr(), out.data_ptr(), _stream(x, stream))
     if ak == SOFTMAX:
         st = lib.favor_feature_map(B, H, L, d, m, dt, *args)

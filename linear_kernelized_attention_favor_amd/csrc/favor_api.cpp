@@ -44,33 +44,6 @@ float norm_coefficient(int32_t attn_kernel) {
   }
 }
 
-int forward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
-            int32_t attn_kernel, const void* Q, const void* K, const void* V, const float* W,
-            void* O, void* ws, size_t ws_bytes, void* stream) {
-  const int status = check_shape(B, H, L, d, m, dtype);
-  if (status != FAVOR_OK) return status;
-  const float knorm = norm_coefficient(attn_kernel);
-  if (knorm < 0.f) return FAVOR_ERR_UNSUPPORTED;
-  if (!Q || !K || !V || !W || !O || !ws) return FAVOR_ERR_NULL;
-  if (!is_aligned(Q, 16) || !is_aligned(K, 16) || !is_aligned(V, 16) || !is_aligned(W, 16) ||
-      !is_aligned(O, 16) || !is_aligned(ws, 256))
-    return FAVOR_ERR_ALIGN;
-  Plan p;
-  make_plan(B, H, L, d, m, dtype, causal, &p);
-  if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
-  p.knorm = knorm;
-  p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (p.path == kPathMfma)
-    e = causal ? mfma_causal_forward(p, Q, K, V, W, O, ws, st)
-               : mfma_bidir_forward(p, Q, K, V, W, O, ws, st);
-  else
-    e = generic_forward(p, Q, K, V, W, O, ws, st);
-  if (e != hipSuccess) return fail_hip(e);
-  return FAVOR_OK;
-}
-
 int backward(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
              int32_t attn_kernel, const void* Q, const void* K, const void* V, const float* W,
              const void* dO, void* dQ, void* dK, void* dV, void* ws, size_t ws_bytes,
@@ -130,6 +103,36 @@ int check_state(int32_t B, int32_t H, int32_t d, int32_t m, int32_t attn_kernel)
 
 }  // namespace
 
+int forward_call(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype, int32_t causal,
+            int32_t attn_kernel, const void* Q, const void* K, const void* V, const float* W,
+            void* O, void* ws, size_t ws_bytes, void* stream) {
+  const int status = check_shape(B, H, L, d, m, dtype);
+  if (status != FAVOR_OK) return status;
+  const float knorm = norm_coefficient(attn_kernel);
+  if (knorm < 0.f) return FAVOR_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !W || !O || !ws) return FAVOR_ERR_NULL;
+  if (!is_aligned(Q, 16) || !is_aligned(K, 16) || !is_aligned(V, 16) || !is_aligned(W, 16) ||
+      !is_aligned(O, 16) || !is_aligned(ws, 256))
+    return FAVOR_ERR_ALIGN;
+  Plan p;
+  make_plan(B, H, L, d, m, dtype, causal, &p, true);
+  if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
+  p.knorm = knorm;
+  p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p.path == kPathFused)
+    e = fused_bidir_forward(p, Q, K, V, W, O, ws, st);
+  else if (p.path == kPathMfma)
+    e = causal ? mfma_causal_forward(p, Q, K, V, W, O, ws, st)
+               : mfma_bidir_forward(p, Q, K, V, W, O, ws, st);
+  else
+    e = generic_forward(p, Q, K, V, W, O, ws, st);
+  if (e != hipSuccess) return fail_hip(e);
+  return FAVOR_OK;
+}
+
+
 void make_generic_plan(Plan* p);
 
 void make_generic_only_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
@@ -147,13 +150,25 @@ int record_hip_error(hipError_t e) {
 }
 
 void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
-               int32_t causal, Plan* p) {
+               int32_t causal, Plan* p, bool forward) {
   std::memset(p, 0, sizeof(*p));
   p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
   p->BH = B * H;
   const size_t ncol = static_cast<size_t>(d) + 1;
   const size_t BH = static_cast<size_t>(p->BH);
   size_t off = 0;
+  if (forward && !causal && fused_bidir_supported(B, H, L, d, m, dtype)) {
+    p->path = kPathFused;
+    fused_bidir_layout(p, kPlanCUs);
+    p->off_T = off;
+    p->off_cseg = off;
+    p->off_cP = off;   off = align256(off + static_cast<size_t>(m) * (d + 8) * 2);
+    p->off_KV = off;   off = align256(off + BH * (d + 16) * (static_cast<size_t>(m) + 8) * 2);
+    p->off_cfin = off; off = align256(off + BH * m * sizeof(float));
+    p->off_ctrl = off; off = align256(off + fused_ctrl_words(p->BH) * 4);
+    p->bytes = off;
+    return;
+  }
   if (!causal && mfma_bidir_supported(d, m, dtype)) {
     p->path = kPathMfma;
     // Splits: about 512 key-side token groups in total (one or two per
@@ -289,7 +304,7 @@ int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
   if (st != FAVOR_OK) return st;
   if (!bytes) return FAVOR_ERR_NULL;
   favor::Plan p;
-  favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p);
+  favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p, true);
   *bytes = p.bytes;
   return FAVOR_OK;
 }
@@ -300,7 +315,7 @@ int favor_plan_describe(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, i
   if (st != FAVOR_OK) return st;
   if (!path || !nseg || !seg) return FAVOR_ERR_NULL;
   favor::Plan p;
-  favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p);
+  favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p, true);
   *path = p.path;
   *nseg = p.nseg;
   *seg = p.seg;
@@ -310,14 +325,14 @@ int favor_plan_describe(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, i
 int favor_fwd_bidir(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                     const void* Q, const void* K, const void* V, const float* W, void* O,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  return favor::forward(B, H, L, d, m, dtype, 0, FAVOR_SOFTMAX, Q, K, V, W, O, workspace,
+  return favor::forward_call(B, H, L, d, m, dtype, 0, FAVOR_SOFTMAX, Q, K, V, W, O, workspace,
                         workspace_bytes, stream);
 }
 
 int favor_fwd_causal(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
                      const void* Q, const void* K, const void* V, const float* W, void* O,
                      void* workspace, size_t workspace_bytes, void* stream) {
-  return favor::forward(B, H, L, d, m, dtype, 1, FAVOR_SOFTMAX, Q, K, V, W, O, workspace,
+  return favor::forward_call(B, H, L, d, m, dtype, 1, FAVOR_SOFTMAX, Q, K, V, W, O, workspace,
                         workspace_bytes, stream);
 }
 
@@ -325,7 +340,7 @@ int favor_fwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
                    int32_t causal, int32_t attn_kernel, const void* Q, const void* K,
                    const void* V, const float* W, void* O, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  return favor::forward(B, H, L, d, m, dtype, causal ? 1 : 0, attn_kernel, Q, K, V, W, O,
+  return favor::forward_call(B, H, L, d, m, dtype, causal ? 1 : 0, attn_kernel, Q, K, V, W, O,
                         workspace, workspace_bytes, stream);
 }
 
@@ -402,7 +417,7 @@ int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t
     favor_state_bytes(B, H, d, m, &sb);
     const auto* a = reinterpret_cast<const char*>(state_in);
     const auto* b = reinterpret_cast<const char*>(state_out);
-    if (a < b + sb && b < a + sb) return FAVOR_ERR_UNSUPPORTED;
+    if (a < b + sb && b < a + sb) return FAVOR_ERR_ALIAS;
   }
   favor::Plan p;
   favor::make_generic_only_plan(B, H, L, d, m, dtype, 1, favor::kPrefillSeg, &p);
@@ -498,6 +513,8 @@ const char* favor_status_string(int status) {
       return "workspace smaller than favor_workspace_bytes() (favor_bwd_workspace_bytes() for "
              "the backward pass)";
     case FAVOR_ERR_HIP: return "a HIP runtime call failed (see favor_last_hip_error)";
+    case FAVOR_ERR_ALIAS:
+      return "two buffers that must be distinct overlap (favor_prefill: state_in and state_out)";
     default: return "unknown status";
   }
 }

@@ -16,6 +16,7 @@ namespace favor {
 enum Path : int32_t {
   kPathGeneric = 0,  // fp32 FMA kernels, any supported shape and dtype
   kPathMfma = 1,     // bf16 MFMA kernels (see mfma_*_supported)
+  kPathFused = 2,    // bf16 MFMA, bidirectional in one persistent kernel
 };
 
 struct Plan {
@@ -44,6 +45,11 @@ struct Plan {
   //   cseg [BH][nseg][m]       per-feature references of the segment states
   //   cP   [BH][nseg][m]       references of the prefixes (s >= 1)
   size_t off_T, off_cseg, off_cP, off_KV, off_cfin;
+  // Fused bidirectional path (path kPathFused: matrix cores, one persistent
+  // kernel): cP (W' fp16 [m][d+8]), KV (state, bf16) and cfin as the MFMA
+  // bidirectional path, plus the work queues' control block:
+  //   ctrl [12 + BH] u32 words, 128 bytes apart
+  size_t off_ctrl;
   size_t bytes;
   // Features (set per call): exp(w.k - knorm |k|^2) with knorm = 1/2 (softmax
   // kernel) or 1 (Gaussian kernel), or, with relu = 1, max(w.x, 0)
@@ -53,8 +59,16 @@ struct Plan {
 };
 
 // Fills *p for a validated shape (the C-ABI layer validates first).
+// forward: the plan of a forward call (which may take the fused
+// bidirectional path); other users (backward, prefill) get the
+// three-kernel layout of the key partials.
 void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
-               int32_t causal, Plan* p);
+               int32_t causal, Plan* p, bool forward = false);
+// Compute units the plans are laid out for (an MI355X has 256; the fused
+// kernel's grid is the device's own count, its work queue adapts).
+constexpr int kPlanCUs = 256;
+// u32 words of the fused path's control block for BH heads.
+inline size_t fused_ctrl_words(int32_t BH) { return 32 * (12 + static_cast<size_t>(BH)); }
 
 // Backward pass: the generic path's key-state layout (Plan, path forced to
 // kPathGeneric) followed by
@@ -144,6 +158,13 @@ int mfma_bidir_query_workgroups();   // query-side work-groups the plan aims for
 hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                               const float* W, void* O, void* ws, hipStream_t stream);
 
+// Fused bidirectional path (bf16, d = 64, m = 256, at least 64 heads).
+bool fused_bidir_supported(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype);
+// Splits (seg, nseg) and query blocks (qblk) for `cus` compute units.
+void fused_bidir_layout(Plan* p, int cus);
+hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
+                               const float* W, void* O, void* ws, hipStream_t stream);
+
 // MFMA path (bf16 inputs): shape support, and the causal forward.
 bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype);
 // state_in (exported layout, nullptr: none) is a carried state that every
@@ -157,6 +178,12 @@ hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, cons
 // `kernel` must be a string literal.
 void timing_before(hipStream_t st);
 void timing_after(hipStream_t st, const char* kernel);
+
+// The forward entry points' common body: validation, plan, workspace check
+// and the launches on `stream` (a FAVOR_* status).
+int forward_call(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                 int32_t causal, int32_t attn_kernel, const void* Q, const void* K, const void* V,
+                 const float* W, void* O, void* ws, size_t ws_bytes, void* stream);
 
 // Records a failed HIP call for favor_last_hip_error(); returns FAVOR_ERR_HIP.
 int record_hip_error(hipError_t e);

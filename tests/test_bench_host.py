@@ -46,7 +46,7 @@ def test_backward_work_model_sums_to_the_pass_totals():
     th = w.heads * w.L
     names = ("cscan_lp", "cbq", "cbg", "cbk_dk", "cbk_dv")
     nbytes = sum(bench.kernel_work(n, w, 1, w.L, 2)[0] for n in names)
-    nbytes += 2 * w.d * 2 * th          # kpart's K and V (every segment)
+    nbytes += bench.kernel_work("kpart", w, 1, w.L, 2, backward=True)[0]   # K and V
     assert nbytes == 7 * w.d * 2 * th
     wb = workloads.workload("text_bidir")
     names = ("bq_den", "bq_dq", "bq_g", "bkey_dk", "bkey_dv")
@@ -59,3 +59,20 @@ def test_bench_refuses_several_gpus():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr)
+
+
+@pytest.mark.parametrize("name,causal", [("text_bidir", False), ("text_causal", True),
+                                         ("protein_long", True), ("wide_many", False)])
+def test_forward_work_model_sums_to_the_call_totals(name, causal):
+    # Each forward call moves 4 d elements per token*head once and does
+    # 8 d m flops; the per-kernel figures add up to exactly that (a causal
+    # segment-state pass that re-reads K and V is credited nothing).
+    w = workloads.workload(name).with_(causal=causal)
+    th = w.heads * w.L
+    names = (("kpart", "kprefix", "cscan") if causal else ("kpart", "kcombine", "qapply"))
+    if name == "wide_many":
+        names = ("kpart", "kcombine", "qstream")
+    nb = sum(bench.kernel_work(n, w, 8, 512, 2)[0] for n in names)
+    nf = sum(bench.kernel_work(n, w, 8, 512, 2)[1] for n in names)
+    assert nb == 4 * w.d * 2 * th
+    assert nf == 8.0 * w.d * w.m * th

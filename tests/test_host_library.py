@@ -23,7 +23,7 @@ HEADER = os.path.join(ROOT, "include", "favor.h")
 fv = pytest.importorskip("linear_kernelized_attention_favor_amd")
 lib = fv._binding.lib
 
-OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, EALIAS = 0, -1, -2, -3, -4, -5, -6, -7
 
 
 def declared_functions():
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, 12345):
+    for s in (OK, ENULL, ESHAPE, EUNSUP, EALIGN, EWS, EHIP, EALIAS, 12345):
         assert isinstance(fv.status_string(s), str) and fv.status_string(s)
     assert lib.favor_last_hip_error() == 0
 
@@ -188,9 +188,9 @@ def test_state_entry_validation():
     assert pre(so=MIS) == EALIGN
     assert pre(wsb=need - 1) == EWS
     # state_in and state_out may not overlap (1 x 1 x 64 x 68 floats = 17408 bytes)
-    assert pre(si=A, so=A) == EUNSUP
-    assert pre(si=A, so=A + 17408 - 16) == EUNSUP
-    assert pre(si=A + 17392, so=A) == EUNSUP
+    assert pre(si=A, so=A) == EALIAS
+    assert pre(si=A, so=A + 17408 - 16) == EALIAS
+    assert pre(si=A + 17392, so=A) == EALIAS
 
     def dec(**kw):
         a = dict(B=1, H=1, d=64, m=64, dtype=1, attn=0, q=A, k=A, v=A, W=A, o=A, st=A)
@@ -293,9 +293,14 @@ def test_plan_describe():
                                     (1, 16, 32768, 64, 256, 1), (1, 3, 1000, 64, 128, 1),
                                     (2, 1, 255, 64, 256, 1)]:
         path, nseg, seg = fv.plan_describe(B, H, L, d, m, fv.BF16, causal)
-        assert path == 1
+        # (the text shape's bidirectional form: the fused persistent kernel)
+        assert path == (2 if (B * H >= 64 and d == 64 and m == 256 and not causal) else 1)
         assert seg % 32 == 0 and nseg == -(-L // seg) and (nseg - 1) * seg < L
     assert fv.plan_describe(4, 32, 16384, 128, 512, fv.BF16, 0)[0] == 1
+    assert fv.plan_describe(1, 64, 1000, 64, 256, fv.BF16, 0)[0] == 2
+    assert fv.plan_describe(1, 63, 1000, 64, 256, fv.BF16, 0)[0] == 1    # too few heads
+    assert fv.plan_describe(1, 64, 1000, 64, 192, fv.BF16, 0)[0] == 1
+    assert fv.plan_describe(1, 64, 1000, 64, 256, fv.F32, 0)[0] == 0
     assert fv.plan_describe(1, 1, 500, 64, 768, fv.BF16, 0)[0] == 1
     assert fv.plan_describe(1, 1, 500, 64, 576, fv.BF16, 0)[0] == 0   # 9 key waves: generic
     # fp32 and shapes outside the matrix-core kernels take the generic path.
