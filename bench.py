@@ -79,7 +79,7 @@ def parse():
 
 # The sources the forward pass's counted kernels are compiled from: a change
 # to any of them voids the committed counter summary.
-FORWARD_SOURCES = ("kernels_mfma.hip", "mfma_common.h", "favor_internal.h")
+FORWARD_SOURCES = ("kernels_mfma.hip", "kernels_fused.hip", "mfma_common.h", "favor_internal.h")
 
 
 def kernel_source_digest() -> str:
@@ -185,6 +185,10 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int, backward: bool = F
         return (0, 0.0)
     if name in ("kpart", "qapply", "qstream", "g_state", "g_apply"):
         return half
+    if name == "fused":
+        # the persistent bidirectional kernel: both sides, the whole path's
+        # algorithmic work (fprep, before it, only converts W)
+        return (2 * half[0], 2 * half[1])
     return (0, 0.0)
 
 
@@ -287,7 +291,7 @@ def copy_calibration(steps: int):
                       "GB_s": round(8 * COPY_ELEMS / ms / 1e6, 1)}), flush=True)
 
 
-FAVOR_KERNELS = ("kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "g_state",
+FAVOR_KERNELS = ("fprep", "fused", "kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "g_state",
                  "g_combine", "g_apply", "gb_query", "gb_gstate", "gb_gcombine", "gb_key",
                  "bprep", "bcombine", "bqr", "gcombine", "bkeyr", "sexport", "g_decode",
                  "g_state_reset", "draw_block", "g_feature_map", "cbq", "cbg", "cbsuffix")

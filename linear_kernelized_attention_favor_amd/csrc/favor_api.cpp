@@ -160,11 +160,12 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
   if (forward && !causal && fused_bidir_supported(B, H, L, d, m, dtype)) {
     p->path = kPathFused;
     fused_bidir_layout(p, kPlanCUs);
-    p->off_T = off;
-    p->off_cseg = off;
+    const size_t ns = static_cast<size_t>(p->nseg);
     p->off_cP = off;   off = align256(off + static_cast<size_t>(m) * (d + 8) * 2);
-    p->off_KV = off;   off = align256(off + BH * (d + 16) * (static_cast<size_t>(m) + 8) * 2);
-    p->off_cfin = off; off = align256(off + BH * m * sizeof(float));
+    p->off_T = off;    off = align256(off + BH * ns * ncol * m * sizeof(float));
+    p->off_cseg = off; off = align256(off + BH * ns * m * sizeof(float));
+    p->off_KV = off;
+    p->off_cfin = off;
     p->off_ctrl = off; off = align256(off + fused_ctrl_words(p->BH) * 4);
     p->bytes = off;
     return;

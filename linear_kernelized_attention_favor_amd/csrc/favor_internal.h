@@ -46,9 +46,10 @@ struct Plan {
   //   cP   [BH][nseg][m]       references of the prefixes (s >= 1)
   size_t off_T, off_cseg, off_cP, off_KV, off_cfin;
   // Fused bidirectional path (path kPathFused: matrix cores, one persistent
-  // kernel): cP (W' fp16 [m][d+8]), KV (state, bf16) and cfin as the MFMA
-  // bidirectional path, plus the work queues' control block:
-  //   ctrl [12 + BH] u32 words, 128 bytes apart
+  // kernel): cP (W' fp16 [m][d+8]), T and cseg (the splits' partial states
+  // and references) as the MFMA bidirectional path, plus the work queues'
+  // control block:
+  //   ctrl [20 + BH] u32 words, 128 bytes apart
   size_t off_ctrl;
   size_t bytes;
   // Features (set per call): exp(w.k - knorm |k|^2) with knorm = 1/2 (softmax
@@ -68,7 +69,7 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
 // kernel's grid is the device's own count, its work queue adapts).
 constexpr int kPlanCUs = 256;
 // u32 words of the fused path's control block for BH heads.
-inline size_t fused_ctrl_words(int32_t BH) { return 32 * (12 + static_cast<size_t>(BH)); }
+inline size_t fused_ctrl_words(int32_t BH) { return 32 * (20 + static_cast<size_t>(BH)); }
 
 // Backward pass: the generic path's key-state layout (Plan, path forced to
 // kPathGeneric) followed by

@@ -11,18 +11,21 @@
 //           the control block of the persistent kernel cleared (a fill
 //           kernel: no memset node when the call is captured in a graph).
 //   fused   one work-group of 8 waves per compute unit.  Heads are dealt to
-//           the eight accelerator dies (XCDs, each with its own L2) in turn,
-//           and each die's work-groups take work items from their die's queue
-//           (then from the other dies' queues once theirs is empty): first
-//           the key items (head, 64-feature block), then the query items
-//           (head, query block).  A key item computes its block's columns of
-//           the state [(K')^T V | (K')^T 1] over every token of the head (the
-//           four blocks of a head read the same K and V through one L2),
-//           writes them as the query side's bf16 operand and arrives at the
-//           head.  A query item stages W', waits for the head's four blocks,
-//           stages the state and applies it to its tokens.  Items are taken
-//           in queue order, so a query item only waits for key items that
-//           running work-groups already hold: the wait always ends.
+//           the eight accelerator dies (XCDs, each with its own L2) in turn;
+//           each die has a queue of key items and a queue of query items for
+//           its heads.  A work-group claims key items (its die's first,
+//           then the other dies') until every key queue is empty, then query
+//           items the same way.  A key item (head, split) computes the
+//           partial state [(K')^T V | (K')^T 1] of one split of the head's
+//           tokens over all 256 features: its two groups of four waves take
+//           alternate 32-token tiles, the four waves of a group one
+//           64-feature block each, sharing the tile's K and V through LDS.
+//           It writes the partial in fp32 with its per-feature references and
+//           arrives at the head.  A query item (head, query block) stages W',
+//           waits for the head's splits, sums their partials into the bf16
+//           state and applies it to its tokens.  A work-group starts query
+//           items only once every key item has been taken by a running
+//           work-group, and key items wait for nothing: every wait ends.
 //
 // The key exponent needs no reference on the fast path.  With
 // W' = W log2(e), the key feature's exponent is
@@ -33,14 +36,15 @@
 // The query side likewise uses its own norm as the per-row shift (it cancels
 // in D^-1).  Robustness: a key item whose sums are not finite, or whose ones
 // column underflows (keys far from every projection row), is redone with
-// per-feature references (set from each wave's first tile, raised lazily:
-// the slow key loop), and a query tile whose denominators leave
-// [2^-100, 2^100] (or whose head carries references) is redone with a
-// per-row reference from its exact row maximum (the slow query tile).
-// Every shift is exact: per-feature key shifts are compensated on the query
-// exponent, per-row query shifts cancel in D^-1.
+// per-feature references (set from each wave's first tile, raised lazily),
+// and a query tile whose denominators leave [2^-100, 2^100] (or whose head
+// carries references) is redone with a per-row reference from its exact row
+// maximum.  Every shift is exact: per-feature key shifts are compensated on
+// the query exponent, per-row query shifts cancel in D^-1.  The slow forms
+// run the same code as the fast ones with a flag (the kernel makes no
+// function calls: a kernel that calls keeps a stack in scratch memory).
 //
-// Exchange between work-groups: the state, its references and the arrival
+// Exchange between work-groups: partial states, references and arrival
 // counts are written with device-scope (sc1) stores, which write through to
 // the device's coherence point, and read with device-scope loads; a
 // work-group waits for its stores to complete (vmcnt 0) before it signals
@@ -49,6 +53,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "favor.h"
 #include "favor_internal.h"
@@ -64,71 +69,81 @@ constexpr int FM = 256;           // features
 constexpr int FTT = 32;           // tokens per tile
 constexpr int FNT = 512;          // threads per work-group (8 waves)
 constexpr int NW = FNT / 64;      // waves per work-group
-constexpr int NFB = FM / 64;      // feature blocks (key items) per head
+constexpr int NTG = 2;            // token groups of a key item
+constexpr int NFW = NW / NTG;     // waves per token group (one 64-feature block each)
+constexpr int NSPLIT = 4;         // at most this many key items (splits) per head
 constexpr int FNCH = FM / 64;     // 64-feature chunks of the query side
 constexpr int WROW = FD + 8;      // fp16 per W' row (workspace and LDS)
-constexpr int KZROW = FM + 8;     // bf16 per state row (workspace and LDS)
+constexpr int KZROW = FM + 8;     // bf16 per state row (LDS)
 constexpr int KZROWS = FD + 16;   // state rows: 64 value columns, z, zero rows to 80
+constexpr int PROWS = FD + 1;     // rows of a partial state (value columns, z)
 constexpr int QTILE = 32;         // tokens per query tile (two 16-token columns)
 constexpr int NXCD = 8;           // accelerator dies of the part
 
 constexpr float kKeyBiasF = 40.0f;   // slow key loop: features start at <= 2^-40
 constexpr unsigned kSpinLimit = 1u << 25;   // ~1 s of polling before giving up
 
-// LDS of the key phase, per wave: a three-slot ring of V tiles ([32][64]
-// bf16 rows of 128 bytes, the 16-byte units of row r XOR-swizzled by r & 7)
-// and the tile's negated norm terms.
-constexpr int VT_BYTES = FTT * FD * 2;
-constexpr int KW_NB = 3 * VT_BYTES;            // offset of the norms in a wave's area
-constexpr int KW_BYTES = 3 * VT_BYTES + FTT * 4;
-// The waves' merge: per lane 20 accumulator quads and the references.
+// LDS of the key phase: per token group a six-slot ring of tiles, a slot
+// holding K (bf16 as it lands, fp16 once converted), V ([32][64] rows of 128
+// bytes, the 16-byte units of row r XOR-swizzled by r & 7) and the tile's 32
+// norm terms; the merge slots of the second group's waves (20 accumulator
+// quads and the references per lane) over the same bytes.
+constexpr int KT_BYTES = FTT * FD * 2;
+constexpr int SLOT_NB = 2 * KT_BYTES;
+constexpr int SLOT_BYTES = 2 * KT_BYTES + FTT * 4;
+constexpr int NSLOT = 6;
+constexpr int RING_BYTES = NTG * NSLOT * SLOT_BYTES;
 constexpr int MERGE_SLOT = 21 * 64 * 16;
-// The finished block [65][64] fp32 and its references.
-constexpr int BLK_BYTES = (FD + 1) * 64 * 4 + 64 * 4;
-// The query phase: W' [256][72] fp16, the state [80][264] bf16, c [256] fp32.
+constexpr int MERGE_BYTES = NFW * MERGE_SLOT;
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int KPHASE_BYTES = cmax(RING_BYTES, MERGE_BYTES);
+// The query phase: W' [256][72] fp16, the state [80][264] bf16, the combined
+// references c [256] fp32, the splits' scale factors [4][256] fp32.
 constexpr int QW_BYTES = FM * WROW * 2;
 constexpr int QK_BYTES = KZROWS * KZROW * 2;
 constexpr int QC_BYTES = FM * 4;
-constexpr int QPHASE_BYTES = QW_BYTES + QK_BYTES + QC_BYTES;
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int FUSED_LDS =
-    cmax(cmax(NW * KW_BYTES, (NW / 2) * MERGE_SLOT), cmax(BLK_BYTES, QPHASE_BYTES)) + 64;
+constexpr int QS_BYTES = NSPLIT * FM * 4;
+constexpr int QPHASE_BYTES = QW_BYTES + QK_BYTES + QC_BYTES + QS_BYTES;
+constexpr int FUSED_LDS = cmax(KPHASE_BYTES, QPHASE_BYTES) + 64;
 static_assert(FUSED_LDS <= 160 * 1024, "LDS of one work-group");
 
-// Control block (u32, in the workspace): one queue head per die, a timeout
-// flag, then per head the arrival count of its feature blocks; each word on
-// a 128-byte line of its own (atomics on one line from many work-groups
-// serialize).
+// Control block (u32, in the workspace): per die a key-queue and a
+// query-queue head, a timeout flag, then per head the arrival count of its
+// splits; each word on a 128-byte line of its own (atomics on one line from
+// many work-groups serialize).
 struct Ctrl {
-  static constexpr int LINE = 32, TIMEOUT = NXCD * LINE, HEADS = NXCD + 4;
-  __device__ static int next(int x) { return x * LINE; }
+  static constexpr int LINE = 32, TIMEOUT = 2 * NXCD * LINE, HEADS = 2 * NXCD + 4;
+  __device__ static int kq(int x) { return x * LINE; }
+  __device__ static int qq(int x) { return (NXCD + x) * LINE; }
   __device__ static int arrive(int bh) { return (HEADS + bh) * LINE; }
 };
+static_assert(Ctrl::HEADS == 20, "the control block's size is stated in favor_internal.h");
 
 // Device-scope (sc1) accesses: cache policy bit 4 of the buffer and
 // LDS-DMA instructions on this architecture.
 constexpr int kSC1 = 16;
 
-__device__ inline void store_sc1(float* p, float x) {
-  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ inline void store_sc1(unsigned* p, unsigned x) {
   __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ inline unsigned load_sc1(const unsigned* p) {
   return __hip_atomic_load(const_cast<unsigned*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ inline void store16_sc1(__amdgpu_buffer_rsrc_t r, int off, uint4 x) {
-  __builtin_amdgcn_raw_buffer_store_b128(u32x4{x.x, x.y, x.z, x.w}, r, off, 0, kSC1);
+__device__ inline uint4 load16_sc1(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSC1);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
-// A pointer known to address global memory (the item functions receive
-// generic pointers, which would otherwise compile to flat instructions).
-template <class T>
-__device__ inline const __attribute__((address_space(1))) T* gptr(const T* p) {
-  return (const __attribute__((address_space(1))) T*)(p);
+__device__ inline float load4_sc1(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kSC1));
+}
+__device__ inline void store4_sc1(__amdgpu_buffer_rsrc_t r, int off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, off, 0, kSC1);
 }
 // This wave's outstanding memory operations have completed.
 __device__ inline void vm_drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
 // ---------------------------------------------------------------------------
 // fprep: W16 [m][72] = fp16(W log2 e) (pad columns zero), control cleared.
@@ -150,41 +165,17 @@ struct Args {
   const uint16_t* V;
   const _Float16* W16;
   uint16_t* O;
-  uint16_t* Kz;      // [BH][80][m+8] state, bf16, query operand order
-  float* cfin;       // [BH][m] its references
+  float* T;          // [BH][nsplit][65][256] partial states, fp32
+  float* cs;         // [BH][nsplit][256] their per-feature references
   unsigned* ctrl;
-  int L, BH, nqb, QB;
+  int L, BH, nsplit, seg, nqb, QB;
   float knorm;
 };
 
-// The work-group's LDS, shared by the key and query phases (file scope, so
-// that every function addresses it as LDS), and the last 64 bytes as a
-// broadcast area for values one thread decides.
+// The work-group's LDS, shared by the key and query phases, and the last 64
+// bytes as a broadcast area for values one thread decides.
 __shared__ __align__(16) unsigned char g_smem[FUSED_LDS];
 __device__ inline unsigned* bcast() { return reinterpret_cast<unsigned*>(g_smem + FUSED_LDS - 64); }
-
-// Values every lane of a wave holds alike, moved to scalar registers: the
-// item functions are called (not inlined), so their arguments arrive in
-// vector registers, and buffer resources built from them would otherwise
-// need a loop over lanes for every load.
-__device__ inline int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
-__device__ inline float uni(float x) {
-  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
-}
-template <class T>
-__device__ inline T* uni(T* p) {
-  const uint64_t x = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
-  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
-}
-__device__ inline Args uni(const Args& a) {
-  Args u;
-  u.Q = uni(a.Q); u.K = uni(a.K); u.V = uni(a.V); u.W16 = uni(a.W16); u.O = uni(a.O);
-  u.Kz = uni(a.Kz); u.cfin = uni(a.cfin); u.ctrl = uni(a.ctrl);
-  u.L = uni(a.L); u.BH = uni(a.BH); u.nqb = uni(a.nqb); u.QB = uni(a.QB); u.knorm = uni(a.knorm);
-  return u;
-}
 
 // Sum over the four lanes {l, l^16, l^32, l^48} (one column of a 16x16 tile).
 __device__ inline float colsum4(float x) {
@@ -194,113 +185,140 @@ __device__ inline float colsum4(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
+// Instruction order for the scheduler in the region since the last
+// scheduling barrier: P matrix instructions (a projection), then C matrix
+// instructions each followed by up to V vector instructions (the features of
+// the projected tile, which depend on the projection only), so that the
+// vector units work while the matrix cores do.
+template <int P, int C, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+  }
+}
+
+// Thread 0: the queue heads of every die (device-scope loads, issued while
+// an item runs; a queue seen empty stays empty).
+__device__ inline void take_snapshot(unsigned* q, unsigned (&c)[NXCD]) {
+#pragma unroll
+  for (int x = 0; x < NXCD; ++x) c[x] = load_sc1(q + Ctrl::LINE * x);
+}
+
+// Weight of a partial with reference c in a sum referred to cn >= c (a part
+// that saw no token has c = -inf and weight 0).
+__device__ inline float rescale(float c, float cn) {
+  return c == -INFINITY ? 0.f : fast_exp2(c - cn);
+}
 
 // ---------------------------------------------------------------------------
-// Key pass (one wave): the head's 32-token tiles w, w + 8, ... for the 64
-// features [f0, f0 + 64) (W' operands in registers).  Per tile: K straight
-// from memory into the projection's operand registers (bf16 -> fp16), each
-// token's -knorm |k|^2 log2(e) summed across the four lanes that hold the
-// token and moved through LDS to the lanes that hold its row of the product
-// (-inf past the sequence); V into the wave's LDS ring by DMA two tiles
-// ahead, read back as the contraction's operand with transposing LDS reads
-// (4 consecutive tokens of one column per read); S = K W'^T - n on the matrix
-// cores (the norm as the C input; the slow loop subtracts the reference c_r
-// there too), K~ = exp2(S) in bf16 and [V | 1]^T K~ accumulated in fp32.
-// Iteration i converts and projects tile i + 1 while tile i is contracted;
-// no barrier: the waves of the work-group run independently.
+// Key pass of one wave over its token group's tiles of the split [t0, t1)
+// (group tg takes tiles tg, tg + 2, ...; the wave takes the 64 features
+// 64 fw .. + 63, W' operands in registers).  Per step the work-group
+// synchronises once.  Every wave DMAs a quarter of its group's tile five
+// tiles ahead (waves fw = 0, 1 the K rows, 2, 3 the V rows) and converts a
+// quarter of the K rows two tiles ahead in place to fp16, with those
+// tokens' norm terms -knorm |k|^2 log2(e) (-inf past the split) beside the
+// tile: each K element is converted once, not once per feature block.  Per
+// tile: S = K W'^T - n on the matrix cores (the norm as the C input; the
+// slow form subtracts the reference c_r there too), K~ = exp2(S) in bf16,
+// and [V | 1]^T K~ accumulated in fp32, V read back as the contraction's
+// operand with transposing LDS reads (4 consecutive tokens of one column per
+// read).  Step i converts tile i + 2, projects tile i + 1 and contracts tile
+// i.
 // ---------------------------------------------------------------------------
 template <bool RELU, bool SLOW>
-__device__ __forceinline__ void key_pass(const Args& a, int bh, int f0, f32x4 (&acc)[5][4],
-                                         float (&cref)[4]) {
-  const int lane = threadIdx.x & 63, wave = uni(static_cast<int>(threadIdx.x) >> 6);
+__device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
+                                         f32x4 (&acc)[5][4], float (&cref)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6), tg = wave / NFW, fw = wave % NFW;
   const int l16 = lane & 15, g = lane >> 4;
-  unsigned char* const kw = g_smem + wave * KW_BYTES;
-  float* const nb = reinterpret_cast<float*>(kw + KW_NB);
-  const int L = a.L;
-  const int ntl = (L + FTT - 1) / FTT;                              // tiles of the head
-  const int ntw = wave < ntl ? (ntl - wave + NW - 1) / NW : 0;      // this wave's tiles
-  const size_t base = static_cast<size_t>(bh) * L * FD;
-  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(a.K + base, L * FD * 2);
-  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(a.V + base, L * FD * 2);
-  auto tok0 = [&](int i) { return (wave + NW * i) * FTT; };
+  unsigned char* const ring = g_smem + tg * NSLOT * SLOT_BYTES;
+  const int n = t1 - t0;
+  const int ntl = (n + FTT - 1) / FTT;      // tiles of the split
+  const int nsteps = (ntl + NTG - 1) / NTG; // tiles per group (group 1 may run one dead tile)
+  const size_t base = (static_cast<size_t>(bh) * a.L + t0) * FD;
+  const __amdgpu_buffer_rsrc_t rsrc_kv = buffer_rsrc((fw < 2 ? a.K : a.V) + base, n * FD * 2);
+  const float nscale = -(a.knorm * kLog2e);
 
   f16x8 wb[4][2];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      wb[nt][ks] = *gptr(reinterpret_cast<const f16x8*>(a.W16 + (f0 + 16 * nt + l16) * WROW +
-                                                        32 * ks + 8 * g));
+      wb[nt][ks] = *reinterpret_cast<const f16x8*>(a.W16 + (64 * fw + 16 * nt + l16) * WROW +
+                                                   32 * ks + 8 * g);
 #pragma unroll
   for (int i = 0; i < 5; ++i)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) cref[nt] = 0.f;
-  if (ntw == 0) return;
 
-  // K operand (raw bf16): token tok0(i) + 16 mt + l16, dims 32 ks + 8 g .. + 7
-  // (rows past the sequence read zero).
-  uint4 kraw[2][2];
-  auto kload = [&](int i) {
+  auto slot = [&](int i) { return ring + (i % NSLOT) * SLOT_BYTES; };
+  // This wave's quarter of tile i of the group (two DMA instructions): slot
+  // unit u = 128 fw + 64 j + lane, units 0..255 the K rows and 256..511 the
+  // V rows; unit u of a row holds the row's global unit (u % 8) ^ (row % 8).
+  // Rows past the split read zero.
+  auto dma_part = [&](int i, int j) {
+    const int tb = (NTG * i + tg) * FTT;
+    unsigned char* const sl = slot(i);
+    const int uu = (128 * fw + 64 * j + lane) & 255, row = uu >> 3, gu = (uu & 7) ^ (row & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc_kv, (lds_ptr)(sl + 16 * (128 * fw + 64 * j)), 16,
+        ((tb + row) * FD + 8 * gu) * 2, 0, 0, 0);
+  };
+  auto dma = [&](int i) {
+    dma_part(i, 0);
+    dma_part(i, 1);
+  };
+  // K rows 8 fw .. + 7 of tile i to fp16 in place (lane: row 8 fw + lane / 8,
+  // 16-byte unit lane % 8) and their norm terms (8 lanes per row).
+  auto convert = [&](int i) {
+    unsigned char* const sl = slot(i);
+    const int row = 8 * fw + (lane >> 3);
+    uint4* const p = reinterpret_cast<uint4*>(sl + row * 128 + (lane & 7) * 16);
+    const uint4 x = *p;
+    float ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.x),
+                                               __builtin_bit_cast(bf16x2, x.x), 0.f, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.y),
+                                         __builtin_bit_cast(bf16x2, x.y), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.z),
+                                         __builtin_bit_cast(bf16x2, x.z), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.w),
+                                         __builtin_bit_cast(bf16x2, x.w), ss, false);
+    ss = group_sum<8>(ss);
+    *p = make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
+                    bf16x2_to_f16x2(x.w));
+    const int tb = (NTG * i + tg) * FTT;
+    if ((lane & 7) == 0)
+      reinterpret_cast<float*>(sl + SLOT_NB)[row] = tb + row < n ? nscale * ss : -INFINITY;
+  };
+  using SArr = f32x4[2][4];
+  // S for tile i: fp16 operands (token 16 mt + l16, dims 32 ks + 8 g .. + 7)
+  // and the C input -n (rows 16 mt + 4 g .. + 3) from the slot.
+  auto proj = [&](int i, SArr& S) {
+    const unsigned char* const sl = slot(i);
+    f16x8 ka[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        kraw[mt][ks] = buffer_load16(rk, ((tok0(i) + 16 * mt + l16) * FD + 32 * ks + 8 * g) * 2);
-  };
-  // V tile i into ring slot sl (4 DMA instructions; instruction j fills LDS
-  // units 64 j + lane: row u / 8 holds at unit u % 8 the row's global unit
-  // (u % 8) ^ (row & 7); rows past the sequence read zero).
-  auto vdma = [&](int i, int sl) {
-    const int tb = tok0(i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = 64 * j + lane, row = u >> 3, gu = (u & 7) ^ (row & 7);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (lds_ptr)(kw + sl * VT_BYTES + 1024 * j), 16,
-          ((tb + row) * FD + 8 * gu) * 2, 0, 0, 0);
-    }
-  };
-  using KOp = f16x8[2][2];
-  // fp16 operands of tile i and the C input -n per product row (from LDS).
-  auto prep = [&](int i, KOp& ka, f32x4 (&nq)[2]) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      float ss = 0.f;
-#pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const uint4 x = kraw[mt][ks];
-        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
-          ss = fmaf(lo, lo, ss);
-          ss = fmaf(hi, hi, ss);
-        }
-        uint4 h;
-        h.x = bf16x2_to_f16x2(x.x); h.y = bf16x2_to_f16x2(x.y);
-        h.z = bf16x2_to_f16x2(x.z); h.w = bf16x2_to_f16x2(x.w);
-        ka[mt][ks] = __builtin_bit_cast(f16x8, h);
+        const int row = 16 * mt + l16, c = 4 * ks + g;
+        ka[mt][ks] = *reinterpret_cast<const f16x8*>(sl + row * 128 + ((c ^ (row & 7)) * 16));
       }
-      ss = colsum4(ss);
-      const bool live = tok0(i) + 16 * mt + l16 < L;
-      if (g == 0) nb[16 * mt + l16] = live ? -(a.knorm * kLog2e) * ss : -INFINITY;
-    }
-    wave_lds_fence();
+    f32x4 nq[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) nq[mt] = *reinterpret_cast<const f32x4*>(&nb[16 * mt + 4 * g]);
-  };
-  using SArr = f32x4[2][4];
-  auto proj = [&](const KOp& ka, const f32x4 (&nq)[2], SArr& S) {
+    for (int mt = 0; mt < 2; ++mt)
+      nq[mt] = *reinterpret_cast<const f32x4*>(sl + SLOT_NB + (16 * mt + 4 * g) * 4);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        f32x4 c = nq[mt];
-        if constexpr (SLOW) c -= cref[nt];
-        S[mt][nt] = mma_f16(ka[mt][0], wb[nt][0], c);
+        if constexpr (SLOW) S[mt][nt] = mma_f16(ka[mt][0], wb[nt][0], nq[mt] - cref[nt]);
+        else S[mt][nt] = mma_f16(ka[mt][0], wb[nt][0], nq[mt]);
       }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -319,7 +337,7 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int f0, f32x4 (&
       kb[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
     }
   };
-  // (slow loop) some feature reached 2, or is not finite
+  // (slow) some feature reached 2, or is not finite
   auto overflow = [&](const bf16x8 (&kb)[4]) {
     uint32_t o = 0;
 #pragma unroll
@@ -329,9 +347,9 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int f0, f32x4 (&
     }
     return __ballot((o & 0x40004000u) != 0) != 0;
   };
-  // (slow loop) reference update from the tile's exact per-feature maximum:
-  // set on the wave's first tile kKeyBias above it, later raised where
-  // exceeded (the accumulators and the projected tile move along).
+  // (slow) reference update from the tile's exact per-feature maximum: set
+  // on the wave's first tile kKeyBias above it, later raised where exceeded
+  // (the accumulators and the projected tile move along).
   auto rebase = [&](SArr& S, bool first) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -353,86 +371,87 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int f0, f32x4 (&
   bf16x8 ones;
 #pragma unroll
   for (int u = 0; u < 8; ++u) ones[u] = static_cast<__bf16>(1.0f);
-  // [V | 1]^T K~ for the tile in slot sl: operand row = value column 16 mv +
-  // l16, positions 8 g + 0..3 / 4..7 = tokens 4 g + 0..3 / 16 + 4 g + 0..3
-  // (read r: lane l16 of the 16-lane group g addresses row 16 r + 4 g + l16/4,
+  // [V | 1]^T K~ for tile i: operand row = value column 16 mv + l16,
+  // positions 8 g + 0..3 / 4..7 = tokens 4 g + 0..3 / 16 + 4 g + 0..3 (read
+  // r: lane l16 of the 16-lane group g addresses row 16 r + 4 g + l16/4,
   // columns 16 mv + 4 (l16 % 4) .. + 3, and receives column 16 mv + l16 of
   // rows 16 r + 4 g .. + 3).
-  auto contract = [&](int sl, const bf16x8 (&kb)[4]) {
-    // The eight transposing reads of the tile are issued together and waited
+  auto contract_half = [&](int i, const bf16x8 (&kb)[4], int half) {
+    // The four transposing reads of the half are issued together and waited
     // for in the same statement (the compiler would otherwise wait for every
-    // LDS DMA in flight before each of them; the DMA of this tile has
-    // landed, see the explicit wait of the iteration).
-    const uint32_t vt = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(kw + sl * VT_BYTES));
+    // LDS DMA in flight before each of them; this tile's DMA has landed).
+    const uint32_t vt = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot(i) + KT_BYTES));
     const int row = 4 * g + (l16 >> 2);
-    uint32_t ad[4];
+    uint32_t ad[2];
 #pragma unroll
-    for (int mv = 0; mv < 4; ++mv)
-      ad[mv] = vt + row * 128 + (((2 * mv + ((l16 & 3) >> 1)) ^ (row & 7)) * 16) + (l16 & 1) * 8;
-    uint64_t h[8];
+    for (int u = 0; u < 2; ++u) {
+      const int mv = 2 * half + u;
+      ad[u] = vt + row * 128 + (((2 * mv + ((l16 & 3) >> 1)) ^ (row & 7)) * 16) + (l16 & 1) * 8;
+    }
+    uint64_t h[4];
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %8\n\t"
-        "ds_read_b64_tr_b16 %1, %8 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %2, %9\n\t"
-        "ds_read_b64_tr_b16 %3, %9 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %4, %10\n\t"
-        "ds_read_b64_tr_b16 %5, %10 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %6, %11\n\t"
-        "ds_read_b64_tr_b16 %7, %11 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+        "ds_read_b64_tr_b16 %2, %5\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]),
-          "=&v"(h[6]), "=&v"(h[7])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+        : "v"(ad[0]), "v"(ad[1])
         : "memory");
 #pragma unroll
-    for (int mv = 0; mv < 4; ++mv) {
-      const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(static_cast<uint32_t>(h[2 * mv]),
-                                                              static_cast<uint32_t>(h[2 * mv] >> 32),
-                                                              static_cast<uint32_t>(h[2 * mv + 1]),
-                                                              static_cast<uint32_t>(h[2 * mv + 1] >> 32)));
+    for (int u = 0; u < 2; ++u) {
+      const int mv = 2 * half + u;
+      const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(static_cast<uint32_t>(h[2 * u]),
+                                                              static_cast<uint32_t>(h[2 * u] >> 32),
+                                                              static_cast<uint32_t>(h[2 * u + 1]),
+                                                              static_cast<uint32_t>(h[2 * u + 1] >> 32)));
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) acc[mv][nt] = mma_bf16(va, kb[nt], acc[mv][nt]);
     }
+    if (half == 1) {
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) acc[4][nt] = mma_bf16(ones, kb[nt], acc[4][nt]);
+      for (int nt = 0; nt < 4; ++nt) acc[4][nt] = mma_bf16(ones, kb[nt], acc[4][nt]);
+    }
   };
 
-  // Prologue: V of tile 0, K of tile 0, V of tile 1 in flight; tile 0
-  // projected (its K arrived, so V of tile 0 did) and its features formed; K
-  // of tile 1 in flight.  Every load is issued even past the wave's last tile
-  // (those rows read zero), so that the count of memory operations in flight
-  // is the same in every iteration.
-  vdma(0, 0);
-  kload(0);
-  vdma(1, 1);
+  // Prologue: tiles 0..4 in flight; tile 0 converted once it has landed
+  // everywhere (this wave's tiles 1..4 may be in flight: eight operations),
+  // tile 1 likewise (six), then tile 0 projected and its features formed.
+  // DMAs past the group's last tile read zeros, so every step issues the
+  // same number of operations.
+#pragma unroll
+  for (int i = 0; i < 5; ++i) dma(i);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  lds_barrier();
+  convert(0);
+  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  lds_barrier();
+  convert(1);
   bf16x8 kbA[4], kbB[4];
   {
-    KOp ka;
-    f32x4 nq[2];
-    prep(0, ka, nq);
     SArr S;
-    proj(ka, nq, S);
+    proj(0, S);
     if constexpr (SLOW) rebase(S, true);
     features(S, kbA);
   }
-  kload(1);
-  // Iteration i (slot i % 3 holds V of tile i): DMA V of tile i + 2; wait
-  // until V of tile i has landed (issued after it: K of tile i, V and K of
-  // tile i + 1, V of tile i + 2, four operations each); convert tile i + 1
-  // (its K has arrived), load K of tile i + 2, project tile i + 1, contract
-  // tile i, form tile i + 1's features.
-  auto step = [&](auto R, int i, const bf16x8 (&kcur)[4], bf16x8 (&knext)[4]) {
-    constexpr int r = decltype(R)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    vdma(i + 2, (r + 2) % 3);
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    KOp ka;
-    f32x4 nq[2];
-    prep(i + 1, ka, nq);
-    kload(i + 2);
+  // Step i: tile i + 2 has landed (this wave's tiles i + 3, i + 4 may be in
+  // flight) and tile i + 1 is converted everywhere; every wave is done with
+  // tile i - 1, whose slot takes tile i + 5.
+  auto step = [&](int i, const bf16x8 (&kcur)[4], bf16x8 (&knext)[4]) {
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    lds_barrier();
+    convert(i + 2);
     SArr S;
-    proj(ka, nq, S);
-    contract(r % 3, kcur);
+    proj(i + 1, S);
+    // The tile's two DMA instructions go between the matrix work (after the
+    // projection, halfway through the contraction) rather than in a burst
+    // after the barrier: an instruction that finds the memory pipeline's
+    // queue full holds up its wave, and spread out it stays behind the
+    // matrix work.
+    dma_part(i + 5, 0);
+    contract_half(i, kcur, 0);
+    dma_part(i + 5, 1);
+    contract_half(i, kcur, 1);
     features(S, knext);
     if constexpr (SLOW) {
       if (__builtin_expect(overflow(knext), 0)) {
@@ -441,37 +460,47 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int f0, f32x4 (&
       }
     }
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  for (int i = 0; i < ntw; i += 6) {
-    step(I0{}, i, kbA, kbB);
-    if (i + 1 >= ntw) break;
-    step(I1{}, i + 1, kbB, kbA);
-    if (i + 2 >= ntw) break;
-    step(I2{}, i + 2, kbA, kbB);
-    if (i + 3 >= ntw) break;
-    step(I0{}, i + 3, kbB, kbA);
-    if (i + 4 >= ntw) break;
-    step(I1{}, i + 4, kbA, kbB);
-    if (i + 5 >= ntw) break;
-    step(I2{}, i + 5, kbB, kbA);
+  for (int i = 0; i < nsteps; i += 2) {
+    step(i, kbA, kbB);
+    if (i + 1 >= nsteps) break;
+    step(i + 1, kbB, kbA);
   }
-  // (the DMAs issued past the wave's last tile land before the ring is reused)
+  // (the DMAs issued past the group's last tile land before the LDS is reused)
   vm_drain();
+  // A group that saw no token carries no reference.
+  if (tg >= ntl) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) cref[nt] = -INFINITY;
+  }
 }
 
-// Merge the 8 waves' sums into wave 0 (fixed order: 4..7 into 0..3, 2..3 into
-// 0..1, 1 into 0), through LDS slots of 21 quads per lane; the slow form
-// rescales to the larger reference.
-template <bool SLOW>
-__device__ __forceinline__ void key_merge(f32x4 (&acc)[5][4], float (&cref)[4]) {
-  const int lane = threadIdx.x & 63, wave = uni(static_cast<int>(threadIdx.x) >> 6);
-#pragma unroll
-  for (int k = NW / 2; k >= 1; k /= 2) {
-    __syncthreads();
-    if (wave >= k && wave < 2 * k) {
-      f32x4* slot = reinterpret_cast<f32x4*>(g_smem + (wave - k) * MERGE_SLOT) + lane;
+// ---------------------------------------------------------------------------
+// Key item (head bh, split s, tokens [s seg, min(L, (s + 1) seg))): the pass
+// and the merge of the two token groups (the second group's sums into the
+// first's, rescaled to the larger reference); if the sums are not finite, or
+// some feature's ones-column sum fell below 2^-100 (its features underflow
+// without a reference), both again with references.  The first group's waves
+// write the partial [65][256] fp32 and its references with device-scope
+// stores; the work-group waits for them and arrives at its head.
+// ---------------------------------------------------------------------------
+template <bool RELU>
+__device__ __forceinline__ void key_item(const Args& a, int bh, int s, unsigned* snapq,
+                                         unsigned (&snap)[NXCD]) {
+  unsigned* const bc = bcast();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6), tg = wave / NFW, fw = wave % NFW;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int t0 = s * a.seg, t1 = min(a.L, t0 + a.seg);
+  f32x4 acc[5][4];
+  float cref[4];
+  for (int pass = 0; pass < 2; ++pass) {
+    const bool slow = pass == 1;
+    if (slow) key_pass<RELU, true>(a, bh, t0, t1, acc, cref);
+    else key_pass<RELU, false>(a, bh, t0, t1, acc, cref);
+    if (tid == 0 && pass == 0) take_snapshot(snapq, snap);
+    __syncthreads();   // the ring is read: the merge slots take its bytes
+    if (tg == 1) {
+      f32x4* slot = reinterpret_cast<f32x4*>(g_smem + fw * MERGE_SLOT) + lane;
 #pragma unroll
       for (int mv = 0; mv < 5; ++mv)
 #pragma unroll
@@ -479,104 +508,58 @@ __device__ __forceinline__ void key_merge(f32x4 (&acc)[5][4], float (&cref)[4]) 
       slot[20 * 64] = f32x4{cref[0], cref[1], cref[2], cref[3]};
     }
     __syncthreads();
-    if (wave < k) {
-      const f32x4* slot = reinterpret_cast<const f32x4*>(g_smem + wave * MERGE_SLOT) + lane;
+    bool bad = false;
+    if (tg == 0) {
+      const f32x4* slot = reinterpret_cast<const f32x4*>(g_smem + fw * MERGE_SLOT) + lane;
       const f32x4 co = slot[20 * 64];
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        if constexpr (SLOW) {
-          const float cn = fmaxf(cref[nt], co[nt]);
-          const float x = fast_exp2(cref[nt] - cn), y = fast_exp2(co[nt] - cn);
+        const float cn = fmaxf(cref[nt], co[nt]);
+        const float x = rescale(cref[nt], cn), y = rescale(co[nt], cn);
 #pragma unroll
-          for (int mv = 0; mv < 5; ++mv) acc[mv][nt] = acc[mv][nt] * x + slot[(mv * 4 + nt) * 64] * y;
-          cref[nt] = cn;
-        } else {
+        for (int mv = 0; mv < 5; ++mv) acc[mv][nt] = acc[mv][nt] * x + slot[(mv * 4 + nt) * 64] * y;
+        cref[nt] = cn;
+      }
+      if (!RELU && !slow) {
 #pragma unroll
-          for (int mv = 0; mv < 5; ++mv) acc[mv][nt] += slot[(mv * 4 + nt) * 64];
+        for (int i = 0; i < 5; ++i)
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) bad |= !__builtin_isfinite(acc[i][nt][v]);
+        if (g == 0) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) bad |= !(acc[4][nt][0] >= 0x1p-100f);
         }
       }
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Key item (head bh, feature block fb): the fast pass and merge; if the sums
-// are not finite, or some feature's ones-column sum fell below 2^-100 (its
-// features underflow without a reference), the slow pass and merge.  Wave 0
-// stages the block [65][64] fp32 and its references in LDS; the work-group
-// writes its columns of the state as the query side's operand (row r,
-// features 32 b + {4 q + i, 16 + 4 q + i} at positions 32 b + 8 q + {i, 4 + i};
-// rows 65..79 zero) and of cfin with 16-byte device-scope stores, waits for
-// them and arrives at its head.
-// ---------------------------------------------------------------------------
-template <bool RELU>
-__device__ __attribute__((noinline)) void key_item(Args a_in, int bh_in, int fb_in) {
-  const Args a = uni(a_in);
-  const int bh = uni(bh_in), fb = uni(fb_in);
-  unsigned* const bc = bcast();
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = uni(tid >> 6), l16 = lane & 15, g = lane >> 4;
-  f32x4 acc[5][4];
-  float cref[4];
-  key_pass<RELU, false>(a, bh, 64 * fb, acc, cref);
-  key_merge<false>(acc, cref);
-  if constexpr (!RELU) {
-    bool bad = false;
-    if (wave == 0) {
-#pragma unroll
-      for (int i = 0; i < 5; ++i)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) bad |= !__builtin_isfinite(acc[i][nt][v]);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) bad |= !(acc[4][nt][0] >= 0x1p-100f);
-    }
+    if (RELU || slow) break;
     if (tid == 0) bc[0] = 0u;
     __syncthreads();
     if (bad) bc[0] = 1u;
     __syncthreads();
-    if (bc[0]) {
-      key_pass<RELU, true>(a, bh, 64 * fb, acc, cref);
-      key_merge<true>(acc, cref);
-    }
+    if (bc[0] == 0u) break;
   }
-  float* const BL = reinterpret_cast<float*>(g_smem);            // [65][64]
-  float* const BLc = BL + (FD + 1) * 64;                         // [64]
-  __syncthreads();   // the merge slots (shared with BL) have been read
-  if (wave == 0) {
+  if (tg == 0) {
+    // Partial rows 16 mv + 4 g + v (row 64: the ones column), features
+    // 64 fw + 16 nt + l16; references of those features.
+    const size_t item = static_cast<size_t>(bh) * a.nsplit + s;
+    const __amdgpu_buffer_rsrc_t rt = buffer_rsrc(a.T + item * PROWS * FM, PROWS * FM * 4);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int f = 16 * nt + l16;
+    for (int mv = 0; mv < 5; ++mv)
 #pragma unroll
-      for (int mv = 0; mv < 4; ++mv)
+      for (int v = 0; v < 4; ++v) {
+        const int row = 16 * mv + 4 * g + v;
+        if (row < PROWS) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) BL[(16 * mv + 4 * g + v) * 64 + f] = acc[mv][nt][v];
-      if (g == 0) {
-        BL[FD * 64 + f] = acc[4][nt][0];
-        BLc[f] = cref[nt];
+          for (int nt = 0; nt < 4; ++nt)
+            store4_sc1(rt, (row * FM + 64 * fw + 16 * nt + l16) * 4, acc[mv][nt][v]);
+        }
       }
-    }
-  }
-  __syncthreads();
-  {
-    const __amdgpu_buffer_rsrc_t rk =
-        buffer_rsrc(a.Kz + static_cast<size_t>(bh) * KZROWS * KZROW, KZROWS * KZROW * 2);
-    for (int e = tid; e < KZROWS * 8; e += FNT) {
-      const int row = e >> 3, b = (e >> 2) & 1, q = e & 3;
-      uint4 o = make_uint4(0, 0, 0, 0);
-      if (row <= FD) {
-        const float4 x = *reinterpret_cast<const float4*>(BL + row * 64 + 32 * b + 4 * q);
-        const float4 y = *reinterpret_cast<const float4*>(BL + row * 64 + 32 * b + 16 + 4 * q);
-        o = make_uint4(pack_bf16(x.x, x.y), pack_bf16(x.z, x.w), pack_bf16(y.x, y.y),
-                       pack_bf16(y.z, y.w));
-      }
-      store16_sc1(rk, (row * KZROW + 64 * fb + 32 * b + 8 * q) * 2, o);
-    }
-    if (tid < 16) {
-      const __amdgpu_buffer_rsrc_t rf =
-          buffer_rsrc(a.cfin + static_cast<size_t>(bh) * FM + 64 * fb, 64 * 4);
-      store16_sc1(rf, 16 * tid, reinterpret_cast<const uint4*>(BLc)[tid]);
+    if (g == 0) {
+      const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.cs + item * FM, FM * 4);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) store4_sc1(rc, (64 * fw + 16 * nt + l16) * 4, cref[nt]);
     }
   }
   vm_drain();
@@ -586,17 +569,18 @@ __device__ __attribute__((noinline)) void key_item(Args a_in, int bh_in, int fb_
 }
 
 // ---------------------------------------------------------------------------
-// Query side.  A query item is block qb of head bh, tokens [qb QB,
-// min(L, (qb+1) QB)), in 32-token tiles (wave w takes tiles w, w + 8, ...).
-// LDS: W' [256][72] fp16, the state [80][264] bf16 and the references c
-// [256] fp32.  Per tile, for each 64-feature chunk: S^T = W' Q^T - n_q (the
-// query norm |q|^2 log2(e) / 2 as the C input: a per-row shift that cancels
-// in D^-1 and bounds the exponent by |w|^2 log2(e) / 2), Q~ = exp2(S^T) in
-// bf16, and [KV | z]^T Q~^T accumulated in fp32; the next chunk is projected
-// while the current one is applied.  O = num / den.  A tile whose
-// denominators leave [2^-100, 2^100], or any tile of a head whose state
-// carries references, is computed by the slow tile: the exact row maximum of
-// s + c_r first, then exp2(s + c_r - M) with the shift on the vector units.
+// Query item: block qb of head bh, tokens [qb QB, min(L, (qb+1) QB)), in
+// 32-token tiles (wave w takes tiles w, w + 8, ...).  LDS: W' [256][72]
+// fp16, the state [80][264] bf16 (query operand order), the references c
+// [256] fp32.  The state is the sum of the head's partials, each rescaled to
+// the per-feature maximum c of their references.  Per tile, for each
+// 64-feature chunk: S^T = W' Q^T + C, Q~ = exp2(S^T) in bf16, and
+// [KV | z]^T Q~^T accumulated in fp32; the next chunk is projected while the
+// current one is applied.  O = num / den.  C is the query's norm term
+// -|q|^2 log2(e) / 2 (a per-row shift that cancels in D^-1 and bounds the
+// exponent by |w|^2 log2(e) / 2); a tile whose denominators leave
+// [2^-100, 2^100], and every tile of a head whose state carries references,
+// takes instead C = c_r - M with M its exact row maximum of s + c_r.
 // ---------------------------------------------------------------------------
 using Qraw = uint4[2][2];
 using Qop = f16x8[2][2];
@@ -604,16 +588,156 @@ using QS = f32x4[4][2];
 using QFeat = bf16x8[2][2];   // [kb][nt]: lane = token, 8 features (perm_of)
 using QAcc = f32x4[5][2];
 
-struct QTile {
-  const _Float16* Wl;
-  const uint16_t* Kzl;
-  const float* cl;
-  uint16_t* O;        // output rows of the head
-  int q1;             // end of the block (tokens)
-  int l16, g;
+// Position of feature f in the state's row (query operand order): within
+// each 32-feature block, feature 4 q + i at 8 q + i and 16 + 4 q + i at
+// 8 q + 4 + i.
+__device__ inline int state_pos(int f) {
+  const int j = f & 31;
+  return (f & ~31) + (j < 16 ? 8 * (j >> 2) + (j & 3) : 8 * ((j - 16) >> 2) + 4 + (j & 3));
+}
 
-  // S^T (+ C) for chunk ch: rows features 64 ch + 16 mt + 4 g + v, column token.
-  __device__ __forceinline__ void proj(int ch, const Qop& qop, const f32x4 (&cq)[2], QS& S) const {
+template <bool RELU>
+__device__ __forceinline__ void query_item(const Args& a, int bh, int qb, unsigned* snapq,
+                                           unsigned (&snap)[NXCD]) {
+  unsigned char* const smem = g_smem;
+  unsigned* const bc = bcast();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int l16 = lane & 15, g = lane >> 4;
+  _Float16* const Wl = reinterpret_cast<_Float16*>(smem);
+  uint16_t* const Kzl = reinterpret_cast<uint16_t*>(smem + QW_BYTES);
+  float* const cl = reinterpret_cast<float*>(smem + QW_BYTES + QK_BYTES);
+  float* const scl = reinterpret_cast<float*>(smem + QW_BYTES + QK_BYTES + QC_BYTES);
+  const int L = a.L, nsplit = a.nsplit;
+  const size_t base = static_cast<size_t>(bh) * L * FD;
+  const int q0 = qb * a.QB, q1 = min(L, q0 + a.QB);
+
+  // W' (written by the previous launch) straight into LDS.
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(a.W16);
+    uint4* dst = reinterpret_cast<uint4*>(Wl);
+    constexpr int n16 = FM * WROW / 8;
+    for (int j = wave; 64 * j < n16; j += NW)
+      if (64 * j + lane < n16) lds_dma16(src + 64 * j + lane, dst + 64 * j);
+  }
+  // The wave's first tile of Q, loaded while the head's state is awaited.
+  const uint16_t* const Qh = a.Q + base;
+  uint16_t* const Oh = a.O + base;
+  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Qh, q1 * FD * 2);
+  const int tstep = NW * QTILE;
+  const int tt0 = q0 + wave * QTILE;
+  const int ntile = tt0 < q1 ? (q1 - tt0 + tstep - 1) / tstep : 0;
+  auto q_load = [&](int tt, Qraw& raw) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        raw[nt][ks] = buffer_load16(rq, ((tt + 16 * nt + l16) * FD + 32 * ks + 8 * g) * 2);
+  };
+  Qraw raw;
+  q_load(tt0, raw);
+
+  // Wait until every split of the head has written its partial.
+  if (tid == 0) {
+    unsigned r = 0, spins = 0;
+    while ((r = load_sc1(a.ctrl + Ctrl::arrive(bh))) < static_cast<unsigned>(nsplit)) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins >= kSpinLimit) {
+        store_sc1(a.ctrl + Ctrl::TIMEOUT, 1u);
+        break;
+      }
+    }
+    bc[0] = r >= static_cast<unsigned>(nsplit) ? 1u : 0u;
+    bc[1] = 0u;
+  }
+  __syncthreads();
+  const unsigned ready = bc[0];
+  if (ready == 0u) {
+    // (the wait gave up: the output of this block is marked invalid)
+    vm_drain();
+    for (int i = tid; i < (q1 - q0) * FD; i += FNT) Oh[static_cast<size_t>(q0) * FD + i] = 0x7FC0u;
+    __syncthreads();
+    return;
+  }
+  // The state: partials (device-scope loads, issued first), the per-feature
+  // maximum c of their references and each split's scale 2^(c_s - c), then
+  // the rescaled sum in bf16.  Thread t sums the 4-feature units t + 512 k
+  // of the [65][256] partial (splits past the head's read zero, scale 0).
+  {
+    const size_t item0 = static_cast<size_t>(bh) * nsplit;
+    const __amdgpu_buffer_rsrc_t rt =
+        buffer_rsrc(a.T + item0 * PROWS * FM, nsplit * PROWS * FM * 4);
+    constexpr int NU = PROWS * FM / 4;           // 4160 units
+    constexpr int NK = (NU + FNT - 1) / FNT;     // 9 per thread at most
+    constexpr int NKA = 5;                       // first batch
+    uint4 x[NKA][NSPLIT];
+#pragma unroll
+    for (int k = 0; k < NKA; ++k)
+#pragma unroll
+      for (int s = 0; s < NSPLIT; ++s)
+        x[k][s] = load16_sc1(rt, ((s * PROWS * FM) + 4 * (tid + FNT * k)) * 4);
+    if (tid < FM) {
+      const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(a.cs + item0 * FM, nsplit * FM * 4);
+      float c[NSPLIT];
+#pragma unroll
+      for (int s = 0; s < NSPLIT; ++s) c[s] = load4_sc1(rc, (s * FM + tid) * 4);
+      float cn = -INFINITY;
+#pragma unroll
+      for (int s = 0; s < NSPLIT; ++s)
+        if (s < nsplit) cn = fmaxf(cn, c[s]);
+#pragma unroll
+      for (int s = 0; s < NSPLIT; ++s) scl[s * FM + tid] = s < nsplit ? rescale(c[s], cn) : 0.f;
+      cl[tid] = cn;
+      if (cn != 0.f) bc[1] = 1u;   // some reference is not 0
+    }
+    __syncthreads();
+    auto combine = [&](int u, const uint4 (&xs)[NSPLIT]) {
+      const int row = u / (FM / 4), f = 4 * (u % (FM / 4));
+      float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int s = 0; s < NSPLIT; ++s) {
+        const float4 w = *reinterpret_cast<const float4*>(&scl[s * FM + f]);
+        const uint4 v = xs[s];
+        sum.x = fmaf(w.x, __uint_as_float(v.x), sum.x);
+        sum.y = fmaf(w.y, __uint_as_float(v.y), sum.y);
+        sum.z = fmaf(w.z, __uint_as_float(v.z), sum.z);
+        sum.w = fmaf(w.w, __uint_as_float(v.w), sum.w);
+      }
+      *reinterpret_cast<uint2*>(&Kzl[row * KZROW + state_pos(f)]) =
+          make_uint2(pack_bf16(sum.x, sum.y), pack_bf16(sum.z, sum.w));
+    };
+#pragma unroll
+    for (int k = 0; k < NKA; ++k) {
+      const int u = tid + FNT * k;
+      if (u < NU) combine(u, x[k]);
+    }
+    uint4 y[NK - NKA][NSPLIT];
+#pragma unroll
+    for (int k = NKA; k < NK; ++k)
+#pragma unroll
+      for (int s = 0; s < NSPLIT; ++s)
+        y[k - NKA][s] = load16_sc1(rt, ((s * PROWS * FM) + 4 * (tid + FNT * k)) * 4);
+#pragma unroll
+    for (int k = NKA; k < NK; ++k) {
+      const int u = tid + FNT * k;
+      if (u < NU) combine(u, y[k - NKA]);
+    }
+    // rows 65..79 of the operand are zero
+    for (int i = tid; i < (KZROWS - PROWS) * FM / 8; i += FNT) {
+      const int row = PROWS + i / (FM / 8), c8 = 8 * (i % (FM / 8));
+      *reinterpret_cast<uint4*>(&Kzl[row * KZROW + c8]) = make_uint4(0, 0, 0, 0);
+    }
+  }
+  vm_drain();   // W' has landed
+  __syncthreads();
+  const bool refs = bc[1] != 0u;
+  if (tid == 0) take_snapshot(snapq, snap);
+
+  // S^T + C for chunk ch: rows features 64 ch + 16 mt + 4 g + v, column
+  // token.  Fast form: C = cq[nt], the per-token norm term, as the matrix
+  // instruction's C operand; slow form: C = c_r + cq[nt].
+  auto proj = [&](auto SLOWC, int ch, const Qop& qop, const f32x4 (&cq)[2], QS& S) {
+    constexpr bool SL = decltype(SLOWC)::value;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       f16x8 wa[4];
@@ -621,14 +745,24 @@ struct QTile {
       for (int mt = 0; mt < 4; ++mt)
         wa[mt] = *reinterpret_cast<const f16x8*>(&Wl[(64 * ch + 16 * mt + l16) * WROW + 32 * ks + 8 * g]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt) {
+        if (ks == 0) {
+          if constexpr (SL) {
+            const f32x4 crow = *reinterpret_cast<const f32x4*>(&cl[64 * ch + 16 * mt + 4 * g]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          S[mt][nt] = mma_f16(wa[mt], qop[nt][ks], ks == 0 ? cq[nt] : S[mt][nt]);
+            for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mma_f16(wa[mt], qop[nt][0], crow + cq[nt]);
+          } else {
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mma_f16(wa[mt], qop[nt][0], cq[nt]);
+          }
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) S[mt][nt] = mma_f16(wa[mt], qop[nt][1], S[mt][nt]);
+        }
+      }
     }
-  }
-  template <bool RELU>
-  __device__ __forceinline__ static void features(const QS& S, QFeat& qt) {
+  };
+  auto features = [&](const QS& S, QFeat& qt) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -642,8 +776,8 @@ struct QTile {
         }
         qt[kb][nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
       }
-  }
-  __device__ __forceinline__ void apply(int ch, const QFeat& qt, QAcc& acc) const {
+  };
+  auto apply = [&](int ch, const QFeat& qt, QAcc& acc) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int kcol = 64 * ch + 32 * kb + 8 * g;
@@ -654,21 +788,57 @@ struct QTile {
         for (int nt = 0; nt < 2; ++nt) acc[mv][nt] = mma_bf16(ka, qt[kb][nt], acc[mv][nt]);
       }
     }
-  }
-  __device__ __forceinline__ static void reset(QAcc& acc) {
+  };
+  // The four chunks of a tile: chunk ch + 1 projected while chunk ch is
+  // applied.
+  auto tile = [&](auto SLOWC, const Qop& qop, const f32x4 (&cq)[2], QAcc& acc) {
 #pragma unroll
     for (int i = 0; i < 5; ++i)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[i][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    QFeat FA, FB;
+    {
+      QS S;
+      proj(SLOWC, 0, qop, cq, S);
+      features(S, FA);
+    }
+    auto regular = [&](const int ch, const QFeat& Fcur, QFeat& Fnext) {
+      __builtin_amdgcn_sched_barrier(0);
+      QS S;
+      proj(SLOWC, ch + 1, qop, cq, S);
+      apply(ch, Fcur, acc);
+      features(S, Fnext);
+      interleave_mfma_valu<16, 20, 3>();
+    };
+    regular(0, FA, FB);
+    regular(1, FB, FA);
+    regular(2, FA, FB);
+    __builtin_amdgcn_sched_barrier(0);
+    apply(3, FB, acc);
+  };
+  // The slow form's C offset: minus the exact row maximum of s + c_r.
+  auto row_max = [&](const Qop& qop, f32x4 (&cq)[2]) {
+    float mx[2] = {-INFINITY, -INFINITY};
+    const f32x4 zc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int ch = 0; ch < FNCH; ++ch) {
+      QS S;
+      proj(std::true_type{}, ch, qop, zc, S);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          mx[nt] = fmaxf(mx[nt], max3(S[mt][nt][0], S[mt][nt][1], fmaxf(S[mt][nt][2], S[mt][nt][3])));
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float m = -colmax4(mx[nt]);
+      cq[nt] = f32x4{m, m, m, m};
+    }
+  };
   // den of token column l16 (row 64: tile 4, row 0, held by lanes g = 0).
-  __device__ __forceinline__ float den_of(const QAcc& acc, int nt) const {
-    return __shfl(acc[4][nt][0], l16, 64);
-  }
-  // O rows of the tile through a buffer resource of the block's rows [0,
-  // q1): stores past the block are dropped.
-  __device__ __forceinline__ void store(const QAcc& acc, int tt) const {
-    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(uni(O), uni(q1) * FD * 2);
+  auto den_of = [&](const QAcc& acc, int nt) { return __shfl(acc[4][nt][0], l16, 64); };
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(Oh, q1 * FD * 2);
+  auto store = [&](const QAcc& acc, int tt) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const float inv = 1.0f / den_of(acc, nt);
@@ -680,254 +850,158 @@ struct QTile {
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{x, y}, ro, (tok * FD + 4 * g + 16 * mv) * 2, 0, 0);
       }
     }
-  }
-};
+  };
 
-// Q^T operands of a 32-token tile (tokens tt + 16 nt + l16, dims 32 ks + 8 g
-// .. + 7) from the head's rows through a buffer resource of the block's rows
-// [0, q1): rows past the block read zeros.
-__device__ __forceinline__ void q_load(__amdgpu_buffer_rsrc_t rq, int tt, int l16, int g,
-                                       Qraw& raw) {
+  for (int ti = 0; ti < ntile; ++ti) {
+    const int tt = tt0 + ti * tstep;
+    // Q^T operands in fp16 (token 16 nt + l16, dims 32 ks + 8 g .. + 7) and
+    // the per-token norm term -|q|^2 log2(e) / 2.
+    Qop qop;
+    f32x4 cq[2];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt) {
+      float ss = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      raw[nt][ks] = buffer_load16(rq, ((tt + 16 * nt + l16) * FD + 32 * ks + 8 * g) * 2);
-}
-template <bool RELU>
-__device__ __forceinline__ void q_convert(const Qraw& r, Qop& qop, float (&nq)[2]) {
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    float ss = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint4 x = r[nt][ks];
-      const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 x = raw[nt][ks];
+        if constexpr (!RELU) {
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.x),
+                                               __builtin_bit_cast(bf16x2, x.x), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.y),
+                                               __builtin_bit_cast(bf16x2, x.y), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.z),
+                                               __builtin_bit_cast(bf16x2, x.z), ss, false);
+          ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.w),
+                                               __builtin_bit_cast(bf16x2, x.w), ss, false);
+        }
+        qop[nt][ks] = __builtin_bit_cast(
+            f16x8, make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
+                              bf16x2_to_f16x2(x.w)));
       }
-      uint4 h;
-      h.x = bf16x2_to_f16x2(x.x); h.y = bf16x2_to_f16x2(x.y);
-      h.z = bf16x2_to_f16x2(x.z); h.w = bf16x2_to_f16x2(x.w);
-      qop[nt][ks] = __builtin_bit_cast(f16x8, h);
+      const float nq = RELU ? 0.f : -0.5f * kLog2e * colsum4(ss);
+      cq[nt] = f32x4{nq, nq, nq, nq};
     }
-    nq[nt] = RELU ? 0.f : -0.5f * kLog2e * colsum4(ss);
-  }
-}
-
-// The slow tile (rare: kept out of line, reloading its Q tile, so that the
-// fast loop keeps its registers).
-template <bool RELU>
-__device__ __attribute__((noinline)) void query_slow_tile(QTile t, const uint16_t* Qh, int tt) {
-  Qraw raw;
-  q_load(buffer_rsrc(uni(Qh), uni(t.q1) * FD * 2), tt, t.l16, t.g, raw);
-  Qop qop;
-  float unused[2];
-  q_convert<RELU>(raw, qop, unused);
-  const f32x4 zq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  float mx[2] = {-INFINITY, -INFINITY};
-  for (int ch = 0; ch < FNCH; ++ch) {
-    QS S;
-    t.proj(ch, qop, zq, S);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float c = t.cl[64 * ch + 16 * mt + 4 * t.g + v];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) mx[nt] = fmaxf(mx[nt], S[mt][nt][v] + c);
-      }
-  }
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) mx[nt] = colmax4(mx[nt]);
-  QAcc acc;
-  QTile::reset(acc);
-  for (int ch = 0; ch < FNCH; ++ch) {
-    QS S;
-    t.proj(ch, qop, zq, S);
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float c = t.cl[64 * ch + 16 * mt + 4 * t.g + v];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) S[mt][nt][v] += c - mx[nt];
-      }
-    QFeat qt;
-    QTile::features<RELU>(S, qt);
-    t.apply(ch, qt, acc);
-  }
-  t.store(acc, tt);
-}
-
-template <bool RELU>
-__device__ __attribute__((noinline)) void query_item(Args a_in, int bh_in, int qb_in) {
-  const Args a = uni(a_in);
-  const int bh = uni(bh_in), qb = uni(qb_in);
-  unsigned char* const smem = g_smem;
-  unsigned* const bc = bcast();
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, g = lane >> 4;
-  _Float16* const Wl = reinterpret_cast<_Float16*>(smem);
-  uint16_t* const Kzl = reinterpret_cast<uint16_t*>(smem + QW_BYTES);
-  float* const cl = reinterpret_cast<float*>(smem + QW_BYTES + QK_BYTES);
-  const int L = a.L;
-  const size_t base = static_cast<size_t>(bh) * L * FD;
-  const int q0 = qb * a.QB, q1 = min(L, q0 + a.QB);
-
-  // W' (written by the previous launch) straight into LDS.
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(a.W16);
-    uint4* dst = reinterpret_cast<uint4*>(Wl);
-    constexpr int n16 = FM * WROW / 8;
-    for (int j = wave; 64 * j < n16; j += FNT / 64)
-      if (64 * j + lane < n16) lds_dma16(src + 64 * j + lane, dst + 64 * j);
-  }
-  // The wave's first tile of Q, loaded while the head's state is awaited.
-  const uint16_t* const Qh = a.Q + base;
-  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(Qh, q1 * FD * 2);
-  const int tstep = (FNT / 64) * QTILE;
-  const int tt0 = q0 + wave * QTILE;
-  const int ntile = tt0 < q1 ? (q1 - tt0 + tstep - 1) / tstep : 0;
-  Qraw raw;
-  q_load(rq, tt0, l16, g, raw);
-
-  // Wait until every feature block of the head has written its columns of
-  // the state.
-  if (tid == 0) {
-    unsigned r = 0, spins = 0;
-    while ((r = load_sc1(a.ctrl + Ctrl::arrive(bh))) < static_cast<unsigned>(NFB)) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins >= kSpinLimit) {
-        store_sc1(a.ctrl + Ctrl::TIMEOUT, 1u);
-        break;
-      }
-    }
-    bc[0] = r >= static_cast<unsigned>(NFB) ? 1u : 0u;
-    bc[1] = 0u;
-  }
-  __syncthreads();
-  const unsigned ready = bc[0];
-  // The state and its references (written by other work-groups: sc1).
-  if (ready) {
-    const uint4* src = reinterpret_cast<const uint4*>(a.Kz + static_cast<size_t>(bh) * KZROWS * KZROW);
-    uint4* dst = reinterpret_cast<uint4*>(Kzl);
-    constexpr int n16 = KZROWS * KZROW / 8;
-    for (int j = wave; 64 * j < n16; j += FNT / 64)
-      if (64 * j + lane < n16)
-        __builtin_amdgcn_global_load_lds(src + 64 * j + lane, dst + 64 * j, 16, 0, kSC1);
-    if (wave == 0 && lane < FM / 4)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const uint4*>(a.cfin + static_cast<size_t>(bh) * FM) + lane,
-          reinterpret_cast<uint4*>(cl), 16, 0, kSC1);
-  }
-  vm_drain();
-  __syncthreads();
-  if (ready && tid < FM && cl[tid] != 0.f) bc[1] = 1u;   // some key reference is not 0
-  __syncthreads();
-  if (ready == 0u) {
-    // (the wait gave up: the output of this block is marked invalid)
-    for (int i = tid; i < (q1 - q0) * FD; i += FNT)
-      a.O[base + static_cast<size_t>(q0) * FD + i] = 0x7FC0u;
-    return;
-  }
-  const bool refs = bc[1] != 0u;
-  const QTile T{Wl, Kzl, cl, a.O + base, q1, l16, g};
-
-  // Fast tiles first; the tiles that need the slow form are noted (one bit
-  // per tile: at most 64 per wave by the plan) and done after the loop, so
-  // that no register of the fast loop is live across the out-of-line call.
-  uint64_t slow = 0;
-  if (RELU || !refs) {
-    Qop qcur;
-    float nq[2];
+    if (ti + 1 < ntile) q_load(tt + tstep, raw);
     QAcc acc;
-    for (int ti = 0; ti < ntile; ++ti) {
-      const int tt = tt0 + ti * tstep;
-      q_convert<RELU>(raw, qcur, nq);
-      if (ti + 1 < ntile) q_load(rq, tt + tstep, l16, g, raw);
-      const f32x4 cq[2] = {f32x4{nq[0], nq[0], nq[0], nq[0]}, f32x4{nq[1], nq[1], nq[1], nq[1]}};
-      QTile::reset(acc);
-      QFeat FA, FB;
-      {
-        QS S;
-        T.proj(0, qcur, cq, S);
-        QTile::features<RELU>(S, FA);
-      }
-      auto regular = [&](const int ch, const QFeat& Fcur, QFeat& Fnext) {
-        __builtin_amdgcn_sched_barrier(0);
-        QS S;
-        T.proj(ch + 1, qcur, cq, S);
-        T.apply(ch, Fcur, acc);
-        QTile::features<RELU>(S, Fnext);
-      };
-      regular(0, FA, FB);
-      regular(1, FB, FA);
-      regular(2, FA, FB);
-      __builtin_amdgcn_sched_barrier(0);
-      T.apply(3, FB, acc);
+    bool slow = !RELU && refs;
+    if (!slow) {
+      tile(std::false_type{}, qop, cq, acc);
       if constexpr (!RELU) {
         bool bad = false;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const float den = T.den_of(acc, nt);
+          const float den = den_of(acc, nt);
           bad |= (tt + 16 * nt + l16 < q1) && !(den >= 0x1p-100f && den <= 0x1p100f);
         }
-        if (__ballot(bad) != 0) {
-          slow |= uint64_t{1} << ti;
-          continue;
-        }
+        slow = __ballot(bad) != 0;
       }
-      T.store(acc, tt);
     }
-  } else {
-    slow = ntile >= 64 ? ~uint64_t{0} : (uint64_t{1} << ntile) - 1;
-  }
-  if constexpr (!RELU) {
-    while (slow) {
-      const int ti = __builtin_ctzll(slow);
-      slow &= slow - 1;
-      query_slow_tile<RELU>(T, Qh, tt0 + ti * tstep);
+    if constexpr (!RELU) {
+      if (slow) {
+        row_max(qop, cq);
+        tile(std::true_type{}, qop, cq, acc);
+      }
     }
+    store(acc, tt);
   }
+  __syncthreads();   // every wave is done with the LDS
 }
 
 // ---------------------------------------------------------------------------
+// fused: the persistent kernel.  Heads are dealt to the eight dies in turn;
+// die x's key queue holds items v = (head index on the die) nsplit + split
+// and its query queue v = (head index) nqb + block, both head-major, so that
+// a head's splits are claimed together and its query blocks soon after.  A
+// work-group claims from its own die's queues (the partials a query item
+// sums were mostly written by work-groups of its die: they are fresh in the
+// die's L2), and once those are empty from any die with items left; no
+// items left anywhere ends the phase.  Key items first, then query items.
+// Thread 0 claims and the item goes through LDS.  It claims a key item and
+// a query item at the start (the query claim is held until every key queue
+// is empty), and while each item runs it reads every die's queue heads: a
+// queue seen empty stays empty, so the next claim (an atomic, which the
+// work-groups of a die would otherwise queue up on) is made only where
+// items may be left, and the phase ends without a claim once all are seen
+// empty.
+// ---------------------------------------------------------------------------
+__device__ inline unsigned die_items(int BH, int x, int per_head) {
+  return static_cast<unsigned>(x < BH ? (BH - x + NXCD - 1) / NXCD * per_head : 0);
+}
 
-// ---------------------------------------------------------------------------
-// fused: the persistent kernel.  Die x's queue holds, for its heads
-// x, x + 8, ...: the key items (head, feature block), then the query items
-// (head, query block).  A work-group serves its own die's queue first, then
-// the others in turn.
-// ---------------------------------------------------------------------------
+// Thread 0: an item of the queues at word `qbase` given the own-die claim
+// `own` and a snapshot `c` of every die's queue head (zeros: not taken):
+// die * 2^24 + index, or -1 when no die has items left.
+__device__ inline int pick_item(unsigned* ctrl, int qbase, int per_head, int BH, int my,
+                                unsigned own, unsigned (&c)[NXCD]) {
+  if (own < die_items(BH, my, per_head)) return (my << 24) | static_cast<int>(own);
+  for (;;) {
+    int pick = -1;
+#pragma unroll
+    for (int k = 1; k < NXCD; ++k) {
+      const int x = (my + k) % NXCD;
+      if (pick < 0 && c[x] < die_items(BH, x, per_head)) pick = x;
+    }
+    if (pick < 0) return -1;
+    const unsigned v = __hip_atomic_fetch_add(ctrl + qbase + Ctrl::LINE * pick, 1u,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v < die_items(BH, pick, per_head)) return (pick << 24) | static_cast<int>(v);
+    // (other work-groups took that die's last items: the counts only grow,
+    // so this loop ends)
+#pragma unroll
+    for (int x = 0; x < NXCD; ++x) c[x] = load_sc1(ctrl + qbase + Ctrl::LINE * x);
+  }
+}
+
 template <bool RELU>
 __global__ __launch_bounds__(FNT, 1) void fused(Args a) {
   unsigned* const bc = bcast();
+  const bool lead = threadIdx.x == 0;
   // (this work-group's die: hardware register XCC_ID, bits 3:0)
   const int my = static_cast<int>(__builtin_amdgcn_s_getreg(20 | (3 << 11))) % NXCD;
-  for (int qi = 0; qi < NXCD; ++qi) {
-    const int x = (my + qi) % NXCD;
-    const int nh = x < a.BH ? (a.BH - x + NXCD - 1) / NXCD : 0;
-    const int nK = nh * NFB, nItems = nK + nh * a.nqb;
-    for (;;) {
-      if (threadIdx.x == 0)
-        bc[8] = __hip_atomic_fetch_add(a.ctrl + Ctrl::next(x), 1u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      const int item = static_cast<int>(bc[8]);
-      __syncthreads();
-      if (item >= nItems) break;
-      if (item < nK) {
-        key_item<RELU>(a, x + NXCD * (item / NFB), item % NFB);
-      } else {
-        const int q = item - nK;
-        query_item<RELU>(a, x + NXCD * (q / a.nqb), q % a.nqb);
-      }
-    }
+  unsigned* const kq = a.ctrl + Ctrl::kq(0);
+  unsigned* const qq = a.ctrl + Ctrl::qq(0);
+  const unsigned kmine = die_items(a.BH, my, a.nsplit), qmine = die_items(a.BH, my, a.nqb);
+  unsigned own = 0, qown = 0;
+  unsigned c[NXCD];
+  if (lead) {
+    // A key item and a query item claimed at once (the query claim is used
+    // once every key queue is empty).
+    own = __hip_atomic_fetch_add(kq + Ctrl::LINE * my, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    qown = __hip_atomic_fetch_add(qq + Ctrl::LINE * my, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int x = 0; x < NXCD; ++x) c[x] = 0u;
+  }
+  for (;;) {
+    if (lead) bc[8] = static_cast<unsigned>(pick_item(a.ctrl, Ctrl::kq(0), a.nsplit, a.BH, my, own, c));
+    __syncthreads();
+    const int it = static_cast<int>(bc[8]);
+    __syncthreads();
+    if (it < 0) break;
+    const int x = it >> 24, v = it & 0xFFFFFF;
+    key_item<RELU>(a, x + NXCD * (v / a.nsplit), v % a.nsplit, kq, c);
+    // (the snapshot taken during the item says whether the own queue can
+    // still have items: only then is another claimed)
+    if (lead)
+      own = c[my] < kmine ? __hip_atomic_fetch_add(kq + Ctrl::LINE * my, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                          : kmine;
+  }
+  if (lead) {
+#pragma unroll
+    for (int x = 0; x < NXCD; ++x) c[x] = 0u;
+  }
+  for (;;) {
+    if (lead) bc[8] = static_cast<unsigned>(pick_item(a.ctrl, Ctrl::qq(0), a.nqb, a.BH, my, qown, c));
+    __syncthreads();
+    const int it = static_cast<int>(bc[8]);
+    __syncthreads();
+    if (it < 0) break;
+    const int x = it >> 24, v = it & 0xFFFFFF;
+    query_item<RELU>(a, x + NXCD * (v / a.nqb), v % a.nqb, qq, c);
+    if (lead)
+      qown = c[my] < qmine ? __hip_atomic_fetch_add(qq + Ctrl::LINE * my, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                           : qmine;
   }
 }
 
@@ -940,16 +1014,19 @@ bool fused_bidir_supported(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m
 
 void fused_bidir_layout(Plan* p, int cus) {
   const int BH = p->BH, L = p->L;
-  // Key items: one per (head, 64-feature block) over every token.
-  p->seg = L;
-  p->nseg = 1;
+  // Key items: up to four splits per head, each a whole number of 32-token
+  // tiles and at least 256 tokens (every split holds at least one token).
+  int64_t seg = (static_cast<int64_t>(L) + NSPLIT - 1) / NSPLIT;
+  seg = (seg + FTT - 1) / FTT * FTT;
+  if (seg < 256) seg = 256;
+  p->seg = static_cast<int32_t>(seg);
+  p->nseg = static_cast<int32_t>((L + seg - 1) / seg);
   // Query blocks: about one query item per compute unit, a multiple of 256
-  // tokens (one 32-token tile per wave), at most 64 tiles per wave (the
-  // query item tracks its slow tiles in a 64-bit mask).
+  // tokens (one 32-token tile per wave).
   const int64_t want = (static_cast<int64_t>(L) * BH + cus - 1) / cus;
   int64_t qb = (want + 255) / 256 * 256;
-  qb = qb < 256 ? 256 : (qb > 64 * 256 ? 64 * 256 : qb);
-  p->qblk = static_cast<int32_t>(qb);
+  qb = qb < 256 ? 256 : qb;
+  p->qblk = static_cast<int32_t>(qb > L ? (static_cast<int64_t>(L) + 255) / 256 * 256 : qb);
 }
 
 hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
@@ -961,11 +1038,13 @@ hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, cons
   a.V = static_cast<const uint16_t*>(V);
   a.O = static_cast<uint16_t*>(O);
   a.W16 = reinterpret_cast<const _Float16*>(w + p.off_cP);
-  a.Kz = reinterpret_cast<uint16_t*>(w + p.off_KV);
-  a.cfin = reinterpret_cast<float*>(w + p.off_cfin);
+  a.T = reinterpret_cast<float*>(w + p.off_T);
+  a.cs = reinterpret_cast<float*>(w + p.off_cseg);
   a.ctrl = reinterpret_cast<unsigned*>(w + p.off_ctrl);
   a.L = p.L;
   a.BH = p.BH;
+  a.nsplit = p.nseg;
+  a.seg = p.seg;
   a.QB = p.qblk;
   a.nqb = (p.L + p.qblk - 1) / p.qblk;
   a.knorm = p.knorm;
@@ -980,7 +1059,7 @@ hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, cons
   e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  const int items = a.BH * (NFB + a.nqb);
+  const int items = a.BH * (a.nsplit + a.nqb);
   const int grid = cus < items ? cus : items;
   timing_before(st);
   if (p.relu)
