@@ -92,7 +92,10 @@ enum favor_status {
                                  workspace base is not 256-byte aligned         */
   FAVOR_ERR_WORKSPACE = -5,   /* workspace_bytes below favor_workspace_bytes()  */
   FAVOR_ERR_HIP = -6,         /* a HIP runtime call failed                      */
-  FAVOR_ERR_ALIAS = -7        /* two buffers that must be distinct overlap      */
+  FAVOR_ERR_ALIAS = -7,       /* two buffers that must be distinct overlap      */
+  FAVOR_ERR_SCRATCH = -8      /* favor_fwd_attn_noalloc: the shape needs more
+                                 than FAVOR_NOALLOC_SCRATCH_BYTES of workspace,
+                                 or the stream is not on the current device    */
 };
 
 /*
@@ -152,6 +155,25 @@ int favor_fwd_attn(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_
                    int32_t causal, int32_t attn_kernel, const void* Q, const void* K,
                    const void* V, const float* W, void* O, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * favor_fwd_attn with no workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is a static device array
+ * of FAVOR_NOALLOC_SCRATCH_BYTES on each GPU the library runs on, held until
+ * the process ends; this call allocates nothing.  It runs on the calling
+ * thread's current device: `stream` (NULL: the null stream) must belong to
+ * it.  Every call on one GPU shares that GPU's array, so calls that overlap
+ * on one GPU (other streams, other threads) race and must be ordered by the
+ * caller.  Errors as favor_fwd_attn, plus FAVOR_ERR_SCRATCH when
+ * favor_workspace_bytes() for the shape exceeds the array (64 MiB: enough for
+ * B*H = 64 heads of L = 4096 at d = 64, m = 256, in either form) or the
+ * stream is on another device.
+ */
+#define FAVOR_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int favor_fwd_attn_noalloc(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
+                           int32_t causal, int32_t attn_kernel, const void* Q, const void* K,
+                           const void* V, const float* W, void* O, void* stream);
 
 /*
  * Workspace size, in bytes, of favor_bwd_attn for this shape (written to

@@ -15,6 +15,7 @@ import numpy as np
 import torch
 
 __all__ = ["FavorError", "LIB_PATH", "lib", "workspace_bytes", "fwd_bidir", "fwd_causal",
+           "fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
            "bwd", "bwd_workspace_bytes", "draw_projection_device", "state_bytes", "state_new", "state_reset", "prefill", "prefill_workspace_bytes",
            "decode",
            "feature_map", "draw_projection", "status_string", "plan_describe", "timing_start", "timing_stop",
@@ -53,6 +54,8 @@ def _load():
         f.restype = ctypes.c_int
     L.favor_fwd_attn.argtypes = [i32] * 8 + [vp, vp, vp, fp, vp, vp, sz, vp]
     L.favor_fwd_attn.restype = ctypes.c_int
+    L.favor_fwd_attn_noalloc.argtypes = [i32] * 8 + [vp, vp, vp, fp, vp, vp]
+    L.favor_fwd_attn_noalloc.restype = ctypes.c_int
     L.favor_bwd_workspace_bytes.argtypes = [i32] * 7 + [ctypes.POINTER(sz)]
     L.favor_bwd_workspace_bytes.restype = ctypes.c_int
     L.favor_bwd_attn.argtypes = [i32] * 8 + [vp, vp, vp, fp, vp, vp, vp, vp, vp, sz, vp]
@@ -182,6 +185,23 @@ def _forward(name, causal, q, k, v, W, out, workspace, stream, kernel="softmax")
         name = "favor_fwd_attn"
         st = lib.favor_fwd_attn(B, H, L, d, m, dt, int(causal), ak, *ptrs)
     _check(st, name)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024   # FAVOR_NOALLOC_SCRATCH_BYTES
+
+
+def fwd_noalloc(q, k, v, W, out, causal=False, kernel="softmax", stream=None):
+    """favor_fwd_attn_noalloc: the forward pass into a caller-supplied `out`, with the
+    library's static per-GPU scratch as the workspace (nothing is allocated; calls
+    that overlap on one GPU race on the scratch)."""
+    ak = _kernel(kernel)
+    B, H, L, d, m, dt = _shape_of(q, k, v, W)
+    _check_out(out, q.shape, q.dtype, q.device, "out")
+    st = lib.favor_fwd_attn_noalloc(B, H, L, d, m, dt, int(bool(causal)), ak, q.data_ptr(),
+                                    k.data_ptr(), v.data_ptr(), W.data_ptr(), out.data_ptr(),
+                                    _stream(q, stream))
+    _check(st, "favor_fwd_attn_noalloc")
     return out
 
 

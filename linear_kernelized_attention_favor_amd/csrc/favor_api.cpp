@@ -514,6 +514,9 @@ const char* favor_status_string(int status) {
       return "workspace smaller than favor_workspace_bytes() (favor_bwd_workspace_bytes() for "
              "the backward pass)";
     case FAVOR_ERR_HIP: return "a HIP runtime call failed (see favor_last_hip_error)";
+    case FAVOR_ERR_SCRATCH:
+      return "favor_fwd_attn_noalloc: the shape needs more workspace than the static scratch "
+             "(FAVOR_NOALLOC_SCRATCH_BYTES), or the stream is not on the current device";
     case FAVOR_ERR_ALIAS:
       return "two buffers that must be distinct overlap (favor_prefill: state_in and state_out)";
     default: return "unknown status";
