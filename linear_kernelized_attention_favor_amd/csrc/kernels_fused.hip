@@ -176,6 +176,18 @@ struct Args {
 // bytes as a broadcast area for values one thread decides.
 __shared__ __align__(16) unsigned char g_smem[FUSED_LDS];
 __device__ inline unsigned* bcast() { return reinterpret_cast<unsigned*>(g_smem + FUSED_LDS - 64); }
+// LDS at byte offset `a` into the work-group's LDS (offsets formed once per
+// lane, constants added at each use).  (An LDS pointer made from an integer
+// would turn offset 0 into the null LDS pointer.)
+template <class T>
+__device__ inline __attribute__((address_space(3))) T* lds_at(uint32_t a) {
+  return (__attribute__((address_space(3))) T*)((__attribute__((address_space(3))) unsigned char*)g_smem + a);
+}
+// The LDS address of g_smem (for instructions written out in assembly).
+__device__ inline uint32_t lds_addr0() {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char*)g_smem));
+}
 
 // Sum over the four lanes {l, l^16, l^32, l^48} (one column of a 16x16 tile).
 __device__ inline float colsum4(float x) {
@@ -257,62 +269,88 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) cref[nt] = 0.f;
 
-  auto slot = [&](int i) { return ring + (i % NSLOT) * SLOT_BYTES; };
-  // This wave's quarter of tile i of the group (two DMA instructions): slot
-  // unit u = 128 fw + 64 j + lane, units 0..255 the K rows and 256..511 the
-  // V rows; unit u of a row holds the row's global unit (u % 8) ^ (row % 8).
-  // Rows past the split read zero.
-  auto dma_part = [&](int i, int j) {
+  // Slot r of the ring holds tiles r, r + 6, ...; the slot index is a
+  // compile-time constant at every use (the step loop is unrolled six
+  // times), so the per-lane LDS addresses below are formed once and the
+  // slot's offset is the instructions' immediate.
+  using I0 = std::integral_constant<int, 0>;
+  const uint32_t ring_a = static_cast<uint32_t>(tg * NSLOT * SLOT_BYTES);   // offset of `ring`
+  // Byte offset of the slot holding tile R: a compile-time constant for the
+  // unrolled fast loop, computed for the slow loop and the ReLU features'
+  // loop (not unrolled: their register allocation does not fit six copies).
+  auto soff = [](auto R) {
+    if constexpr (std::is_integral_v<decltype(R)>) return (R % NSLOT) * SLOT_BYTES;
+    else return decltype(R)::value * SLOT_BYTES;
+  };
+  // This wave's quarter of tile i (slot R) of the group (two DMA
+  // instructions): slot unit u = 128 fw + 64 j + lane, units 0..255 the K rows
+  // and 256..511 the V rows; unit u of a row holds the row's global unit
+  // (u % 8) ^ (row % 8).  Rows past the split read zero.
+  auto dma_part = [&](auto R, int i, int j) {
     const int tb = (NTG * i + tg) * FTT;
-    unsigned char* const sl = slot(i);
     const int uu = (128 * fw + 64 * j + lane) & 255, row = uu >> 3, gu = (uu & 7) ^ (row & 7);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc_kv, (lds_ptr)(sl + 16 * (128 * fw + 64 * j)), 16,
+        rsrc_kv, (lds_ptr)(ring + soff(R) + 16 * (128 * fw + 64 * j)), 16,
         ((tb + row) * FD + 8 * gu) * 2, 0, 0, 0);
   };
-  auto dma = [&](int i) {
-    dma_part(i, 0);
-    dma_part(i, 1);
-  };
-  // K rows 8 fw .. + 7 of tile i to fp16 in place (lane: row 8 fw + lane / 8,
-  // 16-byte unit lane % 8) and their norm terms (8 lanes per row).
-  auto convert = [&](int i) {
-    unsigned char* const sl = slot(i);
-    const int row = 8 * fw + (lane >> 3);
-    uint4* const p = reinterpret_cast<uint4*>(sl + row * 128 + (lane & 7) * 16);
-    const uint4 x = *p;
-    float ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.x),
-                                               __builtin_bit_cast(bf16x2, x.x), 0.f, false);
-    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.y),
-                                         __builtin_bit_cast(bf16x2, x.y), ss, false);
-    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.z),
-                                         __builtin_bit_cast(bf16x2, x.z), ss, false);
-    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.w),
-                                         __builtin_bit_cast(bf16x2, x.w), ss, false);
+  // K rows 8 fw .. + 7 of tile i (slot R) to fp16 in place (lane: row
+  // 8 fw + lane / 8, 16-byte unit lane % 8) and their norm terms (8 lanes per
+  // row).
+  const int crow = 8 * fw + (lane >> 3);
+  const uint32_t cvt_a = ring_a + crow * 128 + (lane & 7) * 16;
+  const uint32_t cvt_nb = ring_a + SLOT_NB + crow * 4;
+  auto convert = [&](auto R, int i) {
+    const int off = soff(R);
+    auto* const p = lds_at<u32x4>(cvt_a + off);
+    const u32x4 x = *p;
+    const uint32_t w0 = x[0], w1 = x[1], w2 = x[2], w3 = x[3];
+    float ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0),
+                                               __builtin_bit_cast(bf16x2, w0), 0.f, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1),
+                                         __builtin_bit_cast(bf16x2, w1), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2),
+                                         __builtin_bit_cast(bf16x2, w2), ss, false);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3),
+                                         __builtin_bit_cast(bf16x2, w3), ss, false);
     ss = group_sum<8>(ss);
-    *p = make_uint4(bf16x2_to_f16x2(x.x), bf16x2_to_f16x2(x.y), bf16x2_to_f16x2(x.z),
-                    bf16x2_to_f16x2(x.w));
+    *p = u32x4{bf16x2_to_f16x2(w0), bf16x2_to_f16x2(w1), bf16x2_to_f16x2(w2), bf16x2_to_f16x2(w3)};
     const int tb = (NTG * i + tg) * FTT;
-    if ((lane & 7) == 0)
-      reinterpret_cast<float*>(sl + SLOT_NB)[row] = tb + row < n ? nscale * ss : -INFINITY;
+    if ((lane & 7) == 0) *lds_at<float>(cvt_nb + off) = tb + crow < n ? nscale * ss : -INFINITY;
   };
+  // Operand addresses of the projection (token 16 mt + l16, dims 32 ks +
+  // 8 g .. + 7, fp16) and of its C input (rows 16 mt + 4 g .. + 3).
+  uint32_t kop_a[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int row = 16 * mt + l16, c = 4 * ks + g;
+      kop_a[mt][ks] = ring_a + row * 128 + ((c ^ (row & 7)) * 16);
+    }
+  const uint32_t nq_a = ring_a + SLOT_NB + 16 * g;
+  // Transposing-read addresses of the contraction's V^T operand (value
+  // column 16 mv + l16; read r of a pair adds 16 rows, 2048 bytes).
+  uint32_t tr_a[4];
+  {
+    const int row = 4 * g + (l16 >> 2);
+#pragma unroll
+    for (int mv = 0; mv < 4; ++mv)
+      tr_a[mv] = lds_addr0() + ring_a + KT_BYTES + row * 128 +
+                 (((2 * mv + ((l16 & 3) >> 1)) ^ (row & 7)) * 16) + (l16 & 1) * 8;
+  }
   using SArr = f32x4[2][4];
   // S for tile i: fp16 operands (token 16 mt + l16, dims 32 ks + 8 g .. + 7)
   // and the C input -n (rows 16 mt + 4 g .. + 3) from the slot.
-  auto proj = [&](int i, SArr& S) {
-    const unsigned char* const sl = slot(i);
+  auto proj = [&](auto R, SArr& S) {
+    const int off = soff(R);
     f16x8 ka[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int row = 16 * mt + l16, c = 4 * ks + g;
-        ka[mt][ks] = *reinterpret_cast<const f16x8*>(sl + row * 128 + ((c ^ (row & 7)) * 16));
-      }
+      for (int ks = 0; ks < 2; ++ks) ka[mt][ks] = *lds_at<const f16x8>(kop_a[mt][ks] + off);
     f32x4 nq[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      nq[mt] = *reinterpret_cast<const f32x4*>(sl + SLOT_NB + (16 * mt + 4 * g) * 4);
+    for (int mt = 0; mt < 2; ++mt) nq[mt] = *lds_at<const f32x4>(nq_a + off + 64 * mt);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -376,28 +414,34 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
   // r: lane l16 of the 16-lane group g addresses row 16 r + 4 g + l16/4,
   // columns 16 mv + 4 (l16 % 4) .. + 3, and receives column 16 mv + l16 of
   // rows 16 r + 4 g .. + 3).
-  auto contract_half = [&](int i, const bf16x8 (&kb)[4], int half) {
+  auto contract_half = [&](auto R, const bf16x8 (&kb)[4], int half) {
     // The four transposing reads of the half are issued together and waited
     // for in the same statement (the compiler would otherwise wait for every
     // LDS DMA in flight before each of them; this tile's DMA has landed).
-    const uint32_t vt = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(slot(i) + KT_BYTES));
-    const int row = 4 * g + (l16 >> 2);
-    uint32_t ad[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int mv = 2 * half + u;
-      ad[u] = vt + row * 128 + (((2 * mv + ((l16 & 3) >> 1)) ^ (row & 7)) * 16) + (l16 & 1) * 8;
-    }
     uint64_t h[4];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %4\n\t"
-        "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
-        "ds_read_b64_tr_b16 %2, %5\n\t"
-        "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
-        : "v"(ad[0]), "v"(ad[1])
-        : "memory");
+    if constexpr (std::is_integral_v<decltype(R)>) {
+      const uint32_t o = static_cast<uint32_t>(soff(R));
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4\n\t"
+          "ds_read_b64_tr_b16 %1, %4 offset:2048\n\t"
+          "ds_read_b64_tr_b16 %2, %5\n\t"
+          "ds_read_b64_tr_b16 %3, %5 offset:2048\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+          : "v"(tr_a[2 * half] + o), "v"(tr_a[2 * half + 1] + o)
+          : "memory");
+    } else {
+      constexpr int off = decltype(R)::value * SLOT_BYTES;
+      asm volatile(
+          "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+          "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+          "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+          "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+          : "v"(tr_a[2 * half]), "v"(tr_a[2 * half + 1]), "n"(off), "n"(off + 2048)
+          : "memory");
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int mv = 2 * half + u;
@@ -419,39 +463,58 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
   // tile 1 likewise (six), then tile 0 projected and its features formed.
   // DMAs past the group's last tile read zeros, so every step issues the
   // same number of operations.
-#pragma unroll
-  for (int i = 0; i < 5; ++i) dma(i);
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I5 = std::integral_constant<int, 5>;
+  dma_part(I0{}, 0, 0); dma_part(I0{}, 0, 1);
+  dma_part(I1{}, 1, 0); dma_part(I1{}, 1, 1);
+  dma_part(I2{}, 2, 0); dma_part(I2{}, 2, 1);
+  dma_part(I3{}, 3, 0); dma_part(I3{}, 3, 1);
+  dma_part(I4{}, 4, 0); dma_part(I4{}, 4, 1);
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
   lds_barrier();
-  convert(0);
+  convert(I0{}, 0);
   asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   lds_barrier();
-  convert(1);
+  convert(I1{}, 1);
   bf16x8 kbA[4], kbB[4];
   {
     SArr S;
-    proj(0, S);
+    proj(I0{}, S);
     if constexpr (SLOW) rebase(S, true);
     features(S, kbA);
   }
-  // Step i: tile i + 2 has landed (this wave's tiles i + 3, i + 4 may be in
-  // flight) and tile i + 1 is converted everywhere; every wave is done with
-  // tile i - 1, whose slot takes tile i + 5.
-  auto step = [&](int i, const bf16x8 (&kcur)[4], bf16x8 (&knext)[4]) {
+  // Step i (tile i in slot R = i % 6): tile i + 2 has landed (this wave's
+  // tiles i + 3, i + 4 may be in flight) and tile i + 1 is converted
+  // everywhere; every wave is done with tile i - 1, whose slot takes tile
+  // i + 5.  The tile's two DMA instructions go between the matrix work
+  // (after the projection, halfway through the contraction) rather than in
+  // a burst after the barrier: an instruction that finds the memory
+  // pipeline's queue full holds up its wave.
+  auto step = [&](auto R, int i, const bf16x8 (&kcur)[4], bf16x8 (&knext)[4]) {
+    auto r1 = [&]() {
+      if constexpr (std::is_integral_v<decltype(R)>) return i + 1;
+      else return std::integral_constant<int, (decltype(R)::value + 1) % NSLOT>{};
+    }();
+    auto r2 = [&]() {
+      if constexpr (std::is_integral_v<decltype(R)>) return i + 2;
+      else return std::integral_constant<int, (decltype(R)::value + 2) % NSLOT>{};
+    }();
+    auto r5 = [&]() {
+      if constexpr (std::is_integral_v<decltype(R)>) return i + 5;
+      else return std::integral_constant<int, (decltype(R)::value + 5) % NSLOT>{};
+    }();
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     lds_barrier();
-    convert(i + 2);
+    convert(r2, i + 2);
     SArr S;
-    proj(i + 1, S);
-    // The tile's two DMA instructions go between the matrix work (after the
-    // projection, halfway through the contraction) rather than in a burst
-    // after the barrier: an instruction that finds the memory pipeline's
-    // queue full holds up its wave, and spread out it stays behind the
-    // matrix work.
-    dma_part(i + 5, 0);
-    contract_half(i, kcur, 0);
-    dma_part(i + 5, 1);
-    contract_half(i, kcur, 1);
+    proj(r1, S);
+    dma_part(r5, i + 5, 0);
+    contract_half(R, kcur, 0);
+    dma_part(r5, i + 5, 1);
+    contract_half(R, kcur, 1);
     features(S, knext);
     if constexpr (SLOW) {
       if (__builtin_expect(overflow(knext), 0)) {
@@ -460,10 +523,25 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
       }
     }
   };
-  for (int i = 0; i < nsteps; i += 2) {
-    step(i, kbA, kbB);
+  static_assert(NSLOT == 6, "the fast step loop is unrolled once around the ring");
+  if constexpr (SLOW || RELU) {
+    for (int i = 0; i < nsteps; i += 2) {
+      step(i, i, kbA, kbB);
+      if (i + 1 >= nsteps) break;
+      step(i + 1, i + 1, kbB, kbA);
+    }
+  } else for (int i = 0; i < nsteps; i += 6) {
+    step(I0{}, i, kbA, kbB);
     if (i + 1 >= nsteps) break;
-    step(i + 1, kbB, kbA);
+    step(I1{}, i + 1, kbB, kbA);
+    if (i + 2 >= nsteps) break;
+    step(I2{}, i + 2, kbA, kbB);
+    if (i + 3 >= nsteps) break;
+    step(I3{}, i + 3, kbB, kbA);
+    if (i + 4 >= nsteps) break;
+    step(I4{}, i + 4, kbA, kbB);
+    if (i + 5 >= nsteps) break;
+    step(I5{}, i + 5, kbB, kbA);
   }
   // (the DMAs issued past the group's last tile land before the LDS is reused)
   vm_drain();
