@@ -575,8 +575,7 @@ __device__ __forceinline__ void key_item(const Args& a, int bh, int s, unsigned*
     const bool slow = pass == 1;
     if (slow) key_pass<RELU, true>(a, bh, t0, t1, acc, cref);
     else key_pass<RELU, false>(a, bh, t0, t1, acc, cref);
-    if (tid == 0 && pass == 0) take_snapshot(snapq, snap);
-    __syncthreads();   // the ring is read: the merge slots take its bytes
+    lds_barrier();   // the ring is read: the merge slots take its bytes
     if (tg == 1) {
       f32x4* slot = reinterpret_cast<f32x4*>(g_smem + fw * MERGE_SLOT) + lane;
 #pragma unroll
@@ -585,7 +584,7 @@ __device__ __forceinline__ void key_item(const Args& a, int bh, int s, unsigned*
         for (int nt = 0; nt < 4; ++nt) slot[(mv * 4 + nt) * 64] = acc[mv][nt];
       slot[20 * 64] = f32x4{cref[0], cref[1], cref[2], cref[3]};
     }
-    __syncthreads();
+    lds_barrier();
     bool bad = false;
     if (tg == 0) {
       const f32x4* slot = reinterpret_cast<const f32x4*>(g_smem + fw * MERGE_SLOT) + lane;
@@ -613,9 +612,9 @@ __device__ __forceinline__ void key_item(const Args& a, int bh, int s, unsigned*
     }
     if (RELU || slow) break;
     if (tid == 0) bc[0] = 0u;
-    __syncthreads();
+    lds_barrier();
     if (bad) bc[0] = 1u;
-    __syncthreads();
+    lds_barrier();
     if (bc[0] == 0u) break;
   }
   if (tg == 0) {
@@ -640,8 +639,10 @@ __device__ __forceinline__ void key_item(const Args& a, int bh, int s, unsigned*
       for (int nt = 0; nt < 4; ++nt) store4_sc1(rc, (64 * fw + 16 * nt + l16) * 4, cref[nt]);
     }
   }
+  // (the queue-head snapshot is read while the stores drain)
+  if (tid == 0) take_snapshot(snapq, snap);
   vm_drain();
-  __syncthreads();
+  lds_barrier();   // every wave's stores have completed
   if (tid == 0)
     __hip_atomic_fetch_add(a.ctrl + Ctrl::arrive(bh), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -728,7 +729,8 @@ __device__ __forceinline__ void query_item(const Args& a, int bh, int qb, unsign
     bc[0] = r >= static_cast<unsigned>(nsplit) ? 1u : 0u;
     bc[1] = 0u;
   }
-  __syncthreads();
+  // (LDS only: W' and the first Q tile stay in flight)
+  lds_barrier();
   const unsigned ready = bc[0];
   if (ready == 0u) {
     // (the wait gave up: the output of this block is marked invalid)
@@ -768,7 +770,7 @@ __device__ __forceinline__ void query_item(const Args& a, int bh, int qb, unsign
       cl[tid] = cn;
       if (cn != 0.f) bc[1] = 1u;   // some reference is not 0
     }
-    __syncthreads();
+    lds_barrier();
     auto combine = [&](int u, const uint4 (&xs)[NSPLIT]) {
       const int row = u / (FM / 4), f = 4 * (u % (FM / 4));
       float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -807,7 +809,7 @@ __device__ __forceinline__ void query_item(const Args& a, int bh, int qb, unsign
     }
   }
   vm_drain();   // W' has landed
-  __syncthreads();
+  lds_barrier();
   const bool refs = bc[1] != 0u;
   if (tid == 0) take_snapshot(snapq, snap);
 
@@ -982,7 +984,7 @@ __device__ __forceinline__ void query_item(const Args& a, int bh, int qb, unsign
     }
     store(acc, tt);
   }
-  __syncthreads();   // every wave is done with the LDS
+  lds_barrier();   // every wave is done with the LDS (the O stores may still drain)
 }
 
 // ---------------------------------------------------------------------------
@@ -1051,9 +1053,9 @@ __global__ __launch_bounds__(FNT, 1) void fused(Args a) {
   }
   for (;;) {
     if (lead) bc[8] = static_cast<unsigned>(pick_item(a.ctrl, Ctrl::kq(0), a.nsplit, a.BH, my, own, c));
-    __syncthreads();
+    lds_barrier();
     const int it = static_cast<int>(bc[8]);
-    __syncthreads();
+    lds_barrier();
     if (it < 0) break;
     const int x = it >> 24, v = it & 0xFFFFFF;
     key_item<RELU>(a, x + NXCD * (v / a.nsplit), v % a.nsplit, kq, c);
@@ -1070,9 +1072,9 @@ __global__ __launch_bounds__(FNT, 1) void fused(Args a) {
   }
   for (;;) {
     if (lead) bc[8] = static_cast<unsigned>(pick_item(a.ctrl, Ctrl::qq(0), a.nqb, a.BH, my, qown, c));
-    __syncthreads();
+    lds_barrier();
     const int it = static_cast<int>(bc[8]);
-    __syncthreads();
+    lds_barrier();
     if (it < 0) break;
     const int x = it >> 24, v = it & 0xFFFFFF;
     query_item<RELU>(a, x + NXCD * (v / a.nqb), v % a.nqb, qq, c);
