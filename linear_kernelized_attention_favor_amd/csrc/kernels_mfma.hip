@@ -81,6 +81,15 @@ constexpr float kQBias = 20.0f;
 #ifndef FAVOR_QAPPLY_WGS
 #define FAVOR_QAPPLY_WGS 512    // query-side work-groups per call the plan aims for
 #endif
+#ifndef FAVOR_QSTREAM_NW
+#define FAVOR_QSTREAM_NW 8      // waves per streamed query-side work-group
+#endif
+#ifndef FAVOR_QSTREAM_NTQ
+#define FAVOR_QSTREAM_NTQ 2     // 16-token tiles per streamed query-side wave
+#endif
+#ifndef FAVOR_QSTREAM_WPE
+#define FAVOR_QSTREAM_WPE 2     // streamed query-side waves per SIMD
+#endif
 constexpr int kTT = 32;        // tokens per key tile
 
 template <int D>
@@ -828,21 +837,31 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
     }
   };
   // O = num / den for one tile; den is row 0 of the last tile (g = 0, v = 0).
+  // O rows: lanes g and g ^ 1 trade a quarter of two 16-value blocks, so
+  // that each lane stores 16 contiguous bytes and the four lanes of a token
+  // 64 (two blocks); streamed past L2 with the non-temporal hint.
   auto finish = [&](int tt) {
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
       const float den = __shfl(acc[C::MV][nt][0], l16, 64);
       const float inv = 1.0f / den;
       const int tok = tt + 16 * nt + l16;
-      if (tok < q1) {
-        uint16_t* orow = O + base + static_cast<size_t>(tok) * D + 4 * g;
+      const bool odd = (g & 1) != 0;
 #pragma unroll
-        for (int mv = 0; mv < C::MV; ++mv) {
-          uint2 o;
-          o.x = pack_bf16(acc[mv][nt][0] * inv, acc[mv][nt][1] * inv);
-          o.y = pack_bf16(acc[mv][nt][2] * inv, acc[mv][nt][3] * inv);
-          *reinterpret_cast<uint2*>(orow + 16 * mv) = o;
-        }
+      for (int pr = 0; pr < C::MV / 2; ++pr) {
+        const f32x4 x0 = acc[2 * pr][nt], x1 = acc[2 * pr + 1][nt];
+        const u32x2 a0 = u32x2{pack_bf16(x0[0] * inv, x0[1] * inv), pack_bf16(x0[2] * inv, x0[3] * inv)};
+        const u32x2 a1 = u32x2{pack_bf16(x1[0] * inv, x1[1] * inv), pack_bf16(x1[2] * inv, x1[3] * inv)};
+        // even g keeps block 2 pr (values 4 g .. 4 g + 7), odd g block
+        // 2 pr + 1 (values 4 (g - 1) .. 4 g + 3)
+        const u32x2 give = odd ? a0 : a1;
+        const u32x2 got = u32x2{static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.x), 16, 64)),
+                                static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.y), 16, 64))};
+        const u32x4 out = odd ? u32x4{got.x, got.y, a1.x, a1.y} : u32x4{a0.x, a0.y, got.x, got.y};
+        const int col = odd ? 16 * (2 * pr + 1) + 4 * (g - 1) : 16 * (2 * pr) + 4 * g;
+        if (tok < q1)
+          __builtin_nontemporal_store(
+              out, reinterpret_cast<u32x4*>(O + base + static_cast<size_t>(tok) * D + col));
       }
     }
   };
@@ -930,11 +949,25 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
 // (m (d+8) + (d+16)(m+8) halves over 160 KB, e.g. d = 128 with m = 512).
 // Grid as qapply.  The NW waves take their 16*NTQ-token tiles in lockstep
 // rounds, and each round streams the features through LDS in 64-feature
-// chunks, double buffered: chunk k+1 travels from global memory straight
-// into LDS (global_load_lds, no registers) while chunk k is used.  Per chunk
+// chunks, in a ring of three buffers: chunks k+1 and k+2 travel from global
+// memory straight into LDS (global_load_lds, no registers) while chunk k is
+// used, and a step waits only for chunk k+1 (the barriers order LDS only,
+// so chunk k+2's loads stay in flight across them).  A wave's Q tile for the
+// next round is fetched at the start of the current one.  Per chunk
 // buffer: W' rows [64][D+8] fp16 (as laid out in the workspace), [KV | z]
 // columns [D+16][64] bf16 with the 16-byte units of row r XOR-swizzled by
 // (r >> 1) & 7 (conflict-free operand reads without padding), c [64] fp32.
+// A chunk is used in two 32-feature halves (projection, features,
+// application), so that only one half's S is live (no spill at d = 128).
+// Every LDS operand read feeds NTQ matrix instructions, so the operand
+// traffic per token falls as 1/NTQ; NTQ = 4 needs one wave per SIMD
+// (WPE = 1, accumulators in the AGPRs), which at d = 128, m = 512 measured
+// slower than eight waves of NTQ = 2 (1128 against 922 us): a lone wave
+// leaves the latency of its exponentials and LDS reads exposed.  Q and O
+// pass with the non-temporal hint (once each; the chunks, re-read every
+// round, stay in L2), O in 64-byte row pieces (finish): stored 8 bytes per
+// lane, plainly the lines cost a fill read each (fetch up by the output's
+// size), with the hint the written bytes doubled.
 // ---------------------------------------------------------------------------
 template <int D>
 struct QsLds {
@@ -951,17 +984,18 @@ struct QsLds {
   static_assert(W16 % 64 == 0 && K16 % 64 == 0, "whole waves per staging job");
 };
 
-template <int D, int NW, int NTQ, int NCH, bool RELU>
-__global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict__ Q,
-                                                   const _Float16* __restrict__ W16,
-                                                   const uint16_t* __restrict__ Kz,
-                                                   const float* __restrict__ cfin,
-                                                   uint16_t* __restrict__ O, int L, int QL) {
+template <int D, int NW, int NTQ, int NCH, bool RELU, int WPE>
+__global__ __launch_bounds__(NW * 64, WPE) void qstream(const uint16_t* __restrict__ Q,
+                                                     const _Float16* __restrict__ W16,
+                                                     const uint16_t* __restrict__ Kz,
+                                                     const float* __restrict__ cfin,
+                                                     uint16_t* __restrict__ O, int L, int QL) {
   using C = QCfg<D, NTQ>;
   using LS = QsLds<D>;
   constexpr int m = 64 * NCH;
   constexpr int kzrow = m + 8;
-  __shared__ __align__(16) unsigned char qs_smem[2 * LS::BUF];
+  constexpr int NBUF = 3;
+  __shared__ __align__(16) unsigned char qs_smem[NBUF * LS::BUF];
   const int nqb = (L + QL - 1) / QL;
   const int item = xcd_major(blockIdx.x, gridDim.x);
   const int qb = item % nqb, bh = item / nqb;
@@ -971,6 +1005,11 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
   const size_t base = static_cast<size_t>(bh) * L * D;
   const int q0 = qb * QL, q1 = min(L, q0 + QL);
   const int nround = (q1 - q0 + NW * C::TQ - 1) / (NW * C::TQ);
+  if constexpr (WPE == 1) {
+    // (an AGPR operand: the compiler then gives the matrix instructions'
+    // accumulators the AGPRs, beside the 256 VGPRs)
+    asm volatile("; accumulators in AGPRs %0" ::"a"(0.f));
+  }
 
   auto Wl = [&](int b) { return reinterpret_cast<_Float16*>(qs_smem + b * LS::BUF); };
   auto Kzl = [&](int b) {
@@ -987,7 +1026,9 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
       reinterpret_cast<const uint4*>(Kz + static_cast<size_t>(bh) * (D + 16) * kzrow);
   const uint4* const csrc = reinterpret_cast<const uint4*>(cfin + static_cast<size_t>(bh) * m);
   auto stage = [&](int ch, int b) {
-    for (int j = wave; j < LS::JOBS; j += NW) {
+#pragma unroll
+    for (int i = 0; i < (LS::JOBS + NW - 1) / NW; ++i) {
+      const int j = wave + NW * i;
       if (j < LS::WJOBS) {
         lds_dma16(wsrc + ch * LS::W16 + 64 * j + lane, reinterpret_cast<uint4*>(Wl(b)) + 64 * j);
       } else if (j < LS::WJOBS + LS::KJOBS) {
@@ -995,153 +1036,174 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
         const int row = u >> 3, c8 = (u & 7) ^ ((row >> 1) & 7);
         lds_dma16(ksrc + (row * kzrow + 64 * ch) / 8 + c8,
                   reinterpret_cast<uint4*>(Kzl(b)) + 64 * (j - LS::WJOBS));
-      } else if (lane < 16) {
+      } else if (j < LS::JOBS && lane < 16) {
         lds_dma16(csrc + 16 * ch + lane, cl(b));
       }
     }
   };
   // This wave's staging loads have landed in LDS (then a barrier publishes).
   auto staged = [&]() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  // ... all but this wave's staging loads of the newest chunk
+  const int myjobs = (LS::JOBS - wave + NW - 1) / NW;
+  auto staged_but_newest = [&]() {
+    constexpr int lo = LS::JOBS / NW;
+    if (myjobs > lo) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lo + 1) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(lo) : "memory");
+  };
 
   using Qop = f16x8[C::NTQ][C::KS];
-  auto qload = [&](int tt, Qop& qop) {
+  using Qraw = u32x4[C::NTQ][C::KS];
+  // Q rows of the tile at tt (zeros past the block), fetched a round ahead
+  auto qfetch = [&](int tt, Qraw& x) {
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
       const int tok = tt + 16 * nt + l16;
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
-        uint4 x = make_uint4(0, 0, 0, 0);
+        x[nt][ks] = u32x4{0u, 0u, 0u, 0u};
         if (tok < q1)
-          x = *reinterpret_cast<const uint4*>(Q + base + static_cast<size_t>(tok) * D + 32 * ks +
-                                              8 * g);
-        uint4 h;
-        h.x = bf16x2_to_f16x2(x.x); h.y = bf16x2_to_f16x2(x.y);
-        h.z = bf16x2_to_f16x2(x.z); h.w = bf16x2_to_f16x2(x.w);
-        qop[nt][ks] = __builtin_bit_cast(f16x8, h);
+          x[nt][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+              Q + base + static_cast<size_t>(tok) * D + 32 * ks + 8 * g));
       }
     }
   };
-
-  f32x4 acc[C::MV + 1][C::NTQ];
-  float M[C::NTQ], lm[C::NTQ];
-  using SArr = f32x4[4][C::NTQ];
-  // S^T = W' Q^T + c for the chunk in buffer b (rows: chunk features).
-  // (W' operands one 16-feature tile ahead: bounded registers, LDS latency
-  // covered by the previous tile's products)
-  auto proj = [&](int b, const Qop& qop, SArr& S) {
-    const _Float16* w = Wl(b);
-    const float* c = cl(b);
-    f16x8 wa[2][C::KS];
-    auto wload = [&](int mt, f16x8 (&dst)[C::KS]) {
+  auto qconv = [&](const Qraw& x, Qop& qop) {
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt)
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        dst[ks] = *reinterpret_cast<const f16x8*>(&w[(16 * mt + l16) * LS::WROW + 32 * ks + 8 * g]);
-    };
-    wload(0, wa[0]);
+        qop[nt][ks] = __builtin_bit_cast(
+            f16x8, u32x4{bf16x2_to_f16x2(x[nt][ks].x), bf16x2_to_f16x2(x[nt][ks].y),
+                         bf16x2_to_f16x2(x[nt][ks].z), bf16x2_to_f16x2(x[nt][ks].w)});
+  };
+
+  f32x4 acc[C::MV + 1][C::NTQ];
+  float M[C::NTQ];
+  using SArr = f32x4[2][C::NTQ];
+  // S^T = W' Q^T + c for half kb of the chunk in buffer b (rows: features
+  // 32 kb + 16 mh + 4 g + v of the chunk).
+  auto proj = [&](int b, int kb, const Qop& qop, SArr& S) {
+    const _Float16* w = Wl(b);
+    const float* c = cl(b);
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (mt + 1 < 4) wload(mt + 1, wa[(mt + 1) & 1]);
+    for (int mh = 0; mh < 2; ++mh) {
+      const int mt = 2 * kb + mh;
+      f16x8 wa[C::KS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        wa[ks] = *reinterpret_cast<const f16x8*>(&w[(16 * mt + l16) * LS::WROW + 32 * ks + 8 * g]);
       const f32x4 cb = *reinterpret_cast<const f32x4*>(&c[16 * mt + 4 * g]);
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
         for (int nt = 0; nt < C::NTQ; ++nt)
-          S[mt][nt] = mma_f16(wa[mt & 1][ks], qop[nt][ks], ks == 0 ? cb : S[mt][nt]);
-      __builtin_amdgcn_sched_barrier(0);
+          S[mh][nt] = mma_f16(wa[ks], qop[nt][ks], ks == 0 ? cb : S[mh][nt]);
     }
   };
-  auto relative = [&](SArr& S) {
+  // The per-token reference M: the exact maximum of the first half, raised
+  // only when a later half exceeds it by more than kTau (the accumulators
+  // are then rescaled by 2^-raise).
+  auto stabilise = [&](SArr& S, bool first) {
+    float lm[C::NTQ];
     bool raise = false;
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= M[nt];
+        for (int v = 0; v < 4; ++v) S[mh][nt][v] -= M[nt];
       const float a = max3(S[0][nt][0], S[0][nt][1], S[0][nt][2]);
       const float b = max3(S[0][nt][3], S[1][nt][0], S[1][nt][1]);
-      const float c = max3(S[1][nt][2], S[1][nt][3], S[2][nt][0]);
-      const float d = max3(S[2][nt][1], S[2][nt][2], S[2][nt][3]);
-      const float e = max3(S[3][nt][0], S[3][nt][1], S[3][nt][2]);
-      lm[nt] = max3(max3(a, b, c), max3(d, e, S[3][nt][3]), a);
+      lm[nt] = max3(a, b, fmaxf(S[1][nt][2], S[1][nt][3]));
       raise |= lm[nt] > kTau;
     }
-    return __ballot(raise) != 0;
-  };
-  auto rebase = [&](SArr& S, bool first) {
-#pragma unroll
-    for (int nt = 0; nt < C::NTQ; ++nt) {
-      const float cm = colmax4(lm[nt]);
-      const float dlt = (first || cm > kTau) ? cm : 0.f;
-      if (!first) {
-        const float f = fast_exp2(-dlt);
-#pragma unroll
-        for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) S[mt][nt][v] -= dlt;
-      M[nt] += dlt;
-    }
-  };
-  auto apply = [&](int b, const SArr& S) {
-    const uint16_t* kz = Kzl(b);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 qt[C::NTQ];
+    if (first || __builtin_expect(__ballot(raise) != 0, 0)) {
 #pragma unroll
       for (int nt = 0; nt < C::NTQ; ++nt) {
-        uint32_t p[4];
+        const float cm = colmax4(lm[nt]);
+        const float dlt = (first || cm > kTau) ? cm : 0.f;
+        if (!first) {
+          const float f = fast_exp2(-dlt);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          p[q] = pack_bf16(feature<RELU>(S[2 * kb][nt][2 * q]),
-                           feature<RELU>(S[2 * kb][nt][2 * q + 1]));
-          p[2 + q] = pack_bf16(feature<RELU>(S[2 * kb + 1][nt][2 * q]),
-                               feature<RELU>(S[2 * kb + 1][nt][2 * q + 1]));
+          for (int i = 0; i <= C::MV; ++i) acc[i][nt] *= f;
         }
-        qt[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
-      }
 #pragma unroll
-      for (int mv = 0; mv <= C::MV; ++mv) {
-        const int row = 16 * mv + l16, c8 = (4 * kb + g) ^ ((row >> 1) & 7);
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kz[row * 64 + 8 * c8]);
+        for (int mh = 0; mh < 2; ++mh)
 #pragma unroll
-        for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[nt], acc[mv][nt]);
-        if (mv % 3 == 2) __builtin_amdgcn_sched_barrier(0);   // bounded operand lookahead
+          for (int v = 0; v < 4; ++v) S[mh][nt][v] -= dlt;
+        M[nt] += dlt;
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  auto apply = [&](int b, int kb, const SArr& S) {
+    const uint16_t* kz = Kzl(b);
+    bf16x8 qt[C::NTQ];
+#pragma unroll
+    for (int nt = 0; nt < C::NTQ; ++nt) {
+      uint32_t p[4];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        p[q] = pack_bf16(feature<RELU>(S[0][nt][2 * q]), feature<RELU>(S[0][nt][2 * q + 1]));
+        p[2 + q] = pack_bf16(feature<RELU>(S[1][nt][2 * q]), feature<RELU>(S[1][nt][2 * q + 1]));
+      }
+      qt[nt] = __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
+    }
+#pragma unroll
+    for (int mv = 0; mv <= C::MV; ++mv) {
+      const int row = 16 * mv + l16, c8 = (4 * kb + g) ^ ((row >> 1) & 7);
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kz[row * 64 + 8 * c8]);
+#pragma unroll
+      for (int nt = 0; nt < C::NTQ; ++nt) acc[mv][nt] = mma_bf16(ka, qt[nt], acc[mv][nt]);
+    }
+  };
+  // O rows: lanes g and g ^ 1 trade a quarter of two 16-value blocks, so
+  // that each lane stores 16 contiguous bytes and the four lanes of a token
+  // 64 (two blocks); streamed past L2 with the non-temporal hint.
   auto finish = [&](int tt) {
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
       const float den = __shfl(acc[C::MV][nt][0], l16, 64);
       const float inv = 1.0f / den;
       const int tok = tt + 16 * nt + l16;
-      if (tok < q1) {
-        uint16_t* orow = O + base + static_cast<size_t>(tok) * D + 4 * g;
+      const bool odd = (g & 1) != 0;
 #pragma unroll
-        for (int mv = 0; mv < C::MV; ++mv) {
-          uint2 o;
-          o.x = pack_bf16(acc[mv][nt][0] * inv, acc[mv][nt][1] * inv);
-          o.y = pack_bf16(acc[mv][nt][2] * inv, acc[mv][nt][3] * inv);
-          *reinterpret_cast<uint2*>(orow + 16 * mv) = o;
-        }
+      for (int pr = 0; pr < C::MV / 2; ++pr) {
+        const f32x4 x0 = acc[2 * pr][nt], x1 = acc[2 * pr + 1][nt];
+        const u32x2 a0 = u32x2{pack_bf16(x0[0] * inv, x0[1] * inv), pack_bf16(x0[2] * inv, x0[3] * inv)};
+        const u32x2 a1 = u32x2{pack_bf16(x1[0] * inv, x1[1] * inv), pack_bf16(x1[2] * inv, x1[3] * inv)};
+        // even g keeps block 2 pr (values 4 g .. 4 g + 7), odd g block
+        // 2 pr + 1 (values 4 (g - 1) .. 4 g + 3)
+        const u32x2 give = odd ? a0 : a1;
+        const u32x2 got = u32x2{static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.x), 16, 64)),
+                                static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.y), 16, 64))};
+        const u32x4 out = odd ? u32x4{got.x, got.y, a1.x, a1.y} : u32x4{a0.x, a0.y, got.x, got.y};
+        const int col = odd ? 16 * (2 * pr + 1) + 4 * (g - 1) : 16 * (2 * pr) + 4 * g;
+        if (tok < q1)
+          __builtin_nontemporal_store(
+              out, reinterpret_cast<u32x4*>(O + base + static_cast<size_t>(tok) * D + col));
       }
     }
   };
 
   // Every wave runs every round and chunk (tiles past the block compute on
   // zeros and store nothing), so the work-group barriers always match.
+  const int T = nround * NCH;
   stage(0, 0);
-  staged();
-  __syncthreads();
-  int b = 0;
+  if (T > 1) {
+    stage(1 % NCH, 1);
+    staged_but_newest();
+  } else {
+    staged();
+  }
+  lds_barrier();
+  int t = 0;
   Qop qcur;
+  Qraw qraw;
+  qfetch(q0 + wave * C::TQ, qraw);
   for (int r = 0; r < nround; ++r) {
     const int tt = q0 + (r * NW + wave) * C::TQ;
-    qload(tt, qcur);
+    qconv(qraw, qcur);
+    if (r + 1 < nround) qfetch(tt + NW * C::TQ, qraw);
 #pragma unroll
     for (int i = 0; i <= C::MV; ++i)
 #pragma unroll
@@ -1149,24 +1211,20 @@ __global__ __launch_bounds__(NW * 64, 2) void qstream(const uint16_t* __restrict
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) M[nt] = 0.f;
 #pragma unroll 1
-    for (int ch = 0; ch < NCH; ++ch) {
-      const bool more = (ch + 1 < NCH) || (r + 1 < nround);
-      // (the other buffer was last read before the previous barrier)
-      if (more) stage((ch + 1) % NCH, b ^ 1);
-      SArr S;
-      proj(b, qcur, S);
-      if constexpr (!RELU) {
-        if (ch == 0) {
-          relative(S);
-          rebase(S, true);
-        } else if (__builtin_expect(relative(S), 0)) {
-          rebase(S, false);
-        }
+    for (int ch = 0; ch < NCH; ++ch, ++t) {
+      // (buffer (t + 2) % 3 was last read in step t - 1, before its barrier)
+      if (t + 2 < T) stage((t + 2) % NCH, (t + 2) % NBUF);
+      const int b = t % NBUF;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        SArr S;
+        proj(b, kb, qcur, S);
+        if constexpr (!RELU) stabilise(S, ch == 0 && kb == 0);
+        apply(b, kb, S);
       }
-      apply(b, S);
-      staged();
-      __syncthreads();
-      b ^= 1;
+      if (t + 2 < T) staged_but_newest();
+      else staged();
+      lds_barrier();
     }
     finish(tt);
   }
@@ -1210,25 +1268,40 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
     rc = make_float4(sr[D + 1] * kLog2e, sr[(D + 4) + D + 1] * kLog2e,
                      sr[2 * (D + 4) + D + 1] * kLog2e, sr[3 * (D + 4) + D + 1] * kLog2e);
   }
-  for (int s = 0; s < nseg; ++s) {
-    const size_t ci = (static_cast<size_t>(bh) * nseg + s) * m + f;
-    float4* pp = reinterpret_cast<float4*>(P + ((static_cast<size_t>(bh) * nseg + s) * (D + 1) + row) * m + f);
-    const bool put = s > 0 || carry;
-    if (row == 0 && put) *reinterpret_cast<float4*>(cP + ci) = rc;
-    if (s + 1 == nseg) {
-      if (put) *pp = run;
-      break;
+  // Segments in batches of KB: the batch's loads are issued together (the
+  // sum is a chain; its latency is paid once per batch, not per segment).
+  constexpr int KB = 8;
+  auto slot = [&](int s) {
+    return reinterpret_cast<float4*>(P + ((static_cast<size_t>(bh) * nseg + s) * (D + 1) + row) * m + f);
+  };
+  auto cidx = [&](int s) { return (static_cast<size_t>(bh) * nseg + s) * m + f; };
+  for (int s0 = 0; s0 < nseg; s0 += KB) {
+    float4 ts[KB], c[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      // (the last segment's own state is never read)
+      if (s0 + k + 1 < nseg) {
+        ts[k] = *slot(s0 + k);
+        c[k] = *reinterpret_cast<const float4*>(cs + cidx(s0 + k));
+      }
     }
-    const float4 ts = *pp;
-    const float4 c = *reinterpret_cast<const float4*>(cs + ci);
-    if (put) *pp = run;
-    float4 nc;
-    nc.x = fmaxf(rc.x, c.x); nc.y = fmaxf(rc.y, c.y); nc.z = fmaxf(rc.z, c.z); nc.w = fmaxf(rc.w, c.w);
-    run.x = run.x * fast_exp2(rc.x - nc.x) + ts.x * fast_exp2(c.x - nc.x);
-    run.y = run.y * fast_exp2(rc.y - nc.y) + ts.y * fast_exp2(c.y - nc.y);
-    run.z = run.z * fast_exp2(rc.z - nc.z) + ts.z * fast_exp2(c.z - nc.z);
-    run.w = run.w * fast_exp2(rc.w - nc.w) + ts.w * fast_exp2(c.w - nc.w);
-    rc = nc;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int s = s0 + k;
+      if (s >= nseg) break;
+      const bool put = s > 0 || carry;
+      if (row == 0 && put) *reinterpret_cast<float4*>(cP + cidx(s)) = rc;
+      if (put) *slot(s) = run;
+      if (s + 1 == nseg) break;
+      float4 nc;
+      nc.x = fmaxf(rc.x, c[k].x); nc.y = fmaxf(rc.y, c[k].y);
+      nc.z = fmaxf(rc.z, c[k].z); nc.w = fmaxf(rc.w, c[k].w);
+      run.x = run.x * fast_exp2(rc.x - nc.x) + ts[k].x * fast_exp2(c[k].x - nc.x);
+      run.y = run.y * fast_exp2(rc.y - nc.y) + ts[k].y * fast_exp2(c[k].y - nc.y);
+      run.z = run.z * fast_exp2(rc.z - nc.z) + ts[k].z * fast_exp2(c[k].z - nc.z);
+      run.w = run.w * fast_exp2(rc.w - nc.w) + ts[k].w * fast_exp2(c[k].w - nc.w);
+      rc = nc;
+    }
   }
 }
 
@@ -1278,7 +1351,6 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   static_assert(kTT * CROW * 4 >= kTT * KROW * 2, "K~ tile fits the partial-output region");
   __shared__ __align__(16) float ured[NW][kTT * CROW];
   __shared__ __align__(16) float cb[NW][64];                // per-feature references
-  __shared__ __align__(16) float fac[NW][64];               // per-feature rescale factors
   __shared__ __align__(16) float mq[NW][kTT];               // per-wave row references
   uint16_t* const Kt = reinterpret_cast<uint16_t*>(&ured[wave][0]);
 
@@ -1357,6 +1429,8 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       if (u < VUN && tok + 1 < j1) vreg[i][1] = *reinterpret_cast<const uint2*>(V + off + D);
     }
   };
+  // -knorm log2(e), kept in a scalar register
+  const float nk2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(-knorm * kLog2e)));
   auto lstore = [&](int buf, int t) {
     const int jt = j0 + t * kTT;
 #pragma unroll
@@ -1384,7 +1458,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
         h.x = bf16x2_to_f16x2(qv.x); h.y = bf16x2_to_f16x2(qv.y);
         h.z = bf16x2_to_f16x2(qv.z); h.w = bf16x2_to_f16x2(qv.w);
         *reinterpret_cast<uint4*>(&Qs[buf][j][ch * 8]) = h;
-        if (ch == 0) Ns[buf][j] = (jt + j < j1) ? -knorm * kLog2e * ss : -INFINITY;
+        if (ch == 0) Ns[buf][j] = (jt + j < j1) ? nk2 * ss : -INFINITY;
       }
     }
 #pragma unroll
@@ -1452,24 +1526,32 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       raise |= (cref[nt] == -INFINITY) || lm[nt] > kTau;
     }
     if (!RELU && __builtin_expect(__ballot(raise) != 0, 0)) {
+      float fk[NT];   // rescale factor of feature 16 nt + l16 (every g)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const float tm = colmax4(lm[nt]);
         const bool empty = cref[nt] == -INFINITY;
         const float base_c = empty ? 0.f : cref[nt];
         const float dlt = (empty || tm > kTau) ? tm : 0.f;
-        if (g == 0) fac[wave][16 * nt + l16] = empty ? 1.f : fast_exp2(-dlt);
+        fk[nt] = empty ? 1.f : fast_exp2(-dlt);
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) SK[mt][nt][v] -= dlt;
         cref[nt] = base_c + dlt;
       }
-      wave_lds_fence();
-      // The state's rows are features 16 mt + 4 g + v.
+      // The state's rows are features 16 mt + 4 g + v: their factors sit in
+      // lanes 4 g + v.  (The lane index is read here, in this rare branch,
+      // so that no register carries it through the scan.)
+      int ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int src = 16 * ((ln >> 4) & 3);   // byte address of lane 4 g
+      auto from = [&](float x, int v) {
+        return __int_as_float(__builtin_amdgcn_ds_bpermute(src + 4 * v, __float_as_int(x)));
+      };
 #pragma unroll
       for (int mt = 0; mt < NT; ++mt) {
-        const f32x4 fv = *reinterpret_cast<const f32x4*>(&fac[wave][16 * mt + 4 * g]);
+        const f32x4 fv = f32x4{from(fk[mt], 0), from(fk[mt], 1), from(fk[mt], 2), from(fk[mt], 3)};
 #pragma unroll
         for (int tv = 0; tv < TV; ++tv) st[mt][tv] *= fv;
       }
@@ -1727,8 +1809,10 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
     timing_after(st, "qapply");
   } else {
     timing_before(st);
-    qstream<D, 8, NTQ, NCH, RELU><<<dim3(nqb * p.BH), 512, 0, st>>>(Q, W16, Kz, cfin, O, p.L,
-                                                                    p.qblk);
+    constexpr int SNW = FAVOR_QSTREAM_NW, SNTQ = FAVOR_QSTREAM_NTQ;
+    static_assert(SNW * 16 * SNTQ == 256, "a streamed round is 256 tokens (the plan's unit)");
+    qstream<D, SNW, SNTQ, NCH, RELU, FAVOR_QSTREAM_WPE><<<dim3(nqb * p.BH), SNW * 64, 0, st>>>(
+        Q, W16, Kz, cfin, O, p.L, p.qblk);
     e = hipGetLastError();
     timing_after(st, "qstream");
   }
