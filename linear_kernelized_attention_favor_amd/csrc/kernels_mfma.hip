@@ -837,31 +837,21 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
     }
   };
   // O = num / den for one tile; den is row 0 of the last tile (g = 0, v = 0).
-  // O rows: lanes g and g ^ 1 trade a quarter of two 16-value blocks, so
-  // that each lane stores 16 contiguous bytes and the four lanes of a token
-  // 64 (two blocks); streamed past L2 with the non-temporal hint.
   auto finish = [&](int tt) {
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
       const float den = __shfl(acc[C::MV][nt][0], l16, 64);
       const float inv = 1.0f / den;
       const int tok = tt + 16 * nt + l16;
-      const bool odd = (g & 1) != 0;
+      if (tok < q1) {
+        uint16_t* orow = O + base + static_cast<size_t>(tok) * D + 4 * g;
 #pragma unroll
-      for (int pr = 0; pr < C::MV / 2; ++pr) {
-        const f32x4 x0 = acc[2 * pr][nt], x1 = acc[2 * pr + 1][nt];
-        const u32x2 a0 = u32x2{pack_bf16(x0[0] * inv, x0[1] * inv), pack_bf16(x0[2] * inv, x0[3] * inv)};
-        const u32x2 a1 = u32x2{pack_bf16(x1[0] * inv, x1[1] * inv), pack_bf16(x1[2] * inv, x1[3] * inv)};
-        // even g keeps block 2 pr (values 4 g .. 4 g + 7), odd g block
-        // 2 pr + 1 (values 4 (g - 1) .. 4 g + 3)
-        const u32x2 give = odd ? a0 : a1;
-        const u32x2 got = u32x2{static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.x), 16, 64)),
-                                static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.y), 16, 64))};
-        const u32x4 out = odd ? u32x4{got.x, got.y, a1.x, a1.y} : u32x4{a0.x, a0.y, got.x, got.y};
-        const int col = odd ? 16 * (2 * pr + 1) + 4 * (g - 1) : 16 * (2 * pr) + 4 * g;
-        if (tok < q1)
-          __builtin_nontemporal_store(
-              out, reinterpret_cast<u32x4*>(O + base + static_cast<size_t>(tok) * D + col));
+        for (int mv = 0; mv < C::MV; ++mv) {
+          uint2 o;
+          o.x = pack_bf16(acc[mv][nt][0] * inv, acc[mv][nt][1] * inv);
+          o.y = pack_bf16(acc[mv][nt][2] * inv, acc[mv][nt][3] * inv);
+          *reinterpret_cast<uint2*>(orow + 16 * mv) = o;
+        }
       }
     }
   };
