@@ -181,13 +181,15 @@ void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dt
     ns = ns < 1 ? 1 : (ns > maxs ? maxs : ns);
     p->seg = ((L + ns - 1) / ns + 31) / 32 * 32;
     p->nseg = (L + p->seg - 1) / p->seg;
-    // Query blocks: about 512 work-groups of 4 waves (qapply) or 256 of 8
-    // (qstream, one per compute unit); a multiple of 64 (256) tokens.
+    // Query blocks: about 512 work-groups of 4 waves (qapply) or 256, one
+    // per compute unit (qstream); a multiple of 64 tokens (qapply) or of
+    // qstream's lockstep round.
     const bool stream = mfma_bidir_streams_queries(d, m);
-    const int64_t nwg = stream ? 256 : mfma_bidir_query_workgroups(), unit = stream ? 256 : 64;
+    const int64_t nwg = stream ? 256 : mfma_bidir_query_workgroups();
+    const int64_t unit = stream ? mfma_bidir_stream_round() : 64;
     const int64_t want = (static_cast<int64_t>(L) * p->BH + nwg - 1) / nwg;
     int64_t qb = (want + unit - 1) / unit * unit;
-    if (qb < 256) qb = 256;
+    if (qb < 256) qb = stream ? unit : 256;
     p->qblk = static_cast<int32_t>(qb);
     p->off_T = off;    off = align256(off + BH * p->nseg * ncol * m * sizeof(float));
     p->off_cseg = off; off = align256(off + BH * p->nseg * m * sizeof(float));

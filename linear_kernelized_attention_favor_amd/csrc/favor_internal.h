@@ -156,6 +156,7 @@ int mfma_bidir_token_groups(int32_t d, int32_t m);
 int mfma_bidir_feature_blocks(int32_t d, int32_t m);
 bool mfma_bidir_streams_queries(int32_t d, int32_t m);
 int mfma_bidir_query_workgroups();   // query-side work-groups the plan aims for (qapply)
+int mfma_bidir_stream_round();       // tokens per lockstep round of qstream
 hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                               const float* W, void* O, void* ws, hipStream_t stream);
 

@@ -82,13 +82,13 @@ constexpr float kQBias = 20.0f;
 #define FAVOR_QAPPLY_WGS 512    // query-side work-groups per call the plan aims for
 #endif
 #ifndef FAVOR_QSTREAM_NW
-#define FAVOR_QSTREAM_NW 8      // waves per streamed query-side work-group
+#define FAVOR_QSTREAM_NW 12     // waves per streamed query-side work-group
 #endif
 #ifndef FAVOR_QSTREAM_NTQ
 #define FAVOR_QSTREAM_NTQ 2     // 16-token tiles per streamed query-side wave
 #endif
 #ifndef FAVOR_QSTREAM_WPE
-#define FAVOR_QSTREAM_WPE 2     // streamed query-side waves per SIMD
+#define FAVOR_QSTREAM_WPE 3     // streamed query-side waves per SIMD
 #endif
 constexpr int kTT = 32;        // tokens per key tile
 
@@ -953,7 +953,10 @@ __global__ __launch_bounds__(NW * 64, FAVOR_QAPPLY_WPE) void qapply(const uint16
 // traffic per token falls as 1/NTQ; NTQ = 4 needs one wave per SIMD
 // (WPE = 1, accumulators in the AGPRs), which at d = 128, m = 512 measured
 // slower than eight waves of NTQ = 2 (1128 against 922 us): a lone wave
-// leaves the latency of its exponentials and LDS reads exposed.  Q and O
+// leaves the latency of its exponentials and LDS reads exposed.  The other
+// way pays: twelve waves of NTQ = 2, three per SIMD (at most 168 registers,
+// so a wave fetches its Q tile at the start of the round instead of one
+// round ahead), measured 3% faster than eight.  Q and O
 // pass with the non-temporal hint (once each; the chunks, re-read every
 // round, stay in L2), O in 64-byte row pieces (finish): stored 8 bytes per
 // lane, plainly the lines cost a fill read each (fetch up by the output's
@@ -1149,13 +1152,19 @@ __global__ __launch_bounds__(NW * 64, WPE) void qstream(const uint16_t* __restri
   // O rows: lanes g and g ^ 1 trade a quarter of two 16-value blocks, so
   // that each lane stores 16 contiguous bytes and the four lanes of a token
   // 64 (two blocks); streamed past L2 with the non-temporal hint.
+  const __amdgpu_buffer_rsrc_t ro = buffer_rsrc(O + base, q1 * D * 2);
   auto finish = [&](int tt) {
+    // (the lane's group, read here: its column offsets are not worth a
+    // register through the round)
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int gq = (ln >> 4) & 3;
+    const bool odd = (gq & 1) != 0;
 #pragma unroll
     for (int nt = 0; nt < C::NTQ; ++nt) {
       const float den = __shfl(acc[C::MV][nt][0], l16, 64);
       const float inv = 1.0f / den;
       const int tok = tt + 16 * nt + l16;
-      const bool odd = (g & 1) != 0;
 #pragma unroll
       for (int pr = 0; pr < C::MV / 2; ++pr) {
         const f32x4 x0 = acc[2 * pr][nt], x1 = acc[2 * pr + 1][nt];
@@ -1167,10 +1176,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void qstream(const uint16_t* __restri
         const u32x2 got = u32x2{static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.x), 16, 64)),
                                 static_cast<uint32_t>(__shfl_xor(static_cast<int>(give.y), 16, 64))};
         const u32x4 out = odd ? u32x4{got.x, got.y, a1.x, a1.y} : u32x4{a0.x, a0.y, got.x, got.y};
-        const int col = odd ? 16 * (2 * pr + 1) + 4 * (g - 1) : 16 * (2 * pr) + 4 * g;
-        if (tok < q1)
-          __builtin_nontemporal_store(
-              out, reinterpret_cast<u32x4*>(O + base + static_cast<size_t>(tok) * D + col));
+        const int col = odd ? 16 * (2 * pr + 1) + 4 * (gq - 1) : 16 * (2 * pr) + 4 * gq;
+        // (a buffer store past the head's last token is dropped; cache
+        // policy 2: non-temporal)
+        __builtin_amdgcn_raw_buffer_store_b128(out, ro, (tok * D + col) * 2, 0, 2);
       }
     }
   };
@@ -1188,12 +1197,20 @@ __global__ __launch_bounds__(NW * 64, WPE) void qstream(const uint16_t* __restri
   lds_barrier();
   int t = 0;
   Qop qcur;
+  // (with three waves per SIMD the registers do not hold a second tile:
+  // the round's tile is fetched at its start)
+  constexpr bool QPF = WPE <= 2;
   Qraw qraw;
-  qfetch(q0 + wave * C::TQ, qraw);
+  if constexpr (QPF) qfetch(q0 + wave * C::TQ, qraw);
   for (int r = 0; r < nround; ++r) {
     const int tt = q0 + (r * NW + wave) * C::TQ;
-    qconv(qraw, qcur);
-    if (r + 1 < nround) qfetch(tt + NW * C::TQ, qraw);
+    if constexpr (QPF) {
+      qconv(qraw, qcur);
+      if (r + 1 < nround) qfetch(tt + NW * C::TQ, qraw);
+    } else {
+      qfetch(tt, qraw);
+      qconv(qraw, qcur);
+    }
 #pragma unroll
     for (int i = 0; i <= C::MV; ++i)
 #pragma unroll
@@ -1800,7 +1817,6 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
   } else {
     timing_before(st);
     constexpr int SNW = FAVOR_QSTREAM_NW, SNTQ = FAVOR_QSTREAM_NTQ;
-    static_assert(SNW * 16 * SNTQ == 256, "a streamed round is 256 tokens (the plan's unit)");
     qstream<D, SNW, SNTQ, NCH, RELU, FAVOR_QSTREAM_WPE><<<dim3(nqb * p.BH), SNW * 64, 0, st>>>(
         Q, W16, Kz, cfin, O, p.L, p.qblk);
     e = hipGetLastError();
@@ -1961,6 +1977,8 @@ bool mfma_bidir_supported(int32_t d, int32_t m, int32_t dtype) {
 }
 
 int mfma_bidir_query_workgroups() { return FAVOR_QAPPLY_WGS; }
+
+int mfma_bidir_stream_round() { return FAVOR_QSTREAM_NW * 16 * FAVOR_QSTREAM_NTQ; }
 
 bool mfma_bidir_streams_queries(int32_t d, int32_t m) {
   return (d == 64 ? qapply_lds_bytes<64>(m) : qapply_lds_bytes<128>(m)) > 160 * 1024;
