@@ -159,6 +159,32 @@ def test_decode_from_an_empty_state(fv, kernel):
     assert oracle.row_rel_err(_np64(o), _np64(got)) <= TOL["f32"]
 
 
+# Decode steps after a prefill across the head shapes (one head with
+# m = 1024; d = 128; d = 16; 256 heads): every step's output against the
+# oracle and the state after the last step.
+DECODE_SHAPES = [(1, 1, 64, 1024), (1, 2, 128, 512), (2, 3, 16, 64), (4, 64, 32, 128)]
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("bhdm", DECODE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_head_shapes(fv, bhdm, kernel):
+    B, H, d, m = bhdm
+    L0, L = 20, 26
+    shape = (B, H, L, d, m)
+    q, k, v, W = _case(shape, "f32", B * H + d + m)
+    Wd = torch.from_numpy(W).cuda()
+    qc, kc, vc = q.cuda(), k.cuda(), v.cuda()
+    print(f"decode B{B} H{H} d{d} m{m} {kernel}", flush=True)
+    _, st = fv.prefill(qc[:, :, :L0].contiguous(), kc[:, :, :L0].contiguous(),
+                       vc[:, :, :L0].contiguous(), Wd, kernel=kernel)
+    outs = [fv.decode(qc[:, :, t].contiguous(), kc[:, :, t].contiguous(), vc[:, :, t].contiguous(),
+                      Wd, st, kernel=kernel) for t in range(L0, L)]
+    torch.cuda.synchronize()
+    ref = _ref_out(q, k, v, W, kernel)[:, :, L0:]
+    assert oracle.row_rel_err(_np64(torch.stack(outs, 2)), ref) <= TOL["f32"]
+    assert _state_err(st, k, v, W, kernel) <= 1e-4
+
+
 def test_state_reset_layout(fv):
     st = torch.full((2, 3, 48, 20), 7.0, device="cuda")     # d = 16
     fv.state_reset(st)
