@@ -160,9 +160,11 @@ def test_decode_from_an_empty_state(fv, kernel):
 
 
 # Decode steps after a prefill across the head shapes (one head with
-# m = 1024; d = 128; d = 16; 256 heads): every step's output against the
-# oracle and the state after the last step.
-DECODE_SHAPES = [(1, 1, 64, 1024), (1, 2, 128, 512), (2, 3, 16, 64), (4, 64, 32, 128)]
+# m = 1024; d = 128; d = 16 with m = 64 and 256; 256 heads; m = 208): every
+# step's output against the oracle, the state after the last step, and the
+# state's two pad columns still zero.
+DECODE_SHAPES = [(1, 1, 64, 1024), (1, 2, 128, 512), (2, 3, 16, 64), (4, 64, 32, 128),
+                 (1, 2, 16, 256), (2, 2, 64, 208)]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -183,6 +185,7 @@ def test_decode_head_shapes(fv, bhdm, kernel):
     ref = _ref_out(q, k, v, W, kernel)[:, :, L0:]
     assert oracle.row_rel_err(_np64(torch.stack(outs, 2)), ref) <= TOL["f32"]
     assert _state_err(st, k, v, W, kernel) <= 1e-4
+    assert torch.all(st[..., d + 2:] == 0)
 
 
 def test_state_reset_layout(fv):
