@@ -177,7 +177,7 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int, backward: bool = F
     if w.causal:
         # The causal scan reads Q, K, V and writes O and does both projections
         # and both contractions: the whole path's algorithmic work.  The
-        # segment-state pass before it (kpart, g_state) re-reads K and V and
+        # segment-state pass before it (ckey, kpart, g_state) re-reads K and V and
         # recomputes the key side: overhead, credited nothing, so that the
         # kernels' bytes sum to 4 d elements per token*head.
         if name in ("cscan", "g_apply"):
@@ -291,7 +291,7 @@ def copy_calibration(steps: int):
                       "GB_s": round(8 * COPY_ELEMS / ms / 1e6, 1)}), flush=True)
 
 
-FAVOR_KERNELS = ("fprep", "fused", "kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "g_state",
+FAVOR_KERNELS = ("fprep", "fused", "ckey", "kpart", "kcombine", "qapply", "qstream", "kprefix", "cscan", "g_state",
                  "g_combine", "g_apply", "gb_query", "gb_gstate", "gb_gcombine", "gb_key",
                  "bprep", "bcombine", "bqr", "gcombine", "bkeyr", "sexport", "g_decode",
                  "g_state_reset", "draw_block", "g_feature_map", "cbq", "cbg", "cbsuffix")

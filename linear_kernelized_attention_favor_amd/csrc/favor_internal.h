@@ -164,6 +164,12 @@ hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const
 bool fused_bidir_supported(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype);
 // Splits (seg, nseg) and query blocks (qblk) for `cus` compute units.
 void fused_bidir_layout(Plan* p, int cus);
+// The causal form's segment key states (every segment but the last) in the
+// layout of T and cseg, for d = 64, m = 256, bf16 inputs, softmax or
+// Gaussian features.
+bool fused_causal_keys_supported(int32_t d, int32_t m, int32_t dtype, int32_t relu);
+hipError_t fused_causal_key_states(const Plan& p, const void* K, const void* V, const float* W,
+                                   float* T, float* cs, hipStream_t st);
 hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                                const float* W, void* O, void* ws, hipStream_t stream);
 

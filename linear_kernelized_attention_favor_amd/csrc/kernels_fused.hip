@@ -164,6 +164,7 @@ struct Args {
   const uint16_t* K;
   const uint16_t* V;
   const _Float16* W16;
+  const float* W32;  // the causal key kernel: W fp32, converted on load
   uint16_t* O;
   float* T;          // [BH][nsplit][65][256] partial states, fp32
   float* cs;         // [BH][nsplit][256] their per-feature references
@@ -241,27 +242,48 @@ __device__ inline float rescale(float c, float cn) {
 // read).  Step i converts tile i + 2, projects tile i + 1 and contracts tile
 // i.
 // ---------------------------------------------------------------------------
-template <bool RELU, bool SLOW>
+//
+// SEP: the two token groups take separate ranges instead (the caller passes
+// each group its own [t0, t1), possibly empty), every tile of its range in
+// order, both for ceil(nmax / 32) steps (a shorter range runs dead tiles);
+// W' is converted from the fp32 W (a.W32) as it is loaded.
+template <bool RELU, bool SLOW, bool SEP = false>
 __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
-                                         f32x4 (&acc)[5][4], float (&cref)[4]) {
+                                         f32x4 (&acc)[5][4], float (&cref)[4], int nmax = 0) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uni(tid >> 6), tg = wave / NFW, fw = wave % NFW;
   const int l16 = lane & 15, g = lane >> 4;
   unsigned char* const ring = g_smem + tg * NSLOT * SLOT_BYTES;
   const int n = t1 - t0;
   const int ntl = (n + FTT - 1) / FTT;      // tiles of the split
-  const int nsteps = (ntl + NTG - 1) / NTG; // tiles per group (group 1 may run one dead tile)
+  // tiles per group (interleaved: group 1 may run one dead tile)
+  const int nsteps = SEP ? (nmax + FTT - 1) / FTT : (ntl + NTG - 1) / NTG;
   const size_t base = (static_cast<size_t>(bh) * a.L + t0) * FD;
   const __amdgpu_buffer_rsrc_t rsrc_kv = buffer_rsrc((fw < 2 ? a.K : a.V) + base, n * FD * 2);
   const float nscale = -(a.knorm * kLog2e);
+  // first token of the group's tile i, relative to t0
+  auto tile_base = [&](int i) { return SEP ? i * FTT : (NTG * i + tg) * FTT; };
 
   f16x8 wb[4][2];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      wb[nt][ks] = *reinterpret_cast<const f16x8*>(a.W16 + (64 * fw + 16 * nt + l16) * WROW +
-                                                   32 * ks + 8 * g);
+    for (int ks = 0; ks < 2; ++ks) {
+      if constexpr (SEP) {
+        const float* wr = a.W32 + (64 * fw + 16 * nt + l16) * FD + 32 * ks + 8 * g;
+        const float4 x = *reinterpret_cast<const float4*>(wr);
+        const float4 y = *reinterpret_cast<const float4*>(wr + 4);
+        f16x8 h;
+        h[0] = static_cast<_Float16>(x.x * kLog2e); h[1] = static_cast<_Float16>(x.y * kLog2e);
+        h[2] = static_cast<_Float16>(x.z * kLog2e); h[3] = static_cast<_Float16>(x.w * kLog2e);
+        h[4] = static_cast<_Float16>(y.x * kLog2e); h[5] = static_cast<_Float16>(y.y * kLog2e);
+        h[6] = static_cast<_Float16>(y.z * kLog2e); h[7] = static_cast<_Float16>(y.w * kLog2e);
+        wb[nt][ks] = h;
+      } else {
+        wb[nt][ks] = *reinterpret_cast<const f16x8*>(a.W16 + (64 * fw + 16 * nt + l16) * WROW +
+                                                     32 * ks + 8 * g);
+      }
+    }
 #pragma unroll
   for (int i = 0; i < 5; ++i)
 #pragma unroll
@@ -287,7 +309,7 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
   // and 256..511 the V rows; unit u of a row holds the row's global unit
   // (u % 8) ^ (row % 8).  Rows past the split read zero.
   auto dma_part = [&](auto R, int i, int j) {
-    const int tb = (NTG * i + tg) * FTT;
+    const int tb = tile_base(i);
     const int uu = (128 * fw + 64 * j + lane) & 255, row = uu >> 3, gu = (uu & 7) ^ (row & 7);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rsrc_kv, (lds_ptr)(ring + soff(R) + 16 * (128 * fw + 64 * j)), 16,
@@ -314,7 +336,7 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
                                          __builtin_bit_cast(bf16x2, w3), ss, false);
     ss = group_sum<8>(ss);
     *p = u32x4{bf16x2_to_f16x2(w0), bf16x2_to_f16x2(w1), bf16x2_to_f16x2(w2), bf16x2_to_f16x2(w3)};
-    const int tb = (NTG * i + tg) * FTT;
+    const int tb = tile_base(i);
     if ((lane & 7) == 0) *lds_at<float>(cvt_nb + off) = tb + crow < n ? nscale * ss : -INFINITY;
   };
   // Operand addresses of the projection (token 16 mt + l16, dims 32 ks +
@@ -546,7 +568,7 @@ __device__ __forceinline__ void key_pass(const Args& a, int bh, int t0, int t1,
   // (the DMAs issued past the group's last tile land before the LDS is reused)
   vm_drain();
   // A group that saw no token carries no reference.
-  if (tg >= ntl) {
+  if (SEP ? ntl == 0 : tg >= ntl) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) cref[nt] = -INFINITY;
   }
@@ -1085,6 +1107,73 @@ __global__ __launch_bounds__(FNT, 1) void fused(Args a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// ckey: the key states of the causal form's segments (every segment but the
+// last; the prefix-sum form needs, for each segment, the sum over the keys
+// of the segments before it).  Work-group (head bh, pair pr) takes segments
+// 2 pr and 2 pr + 1, one per token group, each group over its own segment
+// with the key pass above: a group's sums are its segment's state, so no
+// merge.  The state [(K')^T V | (K')^T 1] of segment s goes to
+// T[bh][s][65][256] in fp32 with its per-feature references in
+// cs[bh][s][256] (log2 units), the layout the prefix kernel reads.  A group
+// whose sums are not finite, or whose ones-column sum fell below 2^-100,
+// makes the work-group redo both segments with per-feature references.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(FNT, 1) void ckey(Args a, int npair, int nneed) {
+  unsigned* const bc = bcast();
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6), tg = wave / NFW, fw = wave % NFW;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int bh = blockIdx.x / npair, pr = blockIdx.x - bh * npair;
+  const int s = 2 * pr + tg;
+  const bool has = s < nneed;
+  const int t0 = has ? s * a.seg : 0, t1 = has ? min(a.L, t0 + a.seg) : 0;
+  f32x4 acc[5][4];
+  float cref[4];
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) key_pass<false, true, true>(a, bh, t0, t1, acc, cref, a.seg);
+    else key_pass<false, false, true>(a, bh, t0, t1, acc, cref, a.seg);
+    if (pass == 1) break;
+    bool bad = false;
+    if (has) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) bad |= !__builtin_isfinite(acc[i][nt][v]);
+      if (g == 0) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) bad |= !(acc[4][nt][0] >= 0x1p-100f);
+      }
+    }
+    // (the barriers also order every wave's last ring reads before a redo's
+    // first DMAs)
+    if (tid == 0) bc[0] = 0u;
+    lds_barrier();
+    if (bad) bc[0] = 1u;
+    lds_barrier();
+    if (bc[0] == 0u) break;
+  }
+  if (!has) return;
+  const size_t item = static_cast<size_t>(bh) * a.nsplit + s;
+  float* const T = a.T + item * PROWS * FM;
+#pragma unroll
+  for (int mv = 0; mv < 5; ++mv)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = 16 * mv + 4 * g + v;
+      if (row < PROWS) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) T[row * FM + 64 * fw + 16 * nt + l16] = acc[mv][nt][v];
+      }
+    }
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) a.cs[item * FM + 64 * fw + 16 * nt + l16] = cref[nt];
+  }
+}
+
 }  // namespace
 
 bool fused_bidir_supported(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype) {
@@ -1148,6 +1237,33 @@ hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, cons
     fused<false><<<dim3(grid), FNT, 0, st>>>(a);
   e = hipGetLastError();
   timing_after(st, "fused");
+  return e;
+}
+
+bool fused_causal_keys_supported(int32_t d, int32_t m, int32_t dtype, int32_t relu) {
+  return d == FD && m == FM && dtype == FAVOR_BF16 && !relu;
+}
+
+hipError_t fused_causal_key_states(const Plan& p, const void* K, const void* V, const float* W,
+                                   float* T, float* cs, hipStream_t st) {
+  const int nneed = p.nseg - 1;
+  if (nneed < 1) return hipSuccess;
+  Args a{};
+  a.K = static_cast<const uint16_t*>(K);
+  a.V = static_cast<const uint16_t*>(V);
+  a.W32 = W;
+  a.T = T;
+  a.cs = cs;
+  a.L = p.L;
+  a.BH = p.BH;
+  a.nsplit = p.nseg;
+  a.seg = p.seg;
+  a.knorm = p.knorm;
+  const int npair = (nneed + 1) / 2;
+  timing_before(st);
+  ckey<<<dim3(p.BH * npair), FNT, 0, st>>>(a, npair, nneed);
+  const hipError_t e = hipGetLastError();
+  timing_after(st, "ckey");
   return e;
 }
 

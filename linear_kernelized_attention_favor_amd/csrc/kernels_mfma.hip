@@ -1833,7 +1833,12 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
   float* cs = reinterpret_cast<float*>(ws + p.off_cseg);
   float* cP = reinterpret_cast<float*>(ws + p.off_cP);
   hipError_t e;
-  if (p.nseg > 1) {
+  if (p.nseg > 1 && !RELU && NW == 4) {
+    // Key states of every segment but the last, two segments per work-group
+    // (m = 256, softmax and Gaussian features).
+    e = fused_causal_key_states(p, K, V, W, P, cs, st);
+    if (e != hipSuccess) return e;
+  } else if (p.nseg > 1) {
     // Key states of every segment but the last (grid nseg - 1; the layout
     // keeps nseg slots per head).
     timing_before(st);

@@ -69,7 +69,7 @@ def test_forward_work_model_sums_to_the_call_totals(name, causal):
     # segment-state pass that re-reads K and V is credited nothing).
     w = workloads.workload(name).with_(causal=causal)
     th = w.heads * w.L
-    names = (("kpart", "kprefix", "cscan") if causal else ("kpart", "kcombine", "qapply"))
+    names = (("ckey", "kprefix", "cscan") if causal else ("kpart", "kcombine", "qapply"))
     if name == "wide_many":
         names = ("kpart", "kcombine", "qstream")
     if name == "text_bidir":

@@ -326,6 +326,29 @@ def test_stabiliser_large_offsets(fv):
             assert err <= tol, (causal, dt, err)
 
 
+def test_causal_segment_states_redone_with_references(fv):
+    # Every key at norm 30: each key exponent w.k - |k|^2/2 lies near -450
+    # (natural units), so without references every feature of a segment
+    # underflows and its ones-column sum is zero.  The segment-state kernel
+    # must then redo the segment with per-feature references.  All keys share
+    # the norm, so the |k|^2 term cancels in D^-1 and the output is an
+    # ordinary attention that the oracle holds in fp64.  L = 1300 at two heads
+    # gives six 224-token segments: five segment states, the last pair of
+    # segments with one empty token group.
+    B, H, L, d, m = 1, 2, 1300, 64, 256
+    rng = np.random.default_rng(77)
+    u = rng.standard_normal((B, H, L, d))
+    k = 30.0 * u / np.linalg.norm(u, axis=-1, keepdims=True)
+    q = rng.standard_normal((B, H, L, d)) * d ** -0.25
+    v = rng.standard_normal((B, H, L, d))
+    qt, kt, vt = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16) for x in (q, k, v))
+    W = _w(77, m, d)
+    out = _np64(_run(fv, True, qt, kt, vt, W))
+    err = oracle.row_rel_err(out, _ref(True, qt, kt, vt, W))
+    print(f"norm-30 keys causal: {err:.3e}", flush=True)
+    assert np.isfinite(out).all() and err <= TOL["bf16"], err
+
+
 def test_redraw_changes_output_consistently(fv):
     # Redrawing W (a new seed, uploaded between calls on the same buffers)
     # gives the oracle's result for each W.
@@ -345,7 +368,7 @@ def test_kernel_timing_records_each_launch(fv):
     Wd = torch.from_numpy(_w(w.seed_w, w.m, w.d)).cuda()
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     for causal, names in ((False, {"kpart", "kcombine", "qapply"}),
-                          (True, {"kpart", "kprefix", "cscan"})):
+                          (True, {"ckey", "kprefix", "cscan"})):
         fwd = fv.fwd_causal if causal else fv.fwd_bidir
         fwd(qd, kd, vd, Wd)
         torch.cuda.synchronize()
