@@ -103,8 +103,9 @@ enum favor_status {
  * favor_fwd_causal (causal = 1) needs for this shape; written to *bytes.
  * The workspace holds the key-side state [(K')^T V | (K')^T 1_L] (m x (d+1)
  * fp32 per head, per sequence split or segment) and its per-feature exponent
- * references.  Returns FAVOR_OK or a validation error (bytes untouched).
- * Pure host function: no HIP call.
+ * references.  The size covers every attention kernel (favor_fwd_attn may
+ * take another path for FAVOR_RELU than for the others).  Returns FAVOR_OK
+ * or a validation error (bytes untouched).  Pure host function: no HIP call.
  */
 int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
                           int32_t dtype, int32_t causal, size_t* bytes);
@@ -113,7 +114,8 @@ int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
  * The execution plan a forward call with these arguments would use:
  * *path = 0 (fp32 FMA kernels), 1 (bf16 matrix-core kernels) or 2 (bf16
  * matrix-core kernels, the bidirectional form in one persistent launch after
- * a small preparation launch: d = 64, m = 256, at least 64 heads); *nseg and
+ * a small preparation launch: d = 64, m = 256, at least 64 heads, softmax and
+ * Gaussian features; FAVOR_RELU features take path 1 there); *nseg and
  * *seg = the number of sequence splits (bidirectional) or segments (causal)
  * per head and their length in tokens.  Pure host function: no HIP call.
  * Returns FAVOR_OK, a validation error or FAVOR_ERR_NULL.

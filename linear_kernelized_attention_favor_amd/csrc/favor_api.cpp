@@ -114,8 +114,11 @@ int forward_call(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t 
   if (!is_aligned(Q, 16) || !is_aligned(K, 16) || !is_aligned(V, 16) || !is_aligned(W, 16) ||
       !is_aligned(O, 16) || !is_aligned(ws, 256))
     return FAVOR_ERR_ALIGN;
+  // The ReLU features take the three-kernel matrix-core path where the
+  // persistent kernel would otherwise run: its ReLU form needs more
+  // registers than a wave has in the key loop.
   Plan p;
-  make_plan(B, H, L, d, m, dtype, causal, &p, true);
+  make_plan(B, H, L, d, m, dtype, causal, &p, true, attn_kernel != FAVOR_RELU);
   if (ws_bytes < p.bytes) return FAVOR_ERR_WORKSPACE;
   p.knorm = knorm;
   p.relu = attn_kernel == FAVOR_RELU ? 1 : 0;
@@ -150,14 +153,14 @@ int record_hip_error(hipError_t e) {
 }
 
 void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
-               int32_t causal, Plan* p, bool forward) {
+               int32_t causal, Plan* p, bool forward, bool allow_fused) {
   std::memset(p, 0, sizeof(*p));
   p->B = B; p->H = H; p->L = L; p->d = d; p->m = m; p->dtype = dtype; p->causal = causal;
   p->BH = B * H;
   const size_t ncol = static_cast<size_t>(d) + 1;
   const size_t BH = static_cast<size_t>(p->BH);
   size_t off = 0;
-  if (forward && !causal && fused_bidir_supported(B, H, L, d, m, dtype)) {
+  if (forward && !causal && allow_fused && fused_bidir_supported(B, H, L, d, m, dtype)) {
     p->path = kPathFused;
     fused_bidir_layout(p, kPlanCUs);
     const size_t ns = static_cast<size_t>(p->nseg);
@@ -309,6 +312,11 @@ int favor_workspace_bytes(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m,
   favor::Plan p;
   favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p, true);
   *bytes = p.bytes;
+  if (p.path == favor::kPathFused) {
+    // enough for the path the ReLU features take as well
+    favor::make_plan(B, H, L, d, m, dtype, causal ? 1 : 0, &p, true, false);
+    if (p.bytes > *bytes) *bytes = p.bytes;
+  }
   return FAVOR_OK;
 }
 

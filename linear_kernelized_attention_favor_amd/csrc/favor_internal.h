@@ -64,7 +64,7 @@ struct Plan {
 // bidirectional path); other users (backward, prefill) get the
 // three-kernel layout of the key partials.
 void make_plan(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype,
-               int32_t causal, Plan* p, bool forward = false);
+               int32_t causal, Plan* p, bool forward = false, bool allow_fused = true);
 // Compute units the plans are laid out for (an MI355X has 256; the fused
 // kernel's grid is the device's own count, its work queue adapts).
 constexpr int kPlanCUs = 256;

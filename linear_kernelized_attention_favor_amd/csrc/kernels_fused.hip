@@ -1230,11 +1230,11 @@ hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, cons
   if (e != hipSuccess) return e;
   const int items = a.BH * (a.nsplit + a.nqb);
   const int grid = cus < items ? cus : items;
+  // (the ReLU features take the three-kernel path: this kernel's ReLU form
+  // spills in its key loop)
+  if (p.relu) return hipErrorInvalidValue;
   timing_before(st);
-  if (p.relu)
-    fused<true><<<dim3(grid), FNT, 0, st>>>(a);
-  else
-    fused<false><<<dim3(grid), FNT, 0, st>>>(a);
+  fused<false><<<dim3(grid), FNT, 0, st>>>(a);
   e = hipGetLastError();
   timing_after(st, "fused");
   return e;

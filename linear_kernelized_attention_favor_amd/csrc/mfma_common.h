@@ -67,9 +67,13 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // features of the softmax and Gaussian kernels, max(s, 0) for the ReLU
 // features of generalized attention (no reference needed: they cannot
 // overflow, and a constant factor on every feature cancels).
+// max(s, 0) is taken on the bits as a signed integer maximum: every
+// negative float (and -0, -inf) is a negative integer, every positive one a
+// positive integer of the same order, so one v_max_i32 does it (fmaxf on a
+// matrix-instruction result costs a canonicalising max as well).
 template <bool RELU>
 __device__ inline float feature(float s) {
-  if constexpr (RELU) return fmaxf(s, 0.f);
+  if constexpr (RELU) return __int_as_float(max(__float_as_int(s), 0));
   else return fast_exp2(s);
 }
 

@@ -99,6 +99,8 @@ def test_fused_shapes(fv, shape):
     _check(fv, q, k, v, _w(11 + L), label="shape")
 
 
+# (The ReLU features take the three-kernel matrix-core path at these shapes:
+# the same calls check it there.)
 @pytest.mark.parametrize("kernel", ["gaussian", "relu"])
 def test_fused_other_kernels(fv, kernel):
     q, k, v = _bf16(*_inputs(1, 64, 1000, 5))
