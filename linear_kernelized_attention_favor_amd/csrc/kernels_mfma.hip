@@ -1351,6 +1351,8 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   __shared__ __align__(16) _Float16 Qs[2][kTT][KROW];
   __shared__ __align__(16) uint32_t Vt[2][D][kTT / 2 + 4];
   __shared__ __align__(16) float Ns[2][kTT];
+  __shared__ __align__(16) float Nq[2][kTT];   // fast pass: -|q|^2 log2(e) / 2 per query
+  __shared__ unsigned vote;
   // Per wave, one region holds first this chunk's K~ over the wave's features
   // (key rows; read only by the wave itself) and then the wave's partial
   // outputs [query][column], columns 0..D-1 the numerator, D the
@@ -1384,26 +1386,29 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   // yet).
   f32x4 st[NT][TV];
   float cref[NT];
-#pragma unroll
-  for (int mt = 0; mt < NT; ++mt) {
-    cref[mt] = -INFINITY;
-#pragma unroll
-    for (int tv = 0; tv < TV; ++tv) st[mt][tv] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  if (s > 0 || carry0) {
-    const size_t pbase = (static_cast<size_t>(bh) * nseg + s) * (D + 1);
-    const size_t cbase = (static_cast<size_t>(bh) * nseg + s) * m;
+  auto carry_in = [&]() {
 #pragma unroll
     for (int mt = 0; mt < NT; ++mt) {
-      const int f = f0 + 16 * mt + 4 * g;
+      cref[mt] = -INFINITY;
 #pragma unroll
-      for (int tv = 0; tv < TV; ++tv) {
-        const int col = 16 * tv + l16;
-        if (col <= D) st[mt][tv] = *reinterpret_cast<const f32x4*>(P + (pbase + col) * m + f);
-      }
-      cref[mt] = cP[cbase + f0 + 16 * mt + l16];   // this lane's feature (S layout)
+      for (int tv = 0; tv < TV; ++tv) st[mt][tv] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-  }
+    if (s > 0 || carry0) {
+      const size_t pbase = (static_cast<size_t>(bh) * nseg + s) * (D + 1);
+      const size_t cbase = (static_cast<size_t>(bh) * nseg + s) * m;
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) {
+        const int f = f0 + 16 * mt + 4 * g;
+#pragma unroll
+        for (int tv = 0; tv < TV; ++tv) {
+          const int col = 16 * tv + l16;
+          if (col <= D) st[mt][tv] = *reinterpret_cast<const f32x4*>(P + (pbase + col) * m + f);
+        }
+        cref[mt] = cP[cbase + f0 + 16 * mt + l16];   // this lane's feature (S layout)
+      }
+    }
+  };
+  carry_in();
 
   const int j0 = s * SEG, j1 = min(L, j0 + SEG);
   const int nch = (j1 - j0 + kTT - 1) / kTT;
@@ -1438,7 +1443,8 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
   };
   // -knorm log2(e), kept in a scalar register
   const float nk2 = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(-knorm * kLog2e)));
-  auto lstore = [&](int buf, int t) {
+  auto lstore = [&](auto FASTC, int buf, int t) {
+    constexpr bool F = decltype(FASTC)::value;
     const int jt = j0 + t * kTT;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -1456,11 +1462,25 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
         }
       }
       ss = group_sum<CPR>(ss);
+      float sq = 0.f;
+      if constexpr (F) {
+        const uint32_t w4[4] = {qreg[i].x, qreg[i].y, qreg[i].z, qreg[i].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = bf16_lo(w4[q]), hi = bf16_hi(w4[q]);
+          sq = fmaf(lo, lo, sq);
+          sq = fmaf(hi, hi, sq);
+        }
+        sq = group_sum<CPR>(sq);
+      }
       if (c < KCH) {
         uint4 h;
         h.x = bf16x2_to_f16x2(kv.x); h.y = bf16x2_to_f16x2(kv.y);
         h.z = bf16x2_to_f16x2(kv.z); h.w = bf16x2_to_f16x2(kv.w);
         *reinterpret_cast<uint4*>(&Ks[buf][j][ch * 8]) = h;
+        if constexpr (F) {
+          if (ch == 0) Nq[buf][j] = -0.5f * kLog2e * sq;
+        }
         const uint4 qv = qreg[i];
         h.x = bf16x2_to_f16x2(qv.x); h.y = bf16x2_to_f16x2(qv.y);
         h.z = bf16x2_to_f16x2(qv.z); h.w = bf16x2_to_f16x2(qv.w);
@@ -1495,7 +1515,15 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
     return onecol;
   };
 
-  auto chunk = [&](const int buf, const int jt) {
+  // FASTC true: the fast pass (softmax and Gaussian features, no carried
+  // reference): no per-feature key reference (the key exponent is at most
+  // |w|^2 log2(e) / 2 whatever k is) and the query's norm term as its row
+  // shift (it cancels in D^-1 and bounds the query exponent the same way),
+  // so the waves' partial outputs share one reference; a query whose
+  // denominator leaves [2^-100, 2^100] (or is not finite) sets `bad`.
+  bool bad = false;
+  auto chunk = [&](auto FASTC, const int buf, const int jt) {
+    constexpr bool F = decltype(FASTC)::value;
     // (1) Key exponents S = K W'^T - n' (lane = feature, rows = tokens).
     f32x4 SK[2][NT];
     {
@@ -1521,7 +1549,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
     bool raise = false;
     float lm[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT && !RELU; ++nt) {
+    for (int nt = 0; nt < NT && !RELU && !F; ++nt) {
       const float c = cref[nt] == -INFINITY ? 0.f : cref[nt];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -1532,7 +1560,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
       lm[nt] = max3(a, b, fmaxf(SK[1][nt][2], SK[1][nt][3]));
       raise |= (cref[nt] == -INFINITY) || lm[nt] > kTau;
     }
-    if (!RELU && __builtin_expect(__ballot(raise) != 0, 0)) {
+    if (!RELU && !F && __builtin_expect(__ballot(raise) != 0, 0)) {
       float fk[NT];   // rescale factor of feature 16 nt + l16 (every g)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -1563,9 +1591,11 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
         for (int tv = 0; tv < TV; ++tv) st[mt][tv] *= fv;
       }
     }
+    if constexpr (!F) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-      if (g == 0) cb[wave][16 * nt + l16] = RELU ? 0.f : cref[nt];
+      for (int nt = 0; nt < NT; ++nt)
+        if (g == 0) cb[wave][16 * nt + l16] = RELU ? 0.f : cref[nt];
+    }
     // K~ (lane = feature, 8 tokens at positions perm_of), and its transpose
     // into Kt (key rows; features permuted within 32-blocks for the MFMA).
     bf16x8 kb[NT];
@@ -1594,9 +1624,18 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
     f32x4 SQ[NT][2];
     {
       f32x4 cq[NT];
+      f32x4 cn[2];   // (fast pass) the query's norm term, lane = query
       f16x8 qa[2][KS];
+      if constexpr (F) {
 #pragma unroll
-      for (int mt = 0; mt < NT; ++mt) cq[mt] = *reinterpret_cast<const f32x4*>(&cb[wave][16 * mt + 4 * g]);
+        for (int nq = 0; nq < 2; ++nq) {
+          const float x = Nq[buf][16 * nq + l16];
+          cn[nq] = f32x4{x, x, x, x};
+        }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < NT; ++mt) cq[mt] = *reinterpret_cast<const f32x4*>(&cb[wave][16 * mt + 4 * g]);
+      }
 #pragma unroll
       for (int nq = 0; nq < 2; ++nq)
 #pragma unroll
@@ -1608,18 +1647,22 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
         for (int mt = 0; mt < NT; ++mt)
 #pragma unroll
           for (int nq = 0; nq < 2; ++nq)
-            SQ[mt][nq] = mma_f16(wreg[mt][ks], qa[nq][ks], ks == 0 ? cq[mt] : SQ[mt][nq]);
+            SQ[mt][nq] = mma_f16(wreg[mt][ks], qa[nq][ks],
+                                 ks == 0 ? (F ? cn[nq] : cq[mt]) : SQ[mt][nq]);
     }
     bf16x8 qt[2][2];   // [kb][nq]: lane = query, 8 features (perm_of within 32-block kb)
 #pragma unroll
     for (int nq = 0; nq < 2; ++nq) {
-      const float a = max3(SQ[0][nq][0], SQ[0][nq][1], SQ[0][nq][2]);
-      const float b = max3(SQ[0][nq][3], SQ[1][nq][0], SQ[1][nq][1]);
-      const float c = max3(SQ[1][nq][2], SQ[1][nq][3], SQ[2][nq][0]);
-      const float d = max3(SQ[2][nq][1], SQ[2][nq][2], SQ[2][nq][3]);
-      const float e = max3(SQ[3][nq][0], SQ[3][nq][1], SQ[3][nq][2]);
-      const float M = RELU ? 0.f : colmax4(max3(max3(a, b, c), max3(d, e, SQ[3][nq][3]), a));
-      if (g == 0) mq[wave][16 * nq + l16] = M;
+      float M = 0.f;
+      if constexpr (!RELU && !F) {
+        const float a = max3(SQ[0][nq][0], SQ[0][nq][1], SQ[0][nq][2]);
+        const float b = max3(SQ[0][nq][3], SQ[1][nq][0], SQ[1][nq][1]);
+        const float c = max3(SQ[1][nq][2], SQ[1][nq][3], SQ[2][nq][0]);
+        const float d = max3(SQ[2][nq][1], SQ[2][nq][2], SQ[2][nq][3]);
+        const float e = max3(SQ[3][nq][0], SQ[3][nq][1], SQ[3][nq][2]);
+        M = colmax4(max3(max3(a, b, c), max3(d, e, SQ[3][nq][3]), a));
+      }
+      if (!F && g == 0) mq[wave][16 * nq + l16] = M;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         uint32_t p[4];
@@ -1718,14 +1761,16 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
     // write O: thread -> (query, 8 columns); eight threads cover one row.
     for (int o = tid; o < kTT * (D / 8); o += NTH) {
       const int i = o / (D / 8), c0 = 8 * (o % (D / 8));
-      float mw[NW], mx = -INFINITY;
+      float mw[NW], mx = F ? 0.f : -INFINITY;
+      if constexpr (!F) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) { mw[w] = mq[w][i]; mx = fmaxf(mx, mw[w]); }
+        for (int w = 0; w < NW; ++w) { mw[w] = mq[w][i]; mx = fmaxf(mx, mw[w]); }
+      }
       float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       float den = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float sc = fast_exp2(mw[w] - mx);
+        const float sc = F ? 1.f : fast_exp2(mw[w] - mx);
         const float* row = &ured[w][i * CROW];
         den = fmaf(sc, row[D], den);
         const f32x4 a = *reinterpret_cast<const f32x4*>(row + c0);
@@ -1737,6 +1782,7 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
         }
       }
       const float inv = 1.0f / den;
+      if constexpr (F) bad |= (jt + i < j1) && !(den >= 0x1p-100f && den <= 0x1p100f);
       if constexpr (BWD) {
         // (the eight threads of a row are consecutive lanes of one wave)
         float pd = 0.f;
@@ -1763,15 +1809,42 @@ __global__ __launch_bounds__(NW * 64, 2) void cscan(const uint16_t* __restrict__
     }
   };
 
-  gload(0);
-  lstore(0, 0);
-  for (int t = 0; t < nch; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nch) gload(t + 1);
+  auto scan = [&](auto FASTC) {
+    gload(0);
+    lstore(FASTC, 0, 0);
+    for (int t = 0; t < nch; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < nch) gload(t + 1);
+      lds_barrier();
+      chunk(FASTC, buf, j0 + t * kTT);
+      if (t + 1 < nch) lstore(FASTC, buf ^ 1, t + 1);
+    }
+  };
+  if constexpr (!RELU && !BWD) {
+    // The fast pass when the carried state has no reference (every earlier
+    // segment's keys were summed without one); the referenced pass again
+    // from the carry-in when any query's denominator came out of range.
+    bool refd = false;
+#pragma unroll
+    for (int mt = 0; mt < NT; ++mt) refd |= cref[mt] != -INFINITY && cref[mt] != 0.f;
+    if (tid == 0) vote = 0u;
     lds_barrier();
-    chunk(buf, j0 + t * kTT);
-    if (t + 1 < nch) lstore(buf ^ 1, t + 1);
+    if (refd) vote = 1u;
+    lds_barrier();
+    if (vote == 0u) {
+#pragma unroll
+      for (int mt = 0; mt < NT; ++mt) cref[mt] = 0.f;
+      scan(std::true_type{});
+      lds_barrier();   // (every wave is done with the LDS tiles and the vote word)
+      if (tid == 0) vote = 0u;
+      lds_barrier();
+      if (bad) vote = 1u;
+      lds_barrier();
+      if (vote == 0u) return;
+      carry_in();
+    }
   }
+  scan(std::false_type{});
 }
 
 // The bidirectional path for m = NFB NW FPW features: kpart in NFB feature
