@@ -445,8 +445,10 @@ int favor_prefill(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t
     pc.knorm = pb.knorm = knorm;
     pc.relu = pb.relu = p.relu;
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = favor::mfma_causal_forward(pc, Q, K, V, W, O, workspace, st, state_in);
-    if (e == hipSuccess && state_out) {
+    bool exported = false;
+    hipError_t e = favor::mfma_causal_forward(pc, Q, K, V, W, O, workspace, st, state_in,
+                                              state_out, &exported);
+    if (e == hipSuccess && state_out && !exported) {
       char* wb = static_cast<char*>(workspace) + off_b;
       e = favor::mfma_bidir_key_partials(pb, K, V, W, wb, st);
       if (e == hipSuccess) e = favor::mfma_state_export(pb, wb, state_in, state_out, st);

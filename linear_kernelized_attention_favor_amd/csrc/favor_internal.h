@@ -164,22 +164,26 @@ hipError_t mfma_bidir_forward(const Plan& p, const void* Q, const void* K, const
 bool fused_bidir_supported(int32_t B, int32_t H, int32_t L, int32_t d, int32_t m, int32_t dtype);
 // Splits (seg, nseg) and query blocks (qblk) for `cus` compute units.
 void fused_bidir_layout(Plan* p, int cus);
-// The causal form's segment key states (every segment but the last) in the
-// layout of T and cseg, for d = 64, m = 256, bf16 inputs, softmax or
-// Gaussian features.
+// The causal form's segment key states (every segment but the last, or
+// every segment when all_segments) in the layout of T and cseg, for d = 64,
+// m = 256, bf16 inputs, softmax or Gaussian features.
 bool fused_causal_keys_supported(int32_t d, int32_t m, int32_t dtype, int32_t relu);
 hipError_t fused_causal_key_states(const Plan& p, const void* K, const void* V, const float* W,
-                                   float* T, float* cs, hipStream_t st);
+                                   float* T, float* cs, hipStream_t st, bool all_segments = false);
 hipError_t fused_bidir_forward(const Plan& p, const void* Q, const void* K, const void* V,
                                const float* W, void* O, void* ws, hipStream_t stream);
 
 // MFMA path (bf16 inputs): shape support, and the causal forward.
 bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype);
 // state_in (exported layout, nullptr: none) is a carried state that every
-// query also attends to.
+// query also attends to.  state_out (nullptr: none): where the path can, the
+// state after the last token (state_in plus every key) is written there in
+// the exported layout and *exported set; otherwise *exported stays false
+// and the caller forms it.
 hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, const void* V,
                                const float* W, void* O, void* ws, hipStream_t stream,
-                               const float* state_in = nullptr);
+                               const float* state_in = nullptr, float* state_out = nullptr,
+                               bool* exported = nullptr);
 
 // Measurement hooks behind favor_timing_*: each kernel launch is bracketed
 // by timing_before / timing_after (no-ops unless this thread is recording).

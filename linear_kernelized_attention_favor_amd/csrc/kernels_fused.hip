@@ -1245,8 +1245,8 @@ bool fused_causal_keys_supported(int32_t d, int32_t m, int32_t dtype, int32_t re
 }
 
 hipError_t fused_causal_key_states(const Plan& p, const void* K, const void* V, const float* W,
-                                   float* T, float* cs, hipStream_t st) {
-  const int nneed = p.nseg - 1;
+                                   float* T, float* cs, hipStream_t st, bool all_segments) {
+  const int nneed = all_segments ? p.nseg : p.nseg - 1;
   if (nneed < 1) return hipSuccess;
   Args a{};
   a.K = static_cast<const uint16_t*>(K);

@@ -1251,13 +1251,18 @@ __global__ __launch_bounds__(NW * 64, WPE) void qstream(const uint16_t* __restri
 // features of one row.  P[bh][s] becomes the sum of segments before s and
 // cP[bh][s] its per-feature reference, for s >= 1 (the scan starts the first
 // segment from a zero state and reads neither).  The last segment's own
-// state is never needed, so kpart leaves it out.  With an imported state Sin
-// (the exported layout [BH][m][D+4], reference in natural-log units) the sum
-// starts from it, and every segment, the first included, gets a carry.
+// state is not needed for the scan, so the state kernels leave it out,
+// unless Sout is given: then P[bh][nseg-1] holds it too and the total (the
+// state after the last token) goes to Sout in the exported layout (values
+// in units of e^c, c in natural-log units, zero pads; softmax and Gaussian
+// features only).  With an imported state Sin (the exported layout
+// [BH][m][D+4], reference in natural-log units) the sum starts from it, and
+// every segment, the first included, gets a carry.
 template <int D>
 __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const float* __restrict__ cs,
                                                float* __restrict__ cP, const float* __restrict__ Sin,
-                                               int m, int nseg, float sin_scale) {
+                                               int m, int nseg, float sin_scale,
+                                               float* __restrict__ Sout = nullptr) {
   const int bh = blockIdx.y;
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int mq = m / 4;
@@ -1286,8 +1291,8 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
     float4 ts[KB], c[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k) {
-      // (the last segment's own state is never read)
-      if (s0 + k + 1 < nseg) {
+      // (the last segment's own state is read only for the total)
+      if (s0 + k + 1 < nseg || (Sout && s0 + k < nseg)) {
         ts[k] = *slot(s0 + k);
         c[k] = *reinterpret_cast<const float4*>(cs + cidx(s0 + k));
       }
@@ -1299,7 +1304,7 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
       const bool put = s > 0 || carry;
       if (row == 0 && put) *reinterpret_cast<float4*>(cP + cidx(s)) = rc;
       if (put) *slot(s) = run;
-      if (s + 1 == nseg) break;
+      if (s + 1 == nseg && !Sout) break;
       float4 nc;
       nc.x = fmaxf(rc.x, c[k].x); nc.y = fmaxf(rc.y, c[k].y);
       nc.z = fmaxf(rc.z, c[k].z); nc.w = fmaxf(rc.w, c[k].w);
@@ -1308,6 +1313,23 @@ __global__ __launch_bounds__(256) void kprefix(float* __restrict__ P, const floa
       run.z = run.z * fast_exp2(rc.z - nc.z) + ts[k].z * fast_exp2(c[k].z - nc.z);
       run.w = run.w * fast_exp2(rc.w - nc.w) + ts[k].w * fast_exp2(c[k].w - nc.w);
       rc = nc;
+      if (s + 1 == nseg) break;
+    }
+  }
+  if (Sout) {
+    float* o = Sout + (static_cast<size_t>(bh) * m + f) * (D + 4);
+    o[row] = run.x;
+    o[(D + 4) + row] = run.y;
+    o[2 * (D + 4) + row] = run.z;
+    o[3 * (D + 4) + row] = run.w;
+    if (row == 0) {
+      const float rcn[4] = {rc.x, rc.y, rc.z, rc.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[j * (D + 4) + D + 1] = rcn[j] * 0.6931471805599453f;
+        o[j * (D + 4) + D + 2] = 0.f;
+        o[j * (D + 4) + D + 3] = 0.f;
+      }
     }
   }
 }
@@ -1901,15 +1923,20 @@ hipError_t launch_d(const Plan& p, const uint16_t* Q, const uint16_t* K, const u
 template <int NW, bool RELU>
 hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                          const float* W, uint16_t* O, char* ws, const float* Sin,
-                         hipStream_t st) {
+                         hipStream_t st, float* Sout, bool* exported) {
+  // The state after the last token comes out of the prefix pass when the
+  // segment states come from ckey (every segment's state, the last one's
+  // included).
+  const bool ckey_path = !RELU && NW == 4;
+  if (!ckey_path) Sout = nullptr;
   float* P = reinterpret_cast<float*>(ws + p.off_T);
   float* cs = reinterpret_cast<float*>(ws + p.off_cseg);
   float* cP = reinterpret_cast<float*>(ws + p.off_cP);
   hipError_t e;
-  if (p.nseg > 1 && !RELU && NW == 4) {
-    // Key states of every segment but the last, two segments per work-group
-    // (m = 256, softmax and Gaussian features).
-    e = fused_causal_key_states(p, K, V, W, P, cs, st);
+  if (ckey_path && (p.nseg > 1 || Sout)) {
+    // Key states of every segment but the last (with Sout: every segment),
+    // two segments per work-group (m = 256, softmax and Gaussian features).
+    e = fused_causal_key_states(p, K, V, W, P, cs, st, Sout != nullptr);
     if (e != hipSuccess) return e;
   } else if (p.nseg > 1) {
     // Key states of every segment but the last (grid nseg - 1; the layout
@@ -1922,13 +1949,14 @@ hipError_t launch_causal(const Plan& p, const uint16_t* Q, const uint16_t* K, co
     timing_after(st, "kpart");
     if (e != hipSuccess) return e;
   }
-  if (p.nseg > 1 || Sin) {
+  if (p.nseg > 1 || Sin || Sout) {
     timing_before(st);
     kprefix<64><<<dim3((65 * p.m / 4 + 255) / 256, p.BH), 256, 0, st>>>(
-        P, cs, cP, Sin, p.m, p.nseg, RELU ? kLog2e : 1.f);
+        P, cs, cP, Sin, p.m, p.nseg, RELU ? kLog2e : 1.f, Sout);
     e = hipGetLastError();
     timing_after(st, "kprefix");
     if (e != hipSuccess) return e;
+    if (Sout && exported) *exported = true;
   }
   timing_before(st);
   cscan<NW, RELU><<<dim3(p.nseg, p.BH), NW * 64, 0, st>>>(Q, K, V, W, P, cP, O, p.L, p.m, p.seg, p.nseg,
@@ -1999,7 +2027,8 @@ bool mfma_causal_supported(int32_t d, int32_t m, int32_t dtype) {
 
 hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, const void* V,
                                const float* W, void* O, void* ws, hipStream_t stream,
-                               const float* state_in) {
+                               const float* state_in, float* state_out, bool* exported) {
+  if (exported) *exported = false;
   const auto* q = static_cast<const uint16_t*>(Q);
   const auto* k = static_cast<const uint16_t*>(K);
   const auto* v = static_cast<const uint16_t*>(V);
@@ -2008,8 +2037,8 @@ hipError_t mfma_causal_forward(const Plan& p, const void* Q, const void* K, cons
   if (p.d == 64) {
 #define FAVOR_CCASE(NW)                                                            \
   case NW:                                                                         \
-    return p.relu ? launch_causal<NW, true>(p, q, k, v, W, o, w, state_in, stream) \
-                  : launch_causal<NW, false>(p, q, k, v, W, o, w, state_in, stream);
+    return p.relu ? launch_causal<NW, true>(p, q, k, v, W, o, w, state_in, stream, state_out, exported) \
+                  : launch_causal<NW, false>(p, q, k, v, W, o, w, state_in, stream, state_out, exported);
     switch (p.m / 64) {
       FAVOR_CCASE(1) FAVOR_CCASE(2) FAVOR_CCASE(3) FAVOR_CCASE(4)
       default: break;
