@@ -26,6 +26,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "favor.h"
 #include "favor_internal.h"
@@ -434,14 +435,19 @@ __global__ __launch_bounds__(kThreads) void g_state_reset(float* __restrict__ st
 // raised to cover the new key), then o = q~ [S | z] -> num / den with the
 // query's own row reference.  grid (BH), one work-group per head; the state
 // rows move as float4 quads, a quad column per thread and the rows split
-// over groups of threads.
-template <typename T>
+// over groups of threads.  The step is a chain of dependent memory round
+// trips, so every load a thread needs is issued before its first use: the
+// head dimension D is a template argument (a row of W is D / 4 float4 loads
+// issued at once), and the state rows go in batches of RB whose loads all
+// precede their stores.
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void g_decode(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v,
                                                      const float* __restrict__ W,
                                                      T* __restrict__ o, float* __restrict__ st,
-                                                     int d, int m, float knorm, int relu) {
+                                                     int m, float knorm, int relu) {
+  constexpr int d = D;
   const int bh = blockIdx.x, t = threadIdx.x;
   const int sw = d + 4, nq = sw / 4;
   const int ng = kThreads / nq;                  // row groups
@@ -468,9 +474,20 @@ __global__ __launch_bounds__(kThreads) void g_decode(const T* __restrict__ q,
   float* S = st + static_cast<size_t>(bh) * m * sw;
   float mx = -INFINITY;
   for (int r = t; r < m; r += kThreads) {
-    const float* w = W + static_cast<size_t>(r) * d;
-    const float e = dot_w(w, xk, d) - nk;
+    const float4* w4 = reinterpret_cast<const float4*>(W + static_cast<size_t>(r) * d);
+    float4 wr[D / 4];
+#pragma unroll
+    for (int a = 0; a < D / 4; ++a) wr[a] = w4[a];
     const float c = S[static_cast<size_t>(r) * sw + d + 1];
+    float e0 = 0.f, e1 = 0.f, s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int a = 0; a < D / 4; ++a) {
+      e0 = fmaf(wr[a].x, xk[4 * a], e0); e1 = fmaf(wr[a].y, xk[4 * a + 1], e1);
+      e0 = fmaf(wr[a].z, xk[4 * a + 2], e0); e1 = fmaf(wr[a].w, xk[4 * a + 3], e1);
+      s0 = fmaf(wr[a].x, xq[4 * a], s0); s1 = fmaf(wr[a].y, xq[4 * a + 1], s1);
+      s0 = fmaf(wr[a].z, xq[4 * a + 2], s0); s1 = fmaf(wr[a].w, xq[4 * a + 3], s1);
+    }
+    const float e = (e0 + e1) - nk;
     float cn;
     if (relu) {
       cn = 0.f;
@@ -482,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void g_decode(const T* __restrict__ q,
       kt[r] = expf(e - cn);
     }
     S[static_cast<size_t>(r) * sw + d + 1] = cn;
-    const float s = dot_w(w, xq, d);
+    const float s = s0 + s1;
     qt[r] = relu ? fmaxf(s, 0.f) : s + cn;
     mx = fmaxf(mx, qt[r]);
   }
@@ -506,18 +523,31 @@ __global__ __launch_bounds__(kThreads) void g_decode(const T* __restrict__ q,
     const float v0 = xv[c0], v1 = xv[c0 + 1], v2 = xv[c0 + 2], v3 = xv[c0 + 3];
     const bool up1 = c0 + 1 <= d, up2 = c0 + 2 <= d, up3 = c0 + 3 <= d;
     float4* S4 = reinterpret_cast<float4*>(S);
-    for (int r = g; r < m; r += ng) {
-      float4 x = S4[static_cast<size_t>(r) * nq + j];
-      const float a = sc[r], b = kt[r], qr = qt[r];
-      x.x = fmaf(x.x, a, b * v0);
-      if (up1) x.y = fmaf(x.y, a, b * v1);
-      if (up2) x.z = fmaf(x.z, a, b * v2);
-      if (up3) x.w = fmaf(x.w, a, b * v3);
-      S4[static_cast<size_t>(r) * nq + j] = x;
-      acc.x = fmaf(qr, x.x, acc.x);
-      acc.y = fmaf(qr, x.y, acc.y);
-      acc.z = fmaf(qr, x.z, acc.z);
-      acc.w = fmaf(qr, x.w, acc.w);
+    constexpr int RB = 24;   // (m = 256, d = 64: one batch)
+    for (int r0 = g; r0 < m; r0 += RB * ng) {
+      float4 xs[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int r = r0 + u * ng;
+        if (r < m) xs[u] = S4[static_cast<size_t>(r) * nq + j];
+      }
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int r = r0 + u * ng;
+        if (r < m) {
+          float4 x = xs[u];
+          const float a = sc[r], b = kt[r], qr = qt[r];
+          x.x = fmaf(x.x, a, b * v0);
+          if (up1) x.y = fmaf(x.y, a, b * v1);
+          if (up2) x.z = fmaf(x.z, a, b * v2);
+          if (up3) x.w = fmaf(x.w, a, b * v3);
+          S4[static_cast<size_t>(r) * nq + j] = x;
+          acc.x = fmaf(qr, x.x, acc.x);
+          acc.y = fmaf(qr, x.y, acc.y);
+          acc.z = fmaf(qr, x.z, acc.z);
+          acc.w = fmaf(qr, x.w, acc.w);
+        }
+      }
     }
     part[g][c0] = acc.x;
     part[g][c0 + 1] = acc.y;
@@ -549,14 +579,24 @@ hipError_t generic_decode(int32_t BH, int32_t d, int32_t m, int32_t dtype, float
                           int32_t relu, const void* q, const void* k, const void* v,
                           const float* W, void* o, float* state, hipStream_t stream) {
   timing_before(stream);
-  if (dtype == FAVOR_F32)
-    g_decode<float><<<BH, kThreads, 0, stream>>>(
-        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
-        W, static_cast<float*>(o), state, d, m, knorm, relu);
-  else
-    g_decode<uint16_t><<<BH, kThreads, 0, stream>>>(
-        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-        static_cast<const uint16_t*>(v), W, static_cast<uint16_t*>(o), state, d, m, knorm, relu);
+  auto launch = [&](auto DC) {
+    constexpr int D = decltype(DC)::value;
+    if (dtype == FAVOR_F32)
+      g_decode<float, D><<<BH, kThreads, 0, stream>>>(
+          static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+          W, static_cast<float*>(o), state, m, knorm, relu);
+    else
+      g_decode<uint16_t, D><<<BH, kThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+          static_cast<const uint16_t*>(v), W, static_cast<uint16_t*>(o), state, m, knorm, relu);
+  };
+  switch (d) {
+    case 16: launch(std::integral_constant<int, 16>{}); break;
+    case 32: launch(std::integral_constant<int, 32>{}); break;
+    case 64: launch(std::integral_constant<int, 64>{}); break;
+    case 128: launch(std::integral_constant<int, 128>{}); break;
+    default: return hipErrorInvalidValue;
+  }
   const hipError_t e = hipGetLastError();
   timing_after(stream, "g_decode");
   return e;
