@@ -47,6 +47,7 @@ __device__ inline void load_rows(const T* __restrict__ X, size_t base, int j0, i
 __device__ inline void norm_terms(const float (*rows)[kMaxD + 1], int d, float knorm, float* nrm) {
   if (threadIdx.x < kTT) {
     float acc = 0.f;
+#pragma unroll 16
     for (int a = 0; a < d; ++a) acc = fmaf(rows[threadIdx.x][a], rows[threadIdx.x][a], acc);
     nrm[threadIdx.x] = knorm * acc;
   }
@@ -60,6 +61,7 @@ __device__ inline float feat(float e, int relu) { return relu ? fmaxf(e, 0.f) : 
 // w . x over d coordinates, w from global memory (row of W), x from LDS.
 __device__ inline float dot_w(const float* __restrict__ w, const float* x, int d) {
   float acc = 0.f;
+#pragma unroll 8
   for (int a = 0; a < d; a += 4) {
     const float4 wv = *reinterpret_cast<const float4*>(w + a);
     acc = fmaf(wv.x, x[a], acc);

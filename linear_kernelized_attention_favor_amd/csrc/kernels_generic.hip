@@ -40,13 +40,16 @@ using namespace generic_detail;
 // ---------------------------------------------------------------------------
 // 1. Per-segment key state.  grid (nseg, ceil(m / kFB), BH).
 // ---------------------------------------------------------------------------
-template <typename T>
+// (D: the head dimension, a template argument so that every loop over it
+// is unrolled and its loads issued together.)
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void g_state(const T* __restrict__ K,
                                                     const T* __restrict__ V,
                                                     const float* __restrict__ W,
                                                     float* __restrict__ Tout,
-                                                    float* __restrict__ cseg, int L, int d, int m,
+                                                    float* __restrict__ cseg, int L, int m,
                                                     int seg, int nseg, float knorm, int relu) {
+  constexpr int d = D;
   const int s = blockIdx.x, fb = blockIdx.y, bh = blockIdx.z;
   const int t = threadIdx.x;
   const int r = t % kFB, jj = t / kFB;  // this thread's feature and tile row
@@ -185,12 +188,13 @@ __global__ __launch_bounds__(kThreads) void g_combine(float* __restrict__ Tst,
 // ---------------------------------------------------------------------------
 // 3. Query side.  grid (ceil(L/kTT), BH).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void g_apply(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ W, const float* __restrict__ KVst, const float* __restrict__ cst,
-    const float* __restrict__ csg, T* __restrict__ O, int L, int d, int m, int seg, int nseg,
+    const float* __restrict__ csg, T* __restrict__ O, int L, int m, int seg, int nseg,
     int causal, float knorm, int relu) {
+  constexpr int d = D;
   const int tile = blockIdx.x, bh = blockIdx.y;
   const int t = threadIdx.x;
   const int i0 = tile * kTT;
@@ -378,8 +382,14 @@ hipError_t key_state_t(const Plan& p, const T* K, const T* V, const float* W, ch
   float* KV = reinterpret_cast<float*>(ws + p.off_KV);
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   timing_before(st);
-  g_state<T><<<dim3(p.nseg, (p.m + kFB - 1) / kFB, p.BH), kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.d,
-                                                                  p.m, p.seg, p.nseg, p.knorm, p.relu);
+  const dim3 gs(p.nseg, (p.m + kFB - 1) / kFB, p.BH);
+  switch (p.d) {
+    case 16: g_state<T, 16><<<gs, kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.m, p.seg, p.nseg, p.knorm, p.relu); break;
+    case 32: g_state<T, 32><<<gs, kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.m, p.seg, p.nseg, p.knorm, p.relu); break;
+    case 64: g_state<T, 64><<<gs, kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.m, p.seg, p.nseg, p.knorm, p.relu); break;
+    case 128: g_state<T, 128><<<gs, kThreads, 0, st>>>(K, V, W, Tst, cseg, p.L, p.m, p.seg, p.nseg, p.knorm, p.relu); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   timing_after(st, "g_state");
   if (e != hipSuccess) return e;
@@ -405,12 +415,21 @@ hipError_t forward_t(const Plan& p, const T* Q, const T* K, const T* V, const fl
   float* cfin = reinterpret_cast<float*>(ws + p.off_cfin);
   const dim3 ga((p.L + kTT - 1) / kTT, p.BH);
   timing_before(st);
-  if (p.causal)
-    g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, Tst, cP, cseg, O, p.L, p.d, p.m, p.seg,
-                                        p.nseg, 1, p.knorm, p.relu);
-  else
-    g_apply<T><<<ga, kThreads, 0, st>>>(Q, K, V, W, KV, cfin, nullptr, O, p.L, p.d, p.m, p.seg,
-                                        p.nseg, 0, p.knorm, p.relu);
+  const float* kvs = p.causal ? Tst : KV;
+  const float* cst = p.causal ? cP : cfin;
+  const float* csg = p.causal ? cseg : nullptr;
+  auto apply = [&](auto DC) {
+    constexpr int D = decltype(DC)::value;
+    g_apply<T, D><<<ga, kThreads, 0, st>>>(Q, K, V, W, kvs, cst, csg, O, p.L, p.m, p.seg, p.nseg,
+                                           p.causal ? 1 : 0, p.knorm, p.relu);
+  };
+  switch (p.d) {
+    case 16: apply(std::integral_constant<int, 16>{}); break;
+    case 32: apply(std::integral_constant<int, 32>{}); break;
+    case 64: apply(std::integral_constant<int, 64>{}); break;
+    case 128: apply(std::integral_constant<int, 128>{}); break;
+    default: return hipErrorInvalidValue;
+  }
   e = hipGetLastError();
   timing_after(st, "g_apply");
   return e;
