@@ -231,7 +231,18 @@ void make_generic_plan(Plan* p) {
   p->path = kPathGeneric;
   // Sequence splits (bidirectional) and segments (causal); a multiple of the
   // 8-token tile of the generic kernels (a caller may preset a segment length).
-  if (p->seg <= 0) p->seg = causal ? 256 : 512;
+  // Causal segments of 64 tokens (the masked in-segment term costs O(segment)
+  // per token), doubled up to 256 while the segment states would pass 512 MB.
+  if (p->seg <= 0) {
+    if (causal) {
+      p->seg = 64;
+      while (p->seg < 256 && BH * ((static_cast<size_t>(L) + p->seg - 1) / p->seg) * m * ncol *
+                                     sizeof(float) > (static_cast<size_t>(512) << 20))
+        p->seg *= 2;
+    } else {
+      p->seg = 512;
+    }
+  }
   p->nseg = (L + p->seg - 1) / p->seg;
   p->off_T = off;    off = align256(off + BH * p->nseg * m * ncol * sizeof(float));
   p->off_cseg = off; off = align256(off + BH * p->nseg * m * sizeof(float));
