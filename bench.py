@@ -153,7 +153,7 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int, backward: bool = F
            # (projection, dv)
            "bq_den": (2, 4.0), "bq_dq": (1, 6.0), "bq_g": (0, 4.0),
            "bkey_dk": (1, 6.0), "bkey_dv": (1, 4.0),
-           # causal matrix-core backward (kpart owns the K, V reads and the
+           # causal matrix-core backward (kpart or ckey owns the K, V reads and the
            # key state): the scan for (L, p) reads Q and dO (both
            # projections, [num | den], the state update: 8 d m); dq (both
            # projections, T, state update, dq: 10 d m); the segments' query
@@ -172,8 +172,8 @@ def kernel_work(name: str, w, nseg: int, seg: int, elem: int, backward: bool = F
         return (nb * w.d * elem * th, nf * w.d * w.m * th)
     half = (2 * w.d * elem * th, 4.0 * w.d * w.m * th)
     if backward:
-        # the backward's key state: kpart (or g_state) reads K and V once
-        return half if name in ("kpart", "g_state") else (0, 0.0)
+        # the backward's key state: kpart, ckey or g_state reads K and V once
+        return half if name in ("kpart", "ckey", "g_state") else (0, 0.0)
     if w.causal:
         # The causal scan reads Q, K, V and writes O and does both projections
         # and both contractions: the whole path's algorithmic work.  The

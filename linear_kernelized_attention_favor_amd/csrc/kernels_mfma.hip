@@ -1976,11 +1976,18 @@ hipError_t launch_rowstats(const Plan& p, const uint16_t* Q, const uint16_t* K, 
   float* P = reinterpret_cast<float*>(ws + p.off_T);
   float* cs = reinterpret_cast<float*>(ws + p.off_cseg);
   float* cP = reinterpret_cast<float*>(ws + p.off_cP);
-  timing_before(st);
-  kpart<64, NW, 1, RELU><<<dim3(p.nseg * p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
-                                                                  p.nseg, p.nseg, p.knorm);
-  hipError_t e = hipGetLastError();
-  timing_after(st, "kpart");
+  hipError_t e;
+  if (!RELU && NW == 4) {
+    // every segment's state, two segments per work-group (m = 256, softmax
+    // and Gaussian features)
+    e = fused_causal_key_states(p, K, V, W, P, cs, st, true);
+  } else {
+    timing_before(st);
+    kpart<64, NW, 1, RELU><<<dim3(p.nseg * p.BH), NW * 64, 0, st>>>(K, V, W, P, cs, p.L, p.m, p.seg,
+                                                                    p.nseg, p.nseg, p.knorm);
+    e = hipGetLastError();
+    timing_after(st, "kpart");
+  }
   if (e != hipSuccess) return e;
   if (p.nseg > 1) {
     timing_before(st);
