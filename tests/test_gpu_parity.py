@@ -238,6 +238,31 @@ def test_full_size_all_heads(fv, name, causal):
     _all_heads(f"{name} causal={causal}", w, causal, q, k, v, out, W, _ref)
 
 
+# The generic causal path's segments are 64 tokens, doubled (up to 256) while
+# the per-segment states would pass 512 MB: these fp32 shapes (m = 1024 is
+# beyond the matrix-core forms) take the 128- and 256-token segments.  Every
+# head against the oracle at the fp32 bar.
+@pytest.mark.parametrize("H,seg", [(16, 128), (32, 256)])
+def test_generic_causal_long_segments_all_heads(fv, H, seg):
+    B, L, d, m = 1, 8192, 64, 1024
+    path, nseg, got_seg = fv.plan_describe(B, H, L, d, m, fv.F32, True)
+    assert (path, nseg, got_seg) == (0, L // seg, seg)
+    q, k, v = _case(B, H, L, d, m, "f32", seed=80 + H)
+    W = _w(90 + H, m, d)
+    out = fv.fwd_causal(q.cuda(), k.cuda(), v.cuda(), torch.from_numpy(W).cuda())
+    torch.cuda.synchronize()
+    qf, kf, vf = (x.reshape(B * H, L, d) for x in (q, k, v))
+    of = out.cpu().reshape(B * H, L, d).double().numpy()
+
+    def job(h0, h1):
+        ref = _ref(True, qf[h0:h1], kf[h0:h1], vf[h0:h1], W)
+        return [oracle.row_rel_err(of[h0 + i], ref[i]) for i in range(h1 - h0)]
+
+    errs = fullsize.per_head(B * H, 4, job)
+    worst, e = fullsize.report(f"generic causal, {seg}-token segments", errs)
+    assert e <= TOL["f32"], (worst, e)
+
+
 # ---------------------------------------------------------------------------
 # Feature map (projection and exponent arithmetic) and robustness.
 # ---------------------------------------------------------------------------
